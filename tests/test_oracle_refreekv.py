@@ -1,0 +1,167 @@
+"""Pins for the ReFreeKV oracle (CPU only).
+
+Closed forms from tests/golden/refreekv_closed_forms.txt (uniform attention,
+spikes, geometric energies), a brute-force linear search with exactly rounded
+sums, a library softmax, and invariants (kept energy reaches the threshold,
+one token less does not; monotone in T; first two layers whole).
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import refreekv as rf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _closed_forms(kind):
+    rows = []
+    with open(os.path.join(GOLDEN, "refreekv_closed_forms.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line.startswith(kind + " "):
+                rows.append({k: float(v) for k, v in (t.split("=") for t in line.split()[1:])})
+    assert rows
+    return rows
+
+
+def test_rank_order_closed_form():
+    assert rf.rank_order(10, 4).tolist() == [0, 1, 2, 3, 9, 8, 7, 6, 5, 4]
+    assert rf.rank_order(3, 4).tolist() == [0, 1, 2]
+    assert rf.rank_order(5, 4).tolist() == [0, 1, 2, 3, 4]
+    assert rf.rank_order(0, 4).tolist() == []
+
+
+def test_last_row_attention_two_keys():
+    # d = 4: logits (q.k)/2 = 3 and 0 -> a0 = e^3/(e^3+1)
+    q = np.array([[1.0, 1.0, 1.0, 1.0]])
+    k = np.array([[1.5, 1.5, 1.5, 1.5], [0, 0, 0, 0]])
+    a0 = math.exp(3.0) / (math.exp(3.0) + 1.0)
+    assert rf.last_row_attention(q, k)[0] == pytest.approx([a0, 1 - a0], abs=1e-15)
+
+
+def test_last_row_attention_matches_library():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((7, 128)) * 3
+    k = rng.standard_normal((333, 128))
+    want = scipy.special.softmax(q @ k.T / math.sqrt(128), axis=1)
+    assert np.allclose(rf.last_row_attention(q, k), want, rtol=1e-12, atol=0)
+
+
+def test_energy_is_group_frobenius():
+    a = np.array([[0.5, 0.5, 0.0], [0.0, 0.25, 0.75]])
+    assert rf.energies(a) == pytest.approx([0.25, 0.3125, 0.5625], abs=1e-16)
+    assert rf.energies(a).sum() == pytest.approx(np.linalg.norm(a, "fro") ** 2, abs=1e-15)
+
+
+@pytest.mark.parametrize("row", _closed_forms("uniform"), ids=lambda r: f"n{int(r['n'])}")
+def test_uniform_attention_closed_form(row):
+    n, m, T, L = int(row["n"]), int(row["m"]), row["T"], int(row["L"])
+    d = 16
+    rng = np.random.default_rng(n)
+    k = rng.standard_normal((1, 1, n, d))
+    got, _ = rf.threshold_cut(np.zeros((1, 1, d)), k, [n], layer=5, m=m, T=T)
+    assert int(got[0, 0]) == L
+
+
+@pytest.mark.parametrize("row", _closed_forms("spike"), ids=lambda r: f"t{int(r['t'])}")
+def test_spike_attention_closed_form(row):
+    n, m, t, T, L = int(row["n"]), int(row["m"]), int(row["t"]), row["T"], int(row["L"])
+    d = 8
+    k = np.zeros((1, 1, n, d))
+    spikes = list(range(m)) + list(range(n - t, n))
+    k[0, 0, spikes, 0] = 30.0 * math.sqrt(d)       # logit 30 with q = e0
+    q = np.zeros((1, 1, d))
+    q[0, 0, 0] = 1.0
+    got, _ = rf.threshold_cut(q, k, [n], layer=2, m=m, T=T)
+    assert int(got[0, 0]) == L
+
+
+@pytest.mark.parametrize("row", _closed_forms("geometric"), ids=lambda r: f"r{r['r']}")
+def test_geometric_energy_closed_form(row):
+    n, m, r, T, L = int(row["n"]), int(row["m"]), row["r"], row["T"], int(row["L"])
+    e = np.zeros(n)
+    e[m:] = r ** (n - 1 - np.arange(m, n))
+    assert rf.cut_length(e, m, T) == L
+    # the fixed-point form reaches the same cut on the same energies
+    E = np.floor(e * 2.0 ** 52).astype(np.uint64)
+    assert rf.cut_length_fixed(E, m, T) == L
+
+
+def _linear_search(e, m, T):
+    """Independent: for p = 1.. test the exactly rounded energy of the first p ranked."""
+    n = len(e)
+    if n == 0:
+        return 0
+    order = list(range(min(m, n))) + list(range(n - 1, min(m, n) - 1, -1))
+    total = math.fsum(e)
+    for p in range(1, n + 1):
+        if math.fsum(e[j] for j in order[:p]) >= (1 - T) * total:
+            return max(min(m, n), p)
+    return n
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_cut_matches_linear_search(seed):
+    rng = np.random.default_rng(200 + seed)
+    n = int(rng.integers(1, 300))
+    e = rng.exponential(size=n) * (rng.random(n) < 0.7)
+    e[-min(5, n):] *= 20
+    T = float(rng.choice([0.001, 0.01, 0.1, 0.3]))
+    assert rf.cut_length(e, 4, T) == _linear_search(e, 4, T)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_cut_invariants_and_monotone(seed):
+    rng = np.random.default_rng(300 + seed)
+    n, d, g = int(rng.integers(50, 900)), 32, 4
+    q = rng.standard_normal((g, d)) * 2
+    k = rng.standard_normal((n, d))
+    e = rf.energies(rf.last_row_attention(q, k))
+    total = e.sum()
+    order = rf.rank_order(n, 4)
+    prev = n + 1
+    for T in [0.0001, 0.001, 0.01, 0.05, 0.1, 0.5]:
+        L = rf.cut_length(e, 4, T)
+        kept = e[order[:L]].sum()
+        assert kept >= (1 - T) * total * (1 - 1e-12)
+        if L > 4:
+            assert e[order[:L - 1]].sum() < (1 - T) * total
+        assert L <= prev
+        prev = L
+        pos = rf.kept_positions(n, L, 4)
+        assert len(pos) == L and sorted(set(order[:L].tolist())) == pos.tolist()
+
+
+def test_first_layers_keep_everything_and_edges():
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((2, 2, 64, 16))
+    q = rng.standard_normal((2, 4, 16))
+    for layer in (0, 1):
+        L, _ = rf.threshold_cut(q, k, [64, 10], layer=layer)
+        assert L.tolist() == [[64, 64], [10, 10]]
+    L, _ = rf.threshold_cut(q, k, [0, 3], layer=2)
+    assert L.tolist() == [[0, 0], [3, 3]]
+
+
+def test_fixed_point_energies_exact():
+    a = np.array([[0.5, 0.25], [0.5, 0.0]], dtype=np.float32)
+    E = rf.energies_fixed(a)
+    assert E.tolist() == [2 ** 51, 2 ** 48]          # 0.25+0.25 and 1/16, times 2^52
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_fixed_point_cut_agrees_with_fp64(seed):
+    rng = np.random.default_rng(400 + seed)
+    n, d, g = int(rng.integers(100, 3000)), 64, 7
+    q = rng.standard_normal((g, d)) * 3
+    k = rng.standard_normal((n, d))
+    a = rf.last_row_attention(q, k)
+    L64 = rf.cut_length(rf.energies(a), 4, 0.01)
+    Lfx = rf.cut_length_fixed(rf.energies_fixed(a.astype(np.float32)), 4, 0.01)
+    # both are valid cuts of the same energies up to fp32 rounding of a
+    assert abs(L64 - Lfx) <= 1
