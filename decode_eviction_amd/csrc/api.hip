@@ -1,0 +1,418 @@
+// libkvsel C ABI: argument checks, workspace carving and launch sequences.
+// Nothing here allocates memory or keeps state; every launch goes to the
+// caller's stream.  The formulas each entry point computes are stated in
+// include/kvsel.h.
+#include <math.h>
+
+#include "../../include/kvsel.h"
+#include "kernels.hpp"
+
+using namespace kvsel;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int rows_padded(int m) { return m <= 32 ? 32 : (m <= 64 ? 64 : 128); }
+
+kvsel_status hip_status(hipError_t e) { return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP; }
+
+#define KV_TRY(expr)                         \
+  do {                                       \
+    hipError_t e_ = (expr);                  \
+    if (e_ != hipSuccess) return KVSEL_ERR_HIP; \
+  } while (0)
+
+// -------------------------------------------------------------- R-KV layout
+
+struct ScoreWs {
+  int32_t* err;
+  float2* cstat;
+  float2* rstat;
+  float* spart;
+  float* ssum;
+  float* inv_norm;
+  float* imp;
+  float* z;
+  size_t bytes;
+};
+
+ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap) {
+  const size_t heads = (size_t)b * hkv;
+  const int nchunk = (cap + kChunk - 1) / kChunk;
+  const int mp = rows_padded(m);
+  Carver c{static_cast<char*>(base)};
+  ScoreWs w;
+  w.err = c.take<int32_t>(64);
+  w.cstat = c.take<float2>(heads * nchunk * mp);
+  w.rstat = c.take<float2>(heads * mp);
+  w.spart = c.take<float>(heads * nchunk * d);
+  w.ssum = c.take<float>(heads * d);
+  w.inv_norm = c.take<float>(heads * cap);
+  w.imp = c.take<float>(heads * cap);
+  w.z = c.take<float>(heads * cap);
+  w.bytes = (c.off + kAlign - 1) / kAlign * kAlign;
+  return w;
+}
+
+kvsel_status check_score_args(kvsel_dtype dt, kvsel_redundancy mode, const void* q,
+                              const void* k, const int32_t* lengths, int b, int hq, int hkv,
+                              int d, int w, int cap, float lambda) {
+  if (dt != KVSEL_BF16 && dt != KVSEL_F32) return KVSEL_ERR_INVALID_ARG;
+  if (mode != KVSEL_R_GRAM && mode != KVSEL_R_KEYSUM) return KVSEL_ERR_INVALID_ARG;
+  if (!q || !k || !lengths) return KVSEL_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k)) return KVSEL_ERR_INVALID_ARG;
+  if (b < 1 || hq < 1 || hkv < 1 || w < 1 || cap < 1) return KVSEL_ERR_INVALID_ARG;
+  if (b > 65535 || hkv > 65535 || cap >= (1 << 24)) return KVSEL_ERR_UNSUPPORTED;
+  if (hq % hkv != 0) return KVSEL_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return KVSEL_ERR_UNSUPPORTED;
+  if ((long)(hq / hkv) * w > kMaxRows) return KVSEL_ERR_UNSUPPORTED;
+  if (!(lambda >= 0.f && lambda <= 1.f)) return KVSEL_ERR_INVALID_ARG;
+  return KVSEL_OK;
+}
+
+kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, const void* k,
+                        const int32_t* lengths, int b, int hq, int hkv, int d, int w, int cap,
+                        float lambda, float* i_out, float* r_out, float* z_out,
+                        const ScoreWs& ws, hipStream_t stream, Trace* tr) {
+  const int g = hq / hkv;
+  ScoreParams p{};
+  p.q = static_cast<const char*>(q);
+  p.k = static_cast<const char*>(k);
+  p.lengths = lengths;
+  p.b = b;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.g = g;
+  p.w = w;
+  p.m = g * w;
+  p.mp = rows_padded(p.m);
+  p.cap = cap;
+  p.nchunk = (cap + kChunk - 1) / kChunk;
+  p.scale = 1.0f / sqrtf((float)d);
+  p.lambda = lambda;
+  p.cstat = ws.cstat;
+  p.rstat = ws.rstat;
+  p.spart = ws.spart;
+  p.ssum = ws.ssum;
+  p.inv_norm = ws.inv_norm;
+  p.logits = nullptr;
+  p.err = ws.err;
+  p.i_out = i_out ? i_out : ws.imp;
+  p.r_out = r_out;
+  p.z_out = z_out;
+  const int sm = mode == KVSEL_R_GRAM ? kModeGram : kModeKeysum;
+  KV_TRY(launch_stats(dt, d, sm, p, stream, tr));
+  KV_TRY(launch_reduce(d, sm, p, stream, tr));
+  KV_TRY(launch_pool(dt, d, sm, p, stream, tr));
+  if (mode == KVSEL_R_GRAM) {
+    GramParams gp{};
+    gp.k = p.k;
+    gp.lengths = lengths;
+    gp.b = b;
+    gp.hkv = hkv;
+    gp.cap = cap;
+    gp.lambda = lambda;
+    gp.inv_norm = ws.inv_norm;
+    gp.i_in = p.i_out;
+    gp.r_out = r_out;
+    gp.z_out = z_out;
+    KV_TRY(launch_gram(dt, d, gp, stream, tr));
+  }
+  return KVSEL_OK;
+}
+
+// ---------------------------------------------------------- ReFreeKV layout
+
+struct CutWs {
+  int32_t* err;
+  float2* cstat;
+  float2* rstat;
+  float* logits;
+  uint64_t* energy;
+  uint64_t* ctot;
+  size_t bytes;
+};
+
+CutWs cut_ws(void* base, int b, int hkv, int g, int cap) {
+  const size_t heads = (size_t)b * hkv;
+  const int nchunk = (cap + kChunk - 1) / kChunk;
+  const int mp = rows_padded(g);
+  Carver c{static_cast<char*>(base)};
+  CutWs w;
+  w.err = c.take<int32_t>(64);
+  w.cstat = c.take<float2>(heads * nchunk * mp);
+  w.rstat = c.take<float2>(heads * mp);
+  w.logits = c.take<float>(heads * g * (size_t)nchunk * kChunk);
+  w.energy = c.take<uint64_t>(heads * (size_t)nchunk * kChunk);
+  w.ctot = c.take<uint64_t>(heads * nchunk);
+  w.bytes = (c.off + kAlign - 1) / kAlign * kAlign;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvsel_status_string(kvsel_status s) {
+  switch (s) {
+    case KVSEL_OK: return "ok";
+    case KVSEL_ERR_INVALID_ARG: return "invalid argument";
+    case KVSEL_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case KVSEL_ERR_WORKSPACE: return "workspace too small";
+    case KVSEL_ERR_HIP: return "HIP launch or copy failed";
+  }
+  return "unknown status";
+}
+
+size_t kvsel_score_evict_workspace(int b, int hq, int hkv, int d, int w, int cap, int budget) {
+  (void)budget;
+  if (b < 1 || hq < 1 || hkv < 1 || w < 1 || cap < 1 || (d != 64 && d != 128)) return 0;
+  return score_ws(nullptr, b, hkv, d, (hq / hkv) * w, cap).bytes;
+}
+
+kvsel_status kvsel_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q_window,
+                          const void* k, const int32_t* lengths, int b, int hq, int hkv, int d,
+                          int w, int cap, float lambda, float* i_out, float* r_out, float* z_out,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
+  kvsel_status st = check_score_args(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda);
+  if (st != KVSEL_OK) return st;
+  if (!z_out) return KVSEL_ERR_INVALID_ARG;
+  const ScoreWs need = score_ws(nullptr, b, hkv, d, (hq / hkv) * w, cap);
+  if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
+  const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap);
+  return run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, i_out, r_out,
+                    z_out, ws, stream, nullptr);
+}
+
+size_t kvsel_select_workspace(int b, int hkv, int cap) {
+  (void)b;
+  (void)hkv;
+  (void)cap;
+  return 0;
+}
+
+kvsel_status kvsel_select_topb(const float* z, const int32_t* lengths, int b, int hkv, int cap,
+                               int budget, int32_t* idx_out, void* workspace, size_t ws_bytes,
+                               hipStream_t stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (!z || !lengths || !idx_out) return KVSEL_ERR_INVALID_ARG;
+  if (b < 1 || hkv < 1 || cap < 1 || budget < 1) return KVSEL_ERR_INVALID_ARG;
+  if (b > 65535 || hkv > 65535 || cap >= (1 << 24) || budget > 65536) return KVSEL_ERR_UNSUPPORTED;
+  SelectParams p{z, lengths, b, hkv, cap, budget, idx_out};
+  return hip_status(launch_select(p, stream, nullptr));
+}
+
+kvsel_status kvsel_gather(kvsel_dtype dt, const void* k, const void* v, const int32_t* idx, int b,
+                          int hkv, int d, int cap, int budget, void* k_out, void* v_out,
+                          int cap_out, hipStream_t stream) {
+  if (dt != KVSEL_BF16 && dt != KVSEL_F32) return KVSEL_ERR_INVALID_ARG;
+  if (!k || !v || !idx || !k_out || !v_out) return KVSEL_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out))
+    return KVSEL_ERR_INVALID_ARG;
+  if (b < 1 || hkv < 1 || cap < 1 || budget < 1 || cap_out < budget) return KVSEL_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return KVSEL_ERR_UNSUPPORTED;
+  if (b > 65535 || hkv > 65535 || cap >= (1 << 24) || budget > 65536) return KVSEL_ERR_UNSUPPORTED;
+  GatherParams p{static_cast<const char*>(k), static_cast<const char*>(v), idx, b, hkv, cap, budget,
+                 cap_out, static_cast<char*>(k_out), static_cast<char*>(v_out)};
+  return hip_status(launch_gather(dt, d, p, stream, nullptr));
+}
+
+static kvsel_status score_evict_impl(kvsel_dtype dt, kvsel_redundancy mode, const void* q_window,
+                                     const void* k, const void* v, const int32_t* lengths, int b,
+                                     int hq, int hkv, int d, int w, int cap, float lambda,
+                                     int budget, void* k_out, void* v_out, int cap_out,
+                                     int32_t* idx_out, float* scores_out, void* workspace,
+                                     size_t ws_bytes, hipStream_t stream, Trace* tr) {
+  kvsel_status st = check_score_args(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda);
+  if (st != KVSEL_OK) return st;
+  if (!v || !k_out || !v_out || !idx_out) return KVSEL_ERR_INVALID_ARG;
+  if (!aligned16(v) || !aligned16(k_out) || !aligned16(v_out)) return KVSEL_ERR_INVALID_ARG;
+  if (budget < 1 || budget > cap_out) return KVSEL_ERR_INVALID_ARG;
+  if (budget > 65536) return KVSEL_ERR_UNSUPPORTED;
+  const ScoreWs need = score_ws(nullptr, b, hkv, d, (hq / hkv) * w, cap);
+  if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
+  const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap);
+  float* z = scores_out ? scores_out : ws.z;
+  st = run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, nullptr, nullptr,
+                  z, ws, stream, tr);
+  if (st != KVSEL_OK) return st;
+  SelectParams sp{z, lengths, b, hkv, cap, budget, idx_out};
+  KV_TRY(launch_select(sp, stream, tr));
+  GatherParams gp{static_cast<const char*>(k), static_cast<const char*>(v), idx_out, b, hkv, cap,
+                  budget, cap_out, static_cast<char*>(k_out), static_cast<char*>(v_out)};
+  KV_TRY(launch_gather(dt, d, gp, stream, tr));
+  return KVSEL_OK;
+}
+
+kvsel_status kvsel_score_evict(kvsel_dtype dt, kvsel_redundancy mode, const void* q_window,
+                               const void* k, const void* v, const int32_t* lengths, int b, int hq,
+                               int hkv, int d, int w, int cap, float lambda, int budget,
+                               void* k_out, void* v_out, int cap_out, int32_t* idx_out,
+                               float* scores_out, void* workspace, size_t ws_bytes,
+                               hipStream_t stream) {
+  return score_evict_impl(dt, mode, q_window, k, v, lengths, b, hq, hkv, d, w, cap, lambda, budget,
+                          k_out, v_out, cap_out, idx_out, scores_out, workspace, ws_bytes, stream,
+                          nullptr);
+}
+
+kvsel_status kvsel_score_evict_traced(kvsel_dtype dt, kvsel_redundancy mode, const void* q_window,
+                                      const void* k, const void* v, const int32_t* lengths, int b,
+                                      int hq, int hkv, int d, int w, int cap, float lambda,
+                                      int budget, void* k_out, void* v_out, int cap_out,
+                                      int32_t* idx_out, float* scores_out, void* workspace,
+                                      size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
+                                      int n_events) {
+  if (!events || n_events < 2) return KVSEL_ERR_INVALID_ARG;
+  Trace tr{events, n_events, 0};
+  return score_evict_impl(dt, mode, q_window, k, v, lengths, b, hq, hkv, d, w, cap, lambda, budget,
+                          k_out, v_out, cap_out, idx_out, scores_out, workspace, ws_bytes, stream,
+                          &tr);
+}
+
+size_t kvsel_threshold_cut_workspace(int b, int hq, int hkv, int d, int cap) {
+  (void)d;
+  if (b < 1 || hq < 1 || hkv < 1 || cap < 1 || hq % hkv) return 0;
+  return cut_ws(nullptr, b, hkv, hq / hkv, cap).bytes;
+}
+
+static kvsel_status check_cut_common(const int32_t* lengths, int b, int hq, int hkv, int cap,
+                                     int n_sink, float T, const int32_t* kept) {
+  if (!lengths || !kept) return KVSEL_ERR_INVALID_ARG;
+  if (b < 1 || hq < 1 || hkv < 1 || cap < 1 || n_sink < 0) return KVSEL_ERR_INVALID_ARG;
+  if (hq % hkv != 0) return KVSEL_ERR_INVALID_ARG;
+  if (b > 65535 || hkv > 65535 || cap >= (1 << 24)) return KVSEL_ERR_UNSUPPORTED;
+  if (hq / hkv > 32) return KVSEL_ERR_UNSUPPORTED;
+  if (!(T >= 0.f && T < 1.f)) return KVSEL_ERR_INVALID_ARG;
+  return KVSEL_OK;
+}
+
+static CutParams cut_params(const CutWs& ws, const int32_t* lengths, int b, int hq, int hkv,
+                            int cap, int n_sink, float T, int32_t* kept) {
+  CutParams c{};
+  c.rstat = ws.rstat;
+  c.lengths = lengths;
+  c.b = b;
+  c.hq = hq;
+  c.hkv = hkv;
+  c.g = hq / hkv;
+  c.mp = rows_padded(c.g);
+  c.cap = cap;
+  c.nchunk = (cap + kChunk - 1) / kChunk;
+  c.lstride = c.nchunk * kChunk;
+  c.n_sink = n_sink;
+  c.T = T;
+  c.energy = ws.energy;
+  c.ctot = ws.ctot;
+  c.kept = kept;
+  c.err = ws.err;
+  return c;
+}
+
+static kvsel_status threshold_cut_impl(kvsel_dtype dt, const void* q_last, const void* k,
+                                 const int32_t* lengths, int b, int hq, int hkv, int d, int cap,
+                                 int layer, int n_full_layers, int n_sink, float T,
+                                 int32_t* kept_len_out, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream, Trace* tr) {
+  if (dt != KVSEL_BF16 && dt != KVSEL_F32) return KVSEL_ERR_INVALID_ARG;
+  kvsel_status st = check_cut_common(lengths, b, hq, hkv, cap, n_sink, T, kept_len_out);
+  if (st != KVSEL_OK) return st;
+  if (layer < 0 || n_full_layers < 0) return KVSEL_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return KVSEL_ERR_UNSUPPORTED;
+  const int g = hq / hkv;
+  const CutWs need = cut_ws(nullptr, b, hkv, g, cap);
+  if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
+  const CutWs ws = cut_ws(workspace, b, hkv, g, cap);
+  CutParams c = cut_params(ws, lengths, b, hq, hkv, cap, n_sink, T, kept_len_out);
+  if (layer < n_full_layers) return hip_status(launch_cut_full(c, stream, tr));
+  if (!q_last || !k || !aligned16(q_last) || !aligned16(k)) return KVSEL_ERR_INVALID_ARG;
+
+  ScoreParams p{};
+  p.q = static_cast<const char*>(q_last);
+  p.k = static_cast<const char*>(k);
+  p.lengths = lengths;
+  p.b = b;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.g = g;
+  p.w = 1;
+  p.m = g;
+  p.mp = rows_padded(g);
+  p.cap = cap;
+  p.nchunk = c.nchunk;
+  p.scale = 1.0f / sqrtf((float)d);
+  p.cstat = ws.cstat;
+  p.rstat = ws.rstat;
+  p.logits = ws.logits;
+  p.err = ws.err;
+  KV_TRY(launch_stats(dt, d, kModeCut, p, stream, tr));
+  KV_TRY(launch_reduce(d, kModeCut, p, stream, tr));
+  c.logits = ws.logits;
+  c.attn = nullptr;
+  KV_TRY(launch_cut_energy(c, stream, tr));
+  KV_TRY(launch_cut_scan(c, stream, tr));
+  return KVSEL_OK;
+}
+
+kvsel_status kvsel_threshold_cut(kvsel_dtype dt, const void* q_last, const void* k,
+                                 const int32_t* lengths, int b, int hq, int hkv, int d, int cap,
+                                 int layer, int n_full_layers, int n_sink, float T,
+                                 int32_t* kept_len_out, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream) {
+  return threshold_cut_impl(dt, q_last, k, lengths, b, hq, hkv, d, cap, layer, n_full_layers,
+                            n_sink, T, kept_len_out, workspace, ws_bytes, stream, nullptr);
+}
+
+kvsel_status kvsel_threshold_cut_traced(kvsel_dtype dt, const void* q_last, const void* k,
+                                        const int32_t* lengths, int b, int hq, int hkv, int d,
+                                        int cap, int layer, int n_full_layers, int n_sink, float T,
+                                        int32_t* kept_len_out, void* workspace, size_t ws_bytes,
+                                        hipStream_t stream, hipEvent_t* events, int n_events) {
+  if (!events || n_events < 2) return KVSEL_ERR_INVALID_ARG;
+  Trace tr{events, n_events, 0};
+  return threshold_cut_impl(dt, q_last, k, lengths, b, hq, hkv, d, cap, layer, n_full_layers,
+                            n_sink, T, kept_len_out, workspace, ws_bytes, stream, &tr);
+}
+
+kvsel_status kvsel_threshold_cut_from_attn(const float* attn_last, const int32_t* lengths, int b,
+                                           int hq, int hkv, int cap, int n_sink, float T,
+                                           int32_t* kept_len_out, void* workspace,
+                                           size_t ws_bytes, hipStream_t stream) {
+  kvsel_status st = check_cut_common(lengths, b, hq, hkv, cap, n_sink, T, kept_len_out);
+  if (st != KVSEL_OK) return st;
+  if (!attn_last) return KVSEL_ERR_INVALID_ARG;
+  const int g = hq / hkv;
+  const CutWs need = cut_ws(nullptr, b, hkv, g, cap);
+  if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
+  const CutWs ws = cut_ws(workspace, b, hkv, g, cap);
+  CutParams c = cut_params(ws, lengths, b, hq, hkv, cap, n_sink, T, kept_len_out);
+  c.attn = attn_last;
+  c.logits = nullptr;
+  KV_TRY(launch_cut_energy(c, stream, nullptr));
+  KV_TRY(launch_cut_scan(c, stream, nullptr));
+  return KVSEL_OK;
+}
+
+kvsel_status kvsel_workspace_error(const void* workspace, int32_t* flags_host, hipStream_t stream) {
+  if (!workspace || !flags_host) return KVSEL_ERR_INVALID_ARG;
+  KV_TRY(hipMemcpyAsync(flags_host, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+  KV_TRY(hipStreamSynchronize(stream));
+  return KVSEL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,188 @@
+// Device helpers shared by the libkvsel kernels (gfx950, wave64).
+//
+// Matrix-core tiles.  All score kernels work on 32 x 32 output tiles of
+// v_mfma_f32_32x32x16_bf16 (bf16 inputs) or v_mfma_f32_32x32x2_f32 (fp32
+// inputs), accumulating in fp32.  A row of d elements is split into 16-byte
+// chunks; lane l of a wave feeds row (l % 32) of its operand and takes the
+// chunks 2j + (l / 32), j = 0 .. NC-1.  Any fixed lane->element assignment
+// gives the same dot products as long as both operands use it, so A and B
+// fragments are loaded by the same routine.  Output layout of a 32 x 32 tile
+// (C = A.B^T over the chunked dimension): lane l, register i holds
+//   column  l % 32  (the B-operand row)
+//   row     8*(i/4) + 4*(l/32) + (i%4)  (the A-operand row).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvsel {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// element-type tags
+struct BF16 {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerChunk = 8;
+};
+struct F32 {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerChunk = 4;
+};
+
+template <typename E, int D>
+struct Geo {
+  static constexpr int kRowBytes = D * E::kBytes;
+  static constexpr int kChunks = kRowBytes / 16;  // 16-byte chunks per row
+  static constexpr int kNC = kChunks / 2;         // chunks per lane
+  static constexpr int kLaneElems = kNC * E::kPerChunk;
+};
+
+template <int NC>
+struct Frag {
+  u32x4_t c[NC];
+};
+
+__device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// Row `row` of a row-major matrix whose rows are kRowBytes long; zero when !valid.
+template <typename E, int D>
+__device__ __forceinline__ void load_frag(Frag<Geo<E, D>::kNC>& f, const char* base, long row,
+                                          bool valid, int hf) {
+  const char* p = base + row * Geo<E, D>::kRowBytes + hf * 16;
+#pragma unroll
+  for (int j = 0; j < Geo<E, D>::kNC; ++j) f.c[j] = valid ? ld16(p + 32 * j) : zero4();
+}
+
+// acc += A_frag . B_frag^T over all chunks
+template <typename E, int NC>
+__device__ __forceinline__ f32x16_t mfma_tile(const Frag<NC>& a, const Frag<NC>& b, f32x16_t acc);
+
+template <>
+__device__ __forceinline__ f32x16_t mfma_tile<BF16, 8>(const Frag<8>& a, const Frag<8>& b,
+                                                       f32x16_t acc) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a.c[j]),
+                                                  __builtin_bit_cast(bf16x8_t, b.c[j]), acc, 0, 0, 0);
+  return acc;
+}
+template <>
+__device__ __forceinline__ f32x16_t mfma_tile<BF16, 4>(const Frag<4>& a, const Frag<4>& b,
+                                                       f32x16_t acc) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a.c[j]),
+                                                  __builtin_bit_cast(bf16x8_t, b.c[j]), acc, 0, 0, 0);
+  return acc;
+}
+template <int NC>
+__device__ __forceinline__ f32x16_t mfma_tile_f32(const Frag<NC>& a, const Frag<NC>& b,
+                                                  f32x16_t acc) {
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.c[j][e]),
+                                                 __uint_as_float(b.c[j][e]), acc, 0, 0, 0);
+  }
+  return acc;
+}
+template <>
+__device__ __forceinline__ f32x16_t mfma_tile<F32, 8>(const Frag<8>& a, const Frag<8>& b,
+                                                      f32x16_t acc) {
+  return mfma_tile_f32<8>(a, b, acc);
+}
+template <>
+__device__ __forceinline__ f32x16_t mfma_tile<F32, 16>(const Frag<16>& a, const Frag<16>& b,
+                                                       f32x16_t acc) {
+  return mfma_tile_f32<16>(a, b, acc);
+}
+
+// Element e (0 .. kPerChunk-1) of chunk j of a fragment, widened to fp32.
+template <typename E>
+__device__ __forceinline__ float frag_elem(u32x4_t c, int e);
+template <>
+__device__ __forceinline__ float frag_elem<BF16>(u32x4_t c, int e) {
+  uint32_t w = c[e >> 1];
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+template <>
+__device__ __forceinline__ float frag_elem<F32>(u32x4_t c, int e) {
+  return __uint_as_float(c[e]);
+}
+
+// Squared norm of this lane's share of its row (add the partner lane's).
+template <typename E, int NC>
+__device__ __forceinline__ float frag_sumsq(const Frag<NC>& f) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int e = 0; e < E::kPerChunk; ++e) {
+      float x = frag_elem<E>(f.c[j], e);
+      s = fmaf(x, x, s);
+    }
+  return s;
+}
+
+// Dimension index of element e of chunk j for lane half hf.
+template <typename E>
+__device__ __forceinline__ int frag_dim(int j, int e, int hf) {
+  return (2 * j + hf) * E::kPerChunk + e;
+}
+
+__device__ __forceinline__ float inv_norm_of(float sumsq) {
+  return sumsq > 0.f ? 1.0f / sqrtf(sumsq) : 0.f;
+}
+
+// Row of register i in the 32x32 output tile for lane half hf.
+__device__ __forceinline__ int tile_row(int i, int hf) { return 8 * (i >> 2) + 4 * hf + (i & 3); }
+
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 -> +0.
+__device__ __forceinline__ uint32_t score_key(float z) {
+  uint32_t u = __float_as_uint(z + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// merge two (max, sum-of-exp) softmax partials
+__device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, float s2) {
+  float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) {
+    m = mm;
+    s = 0.f;
+    return;
+  }
+  s = s * __expf(m - mm) + s2 * __expf(m2 - mm);
+  m = mm;
+}
+
+}  // namespace kvsel

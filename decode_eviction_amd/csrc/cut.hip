@@ -1,0 +1,171 @@
+// ReFreeKV threshold cut (review "论文综述：ReFreeKV：迈向无阈值的KV缓存压缩",
+// section 二: sinks first then newest to oldest; stop once the energy left out
+// falls below T; last attention row only; first two layers kept whole).
+//
+// The last-row logits and their per-row softmax statistics come from k_stats
+// / k_reduce (scores.hip, cut mode).  Here:
+//   k_cut_energy  per 256-token chunk: a = exp(s - max) / sum for each of the
+//                 g query rows of the group, E[j] = sum_q floor(fl32(a*a) * 2^52)
+//                 as a 64-bit integer, and the chunk's exact integer total;
+//   k_cut_scan    per KV head: tau = ceil(E_total * (1 - T)); if the sinks
+//                 alone reach tau the cut is m, otherwise a block-wide
+//                 inclusive scan walks the chunk totals from the newest chunk
+//                 back to the crossing chunk, then the tokens inside it, and
+//                 L = m + (number of newest tokens kept).
+// All sums are integer, so the result does not depend on summation order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace kvsel {
+
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* wsum, int tid) {
+  v = wave_sum_u64(v);
+  if ((tid & 63) == 0) wsum[tid >> 6] = v;
+  __syncthreads();
+  const uint64_t t = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, uint64_t* wsum, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  uint64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint64_t before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  __syncthreads();
+  return before + x;
+}
+
+__device__ __forceinline__ void write_err(const CutParams& p) {
+  int f = 0;
+  for (int i = 0; i < p.b; ++i) f |= p.lengths[i] > p.cap ? 1 : 0;
+  *p.err = f;
+}
+
+__global__ __launch_bounds__(256) void k_cut_energy(CutParams p) {
+  __shared__ uint64_t wsum[4];
+  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
+  if (p.attn && chunk == 0 && h == 0 && bi == 0 && tid == 0) write_err(p);
+  const int n = min(p.lengths[bi], p.cap);
+  const int c0 = chunk * kChunk;
+  if (c0 >= n) return;
+  const long head = (long)bi * p.hkv + h;
+  const int tok = c0 + tid;
+  uint64_t e = 0;
+  if (tok < n) {
+    for (int q = 0; q < p.g; ++q) {
+      float a;
+      if (p.attn) {
+        a = p.attn[((long)bi * p.hq + (long)h * p.g + q) * p.cap + tok];
+      } else {
+        const float2 st = p.rstat[head * p.mp + q];
+        a = __expf(p.logits[(head * p.g + q) * (long)p.lstride + tok] - st.x) * st.y;
+      }
+      const float sq = fminf(__fmul_rn(a, a), 1.0f);
+      e += (uint64_t)((double)sq * 4503599627370496.0);  // floor(sq * 2^52)
+    }
+  }
+  p.energy[head * (long)p.nchunk * kChunk + tok] = e;
+  const uint64_t tot = block_sum_u64(e, wsum, tid);
+  if (tid == 0) p.ctot[head * p.nchunk + chunk] = tot;
+}
+
+__global__ __launch_bounds__(256) void k_cut_scan(CutParams p) {
+  __shared__ uint64_t wsum[4];
+  __shared__ int found;
+  __shared__ uint64_t found_above;
+  const int h = blockIdx.x, bi = blockIdx.y, tid = threadIdx.x;
+  const long head = (long)bi * p.hkv + h;
+  const int n = min(p.lengths[bi], p.cap);
+  if (n == 0) {
+    if (tid == 0) p.kept[head] = 0;
+    return;
+  }
+  const uint64_t* E = p.energy + head * (long)p.nchunk * kChunk;
+  const uint64_t* ct = p.ctot + head * p.nchunk;
+  const int nch = (n + kChunk - 1) / kChunk;
+  const int m = min(p.n_sink, n);
+
+  uint64_t tot = 0, esk = 0;
+  for (int c = tid; c < nch; c += 256) tot += ct[c];
+  for (int j = tid; j < m; j += 256) esk += E[j];
+  tot = block_sum_u64(tot, wsum, tid);
+  esk = block_sum_u64(esk, wsum, tid);
+  const double taud = ceil((double)tot * (1.0 - (double)p.T));
+  const uint64_t tau = (uint64_t)taud;
+  if (m > 0 && esk >= tau) {
+    if (tid == 0) p.kept[head] = m;
+    return;
+  }
+
+  // chunk level: walk chunks newest first over positions >= m
+  const int cm = m / kChunk;  // first chunk holding a non-sink position
+  if (tid == 0) found = -1;
+  __syncthreads();
+  uint64_t acc = 0;
+  for (int r = 0; r * 256 < nch - cm; ++r) {
+    const int c = nch - 1 - (r * 256 + tid);
+    uint64_t v = 0;
+    if (c >= cm) {
+      if (c * kChunk >= m) {
+        v = ct[c];
+      } else {  // chunk straddles the sink boundary
+        const int hi = min(n, (c + 1) * kChunk);
+        for (int t = m; t < hi; ++t) v += E[t];
+      }
+    }
+    const uint64_t incl = acc + block_incl_scan_u64(v, wsum, tid);
+    if (c >= cm && esk + incl >= tau && esk + incl - v < tau) {
+      found = c;
+      found_above = incl - v;
+    }
+    acc = acc + block_sum_u64(v, wsum, tid);
+    __syncthreads();
+    if (found >= 0) break;
+  }
+  const int cstar = found;
+  if (cstar < 0) {
+    if (tid == 0) p.kept[head] = n;
+    return;
+  }
+  // token level inside the crossing chunk, newest first
+  const uint64_t above = found_above;
+  const int top = min(n, (cstar + 1) * kChunk) - 1;
+  const int low = max(m, cstar * kChunk);
+  const int pos = top - tid;
+  const uint64_t v = pos >= low ? E[pos] : 0;
+  __syncthreads();
+  if (tid == 0) found = -1;
+  __syncthreads();
+  const uint64_t incl = above + block_incl_scan_u64(v, wsum, tid);
+  if (pos >= low && esk + incl >= tau && esk + incl - v < tau) found = pos;
+  __syncthreads();
+  if (tid == 0) p.kept[head] = found >= 0 ? m + (n - found) : n;
+}
+
+__global__ void k_cut_full(CutParams p) {
+  const int h = blockIdx.x, bi = blockIdx.y;
+  if (h == 0 && bi == 0 && threadIdx.x == 0) write_err(p);
+  if (threadIdx.x == 0) p.kept[(long)bi * p.hkv + h] = min(p.lengths[bi], p.cap);
+}
+
+hipError_t launch_cut_energy(const CutParams& p, hipStream_t s, Trace* tr) {
+  return launch_k(k_cut_energy, dim3(p.nchunk, p.hkv, p.b), dim3(256), s, tr, p);
+}
+
+hipError_t launch_cut_scan(const CutParams& p, hipStream_t s, Trace* tr) {
+  return launch_k(k_cut_scan, dim3(p.hkv, p.b), dim3(256), s, tr, p);
+}
+
+hipError_t launch_cut_full(const CutParams& p, hipStream_t s, Trace* tr) {
+  return launch_k(k_cut_full, dim3(p.hkv, p.b), dim3(64), s, tr, p);
+}
+
+}  // namespace kvsel

@@ -1,0 +1,114 @@
+// Internal interface between the C-ABI host code (api.hip) and the kernel
+// translation units.  Every launcher enqueues on the given stream and returns
+// the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvsel {
+
+constexpr int kChunk = 256;        // tokens per work-group in the streaming passes
+constexpr int kMaxRows = 128;      // g*w (R-KV) or g (cut) rows, in 32-row tiles
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectLdsKeys = 32768;
+
+enum ScoreMode { kModeGram = 0, kModeKeysum = 1, kModeCut = 2 };
+
+struct ScoreParams {
+  const char* q;            // [b][Hq][w][d]  (cut: [b][Hq][d], w = 1)
+  const char* k;            // [b][Hkv][cap][d]
+  const int32_t* lengths;   // [b]
+  int b, hq, hkv, g, w, m;  // m = g*w query rows per KV head
+  int mp;                   // m rounded up to 32
+  int cap, nchunk;          // nchunk = ceil(cap / kChunk)
+  float scale;              // 1/sqrt(d)
+  float lambda;
+  // workspace
+  float2* cstat;            // [b][Hkv][nchunk][mp]  chunk (max, sum exp)
+  float2* rstat;            // [b][Hkv][mp]          (max, 1/sum)
+  float* spart;             // [b][Hkv][nchunk][d]   keysum: chunk sums of unit keys
+  float* ssum;              // [b][Hkv][d]           keysum: sum of unit keys
+  float* inv_norm;          // [b][Hkv][cap]         gram: 1/||k_j||
+  float* logits;            // [b][Hkv][g][nchunk*kChunk]  cut: scaled logits
+  int32_t* err;             // error word
+  // outputs (never null; the host substitutes workspace buffers)
+  float* i_out;             // [b][Hkv][cap]
+  float* r_out;             // [b][Hkv][cap] (may be null in keysum mode)
+  float* z_out;             // [b][Hkv][cap]
+};
+
+struct GramParams {
+  const char* k;
+  const int32_t* lengths;
+  int b, hkv, cap;
+  float lambda;
+  const float* inv_norm;    // [b][Hkv][cap]
+  const float* i_in;        // [b][Hkv][cap]
+  float* r_out;             // nullable
+  float* z_out;
+};
+
+struct SelectParams {
+  const float* z;           // [b][Hkv][cap]
+  const int32_t* lengths;
+  int b, hkv, cap, budget;
+  int32_t* idx;             // [b][Hkv][budget]
+};
+
+struct GatherParams {
+  const char* k;
+  const char* v;
+  const int32_t* idx;       // [b][Hkv][budget]
+  int b, hkv, cap, budget, cap_out;
+  char* k_out;
+  char* v_out;
+};
+
+struct CutParams {
+  const float* logits;      // [b][Hkv][g][lstride]   (or null with attn)
+  const float* attn;        // [b][Hq][cap]           stage entry (or null)
+  const float2* rstat;      // [b][Hkv][mp]
+  const int32_t* lengths;
+  int b, hq, hkv, g, mp, cap, nchunk, lstride, n_sink;
+  float T;
+  uint64_t* energy;         // [b][Hkv][nchunk*kChunk]
+  uint64_t* ctot;           // [b][Hkv][nchunk]
+  int32_t* kept;            // [b][Hkv]
+  int32_t* err;
+};
+
+// Optional per-kernel timing: the k-th kernel an entry point launches records
+// ev[2k] when it starts and ev[2k+1] when it ends (hipExtLaunchKernelGGL).
+struct Trace {
+  hipEvent_t* ev;
+  int n;
+  int k;
+};
+
+template <typename F, typename... Args>
+inline hipError_t launch_k(F kern, dim3 grid, dim3 block, hipStream_t s, Trace* tr, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (tr) {
+    if (2 * tr->k + 1 < tr->n) {
+      e0 = tr->ev[2 * tr->k];
+      e1 = tr->ev[2 * tr->k + 1];
+    }
+    tr->k++;
+  }
+  hipExtLaunchKernelGGL(kern, grid, block, 0, s, e0, e1, 0, args...);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats(int dt, int d, int mode, const ScoreParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_reduce(int d, int mode, const ScoreParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_pool(int dt, int d, int mode, const ScoreParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_gram(int dt, int d, const GramParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_select(const SelectParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_gather(int dt, int d, const GatherParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_cut_energy(const CutParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_cut_scan(const CutParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_cut_full(const CutParams& p, hipStream_t s, Trace* tr);
+
+}  // namespace kvsel

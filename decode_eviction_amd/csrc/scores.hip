@@ -1,0 +1,326 @@
+// Streaming score kernels: attention statistics, importance pooling and the
+// key-sum form of redundancy.
+//
+// R-KV importance (QbitAI R-KV article, section "R-KV三步走", importance
+// scoring from multi-head attention): for KV head h the g*w window rows of its
+// GQA group attend over the n cached keys; I[j] is the mean of their softmax
+// rows.  The softmax needs each row's global max and sum of exponentials, so
+// K is streamed twice:
+//   k_stats  per 256-token chunk: logits on the matrix cores, per-row chunk
+//            max / sum-exp, key norms (and, key-sum mode, the chunk's sum of
+//            unit keys); ReFreeKV mode also stores the scaled logits;
+//   k_reduce per head: merges chunk partials (online-softmax merge) and the
+//            unit-key sums;
+//   k_pool   per 256-token chunk: logits again, p = exp(s - max) / sum,
+//            I[j] = mean over rows; key-sum mode adds
+//            R[j] = (u_j.S - u_j.u_j) / (n-1),  S = sum_i u_i, u = k/||k||
+//            and Z[j] = lambda I[j] - (1-lambda) R[j].
+//
+// Tiles: each 256-thread work-group covers 256 tokens; each wave takes two
+// 32-token tiles.  k_stats forms C[token][row] so a lane owns one query row
+// and reduces over tokens in registers; k_pool forms C[row][token] so a lane
+// owns one token and reduces over rows in registers (plus one lane swap).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace kvsel {
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+template <typename E, int D, int MT, int MODE>
+__global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
+  using G = Geo<E, D>;
+  constexpr int NC = G::kNC;
+  constexpr int LE = G::kLaneElems;
+  constexpr int PC = E::kPerChunk;
+  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+
+  if (chunk == 0 && h == 0 && bi == 0 && tid == 0) {
+    int f = 0;
+    for (int i = 0; i < p.b; ++i) f |= p.lengths[i] > p.cap ? 1 : 0;
+    *p.err = f;
+  }
+  const int n = min(p.lengths[bi], p.cap);
+  const int c0 = chunk * kChunk;
+  if (c0 >= n) return;
+  const long head = (long)bi * p.hkv + h;
+  const char* kb = p.k + head * (long)p.cap * G::kRowBytes;
+  const char* qb = p.q + ((long)bi * p.hq + (long)h * p.g) * p.w * G::kRowBytes;
+
+  Frag<NC> qf[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int r = 32 * t + l32;
+    load_frag<E, D>(qf[t], qb, r, r < p.m, hf);
+  }
+  const int tok0 = c0 + wave * 64;
+  Frag<NC> kf[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tok = tok0 + 32 * tt + l32;
+    load_frag<E, D>(kf[tt], kb, tok, tok < n, hf);
+  }
+
+  // C[token][row]: lane owns query row 32t + l32 and tokens tile_row(i, hf)
+  f32x16_t acc[2][MT];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[tt][t] = mfma_tile<E, NC>(kf[tt], qf[t], zero16());
+
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool ok = tok0 + 32 * tt + tile_row(i, hf) < n;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[tt][t][i] = ok ? acc[tt][t][i] * p.scale : -INFINITY;
+    }
+
+  __shared__ float2 wst[4][MT * 32];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[tt][t][i]);
+    m = fmaxf(m, xor32(m));
+    float s = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += __expf(acc[tt][t][i] - m);
+    }
+    s += xor32(s);
+    if (hf == 0) wst[wave][32 * t + l32] = make_float2(m, s);
+  }
+
+  if constexpr (MODE == kModeCut) {
+    // scaled logits of rows < g, 4 consecutive tokens per store
+    if (l32 < p.g) {
+      const long ls = (long)p.nchunk * kChunk;
+      float* lrow = p.logits + (head * p.g + l32) * ls;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int tb = tok0 + 32 * tt + 8 * q4 + 4 * hf;
+          f32x4_t v;
+          v[0] = acc[tt][0][4 * q4 + 0];
+          v[1] = acc[tt][0][4 * q4 + 1];
+          v[2] = acc[tt][0][4 * q4 + 2];
+          v[3] = acc[tt][0][4 * q4 + 3];
+          *reinterpret_cast<f32x4_t*>(lrow + tb) = v;
+        }
+    }
+  } else {
+    float inv[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float ss = frag_sumsq<E, NC>(kf[tt]);
+      ss += xor32(ss);
+      inv[tt] = inv_norm_of(ss);
+      const int tok = tok0 + 32 * tt + l32;
+      if (MODE == kModeGram && hf == 0 && tok < n) p.inv_norm[head * p.cap + tok] = inv[tt];
+    }
+    if constexpr (MODE == kModeKeysum) {
+      constexpr int LP = LE + 4;  // padded lane stride (floats)
+      __shared__ float sred[4 * 64 * LP];
+      float* mine = sred + (wave * 64 + lane) * LP;
+#pragma unroll
+      for (int j = 0; j < NC; ++j)
+#pragma unroll
+        for (int e = 0; e < PC; ++e)
+          mine[j * PC + e] = inv[0] * frag_elem<E>(kf[0].c[j], e) + inv[1] * frag_elem<E>(kf[1].c[j], e);
+      __syncthreads();
+      if (tid < D) {
+        const int dim = tid, ch = dim / PC, hfd = ch & 1, slot = (ch >> 1) * PC + dim % PC;
+        float a = 0.f;
+        for (int wv = 0; wv < 4; ++wv)
+          for (int l = 0; l < 32; ++l) a += sred[(wv * 64 + hfd * 32 + l) * LP + slot];
+        p.spart[(head * p.nchunk + chunk) * D + dim] = a;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < MT * 32) {
+    float m = -INFINITY, s = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) softmax_merge(m, s, wst[wv][tid].x, wst[wv][tid].y);
+    p.cstat[(head * p.nchunk + chunk) * p.mp + tid] = make_float2(m, s);
+  }
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void k_reduce(ScoreParams p) {
+  const int h = blockIdx.x, bi = blockIdx.y, tid = threadIdx.x;
+  const int n = min(p.lengths[bi], p.cap);
+  const int nch = (n + kChunk - 1) / kChunk;
+  const long head = (long)bi * p.hkv + h;
+  if (tid < p.mp) {
+    float m = -INFINITY, s = 0.f;
+    for (int c = 0; c < nch; ++c) {
+      const float2 v = p.cstat[(head * p.nchunk + c) * p.mp + tid];
+      softmax_merge(m, s, v.x, v.y);
+    }
+    p.rstat[head * p.mp + tid] = make_float2(m, s > 0.f ? 1.0f / s : 0.f);
+  }
+  if (MODE == kModeKeysum && tid < D) {
+    float a = 0.f;
+    for (int c = 0; c < nch; ++c) a += p.spart[(head * p.nchunk + c) * D + tid];
+    p.ssum[head * D + tid] = a;
+  }
+}
+
+template <typename E, int D, int MT, int MODE>
+__global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
+  using G = Geo<E, D>;
+  constexpr int NC = G::kNC;
+  constexpr int LE = G::kLaneElems;
+  constexpr int PC = E::kPerChunk;
+  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int n = min(p.lengths[bi], p.cap);
+  const int c0 = chunk * kChunk;
+  if (c0 >= n) return;
+  const long head = (long)bi * p.hkv + h;
+  const char* kb = p.k + head * (long)p.cap * G::kRowBytes;
+  const char* qb = p.q + ((long)bi * p.hq + (long)h * p.g) * p.w * G::kRowBytes;
+
+  __shared__ float2 rs[MT * 32];
+  if (tid < MT * 32) {
+    float2 v = p.rstat[head * p.mp + tid];
+    rs[tid] = tid < p.m ? v : make_float2(0.f, 0.f);  // padding rows contribute 0
+  }
+  Frag<NC> qf[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int r = 32 * t + l32;
+    load_frag<E, D>(qf[t], qb, r, r < p.m, hf);
+  }
+  const int tok0 = c0 + wave * 64;
+  Frag<NC> kf[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tok = tok0 + 32 * tt + l32;
+    load_frag<E, D>(kf[tt], kb, tok, tok < n, hf);
+  }
+  float sv[MODE == kModeKeysum ? LE : 1];
+  if constexpr (MODE == kModeKeysum) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int e = 0; e < PC; ++e) sv[j * PC + e] = p.ssum[head * D + frag_dim<E>(j, e, hf)];
+  }
+  __syncthreads();
+
+  const float inv_m = 1.0f / (float)p.m;
+  const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    float isum = 0.f;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      // C[row][token]: lane owns token l32, rows 32t + tile_row(i, hf)
+      const f32x16_t a = mfma_tile<E, NC>(qf[t], kf[tt], zero16());
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float2 st = rs[32 * t + tile_row(i, hf)];
+        isum += __expf(a[i] * p.scale - st.x) * st.y;
+      }
+    }
+    isum += xor32(isum);
+    const float imp = isum * inv_m;
+    const int tok = tok0 + 32 * tt + l32;
+    const long o = head * p.cap + tok;
+    if constexpr (MODE == kModeGram) {
+      if (hf == 0 && tok < n) p.i_out[o] = imp;
+    } else {
+      float ss = frag_sumsq<E, NC>(kf[tt]);
+      ss += xor32(ss);
+      const float inv = inv_norm_of(ss);
+      float dot = 0.f;
+#pragma unroll
+      for (int j = 0; j < NC; ++j)
+#pragma unroll
+        for (int e = 0; e < PC; ++e) dot = fmaf(frag_elem<E>(kf[tt].c[j], e), sv[j * PC + e], dot);
+      dot += xor32(dot);
+      const float red = (inv * dot - inv * inv * ss) * inv_nm1;
+      const float z = p.lambda * imp - (1.0f - p.lambda) * red;
+      if (hf == 0 && tok < n) {
+        p.i_out[o] = imp;
+        if (p.r_out) p.r_out[o] = red;
+        p.z_out[o] = z;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <typename E, int D, int MT>
+static hipError_t stats_t(int mode, const ScoreParams& p, hipStream_t s, Trace* tr) {
+  const dim3 grid(p.nchunk, p.hkv, p.b);
+  switch (mode) {
+    case kModeGram: return launch_k(k_stats<E, D, MT, kModeGram>, grid, dim3(256), s, tr, p);
+    case kModeKeysum: return launch_k(k_stats<E, D, MT, kModeKeysum>, grid, dim3(256), s, tr, p);
+    default:
+      if constexpr (MT == 1) return launch_k(k_stats<E, D, 1, kModeCut>, grid, dim3(256), s, tr, p);
+      else return hipErrorInvalidValue;
+  }
+}
+
+template <typename E, int D>
+static hipError_t stats_d(int mode, const ScoreParams& p, hipStream_t s, Trace* tr) {
+  switch (p.mp / 32) {
+    case 1: return stats_t<E, D, 1>(mode, p, s, tr);
+    case 2: return stats_t<E, D, 2>(mode, p, s, tr);
+    case 4: return stats_t<E, D, 4>(mode, p, s, tr);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_stats(int dt, int d, int mode, const ScoreParams& p, hipStream_t s, Trace* tr) {
+  if (dt == 0) return d == 64 ? stats_d<BF16, 64>(mode, p, s, tr) : stats_d<BF16, 128>(mode, p, s, tr);
+  return d == 64 ? stats_d<F32, 64>(mode, p, s, tr) : stats_d<F32, 128>(mode, p, s, tr);
+}
+
+hipError_t launch_reduce(int d, int mode, const ScoreParams& p, hipStream_t s, Trace* tr) {
+  const dim3 grid(p.hkv, p.b);
+  if (mode == kModeKeysum)
+    return d == 64 ? launch_k(k_reduce<64, kModeKeysum>, grid, dim3(256), s, tr, p)
+                   : launch_k(k_reduce<128, kModeKeysum>, grid, dim3(256), s, tr, p);
+  return launch_k(k_reduce<128, kModeGram>, grid, dim3(256), s, tr, p);
+}
+
+template <typename E, int D, int MT>
+static hipError_t pool_t(int mode, const ScoreParams& p, hipStream_t s, Trace* tr) {
+  const dim3 grid(p.nchunk, p.hkv, p.b);
+  if (mode == kModeKeysum) return launch_k(k_pool<E, D, MT, kModeKeysum>, grid, dim3(256), s, tr, p);
+  return launch_k(k_pool<E, D, MT, kModeGram>, grid, dim3(256), s, tr, p);
+}
+
+template <typename E, int D>
+static hipError_t pool_d(int mode, const ScoreParams& p, hipStream_t s, Trace* tr) {
+  switch (p.mp / 32) {
+    case 1: return pool_t<E, D, 1>(mode, p, s, tr);
+    case 2: return pool_t<E, D, 2>(mode, p, s, tr);
+    case 4: return pool_t<E, D, 4>(mode, p, s, tr);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_pool(int dt, int d, int mode, const ScoreParams& p, hipStream_t s, Trace* tr) {
+  if (dt == 0) return d == 64 ? pool_d<BF16, 64>(mode, p, s, tr) : pool_d<BF16, 128>(mode, p, s, tr);
+  return d == 64 ? pool_d<F32, 64>(mode, p, s, tr) : pool_d<F32, 128>(mode, p, s, tr);
+}
+
+}  // namespace kvsel

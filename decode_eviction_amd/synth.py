@@ -233,17 +233,28 @@ def batched_case(seed: int = 0, b: int = 64, n: int = 8192, layer: int = 0) -> R
 
 @dataclass
 class DecodeStream:
-    """Per-layer token stream for the decode loop: keys/values of every decoded
-    token (uint16 bf16 bits, [hkv][total][d]) and one query row per q head per
-    token ([hq][total][d]); the window at any step is the last w tokens' queries."""
+    """Per-layer token stream for the decode loop: keys and values of every
+    decoded token (uint16 bf16 bits, [hkv][total][d]).  The query rows of token
+    t (one per q head) are drawn on demand from their own seed, so a window of
+    the last w tokens' queries can be formed at any step."""
     layer: int
+    seed: int
     hq: int
     hkv: int
     d: int
     total: int
     k: np.ndarray
     v: np.ndarray
-    q: np.ndarray
+
+    def queries(self, t: int) -> np.ndarray:
+        """bf16 bits [hq][d]: the query rows token t produced."""
+        rng = _rng(self.seed, WL_DECODE, 20_000 + self.layer, t)
+        return f32_to_bf16_bits(rng.standard_normal((self.hq, self.d), dtype=np.float32))
+
+    def window(self, t_end: int, w: int) -> np.ndarray:
+        """bf16 bits [1][hq][w][d]: queries of tokens t_end-w .. t_end-1."""
+        rows = np.stack([self.queries(t) for t in range(t_end - w, t_end)], axis=1)
+        return rows[None]
 
 
 def decode_stream(layer: int, seed: int = 0, total: int = 32768, hq: int = 32,
@@ -262,9 +273,7 @@ def decode_stream(layer: int, seed: int = 0, total: int = 32768, hq: int = 32,
 
     with ThreadPoolExecutor(_THREADS) as ex:
         list(ex.map(one, range(hkv)))
-    qrng = _rng(seed, WL_DECODE, 20_000 + layer)
-    q = f32_to_bf16_bits(qrng.standard_normal((hq, total, d), dtype=np.float32))
-    return DecodeStream(layer, hq, hkv, d, total, k, v, q)
+    return DecodeStream(layer, seed, hq, hkv, d, total, k, v)
 
 
 # ----------------------------------------------------------------------------

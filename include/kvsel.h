@@ -1,0 +1,176 @@
+/*
+ * kvsel.h — C ABI of libkvsel, the MI355X (gfx950) KV-cache score-and-evict
+ * library.  Every entry point launches hand-written HIP kernels on the
+ * caller's stream and returns without synchronising.
+ *
+ * Two selection rules:
+ *
+ *  R-KV (QbitAI R-KV article, section "R-KV三步走：冗余识别+重要性评估+动态淘汰"):
+ *   per KV head h of sequence b, with n = lengths[b] cached tokens,
+ *     importance  I[j] = mean over the g*w window rows (q, r) of the GQA group
+ *                        of softmax_j(Q[q,r] . K[j] / sqrt(d))
+ *     redundancy  R[j] = (1/(n-1)) * sum over i != j of cos(K[i], K[j])
+ *                        (a zero key has cosine 0; R = 0 when n == 1)
+ *     score       Z[j] = lambda * I[j] - (1 - lambda) * R[j]
+ *     selection   the min(budget, n) largest Z, equal Z -> lower position,
+ *                 written in ascending position order
+ *     compaction  K_out[t] = K[idx[t]], V_out[t] = V[idx[t]] (bit copies).
+ *   The article names the parts (attention-based importance, key-cosine
+ *   redundancy, joint eviction under a KV budget, lambda about 0.1); the exact
+ *   formulas above are the plain reading of it.
+ *
+ *  ReFreeKV (review "论文综述：ReFreeKV：迈向无阈值的KV缓存压缩", section 二, first
+ *   and second step and the efficiency paragraph): per KV head, tokens are
+ *   queued sinks first (positions 0..m-1) then newest to oldest; the energy of
+ *   token j is e[j] = sum over the group's g last-row queries of a[q,j]^2 with
+ *   a = softmax_j(q_last . K[j] / sqrt(d)); the kept length is
+ *     L = max(min(m, n), smallest p >= 1 whose first p queued tokens hold
+ *             >= (1 - T) of the total energy),
+ *   layers below n_full_layers keep L = n.  Energies enter the walk as
+ *   fixed-point integers (each fp32 square floored at 2^-52 resolution) so the
+ *   walk itself is exact and independent of summation order.
+ *
+ * Layouts (all row-major, element type per kvsel_dtype):
+ *   q_window [b][Hq][w][d], q_last [b][Hq][d],
+ *   k, v     [b][Hkv][cap][d]        (token j of head h of sequence b at row j)
+ *   lengths  [b] int32 on the device; values above cap are clamped to cap and
+ *            reported by kvsel_workspace_error().
+ *   GQA: query head q belongs to KV head q / (Hq / Hkv).
+ *
+ * Ownership: the caller allocates every buffer, device workspace included;
+ * the library allocates nothing and keeps no state between calls.  Inputs are
+ * never written.  A workspace may serve one call at a time; calls that share
+ * one must be ordered on one stream.
+ *
+ * Errors: argument checks run on the host before any launch and return
+ * KVSEL_ERR_INVALID_ARG / KVSEL_ERR_UNSUPPORTED / KVSEL_ERR_WORKSPACE with
+ * nothing launched; a failed launch returns KVSEL_ERR_HIP.  Pointers are
+ * device pointers unless stated otherwise.
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVSEL_OK = 0,
+  KVSEL_ERR_INVALID_ARG = 1,
+  KVSEL_ERR_UNSUPPORTED = 2,
+  KVSEL_ERR_WORKSPACE = 3,
+  KVSEL_ERR_HIP = 4
+} kvsel_status;
+
+typedef enum { KVSEL_BF16 = 0, KVSEL_F32 = 1 } kvsel_dtype;
+
+/* How R is evaluated.  Both give the same R up to fp32 rounding.
+ *  KVSEL_R_GRAM:   the n x n Gram matrix K.K^T on bf16 matrix cores (fp32
+ *                  accumulation), weighted by inverse norms and row-summed in
+ *                  registers; the n x n matrix never reaches memory.  O(n^2 d).
+ *  KVSEL_R_KEYSUM: the regrouped sum  sum_{i!=j} u_i.u_j = u_j.(sum_i u_i) - u_j.u_j
+ *                  over unit keys u, fused into the importance pass.  O(n d). */
+typedef enum { KVSEL_R_GRAM = 0, KVSEL_R_KEYSUM = 1 } kvsel_redundancy;
+
+/* Supported: d in {64, 128}; g*w <= 128 (R-KV); g <= 32 (ReFreeKV);
+ * 1 <= budget <= 65536; cap <= 2^24 - 1. */
+
+const char* kvsel_status_string(kvsel_status s);
+
+/* ---------------------------------------------------------------- R-KV */
+
+/* Bytes of device workspace kvsel_scores / kvsel_score_evict need. */
+size_t kvsel_score_evict_workspace(int b, int Hq, int Hkv, int d, int w, int cap, int budget);
+
+/* Scores only.  Writes Z (and I, R when non-null) as fp32 [b][Hkv][cap];
+ * entries at positions >= n are left untouched.  lambda in [0, 1]. */
+kvsel_status kvsel_scores(kvsel_dtype dt, kvsel_redundancy mode,
+                          const void* q_window, const void* k, const int32_t* lengths,
+                          int b, int Hq, int Hkv, int d, int w, int cap, float lambda,
+                          float* i_out, float* r_out, float* z_out,
+                          void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Top-budget choice from given scores z [b][Hkv][cap] (fp32).  idx_out
+ * [b][Hkv][budget] int32 receives the positions of the min(budget, n) largest
+ * scores (equal scores: lower position first) in ascending order, then -1.
+ * -0.0 is treated as +0.0; z must hold no NaN. */
+size_t kvsel_select_workspace(int b, int Hkv, int cap);
+kvsel_status kvsel_select_topb(const float* z, const int32_t* lengths, int b, int Hkv,
+                               int cap, int budget, int32_t* idx_out,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Gather-compaction: for t < budget with idx[t] >= 0, row t of k_out/v_out
+ * [b][Hkv][cap_out][d] becomes row idx[t] of k/v (bit copy); other rows are
+ * left untouched.  idx values must lie in [0, cap) or be -1. */
+kvsel_status kvsel_gather(kvsel_dtype dt, const void* k, const void* v, const int32_t* idx,
+                          int b, int Hkv, int d, int cap, int budget,
+                          void* k_out, void* v_out, int cap_out, hipStream_t stream);
+
+/* The whole step: scores, top-budget, gather.  budget <= cap_out.
+ * scores_out (nullable) receives Z as in kvsel_scores. */
+kvsel_status kvsel_score_evict(kvsel_dtype dt, kvsel_redundancy mode,
+                               const void* q_window, const void* k, const void* v,
+                               const int32_t* lengths, int b, int Hq, int Hkv, int d, int w,
+                               int cap, float lambda, int budget,
+                               void* k_out, void* v_out, int cap_out,
+                               int32_t* idx_out, float* scores_out,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Same step with per-kernel timing for profilers and benchmarks: kernel k of
+ * the call records events[2k] when it starts and events[2k+1] when it ends
+ * (k < n_events / 2; events are created by the caller with hipEventCreate).
+ * Launch order: KVSEL_R_GRAM: stats, reduce, pool, gram, select, gather;
+ * KVSEL_R_KEYSUM: stats, reduce, pool, select, gather. */
+kvsel_status kvsel_score_evict_traced(kvsel_dtype dt, kvsel_redundancy mode,
+                                      const void* q_window, const void* k, const void* v,
+                                      const int32_t* lengths, int b, int Hq, int Hkv, int d,
+                                      int w, int cap, float lambda, int budget,
+                                      void* k_out, void* v_out, int cap_out,
+                                      int32_t* idx_out, float* scores_out,
+                                      void* workspace, size_t ws_bytes, hipStream_t stream,
+                                      hipEvent_t* events, int n_events);
+
+/* ------------------------------------------------------------ ReFreeKV */
+
+size_t kvsel_threshold_cut_workspace(int b, int Hq, int Hkv, int d, int cap);
+
+/* Kept length per (sequence, KV head) into kept_len_out [b][Hkv] int32.
+ * layer < n_full_layers: L = n without reading K.  n_sink >= 0, T in [0, 1). */
+kvsel_status kvsel_threshold_cut(kvsel_dtype dt, const void* q_last, const void* k,
+                                 const int32_t* lengths, int b, int Hq, int Hkv, int d, int cap,
+                                 int layer, int n_full_layers, int n_sink, float T,
+                                 int32_t* kept_len_out,
+                                 void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* kvsel_threshold_cut with per-kernel timing as in kvsel_score_evict_traced.
+ * Launch order: stats, reduce, energy, scan (layer >= n_full_layers) or a
+ * single fill kernel (layer < n_full_layers). */
+kvsel_status kvsel_threshold_cut_traced(kvsel_dtype dt, const void* q_last, const void* k,
+                                        const int32_t* lengths, int b, int Hq, int Hkv, int d,
+                                        int cap, int layer, int n_full_layers, int n_sink, float T,
+                                        int32_t* kept_len_out, void* workspace, size_t ws_bytes,
+                                        hipStream_t stream, hipEvent_t* events, int n_events);
+
+/* Stage entry: the same cut from given fp32 last-row attention probabilities
+ * attn_last [b][Hq][cap] (values in [0, 1], used as given; squares are
+ * clamped to 1).  Same workspace size as kvsel_threshold_cut. */
+kvsel_status kvsel_threshold_cut_from_attn(const float* attn_last, const int32_t* lengths,
+                                           int b, int Hq, int Hkv, int cap, int n_sink, float T,
+                                           int32_t* kept_len_out,
+                                           void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ utility */
+
+/* Reads the device error word left in the workspace by the last call that
+ * used it (synchronises the stream).  Bit 0: some lengths[i] exceeded cap and
+ * was clamped.  Returns KVSEL_ERR_HIP if the copy fails. */
+kvsel_status kvsel_workspace_error(const void* workspace, int32_t* flags_host, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVSEL_H */

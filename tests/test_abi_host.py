@@ -1,0 +1,109 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kvsel.h declares, sizes workspaces, and rejects bad arguments on the
+host before launching anything."""
+
+import ctypes
+
+import pytest
+
+from decode_eviction_amd import kvsel as K
+
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return K.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = K.header_functions()
+    assert len(names) >= 10
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(names) == set(K._SIGS)
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert K.status_string(s)
+    assert K.status_string(99) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    ws = K.kvsel_score_evict_workspace(1, 32, 8, 128, 8, 32768, 2048)
+    # at least the fp32 importance and score buffers, 8 heads x 32768 tokens x 4 B each
+    assert ws >= 2 * 8 * 32768 * 4
+    assert K.kvsel_score_evict_workspace(0, 32, 8, 128, 8, 32768, 2048) == 0
+    assert K.kvsel_score_evict_workspace(1, 32, 8, 96, 8, 32768, 2048) == 0
+    cw = K.kvsel_threshold_cut_workspace(16, 28, 4, 128, 16384)
+    assert cw >= 16 * 4 * 16384 * (8 + 7 * 4)      # energies + logits
+    assert K.kvsel_threshold_cut_workspace(1, 28, 3, 128, 100) == 0
+
+
+def _fake(addr=0x10000):
+    return ctypes.c_void_p(addr)
+
+
+def _score_evict(lib, **over):
+    a = dict(dt=K.KVSEL_BF16, mode=K.KVSEL_R_GRAM, q=_fake(), k=_fake(), v=_fake(), lens=_fake(),
+             b=1, hq=32, hkv=8, d=128, w=8, cap=4096, lam=0.1, budget=1024, ko=_fake(), vo=_fake(),
+             cap_out=1024, idx=_fake(), z=NULL, ws=_fake(), wsb=1 << 30)
+    a.update(over)
+    return lib.kvsel_score_evict(a["dt"], a["mode"], a["q"], a["k"], a["v"], a["lens"], a["b"],
+                                 a["hq"], a["hkv"], a["d"], a["w"], a["cap"], a["lam"], a["budget"],
+                                 a["ko"], a["vo"], a["cap_out"], a["idx"], a["z"], a["ws"], a["wsb"],
+                                 NULL)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=NULL), K.KVSEL_ERR_INVALID_ARG),
+    (dict(k=NULL), K.KVSEL_ERR_INVALID_ARG),
+    (dict(v=NULL), K.KVSEL_ERR_INVALID_ARG),
+    (dict(idx=NULL), K.KVSEL_ERR_INVALID_ARG),
+    (dict(k=_fake(0x10008)), K.KVSEL_ERR_INVALID_ARG),          # misaligned
+    (dict(hq=30), K.KVSEL_ERR_INVALID_ARG),                      # Hq % Hkv != 0
+    (dict(d=96), K.KVSEL_ERR_UNSUPPORTED),
+    (dict(w=64), K.KVSEL_ERR_UNSUPPORTED),                       # g*w > 128
+    (dict(budget=0), K.KVSEL_ERR_INVALID_ARG),
+    (dict(budget=2000), K.KVSEL_ERR_INVALID_ARG),                # > cap_out
+    (dict(lam=1.5), K.KVSEL_ERR_INVALID_ARG),
+    (dict(lam=float("nan")), K.KVSEL_ERR_INVALID_ARG),
+    (dict(mode=7), K.KVSEL_ERR_INVALID_ARG),
+    (dict(dt=5), K.KVSEL_ERR_INVALID_ARG),
+    (dict(wsb=1024), K.KVSEL_ERR_WORKSPACE),
+    (dict(ws=NULL), K.KVSEL_ERR_WORKSPACE),
+    (dict(cap=1 << 24), K.KVSEL_ERR_UNSUPPORTED),
+])
+def test_score_evict_rejects(lib, over, code):
+    assert _score_evict(lib, **over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(T=1.0), K.KVSEL_ERR_INVALID_ARG),
+    (dict(T=-0.1), K.KVSEL_ERR_INVALID_ARG),
+    (dict(n_sink=-1), K.KVSEL_ERR_INVALID_ARG),
+    (dict(hq=28, hkv=3), K.KVSEL_ERR_INVALID_ARG),
+    (dict(hq=66, hkv=2), K.KVSEL_ERR_UNSUPPORTED),               # g > 32
+    (dict(d=80), K.KVSEL_ERR_UNSUPPORTED),
+    (dict(kept=NULL), K.KVSEL_ERR_INVALID_ARG),
+    (dict(wsb=16), K.KVSEL_ERR_WORKSPACE),
+])
+def test_threshold_cut_rejects(lib, over, code):
+    a = dict(dt=K.KVSEL_BF16, q=_fake(), k=_fake(), lens=_fake(), b=16, hq=28, hkv=4, d=128,
+             cap=16384, layer=5, nfull=2, n_sink=4, T=0.01, kept=_fake(), ws=_fake(), wsb=1 << 34)
+    a.update(over)
+    got = lib.kvsel_threshold_cut(a["dt"], a["q"], a["k"], a["lens"], a["b"], a["hq"], a["hkv"],
+                                  a["d"], a["cap"], a["layer"], a["nfull"], a["n_sink"], a["T"],
+                                  a["kept"], a["ws"], a["wsb"], NULL)
+    assert got == code
+
+
+def test_stage_entries_reject(lib):
+    assert lib.kvsel_select_topb(NULL, _fake(), 1, 1, 10, 5, _fake(), NULL, 0, NULL) == K.KVSEL_ERR_INVALID_ARG
+    assert lib.kvsel_select_topb(_fake(), _fake(), 1, 1, 10, 0, _fake(), NULL, 0, NULL) == K.KVSEL_ERR_INVALID_ARG
+    assert lib.kvsel_gather(K.KVSEL_BF16, _fake(), _fake(), _fake(), 1, 1, 128, 10, 5, _fake(), _fake(),
+                            4, NULL) == K.KVSEL_ERR_INVALID_ARG          # cap_out < budget
+    assert lib.kvsel_threshold_cut_from_attn(NULL, _fake(), 1, 4, 1, 10, 4, 0.01, _fake(), _fake(),
+                                             1 << 20, NULL) == K.KVSEL_ERR_INVALID_ARG
+    assert lib.kvsel_workspace_error(NULL, NULL, NULL) == K.KVSEL_ERR_INVALID_ARG
