@@ -53,13 +53,19 @@ __device__ __forceinline__ u32x4_t ld16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-// Row `row` of a row-major matrix whose rows are kRowBytes long; zero when !valid.
+// Row `row` of a row-major matrix whose rows are kRowBytes long; zero when
+// !valid.  The load itself is unconditional (row 0 stands in for an invalid
+// row) so that every load of a fragment is in flight before the first use.
 template <typename E, int D>
 __device__ __forceinline__ void load_frag(Frag<Geo<E, D>::kNC>& f, const char* base, long row,
                                           bool valid, int hf) {
-  const char* p = base + row * Geo<E, D>::kRowBytes + hf * 16;
+  const char* p = base + (valid ? row : 0) * Geo<E, D>::kRowBytes + hf * 16;
 #pragma unroll
-  for (int j = 0; j < Geo<E, D>::kNC; ++j) f.c[j] = valid ? ld16(p + 32 * j) : zero4();
+  for (int j = 0; j < Geo<E, D>::kNC; ++j) f.c[j] = ld16(p + 32 * j);
+  if (!valid) {
+#pragma unroll
+    for (int j = 0; j < Geo<E, D>::kNC; ++j) f.c[j] = zero4();
+  }
 }
 
 // acc += A_frag . B_frag^T over all chunks

@@ -11,32 +11,50 @@
 // registers: after each 256 x 128 tile each lane folds its 16 outputs into 16
 // running row sums weighted by its column's w_i.
 //
-// Work-group: 4 waves, 256 rows resident in registers (each wave 64 rows =
-// two 32-row tiles); the columns stream through LDS 128 keys at a time,
-// double-buffered, with the next block prefetched into registers while the
-// matrix cores work on the current one.  The epilogue combines R with the
+// Work-group: 8 waves (two per SIMD), 256 rows resident in registers (each
+// row group of 64 rows is held by two waves that split every column block).
+// Columns stream through LDS 128 keys at a time, double-buffered, with
+// direct global->LDS loads issued one block ahead; each wave keeps two
+// accumulator sets so the fp32 epilogue of one tile runs between the
+// matrix-core instructions of the next.  The last step combines R with the
 // importance from k_pool into Z = lambda I - (1-lambda) R.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace kvsel {
 
+// Map the linear work-group index to (head, row block) so that consecutive
+// indices on one XCD (work-groups are dealt to the 8 XCDs round-robin) take
+// row blocks of the same head: the CUs of an XCD then sweep the same keys
+// through their shared L2.
+__device__ __forceinline__ int xcd_major(int L, int total) {
+  constexpr int kXcd = 8;
+  if (total % kXcd != 0) return L;
+  return (L % kXcd) * (total / kXcd) + L / kXcd;
+}
+
 template <typename E, int D>
-__global__ __launch_bounds__(256) void k_gram(GramParams p) {
+__global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
   using G = Geo<E, D>;
   constexpr int NC = G::kNC;
   constexpr int RB = G::kRowBytes;
-  constexpr int CPR = G::kChunks;       // 16-byte chunks per key
-  constexpr int ROWS = 256;
-  constexpr int COLS = 128;
-  constexpr int LROW = RB + 16;         // padded LDS row
-  constexpr int PER = COLS * CPR / 256; // staged chunks per thread
-  __shared__ __attribute__((aligned(16))) char lds[2][COLS * LROW];
+  constexpr int CPR = G::kChunks;        // 16-byte chunks per key
+  constexpr int ROWS = 256;              // rows per work-group (4 row groups x 64)
+  constexpr int COLS = 128;              // columns per step (2 column groups x 64)
+  constexpr int STAGE = COLS * RB;       // one staged column block, unpadded
+  constexpr int PER = COLS * CPR / 512;  // 16-byte chunks each thread streams per step
+  constexpr int RED = 65;                // padded row stride of the final reduction
+  constexpr int LDSB = 2 * STAGE > ROWS * RED * 4 ? 2 * STAGE : ROWS * RED * 4;
+  __shared__ __attribute__((aligned(16))) char lds_raw[LDSB];
   __shared__ float wcol[2][COLS];
   __shared__ float rowss[ROWS];
 
-  const int rb = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int nrb = (p.cap + ROWS - 1) / ROWS;
+  const int W = xcd_major(blockIdx.x, nrb * p.hkv * p.b);
+  const int rb = W % nrb, hh = W / nrb;
+  const int h = hh % p.hkv, bi = hh / p.hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int rg = wave >> 1, cg = wave & 1;
   const int n = min(p.lengths[bi], p.cap);
   const int r0 = rb * ROWS;
   if (r0 >= n) return;
@@ -44,14 +62,21 @@ __global__ __launch_bounds__(256) void k_gram(GramParams p) {
   const char* kb = p.k + head * (long)p.cap * RB;
   const float* wv = p.inv_norm + head * p.cap;
 
+  // LDS layout of a staged block: key r, chunk c sits at 16-byte slot
+  // r*CPR + (c ^ (r % CPR)); the XOR swizzle makes the 32 keys of a fragment
+  // read hit distinct banks without padding.
+  auto slot = [](int r, int c) { return r * CPR + (c ^ (r & (CPR - 1))); };
+
   Frag<NC> af[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    const int row = r0 + wave * 64 + 32 * rt + l32;
+    const int row = r0 + rg * 64 + 32 * rt + l32;
     load_frag<E, D>(af[rt], kb, row, row < n, hf);
-    float ss = frag_sumsq<E, NC>(af[rt]);
-    ss += xor32(ss);
-    if (hf == 0) rowss[wave * 64 + 32 * rt + l32] = ss;
+    if (cg == 0) {
+      float ss = frag_sumsq<E, NC>(af[rt]);
+      ss += xor32(ss);
+      if (hf == 0) rowss[rg * 64 + 32 * rt + l32] = ss;
+    }
   }
 
   float rsum[2][16];
@@ -60,85 +85,109 @@ __global__ __launch_bounds__(256) void k_gram(GramParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) rsum[rt][i] = 0.f;
 
-  u32x4_t stage[PER];
+  // Column block -> LDS with direct global->LDS loads: lane l of a wave
+  // instruction fills slot (instruction base + l), so each lane fetches the
+  // chunk that belongs in its slot.  Columns past n are clamped to n-1; their
+  // weight is 0, so they add nothing.
   float wstage = 0.f;
-  auto gload = [&](int c0) {
+  auto stream = [&](int c0, int buf) {
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-      const int cid = it * 256 + tid, r = cid / CPR, ch = cid % CPR, col = c0 + r;
-      stage[it] = col < n ? ld16(kb + (long)col * RB + ch * 16) : zero4();
+      const int P = it * 512 + tid;
+      const int r = P / CPR, sl = P % CPR;
+      const int c = sl ^ (r & (CPR - 1));
+      const char* src = kb + (long)min(c0 + r, n - 1) * RB + c * 16;
+      char* dst = lds_raw + buf * STAGE + (it * 512 + wave * 64) * 16;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
-    if (tid < COLS) wstage = c0 + tid < n ? wv[c0 + tid] : 0.f;
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int cid = it * 256 + tid, r = cid / CPR, ch = cid % CPR;
-      *reinterpret_cast<u32x4_t*>(&lds[buf][r * LROW + ch * 16]) = stage[it];
-    }
-    if (tid < COLS) wcol[buf][tid] = wstage;
+    const int wc = c0 + (tid & (COLS - 1));
+    wstage = wv[min(wc, n - 1)];
+    wstage = wc < n ? wstage : 0.f;
   };
 
-  const int nsteps = (n + COLS - 1) / COLS;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nsteps) gload((st + 1) * COLS);
-    f32x16_t acc[2][4];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[rt][ct][i] = 0.f;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      Frag<NC> bfr;
-      const char* rp = &lds[buf][(32 * ct + l32) * LROW + hf * 16];
-#pragma unroll
-      for (int j = 0; j < NC; ++j) bfr.c[j] = *reinterpret_cast<const u32x4_t*>(rp + 32 * j);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) acc[rt][ct] = mfma_tile<E, NC>(af[rt], bfr, acc[rt][ct]);
-    }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const float w = wcol[buf][32 * ct + l32];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) rsum[rt][i] = fmaf(acc[rt][ct][i], w, rsum[rt][i]);
-    }
-    if (st + 1 < nsteps) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // row sums: lane (hf, l32) holds rows wave*64 + 32rt + tile_row(i, hf), column share l32
-  float* red = reinterpret_cast<float*>(&lds[0][0]);
+  // Two accumulator sets: the fp32 epilogue of one column tile is issued
+  // between the matrix-core instructions of the next tile.
+  f32x16_t acc_a[2], acc_b[2];
+  float w_b = 0.f;
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) red[(wave * 64 + 32 * rt + tile_row(i, hf)) * 33 + l32] = rsum[rt][i];
+    for (int i = 0; i < 16; ++i) acc_b[rt][i] = 0.f;
+  auto tile = [&](int buf, int ct, f32x16_t (&acc)[2]) {
+    const int col = cg * 64 + 32 * ct + l32;
+    Frag<NC> bfr;
+    const u32x4_t* base = reinterpret_cast<const u32x4_t*>(lds_raw + buf * STAGE);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) bfr.c[j] = base[slot(col, 2 * j + hf)];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rt][i] = 0.f;
+      acc[rt] = mfma_tile<E, NC>(af[rt], bfr, acc[rt]);
+    }
+    return wcol[buf][col];
+  };
+  auto fold = [&](const f32x16_t (&acc)[2], float w) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rsum[rt][i] = fmaf(acc[rt][i], w, rsum[rt][i]);
+  };
+
+  const int nsteps = (n + COLS - 1) / COLS;
+  stream(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  wcol[0][tid & (COLS - 1)] = wstage;  // the 4 threads of a slot store the same weight
   __syncthreads();
-  const int j = r0 + tid;
-  if (j < n) {
-    float s = 0.f;
-    for (int l = 0; l < 32; ++l) s += red[tid * 33 + l];
-    const float ss = rowss[tid];
-    const float inv = inv_norm_of(ss);
-    const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
-    const float red_j = (inv * s - inv * inv * ss) * inv_nm1;
-    const long o = head * p.cap + j;
-    if (p.r_out) p.r_out[o] = red_j;
-    p.z_out[o] = p.lambda * p.i_in[o] - (1.0f - p.lambda) * red_j;
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nsteps) stream((st + 1) * COLS, buf ^ 1);
+    const float w_a = tile(buf, 0, acc_a);
+    fold(acc_b, w_b);
+    w_b = tile(buf, 1, acc_b);
+    fold(acc_a, w_a);
+    if constexpr (NC == 8 && E::kBytes == 2) {
+      // 32 MFMAs, each followed by two of the 64 epilogue FMAs
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    wcol[buf ^ 1][tid & (COLS - 1)] = wstage;
+    __syncthreads();
+  }
+  fold(acc_b, w_b);
+
+  // row sums: lane (hf, l32) of wave (rg, cg) holds rows rg*64 + 32rt + tile_row(i, hf)
+  float* red = reinterpret_cast<float*>(lds_raw);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      red[(rg * 64 + 32 * rt + tile_row(i, hf)) * RED + cg * 32 + l32] = rsum[rt][i];
+  __syncthreads();
+  if (tid < ROWS) {
+    const int j = r0 + tid;
+    if (j < n) {
+      float s = 0.f;
+      for (int l = 0; l < 64; ++l) s += red[tid * RED + l];
+      const float ss = rowss[tid];
+      const float inv = inv_norm_of(ss);
+      const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
+      const float red_j = (inv * s - inv * inv * ss) * inv_nm1;
+      const long o = head * p.cap + j;
+      if (p.r_out) p.r_out[o] = red_j;
+      p.z_out[o] = p.lambda * p.i_in[o] - (1.0f - p.lambda) * red_j;
+    }
   }
 }
 
 template <typename E, int D>
 static hipError_t gram_t(const GramParams& p, hipStream_t s, Trace* tr) {
-  const dim3 grid((p.cap + 255) / 256, p.hkv, p.b);
-  return launch_k(k_gram<E, D>, grid, dim3(256), s, tr, p);
+  const int blocks = (p.cap + 255) / 256 * p.hkv * p.b;
+  return launch_k(k_gram<E, D>, dim3(blocks), dim3(512), s, tr, p);
 }
 
 hipError_t launch_gram(int dt, int d, const GramParams& p, hipStream_t s, Trace* tr) {

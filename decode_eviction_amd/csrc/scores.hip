@@ -159,24 +159,62 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
   }
 }
 
+// One work-group of 1024 threads per head.  Chunk partials are spread over
+// all threads with several independent loads in flight per thread, then
+// merged through LDS in a fixed order (deterministic).
 template <int D, int MODE>
-__global__ __launch_bounds__(256) void k_reduce(ScoreParams p) {
+__global__ __launch_bounds__(1024) void k_reduce(ScoreParams p) {
+  constexpr int U = 4;
+  __shared__ float2 part[1024];
+  __shared__ float spar[1024];
   const int h = blockIdx.x, bi = blockIdx.y, tid = threadIdx.x;
   const int n = min(p.lengths[bi], p.cap);
   const int nch = (n + kChunk - 1) / kChunk;
   const long head = (long)bi * p.hkv + h;
+  {
+    const int r = tid % p.mp, gi = tid / p.mp, G = 1024 / p.mp;
+    float m = -INFINITY, s = 0.f;
+    const float2* cs = p.cstat + head * p.nchunk * p.mp + r;
+    for (int c0 = gi; c0 < nch; c0 += G * U) {
+      float2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * G;
+        v[u] = c < nch ? cs[(long)c * p.mp] : make_float2(-INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) softmax_merge(m, s, v[u].x, v[u].y);
+    }
+    part[tid] = make_float2(m, s);
+  }
+  if constexpr (MODE == kModeKeysum) {
+    const int dim = tid % D, gi = tid / D, G = 1024 / D;
+    const float* sp = p.spart + head * p.nchunk * D + dim;
+    float a = 0.f;
+    for (int c0 = gi; c0 < nch; c0 += G * U) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * G;
+        v[u] = c < nch ? sp[(long)c * D] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) a += v[u];
+    }
+    spar[tid] = a;
+  }
+  __syncthreads();
   if (tid < p.mp) {
     float m = -INFINITY, s = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const float2 v = p.cstat[(head * p.nchunk + c) * p.mp + tid];
-      softmax_merge(m, s, v.x, v.y);
-    }
+    for (int g = 0; g < 1024 / p.mp; ++g) softmax_merge(m, s, part[g * p.mp + tid].x, part[g * p.mp + tid].y);
     p.rstat[head * p.mp + tid] = make_float2(m, s > 0.f ? 1.0f / s : 0.f);
   }
-  if (MODE == kModeKeysum && tid < D) {
-    float a = 0.f;
-    for (int c = 0; c < nch; ++c) a += p.spart[(head * p.nchunk + c) * D + tid];
-    p.ssum[head * D + tid] = a;
+  if constexpr (MODE == kModeKeysum) {
+    if (tid < D) {
+      float a = 0.f;
+      for (int g = 0; g < 1024 / D; ++g) a += spar[g * D + tid];
+      p.ssum[head * D + tid] = a;
+    }
   }
 }
 
@@ -296,9 +334,9 @@ hipError_t launch_stats(int dt, int d, int mode, const ScoreParams& p, hipStream
 hipError_t launch_reduce(int d, int mode, const ScoreParams& p, hipStream_t s, Trace* tr) {
   const dim3 grid(p.hkv, p.b);
   if (mode == kModeKeysum)
-    return d == 64 ? launch_k(k_reduce<64, kModeKeysum>, grid, dim3(256), s, tr, p)
-                   : launch_k(k_reduce<128, kModeKeysum>, grid, dim3(256), s, tr, p);
-  return launch_k(k_reduce<128, kModeGram>, grid, dim3(256), s, tr, p);
+    return d == 64 ? launch_k(k_reduce<64, kModeKeysum>, grid, dim3(1024), s, tr, p)
+                   : launch_k(k_reduce<128, kModeKeysum>, grid, dim3(1024), s, tr, p);
+  return launch_k(k_reduce<128, kModeGram>, grid, dim3(1024), s, tr, p);
 }
 
 template <typename E, int D, int MT>
