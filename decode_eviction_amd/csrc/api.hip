@@ -62,7 +62,7 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap) {
   w.rstat = c.take<float2>(heads * mp);
   w.spart = c.take<float>(heads * nchunk * d);
   w.ssum = c.take<float>(heads * d);
-  w.inv_norm = c.take<float>(heads * cap);
+  w.inv_norm = c.take<float>(heads * nchunk * kChunk);
   w.imp = c.take<float>(heads * cap);
   w.z = c.take<float>(heads * cap);
   w.bytes = (c.off + kAlign - 1) / kAlign * kAlign;
@@ -128,6 +128,7 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
     gp.cap = cap;
     gp.lambda = lambda;
     gp.inv_norm = ws.inv_norm;
+    gp.wstride = p.nchunk * kChunk;
     gp.i_in = p.i_out;
     gp.r_out = r_out;
     gp.z_out = z_out;

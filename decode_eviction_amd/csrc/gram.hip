@@ -13,8 +13,8 @@
 //
 // Work-group: 8 waves (two per SIMD), 256 rows resident in registers (each
 // row group of 64 rows is held by two waves that split every column block).
-// Columns stream through LDS 128 keys at a time, double-buffered, with
-// direct global->LDS loads issued one block ahead; each wave keeps two
+// Columns stream through LDS 128 keys at a time in a ring of three blocks,
+// with direct global->LDS loads issued two blocks ahead; each wave keeps two
 // accumulator sets so the fp32 epilogue of one tile runs between the
 // matrix-core instructions of the next.  The last step combines R with the
 // importance from k_pool into Z = lambda I - (1-lambda) R.
@@ -33,6 +33,10 @@ __device__ __forceinline__ int xcd_major(int L, int total) {
   return (L % kXcd) * (total / kXcd) + L / kXcd;
 }
 
+// s_waitcnt immediates (gfx9 encoding): wait until at most N vector memory
+// operations of this wave are outstanding; LDS/scalar counters untouched.
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 template <typename E, int D>
 __global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
   using G = Geo<E, D>;
@@ -41,12 +45,16 @@ __global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
   constexpr int CPR = G::kChunks;        // 16-byte chunks per key
   constexpr int ROWS = 256;              // rows per work-group (4 row groups x 64)
   constexpr int COLS = 128;              // columns per step (2 column groups x 64)
-  constexpr int STAGE = COLS * RB;       // one staged column block, unpadded
-  constexpr int PER = COLS * CPR / 512;  // 16-byte chunks each thread streams per step
+  constexpr int STAGE = COLS * RB;       // one staged key block, unpadded
+  constexpr int NBUF = 3 * STAGE <= 96 * 1024 ? 3 : 2;  // ring: current block + NBUF-1 ahead
+  constexpr int AHEAD = NBUF - 1;
+  constexpr int PER = COLS * CPR / 512;  // 16-byte key chunks each thread streams per step
+  constexpr int VM_STEP = PER + 1;       // vector memory operations per thread per step
   constexpr int RED = 65;                // padded row stride of the final reduction
-  constexpr int LDSB = 2 * STAGE > ROWS * RED * 4 ? 2 * STAGE : ROWS * RED * 4;
+  constexpr int KBYTES = NBUF * STAGE;
+  constexpr int LDSB = KBYTES > ROWS * RED * 4 ? KBYTES : ROWS * RED * 4;
   __shared__ __attribute__((aligned(16))) char lds_raw[LDSB];
-  __shared__ float wcol[2][COLS];
+  __shared__ __attribute__((aligned(16))) float wcol[NBUF][COLS];
   __shared__ float rowss[ROWS];
 
   const int nrb = (p.cap + ROWS - 1) / ROWS;
@@ -60,12 +68,7 @@ __global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
   if (r0 >= n) return;
   const long head = (long)bi * p.hkv + h;
   const char* kb = p.k + head * (long)p.cap * RB;
-  const float* wv = p.inv_norm + head * p.cap;
-
-  // LDS layout of a staged block: key r, chunk c sits at 16-byte slot
-  // r*CPR + (c ^ (r % CPR)); the XOR swizzle makes the 32 keys of a fragment
-  // read hit distinct banks without padding.
-  auto slot = [](int r, int c) { return r * CPR + (c ^ (r & (CPR - 1))); };
+  const float* wv = p.inv_norm + head * (long)p.wstride;
 
   Frag<NC> af[2];
 #pragma unroll
@@ -79,31 +82,46 @@ __global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
     }
   }
 
+  // LDS layout of a staged block: key r, chunk c at 16-byte slot
+  // r*CPR + (c ^ (r % CPR)); the XOR swizzle makes the 32 keys of a fragment
+  // read hit distinct banks without padding.  The direct global->LDS loads
+  // write lane l of a wave instruction to slot (instruction base + l), so each
+  // lane fetches the chunk that belongs in its slot.
+  int srow[PER], soff[PER];
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int P = it * 512 + tid, r = P / CPR, c = (P % CPR) ^ (r & (CPR - 1));
+    srow[it] = r;
+    soff[it] = c * 16;
+  }
+  // Columns past n are clamped to key n-1 (finite data); their weights are 0.
+  auto stream = [&](int c0, int buf) {
+    const bool full = c0 + COLS <= n;
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int row = full ? c0 + srow[it] : min(c0 + srow[it], n - 1);
+      const char* src = kb + (long)row * RB + soff[it];
+      char* dst = lds_raw + buf * STAGE + (it * 512 + wave * 64) * 16;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+    // weights: each wave streams one half of the block's 128 (the four copies agree)
+    const float* wsrc = wv + c0 + (wave & 1) * 64 + lane;
+    float* wdst = &wcol[buf][(wave & 1) * 64];
+    __builtin_amdgcn_global_load_lds(wsrc, (__attribute__((address_space(3))) void*)wdst, 4, 0, 0);
+  };
+
+  int rdoff[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) rdoff[j] = ((2 * j + hf) ^ (l32 & (CPR - 1))) * 16;
+  int colrb[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) colrb[ct] = (cg * 64 + 32 * ct + l32) * RB;
+
   float rsum[2][16];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) rsum[rt][i] = 0.f;
-
-  // Column block -> LDS with direct global->LDS loads: lane l of a wave
-  // instruction fills slot (instruction base + l), so each lane fetches the
-  // chunk that belongs in its slot.  Columns past n are clamped to n-1; their
-  // weight is 0, so they add nothing.
-  float wstage = 0.f;
-  auto stream = [&](int c0, int buf) {
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int P = it * 512 + tid;
-      const int r = P / CPR, sl = P % CPR;
-      const int c = sl ^ (r & (CPR - 1));
-      const char* src = kb + (long)min(c0 + r, n - 1) * RB + c * 16;
-      char* dst = lds_raw + buf * STAGE + (it * 512 + wave * 64) * 16;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-    }
-    const int wc = c0 + (tid & (COLS - 1));
-    wstage = wv[min(wc, n - 1)];
-    wstage = wc < n ? wstage : 0.f;
-  };
 
   // Two accumulator sets: the fp32 epilogue of one column tile is issued
   // between the matrix-core instructions of the next tile.
@@ -114,18 +132,17 @@ __global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc_b[rt][i] = 0.f;
   auto tile = [&](int buf, int ct, f32x16_t (&acc)[2]) {
-    const int col = cg * 64 + 32 * ct + l32;
     Frag<NC> bfr;
-    const u32x4_t* base = reinterpret_cast<const u32x4_t*>(lds_raw + buf * STAGE);
+    const char* base = lds_raw + buf * STAGE + colrb[ct];
 #pragma unroll
-    for (int j = 0; j < NC; ++j) bfr.c[j] = base[slot(col, 2 * j + hf)];
+    for (int j = 0; j < NC; ++j) bfr.c[j] = *reinterpret_cast<const u32x4_t*>(base + rdoff[j]);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[rt][i] = 0.f;
       acc[rt] = mfma_tile<E, NC>(af[rt], bfr, acc[rt]);
     }
-    return wcol[buf][col];
+    return wcol[buf][cg * 64 + 32 * ct + l32];
   };
   auto fold = [&](const f32x16_t (&acc)[2], float w) {
 #pragma unroll
@@ -134,14 +151,18 @@ __global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
       for (int i = 0; i < 16; ++i) rsum[rt][i] = fmaf(acc[rt][i], w, rsum[rt][i]);
   };
 
+  // The ring always issues one block per step so that the wait count is a
+  // constant: past the last block it re-streams the last block into the
+  // buffer no later step reads.
   const int nsteps = (n + COLS - 1) / COLS;
-  stream(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  wcol[0][tid & (COLS - 1)] = wstage;  // the 4 threads of a slot store the same weight
+  constexpr int VM_KEEP = (AHEAD - 1) * VM_STEP;  // loads allowed in flight at a step's end
+#pragma unroll
+  for (int a = 0; a < AHEAD; ++a) stream(min(a, nsteps - 1) * COLS, a);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_KEEP));
   __syncthreads();
   for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nsteps) stream((st + 1) * COLS, buf ^ 1);
+    const int buf = st % NBUF;
+    stream(min(st + AHEAD, nsteps - 1) * COLS, (st + AHEAD) % NBUF);
     const float w_a = tile(buf, 0, acc_a);
     fold(acc_b, w_b);
     w_b = tile(buf, 1, acc_b);
@@ -154,10 +175,11 @@ __global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    wcol[buf ^ 1][tid & (COLS - 1)] = wstage;
+    // block st+1 has landed once only the newer blocks may still be in flight
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_KEEP));
     __syncthreads();
   }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   fold(acc_b, w_b);
 
   // row sums: lane (hf, l32) of wave (rg, cg) holds rows rg*64 + 32rt + tile_row(i, hf)

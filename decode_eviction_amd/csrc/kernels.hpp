@@ -30,7 +30,7 @@ struct ScoreParams {
   float2* rstat;            // [b][Hkv][mp]          (max, 1/sum)
   float* spart;             // [b][Hkv][nchunk][d]   keysum: chunk sums of unit keys
   float* ssum;              // [b][Hkv][d]           keysum: sum of unit keys
-  float* inv_norm;          // [b][Hkv][cap]         gram: 1/||k_j||
+  float* inv_norm;          // [b][Hkv][nchunk*kChunk] gram: 1/||k_j||, 0 past n
   float* logits;            // [b][Hkv][g][nchunk*kChunk]  cut: scaled logits
   int32_t* err;             // error word
   // outputs (never null; the host substitutes workspace buffers)
@@ -44,7 +44,8 @@ struct GramParams {
   const int32_t* lengths;
   int b, hkv, cap;
   float lambda;
-  const float* inv_norm;    // [b][Hkv][cap]
+  const float* inv_norm;    // [b][Hkv][wstride], 0 past n
+  int wstride;              // per-head stride of inv_norm (multiple of 256)
   const float* i_in;        // [b][Hkv][cap]
   float* r_out;             // nullable
   float* z_out;

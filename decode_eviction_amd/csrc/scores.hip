@@ -129,7 +129,9 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
       ss += xor32(ss);
       inv[tt] = inv_norm_of(ss);
       const int tok = tok0 + 32 * tt + l32;
-      if (MODE == kModeGram && hf == 0 && tok < n) p.inv_norm[head * p.cap + tok] = inv[tt];
+      // every slot of the chunk is written (0 past n): the Gram kernel streams
+      // whole 128-key blocks of weights
+      if (MODE == kModeGram && hf == 0) p.inv_norm[head * (long)p.nchunk * kChunk + tok] = inv[tt];
     }
     if constexpr (MODE == kModeKeysum) {
       constexpr int LP = LE + 4;  // padded lane stride (floats)
