@@ -6,7 +6,8 @@ budget B = 2048, lambda = 0.1).  Steps rotate over --layers distinct seeded
 synthetic layer caches (32 x 128 MiB of K+V, beyond the 256 MB last-level
 cache) that are resident in HBM before timing starts.
 
-Per step the library launches stats, reduce, pool, [gram,] select, gather.
+Per step the library launches stats, reduce, pool, [gram,] thresh, compact
+(the compaction kernel also gathers the kept K/V rows).
 The timed region (`value`, `ms_per_step`) runs kvsel_score_evict; right
 after it the same steps run through kvsel_score_evict_traced, whose kernels
 record start/stop HIP events on the benchmark's stream, giving each kernel's
@@ -40,8 +41,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 
 KERNELS = {
-    "gram": ["stats", "reduce", "pool", "gram", "select", "gather"],
-    "keysum": ["stats", "reduce", "pool", "select", "gather"],
+    "gram": ["stats", "reduce", "pool", "gram", "thresh", "compact"],
+    "keysum": ["stats", "reduce", "pool", "thresh", "compact"],
 }
 
 
@@ -57,8 +58,8 @@ def algorithmic_cost(mode: str) -> dict:
         "stats": {"bytes": kb + (4 * tok if mode == "gram" else 0)},
         "reduce": {"bytes": 0},
         "pool": {"bytes": kb + (4 * tok if mode == "gram" else 8 * tok)},
-        "select": {"bytes": 4 * tok + 4 * HKV * BUDGET},
-        "gather": {"bytes": gath},
+        "thresh": {"bytes": 4 * tok},
+        "compact": {"bytes": 4 * tok + 4 * HKV * BUDGET + gath},
     }
     if mode == "gram":
         cost["gram"] = {"bytes": kb + 4 * tok * 3, "flops": 2.0 * N * N * D * HKV}
@@ -189,7 +190,7 @@ def run_mode(mode, layers, steps, warmup, hip):
 
 
 KERNEL_SOURCES = {"stats": "scores.hip", "reduce": "scores.hip", "pool": "scores.hip",
-                  "gram": "gram.hip", "select": "select.hip", "gather": "select.hip"}
+                  "gram": "gram.hip", "thresh": "select.hip", "compact": "select.hip"}
 
 
 def source_digest(kernel: str) -> str:

@@ -48,6 +48,13 @@ struct ScoreWs {
   float* inv_norm;
   float* imp;
   float* z;
+  struct {
+    uint32_t* hist;
+    uint32_t* thr;
+    uint32_t* coff;
+    uint32_t* ceqb;
+    int nsc;
+  } sel;
   size_t bytes;
 };
 
@@ -65,6 +72,11 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap) {
   w.inv_norm = c.take<float>(heads * nchunk * kChunk);
   w.imp = c.take<float>(heads * cap);
   w.z = c.take<float>(heads * cap);
+  w.sel.nsc = (cap + kSelChunk - 1) / kSelChunk;
+  w.sel.hist = c.take<uint32_t>(heads * kHistBins);
+  w.sel.thr = c.take<uint32_t>(heads * 2);
+  w.sel.coff = c.take<uint32_t>(heads * w.sel.nsc);
+  w.sel.ceqb = c.take<uint32_t>(heads * w.sel.nsc);
   w.bytes = (c.off + kAlign - 1) / kAlign * kAlign;
   return w;
 }
@@ -88,7 +100,7 @@ kvsel_status check_score_args(kvsel_dtype dt, kvsel_redundancy mode, const void*
 kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, const void* k,
                         const int32_t* lengths, int b, int hq, int hkv, int d, int w, int cap,
                         float lambda, float* i_out, float* r_out, float* z_out,
-                        const ScoreWs& ws, hipStream_t stream, Trace* tr) {
+                        uint32_t* hist, const ScoreWs& ws, hipStream_t stream, Trace* tr) {
   const int g = hq / hkv;
   ScoreParams p{};
   p.q = static_cast<const char*>(q);
@@ -115,6 +127,7 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
   p.i_out = i_out ? i_out : ws.imp;
   p.r_out = r_out;
   p.z_out = z_out;
+  p.hist = hist;
   const int sm = mode == KVSEL_R_GRAM ? kModeGram : kModeKeysum;
   KV_TRY(launch_stats(dt, d, sm, p, stream, tr));
   KV_TRY(launch_reduce(d, sm, p, stream, tr));
@@ -132,9 +145,49 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
     gp.i_in = p.i_out;
     gp.r_out = r_out;
     gp.z_out = z_out;
+    gp.hist = hist;
     KV_TRY(launch_gram(dt, d, gp, stream, tr));
   }
   return KVSEL_OK;
+}
+
+// ------------------------------------------------------------ select layout
+
+struct SelWs {
+  uint32_t* hist;
+  uint32_t* thr;
+  uint32_t* coff;
+  uint32_t* ceqb;
+  int nsc;
+};
+
+SelWs carve_select(Carver& c, int b, int hkv, int cap) {
+  const size_t heads = (size_t)b * hkv;
+  SelWs w;
+  w.nsc = (cap + kSelChunk - 1) / kSelChunk;
+  w.hist = c.take<uint32_t>(heads * kHistBins);
+  w.thr = c.take<uint32_t>(heads * 2);
+  w.coff = c.take<uint32_t>(heads * w.nsc);
+  w.ceqb = c.take<uint32_t>(heads * w.nsc);
+  return w;
+}
+
+SelectParams select_params(const SelWs& w, const float* z, const int32_t* lengths, int b, int hkv,
+                           int cap, int budget, int32_t* idx) {
+  SelectParams sp{};
+  sp.z = z;
+  sp.lengths = lengths;
+  sp.b = b;
+  sp.hkv = hkv;
+  sp.cap = cap;
+  sp.budget = budget;
+  sp.idx = idx;
+  sp.hist = w.hist;
+  sp.thr = w.thr;
+  sp.coff = w.coff;
+  sp.ceqb = w.ceqb;
+  sp.nsc = w.nsc;
+  return sp;
 }
 
 // ---------------------------------------------------------- ReFreeKV layout
@@ -197,25 +250,27 @@ kvsel_status kvsel_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q_w
   if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
   const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap);
   return run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, i_out, r_out,
-                    z_out, ws, stream, nullptr);
+                    z_out, nullptr, ws, stream, nullptr);
 }
 
 size_t kvsel_select_workspace(int b, int hkv, int cap) {
-  (void)b;
-  (void)hkv;
-  (void)cap;
-  return 0;
+  if (b < 1 || hkv < 1 || cap < 1) return 0;
+  Carver c{nullptr};
+  carve_select(c, b, hkv, cap);
+  return (c.off + kAlign - 1) / kAlign * kAlign;
 }
 
 kvsel_status kvsel_select_topb(const float* z, const int32_t* lengths, int b, int hkv, int cap,
                                int budget, int32_t* idx_out, void* workspace, size_t ws_bytes,
                                hipStream_t stream) {
-  (void)workspace;
-  (void)ws_bytes;
   if (!z || !lengths || !idx_out) return KVSEL_ERR_INVALID_ARG;
   if (b < 1 || hkv < 1 || cap < 1 || budget < 1) return KVSEL_ERR_INVALID_ARG;
   if (b > 65535 || hkv > 65535 || cap >= (1 << 24) || budget > 65536) return KVSEL_ERR_UNSUPPORTED;
-  SelectParams p{z, lengths, b, hkv, cap, budget, idx_out};
+  if (!workspace || ws_bytes < kvsel_select_workspace(b, hkv, cap)) return KVSEL_ERR_WORKSPACE;
+  Carver c{static_cast<char*>(workspace)};
+  const SelWs w = carve_select(c, b, hkv, cap);
+  SelectParams p = select_params(w, z, lengths, b, hkv, cap, budget, idx_out);
+  if (cap <= kSelectLdsKeys) KV_TRY(launch_hist(p, stream, nullptr));
   return hip_status(launch_select(p, stream, nullptr));
 }
 
@@ -250,10 +305,27 @@ static kvsel_status score_evict_impl(kvsel_dtype dt, kvsel_redundancy mode, cons
   if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
   const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap);
   float* z = scores_out ? scores_out : ws.z;
+  uint32_t* hist = cap <= kSelectLdsKeys ? ws.sel.hist : nullptr;
   st = run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, nullptr, nullptr,
-                  z, ws, stream, tr);
+                  z, hist, ws, stream, tr);
   if (st != KVSEL_OK) return st;
-  SelectParams sp{z, lengths, b, hkv, cap, budget, idx_out};
+  SelWs sw;
+  sw.hist = ws.sel.hist;
+  sw.thr = ws.sel.thr;
+  sw.coff = ws.sel.coff;
+  sw.ceqb = ws.sel.ceqb;
+  sw.nsc = ws.sel.nsc;
+  SelectParams sp = select_params(sw, z, lengths, b, hkv, cap, budget, idx_out);
+  if (cap <= kSelectLdsKeys) {  // the compaction kernel also gathers the kept rows
+    sp.k = static_cast<const char*>(k);
+    sp.v = static_cast<const char*>(v);
+    sp.k_out = static_cast<char*>(k_out);
+    sp.v_out = static_cast<char*>(v_out);
+    sp.cap_out = cap_out;
+    sp.row_bytes = d * (dt == KVSEL_BF16 ? 2 : 4);
+    KV_TRY(launch_select(sp, stream, tr));
+    return KVSEL_OK;
+  }
   KV_TRY(launch_select(sp, stream, tr));
   GatherParams gp{static_cast<const char*>(k), static_cast<const char*>(v), idx_out, b, hkv, cap,
                   budget, cap_out, static_cast<char*>(k_out), static_cast<char*>(v_out)};

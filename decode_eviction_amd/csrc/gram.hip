@@ -52,7 +52,8 @@ __global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
   constexpr int VM_STEP = PER + 1;       // vector memory operations per thread per step
   constexpr int RED = 65;                // padded row stride of the final reduction
   constexpr int KBYTES = NBUF * STAGE;
-  constexpr int LDSB = KBYTES > ROWS * RED * 4 ? KBYTES : ROWS * RED * 4;
+  constexpr int HOFF = ROWS * RED * 4;   // LDS histogram after the reduction buffer
+  constexpr int LDSB = KBYTES > HOFF + kHistBins * 4 ? KBYTES : HOFF + kHistBins * 4;
   __shared__ __attribute__((aligned(16))) char lds_raw[LDSB];
   __shared__ __attribute__((aligned(16))) float wcol[NBUF][COLS];
   __shared__ float rowss[ROWS];
@@ -184,11 +185,14 @@ __global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
 
   // row sums: lane (hf, l32) of wave (rg, cg) holds rows rg*64 + 32rt + tile_row(i, hf)
   float* red = reinterpret_cast<float*>(lds_raw);
+  uint32_t* lh = reinterpret_cast<uint32_t*>(lds_raw + HOFF);
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       red[(rg * 64 + 32 * rt + tile_row(i, hf)) * RED + cg * 32 + l32] = rsum[rt][i];
+  if (p.hist)
+    for (int t = tid; t < kHistBins; t += 512) lh[t] = 0u;
   __syncthreads();
   if (tid < ROWS) {
     const int j = r0 + tid;
@@ -201,8 +205,15 @@ __global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
       const float red_j = (inv * s - inv * inv * ss) * inv_nm1;
       const long o = head * p.cap + j;
       if (p.r_out) p.r_out[o] = red_j;
-      p.z_out[o] = p.lambda * p.i_in[o] - (1.0f - p.lambda) * red_j;
+      const float z = p.lambda * p.i_in[o] - (1.0f - p.lambda) * red_j;
+      p.z_out[o] = z;
+      if (p.hist) atomicAdd(&lh[hist_bin(score_key(z))], 1u);
     }
+  }
+  if (p.hist) {
+    __syncthreads();
+    for (int t = tid; t < kHistBins; t += 512)
+      if (lh[t]) atomicAdd(&p.hist[head * kHistBins + t], lh[t]);
   }
 }
 

@@ -13,6 +13,10 @@ constexpr int kChunk = 256;        // tokens per work-group in the streaming pas
 constexpr int kMaxRows = 128;      // g*w (R-KV) or g (cut) rows, in 32-row tiles
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectLdsKeys = 32768;
+// First-level histogram of score keys: the top kHistBits bits.
+constexpr int kHistBits = 11;
+constexpr int kHistBins = 1 << kHistBits;
+__device__ __forceinline__ uint32_t hist_bin(uint32_t key) { return key >> (32 - kHistBits); }
 
 enum ScoreMode { kModeGram = 0, kModeKeysum = 1, kModeCut = 2 };
 
@@ -37,6 +41,7 @@ struct ScoreParams {
   float* i_out;             // [b][Hkv][cap]
   float* r_out;             // [b][Hkv][cap] (may be null in keysum mode)
   float* z_out;             // [b][Hkv][cap]
+  uint32_t* hist;           // nullable [b][Hkv][kHistBins]: first-level key histogram of Z
 };
 
 struct GramParams {
@@ -49,13 +54,28 @@ struct GramParams {
   const float* i_in;        // [b][Hkv][cap]
   float* r_out;             // nullable
   float* z_out;
+  uint32_t* hist;           // nullable [b][Hkv][kHistBins]
 };
+
+constexpr int kSelChunk = 512;     // positions per compaction work-group
 
 struct SelectParams {
   const float* z;           // [b][Hkv][cap]
   const int32_t* lengths;
   int b, hkv, cap, budget;
   int32_t* idx;             // [b][Hkv][budget]
+  uint32_t* hist;           // [b][Hkv][kHistBins]: first-level key histogram of z
+  // split select (cap <= kSelectLdsKeys): threshold per head, offsets per chunk
+  uint32_t* thr;            // [b][Hkv][2]: threshold key, copies of it to keep
+  uint32_t* coff;           // [b][Hkv][nsc]: output slot of the chunk's first kept position
+  uint32_t* ceqb;           // [b][Hkv][nsc]: keys equal to the threshold before the chunk
+  int nsc;                  // ceil(cap / kSelChunk)
+  // fused gather (k == nullptr: indices only)
+  const char* k;
+  const char* v;
+  char* k_out;
+  char* v_out;
+  int cap_out, row_bytes;
 };
 
 struct GatherParams {
@@ -107,6 +127,7 @@ hipError_t launch_reduce(int d, int mode, const ScoreParams& p, hipStream_t s, T
 hipError_t launch_pool(int dt, int d, int mode, const ScoreParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_gram(int dt, int d, const GramParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_select(const SelectParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_hist(const SelectParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_gather(int dt, int d, const GatherParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_cut_energy(const CutParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_cut_scan(const CutParams& p, hipStream_t s, Trace* tr);

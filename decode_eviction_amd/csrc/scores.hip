@@ -48,8 +48,10 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
   }
   const int n = min(p.lengths[bi], p.cap);
   const int c0 = chunk * kChunk;
-  if (c0 >= n) return;
   const long head = (long)bi * p.hkv + h;
+  if (p.hist && chunk == 0)  // the later passes accumulate into it
+    for (int t = tid; t < kHistBins; t += 256) p.hist[head * kHistBins + t] = 0u;
+  if (c0 >= n) return;
   const char* kb = p.k + head * (long)p.cap * G::kRowBytes;
   const char* qb = p.q + ((long)bi * p.hq + (long)h * p.g) * p.w * G::kRowBytes;
 
@@ -236,6 +238,11 @@ __global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
   const char* qb = p.q + ((long)bi * p.hq + (long)h * p.g) * p.w * G::kRowBytes;
 
   __shared__ float2 rs[MT * 32];
+  __shared__ uint32_t lh[MODE == kModeKeysum ? kHistBins : 1];
+  if constexpr (MODE == kModeKeysum) {
+    if (p.hist)
+      for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
+  }
   if (tid < MT * 32) {
     float2 v = p.rstat[head * p.mp + tid];
     rs[tid] = tid < p.m ? v : make_float2(0.f, 0.f);  // padding rows contribute 0
@@ -299,7 +306,15 @@ __global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
         p.i_out[o] = imp;
         if (p.r_out) p.r_out[o] = red;
         p.z_out[o] = z;
+        if (p.hist) atomicAdd(&lh[hist_bin(score_key(z))], 1u);
       }
+    }
+  }
+  if constexpr (MODE == kModeKeysum) {
+    if (p.hist) {
+      __syncthreads();
+      for (int t = tid; t < kHistBins; t += 256)
+        if (lh[t]) atomicAdd(&p.hist[head * kHistBins + t], lh[t]);
     }
   }
 }

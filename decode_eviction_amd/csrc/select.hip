@@ -185,17 +185,112 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(SelectParams p) {
   }
 }
 
-// Register-resident variant for cap <= 32768: 512 threads, thread t holds the
-// keys of positions t + 512 i (i < 64).  Each wave counts into its own LDS histogram,
-// so atomics only contend inside a wave; compaction counts per (round, wave)
-// with ballots, scans the 512 packed counts once, then writes.
-constexpr int kRegThreads = 512;
+// Split select for cap <= 32768.
+//
+// The kernels that produce Z also count its keys into a first-level
+// histogram on the top kHistBits bits (hist).  k_select_thresh (one
+// 1024-thread work-group per head) finds the bin holding the B-th largest key
+// from that histogram, then refines inside the bin: thread t holds the keys of
+// positions t + 1024 i (i < 32) in registers.  The level-1 bin holds a small
+// share of the keys (its size is known from the histogram): those keys and
+// their positions are compacted into LDS with ballots, and the remaining radix
+// rounds touch only them.  A bin too large for LDS (many ties) is refined over
+// the register keys instead.  It then
+// counts, per 512-position chunk, the keys above the threshold and equal to
+// it, and writes each chunk's first output slot.  k_compact (one 256-thread
+// work-group per chunk and head) gives every kept position its ascending
+// output slot with one block scan of packed (greater, equal) counts and copies
+// the kept K and V rows (the gather is fused).
+constexpr int kRegThreads = 1024;
 constexpr int kRegWaves = kRegThreads / kWave;
-constexpr int kKeysPerThread = kSelectLdsKeys / kRegThreads;
+constexpr int kKeysPerThread = kSelectLdsKeys / kRegThreads;   // 32
+constexpr int kChunksPerRound = kRegThreads / kSelChunk;       // 2
 
-__global__ __launch_bounds__(kRegThreads) void k_select_reg(SelectParams p) {
-  __shared__ uint32_t sub[kRegWaves][kSelBins];
-  __shared__ uint32_t cnt[kKeysPerThread * kRegWaves];
+constexpr int kCandMax = 8192;   // candidates refined in LDS; larger bins use the register path
+
+// Per-chunk offsets from per-chunk (greater, equal) counts; run by wave 0,
+// lane c = chunk c (at most 64 chunks).
+__device__ __forceinline__ void write_chunk_offsets(const SelectParams& p, long head, int n,
+                                                    uint32_t gt, uint32_t eq, uint32_t kth,
+                                                    uint32_t need_eq, int lane) {
+  const int nch = (n + kSelChunk - 1) / kSelChunk;
+  if (lane >= nch) gt = eq = 0u;
+  uint32_t x = eq;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  const uint32_t eqb = x - eq;
+  const uint32_t rem = need_eq > eqb ? need_eq - eqb : 0u;
+  const uint32_t kept = gt + min(eq, rem);
+  uint32_t y2 = kept;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(y2, o, 64);
+    if (lane >= o) y2 += y;
+  }
+  if (lane < nch) {
+    p.coff[head * p.nsc + lane] = y2 - kept;
+    p.ceqb[head * p.nsc + lane] = eqb;
+  }
+  if (lane == 0) {
+    p.thr[head * 2 + 0] = kth;
+    p.thr[head * 2 + 1] = need_eq;
+  }
+}
+
+// Orders this wave's LDS accesses.  Lanes of one wave read counters that other
+// lanes of the same wave updated atomically; without a fence the compiler may
+// treat those reads as unaffected by other lanes and forward a lane's own
+// earlier store (for instance the zero it wrote) instead of loading.
+__device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup"); }
+
+// One refinement round of the adaptive radix select over keys supplied by
+// `visit(f)` (which calls f(key) for every candidate key of this thread).
+// hist: kSelBins counters (zeroed here); returns the new (lo, hi, need).
+template <int NW, typename Visit>
+__device__ __forceinline__ void refine_round(uint32_t& lo, uint32_t& hi, uint32_t& need,
+                                             uint32_t* hist, uint32_t* wsum, uint32_t* bc,
+                                             int tid, Visit visit) {
+  const uint32_t span = hi - lo;
+  const int bits = 32 - __clz(span);
+  const int shift = bits > 11 ? bits - 11 : 0;
+  const int nb = (int)(span >> shift) + 1;
+  __syncthreads();
+  for (int t = tid; t < kSelBins; t += NW * kWave) hist[t] = 0u;
+  __syncthreads();
+  visit([&](uint32_t key) {
+    const uint32_t off = key - lo;
+    if (off <= span) atomicAdd(&hist[off >> shift], 1u);
+  });
+  __syncthreads();
+  const uint32_t d0 = 2 * tid < nb ? hist[2 * tid] : 0u;
+  const uint32_t d1 = 2 * tid + 1 < nb ? hist[2 * tid + 1] : 0u;
+  const uint2 sc = block_scan_u32<NW>(d0 + d1, wsum, tid);
+  const uint32_t above = sc.y - sc.x - (d0 + d1);
+  if (above < need && above + d1 >= need) {
+    bc[0] = 2 * tid + 1;
+    bc[1] = above;
+  } else if (above + d1 < need && above + d1 + d0 >= need) {
+    bc[0] = 2 * tid;
+    bc[1] = above + d1;
+  }
+  __syncthreads();
+  const uint32_t bin = bc[0];
+  need -= bc[1];
+  const uint64_t nlo = (uint64_t)lo + ((uint64_t)bin << shift);
+  const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
+  lo = (uint32_t)nlo;
+  hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+}
+
+__global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
+  __shared__ uint32_t hist[kSelBins];
+  __shared__ uint32_t cand_key[kCandMax];
+  __shared__ int32_t cand_pos[kCandMax];
+  __shared__ uint32_t cnt[kKeysPerThread][kRegWaves];   // keys above the level-1 bin per (round, wave)
+  __shared__ uint32_t ccnt[64][2];                       // candidate (greater, equal) per chunk
   __shared__ uint32_t wsum[2][kRegWaves];
   __shared__ uint32_t bc[2];
 
@@ -204,125 +299,333 @@ __global__ __launch_bounds__(kRegThreads) void k_select_reg(SelectParams p) {
   const int n = min(p.lengths[bi], p.cap);
   const int B = p.budget;
   const long head = (long)bi * p.hkv + h;
-  int32_t* out = p.idx + head * B;
+  if (n <= B) return;  // k_compact keeps everything
   const float* z = p.z + head * p.cap;
-  if (n <= B) {
-    for (int t = tid; t < B; t += kRegThreads) out[t] = t < n ? t : -1;
+
+  // unconditional loads (index clamped into range): all in flight before use
+  uint32_t key[kKeysPerThread];
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread; ++i) key[i] = __float_as_uint(z[min(tid + i * kRegThreads, n - 1)]);
+
+  // level 1: the bin (of kHistBins) where the count from the top reaches B
+  const uint32_t c0 = p.hist[head * kHistBins + 2 * tid];
+  const uint32_t c1 = p.hist[head * kHistBins + 2 * tid + 1];
+  uint32_t need = (uint32_t)B;
+  if (tid < 64) ccnt[tid][0] = ccnt[tid][1] = 0u;
+  {
+    const uint2 sc = block_scan_u32<kRegWaves>(c0 + c1, wsum[0], tid);
+    const uint32_t above = sc.y - sc.x - (c0 + c1);
+    if (above < need && above + c1 >= need) {
+      bc[0] = 2 * tid + 1;
+      bc[1] = above;
+    } else if (above + c1 < need && above + c1 + c0 >= need) {
+      bc[0] = 2 * tid;
+      bc[1] = above + c1;
+    }
+    __syncthreads();
+  }
+  const uint32_t b1 = bc[0];
+  const uint32_t bin_count = p.hist[head * kHistBins + b1];
+  uint32_t lo = b1 << (32 - kHistBits);
+  uint32_t hi = lo | ((1u << (32 - kHistBits)) - 1u);
+  need -= bc[1];
+
+  // positions past n get key 0: below every bin a valid score can fall in
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread; ++i)
+    key[i] = tid + i * kRegThreads < n ? score_key(__uint_as_float(key[i])) : 0u;
+
+  if (bin_count <= (uint32_t)kCandMax) {
+    // pass 1: per wave, the bin's keys and the keys above the bin (ballots only)
+    uint32_t mine = 0, wcand = 0;
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread; ++i) {
+      const uint32_t kb = hist_bin(key[i]);
+      const uint64_t babove = __ballot(kb > b1);
+      const uint64_t bin = __ballot(kb == b1);
+      mine = lane == i ? (uint32_t)__popcll(babove) : mine;
+      wcand += (uint32_t)__popcll(bin);
+    }
+    if (lane < kKeysPerThread) cnt[lane][wave] = mine;
+    if (lane == 0) wsum[1][wave] = wcand;
+    __syncthreads();
+    uint32_t wbase = 0, nc = 0;
+#pragma unroll
+    for (int w = 0; w < kRegWaves; ++w) {
+      const uint32_t t = wsum[1][w];
+      wbase += w < wave ? t : 0u;
+      nc += t;
+    }
+    // pass 2: write the candidates (key, position) in wave order
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread; ++i) {
+      const bool in = hist_bin(key[i]) == b1;
+      const uint64_t bin = __ballot(in);
+      if (in) {
+        const uint32_t slot = wbase + lanemask_lt_count(bin, lane);
+        cand_key[slot] = key[i];
+        cand_pos[slot] = tid + i * kRegThreads;
+      }
+      wbase += (uint32_t)__popcll(bin);
+    }
+    __syncthreads();
+    // refinement inside the bin by wave 0 alone (no block barriers): a
+    // wave-private histogram, lanes own 32 consecutive bins each
+    if (wave == 0) {
+      while (lo < hi) {
+        const uint32_t span = hi - lo;
+        const int bits = 32 - __clz(span);
+        const int shift = bits > 11 ? bits - 11 : 0;
+#pragma unroll
+        for (int e = 0; e < kSelBins / kWave; ++e) hist[lane * (kSelBins / kWave) + e] = 0u;
+        wave_lds_sync();
+        for (uint32_t c = lane; c < nc; c += kWave) {
+          const uint32_t off = cand_key[c] - lo;
+          if (off <= span) atomicAdd(&hist[off >> shift], 1u);
+        }
+        wave_lds_sync();
+        uint32_t mysum = 0;
+#pragma unroll
+        for (int e = 0; e < kSelBins / kWave; ++e) mysum += hist[lane * (kSelBins / kWave) + e];
+        // inclusive suffix sum over lanes: keys in bins at or above my first bin
+        uint32_t suf = mysum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_down(suf, o, 64);
+          if (lane + o < 64) suf += y;
+        }
+        const uint32_t above_me = suf - mysum;  // keys in higher lanes' bins
+        const bool mine_has = above_me < need && suf >= need;
+        const uint64_t who = __ballot(mine_has);
+        const int src = __ffsll((unsigned long long)who) - 1;
+        uint32_t bin = 0, above = 0;
+        if (lane == src) {
+          uint32_t acc = above_me;
+          for (int e = kSelBins / kWave - 1; e >= 0; --e) {
+            const uint32_t cnt_e = hist[lane * (kSelBins / kWave) + e];
+            if (acc < need && acc + cnt_e >= need) {
+              bin = lane * (kSelBins / kWave) + e;
+              above = acc;
+              break;
+            }
+            acc += cnt_e;
+          }
+        }
+        bin = __shfl(bin, src, 64);
+        above = __shfl(above, src, 64);
+        wave_lds_sync();  // every lane is done reading before the next round clears the bins
+        need -= above;
+        const uint64_t nlo = (uint64_t)lo + ((uint64_t)bin << shift);
+        const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
+        lo = (uint32_t)nlo;
+        hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+      }
+      const uint32_t kth = lo;
+      for (uint32_t c = lane; c < nc; c += kWave) {
+        const uint32_t k = cand_key[c];
+        const int ch = cand_pos[c] / kSelChunk;
+        if (k > kth) atomicAdd(&ccnt[ch][0], 1u);
+        else if (k == kth) atomicAdd(&ccnt[ch][1], 1u);
+      }
+      wave_lds_sync();
+      uint32_t gt = 0, eq = 0;
+      // chunk c = round c / 2, waves of half c % 2
+      const int i = lane / kChunksPerRound, w0 = (lane % kChunksPerRound) * (kRegWaves / kChunksPerRound);
+      if (i < kKeysPerThread) {
+#pragma unroll
+        for (int w = 0; w < kRegWaves / kChunksPerRound; ++w) gt += cnt[i][w0 + w];
+      }
+      gt += ccnt[lane][0];
+      eq = ccnt[lane][1];
+      write_chunk_offsets(p, head, n, gt, eq, kth, need, lane);
+    }
     return;
   }
 
-  // unconditional loads (index clamped into range) so all of them are in
-  // flight before the first use
-  float zr[kKeysPerThread];
+  // large bin (many ties or a narrow spread): refine over the register keys
+  while (lo < hi)
+    refine_round<kRegWaves>(lo, hi, need, hist, wsum[0], bc, tid, [&](auto f) {
 #pragma unroll
-  for (int i = 0; i < kKeysPerThread; ++i) zr[i] = z[min(tid + i * kRegThreads, n - 1)];
-  uint32_t key[kKeysPerThread];
-#pragma unroll
-  for (int i = 0; i < kKeysPerThread; ++i) key[i] = tid + i * kRegThreads < n ? score_key(zr[i]) : 0u;
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-  for (int i = 0; i < kKeysPerThread; ++i) {
-    if (tid + i * kRegThreads < n) {
-      kmin = min(kmin, key[i]);
-      kmax = max(kmax, key[i]);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
-  if (lane == 0) {
-    wsum[0][wave] = kmin;
-    wsum[1][wave] = kmax;
-  }
-  __syncthreads();
-  uint32_t lo = 0xffffffffu, hi = 0u;
-#pragma unroll
-  for (int w = 0; w < kRegWaves; ++w) {
-    lo = min(lo, wsum[0][w]);
-    hi = max(hi, wsum[1][w]);
-  }
-  __syncthreads();
-
-  uint32_t need = (uint32_t)B;
-  while (lo < hi) {
-    const uint32_t span = hi - lo;
-    const int bits = 32 - __clz(span);
-    const int shift = bits > 11 ? bits - 11 : 0;
-    const int nb = (int)(span >> shift) + 1;
-    for (int t = lane; t < nb; t += kWave) sub[wave][t] = 0u;
-#pragma unroll
-    for (int i = 0; i < kKeysPerThread; ++i) {
-      const uint32_t u = key[i];
-      if (tid + i * kRegThreads < n && u >= lo && u <= hi) atomicAdd(&sub[wave][(u - lo) >> shift], 1u);
-    }
-    __syncthreads();
-    uint32_t c0 = 0, c1 = 0;
-    // thread t owns bins 4t .. 4t+3
-    uint32_t c[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (4 * tid + e < nb) {
-#pragma unroll
-        for (int w = 0; w < kRegWaves; ++w) c[e] += sub[w][4 * tid + e];
-      }
-    }
-    const uint32_t tsum = c[0] + c[1] + c[2] + c[3];
-    const uint2 sc = block_scan_u32<kRegWaves>(tsum, wsum[0], tid);
-    uint32_t above = sc.y - sc.x - tsum;  // keys in bins above 4t+3
-#pragma unroll
-    for (int e = 3; e >= 0; --e) {
-      if (above < need && above + c[e] >= need) {
-        bc[0] = 4 * tid + e;
-        bc[1] = above;
-      }
-      above += c[e];
-    }
-    __syncthreads();
-    const uint32_t bin = bc[0];
-    need -= bc[1];
-    const uint64_t nlo = (uint64_t)lo + ((uint64_t)bin << shift);
-    const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
-    lo = (uint32_t)nlo;
-    hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
-  }
+      for (int i = 0; i < kKeysPerThread; ++i) f(key[i]);
+    });
   const uint32_t kth = lo;
-  const uint32_t need_eq = need;
-
-  // counts of (greater, equal) per (round i, wave) packed as gt | eq << 16
+  uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < kKeysPerThread; ++i) {
-    const bool ok = tid + i * kRegThreads < n;
-    const uint64_t bgt = __ballot(ok && key[i] > kth);
-    const uint64_t beq = __ballot(ok && key[i] == kth);
-    if (lane == 0) cnt[i * kRegWaves + wave] = (uint32_t)__popcll(bgt) | ((uint32_t)__popcll(beq) << 16);
+    const uint64_t bgt = __ballot(key[i] > kth);
+    const uint64_t beq = __ballot(key[i] == kth);
+    const uint32_t v = (uint32_t)__popcll(bgt) | ((uint32_t)__popcll(beq) << 16);
+    mine = lane == i ? v : mine;
   }
+  if (lane < kKeysPerThread) cnt[lane][wave] = mine;
   __syncthreads();
-  const uint32_t mine = cnt[tid];
-  const uint2 sc = block_scan_u32<kRegWaves>(mine, wsum[0], tid);
-  cnt[tid] = sc.x;
-  __syncthreads();
+  if (wave == 0) {
+    uint32_t gt = 0, eq = 0;
+    const int i = lane / kChunksPerRound, w0 = (lane % kChunksPerRound) * (kRegWaves / kChunksPerRound);
+    if (i < kKeysPerThread) {
 #pragma unroll
-  for (int i = 0; i < kKeysPerThread; ++i) {
-    const int j = tid + i * kRegThreads;
-    const bool ok = j < n;
-    const bool gt = ok && key[i] > kth;
-    const bool eq = ok && key[i] == kth;
-    const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
-    const uint32_t pre = cnt[i * kRegWaves + wave];
-    const uint32_t gt_before = (pre & 0xffffu) + lanemask_lt_count(bgt, lane);
-    const uint32_t eq_before = (pre >> 16) + lanemask_lt_count(beq, lane);
-    if (gt || (eq && eq_before < need_eq)) {
-      const uint32_t pos = gt_before + min(eq_before, need_eq);
-      if (pos < (uint32_t)B) out[pos] = j;
+      for (int w = 0; w < kRegWaves / kChunksPerRound; ++w) {
+        const uint32_t v = cnt[i][w0 + w];
+        gt += v & 0xffffu;
+        eq += v >> 16;
+      }
+    }
+    write_chunk_offsets(p, head, n, gt, eq, kth, need, lane);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_compact(SelectParams p) {
+  constexpr int PPT = kSelChunk / 256;  // positions per thread
+  __shared__ uint32_t wsum[4];
+  __shared__ int32_t rows[kSelChunk];   // kept positions by slot - chunk offset
+  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
+  const int n = min(p.lengths[bi], p.cap);
+  const int B = p.budget;
+  const long head = (long)bi * p.hkv + h;
+  int32_t* out = p.idx + head * B;
+  const int c0 = chunk * kSelChunk;
+  if (chunk == 0)
+    for (int t = min(n, B) + tid; t < B; t += 256) out[t] = -1;
+  if (c0 >= n) return;
+  const bool all = n <= B;
+  uint32_t kth = 0, need_eq = 0, off = 0, eqb = 0;
+  if (!all) {
+    kth = p.thr[head * 2 + 0];
+    need_eq = p.thr[head * 2 + 1];
+    off = p.coff[head * p.nsc + chunk];
+    eqb = p.ceqb[head * p.nsc + chunk];
+  } else {
+    off = c0;
+  }
+  const float* z = p.z + head * p.cap;
+  const int p0 = c0 + tid * PPT;
+  bool gt[PPT], eq[PPT];
+  uint32_t cg = 0, ce = 0;
+  if (!all) {
+    float zv[PPT];
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) zv[e] = z[min(p0 + e, n - 1)];
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) {
+      const bool ok = p0 + e < n;
+      const uint32_t kk = score_key(zv[e]);
+      gt[e] = ok && kk > kth;
+      eq[e] = ok && kk == kth;
+      cg += gt[e];
+      ce += eq[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) {
+      gt[e] = p0 + e < n;
+      eq[e] = false;
+      cg += gt[e];
+    }
+  }
+  // exclusive scan of packed counts over the 256 threads (each field < 2^16)
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint32_t v = cg | (ce << 16);
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    before += w < wave ? wsum[w] : 0u;
+    total += wsum[w];
+  }
+  const uint32_t pre = before + x - v;
+  const uint32_t rem = need_eq > eqb ? need_eq - eqb : 0u;
+  uint32_t gtb = pre & 0xffffu, eqbf = pre >> 16;
+#pragma unroll
+  for (int e = 0; e < PPT; ++e) {
+    int r = -1;
+    if (gt[e]) {
+      r = (int)(gtb + min(eqbf, rem));
+      ++gtb;
+    } else if (eq[e]) {
+      if (eqbf < rem) r = (int)(gtb + eqbf);
+      ++eqbf;
+    }
+    if (r >= 0 && off + r < (uint32_t)B) {
+      out[off + r] = p0 + e;
+      rows[r] = p0 + e;
+    }
+  }
+  if (!p.k) return;
+  const int kept = (int)((total & 0xffffu) + min(total >> 16, rem));
+  const int nk = min(kept, B - (int)off);
+  __syncthreads();
+  // fused gather: row_bytes/16 lanes per row, all loads of a thread issued first
+  const int lpr = p.row_bytes / 16, rpi = 256 / lpr;
+  const int lr = tid / lpr, lc = tid % lpr;
+  constexpr int U = 4;
+  for (int r0 = lr; r0 < nk; r0 += rpi * U) {
+    u32x4_t kv[U], vv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = min(r0 + u * rpi, nk - 1);
+      const long src = (head * p.cap + rows[r]) * (long)p.row_bytes + lc * 16;
+      kv[u] = ld16(p.k + src);
+      vv[u] = ld16(p.v + src);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u * rpi;
+      if (r < nk) {
+        const long dst = (head * p.cap_out + (long)(off + r)) * p.row_bytes + lc * 16;
+        *reinterpret_cast<u32x4_t*>(p.k_out + dst) = kv[u];
+        *reinterpret_cast<u32x4_t*>(p.v_out + dst) = vv[u];
+      }
     }
   }
 }
 
+// Stage entry (scores given by the caller): zero, then fill the first-level
+// histogram, one 256-thread work-group per 2048 positions.
+__global__ __launch_bounds__(256) void k_hist_zero(SelectParams p) {
+  const long head = (long)blockIdx.y * p.hkv + blockIdx.x;
+  for (int t = threadIdx.x; t < kHistBins; t += 256) p.hist[head * kHistBins + t] = 0u;
+}
+
+__global__ __launch_bounds__(256) void k_hist(SelectParams p) {
+  __shared__ uint32_t lh[kHistBins];
+  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
+  const int n = min(p.lengths[bi], p.cap);
+  const int c0 = chunk * 2048;
+  if (c0 >= n) return;
+  const long head = (long)bi * p.hkv + h;
+  const float* z = p.z + head * p.cap;
+  for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
+  __syncthreads();
+  float zv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zv[e] = z[min(c0 + e * 256 + tid, n - 1)];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (c0 + e * 256 + tid < n) atomicAdd(&lh[hist_bin(score_key(zv[e]))], 1u);
+  __syncthreads();
+  for (int t = tid; t < kHistBins; t += 256)
+    if (lh[t]) atomicAdd(&p.hist[head * kHistBins + t], lh[t]);
+}
+
+hipError_t launch_hist(const SelectParams& p, hipStream_t s, Trace* tr) {
+  hipError_t e = launch_k(k_hist_zero, dim3(p.hkv, p.b), dim3(256), s, tr, p);
+  if (e != hipSuccess) return e;
+  return launch_k(k_hist, dim3((p.cap + 2047) / 2048, p.hkv, p.b), dim3(256), s, tr, p);
+}
+
 hipError_t launch_select(const SelectParams& p, hipStream_t s, Trace* tr) {
-  if (p.cap <= kSelectLdsKeys)
-    return launch_k(k_select_reg, dim3(p.hkv, p.b), dim3(kRegThreads), s, tr, p);
+  if (p.cap <= kSelectLdsKeys) {
+    hipError_t e = launch_k(k_select_thresh, dim3(p.hkv, p.b), dim3(kRegThreads), s, tr, p);
+    if (e != hipSuccess) return e;
+    return launch_k(k_compact, dim3(p.nsc, p.hkv, p.b), dim3(256), s, tr, p);
+  }
   return launch_k(k_select, dim3(p.hkv, p.b), dim3(kSelectThreads), s, tr, p);
 }
 

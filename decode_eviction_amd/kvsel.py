@@ -139,13 +139,18 @@ def kvsel_scores(q_window, k, lengths, lam=0.1, mode="gram", i_out=None, r_out=N
     return i_out, r_out, z_out
 
 
-def kvsel_select_topb(z, lengths, budget, idx_out=None, stream=None):
+def kvsel_select_workspace(b, hkv, cap) -> int:
+    return int(lib().kvsel_select_workspace(b, hkv, cap))
+
+
+def kvsel_select_topb(z, lengths, budget, idx_out=None, workspace=None, stream=None):
     _need_cuda(z, lengths, idx_out)
     b, hkv, cap = z.shape
     if idx_out is None:
         idx_out = torch.empty((b, hkv, budget), dtype=torch.int32, device=z.device)
+    ws = _workspace(kvsel_select_workspace(b, hkv, cap), z.device, workspace)
     st = lib().kvsel_select_topb(_ptr(z), _ptr(lengths), b, hkv, cap, int(budget), _ptr(idx_out),
-                                 None, 0, _stream(stream))
+                                 _ptr(ws), ws.numel(), _stream(stream))
     _check("kvsel_select_topb", st)
     return idx_out
 

@@ -97,7 +97,8 @@ kvsel_status kvsel_scores(kvsel_dtype dt, kvsel_redundancy mode,
 /* Top-budget choice from given scores z [b][Hkv][cap] (fp32).  idx_out
  * [b][Hkv][budget] int32 receives the positions of the min(budget, n) largest
  * scores (equal scores: lower position first) in ascending order, then -1.
- * -0.0 is treated as +0.0; z must hold no NaN. */
+ * -0.0 is treated as +0.0; z must hold no NaN.  Needs a device workspace of
+ * kvsel_select_workspace() bytes. */
 size_t kvsel_select_workspace(int b, int Hkv, int cap);
 kvsel_status kvsel_select_topb(const float* z, const int32_t* lengths, int b, int Hkv,
                                int cap, int budget, int32_t* idx_out,
@@ -123,8 +124,10 @@ kvsel_status kvsel_score_evict(kvsel_dtype dt, kvsel_redundancy mode,
 /* Same step with per-kernel timing for profilers and benchmarks: kernel k of
  * the call records events[2k] when it starts and events[2k+1] when it ends
  * (k < n_events / 2; events are created by the caller with hipEventCreate).
- * Launch order: KVSEL_R_GRAM: stats, reduce, pool, gram, select, gather;
- * KVSEL_R_KEYSUM: stats, reduce, pool, select, gather. */
+ * Launch order for cap <= 32768: KVSEL_R_GRAM: stats, reduce, pool, gram,
+ * threshold, compact (the compaction kernel also gathers the kept rows);
+ * KVSEL_R_KEYSUM: stats, reduce, pool, threshold, compact.  For larger cap
+ * the last two are replaced by select, gather. */
 kvsel_status kvsel_score_evict_traced(kvsel_dtype dt, kvsel_redundancy mode,
                                       const void* q_window, const void* k, const void* v,
                                       const int32_t* lengths, int b, int Hq, int Hkv, int d,
