@@ -14,11 +14,19 @@ record start/stop HIP events on the benchmark's stream, giving each kernel's
 average duration (the roofline figure uses the dominant kernel's).  Both redundancy forms are
 measured; --mode picks which one is the headline `value`.
 
+Variants (each with its own value, per-kernel times and roofline):
+  decode_<mode>   the decode loop: 32 layers x 240 calls compressing a
+                  2176-slot cache to 2048 rows (per-call latency);
+  batched_<mode>  64 sequences x 8192 tokens, B = 1024 (2 GiB of K and V);
+  refreekv        the ReFreeKV threshold cut at the Qwen2.5-7B shape
+                  (28 q / 4 KV heads), 16 ragged sequences of 1K-16K tokens.
+
 The CPU baseline times the fp64 oracle (definition form, n x n cosine
 matrix) on a bounded sample: whole KV heads of one layer until --cpu-seconds
 have passed, scaled to a full layer.
 
     python bench.py [--gpus 1] [--steps 64] [--warmup 8] [--mode gram|keysum]
+                    [--no-variants | --variant decode|batched|refreekv ...]
 """
 
 from __future__ import annotations
@@ -46,29 +54,45 @@ KERNELS = {
 }
 
 
-def algorithmic_cost(mode: str) -> dict:
-    """Bytes (and flops) each kernel must move per call at the headline shape.
+def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int = HKV,
+             d: int = D) -> dict:
+    """Bytes (and flops) each R-KV kernel must move per call.
 
-    K bytes = Hkv*n*d*2; scores are fp32 per token per head; the gather moves
-    B kept rows of K and V in and out."""
-    kb = HKV * N * D * 2
-    tok = HKV * N
-    gath = 2 * 2 * HKV * BUDGET * D * 2
+    K bytes = b*Hkv*n*d*2; scores are fp32 per token per head; the gather moves
+    min(B, n) kept rows of K and V in and out."""
+    tok = b * hkv * n
+    kb = tok * d * 2
+    gath = 2 * 2 * b * hkv * min(budget, n) * d * 2
     cost = {
         "stats": {"bytes": kb + (4 * tok if mode == "gram" else 0)},
         "reduce": {"bytes": 0},
         "pool": {"bytes": kb + (4 * tok if mode == "gram" else 8 * tok)},
         "thresh": {"bytes": 4 * tok},
-        "compact": {"bytes": 4 * tok + 4 * HKV * BUDGET + gath},
+        "compact": {"bytes": 4 * tok + 4 * b * hkv * budget + gath},
     }
     if mode == "gram":
-        cost["gram"] = {"bytes": kb + 4 * tok * 3, "flops": 2.0 * N * N * D * HKV}
+        cost["gram"] = {"bytes": kb + 4 * tok * 3, "flops": 2.0 * b * hkv * n * n * d}
     return cost
 
 
-def step_bytes(mode: str) -> int:
-    """Algorithmic floor of one call: K once, scores, the gather."""
-    return HKV * N * D * 2 + 3 * 4 * HKV * N + 2 * 2 * HKV * BUDGET * D * 2
+def rkv_step_bytes(b: int = 1, n: int = N, budget: int = BUDGET, hkv: int = HKV, d: int = D) -> int:
+    """Algorithmic floor of one R-KV call: K once, scores, the gather."""
+    tok = b * hkv * n
+    return tok * d * 2 + 3 * 4 * tok + 2 * 2 * b * hkv * min(budget, n) * d * 2
+
+
+def cut_cost(lengths, hq: int, hkv: int, d: int = D) -> dict:
+    """Bytes each ReFreeKV kernel moves per scored layer: stats reads K and
+    writes the g last-row logits of every token (fp32), cut_energy reads them
+    back and writes one 64-bit energy per token, cut_scan reads chunk totals."""
+    tok = int(np.sum(lengths)) * hkv
+    g = hq // hkv
+    return {
+        "stats": {"bytes": tok * d * 2 + tok * g * 4},
+        "reduce": {"bytes": 0},
+        "cut_energy": {"bytes": tok * g * 4 + tok * 8},
+        "cut_scan": {"bytes": 0},
+    }
 
 
 class Hip:
@@ -116,65 +140,37 @@ def make_layers(n_layers: int):
     return layers, first
 
 
-def run_mode(mode, layers, steps, warmup, hip):
+def time_calls(call, names, cost, steps, warmup, hip, traced_steps=None):
+    """Warm up, time `steps` plain calls (`call(i, None)`), then time the same
+    calls with per-kernel HIP events (`call(i, events)`) on the same stream."""
     import torch
-
-    from decode_eviction_amd import kvsel as K
-    lib = K.lib()
-    mcode = K.MODES[mode]
-    names = KERNELS[mode]
     nk = len(names)
-    lens = torch.tensor([N], dtype=torch.int32, device="cuda")
-    k_out = torch.empty((1, HKV, BUDGET, D), dtype=torch.bfloat16, device="cuda")
-    v_out = torch.empty_like(k_out)
-    idx = torch.empty((1, HKV, BUDGET), dtype=torch.int32, device="cuda")
-    ws_bytes = K.kvsel_score_evict_workspace(1, HQ, HKV, D, W, N, BUDGET)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    P = ctypes.c_void_p
-
-    def call(i, events=None):
-        q, k, v = layers[i % len(layers)]
-        args = (K.KVSEL_BF16, mcode, P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
-                P(lens.data_ptr()), 1, HQ, HKV, D, W, N, LAM, BUDGET, P(k_out.data_ptr()),
-                P(v_out.data_ptr()), BUDGET, P(idx.data_ptr()), None, P(ws.data_ptr()), ws_bytes, sp)
-        if events is None:
-            st = lib.kvsel_score_evict(*args)
-        else:
-            st = lib.kvsel_score_evict_traced(*args, events, 2 * nk)
-        if st != 0:
-            raise RuntimeError(f"kvsel_score_evict: {K.status_string(st)}")
-
     for i in range(warmup):
-        call(i)
+        call(i, None)
     torch.cuda.synchronize()
-
-    # timed region: the plain library call
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(steps):
-        call(i)
+        call(i, None)
     t1.record()
     torch.cuda.synchronize()
     ms_plain = t0.elapsed_time(t1) / steps
 
-    # the same steps again with per-kernel events on the same stream
-    evs = [hip.events(2 * nk) for _ in range(steps)]
+    ts = traced_steps or steps
+    evs = [hip.events(2 * nk) for _ in range(ts)]
     torch.cuda.synchronize()
     t0.record()
-    for i in range(steps):
+    for i in range(ts):
         call(i, evs[i])
     t1.record()
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    ms = t0.elapsed_time(t1) / ts
     per = {nm: [] for nm in names}
     for e in evs:
         for j, nm in enumerate(names):
             per[nm].append(hip.elapsed_ms(e[2 * j], e[2 * j + 1]))
         hip.destroy(e)
     kern = {}
-    cost = algorithmic_cost(mode)
     for nm in names:
         us = 1000.0 * float(np.mean(per[nm]))
         entry = {"avg_us": round(us, 3), "min_us": round(1000.0 * float(np.min(per[nm])), 3)}
@@ -189,8 +185,155 @@ def run_mode(mode, layers, steps, warmup, hip):
     return dict(ms=ms, ms_plain=ms_plain, kernels=kern)
 
 
+def rkv_caller(mode, layers, b, n, budget, out_bufs=None):
+    """call(i, events) running kvsel_score_evict[_traced] on layer i % len(layers).
+    layers: list of (q, k, v) device tensors.  With out_bufs the outputs go to
+    out_bufs[i % len], else to one shared output."""
+    import torch
+
+    from decode_eviction_amd import kvsel as K
+    lib = K.lib()
+    mcode = K.MODES[mode]
+    nk = len(KERNELS[mode])
+    q0, k0, _ = layers[0]
+    hq, w = q0.shape[1], q0.shape[2]
+    hkv, cap = k0.shape[1], k0.shape[2]
+    lens = torch.full((b,), n, dtype=torch.int32, device="cuda")
+    if out_bufs is None:
+        ko = torch.empty((b, hkv, budget, D), dtype=torch.bfloat16, device="cuda")
+        out_bufs = [(ko, torch.empty_like(ko))]
+    idx = torch.empty((b, hkv, budget), dtype=torch.int32, device="cuda")
+    ws_bytes = K.kvsel_score_evict_workspace(b, hq, hkv, D, w, cap, budget)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
+
+    def call(i, events=None):
+        q, k, v = layers[i % len(layers)]
+        ko, vo = out_bufs[i % len(out_bufs)]
+        args = (K.KVSEL_BF16, mcode, P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
+                P(lens.data_ptr()), b, hq, hkv, D, w, cap, LAM, budget, P(ko.data_ptr()),
+                P(vo.data_ptr()), ko.shape[2], P(idx.data_ptr()), None, P(ws.data_ptr()),
+                ws_bytes, sp)
+        if events is None:
+            st = lib.kvsel_score_evict(*args)
+        else:
+            st = lib.kvsel_score_evict_traced(*args, events, 2 * nk)
+        if st != 0:
+            raise RuntimeError(f"kvsel_score_evict: {K.status_string(st)}")
+
+    return call, (idx, ws)
+
+
+def run_mode(mode, layers, steps, warmup, hip):
+    call, keep = rkv_caller(mode, layers, 1, N, BUDGET)
+    return time_calls(call, KERNELS[mode], rkv_cost(mode), steps, warmup, hip)
+
+
+def bf16_dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def run_decode(mode, n_layers, hip, calls_per_layer=240):
+    """Decode-loop workload: per layer a 2176-slot cache compressed to 2048 rows
+    every 128 decoded tokens, 240 calls per layer over n_layers layers.  Each
+    layer keeps two caches that swap roles every call (the output of one call
+    is the next call's input); their last 128 slots hold the next 128 tokens
+    of the layer's synthetic stream."""
+    import torch
+
+    from decode_eviction_amd import synth
+    cap, budget, w = 2176, 2048, W
+    layers, outs = [], []
+    for layer in range(n_layers):
+        ds = synth.decode_stream(layer, total=cap + (cap - budget))
+        q = bf16_dev(ds.window(cap, w))
+        k = bf16_dev(ds.k[None, :, :cap])
+        v = bf16_dev(ds.v[None, :, :cap])
+        k2, v2 = k.clone(), v.clone()
+        k2[:, :, budget:] = k[:, :, budget:] = bf16_dev(ds.k[None, :, cap:])
+        v2[:, :, budget:] = v[:, :, budget:] = bf16_dev(ds.v[None, :, cap:])
+        layers.append([(q, k, v), (q, k2, v2)])
+    # call i: layer l = i % n_layers, its j-th call with j = i // n_layers;
+    # input cache j % 2, output the other one
+    seq, obuf = [], []
+    for j in range(2):
+        for l in range(n_layers):
+            seq.append(layers[l][j])
+            _, ko, vo = layers[l][1 - j]
+            obuf.append((ko, vo))
+    call, keep = rkv_caller(mode, seq, 1, cap, budget, out_bufs=obuf)
+    total = n_layers * calls_per_layer
+    cost = rkv_cost(mode, 1, cap, budget)
+    r = time_calls(call, KERNELS[mode], cost, total, 2 * n_layers, hip, traced_steps=512)
+    r["calls"] = total
+    r["tokens"] = total * cap
+    return r
+
+
+def run_batched(mode, hip, steps):
+    """Batched prefill workload: 64 sequences of 8192 tokens, B = 1024 (1 GiB
+    of K and 1 GiB of V, far beyond the 256 MB last-level cache)."""
+    from decode_eviction_amd import synth
+    c = synth.batched_case(seed=0)
+    layer = (bf16_dev(c.q), bf16_dev(c.k), bf16_dev(c.v))
+    del c
+    b, n, budget = 64, 8192, 1024
+    call, keep = rkv_caller(mode, [layer], b, n, budget)
+    r = time_calls(call, KERNELS[mode], rkv_cost(mode, b, n, budget), steps, 2, hip)
+    r["tokens"] = b * n
+    r["step_bytes"] = rkv_step_bytes(b, n, budget)
+    return r
+
+
+CUT_KERNELS = ["stats", "reduce", "cut_energy", "cut_scan"]
+
+
+def run_refreekv(hip, n_layers, steps):
+    """ReFreeKV threshold cut at the Qwen2.5-7B shape (28 q / 4 KV heads,
+    d=128, bf16), 16 sequences of 1024-16384 tokens, one scored layer per
+    call (layers 0-1 keep everything and cost one tiny kernel); rotates over
+    n_layers distinct layers of K."""
+    import torch
+
+    from decode_eviction_amd import kvsel as K
+    from decode_eviction_amd import synth
+    hq, hkv, b = 28, 4, 16
+    lengths = synth.refreekv_lengths(0, b)
+    cap = int(lengths.max())
+    layers = []
+    for layer in range(2, 2 + n_layers):
+        c = synth.cut_case(layer=layer, seed=0, lengths=lengths, cap=cap)
+        layers.append((bf16_dev(c.q), bf16_dev(c.k)))
+    lens = torch.from_numpy(lengths).to("cuda")
+    kept = torch.empty((b, hkv), dtype=torch.int32, device="cuda")
+    ws_bytes = K.kvsel_threshold_cut_workspace(b, hq, hkv, D, cap)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    lib = K.lib()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
+
+    def call(i, events=None):
+        q, k = layers[i % len(layers)]
+        args = (K.KVSEL_BF16, P(q.data_ptr()), P(k.data_ptr()), P(lens.data_ptr()), b, hq, hkv,
+                D, cap, 2 + i % len(layers), 2, 4, 0.01, P(kept.data_ptr()), P(ws.data_ptr()),
+                ws_bytes, sp)
+        st = (lib.kvsel_threshold_cut(*args) if events is None else
+              lib.kvsel_threshold_cut_traced(*args, events, 2 * len(CUT_KERNELS)))
+        if st != 0:
+            raise RuntimeError(f"kvsel_threshold_cut: {K.status_string(st)}")
+
+    r = time_calls(call, CUT_KERNELS, cut_cost(lengths, hq, hkv), steps, 4, hip)
+    r["tokens"] = int(lengths.sum())
+    r["step_bytes"] = int(lengths.sum()) * hkv * D * 2
+    r["layer_bytes"] = layers[0][1].numel() * 2
+    return r
+
+
 KERNEL_SOURCES = {"stats": "scores.hip", "reduce": "scores.hip", "pool": "scores.hip",
-                  "gram": "gram.hip", "thresh": "select.hip", "compact": "select.hip"}
+                  "gram": "gram.hip", "thresh": "select.hip", "compact": "select.hip",
+                  "cut_energy": "cut.hip", "cut_scan": "cut.hip"}
 
 
 def source_digest(kernel: str) -> str:
@@ -221,11 +364,14 @@ def measured_traffic(profiles: str, mode: str, kernel: str):
     return int(float(vals["bytes_per_launch"]))
 
 
-def roofline(mode, res, profiles):
+def roofline(res, cost, profiles, tag):
+    """Roofline of the call's dominant (longest) kernel: algorithmic flops or
+    bytes per launch over its average duration, with the counter-measured HBM
+    traffic from profiles/traffic_<tag>_<kernel>.txt when it is current."""
     kern = res["kernels"]
     dom = max(kern, key=lambda k: kern[k]["avg_us"])
-    c = algorithmic_cost(mode)[dom]
-    traffic = measured_traffic(profiles, mode, dom)
+    c = cost[dom]
+    traffic = measured_traffic(profiles, tag, dom)
     if "flops" in c:
         ach = c["flops"] / (kern[dom]["avg_us"] * 1e-6) / 1e12
         return {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
@@ -233,6 +379,10 @@ def roofline(mode, res, profiles):
     ach = c["bytes"] / (kern[dom]["avg_us"] * 1e-6) / 1e9
     return {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+
+def hbm_frac(nbytes, ms):
+    return round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
 
 
 def cpu_baseline(case, seconds: float) -> dict:
@@ -275,6 +425,63 @@ def copy_calibration(mib: int = 512):
     print(json.dumps({"copy_calibration_bytes": mib << 20, "launches": 5}))
 
 
+def run_variants(a, hip) -> dict:
+    """The other workloads, each reported with its own value and kernels."""
+    import torch
+    want = a.variant or ["decode", "batched", "refreekv"]
+    out = {}
+
+    def log(name, r):
+        print(f"# {name}: {r['ms_plain'] * 1000:.1f} us/call, {r['ms'] * 1000:.1f} us/call traced; "
+              + ", ".join(f"{k} {v['avg_us']:.1f}us" for k, v in r["kernels"].items()),
+              file=sys.stderr, flush=True)
+
+    if "decode" in want:
+        for mode in KERNELS:
+            r = run_decode(mode, 32, hip)
+            log(f"decode/{mode}", r)
+            out[f"decode_{mode}"] = {
+                "workload": "R-KV decode loop: 32 layers x 240 calls, each compressing a "
+                            "2176-slot cache to B=2048 (8B shape, batch 1, w=8)",
+                "value": round(r["tokens"] / (r["ms_plain"] * 1e-3 * r["calls"]), 1),
+                "unit": "cache tokens scored/s", "us_per_call": round(r["ms_plain"] * 1000, 2),
+                "us_per_call_traced": round(r["ms"] * 1000, 2), "calls": r["calls"],
+                "loop_ms": round(r["ms_plain"] * r["calls"], 3),
+                "roofline": roofline(r, rkv_cost(mode, 1, 2176, 2048), a.profiles, f"decode_{mode}"),
+                "step_hbm_frac": hbm_frac(rkv_step_bytes(1, 2176, 2048), r["ms_plain"]),
+                "kernels": r["kernels"]}
+            torch.cuda.empty_cache()
+    if "batched" in want:
+        for mode in KERNELS:
+            r = run_batched(mode, hip, 16 if mode == "keysum" else 6)
+            log(f"batched/{mode}", r)
+            out[f"batched_{mode}"] = {
+                "workload": "R-KV batched: 64 sequences x 8192 tokens, B=1024 (8B shape, w=8)",
+                "value": round(r["tokens"] / (r["ms_plain"] * 1e-3), 1), "unit": "tokens/s/layer",
+                "ms_per_step": round(r["ms_plain"], 5), "ms_per_step_traced": round(r["ms"], 5),
+                "roofline": roofline(r, rkv_cost(mode, 64, 8192, 1024), a.profiles, f"batched_{mode}"),
+                "step_hbm_frac": hbm_frac(r["step_bytes"], r["ms_plain"]), "kernels": r["kernels"]}
+            torch.cuda.empty_cache()
+    if "refreekv" in want:
+        r = run_refreekv(hip, 4, 32)
+        log("refreekv", r)
+        out["refreekv"] = {
+            "workload": "ReFreeKV threshold cut, one scored layer at the Qwen2.5-7B shape: 28 q / "
+                        "4 KV heads, d=128, 16 sequences of 1024-16384 tokens (sum "
+                        f"{r['tokens']}), m=4, T=0.01; 4 distinct layers of "
+                        f"{r['layer_bytes'] >> 20} MiB K rotated",
+            "value": round(r["tokens"] / (r["ms_plain"] * 1e-3), 1), "unit": "tokens/s/layer",
+            "ms_per_step": round(r["ms_plain"], 5), "ms_per_step_traced": round(r["ms"], 5),
+            "roofline": roofline(r, cut_cost(synth_lengths(), 28, 4), a.profiles, "refreekv"),
+            "step_hbm_frac": hbm_frac(r["step_bytes"], r["ms_plain"]), "kernels": r["kernels"]}
+    return out
+
+
+def synth_lengths():
+    from decode_eviction_amd import synth
+    return synth.refreekv_lengths(0, 16)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,6 +493,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-mode", action="store_true", help="skip the other redundancy form")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the decode-loop, batched and ReFreeKV workloads")
+    ap.add_argument("--variant", action="append", choices=["decode", "batched", "refreekv"],
+                    help="run only these extra workloads (repeatable)")
     ap.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args()
 
@@ -333,8 +544,8 @@ def main():
                                "d=128, batch 1, n=32768, w=8, B=2048, lambda=0.1",
                    "redundancy": a.mode, "distinct_layer_caches": a.layers,
                    "kernels_per_step": len(KERNELS[a.mode])},
-        "roofline": roofline(a.mode, main_res, a.profiles),
-        "step_hbm_frac": round(step_bytes(a.mode) / (main_res["ms_plain"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "roofline": roofline(main_res, rkv_cost(a.mode), a.profiles, a.mode),
+        "step_hbm_frac": hbm_frac(rkv_step_bytes(), main_res["ms_plain"]),
         "ms_per_step_traced": round(main_res["ms"], 5),
         "kernels": main_res["kernels"],
     }
@@ -342,11 +553,13 @@ def main():
         r = res[mode]
         out.setdefault("variants", {})[mode] = {
             "value": round(N / (r["ms_plain"] * 1e-3), 1), "ms_per_step": round(r["ms_plain"], 5),
-            "ms_per_step_traced": round(r["ms"], 5), "roofline": roofline(mode, r, a.profiles),
-            "step_hbm_frac": round(step_bytes(mode) / (r["ms_plain"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "kernels": r["kernels"]}
+            "ms_per_step_traced": round(r["ms"], 5),
+            "roofline": roofline(r, rkv_cost(mode), a.profiles, mode),
+            "step_hbm_frac": hbm_frac(rkv_step_bytes(), r["ms_plain"]), "kernels": r["kernels"]}
     del layers
     torch.cuda.empty_cache()
+    if not a.no_variants:
+        out.setdefault("variants", {}).update(run_variants(a, hip))
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(first, a.cpu_seconds)
     print(json.dumps(out))

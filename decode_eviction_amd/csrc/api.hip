@@ -37,6 +37,8 @@ kvsel_status hip_status(hipError_t e) { return e == hipSuccess ? KVSEL_OK : KVSE
     if (e_ != hipSuccess) return KVSEL_ERR_HIP; \
   } while (0)
 
+constexpr float kLog2e = 1.44269504088896340736f;
+
 // -------------------------------------------------------------- R-KV layout
 
 struct ScoreWs {
@@ -115,7 +117,7 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
   p.mp = rows_padded(p.m);
   p.cap = cap;
   p.nchunk = (cap + kChunk - 1) / kChunk;
-  p.scale = 1.0f / sqrtf((float)d);
+  p.scale2 = kLog2e / sqrtf((float)d);
   p.lambda = lambda;
   p.cstat = ws.cstat;
   p.rstat = ws.rstat;
@@ -428,7 +430,7 @@ static kvsel_status threshold_cut_impl(kvsel_dtype dt, const void* q_last, const
   p.mp = rows_padded(g);
   p.cap = cap;
   p.nchunk = c.nchunk;
-  p.scale = 1.0f / sqrtf((float)d);
+  p.scale2 = kLog2e / sqrtf((float)d);
   p.cstat = ws.cstat;
   p.rstat = ws.rstat;
   p.logits = ws.logits;

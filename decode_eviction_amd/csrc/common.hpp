@@ -126,19 +126,56 @@ __device__ __forceinline__ float frag_elem<F32>(u32x4_t c, int e) {
   return __uint_as_float(c[e]);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// w.lo * v.lo + w.hi * v.hi + acc for words holding two bf16 values (the
+// products are exact in fp32).
+__device__ __forceinline__ float dot2_bf16(uint32_t w, uint32_t v, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                         __builtin_bit_cast(bf16x2_t, v), acc, false);
+}
+
 // Squared norm of this lane's share of its row (add the partner lane's).
 template <typename E, int NC>
-__device__ __forceinline__ float frag_sumsq(const Frag<NC>& f) {
+__device__ __forceinline__ float frag_sumsq(const Frag<NC>& f);
+template <>
+__device__ __forceinline__ float frag_sumsq<BF16, 8>(const Frag<8>& f) {
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s0 = dot2_bf16(f.c[j][0], f.c[j][0], s0);
+    s1 = dot2_bf16(f.c[j][1], f.c[j][1], s1);
+    s0 = dot2_bf16(f.c[j][2], f.c[j][2], s0);
+    s1 = dot2_bf16(f.c[j][3], f.c[j][3], s1);
+  }
+  return s0 + s1;
+}
+template <>
+__device__ __forceinline__ float frag_sumsq<BF16, 4>(const Frag<4>& f) {
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s0 = dot2_bf16(f.c[j][0], f.c[j][0], s0);
+    s1 = dot2_bf16(f.c[j][1], f.c[j][1], s1);
+    s0 = dot2_bf16(f.c[j][2], f.c[j][2], s0);
+    s1 = dot2_bf16(f.c[j][3], f.c[j][3], s1);
+  }
+  return s0 + s1;
+}
+template <int NC>
+__device__ __forceinline__ float frag_sumsq_f32(const Frag<NC>& f) {
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < NC; ++j)
 #pragma unroll
-    for (int e = 0; e < E::kPerChunk; ++e) {
-      float x = frag_elem<E>(f.c[j], e);
-      s = fmaf(x, x, s);
-    }
+    for (int e = 0; e < 4; ++e) s = fmaf(__uint_as_float(f.c[j][e]), __uint_as_float(f.c[j][e]), s);
   return s;
 }
+template <>
+__device__ __forceinline__ float frag_sumsq<F32, 8>(const Frag<8>& f) { return frag_sumsq_f32<8>(f); }
+template <>
+__device__ __forceinline__ float frag_sumsq<F32, 16>(const Frag<16>& f) { return frag_sumsq_f32<16>(f); }
+
 
 // Dimension index of element e of chunk j for lane half hf.
 template <typename E>
@@ -179,7 +216,12 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
-// merge two (max, sum-of-exp) softmax partials
+// 2^x on the transcendental unit (v_exp_f32)
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Softmax statistics are kept in base 2: logits are pre-multiplied by
+// log2(e)/sqrt(d), so exp(s - max) = 2^(t - max_t) with t = s * log2(e).
+// Merge two (max, sum of 2^(t - max)) partials.
 __device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, float s2) {
   float mm = fmaxf(m, m2);
   if (mm == -INFINITY) {
@@ -187,7 +229,7 @@ __device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, floa
     s = 0.f;
     return;
   }
-  s = s * __expf(m - mm) + s2 * __expf(m2 - mm);
+  s = s * exp2_fast(m - mm) + s2 * exp2_fast(m2 - mm);
   m = mm;
 }
 

@@ -4,7 +4,7 @@
 //
 // The last-row logits and their per-row softmax statistics come from k_stats
 // / k_reduce (scores.hip, cut mode).  Here:
-//   k_cut_energy  per 256-token chunk: a = exp(s - max) / sum for each of the
+//   k_cut_energy  per 256-token chunk: a = 2^(t - max) / sum for each of the
 //                 g query rows of the group, E[j] = sum_q floor(fl32(a*a) * 2^52)
 //                 as a 64-bit integer, and the chunk's exact integer total;
 //   k_cut_scan    per KV head: tau = ceil(E_total * (1 - T)); if the sinks
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void k_cut_energy(CutParams p) {
         a = p.attn[((long)bi * p.hq + (long)h * p.g + q) * p.cap + tok];
       } else {
         const float2 st = p.rstat[head * p.mp + q];
-        a = __expf(p.logits[(head * p.g + q) * (long)p.lstride + tok] - st.x) * st.y;
+        a = exp2_fast(p.logits[(head * p.g + q) * (long)p.lstride + tok] - st.x) * st.y;
       }
       const float sq = fminf(__fmul_rn(a, a), 1.0f);
       e += (uint64_t)((double)sq * 4503599627370496.0);  // floor(sq * 2^52)
@@ -93,11 +93,19 @@ __global__ __launch_bounds__(256) void k_cut_scan(CutParams p) {
   const int nch = (n + kChunk - 1) / kChunk;
   const int m = min(p.n_sink, n);
 
-  uint64_t tot = 0, esk = 0;
+  // the chunk holding the first non-sink position; its sink part is summed
+  // here so that its non-sink energy is its total minus that part
+  const int cm = m / kChunk;
+  uint64_t tot = 0, esk = 0, esk_cm = 0;
   for (int c = tid; c < nch; c += 256) tot += ct[c];
-  for (int j = tid; j < m; j += 256) esk += E[j];
+  for (int j = tid; j < m; j += 256) {
+    const uint64_t e = E[j];
+    esk += e;
+    esk_cm += j >= cm * kChunk ? e : 0u;
+  }
   tot = block_sum_u64(tot, wsum, tid);
   esk = block_sum_u64(esk, wsum, tid);
+  esk_cm = block_sum_u64(esk_cm, wsum, tid);
   const double taud = ceil((double)tot * (1.0 - (double)p.T));
   const uint64_t tau = (uint64_t)taud;
   if (m > 0 && esk >= tau) {
@@ -106,21 +114,13 @@ __global__ __launch_bounds__(256) void k_cut_scan(CutParams p) {
   }
 
   // chunk level: walk chunks newest first over positions >= m
-  const int cm = m / kChunk;  // first chunk holding a non-sink position
   if (tid == 0) found = -1;
   __syncthreads();
   uint64_t acc = 0;
   for (int r = 0; r * 256 < nch - cm; ++r) {
     const int c = nch - 1 - (r * 256 + tid);
     uint64_t v = 0;
-    if (c >= cm) {
-      if (c * kChunk >= m) {
-        v = ct[c];
-      } else {  // chunk straddles the sink boundary
-        const int hi = min(n, (c + 1) * kChunk);
-        for (int t = m; t < hi; ++t) v += E[t];
-      }
-    }
+    if (c >= cm) v = c > cm ? ct[c] : ct[c] - esk_cm;
     const uint64_t incl = acc + block_incl_scan_u64(v, wsum, tid);
     if (c >= cm && esk + incl >= tau && esk + incl - v < tau) {
       found = c;

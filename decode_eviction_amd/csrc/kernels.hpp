@@ -27,15 +27,15 @@ struct ScoreParams {
   int b, hq, hkv, g, w, m;  // m = g*w query rows per KV head
   int mp;                   // m rounded up to 32
   int cap, nchunk;          // nchunk = ceil(cap / kChunk)
-  float scale;              // 1/sqrt(d)
+  float scale2;             // log2(e)/sqrt(d): logits in base-2 units
   float lambda;
   // workspace
-  float2* cstat;            // [b][Hkv][nchunk][mp]  chunk (max, sum exp)
-  float2* rstat;            // [b][Hkv][mp]          (max, 1/sum)
+  float2* cstat;            // [b][Hkv][nchunk][mp]  chunk (max, sum 2^(t - max))
+  float2* rstat;            // [b][Hkv][mp]          (max, 1/sum), base 2
   float* spart;             // [b][Hkv][nchunk][d]   keysum: chunk sums of unit keys
   float* ssum;              // [b][Hkv][d]           keysum: sum of unit keys
   float* inv_norm;          // [b][Hkv][nchunk*kChunk] gram: 1/||k_j||, 0 past n
-  float* logits;            // [b][Hkv][g][nchunk*kChunk]  cut: scaled logits
+  float* logits;            // [b][Hkv][g][nchunk*kChunk]  cut: logits in base-2 units
   int32_t* err;             // error word
   // outputs (never null; the host substitutes workspace buffers)
   float* i_out;             // [b][Hkv][cap]

@@ -32,6 +32,30 @@ __device__ __forceinline__ f32x16_t zero16() {
   return z;
 }
 
+// One reduce-scatter step over lanes l and l ^ M of a 32-lane half: the
+// lane with bit M set keeps the upper half of v (summed with its partner's),
+// the other the lower half.
+template <int L, int M>
+__device__ __forceinline__ void scatter_step(float* v, int l32) {
+  const bool up = (l32 & M) != 0;
+#pragma unroll
+  for (int i = 0; i < L / 2; ++i) {
+    const float send = up ? v[i] : v[L / 2 + i];
+    const float keep = up ? v[L / 2 + i] : v[i];
+    v[i] = keep + __shfl_xor(send, M, 64);
+  }
+}
+// Repeat until PC values are left: with NC chunks per lane the lane then holds
+// chunk (l32 / (32 / NC)) of its half, summed over the lanes that differ from
+// it in the upper log2(NC) bits of l32.
+template <int L, int M, int PC>
+__device__ __forceinline__ void scatter_down(float* v, int l32) {
+  if constexpr (L > PC) {
+    scatter_step<L, M>(v, l32);
+    scatter_down<L / 2, M / 2, PC>(v, l32);
+  }
+}
+
 template <typename E, int D, int MT, int MODE>
 __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
   using G = Geo<E, D>;
@@ -76,15 +100,10 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[tt][t] = mfma_tile<E, NC>(kf[tt], qf[t], zero16());
 
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool ok = tok0 + 32 * tt + tile_row(i, hf) < n;
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[tt][t][i] = ok ? acc[tt][t][i] * p.scale : -INFINITY;
-    }
-
+  // per-row max and sum of 2^(t - max), t = logit * log2(e) / sqrt(d); only
+  // the wave holding the end of the sequence masks tokens
+  const bool full = tok0 + 64 <= n;
+  const float sc2 = p.scale2;
   __shared__ float2 wst[4][MT * 32];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -92,21 +111,29 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[tt][t][i]);
+      for (int i = 0; i < 16; ++i) {
+        const bool ok = full || tok0 + 32 * tt + tile_row(i, hf) < n;
+        m = ok ? fmaxf(m, acc[tt][t][i]) : m;
+      }
     m = fmaxf(m, xor32(m));
+    const float m2 = m * sc2;  // sc2 > 0: the max of the scaled logits
     float s = 0.f;
     if (m != -INFINITY) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s += __expf(acc[tt][t][i] - m);
+        for (int i = 0; i < 16; ++i) {
+          const bool ok = full || tok0 + 32 * tt + tile_row(i, hf) < n;
+          const float e = exp2_fast(fmaf(acc[tt][t][i], sc2, -m2));
+          s += ok ? e : 0.f;
+        }
     }
     s += xor32(s);
-    if (hf == 0) wst[wave][32 * t + l32] = make_float2(m, s);
+    if (hf == 0) wst[wave][32 * t + l32] = make_float2(m2, s);
   }
 
   if constexpr (MODE == kModeCut) {
-    // scaled logits of rows < g, 4 consecutive tokens per store
+    // logits of rows < g in base-2 units, 4 consecutive tokens per store
     if (l32 < p.g) {
       const long ls = (long)p.nchunk * kChunk;
       float* lrow = p.logits + (head * p.g + l32) * ls;
@@ -116,10 +143,10 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
         for (int q4 = 0; q4 < 4; ++q4) {
           const int tb = tok0 + 32 * tt + 8 * q4 + 4 * hf;
           f32x4_t v;
-          v[0] = acc[tt][0][4 * q4 + 0];
-          v[1] = acc[tt][0][4 * q4 + 1];
-          v[2] = acc[tt][0][4 * q4 + 2];
-          v[3] = acc[tt][0][4 * q4 + 3];
+          v[0] = acc[tt][0][4 * q4 + 0] * sc2;
+          v[1] = acc[tt][0][4 * q4 + 1] * sc2;
+          v[2] = acc[tt][0][4 * q4 + 2] * sc2;
+          v[3] = acc[tt][0][4 * q4 + 3] * sc2;
           *reinterpret_cast<f32x4_t*>(lrow + tb) = v;
         }
     }
@@ -136,21 +163,29 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
       if (MODE == kModeGram && hf == 0) p.inv_norm[head * (long)p.nchunk * kChunk + tok] = inv[tt];
     }
     if constexpr (MODE == kModeKeysum) {
-      constexpr int LP = LE + 4;  // padded lane stride (floats)
-      __shared__ float sred[4 * 64 * LP];
-      float* mine = sred + (wave * 64 + lane) * LP;
+      // this chunk's sum of unit keys: per lane its two tokens, then a
+      // reduce-scatter over the 32 lanes of the half, then across waves
+      float v[LE];
 #pragma unroll
       for (int j = 0; j < NC; ++j)
 #pragma unroll
         for (int e = 0; e < PC; ++e)
-          mine[j * PC + e] = inv[0] * frag_elem<E>(kf[0].c[j], e) + inv[1] * frag_elem<E>(kf[1].c[j], e);
+          v[j * PC + e] = inv[0] * frag_elem<E>(kf[0].c[j], e) + inv[1] * frag_elem<E>(kf[1].c[j], e);
+      scatter_down<LE, 16, PC>(v, l32);
+      constexpr int R = 32 / NC;  // lanes of a half still to be summed
+      __shared__ float red[256 * PC];
+      float* mine = red + (wave * 64 + lane) * PC;
+#pragma unroll
+      for (int e = 0; e < PC; ++e) mine[e] = v[e];
       __syncthreads();
       if (tid < D) {
-        const int dim = tid, ch = dim / PC, hfd = ch & 1, slot = (ch >> 1) * PC + dim % PC;
+        const int ch = tid / PC, e = tid % PC, hfd = ch & 1, j = ch >> 1;
         float a = 0.f;
+#pragma unroll
         for (int wv = 0; wv < 4; ++wv)
-          for (int l = 0; l < 32; ++l) a += sred[(wv * 64 + hfd * 32 + l) * LP + slot];
-        p.spart[(head * p.nchunk + chunk) * D + dim] = a;
+#pragma unroll
+          for (int q = 0; q < R; ++q) a += red[(wv * 64 + hfd * 32 + j * R + q) * PC + e];
+        p.spart[(head * p.nchunk + chunk) * D + tid] = a;
       }
     }
   }
@@ -269,6 +304,7 @@ __global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
   }
   __syncthreads();
 
+  const float sc2 = p.scale2;
   const float inv_m = 1.0f / (float)p.m;
   const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
 #pragma unroll
@@ -281,7 +317,7 @@ __global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float2 st = rs[32 * t + tile_row(i, hf)];
-        isum += __expf(a[i] * p.scale - st.x) * st.y;
+        isum = fmaf(exp2_fast(fmaf(a[i], sc2, -st.x)), st.y, isum);
       }
     }
     isum += xor32(isum);
