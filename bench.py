@@ -49,7 +49,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 
 KERNELS = {
-    "gram": ["stats", "reduce", "pool", "gram", "thresh", "compact"],
+    "gram": ["stats", "reduce", "pool", "gram", "gram_fin", "thresh", "compact"],
     "keysum": ["stats", "reduce", "pool", "thresh", "compact"],
 }
 
@@ -71,7 +71,15 @@ def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int =
         "compact": {"bytes": 4 * tok + 4 * b * hkv * budget + gath},
     }
     if mode == "gram":
-        cost["gram"] = {"bytes": kb + 4 * tok * 3, "flops": 2.0 * b * hkv * n * n * d}
+        # symmetric Gram: each pair of 256-key blocks once; matrix-core flops
+        # as executed (2 d per key pair and block padding included)
+        nb = -(-n // 256)
+        blocks = sum(1 + (nb - 1) // 2 + (1 if nb % 2 == 0 and i < nb // 2 else 0)
+                     for i in range(nb))
+        ns = nb // 2
+        cost["gram"] = {"bytes": kb + 4 * tok * 2 + 4 * tok * ns // 2,
+                        "flops": 2.0 * b * hkv * blocks * 256 * 256 * d}
+        cost["gram_fin"] = {"bytes": 4 * tok * 5 + 4 * tok * ns // 2}
     return cost
 
 
@@ -332,7 +340,8 @@ def run_refreekv(hip, n_layers, steps):
 
 
 KERNEL_SOURCES = {"stats": "scores.hip", "reduce": "scores.hip", "pool": "scores.hip",
-                  "gram": "gram.hip", "thresh": "select.hip", "compact": "select.hip",
+                  "gram": "gram.hip", "gram_fin": "gram.hip", "thresh": "select.hip",
+                  "compact": "select.hip",
                   "cut_energy": "cut.hip", "cut_scan": "cut.hip"}
 
 

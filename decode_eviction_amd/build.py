@@ -32,10 +32,15 @@ HIP_FLAGS = [
 
 SOURCES = ["api.hip", "scores.hip", "gram.hip", "select.hip", "cut.hip"]
 
+# Per-file code generation options.  The Gram kernel folds every matrix-core
+# result with fp32 FMAs; keeping the results (and accumulator inputs) in
+# ordinary VGPRs avoids a copy out of the accumulation registers per value.
+EXTRA_FLAGS = {"gram.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -50,6 +50,9 @@ struct ScoreWs {
   float* inv_norm;
   float* imp;
   float* z;
+  float* grs;    // Gram form: own-block row sums
+  float* gpart;  // Gram form: column sums from the other blocks
+  int nsmax;
   struct {
     uint32_t* hist;
     uint32_t* thr;
@@ -74,6 +77,9 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap) {
   w.inv_norm = c.take<float>(heads * nchunk * kChunk);
   w.imp = c.take<float>(heads * cap);
   w.z = c.take<float>(heads * cap);
+  w.nsmax = ((cap + 255) / 256) / 2;
+  w.grs = c.take<float>(heads * cap);
+  w.gpart = c.take<float>(heads * (size_t)w.nsmax * cap);
   w.sel.nsc = (cap + kSelChunk - 1) / kSelChunk;
   w.sel.hist = c.take<uint32_t>(heads * kHistBins);
   w.sel.thr = c.take<uint32_t>(heads * 2);
@@ -148,6 +154,9 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
     gp.r_out = r_out;
     gp.z_out = z_out;
     gp.hist = hist;
+    gp.rs = ws.grs;
+    gp.part = ws.gpart;
+    gp.nsmax = ws.nsmax;
     KV_TRY(launch_gram(dt, d, gp, stream, tr));
   }
   return KVSEL_OK;

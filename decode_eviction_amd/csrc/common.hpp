@@ -216,6 +216,30 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
+// Direct global->LDS copies (global_load_lds): lane l of the wave writes its
+// 16 (or 4) bytes to LDS at base + 16 l (4 l); base must be wave-uniform.
+// Written as inline assembly on purpose: when the compiler sees an LDS DMA it
+// makes every later LDS read wait for all outstanding vector memory
+// operations (it cannot tell ring slots apart), which would serialise a
+// prefetch ring.  Callers order the copies themselves with an explicit
+// s_waitcnt vmcnt and a barrier before reading what they wrote.  The
+// instructions write no registers; their address registers are read at issue.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma_lds16(const void* g, const void* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_offset(lds_wave_base)))
+               : "m0");
+}
+__device__ __forceinline__ void dma_lds4(const void* g, const void* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_offset(lds_wave_base)))
+               : "m0");
+}
+
 // 2^x on the transcendental unit (v_exp_f32)
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

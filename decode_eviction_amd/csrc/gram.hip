@@ -8,16 +8,26 @@
 // accumulation); the inverse norms are applied in fp32 afterwards, because
 // rounding normalised keys to bf16 first would cost about three decimal
 // digits of R.  The n x n Gram matrix only ever lives in accumulator
-// registers: after each 256 x 128 tile each lane folds its 16 outputs into 16
-// running row sums weighted by its column's w_i.
+// registers.
 //
-// Work-group: 8 waves (two per SIMD), 256 rows resident in registers (each
-// row group of 64 rows is held by two waves that split every column block).
-// Columns stream through LDS 128 keys at a time in a ring of three blocks,
-// with direct global->LDS loads issued two blocks ahead; each wave keeps two
-// accumulator sets so the fp32 epilogue of one tile runs between the
-// matrix-core instructions of the next.  The last step combines R with the
-// importance from k_pool into Z = lambda I - (1-lambda) R.
+// Symmetry: G = K K^T, so each unordered pair of 256-key blocks {I, J} is
+// computed once.  Row block I takes the diagonal block and the blocks
+// J = I + d (mod nb) for d = 1 .. (nb-1)/2, plus d = nb/2 when nb is even and
+// I < nb/2; every pair is covered exactly once and all work-groups of a head
+// get the same number of blocks.  An off-diagonal tile adds its w-weighted row
+// sums to block I (in registers) and its w-weighted column sums to block J:
+// those go to a partial buffer, one slot per distance d, so that no two
+// work-groups write the same word.  k_gram_fin then adds, per key, its own
+// row sums and the slots that have a contributor, in a fixed order
+// (deterministic), and forms R and Z = lambda I - (1-lambda) R.
+//
+// Work-group: 4 waves (one per SIMD, up to 512 registers each), 256 rows
+// resident in registers, 64 per wave.  Columns stream through LDS 128 keys at
+// a time in a ring of three blocks, with direct global->LDS loads issued two
+// blocks ahead.  Each wave sweeps the four 32-column tiles of a block with
+// double-buffered B fragments (the next tile's LDS reads overlap this tile's
+// matrix-core instructions) and two accumulator sets (a tile's fp32 epilogue
+// runs between the matrix-core instructions of the next tile).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,86 +47,89 @@ __device__ __forceinline__ int xcd_major(int L, int total) {
 // operations of this wave are outstanding; LDS/scalar counters untouched.
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
+// Blocks of columns (of 256 keys) that row block I computes; see above.
+__device__ __forceinline__ int gram_blocks(int I, int nb) {
+  return 1 + (nb - 1) / 2 + ((nb % 2 == 0 && I < nb / 2) ? 1 : 0);
+}
+
 template <typename E, int D>
-__global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
+__global__ __launch_bounds__(256, 1) void k_gram(GramParams p) {
   using G = Geo<E, D>;
   constexpr int NC = G::kNC;
   constexpr int RB = G::kRowBytes;
-  constexpr int CPR = G::kChunks;        // 16-byte chunks per key
-  constexpr int ROWS = 256;              // rows per work-group (4 row groups x 64)
-  constexpr int COLS = 128;              // columns per step (2 column groups x 64)
-  constexpr int STAGE = COLS * RB;       // one staged key block, unpadded
+  constexpr int NT = 256;                // threads: one wave per SIMD
+  constexpr int ROWS = 256;              // rows per work-group: 4 waves x 64
+  constexpr int COLS = 128;              // columns per step: 4 tiles of 32
+  constexpr int STAGE = COLS * RB;       // one staged key block
   constexpr int NBUF = 3 * STAGE <= 96 * 1024 ? 3 : 2;  // ring: current block + NBUF-1 ahead
   constexpr int AHEAD = NBUF - 1;
-  constexpr int PER = COLS * CPR / 512;  // 16-byte key chunks each thread streams per step
+  constexpr int PER = NC;                // 16-byte chunk pairs: global->LDS loads per thread per step
   constexpr int VM_STEP = PER + 1;       // vector memory operations per thread per step
-  constexpr int RED = 65;                // padded row stride of the final reduction
+  constexpr int RED = 33;                // padded row stride of the final reduction
   constexpr int KBYTES = NBUF * STAGE;
-  constexpr int HOFF = ROWS * RED * 4;   // LDS histogram after the reduction buffer
-  constexpr int LDSB = KBYTES > HOFF + kHistBins * 4 ? KBYTES : HOFF + kHistBins * 4;
+  constexpr int LDSB = KBYTES > ROWS * RED * 4 ? KBYTES : ROWS * RED * 4;
   __shared__ __attribute__((aligned(16))) char lds_raw[LDSB];
   __shared__ __attribute__((aligned(16))) float wcol[NBUF][COLS];
-  __shared__ float rowss[ROWS];
+  __shared__ float colred[3][4][2][COLS];  // column sums per wave (and lane half), by step mod 3
 
   const int nrb = (p.cap + ROWS - 1) / ROWS;
   const int W = xcd_major(blockIdx.x, nrb * p.hkv * p.b);
   const int rb = W % nrb, hh = W / nrb;
   const int h = hh % p.hkv, bi = hh / p.hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
-  const int rg = wave >> 1, cg = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
   const int n = min(p.lengths[bi], p.cap);
   const int r0 = rb * ROWS;
   if (r0 >= n) return;
+  const int nb = (n + ROWS - 1) / ROWS;
+  const int nsteps = 2 * gram_blocks(rb, nb);
   const long head = (long)bi * p.hkv + h;
   const char* kb = p.k + head * (long)p.cap * RB;
   const float* wv = p.inv_norm + head * (long)p.wstride;
+  // first column of step t: block J = rb + t/2 (mod nb), half t%2
+  auto col0 = [&](int t) {
+    int J = rb + (t >> 1);
+    J -= J >= nb ? nb : 0;
+    return J * ROWS + (t & 1) * COLS;
+  };
 
+  // this wave's 64 rows, resident for the whole sweep (matrix-core operands only)
   Frag<NC> af[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    const int row = r0 + rg * 64 + 32 * rt + l32;
+    const int row = r0 + wave * 64 + 32 * rt + l32;
     load_frag<E, D>(af[rt], kb, row, row < n, hf);
-    if (cg == 0) {
-      float ss = frag_sumsq<E, NC>(af[rt]);
-      ss += xor32(ss);
-      if (hf == 0) rowss[rg * 64 + 32 * rt + l32] = ss;
-    }
   }
-
-  // LDS layout of a staged block: key r, chunk c at 16-byte slot
-  // r*CPR + (c ^ (r % CPR)); the XOR swizzle makes the 32 keys of a fragment
-  // read hit distinct banks without padding.  The direct global->LDS loads
-  // write lane l of a wave instruction to slot (instruction base + l), so each
-  // lane fetches the chunk that belongs in its slot.
-  int srow[PER], soff[PER];
+  // weights of the 32 rows this lane's accumulators cover (0 past n)
+  float wrow[2][16];
 #pragma unroll
-  for (int it = 0; it < PER; ++it) {
-    const int P = it * 512 + tid, r = P / CPR, c = (P % CPR) ^ (r & (CPR - 1));
-    srow[it] = r;
-    soff[it] = c * 16;
-  }
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4_t w4 =
+          *reinterpret_cast<const f32x4_t*>(wv + r0 + wave * 64 + 32 * rt + 8 * q + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wrow[rt][4 * q + e] = w4[e];
+    }
+
+  // LDS layout of a staged block: key r, 16-byte chunk c at slot
+  // (c / 2) * 256 + 2 r + c % 2.  A fragment read (32 keys, chunks 2j and
+  // 2j+1 for the two lane halves) is then 64 consecutive slots: no bank
+  // conflicts, and the chunk index only moves an immediate offset.  The
+  // direct global->LDS loads write lane l of a wave instruction to slot
+  // (instruction base + l), so for instruction it thread tid streams key
+  // tid / 2, chunk 2 it + tid % 2.
+  const int schunk_off = (tid & 1) * 16;
   // Columns past n are clamped to key n-1 (finite data); their weights are 0.
   auto stream = [&](int c0, int buf) {
-    const bool full = c0 + COLS <= n;
+    const int row = min(c0 + (tid >> 1), n - 1);
+    const char* src = kb + (long)row * RB + schunk_off;
 #pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int row = full ? c0 + srow[it] : min(c0 + srow[it], n - 1);
-      const char* src = kb + (long)row * RB + soff[it];
-      char* dst = lds_raw + buf * STAGE + (it * 512 + wave * 64) * 16;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-    }
-    // weights: each wave streams one half of the block's 128 (the four copies agree)
-    const float* wsrc = wv + c0 + (wave & 1) * 64 + lane;
-    float* wdst = &wcol[buf][(wave & 1) * 64];
-    __builtin_amdgcn_global_load_lds(wsrc, (__attribute__((address_space(3))) void*)wdst, 4, 0, 0);
+    for (int it = 0; it < PER; ++it) dma_lds16(src + it * 32, lds_raw + buf * STAGE + it * 4096 + wave * 1024);
+    // weights: waves 0 and 1 stream the block's 128 (the other two fetch a copy)
+    dma_lds4(wv + c0 + (wave & 1) * 64 + lane, &wcol[buf][(wave & 1) * 64]);
   };
-
-  int rdoff[NC];
-#pragma unroll
-  for (int j = 0; j < NC; ++j) rdoff[j] = ((2 * j + hf) ^ (l32 & (CPR - 1))) * 16;
-  int colrb[2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) colrb[ct] = (cg * 64 + 32 * ct + l32) * RB;
+  const int rdbase = (2 * l32 + hf) * 16;  // + 1024 ct + 4096 j
 
   float rsum[2][16];
 #pragma unroll
@@ -124,95 +137,166 @@ __global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) rsum[rt][i] = 0.f;
 
-  // Two accumulator sets: the fp32 epilogue of one column tile is issued
-  // between the matrix-core instructions of the next tile.
-  f32x16_t acc_a[2], acc_b[2];
-  float w_b = 0.f;
+  auto read_b = [&](Frag<NC>& f, int buf, int ct) {
+    const char* base = lds_raw + buf * STAGE + rdbase + ct * 1024;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc_b[rt][i] = 0.f;
-  auto tile = [&](int buf, int ct, f32x16_t (&acc)[2]) {
-    Frag<NC> bfr;
-    const char* base = lds_raw + buf * STAGE + colrb[ct];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) bfr.c[j] = *reinterpret_cast<const u32x4_t*>(base + rdoff[j]);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[rt][i] = 0.f;
-      acc[rt] = mfma_tile<E, NC>(af[rt], bfr, acc[rt]);
-    }
-    return wcol[buf][cg * 64 + 32 * ct + l32];
+    for (int j = 0; j < NC; ++j) f.c[j] = *reinterpret_cast<const u32x4_t*>(base + j * 4096);
   };
-  auto fold = [&](const f32x16_t (&acc)[2], float w) {
+  // row sums weighted by the column's w; column sums weighted by the rows' w
+  auto fold = [&](const f32x16_t (&acc)[2], float w, int ct, int t) {
+    float cs = 0.f;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) rsum[rt][i] = fmaf(acc[rt][i], w, rsum[rt][i]);
+      for (int i = 0; i < 16; ++i) {
+        rsum[rt][i] = fmaf(acc[rt][i], w, rsum[rt][i]);
+        cs = fmaf(acc[rt][i], wrow[rt][i], cs);
+      }
+    cs += xor32(cs);
+    // both lane halves hold the sum; each writes its own copy (no branch, so
+    // the step stays one scheduling region).  t = -1 (the empty carried tile
+    // before the first step) writes zeros into the buffer of step 2, which
+    // overwrites them before it is flushed.
+    colred[(t + 3) % 3][wave][hf][ct * 32 + l32] = cs;
   };
+  // column sums of step t to its partial slot (distance t/2; none for the
+  // diagonal block); run after the barrier that completes step t
+  auto flush = [&](int t) {
+    if (tid < COLS && (t >> 1) >= 1) {
+      const int c = col0(t) + tid;
+      const float v = colred[t % 3][0][0][tid] + colred[t % 3][1][0][tid] + colred[t % 3][2][0][tid] +
+                      colred[t % 3][3][0][tid];
+      if (c < n) p.part[(head * p.nsmax + (t >> 1) - 1) * (long)p.cap + c] = v;
+    }
+  };
+
+  // Two accumulator sets: tile ct's fold runs between the matrix-core
+  // instructions of tile ct+1; the last tile of a step is folded during the
+  // first tile of the next.
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[1][rt][i] = 0.f;
+  float w_carry = 0.f;
 
   // The ring always issues one block per step so that the wait count is a
   // constant: past the last block it re-streams the last block into the
   // buffer no later step reads.
-  const int nsteps = (n + COLS - 1) / COLS;
   constexpr int VM_KEEP = (AHEAD - 1) * VM_STEP;  // loads allowed in flight at a step's end
 #pragma unroll
-  for (int a = 0; a < AHEAD; ++a) stream(min(a, nsteps - 1) * COLS, a);
+  for (int a = 0; a < AHEAD; ++a) stream(col0(min(a, nsteps - 1)), a);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_KEEP));
   __syncthreads();
   for (int st = 0; st < nsteps; ++st) {
     const int buf = st % NBUF;
-    stream(min(st + AHEAD, nsteps - 1) * COLS, (st + AHEAD) % NBUF);
-    const float w_a = tile(buf, 0, acc_a);
-    fold(acc_b, w_b);
-    w_b = tile(buf, 1, acc_b);
-    fold(acc_a, w_a);
-    if constexpr (NC == 8 && E::kBytes == 2) {
-      // 32 MFMAs, each followed by two of the 64 epilogue FMAs
+    if (st >= 2) flush(st - 2);
+    stream(col0(min(st + AHEAD, nsteps - 1)), (st + AHEAD) % NBUF);
+    Frag<NC> bq[2];
+    read_b(bq[0], buf, 0);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    for (int ct = 0; ct < 4; ++ct) {
+      if (ct < 3) read_b(bq[(ct + 1) & 1], buf, ct + 1);
+      const float w = wcol[buf][ct * 32 + l32];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        f32x16_t z;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = 0.f;
+        acc[ct & 1][rt] = mfma_tile<E, NC>(af[rt], bq[ct & 1], z);
       }
+      if (ct == 0) fold(acc[1], w_carry, 3, st - 1);
+      else fold(acc[(ct - 1) & 1], wcol[buf][(ct - 1) * 32 + l32], ct - 1, st);
+      if (ct == 3) w_carry = w;
+    }
+    if constexpr (NC == 8 && E::kBytes == 2) {
+      // Schedule of a step: tile 0's LDS reads, then per tile its 16
+      // matrix-core instructions interleaved with the next tile's 8 LDS reads
+      // and the previous tile's epilogue FMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (ct < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
     }
     // block st+1 has landed once only the newer blocks may still be in flight
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_KEEP));
     __syncthreads();
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  fold(acc_b, w_b);
+  fold(acc[1], w_carry, 3, nsteps - 1);
 
-  // row sums: lane (hf, l32) of wave (rg, cg) holds rows rg*64 + 32rt + tile_row(i, hf)
+  // row sums: lane (hf, l32) of wave w holds rows w*64 + 32rt + tile_row(i, hf)
   float* red = reinterpret_cast<float*>(lds_raw);
-  uint32_t* lh = reinterpret_cast<uint32_t*>(lds_raw + HOFF);
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      red[(rg * 64 + 32 * rt + tile_row(i, hf)) * RED + cg * 32 + l32] = rsum[rt][i];
-  if (p.hist)
-    for (int t = tid; t < kHistBins; t += 512) lh[t] = 0u;
+    for (int i = 0; i < 16; ++i) red[(wave * 64 + 32 * rt + tile_row(i, hf)) * RED + l32] = rsum[rt][i];
   __syncthreads();
-  if (tid < ROWS) {
+  if (nsteps >= 2) flush(nsteps - 2);
+  flush(nsteps - 1);
+  {
     const int j = r0 + tid;
     if (j < n) {
       float s = 0.f;
-      for (int l = 0; l < 64; ++l) s += red[tid * RED + l];
-      const float ss = rowss[tid];
-      const float inv = inv_norm_of(ss);
-      const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
-      const float red_j = (inv * s - inv * inv * ss) * inv_nm1;
-      const long o = head * p.cap + j;
-      if (p.r_out) p.r_out[o] = red_j;
-      const float z = p.lambda * p.i_in[o] - (1.0f - p.lambda) * red_j;
-      p.z_out[o] = z;
-      if (p.hist) atomicAdd(&lh[hist_bin(score_key(z))], 1u);
+#pragma unroll 8
+      for (int l = 0; l < 32; ++l) s += red[tid * RED + l];
+      // own row sums minus the self term w_j ||k_j||^2 = 1 / w_j (0 for a zero key)
+      const float w = wv[j];
+      p.rs[head * p.cap + j] = s - (w > 0.f ? 1.0f / w : 0.f);
     }
+  }
+}
+
+// R and Z per key: own row sums plus the column sums of the blocks that
+// computed this key's block as their column block, in slot order.
+__global__ __launch_bounds__(256) void k_gram_fin(GramParams p) {
+  __shared__ uint32_t lh[kHistBins];
+  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
+  const int n = min(p.lengths[bi], p.cap);
+  if (chunk * 256 >= n) return;
+  const long head = (long)bi * p.hkv + h;
+  if (p.hist)
+    for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
+  __syncthreads();
+  const int j = chunk * 256 + tid;
+  if (j < n) {
+    const int nb = (n + 255) / 256, J = j / 256, ns = nb / 2;
+    // slot s holds the contribution of block J - (s+1); the slot of
+    // distance nb/2 (nb even) is filled only for J >= nb/2
+    const int nfull = (nb - 1) / 2;
+    const bool opp = nb % 2 == 0 && ns >= 1 && J >= nb / 2;
+    const float* pp = p.part + head * (long)p.nsmax * p.cap + j;
+    float tot = p.rs[head * p.cap + j];
+    int s = 0;
+    for (; s + 4 <= nfull; s += 4) {
+      const float a0 = pp[(long)(s + 0) * p.cap], a1 = pp[(long)(s + 1) * p.cap];
+      const float a2 = pp[(long)(s + 2) * p.cap], a3 = pp[(long)(s + 3) * p.cap];
+      tot += a0;
+      tot += a1;
+      tot += a2;
+      tot += a3;
+    }
+    for (; s < nfull; ++s) tot += pp[(long)s * p.cap];
+    if (opp) tot += pp[(long)(ns - 1) * p.cap];
+    const float w = p.inv_norm[head * (long)p.wstride + j];
+    const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
+    const float red_j = w * tot * inv_nm1;
+    const long o = head * p.cap + j;
+    if (p.r_out) p.r_out[o] = red_j;
+    const float z = p.lambda * p.i_in[o] - (1.0f - p.lambda) * red_j;
+    p.z_out[o] = z;
+    if (p.hist) atomicAdd(&lh[hist_bin(score_key(z))], 1u);
   }
   if (p.hist) {
     __syncthreads();
-    for (int t = tid; t < kHistBins; t += 512)
+    for (int t = tid; t < kHistBins; t += 256)
       if (lh[t]) atomicAdd(&p.hist[head * kHistBins + t], lh[t]);
   }
 }
@@ -220,12 +304,15 @@ __global__ __launch_bounds__(512, 1) void k_gram(GramParams p) {
 template <typename E, int D>
 static hipError_t gram_t(const GramParams& p, hipStream_t s, Trace* tr) {
   const int blocks = (p.cap + 255) / 256 * p.hkv * p.b;
-  return launch_k(k_gram<E, D>, dim3(blocks), dim3(512), s, tr, p);
+  return launch_k(k_gram<E, D>, dim3(blocks), dim3(256), s, tr, p);
 }
 
 hipError_t launch_gram(int dt, int d, const GramParams& p, hipStream_t s, Trace* tr) {
-  if (dt == 0) return d == 64 ? gram_t<BF16, 64>(p, s, tr) : gram_t<BF16, 128>(p, s, tr);
-  return d == 64 ? gram_t<F32, 64>(p, s, tr) : gram_t<F32, 128>(p, s, tr);
+  hipError_t e;
+  if (dt == 0) e = d == 64 ? gram_t<BF16, 64>(p, s, tr) : gram_t<BF16, 128>(p, s, tr);
+  else e = d == 64 ? gram_t<F32, 64>(p, s, tr) : gram_t<F32, 128>(p, s, tr);
+  if (e != hipSuccess) return e;
+  return launch_k(k_gram_fin, dim3((p.cap + 255) / 256, p.hkv, p.b), dim3(256), s, tr, p);
 }
 
 }  // namespace kvsel

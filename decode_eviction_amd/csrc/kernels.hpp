@@ -55,6 +55,9 @@ struct GramParams {
   float* r_out;             // nullable
   float* z_out;
   uint32_t* hist;           // nullable [b][Hkv][kHistBins]
+  float* rs;                // [b][Hkv][cap]  a key's own-block row sums minus its self term
+  float* part;              // [b][Hkv][nsmax][cap]  column sums by block distance - 1
+  int nsmax;                // (ceil(cap / 256)) / 2
 };
 
 constexpr int kSelChunk = 512;     // positions per compaction work-group

@@ -71,7 +71,9 @@ typedef enum { KVSEL_BF16 = 0, KVSEL_F32 = 1 } kvsel_dtype;
 /* How R is evaluated.  Both give the same R up to fp32 rounding.
  *  KVSEL_R_GRAM:   the n x n Gram matrix K.K^T on bf16 matrix cores (fp32
  *                  accumulation), weighted by inverse norms and row-summed in
- *                  registers; the n x n matrix never reaches memory.  O(n^2 d).
+ *                  registers; the n x n matrix never reaches memory.  Each
+ *                  pair of 256-key blocks is computed once (symmetry), about
+ *                  n^2 d multiply-adds.  O(n^2 d).
  *  KVSEL_R_KEYSUM: the regrouped sum  sum_{i!=j} u_i.u_j = u_j.(sum_i u_i) - u_j.u_j
  *                  over unit keys u, fused into the importance pass.  O(n d). */
 typedef enum { KVSEL_R_GRAM = 0, KVSEL_R_KEYSUM = 1 } kvsel_redundancy;
@@ -125,7 +127,7 @@ kvsel_status kvsel_score_evict(kvsel_dtype dt, kvsel_redundancy mode,
  * the call records events[2k] when it starts and events[2k+1] when it ends
  * (k < n_events / 2; events are created by the caller with hipEventCreate).
  * Launch order for cap <= 32768: KVSEL_R_GRAM: stats, reduce, pool, gram,
- * threshold, compact (the compaction kernel also gathers the kept rows);
+ * gram_fin, threshold, compact (the compaction kernel also gathers the kept rows);
  * KVSEL_R_KEYSUM: stats, reduce, pool, threshold, compact.  For larger cap
  * the last two are replaced by select, gather. */
 kvsel_status kvsel_score_evict_traced(kvsel_dtype dt, kvsel_redundancy mode,
