@@ -61,8 +61,11 @@ __global__ __launch_bounds__(256, 1) void k_gram(GramParams p) {
   constexpr int ROWS = 256;              // rows per work-group: 4 waves x 64
   constexpr int COLS = 128;              // columns per step: 4 tiles of 32
   constexpr int STAGE = COLS * RB;       // one staged key block
-  constexpr int NBUF = 3 * STAGE <= 96 * 1024 ? 3 : 2;  // ring: current block + NBUF-1 ahead
-  constexpr int AHEAD = NBUF - 1;
+  // bf16, d = 128: the explicitly pipelined step below (four ring slots,
+  // copies two blocks ahead); other shapes: a plain step loop.
+  constexpr bool kFast = NC == 8 && E::kBytes == 2;
+  constexpr int NBUF = kFast ? 4 : (3 * STAGE <= 96 * 1024 ? 3 : 2);
+  constexpr int AHEAD = kFast ? 2 : NBUF - 1;  // blocks streamed ahead of the one being read
   constexpr int PER = NC;                // 16-byte chunk pairs: global->LDS loads per thread per step
   constexpr int VM_STEP = PER + 1;       // vector memory operations per thread per step
   constexpr int RED = 33;                // padded row stride of the final reduction
@@ -113,13 +116,15 @@ __global__ __launch_bounds__(256, 1) void k_gram(GramParams p) {
     }
 
   // LDS layout of a staged block: key r, 16-byte chunk c at slot
-  // (c / 2) * 256 + 2 r + c % 2.  A fragment read (32 keys, chunks 2j and
-  // 2j+1 for the two lane halves) is then 64 consecutive slots: no bank
-  // conflicts, and the chunk index only moves an immediate offset.  The
-  // direct global->LDS loads write lane l of a wave instruction to slot
-  // (instruction base + l), so for instruction it thread tid streams key
-  // tid / 2, chunk 2 it + tid % 2.
-  const int schunk_off = (tid & 1) * 16;
+  // (c / 2) * 256 + 2 r + ((c % 2) ^ sw(r)),  sw(r) = bit 2 of r xor bit 3.
+  // A fragment read (32 keys, chunks 2j and 2j+1 for the two lane halves)
+  // covers 64 consecutive slots, and sw makes any 8 or 16 consecutive lanes
+  // of it hit distinct banks.  The chunk index only moves an immediate
+  // offset.  The direct global->LDS loads write lane l of a wave instruction
+  // to slot (instruction base + l), so for instruction it thread tid streams
+  // key tid / 2, chunk 2 it + ((tid % 2) ^ sw(tid / 2)).
+  auto sw = [](int r) { return ((r >> 2) ^ (r >> 3)) & 1; };
+  const int schunk_off = ((tid & 1) ^ sw(tid >> 1)) * 16;
   // Columns past n are clamped to key n-1 (finite data); their weights are 0.
   auto stream = [&](int c0, int buf) {
     const int row = min(c0 + (tid >> 1), n - 1);
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(256, 1) void k_gram(GramParams p) {
     // weights: waves 0 and 1 stream the block's 128 (the other two fetch a copy)
     dma_lds4(wv + c0 + (wave & 1) * 64 + lane, &wcol[buf][(wave & 1) * 64]);
   };
-  const int rdbase = (2 * l32 + hf) * 16;  // + 1024 ct + 4096 j
+  const int rdbase = (2 * l32 + (hf ^ sw(l32))) * 16;  // + 1024 ct + 4096 j
 
   float rsum[2][16];
 #pragma unroll
@@ -152,9 +157,8 @@ __global__ __launch_bounds__(256, 1) void k_gram(GramParams p) {
         rsum[rt][i] = fmaf(acc[rt][i], w, rsum[rt][i]);
         cs = fmaf(acc[rt][i], wrow[rt][i], cs);
       }
-    cs += xor32(cs);
-    // both lane halves hold the sum; each writes its own copy (no branch, so
-    // the step stays one scheduling region).  t = -1 (the empty carried tile
+    // each lane half stores the sum over its 16 rows; the flush adds the two
+    // halves (no cross-lane exchange here).  t = -1 (the empty carried tile
     // before the first step) writes zeros into the buffer of step 2, which
     // overwrites them before it is flushed.
     colred[(t + 3) % 3][wave][hf][ct * 32 + l32] = cs;
@@ -164,8 +168,9 @@ __global__ __launch_bounds__(256, 1) void k_gram(GramParams p) {
   auto flush = [&](int t) {
     if (tid < COLS && (t >> 1) >= 1) {
       const int c = col0(t) + tid;
-      const float v = colred[t % 3][0][0][tid] + colred[t % 3][1][0][tid] + colred[t % 3][2][0][tid] +
-                      colred[t % 3][3][0][tid];
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v += colred[t % 3][w][0][tid] + colred[t % 3][w][1][tid];
       if (c < n) p.part[(head * p.nsmax + (t >> 1) - 1) * (long)p.cap + c] = v;
     }
   };
@@ -188,48 +193,106 @@ __global__ __launch_bounds__(256, 1) void k_gram(GramParams p) {
   for (int a = 0; a < AHEAD; ++a) stream(col0(min(a, nsteps - 1)), a);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_KEEP));
   __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st % NBUF;
-    if (st >= 2) flush(st - 2);
-    stream(col0(min(st + AHEAD, nsteps - 1)), (st + AHEAD) % NBUF);
+  if constexpr (kFast) {
+    // Step st reads ring slot st % 4 and copies block st+2 into slot
+    // (st+2) % 4, last read in step st-2.  One barrier per step, before
+    // tile 3: by then block st+1 has landed (each thread waits for its own
+    // copies, the barrier for everyone's), so tile 3 can prefetch tile 0 of
+    // block st+1; and every wave is past step st-1, which makes the next
+    // step's copy into slot (st+3) % 4 safe.
+    // Group j of tile ct: the two matrix-core instructions of tile ct for
+    // k-chunk j, one eighth of the previous tile's fold (4 row and 4 column
+    // FMAs), the LDS read of chunk j of the next tile into the buffer the
+    // previous tile released, and (tile 0) one of the step's copies.  Each
+    // group is pinned by a scheduling barrier.
     Frag<NC> bq[2];
-    read_b(bq[0], buf, 0);
+    read_b(bq[0], 0, 0);
+    for (int st = 0; st < nsteps; ++st) {
+      const int buf = st % NBUF, nbuf = (st + 1) % NBUF, dbuf = (st + AHEAD) % NBUF;
+      if (st >= 2) flush(st - 2);
+      const int c0n = col0(min(st + AHEAD, nsteps - 1));
+      const char* src = kb + (long)min(c0n + (tid >> 1), n - 1) * RB + schunk_off;
+      const char* dst = lds_raw + dbuf * STAGE + wave * 1024;
+      float wt[4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      if (ct < 3) read_b(bq[(ct + 1) & 1], buf, ct + 1);
-      const float w = wcol[buf][ct * 32 + l32];
+      for (int ct = 0; ct < 4; ++ct) wt[ct] = wcol[buf][ct * 32 + l32];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        f32x16_t z;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) z[i] = 0.f;
-        acc[ct & 1][rt] = mfma_tile<E, NC>(af[rt], bq[ct & 1], z);
-      }
-      if (ct == 0) fold(acc[1], w_carry, 3, st - 1);
-      else fold(acc[(ct - 1) & 1], wcol[buf][(ct - 1) * 32 + l32], ct - 1, st);
-      if (ct == 3) w_carry = w;
-    }
-    if constexpr (NC == 8 && E::kBytes == 2) {
-      // Schedule of a step: tile 0's LDS reads, then per tile its 16
-      // matrix-core instructions interleaved with the next tile's 8 LDS reads
-      // and the previous tile's epilogue FMAs.
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (ct < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      for (int ct = 0; ct < 4; ++ct) {
+        if (ct == 3) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_KEEP));
+          __syncthreads();
         }
+        const int cur = ct & 1, prv = cur ^ 1;
+        const float wp = ct == 0 ? w_carry : wt[ct - 1];
+        float cs0 = 0.f, cs1 = 0.f, cs2 = 0.f, cs3 = 0.f;
+        const char* nx = ct < 3 ? lds_raw + buf * STAGE + rdbase + (ct + 1) * 1024
+                                : lds_raw + nbuf * STAGE + rdbase;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (ct == 0) {
+            dma_lds16(src + j * 32, dst + j * 4096);
+            if (j == 0) dma_lds4(wv + c0n + (wave & 1) * 64 + lane, &wcol[dbuf][(wave & 1) * 64]);
+          }
+          const bf16x8_t bj = __builtin_bit_cast(bf16x8_t, bq[cur].c[j]);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            f32x16_t c = acc[cur][rt];
+            if (j == 0) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) c[i] = 0.f;
+            }
+            acc[cur][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, af[rt].c[j]), bj, c, 0, 0, 0);
+          }
+          const int i0 = 2 * j, i1 = 2 * j + 1;
+          rsum[0][i0] = fmaf(acc[prv][0][i0], wp, rsum[0][i0]);
+          rsum[0][i1] = fmaf(acc[prv][0][i1], wp, rsum[0][i1]);
+          rsum[1][i0] = fmaf(acc[prv][1][i0], wp, rsum[1][i0]);
+          rsum[1][i1] = fmaf(acc[prv][1][i1], wp, rsum[1][i1]);
+          cs0 = fmaf(acc[prv][0][i0], wrow[0][i0], cs0);
+          cs1 = fmaf(acc[prv][0][i1], wrow[0][i1], cs1);
+          cs2 = fmaf(acc[prv][1][i0], wrow[1][i0], cs2);
+          cs3 = fmaf(acc[prv][1][i1], wrow[1][i1], cs3);
+          bq[prv].c[j] = *reinterpret_cast<const u32x4_t*>(nx + j * 4096);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const float cs = (cs0 + cs1) + (cs2 + cs3);
+        // the previous tile: tile 3 of step st-1 when ct = 0, else tile ct-1
+        colred[((ct == 0 ? st - 1 : st) + 3) % 3][wave][hf][(ct == 0 ? 3 : ct - 1) * 32 + l32] = cs;
+        if (ct == 3) w_carry = wt[3];
+      }
     }
-    // block st+1 has landed once only the newer blocks may still be in flight
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_KEEP));
-    __syncthreads();
+  } else {
+    for (int st = 0; st < nsteps; ++st) {
+      const int buf = st % NBUF;
+      if (st >= 2) flush(st - 2);
+      stream(col0(min(st + AHEAD, nsteps - 1)), (st + AHEAD) % NBUF);
+      Frag<NC> bq[2];
+      read_b(bq[0], buf, 0);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        if (ct < 3) read_b(bq[(ct + 1) & 1], buf, ct + 1);
+        const float w = wcol[buf][ct * 32 + l32];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          f32x16_t z;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) z[i] = 0.f;
+          acc[ct & 1][rt] = mfma_tile<E, NC>(af[rt], bq[ct & 1], z);
+        }
+        if (ct == 0) fold(acc[1], w_carry, 3, st - 1);
+        else fold(acc[(ct - 1) & 1], wcol[buf][(ct - 1) * 32 + l32], ct - 1, st);
+        if (ct == 3) w_carry = w;
+      }
+      // block st+1 has landed once only the newer blocks may still be in flight
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_KEEP));
+      __syncthreads();
+    }
   }
+  // every copy has landed (the ring's last copies overlap the reduction
+  // buffer below) before anyone writes it
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
   fold(acc[1], w_carry, 3, nsteps - 1);
 
   // row sums: lane (hf, l32) of wave w holds rows w*64 + 32rt + tile_row(i, hf)
