@@ -63,6 +63,10 @@ struct ScoreWs {
   size_t bytes;
 };
 
+// per-head stride of the inverse-norm buffer: the Gram kernels read weights
+// in blocks of up to 512 keys
+int gram_wstride(int cap) { return (cap + 511) / 512 * 512; }
+
 ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap) {
   const size_t heads = (size_t)b * hkv;
   const int nchunk = (cap + kChunk - 1) / kChunk;
@@ -74,7 +78,7 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap) {
   w.rstat = c.take<float2>(heads * mp);
   w.spart = c.take<float>(heads * nchunk * d);
   w.ssum = c.take<float>(heads * d);
-  w.inv_norm = c.take<float>(heads * nchunk * kChunk);
+  w.inv_norm = c.take<float>(heads * gram_wstride(cap));
   w.imp = c.take<float>(heads * cap);
   w.z = c.take<float>(heads * cap);
   w.nsmax = ((cap + 255) / 256) / 2;
@@ -130,6 +134,7 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
   p.spart = ws.spart;
   p.ssum = ws.ssum;
   p.inv_norm = ws.inv_norm;
+  p.wstride = gram_wstride(cap);
   p.logits = nullptr;
   p.err = ws.err;
   p.i_out = i_out ? i_out : ws.imp;
@@ -149,7 +154,7 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
     gp.cap = cap;
     gp.lambda = lambda;
     gp.inv_norm = ws.inv_norm;
-    gp.wstride = p.nchunk * kChunk;
+    gp.wstride = p.wstride;
     gp.i_in = p.i_out;
     gp.r_out = r_out;
     gp.z_out = z_out;

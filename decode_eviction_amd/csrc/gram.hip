@@ -317,6 +317,228 @@ __global__ __launch_bounds__(256, 1) void k_gram(GramParams p) {
   }
 }
 
+// The same sweep for bf16 keys of 128 dimensions at large n, over blocks of
+// 512 keys: each wave keeps 128 rows resident, so every B fragment read from
+// LDS feeds 32 matrix-core instructions and the per-step copies and barrier
+// are spread over twice the work.  A wave's rows form two sets of 64 whose
+// accumulators alternate: the matrix-core instructions of one set run while
+// the other set's fp32 fold executes.  Weights at positions >= n are
+// replaced by 0 in registers (the inverse-norm buffer is only written up to
+// the end of the 256-key chunk holding n-1).
+__global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
+  using E = BF16;
+  constexpr int D = 128;
+  using G = Geo<E, D>;
+  constexpr int NC = G::kNC;             // 8 chunk pairs
+  constexpr int RB = G::kRowBytes;       // 256
+  constexpr int ROWS = 512;              // rows per work-group: 4 waves x 128
+  constexpr int COLS = 128;              // columns per step: 4 tiles of 32
+  constexpr int SPB = ROWS / COLS;       // steps per column block
+  constexpr int STAGE = COLS * RB;
+  constexpr int NBUF = 4, AHEAD = 2;
+  constexpr int VM_STEP = NC + 1;        // copies per thread per step
+  constexpr int VM_KEEP = (AHEAD - 1) * VM_STEP;
+  constexpr int RED = 33;
+  constexpr int LDSB = NBUF * STAGE > ROWS * RED * 4 ? NBUF * STAGE : ROWS * RED * 4;
+  __shared__ __attribute__((aligned(16))) char lds_raw[LDSB];
+  __shared__ __attribute__((aligned(16))) float wcol[NBUF][COLS];
+  __shared__ float colred[3][4][2][COLS];
+
+  const int nrb = (p.cap + ROWS - 1) / ROWS;
+  const int W = xcd_major(blockIdx.x, nrb * p.hkv * p.b);
+  const int rb = W % nrb, hh = W / nrb;
+  const int h = hh % p.hkv, bi = hh / p.hkv;
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = min(p.lengths[bi], p.cap);
+  const int r0 = rb * ROWS;
+  if (r0 >= n) return;
+  const int nb = (n + ROWS - 1) / ROWS;
+  const int nsteps = SPB * gram_blocks(rb, nb);
+  const long head = (long)bi * p.hkv + h;
+  const char* kb = p.k + head * (long)p.cap * RB;
+  const float* wv = p.inv_norm + head * (long)p.wstride;
+  auto col0 = [&](int t) {
+    int J = rb + t / SPB;
+    J -= J >= nb ? nb : 0;
+    return J * ROWS + (t % SPB) * COLS;
+  };
+
+  Frag<NC> af[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int row = r0 + wave * 128 + 32 * rt + l32;
+    load_frag<E, D>(af[rt], kb, row, row < n, hf);
+  }
+  float wrow[4][16];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rbase = r0 + wave * 128 + 32 * rt + 8 * q + 4 * hf;
+      const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(wv + rbase);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wrow[rt][4 * q + e] = rbase + e < n ? w4[e] : 0.f;
+    }
+
+  // staged layout and copies as in k_gram (slot (c/2)*256 + 2r + ((c%2)^sw(r)))
+  auto sw = [](int r) { return ((r >> 2) ^ (r >> 3)) & 1; };
+  const int schunk_off = ((tid & 1) ^ sw(tid >> 1)) * 16;
+  const int rdbase = (2 * l32 + (hf ^ sw(l32))) * 16;
+  auto stream_all = [&](int c0, int buf) {
+    const char* src = kb + (long)min(c0 + (tid >> 1), n - 1) * RB + schunk_off;
+#pragma unroll
+    for (int it = 0; it < NC; ++it) dma_lds16(src + it * 32, lds_raw + buf * STAGE + it * 4096 + wave * 1024);
+    dma_lds4(wv + c0 + (wave & 1) * 64 + lane, &wcol[buf][(wave & 1) * 64]);
+  };
+  auto read_b = [&](Frag<NC>& f, const char* base) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) f.c[j] = *reinterpret_cast<const u32x4_t*>(base + j * 4096);
+  };
+  auto flush = [&](int t) {
+    if (tid < COLS && t / SPB >= 1) {
+      const int c = col0(t) + tid;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v += colred[t % 3][w][0][tid] + colred[t % 3][w][1][tid];
+      if (c < n) p.part[(head * p.nsmax + t / SPB - 1) * (long)p.cap + c] = v;
+    }
+  };
+
+  float rsum[4][16];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rsum[rt][i] = 0.f;
+  f32x16_t acc[2][2];  // [row set][row tile within the set]
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[s2][rt][i] = 0.f;
+  float w_carry = 0.f, csA_carry = 0.f;
+
+  // fold part j of row set S (tiles 2S, 2S+1): 4 row FMAs, 4 column FMAs
+  auto fold_part = [&](int S, int j, float w, float& c0, float& c1, float& c2, float& c3) {
+    const int i0 = 2 * j, i1 = 2 * j + 1;
+    rsum[2 * S][i0] = fmaf(acc[S][0][i0], w, rsum[2 * S][i0]);
+    rsum[2 * S][i1] = fmaf(acc[S][0][i1], w, rsum[2 * S][i1]);
+    rsum[2 * S + 1][i0] = fmaf(acc[S][1][i0], w, rsum[2 * S + 1][i0]);
+    rsum[2 * S + 1][i1] = fmaf(acc[S][1][i1], w, rsum[2 * S + 1][i1]);
+    c0 = fmaf(acc[S][0][i0], wrow[2 * S][i0], c0);
+    c1 = fmaf(acc[S][0][i1], wrow[2 * S][i1], c1);
+    c2 = fmaf(acc[S][1][i0], wrow[2 * S + 1][i0], c2);
+    c3 = fmaf(acc[S][1][i1], wrow[2 * S + 1][i1], c3);
+  };
+  auto mfma2 = [&](int S, int j, const Frag<NC>& b) {
+    const bf16x8_t bj = __builtin_bit_cast(bf16x8_t, b.c[j]);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      f32x16_t c = acc[S][rt];
+      if (j == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[i] = 0.f;
+      }
+      acc[S][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8_t, af[2 * S + rt].c[j]), bj, c, 0, 0, 0);
+    }
+  };
+
+#pragma unroll
+  for (int a = 0; a < AHEAD; ++a) stream_all(col0(min(a, nsteps - 1)), a);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_KEEP));
+  __syncthreads();
+  Frag<NC> bq[2];
+  read_b(bq[0], lds_raw + rdbase);
+  // Ring and barrier as in k_gram: step st reads slot st % 4, copies block
+  // st+2 into slot (st+2) % 4 during tile 0, and waits for block st+1 (own
+  // copies, then a barrier) before tile 3, which prefetches its first tile.
+  // Tile ct: phase A = row set 0 of tile ct with the fold of row set 1 of
+  // the previous tile (and that tile's column sums completed); phase B =
+  // row set 1 of tile ct with the fold of row set 0 of tile ct.
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st % NBUF, nbuf = (st + 1) % NBUF, dbuf = (st + AHEAD) % NBUF;
+    if (st >= 2) flush(st - 2);
+    const int c0 = col0(st);
+    const int c0n = col0(min(st + AHEAD, nsteps - 1));
+    const char* src = kb + (long)min(c0n + (tid >> 1), n - 1) * RB + schunk_off;
+    const char* dst = lds_raw + dbuf * STAGE + wave * 1024;
+    float wt[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) wt[ct] = c0 + ct * 32 + l32 < n ? wcol[buf][ct * 32 + l32] : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (ct == 3) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_KEEP));
+        __syncthreads();
+      }
+      const int cur = ct & 1, prv = cur ^ 1;
+      const char* nx = ct < 3 ? lds_raw + buf * STAGE + rdbase + (ct + 1) * 1024
+                              : lds_raw + nbuf * STAGE + rdbase;
+      const float wprev = ct == 0 ? w_carry : wt[ct - 1];
+      // phase A
+      float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (ct == 0) {
+          dma_lds16(src + j * 32, dst + j * 4096);
+          if (j == 0) dma_lds4(wv + c0n + (wave & 1) * 64 + lane, &wcol[dbuf][(wave & 1) * 64]);
+        }
+        // B fragments only feed the matrix cores: keep them in accumulation
+        // registers (so the fold's fp32 state fits in the ordinary ones); the
+        // constraint sits at the chunk's first use, where its read is waited for
+        asm volatile("" : "+a"(bq[cur].c[j]));
+        mfma2(0, j, bq[cur]);
+        fold_part(1, j, wprev, b0, b1, b2, b3);
+        bq[prv].c[j] = *reinterpret_cast<const u32x4_t*>(nx + j * 4096);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      {
+        const float cs = csA_carry + ((b0 + b1) + (b2 + b3));
+        colred[((ct == 0 ? st - 1 : st) + 3) % 3][wave][hf][(ct == 0 ? 3 : ct - 1) * 32 + l32] = cs;
+      }
+      // phase B
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        mfma2(1, j, bq[cur]);
+        fold_part(0, j, wt[ct], a0, a1, a2, a3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      csA_carry = (a0 + a1) + (a2 + a3);
+      if (ct == 3) w_carry = wt[3];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  {
+    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fold_part(1, j, w_carry, b0, b1, b2, b3);
+    colred[(nsteps - 1) % 3][wave][hf][3 * 32 + l32] = csA_carry + ((b0 + b1) + (b2 + b3));
+  }
+  float* red = reinterpret_cast<float*>(lds_raw);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[(wave * 128 + 32 * rt + tile_row(i, hf)) * RED + l32] = rsum[rt][i];
+  __syncthreads();
+  if (nsteps >= 2) flush(nsteps - 2);
+  flush(nsteps - 1);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int row = tid + 256 * k, j = r0 + row;
+    if (j < n) {
+      float s = 0.f;
+#pragma unroll 8
+      for (int l = 0; l < 32; ++l) s += red[row * RED + l];
+      const float w = wv[j];
+      p.rs[head * p.cap + j] = s - (w > 0.f ? 1.0f / w : 0.f);
+    }
+  }
+}
+
 // R and Z per key: own row sums plus the column sums of the blocks that
 // computed this key's block as their column block, in slot order.
 __global__ __launch_bounds__(256) void k_gram_fin(GramParams p) {
@@ -330,7 +552,7 @@ __global__ __launch_bounds__(256) void k_gram_fin(GramParams p) {
   __syncthreads();
   const int j = chunk * 256 + tid;
   if (j < n) {
-    const int nb = (n + 255) / 256, J = j / 256, ns = nb / 2;
+    const int nb = (n + p.bs - 1) / p.bs, J = j / p.bs, ns = nb / 2;
     // slot s holds the contribution of block J - (s+1); the slot of
     // distance nb/2 (nb even) is filled only for J >= nb/2
     const int nfull = (nb - 1) / 2;
@@ -370,9 +592,16 @@ static hipError_t gram_t(const GramParams& p, hipStream_t s, Trace* tr) {
   return launch_k(k_gram<E, D>, dim3(blocks), dim3(256), s, tr, p);
 }
 
-hipError_t launch_gram(int dt, int d, const GramParams& p, hipStream_t s, Trace* tr) {
+// bf16 keys of 128 dimensions use 512-key blocks once there are at least 16
+// of them per head at full length (enough work-groups to fill the chip at the
+// shapes this path serves); everything else uses 256-key blocks.
+hipError_t launch_gram(int dt, int d, const GramParams& p_in, hipStream_t s, Trace* tr) {
+  GramParams p = p_in;
+  const bool big = dt == 0 && d == 128 && p.cap >= 8192;
+  p.bs = big ? 512 : 256;
   hipError_t e;
-  if (dt == 0) e = d == 64 ? gram_t<BF16, 64>(p, s, tr) : gram_t<BF16, 128>(p, s, tr);
+  if (big) e = launch_k(k_gram512, dim3((p.cap + 511) / 512 * p.hkv * p.b), dim3(256), s, tr, p);
+  else if (dt == 0) e = d == 64 ? gram_t<BF16, 64>(p, s, tr) : gram_t<BF16, 128>(p, s, tr);
   else e = d == 64 ? gram_t<F32, 64>(p, s, tr) : gram_t<F32, 128>(p, s, tr);
   if (e != hipSuccess) return e;
   return launch_k(k_gram_fin, dim3((p.cap + 255) / 256, p.hkv, p.b), dim3(256), s, tr, p);

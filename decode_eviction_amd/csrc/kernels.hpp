@@ -34,7 +34,8 @@ struct ScoreParams {
   float2* rstat;            // [b][Hkv][mp]          (max, 1/sum), base 2
   float* spart;             // [b][Hkv][nchunk][d]   keysum: chunk sums of unit keys
   float* ssum;              // [b][Hkv][d]           keysum: sum of unit keys
-  float* inv_norm;          // [b][Hkv][nchunk*kChunk] gram: 1/||k_j||, 0 past n
+  float* inv_norm;          // [b][Hkv][wstride]     gram: 1/||k_j||, 0 past n in its chunk
+  int wstride;              // per-head stride of inv_norm: cap rounded up to 512
   float* logits;            // [b][Hkv][g][nchunk*kChunk]  cut: logits in base-2 units
   int32_t* err;             // error word
   // outputs (never null; the host substitutes workspace buffers)
@@ -49,15 +50,16 @@ struct GramParams {
   const int32_t* lengths;
   int b, hkv, cap;
   float lambda;
-  const float* inv_norm;    // [b][Hkv][wstride], 0 past n
-  int wstride;              // per-head stride of inv_norm (multiple of 256)
+  const float* inv_norm;    // [b][Hkv][wstride]; only positions < n are read as weights
+  int wstride;              // per-head stride of inv_norm (multiple of 512)
   const float* i_in;        // [b][Hkv][cap]
   float* r_out;             // nullable
   float* z_out;
   uint32_t* hist;           // nullable [b][Hkv][kHistBins]
   float* rs;                // [b][Hkv][cap]  a key's own-block row sums minus its self term
   float* part;              // [b][Hkv][nsmax][cap]  column sums by block distance - 1
-  int nsmax;                // (ceil(cap / 256)) / 2
+  int nsmax;                // (ceil(cap / 256)) / 2: slots per head (enough for any block size)
+  int bs;                   // symmetric block size of the launched Gram kernel (256 or 512)
 };
 
 constexpr int kSelChunk = 512;     // positions per compaction work-group

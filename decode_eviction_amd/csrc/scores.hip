@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
       const int tok = tok0 + 32 * tt + l32;
       // every slot of the chunk is written (0 past n): the Gram kernel streams
       // whole 128-key blocks of weights
-      if (MODE == kModeGram && hf == 0) p.inv_norm[head * (long)p.nchunk * kChunk + tok] = inv[tt];
+      if (MODE == kModeGram && hf == 0) p.inv_norm[head * (long)p.wstride + tok] = inv[tt];
     }
     if constexpr (MODE == kModeKeysum) {
       // this chunk's sum of unit keys: per lane its two tokens, then a
