@@ -227,6 +227,11 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// m0 is named as clobbered for the reader; the compiler keeps no value of its
+// own in m0 in the kernels that use these (checked in their assembly), and
+// warns that a reserved register is listed.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_lds16(const void* g, const void* lds_wave_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :
@@ -239,6 +244,8 @@ __device__ __forceinline__ void dma_lds4(const void* g, const void* lds_wave_bas
                : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_offset(lds_wave_base)))
                : "m0");
 }
+
+#pragma clang diagnostic pop
 
 // 2^x on the transcendental unit (v_exp_f32)
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -369,65 +369,62 @@ __global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
       wbase += (uint32_t)__popcll(bin);
     }
     __syncthreads();
-    // refinement inside the bin by wave 0 alone (no block barriers): a
-    // wave-private histogram, lanes own 32 consecutive bins each
-    if (wave == 0) {
-      while (lo < hi) {
-        const uint32_t span = hi - lo;
-        const int bits = 32 - __clz(span);
-        const int shift = bits > 11 ? bits - 11 : 0;
-#pragma unroll
-        for (int e = 0; e < kSelBins / kWave; ++e) hist[lane * (kSelBins / kWave) + e] = 0u;
-        wave_lds_sync();
-        for (uint32_t c = lane; c < nc; c += kWave) {
-          const uint32_t off = cand_key[c] - lo;
-          if (off <= span) atomicAdd(&hist[off >> shift], 1u);
-        }
-        wave_lds_sync();
-        uint32_t mysum = 0;
-#pragma unroll
-        for (int e = 0; e < kSelBins / kWave; ++e) mysum += hist[lane * (kSelBins / kWave) + e];
-        // inclusive suffix sum over lanes: keys in bins at or above my first bin
-        uint32_t suf = mysum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_down(suf, o, 64);
-          if (lane + o < 64) suf += y;
-        }
-        const uint32_t above_me = suf - mysum;  // keys in higher lanes' bins
-        const bool mine_has = above_me < need && suf >= need;
-        const uint64_t who = __ballot(mine_has);
-        const int src = __ffsll((unsigned long long)who) - 1;
-        uint32_t bin = 0, above = 0;
-        if (lane == src) {
-          uint32_t acc = above_me;
-          for (int e = kSelBins / kWave - 1; e >= 0; --e) {
-            const uint32_t cnt_e = hist[lane * (kSelBins / kWave) + e];
-            if (acc < need && acc + cnt_e >= need) {
-              bin = lane * (kSelBins / kWave) + e;
-              above = acc;
-              break;
-            }
-            acc += cnt_e;
-          }
-        }
-        bin = __shfl(bin, src, 64);
-        above = __shfl(above, src, 64);
-        wave_lds_sync();  // every lane is done reading before the next round clears the bins
-        need -= above;
-        const uint64_t nlo = (uint64_t)lo + ((uint64_t)bin << shift);
-        const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
-        lo = (uint32_t)nlo;
-        hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
-      }
-      const uint32_t kth = lo;
-      for (uint32_t c = lane; c < nc; c += kWave) {
+    // refinement inside the bin: block-wide histogram rounds over the
+    // candidates (each narrows [lo, hi] by 11 bits) until at most 64 of them
+    // remain in range; those are gathered and wave 0 ranks them (larger key,
+    // or equal key at a lower position, first): rank need-1 is the threshold.
+    uint32_t inr = nc;
+    while (lo < hi && inr > (uint32_t)kWave) {
+      refine_round<kRegWaves>(lo, hi, need, hist, wsum[0], bc, tid, [&](auto f) {
+        for (uint32_t c = tid; c < nc; c += kRegThreads) f(cand_key[c]);
+      });
+      inr = hist[bc[0]];  // candidates in the new range
+    }
+    if (lo < hi) {
+      __shared__ uint32_t rk[kWave];
+      __shared__ int32_t rp[kWave];
+      __shared__ uint32_t nr_s;
+      __syncthreads();
+      if (tid == 0) nr_s = 0u;
+      __syncthreads();
+      for (uint32_t c = tid; c < nc; c += kRegThreads) {
         const uint32_t k = cand_key[c];
-        const int ch = cand_pos[c] / kSelChunk;
-        if (k > kth) atomicAdd(&ccnt[ch][0], 1u);
-        else if (k == kth) atomicAdd(&ccnt[ch][1], 1u);
+        if (k >= lo && k <= hi) {
+          const uint32_t slot = atomicAdd(&nr_s, 1u);
+          rk[slot] = k;
+          rp[slot] = cand_pos[c];
+        }
       }
-      wave_lds_sync();
+      __syncthreads();
+      if (wave == 0) {
+        const uint32_t nr = nr_s;
+        const uint32_t mk = lane < (int)nr ? rk[lane] : 0u;
+        const int32_t mpos = lane < (int)nr ? rp[lane] : 0x7fffffff;
+        uint32_t rank = 0;
+        for (uint32_t c = 0; c < nr; ++c)
+          rank += (rk[c] > mk || (rk[c] == mk && rp[c] < mpos)) ? 1u : 0u;
+        const uint64_t who = __ballot(lane < (int)nr && rank == need - 1);
+        const uint32_t kth = __shfl(mk, __ffsll((unsigned long long)who) - 1, 64);
+        uint32_t gtk = 0;
+        for (uint32_t c = 0; c < nr; ++c) gtk += rk[c] > kth ? 1u : 0u;
+        if (lane == 0) {
+          bc[0] = kth;
+          bc[1] = need - gtk;  // copies of the threshold key still to keep
+        }
+      }
+      __syncthreads();
+      lo = hi = bc[0];
+      need = bc[1];
+    }
+    const uint32_t kth = lo;
+    for (uint32_t c = tid; c < nc; c += kRegThreads) {
+      const uint32_t k = cand_key[c];
+      const int ch = cand_pos[c] / kSelChunk;
+      if (k > kth) atomicAdd(&ccnt[ch][0], 1u);
+      else if (k == kth) atomicAdd(&ccnt[ch][1], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
       uint32_t gt = 0, eq = 0;
       // chunk c = round c / 2, waves of half c % 2
       const int i = lane / kChunksPerRound, w0 = (lane % kChunksPerRound) * (kRegWaves / kChunksPerRound);
