@@ -318,37 +318,45 @@ __global__ __launch_bounds__(256, 1) void k_gram(GramParams p) {
 }
 
 // The same sweep for bf16 keys of 128 dimensions at large n, over blocks of
-// 512 keys: each wave keeps 128 rows resident, so every B fragment read from
-// LDS feeds 32 matrix-core instructions and the per-step copies and barrier
-// are spread over twice the work.  A wave's rows form two sets of 64 whose
-// accumulators alternate: the matrix-core instructions of one set run while
-// the other set's fp32 fold executes.  Weights at positions >= n are
-// replaced by 0 in registers (the inverse-norm buffer is only written up to
-// the end of the 256-key chunk holding n-1).
+// 512 keys, on 16x16x32 matrix-core tiles.  Each wave keeps 128 rows
+// resident (eight 16-row tiles) in two sets of 64; a set times a 32-column
+// tile is eight independent accumulator chains, so the matrix cores stay
+// busy while the other set's fp32 fold runs beside them.  In the 16x16
+// output layout a lane holds 4 rows of each tile, so the fold's per-lane row
+// sums and row weights take 32 registers each.  Every B fragment read from
+// LDS feeds 32 matrix-core instructions, and the per-step copies and barrier
+// are spread over a 512-key block.  Weights at positions >= n are replaced by
+// 0 in registers (the inverse-norm buffer is only written up to the end of
+// the 256-key chunk holding n-1).
+//
+// 16x16x32 tiles: lane l supplies row (or column) l % 16 and 16-byte chunk
+// l / 16 of each 32-dimension k-step; result register i of lane l is row
+// 4 (l / 16) + i, column l % 16.  A and B fragments use the same chunk
+// assignment, so their dot products cover every dimension exactly once.
 __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
-  using E = BF16;
-  constexpr int D = 128;
-  using G = Geo<E, D>;
-  constexpr int NC = G::kNC;             // 8 chunk pairs
-  constexpr int RB = G::kRowBytes;       // 256
+  constexpr int RB = 256;                // bytes per key (128 bf16)
   constexpr int ROWS = 512;              // rows per work-group: 4 waves x 128
   constexpr int COLS = 128;              // columns per step: 4 tiles of 32
   constexpr int SPB = ROWS / COLS;       // steps per column block
   constexpr int STAGE = COLS * RB;
   constexpr int NBUF = 4, AHEAD = 2;
-  constexpr int VM_STEP = NC + 1;        // copies per thread per step
+  constexpr int NCP = 8;                 // 32-byte chunk pairs per key
+  constexpr int VM_STEP = NCP + 1;       // copies per thread per step
   constexpr int VM_KEEP = (AHEAD - 1) * VM_STEP;
-  constexpr int RED = 33;
+  constexpr int RED = 17;                // row-sum partials per row: 16 column residues
+  constexpr int CPS = 20;                // column partials: 16 per column (4 waves x 4 lane groups), padded
   constexpr int LDSB = NBUF * STAGE > ROWS * RED * 4 ? NBUF * STAGE : ROWS * RED * 4;
   __shared__ __attribute__((aligned(16))) char lds_raw[LDSB];
   __shared__ __attribute__((aligned(16))) float wcol[NBUF][COLS];
-  __shared__ float colred[3][4][2][COLS];
+  // [step % 3][column][wave * 4 + lane group]: the 64 lanes of a write hit
+  // 64 distinct banks, and a column's 16 partials are four aligned 16-byte reads
+  __shared__ __attribute__((aligned(16))) float colred[3][COLS][CPS];
 
   const int nrb = (p.cap + ROWS - 1) / ROWS;
   const int W = xcd_major(blockIdx.x, nrb * p.hkv * p.b);
   const int rb = W % nrb, hh = W / nrb;
   const int h = hh % p.hkv, bi = hh / p.hkv;
-  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = min(p.lengths[bi], p.cap);
   const int r0 = rb * ROWS;
@@ -364,93 +372,125 @@ __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
     return J * ROWS + (t % SPB) * COLS;
   };
 
-  Frag<NC> af[4];
+  // A fragments: row tile rt (16 rows), k-step j: row l % 16, chunk 4j + l / 16
+  u32x4_t af[8][4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int row = r0 + wave * 128 + 32 * rt + l32;
-    load_frag<E, D>(af[rt], kb, row, row < n, hf);
+  for (int rt = 0; rt < 8; ++rt) {
+    const int row = r0 + wave * 128 + 16 * rt + c16;
+    const char* src = kb + (long)(row < n ? row : 0) * RB + g * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) af[rt][j] = row < n ? ld16(src + 64 * j) : zero4();
   }
-  float wrow[4][16];
+  float wrow[8][4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < 8; ++rt) {
+    const int rbase = r0 + wave * 128 + 16 * rt + 4 * g;
+    const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(wv + rbase);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int rbase = r0 + wave * 128 + 32 * rt + 8 * q + 4 * hf;
-      const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(wv + rbase);
+    for (int e = 0; e < 4; ++e) wrow[rt][e] = rbase + e < n ? w4[e] : 0.f;
+  }
+  // A fragments only feed the matrix cores: keep them in accumulation registers
 #pragma unroll
-      for (int e = 0; e < 4; ++e) wrow[rt][4 * q + e] = rbase + e < n ? w4[e] : 0.f;
-    }
+  for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(af[rt][j]));
 
-  // staged layout and copies as in k_gram (slot (c/2)*256 + 2r + ((c%2)^sw(r)))
+  // staged layout and copies as in k_gram: chunk c of key r at 16-byte slot
+  // (c/2)*256 + 2r + ((c%2)^sw(r)); a 16-lane group reads one chunk of 16
+  // consecutive keys, which covers all 64 banks once
   auto sw = [](int r) { return ((r >> 2) ^ (r >> 3)) & 1; };
   const int schunk_off = ((tid & 1) ^ sw(tid >> 1)) * 16;
-  const int rdbase = (2 * l32 + (hf ^ sw(l32))) * 16;
+  const int rdbase = (g >> 1) * 4096 + (2 * c16 + ((g & 1) ^ sw(c16))) * 16;
   auto stream_all = [&](int c0, int buf) {
     const char* src = kb + (long)min(c0 + (tid >> 1), n - 1) * RB + schunk_off;
 #pragma unroll
-    for (int it = 0; it < NC; ++it) dma_lds16(src + it * 32, lds_raw + buf * STAGE + it * 4096 + wave * 1024);
+    for (int it = 0; it < NCP; ++it) dma_lds16(src + it * 32, lds_raw + buf * STAGE + it * 4096 + wave * 1024);
     dma_lds4(wv + c0 + (wave & 1) * 64 + lane, &wcol[buf][(wave & 1) * 64]);
   };
-  auto read_b = [&](Frag<NC>& f, const char* base) {
-#pragma unroll
-    for (int j = 0; j < NC; ++j) f.c[j] = *reinterpret_cast<const u32x4_t*>(base + j * 4096);
+  // B fragment of column half h2 (16 keys) of 32-column tile ct, k-step j
+  auto b_addr = [&](int buf, int ct, int h2, int j) {
+    return lds_raw + buf * STAGE + rdbase + j * 8192 + ct * 1024 + h2 * 512;
   };
-  auto flush = [&](int t) {
+  // column sums of step t: the first 128 threads add a column's 16 partials;
+  // the reads are issued early and summed later so their latency overlaps
+  // matrix-core work
+  f32x4_t fq[4];
+  auto flush_issue = [&](int t) {
+    if (tid < COLS && t / SPB >= 1) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) fq[k] = *reinterpret_cast<const f32x4_t*>(&colred[t % 3][tid][4 * k]);
+    }
+  };
+  auto flush_finish = [&](int t) {
     if (tid < COLS && t / SPB >= 1) {
       const int c = col0(t) + tid;
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) v += colred[t % 3][w][0][tid] + colred[t % 3][w][1][tid];
+      const f32x4_t q2 = (fq[0] + fq[1]) + (fq[2] + fq[3]);
+      const float v = (q2[0] + q2[1]) + (q2[2] + q2[3]);
       if (c < n) p.part[(head * p.nsmax + t / SPB - 1) * (long)p.cap + c] = v;
     }
   };
+  auto flush = [&](int t) {
+    flush_issue(t);
+    flush_finish(t);
+  };
 
-  float rsum[4][16];
+  float rsum[8][4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) rsum[rt][i] = 0.f;
-  f32x16_t acc[2][2];  // [row set][row tile within the set]
+    for (int i = 0; i < 4; ++i) rsum[rt][i] = 0.f;
+  f32x4_t acc[2][4][2];  // [row set][row tile in the set][column half]
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[s2][rt][i] = 0.f;
-  float w_carry = 0.f, csA_carry = 0.f;
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[s2][rt][h2][i] = 0.f;
+  float w_carry[2] = {0.f, 0.f}, csA_carry[2] = {0.f, 0.f};
 
-  // fold part j of row set S (tiles 2S, 2S+1): 4 row FMAs, 4 column FMAs
-  auto fold_part = [&](int S, int j, float w, float& c0, float& c1, float& c2, float& c3) {
-    const int i0 = 2 * j, i1 = 2 * j + 1;
-    rsum[2 * S][i0] = fmaf(acc[S][0][i0], w, rsum[2 * S][i0]);
-    rsum[2 * S][i1] = fmaf(acc[S][0][i1], w, rsum[2 * S][i1]);
-    rsum[2 * S + 1][i0] = fmaf(acc[S][1][i0], w, rsum[2 * S + 1][i0]);
-    rsum[2 * S + 1][i1] = fmaf(acc[S][1][i1], w, rsum[2 * S + 1][i1]);
-    c0 = fmaf(acc[S][0][i0], wrow[2 * S][i0], c0);
-    c1 = fmaf(acc[S][0][i1], wrow[2 * S][i1], c1);
-    c2 = fmaf(acc[S][1][i0], wrow[2 * S + 1][i0], c2);
-    c3 = fmaf(acc[S][1][i1], wrow[2 * S + 1][i1], c3);
-  };
-  auto mfma2 = [&](int S, int j, const Frag<NC>& b) {
-    const bf16x8_t bj = __builtin_bit_cast(bf16x8_t, b.c[j]);
+  // fold row tile t4 of set S: 8 row-sum FMAs, 8 column-sum FMAs
+  auto fold_part = [&](int S, int t4, const float* w, float* cs) {
+    const int rt = 4 * S + t4;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      f32x16_t c = acc[S][rt];
-      if (j == 0) {
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) c[i] = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        rsum[rt][i] = fmaf(acc[S][t4][h2][i], w[h2], rsum[rt][i]);
+        cs[2 * h2 + (i & 1)] = fmaf(acc[S][t4][h2][i], wrow[rt][i], cs[2 * h2 + (i & 1)]);
       }
-      acc[S][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          __builtin_bit_cast(bf16x8_t, af[2 * S + rt].c[j]), bj, c, 0, 0, 0);
-    }
+  };
+  auto mfma8 = [&](int S, int j, const u32x4_t* b) {
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        f32x4_t c = acc[S][t4][h2];
+        if (j == 0) c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc[S][t4][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, af[4 * S + t4][j]), __builtin_bit_cast(bf16x8_t, b[h2]), c, 0, 0, 0);
+      }
   };
 
 #pragma unroll
   for (int a = 0; a < AHEAD; ++a) stream_all(col0(min(a, nsteps - 1)), a);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_KEEP));
   __syncthreads();
-  Frag<NC> bq[2];
-  read_b(bq[0], lds_raw + rdbase);
+  u32x4_t bq[2][4][2];  // [buffer][k-step][column half]
+  // column weights of the next step, read once its copies have landed
+  float wnext[4][2];
+  auto read_w = [&](int b) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) wnext[ct][h2] = wcol[b][ct * 32 + h2 * 16 + c16];
+  };
+  read_w(0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) bq[0][j][h2] = *reinterpret_cast<const u32x4_t*>(b_addr(0, 0, h2, j));
   // Ring and barrier as in k_gram: step st reads slot st % 4, copies block
   // st+2 into slot (st+2) % 4 during tile 0, and waits for block st+1 (own
   // copies, then a barrier) before tile 3, which prefetches its first tile.
@@ -459,70 +499,88 @@ __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
   // row set 1 of tile ct with the fold of row set 0 of tile ct.
   for (int st = 0; st < nsteps; ++st) {
     const int buf = st % NBUF, nbuf = (st + 1) % NBUF, dbuf = (st + AHEAD) % NBUF;
-    if (st >= 2) flush(st - 2);
+    if (st >= 2) flush_issue(st - 2);
     const int c0 = col0(st);
     const int c0n = col0(min(st + AHEAD, nsteps - 1));
     const char* src = kb + (long)min(c0n + (tid >> 1), n - 1) * RB + schunk_off;
     const char* dst = lds_raw + dbuf * STAGE + wave * 1024;
-    float wt[4];
+    float wt[4][2];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) wt[ct] = c0 + ct * 32 + l32 < n ? wcol[buf][ct * 32 + l32] : 0.f;
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int c = ct * 32 + h2 * 16 + c16;
+        wt[ct][h2] = c0 + c < n ? wnext[ct][h2] : 0.f;
+      }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       if (ct == 3) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_KEEP));
         __syncthreads();
+        read_w(nbuf);
       }
       const int cur = ct & 1, prv = cur ^ 1;
-      const char* nx = ct < 3 ? lds_raw + buf * STAGE + rdbase + (ct + 1) * 1024
-                              : lds_raw + nbuf * STAGE + rdbase;
-      const float wprev = ct == 0 ? w_carry : wt[ct - 1];
+      const int nb_buf = ct < 3 ? buf : nbuf, nct = ct < 3 ? ct + 1 : 0;
+      const float* wprev = ct == 0 ? w_carry : wt[ct - 1];
       // phase A
-      float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+      float b4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         if (ct == 0) {
-          dma_lds16(src + j * 32, dst + j * 4096);
+          dma_lds16(src + (2 * j) * 32, dst + (2 * j) * 4096);
+          dma_lds16(src + (2 * j + 1) * 32, dst + (2 * j + 1) * 4096);
           if (j == 0) dma_lds4(wv + c0n + (wave & 1) * 64 + lane, &wcol[dbuf][(wave & 1) * 64]);
         }
         // B fragments only feed the matrix cores: keep them in accumulation
-        // registers (so the fold's fp32 state fits in the ordinary ones); the
-        // constraint sits at the chunk's first use, where its read is waited for
-        asm volatile("" : "+a"(bq[cur].c[j]));
-        mfma2(0, j, bq[cur]);
-        fold_part(1, j, wprev, b0, b1, b2, b3);
-        bq[prv].c[j] = *reinterpret_cast<const u32x4_t*>(nx + j * 4096);
+        // registers; the constraint sits at the k-step's first use, where
+        // its read is waited for
+        asm volatile("" : "+a"(bq[cur][j][0]), "+a"(bq[cur][j][1]));
+        mfma8(0, j, bq[cur][j]);
+        fold_part(1, j, wprev, b4);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          bq[prv][j][h2] = *reinterpret_cast<const u32x4_t*>(b_addr(nb_buf, nct, h2, j));
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (ct == 0 && st >= 2) flush_finish(st - 2);
       {
-        const float cs = csA_carry + ((b0 + b1) + (b2 + b3));
-        colred[((ct == 0 ? st - 1 : st) + 3) % 3][wave][hf][(ct == 0 ? 3 : ct - 1) * 32 + l32] = cs;
+        const int slot = ((ct == 0 ? st - 1 : st) + 3) % 3;
+        const int pct = ct == 0 ? 3 : ct - 1;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          colred[slot][pct * 32 + h2 * 16 + c16][wave * 4 + g] = csA_carry[h2] + (b4[2 * h2] + b4[2 * h2 + 1]);
       }
       // phase B
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        mfma2(1, j, bq[cur]);
-        fold_part(0, j, wt[ct], a0, a1, a2, a3);
+      for (int j = 0; j < 4; ++j) {
+        mfma8(1, j, bq[cur][j]);
+        fold_part(0, j, wt[ct], a4);
         __builtin_amdgcn_sched_barrier(0);
       }
-      csA_carry = (a0 + a1) + (a2 + a3);
-      if (ct == 3) w_carry = wt[3];
+      csA_carry[0] = a4[0] + a4[1];
+      csA_carry[1] = a4[2] + a4[3];
+      if (ct == 3) {
+        w_carry[0] = wt[3][0];
+        w_carry[1] = wt[3][1];
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
   {
-    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+    float b4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) fold_part(1, j, w_carry, b0, b1, b2, b3);
-    colred[(nsteps - 1) % 3][wave][hf][3 * 32 + l32] = csA_carry + ((b0 + b1) + (b2 + b3));
+    for (int j = 0; j < 4; ++j) fold_part(1, j, w_carry, b4);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      colred[(nsteps - 1) % 3][3 * 32 + h2 * 16 + c16][wave * 4 + g] = csA_carry[h2] + (b4[2 * h2] + b4[2 * h2 + 1]);
   }
   float* red = reinterpret_cast<float*>(lds_raw);
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) red[(wave * 128 + 32 * rt + tile_row(i, hf)) * RED + l32] = rsum[rt][i];
+    for (int i = 0; i < 4; ++i) red[(wave * 128 + 16 * rt + 4 * g + i) * RED + c16] = rsum[rt][i];
   __syncthreads();
   if (nsteps >= 2) flush(nsteps - 2);
   flush(nsteps - 1);
@@ -531,8 +589,8 @@ __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
     const int row = tid + 256 * k, j = r0 + row;
     if (j < n) {
       float s = 0.f;
-#pragma unroll 8
-      for (int l = 0; l < 32; ++l) s += red[row * RED + l];
+#pragma unroll
+      for (int l = 0; l < 16; ++l) s += red[row * RED + l];
       const float w = wv[j];
       p.rs[head * p.cap + j] = s - (w > 0.f ? 1.0f / w : 0.f);
     }
