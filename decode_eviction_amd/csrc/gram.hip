@@ -540,6 +540,14 @@ __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
           bq[prv][j][h2] = *reinterpret_cast<const u32x4_t*>(b_addr(nb_buf, nct, h2, j));
+        // issue order: one matrix-core instruction, then two vector ALU
+        // instructions, eight times; the next tile's LDS reads after the first
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (k == 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       if (ct == 0 && st >= 2) flush_finish(st - 2);
@@ -556,6 +564,11 @@ __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
       for (int j = 0; j < 4; ++j) {
         mfma8(1, j, bq[cur][j]);
         fold_part(0, j, wt[ct], a4);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       csA_carry[0] = a4[0] + a4[1];
