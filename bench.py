@@ -19,14 +19,16 @@ Variants (each with its own value, per-kernel times and roofline):
                   2176-slot cache to 2048 rows (per-call latency);
   batched_<mode>  64 sequences x 8192 tokens, B = 1024 (2 GiB of K and V);
   refreekv        the ReFreeKV threshold cut at the Qwen2.5-7B shape
-                  (28 q / 4 KV heads), 16 ragged sequences of 1K-16K tokens.
+                  (28 q / 4 KV heads), 16 ragged sequences of 1K-16K tokens;
+  heads_<mode>    the headline layer with one budget per KV head (an uneven
+                  allocation with the same total as B = 2048 per head).
 
 The CPU baseline times the fp64 oracle (definition form, n x n cosine
 matrix) on a bounded sample: whole KV heads of one layer until --cpu-seconds
 have passed, scaled to a full layer.
 
     python bench.py [--gpus 1] [--steps 64] [--warmup 8] [--mode gram|keysum]
-                    [--no-variants | --variant decode|batched|refreekv ...]
+                    [--no-variants | --variant decode|batched|refreekv|heads ...]
 """
 
 from __future__ import annotations
@@ -193,10 +195,11 @@ def time_calls(call, names, cost, steps, warmup, hip, traced_steps=None):
     return dict(ms=ms, ms_plain=ms_plain, kernels=kern)
 
 
-def rkv_caller(mode, layers, b, n, budget, out_bufs=None):
+def rkv_caller(mode, layers, b, n, budget, out_bufs=None, budgets=None):
     """call(i, events) running kvsel_score_evict[_traced] on layer i % len(layers).
     layers: list of (q, k, v) device tensors.  With out_bufs the outputs go to
-    out_bufs[i % len], else to one shared output."""
+    out_bufs[i % len], else to one shared output.  With budgets (int32 device
+    tensor [Hkv]) the per-head entry points run and budget is the row stride."""
     import torch
 
     from decode_eviction_amd import kvsel as K
@@ -219,14 +222,18 @@ def rkv_caller(mode, layers, b, n, budget, out_bufs=None):
     def call(i, events=None):
         q, k, v = layers[i % len(layers)]
         ko, vo = out_bufs[i % len(out_bufs)]
-        args = (K.KVSEL_BF16, mcode, P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
-                P(lens.data_ptr()), b, hq, hkv, D, w, cap, LAM, budget, P(ko.data_ptr()),
-                P(vo.data_ptr()), ko.shape[2], P(idx.data_ptr()), None, P(ws.data_ptr()),
-                ws_bytes, sp)
-        if events is None:
-            st = lib.kvsel_score_evict(*args)
+        head = (K.KVSEL_BF16, mcode, P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
+                P(lens.data_ptr()))
+        tail = (b, hq, hkv, D, w, cap, LAM, budget, P(ko.data_ptr()), P(vo.data_ptr()),
+                ko.shape[2], P(idx.data_ptr()), None, P(ws.data_ptr()), ws_bytes, sp)
+        if budgets is not None:
+            args = head + (P(budgets.data_ptr()),) + tail
+            st = (lib.kvsel_score_evict_heads(*args) if events is None else
+                  lib.kvsel_score_evict_heads_traced(*args, events, 2 * nk))
+        elif events is None:
+            st = lib.kvsel_score_evict(*head, *tail)
         else:
-            st = lib.kvsel_score_evict_traced(*args, events, 2 * nk)
+            st = lib.kvsel_score_evict_traced(*head, *tail, events, 2 * nk)
         if st != 0:
             raise RuntimeError(f"kvsel_score_evict: {K.status_string(st)}")
 
@@ -235,6 +242,19 @@ def rkv_caller(mode, layers, b, n, budget, out_bufs=None):
 
 def run_mode(mode, layers, steps, warmup, hip):
     call, keep = rkv_caller(mode, layers, 1, N, BUDGET)
+    return time_calls(call, KERNELS[mode], rkv_cost(mode), steps, warmup, hip)
+
+
+# an uneven per-head allocation with the same total as B=2048 per head
+HEAD_BUDGETS = [512, 1024, 1536, 2048, 2048, 2560, 3072, 3584]
+
+
+def run_heads(mode, layers, steps, warmup, hip):
+    """The headline layer with one budget per KV head (HEAD_BUDGETS, output
+    stride 3584): same scores, per-head thresholds and compaction."""
+    import torch
+    budgets = torch.tensor(HEAD_BUDGETS, dtype=torch.int32, device="cuda")
+    call, keep = rkv_caller(mode, layers, 1, N, max(HEAD_BUDGETS), budgets=budgets)
     return time_calls(call, KERNELS[mode], rkv_cost(mode), steps, warmup, hip)
 
 
@@ -504,7 +524,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the decode-loop, batched and ReFreeKV workloads")
-    ap.add_argument("--variant", action="append", choices=["decode", "batched", "refreekv"],
+    ap.add_argument("--variant", action="append",
+                    choices=["decode", "batched", "refreekv", "heads"],
                     help="run only these extra workloads (repeatable)")
     ap.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args()
@@ -565,6 +586,21 @@ def main():
             "ms_per_step_traced": round(r["ms"], 5),
             "roofline": roofline(r, rkv_cost(mode), a.profiles, mode),
             "step_hbm_frac": hbm_frac(rkv_step_bytes(), r["ms_plain"]), "kernels": r["kernels"]}
+    if not a.no_variants and (a.variant is None or "heads" in a.variant):
+        for mode in order:
+            r = run_heads(mode, layers, a.steps, a.warmup, hip)
+            print(f"# heads/{mode}: {r['ms_plain'] * 1000:.1f} us/step, "
+                  f"{r['ms'] * 1000:.1f} us/step traced; "
+                  + ", ".join(f"{k} {v['avg_us']:.1f}us" for k, v in r["kernels"].items()),
+                  file=sys.stderr, flush=True)
+            out.setdefault("variants", {})[f"heads_{mode}"] = {
+                "workload": "the headline layer with per-KV-head budgets "
+                            f"{HEAD_BUDGETS} (sum {sum(HEAD_BUDGETS)})",
+                "value": round(N / (r["ms_plain"] * 1e-3), 1), "unit": "tokens/s/layer",
+                "ms_per_step": round(r["ms_plain"], 5), "ms_per_step_traced": round(r["ms"], 5),
+                "roofline": roofline(r, rkv_cost(mode), a.profiles, f"heads_{mode}"),
+                "step_hbm_frac": hbm_frac(rkv_step_bytes(), r["ms_plain"]),
+                "kernels": r["kernels"]}
     del layers
     torch.cuda.empty_cache()
     if not a.no_variants:

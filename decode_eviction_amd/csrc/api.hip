@@ -170,6 +170,7 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
 // ------------------------------------------------------------ select layout
 
 struct SelWs {
+  int32_t* err;  // first, so that kvsel_workspace_error reads it
   uint32_t* hist;
   uint32_t* thr;
   uint32_t* coff;
@@ -180,6 +181,7 @@ struct SelWs {
 SelWs carve_select(Carver& c, int b, int hkv, int cap) {
   const size_t heads = (size_t)b * hkv;
   SelWs w;
+  w.err = c.take<int32_t>(64);
   w.nsc = (cap + kSelChunk - 1) / kSelChunk;
   w.hist = c.take<uint32_t>(heads * kHistBins);
   w.thr = c.take<uint32_t>(heads * 2);
@@ -203,6 +205,7 @@ SelectParams select_params(const SelWs& w, const float* z, const int32_t* length
   sp.coff = w.coff;
   sp.ceqb = w.ceqb;
   sp.nsc = w.nsc;
+  sp.err = w.err;
   return sp;
 }
 
@@ -276,9 +279,9 @@ size_t kvsel_select_workspace(int b, int hkv, int cap) {
   return (c.off + kAlign - 1) / kAlign * kAlign;
 }
 
-kvsel_status kvsel_select_topb(const float* z, const int32_t* lengths, int b, int hkv, int cap,
-                               int budget, int32_t* idx_out, void* workspace, size_t ws_bytes,
-                               hipStream_t stream) {
+static kvsel_status select_impl(const float* z, const int32_t* lengths, const int32_t* budgets,
+                                int b, int hkv, int cap, int budget, int32_t* idx_out,
+                                void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!z || !lengths || !idx_out) return KVSEL_ERR_INVALID_ARG;
   if (b < 1 || hkv < 1 || cap < 1 || budget < 1) return KVSEL_ERR_INVALID_ARG;
   if (b > 65535 || hkv > 65535 || cap >= (1 << 24) || budget > 65536) return KVSEL_ERR_UNSUPPORTED;
@@ -286,8 +289,26 @@ kvsel_status kvsel_select_topb(const float* z, const int32_t* lengths, int b, in
   Carver c{static_cast<char*>(workspace)};
   const SelWs w = carve_select(c, b, hkv, cap);
   SelectParams p = select_params(w, z, lengths, b, hkv, cap, budget, idx_out);
-  if (cap <= kSelectLdsKeys) KV_TRY(launch_hist(p, stream, nullptr));
+  p.budgets = budgets;
+  if (cap <= kSelectLdsKeys) KV_TRY(launch_hist(p, stream, nullptr));  // also clears the error word
+  else KV_TRY(launch_select_err_zero(p, stream, nullptr));
   return hip_status(launch_select(p, stream, nullptr));
+}
+
+kvsel_status kvsel_select_topb(const float* z, const int32_t* lengths, int b, int hkv, int cap,
+                               int budget, int32_t* idx_out, void* workspace, size_t ws_bytes,
+                               hipStream_t stream) {
+  return select_impl(z, lengths, nullptr, b, hkv, cap, budget, idx_out, workspace, ws_bytes,
+                     stream);
+}
+
+kvsel_status kvsel_select_topb_heads(const float* z, const int32_t* lengths,
+                                     const int32_t* budgets, int b, int hkv, int cap,
+                                     int budget_max, int32_t* idx_out, void* workspace,
+                                     size_t ws_bytes, hipStream_t stream) {
+  if (!budgets) return KVSEL_ERR_INVALID_ARG;
+  return select_impl(z, lengths, budgets, b, hkv, cap, budget_max, idx_out, workspace, ws_bytes,
+                     stream);
 }
 
 kvsel_status kvsel_gather(kvsel_dtype dt, const void* k, const void* v, const int32_t* idx, int b,
@@ -306,7 +327,8 @@ kvsel_status kvsel_gather(kvsel_dtype dt, const void* k, const void* v, const in
 }
 
 static kvsel_status score_evict_impl(kvsel_dtype dt, kvsel_redundancy mode, const void* q_window,
-                                     const void* k, const void* v, const int32_t* lengths, int b,
+                                     const void* k, const void* v, const int32_t* lengths,
+                                     const int32_t* budgets, int b,
                                      int hq, int hkv, int d, int w, int cap, float lambda,
                                      int budget, void* k_out, void* v_out, int cap_out,
                                      int32_t* idx_out, float* scores_out, void* workspace,
@@ -331,7 +353,9 @@ static kvsel_status score_evict_impl(kvsel_dtype dt, kvsel_redundancy mode, cons
   sw.coff = ws.sel.coff;
   sw.ceqb = ws.sel.ceqb;
   sw.nsc = ws.sel.nsc;
+  sw.err = ws.err;  // set by the first score kernel; the select kernels add to it
   SelectParams sp = select_params(sw, z, lengths, b, hkv, cap, budget, idx_out);
+  sp.budgets = budgets;
   if (cap <= kSelectLdsKeys) {  // the compaction kernel also gathers the kept rows
     sp.k = static_cast<const char*>(k);
     sp.v = static_cast<const char*>(v);
@@ -355,9 +379,22 @@ kvsel_status kvsel_score_evict(kvsel_dtype dt, kvsel_redundancy mode, const void
                                void* k_out, void* v_out, int cap_out, int32_t* idx_out,
                                float* scores_out, void* workspace, size_t ws_bytes,
                                hipStream_t stream) {
-  return score_evict_impl(dt, mode, q_window, k, v, lengths, b, hq, hkv, d, w, cap, lambda, budget,
-                          k_out, v_out, cap_out, idx_out, scores_out, workspace, ws_bytes, stream,
-                          nullptr);
+  return score_evict_impl(dt, mode, q_window, k, v, lengths, nullptr, b, hq, hkv, d, w, cap, lambda,
+                          budget, k_out, v_out, cap_out, idx_out, scores_out, workspace, ws_bytes,
+                          stream, nullptr);
+}
+
+kvsel_status kvsel_score_evict_heads(kvsel_dtype dt, kvsel_redundancy mode, const void* q_window,
+                                     const void* k, const void* v, const int32_t* lengths,
+                                     const int32_t* budgets, int b, int hq, int hkv, int d, int w,
+                                     int cap, float lambda, int budget_max, void* k_out,
+                                     void* v_out, int cap_out, int32_t* idx_out,
+                                     float* scores_out, void* workspace, size_t ws_bytes,
+                                     hipStream_t stream) {
+  if (!budgets) return KVSEL_ERR_INVALID_ARG;
+  return score_evict_impl(dt, mode, q_window, k, v, lengths, budgets, b, hq, hkv, d, w, cap,
+                          lambda, budget_max, k_out, v_out, cap_out, idx_out, scores_out,
+                          workspace, ws_bytes, stream, nullptr);
 }
 
 kvsel_status kvsel_score_evict_traced(kvsel_dtype dt, kvsel_redundancy mode, const void* q_window,
@@ -369,9 +406,24 @@ kvsel_status kvsel_score_evict_traced(kvsel_dtype dt, kvsel_redundancy mode, con
                                       int n_events) {
   if (!events || n_events < 2) return KVSEL_ERR_INVALID_ARG;
   Trace tr{events, n_events, 0};
-  return score_evict_impl(dt, mode, q_window, k, v, lengths, b, hq, hkv, d, w, cap, lambda, budget,
-                          k_out, v_out, cap_out, idx_out, scores_out, workspace, ws_bytes, stream,
-                          &tr);
+  return score_evict_impl(dt, mode, q_window, k, v, lengths, nullptr, b, hq, hkv, d, w, cap, lambda,
+                          budget, k_out, v_out, cap_out, idx_out, scores_out, workspace, ws_bytes,
+                          stream, &tr);
+}
+
+kvsel_status kvsel_score_evict_heads_traced(kvsel_dtype dt, kvsel_redundancy mode,
+                                            const void* q_window, const void* k, const void* v,
+                                            const int32_t* lengths, const int32_t* budgets, int b,
+                                            int hq, int hkv, int d, int w, int cap, float lambda,
+                                            int budget_max, void* k_out, void* v_out, int cap_out,
+                                            int32_t* idx_out, float* scores_out, void* workspace,
+                                            size_t ws_bytes, hipStream_t stream,
+                                            hipEvent_t* events, int n_events) {
+  if (!budgets || !events || n_events < 2) return KVSEL_ERR_INVALID_ARG;
+  Trace tr{events, n_events, 0};
+  return score_evict_impl(dt, mode, q_window, k, v, lengths, budgets, b, hq, hkv, d, w, cap,
+                          lambda, budget_max, k_out, v_out, cap_out, idx_out, scores_out,
+                          workspace, ws_bytes, stream, &tr);
 }
 
 size_t kvsel_threshold_cut_workspace(int b, int hq, int hkv, int d, int cap) {

@@ -81,6 +81,10 @@ struct SelectParams {
   char* k_out;
   char* v_out;
   int cap_out, row_bytes;
+  // per-head budgets (nullable): head h keeps budgets[h] clamped to [0, budget],
+  // budget being the row stride of idx and of the compacted cache
+  const int32_t* budgets;   // [Hkv]
+  int32_t* err;             // nullable error word: bit 0 length > cap, bit 1 budget clamped
 };
 
 struct GatherParams {
@@ -133,6 +137,7 @@ hipError_t launch_pool(int dt, int d, int mode, const ScoreParams& p, hipStream_
 hipError_t launch_gram(int dt, int d, const GramParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_select(const SelectParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_hist(const SelectParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_select_err_zero(const SelectParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_gather(int dt, int d, const GatherParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_cut_energy(const CutParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_cut_scan(const CutParams& p, hipStream_t s, Trace* tr);

@@ -55,6 +55,26 @@ __device__ __forceinline__ uint2 block_scan_u32(uint32_t v, uint32_t* wsum, int 
   return make_uint2(before + x - v, total);
 }
 
+// Budget of KV head h: the scalar budget, or budgets[h] clamped to
+// [0, budget] (budget is then the row stride of the outputs).
+__device__ __forceinline__ int head_budget(const SelectParams& p, int h) {
+  if (!p.budgets) return p.budget;
+  const int v = p.budgets[h];
+  return v < 0 ? 0 : (v > p.budget ? p.budget : v);
+}
+
+// Error bits of one (sequence, head): a length above cap (bit 0), a per-head
+// budget outside [0, budget] (bit 1).
+__device__ __forceinline__ void flag_select_errors(const SelectParams& p, int h, int bi) {
+  if (!p.err) return;
+  int f = p.lengths[bi] > p.cap ? 1 : 0;
+  if (p.budgets) {
+    const int v = p.budgets[h];
+    f |= (v < 0 || v > p.budget) ? 2 : 0;
+  }
+  if (f) atomicOr(p.err, f);
+}
+
 __global__ __launch_bounds__(kSelectThreads) void k_select(SelectParams p) {
   __shared__ uint32_t keys[kSelectLdsKeys];
   __shared__ uint32_t hist[kSelBins];
@@ -64,15 +84,18 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(SelectParams p) {
   const int h = blockIdx.x, bi = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = min(p.lengths[bi], p.cap);
-  const int B = p.budget;
+  const int B = head_budget(p, h);
   const long head = (long)bi * p.hkv + h;
-  int32_t* out = p.idx + head * B;
+  int32_t* out = p.idx + head * p.budget;
   const float* z = p.z + head * p.cap;
+  if (tid == 0) flag_select_errors(p, h, bi);
 
   if (n <= B) {
-    for (int t = tid; t < B; t += kSelectThreads) out[t] = t < n ? t : -1;
+    for (int t = tid; t < p.budget; t += kSelectThreads) out[t] = t < n ? t : -1;
     return;
   }
+  for (int t = B + tid; t < p.budget; t += kSelectThreads) out[t] = -1;
+  if (B == 0) return;
   const bool inl = n <= kSelectLdsKeys;
 
   uint32_t kmin = 0xffffffffu, kmax = 0u;
@@ -297,9 +320,10 @@ __global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
   const int h = blockIdx.x, bi = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = min(p.lengths[bi], p.cap);
-  const int B = p.budget;
+  const int B = head_budget(p, h);
   const long head = (long)bi * p.hkv + h;
-  if (n <= B) return;  // k_compact keeps everything
+  if (tid == 0) flag_select_errors(p, h, bi);
+  if (n <= B || B == 0) return;  // k_compact keeps everything (or nothing)
   const float* z = p.z + head * p.cap;
 
   // unconditional loads (index clamped into range): all in flight before use
@@ -477,13 +501,13 @@ __global__ __launch_bounds__(256) void k_compact(SelectParams p) {
   __shared__ int32_t rows[kSelChunk];   // kept positions by slot - chunk offset
   const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
   const int n = min(p.lengths[bi], p.cap);
-  const int B = p.budget;
+  const int B = head_budget(p, h);
   const long head = (long)bi * p.hkv + h;
-  int32_t* out = p.idx + head * B;
+  int32_t* out = p.idx + head * p.budget;
   const int c0 = chunk * kSelChunk;
   if (chunk == 0)
-    for (int t = min(n, B) + tid; t < B; t += 256) out[t] = -1;
-  if (c0 >= n) return;
+    for (int t = min(n, B) + tid; t < p.budget; t += 256) out[t] = -1;
+  if (c0 >= n || B == 0) return;
   const bool all = n <= B;
   uint32_t kth = 0, need_eq = 0, off = 0, eqb = 0;
   if (!all) {
@@ -587,6 +611,7 @@ __global__ __launch_bounds__(256) void k_compact(SelectParams p) {
 // histogram, one 256-thread work-group per 2048 positions.
 __global__ __launch_bounds__(256) void k_hist_zero(SelectParams p) {
   const long head = (long)blockIdx.y * p.hkv + blockIdx.x;
+  if (p.err && head == 0 && threadIdx.x == 0) *p.err = 0;
   for (int t = threadIdx.x; t < kHistBins; t += 256) p.hist[head * kHistBins + t] = 0u;
 }
 
@@ -615,6 +640,15 @@ hipError_t launch_hist(const SelectParams& p, hipStream_t s, Trace* tr) {
   hipError_t e = launch_k(k_hist_zero, dim3(p.hkv, p.b), dim3(256), s, tr, p);
   if (e != hipSuccess) return e;
   return launch_k(k_hist, dim3((p.cap + 2047) / 2048, p.hkv, p.b), dim3(256), s, tr, p);
+}
+
+// Clears the error word of a select-only call that builds no histogram.
+__global__ void k_select_err_zero(SelectParams p) {
+  if (threadIdx.x == 0) *p.err = 0;
+}
+
+hipError_t launch_select_err_zero(const SelectParams& p, hipStream_t s, Trace* tr) {
+  return launch_k(k_select_err_zero, dim3(1), dim3(64), s, tr, p);
 }
 
 hipError_t launch_select(const SelectParams& p, hipStream_t s, Trace* tr) {

@@ -33,9 +33,14 @@ _SIGS = {
     "kvsel_scores": (_I, [_I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _S, _P]),
     "kvsel_select_workspace": (_S, [_I, _I, _I]),
     "kvsel_select_topb": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _S, _P]),
+    "kvsel_select_topb_heads": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _S, _P]),
     "kvsel_gather": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P]),
     "kvsel_score_evict": (_I, [_I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                                _P, _P, _I, _P, _P, _P, _S, _P]),
+    "kvsel_score_evict_heads": (_I, [_I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                                     _P, _P, _I, _P, _P, _P, _S, _P]),
+    "kvsel_score_evict_heads_traced": (_I, [_I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                            _F, _I, _P, _P, _I, _P, _P, _P, _S, _P, _P, _I]),
     "kvsel_score_evict_traced": (_I, [_I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                                       _P, _P, _I, _P, _P, _P, _S, _P, _P, _I]),
     "kvsel_threshold_cut_workspace": (_S, [_I] * 5),
@@ -155,6 +160,21 @@ def kvsel_select_topb(z, lengths, budget, idx_out=None, workspace=None, stream=N
     return idx_out
 
 
+def kvsel_select_topb_heads(z, lengths, budgets, budget_max, idx_out=None, workspace=None,
+                            stream=None):
+    """Top-budget per KV head with budgets [Hkv] (int32 device tensor)."""
+    _need_cuda(z, lengths, budgets, idx_out)
+    b, hkv, cap = z.shape
+    if idx_out is None:
+        idx_out = torch.empty((b, hkv, budget_max), dtype=torch.int32, device=z.device)
+    ws = _workspace(kvsel_select_workspace(b, hkv, cap), z.device, workspace)
+    st = lib().kvsel_select_topb_heads(_ptr(z), _ptr(lengths), _ptr(budgets), b, hkv, cap,
+                                       int(budget_max), _ptr(idx_out), _ptr(ws), ws.numel(),
+                                       _stream(stream))
+    _check("kvsel_select_topb_heads", st)
+    return idx_out
+
+
 def kvsel_gather(k, v, idx, k_out=None, v_out=None, stream=None):
     _need_cuda(k, v, idx, k_out, v_out)
     b, hkv, cap, d = k.shape
@@ -188,6 +208,30 @@ def kvsel_score_evict(q_window, k, v, lengths, budget, lam=0.1, mode="gram", k_o
                                  _ptr(k_out), _ptr(v_out), k_out.shape[2], _ptr(idx_out),
                                  _ptr(scores_out), _ptr(ws), ws.numel(), _stream(stream))
     _check("kvsel_score_evict", st)
+    return k_out, v_out, idx_out
+
+
+def kvsel_score_evict_heads(q_window, k, v, lengths, budgets, budget_max, lam=0.1, mode="gram",
+                            k_out=None, v_out=None, idx_out=None, scores_out=None,
+                            workspace=None, stream=None):
+    """The whole step with per-head budgets; returns (k_out, v_out, idx_out)."""
+    _need_cuda(q_window, k, v, lengths, budgets, k_out, v_out, idx_out, scores_out)
+    b, hq, w, d = q_window.shape
+    _, hkv, cap, _ = k.shape
+    dev = k.device
+    if k_out is None:
+        k_out = torch.zeros((b, hkv, budget_max, d), dtype=k.dtype, device=dev)
+    if v_out is None:
+        v_out = torch.zeros((b, hkv, budget_max, d), dtype=v.dtype, device=dev)
+    if idx_out is None:
+        idx_out = torch.empty((b, hkv, budget_max), dtype=torch.int32, device=dev)
+    ws = _workspace(kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, budget_max), dev, workspace)
+    st = lib().kvsel_score_evict_heads(_dtype(k), MODES[mode], _ptr(q_window), _ptr(k), _ptr(v),
+                                       _ptr(lengths), _ptr(budgets), b, hq, hkv, d, w, cap,
+                                       float(lam), int(budget_max), _ptr(k_out), _ptr(v_out),
+                                       k_out.shape[2], _ptr(idx_out), _ptr(scores_out), _ptr(ws),
+                                       ws.numel(), _stream(stream))
+    _check("kvsel_score_evict_heads", st)
     return k_out, v_out, idx_out
 
 

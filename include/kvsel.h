@@ -106,6 +106,21 @@ kvsel_status kvsel_select_topb(const float* z, const int32_t* lengths, int b, in
                                int cap, int budget, int32_t* idx_out,
                                void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Top-budget choice with one budget per KV head: head h keeps the
+ * min(budgets[h], n) largest scores, chosen and ordered as in
+ * kvsel_select_topb.  budgets [Hkv] int32 on the device is one row of a
+ * per-(layer, head) allocation table (the interface a learned or profiled
+ * budget allocator feeds; QbitAI R-KV article, section on joint eviction
+ * under a KV budget, with per-head budgets as the allocation layer above it).
+ * idx_out is [b][Hkv][budget_max]: head h's entries, then -1 up to
+ * budget_max.  A budget outside [0, budget_max] is clamped into it and sets
+ * bit 1 of the workspace error word; budget 0 keeps nothing.  Same workspace
+ * size as kvsel_select_topb. */
+kvsel_status kvsel_select_topb_heads(const float* z, const int32_t* lengths,
+                                     const int32_t* budgets, int b, int Hkv, int cap,
+                                     int budget_max, int32_t* idx_out,
+                                     void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Gather-compaction: for t < budget with idx[t] >= 0, row t of k_out/v_out
  * [b][Hkv][cap_out][d] becomes row idx[t] of k/v (bit copy); other rows are
  * left untouched.  idx values must lie in [0, cap) or be -1. */
@@ -123,6 +138,19 @@ kvsel_status kvsel_score_evict(kvsel_dtype dt, kvsel_redundancy mode,
                                int32_t* idx_out, float* scores_out,
                                void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* The whole step with one budget per KV head (budgets [Hkv] int32 on the
+ * device, as in kvsel_select_topb_heads): k_out/v_out [b][Hkv][cap_out][d]
+ * receive head h's kept rows in rows 0 .. min(budgets[h], n)-1, later rows
+ * are left untouched; idx_out is [b][Hkv][budget_max] with -1 padding.
+ * budget_max <= cap_out.  Same workspace size as kvsel_score_evict. */
+kvsel_status kvsel_score_evict_heads(kvsel_dtype dt, kvsel_redundancy mode,
+                                     const void* q_window, const void* k, const void* v,
+                                     const int32_t* lengths, const int32_t* budgets,
+                                     int b, int Hq, int Hkv, int d, int w, int cap, float lambda,
+                                     int budget_max, void* k_out, void* v_out, int cap_out,
+                                     int32_t* idx_out, float* scores_out,
+                                     void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Same step with per-kernel timing for profilers and benchmarks: kernel k of
  * the call records events[2k] when it starts and events[2k+1] when it ends
  * (k < n_events / 2; events are created by the caller with hipEventCreate).
@@ -138,6 +166,16 @@ kvsel_status kvsel_score_evict_traced(kvsel_dtype dt, kvsel_redundancy mode,
                                       int32_t* idx_out, float* scores_out,
                                       void* workspace, size_t ws_bytes, hipStream_t stream,
                                       hipEvent_t* events, int n_events);
+
+/* kvsel_score_evict_heads with per-kernel timing as in kvsel_score_evict_traced. */
+kvsel_status kvsel_score_evict_heads_traced(kvsel_dtype dt, kvsel_redundancy mode,
+                                            const void* q_window, const void* k, const void* v,
+                                            const int32_t* lengths, const int32_t* budgets,
+                                            int b, int Hq, int Hkv, int d, int w, int cap,
+                                            float lambda, int budget_max, void* k_out,
+                                            void* v_out, int cap_out, int32_t* idx_out,
+                                            float* scores_out, void* workspace, size_t ws_bytes,
+                                            hipStream_t stream, hipEvent_t* events, int n_events);
 
 /* ------------------------------------------------------------ ReFreeKV */
 
@@ -172,6 +210,7 @@ kvsel_status kvsel_threshold_cut_from_attn(const float* attn_last, const int32_t
 
 /* Reads the device error word left in the workspace by the last call that
  * used it (synchronises the stream).  Bit 0: some lengths[i] exceeded cap and
+ * was clamped; bit 1: some per-head budget lay outside [0, budget_max] and
  * was clamped.  Returns KVSEL_ERR_HIP if the copy fails. */
 kvsel_status kvsel_workspace_error(const void* workspace, int32_t* flags_host, hipStream_t stream);
 

@@ -123,16 +123,26 @@ def head_scores(q_rows, k, lam, form: str = "definition"):
     return i_sc, r_sc, combine(i_sc, r_sc, lam)
 
 
+def head_budget(budgets, h: int, budget: int) -> int:
+    """Budget of KV head h: the scalar budget, or budgets[h] clamped to
+    [0, budget] (budget being the row count of the outputs)."""
+    if budgets is None:
+        return budget
+    return min(max(int(budgets[h]), 0), budget)
+
+
 def score_evict(q, k, v, lengths, lam: float, budget: int, form: str = "definition",
-                heads=None):
+                heads=None, budgets=None):
     """Whole call for b sequences.
 
     q: [b][Hq][w][d], k, v: [b][Hkv][cap][d] (exact fp32 values of the inputs),
     lengths: [b].  Returns a dict of per-(b, h) results:
       I, R, Z:   lists indexed [b][h] of fp64 arrays of length n_b
-      idx:       [b][Hkv][budget] int64, ascending, -1 past min(n_b, budget)
+      idx:       [b][Hkv][budget] int64, ascending, -1 past min(n_b, B_h)
       k_out, v_out: [b][Hkv][budget][d] rows of k/v at idx (zeros where idx<0)
     ``heads`` optionally restricts the work to a list of (b, h) pairs.
+    ``budgets`` optionally gives one budget per KV head (the row of a
+    per-head allocation table); B_h = head_budget(budgets, h, budget).
     """
     q = np.asarray(q)
     b, hq, w, d = q.shape
@@ -149,7 +159,7 @@ def score_evict(q, k, v, lengths, lam: float, budget: int, form: str = "definiti
         n = int(lengths[bi])
         rows = q[bi, h * g:(h + 1) * g].reshape(g * w, d)
         i_sc, r_sc, z = head_scores(rows, k[bi, h, :n], lam, form)
-        sel = top_budget(z, budget)
+        sel = top_budget(z, head_budget(budgets, h, budget))
         out_i[bi][h], out_r[bi][h], out_z[bi][h] = i_sc, r_sc, z
         idx[bi, h, :len(sel)] = sel
         k_out[bi, h, :len(sel)] = k[bi, h, sel]

@@ -4,7 +4,8 @@ Cases: the tiny fp32 layer (n=512), the 8B-shaped layer (n=4096), ragged and
 padded batches covering several tiles and ragged tails, d=64 with 8/64/128
 window rows, the n=32768 layer in the launch configuration the benchmark
 times, the batched 64 x 8192 workload (sampled heads), stage entries (top-B
-on oracle scores, gather), determinism and the clamped-length flag.
+on oracle scores, gather), per-head budgets (stage and whole step),
+determinism and the clamped-length flag.
 """
 
 import numpy as np
@@ -182,6 +183,71 @@ def test_select_stage_exact():
                 m = min(nb, budget)
                 assert idx[b, h, :m].tolist() == want.tolist(), (n, budget, kind, b, h)
                 assert (idx[b, h, m:] == -1).all()
+
+
+def test_select_heads_stage_exact():
+    """Per-head budgets on given scores: each head's set is the oracle's for its own budget."""
+    rng = np.random.default_rng(17)
+    for n, cap, bmax, kind in [(2176, 2176, 2048, "normal"), (5000, 5000, 900, "ties"),
+                               (40000, 40001, 3000, "ties"), (300, 512, 256, "normal")]:
+        hkv = 6
+        if kind == "ties":
+            z = (rng.integers(-40, 40, size=(2, hkv, cap)) * 2.0 ** -12).astype(np.float32)
+        else:
+            z = rng.standard_normal((2, hkv, cap)).astype(np.float32) * 1e-3
+        lens = np.array([n, max(1, n // 3)], np.int32)
+        budgets = np.array([0, 1, bmax // 2, bmax, n, bmax + 5], np.int32)
+        budgets = budgets[rng.permutation(hkv)]
+        log(f"[select heads] n={n} cap={cap} Bmax={bmax} budgets={budgets.tolist()} {kind}")
+        ws = torch.empty(K.kvsel_select_workspace(2, hkv, cap), dtype=torch.uint8, device="cuda")
+        idx = K.kvsel_select_topb_heads(dev(z, "f32"), dev_i32(lens), dev_i32(budgets), bmax,
+                                        workspace=ws).cpu().numpy()
+        assert K.kvsel_workspace_error(ws) == 2            # bmax + 5 was clamped
+        for b in range(2):
+            for h in range(hkv):
+                nb = int(lens[b])
+                bh = rkv.head_budget(budgets, h, bmax)
+                want = rkv.top_budget(z[b, h, :nb].astype(np.float64), bh)
+                m = min(nb, bh)
+                assert idx[b, h, :m].tolist() == want.tolist(), (n, kind, b, h, bh)
+                assert (idx[b, h, m:] == -1).all()
+        ok = np.clip(budgets, 0, bmax).astype(np.int32)
+        idx2 = K.kvsel_select_topb_heads(dev(z, "f32"), dev_i32(lens), dev_i32(ok), bmax,
+                                         workspace=ws).cpu().numpy()
+        assert K.kvsel_workspace_error(ws) == 0
+        assert np.array_equal(idx, idx2)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_score_evict_heads(mode):
+    case = synth.rkv_case("heads", seed=12, wl=94, b=2, hq=16, hkv=4, d=128, w=8,
+                          lengths=[3000, 1700], cap=3072, budget=1024)
+    budgets = np.array([1024, 0, 700, 1800], np.int32)      # 1800 > 1024: clamped
+    q, k, v = dev(case.q, "bf16"), dev(case.k, "bf16"), dev(case.v, "bf16")
+    ws = torch.empty(K.kvsel_score_evict_workspace(2, 16, 4, 128, 8, 3072, 1024), dtype=torch.uint8,
+                     device="cuda")
+    z = torch.full((2, 4, 3072), float("nan"), device="cuda")
+    k_out, v_out, idx = K.kvsel_score_evict_heads(q, k, v, dev_i32(case.lengths), dev_i32(budgets),
+                                                  1024, case.lam, mode, scores_out=z, workspace=ws)
+    assert K.kvsel_workspace_error(ws) == 2
+    idx, z = idx.cpu().numpy(), z.cpu().numpy()
+    k_out, v_out = host_bits(k_out), host_bits(v_out)
+    ref = rkv.score_evict(case.as_f32("q"), case.as_f32("k"), case.as_f32("v"), case.lengths,
+                          case.lam, 1024, form="keysum", budgets=budgets)
+    for b in range(2):
+        n = int(case.lengths[b])
+        for h in range(4):
+            bh = rkv.head_budget(budgets, h, 1024)
+            m = min(n, bh)
+            assert score_err(z[b, h, :n], ref["Z"][b][h]) <= SCORE_RTOL
+            assert (idx[b, h, m:] == -1).all()
+            if m:
+                check_idx_structure(idx[b, h], n, m)
+            ns, gap = swaps(idx[b, h, :m], ref["idx"][b, h, :m], ref["Z"][b][h])
+            assert gap < SWAP_WINDOW, (b, h, gap)
+            assert np.array_equal(k_out[b, h, :m], case.k[b, h, idx[b, h, :m]])
+            assert np.array_equal(v_out[b, h, :m], case.v[b, h, idx[b, h, :m]])
+            assert (k_out[b, h, m:] == 0).all()           # rows past the head's budget untouched
 
 
 def test_gather_stage_bit_exact():

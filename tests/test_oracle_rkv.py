@@ -189,6 +189,36 @@ def test_top_budget_permutation_equivariant():
     assert a == b
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_per_head_budgets_brute_force(seed):
+    # each KV head keeps the best subset of its own (clamped) size, and the
+    # head index of the budget row matches the head of the scores
+    rng = np.random.default_rng(300 + seed)
+    hkv, n, d, w, budget = 3, int(rng.integers(1, 10)), 4, 2, 5
+    q = rng.integers(-2, 3, size=(1, hkv, w, d)).astype(np.float64)
+    k = rng.integers(-2, 3, size=(1, hkv, n, d)).astype(np.float64)
+    budgets = rng.integers(-2, budget + 3, size=hkv)
+    out = rkv.score_evict(q, k, k, [n], 0.1, budget, budgets=budgets)
+    for h in range(hkv):
+        bh = min(max(int(budgets[h]), 0), budget)
+        want = _brute_top(out["Z"][0][h], bh)
+        got = out["idx"][0, h]
+        assert got[:len(want)].tolist() == want
+        assert (got[len(want):] == -1).all()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_top_budget_nested(seed):
+    # with ties going to the lower position, a smaller budget's set lies inside a larger one's
+    rng = np.random.default_rng(400 + seed)
+    z = rng.integers(-5, 6, size=300) * 0.25
+    prev = set()
+    for budget in range(0, 301, 7):
+        cur = set(rkv.top_budget(z, budget).tolist())
+        assert prev <= cur and len(cur) == min(budget, 300)
+        prev = cur
+
+
 def test_duplicate_copy_golden():
     g = _golden("rkv_duplicate_copy.txt")
     d, n, budget = int(g["d"][0]), int(g["n"][0]), int(g["budget"][0])
