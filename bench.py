@@ -17,6 +17,8 @@ measured; --mode picks which one is the headline `value`.
 Variants (each with its own value, per-kernel times and roofline):
   decode_<mode>   the decode loop: 32 layers x 240 calls compressing a
                   2176-slot cache to 2048 rows (per-call latency);
+  decode_slots_<mode>  the same loop with slot reuse: evicted slots listed and
+                  refilled by the next 128 tokens, no compaction;
   batched_<mode>  64 sequences x 8192 tokens, B = 1024 (2 GiB of K and V);
   refreekv        the ReFreeKV threshold cut at the Qwen2.5-7B shape
                   (28 q / 4 KV heads), 16 ragged sequences of 1K-16K tokens;
@@ -72,6 +74,8 @@ def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int =
         "thresh": {"bytes": 4 * tok},
         "compact": {"bytes": 4 * tok + 4 * b * hkv * budget + gath},
     }
+    # slot reuse: scores and position map read, evicted list written
+    cost["evict"] = {"bytes": 8 * tok + 4 * b * hkv * max(n - budget, 0)}
     if mode == "gram":
         # symmetric Gram: each pair of 256-key blocks once; matrix-core flops
         # as executed (2 d per key pair and block padding included)
@@ -300,6 +304,72 @@ def run_decode(mode, n_layers, hip, calls_per_layer=240):
     return r
 
 
+def run_decode_slots(mode, n_layers, hip, calls_per_layer=240):
+    """The decode loop with slot reuse: per layer a 2176-slot cache that is
+    never compacted.  Call j of a layer scores it, lists the 128 evicted slots
+    per head (kvsel_score_evict_slots) and writes the layer's stream tokens
+    2176 + 128j .. 2176 + 128j + 127 into them (kvsel_slots_write); both are in
+    the timed call.  The per-kernel trace covers the score and select kernels
+    (the write is one small kernel after them)."""
+    import torch
+
+    from decode_eviction_amd import kvsel as K
+    from decode_eviction_amd import synth
+    cap, budget, w, nb = 2176, 2048, W, 2176 - 2048
+    lib = K.lib()
+    mcode = K.MODES[mode]
+    names = KERNELS[mode][:-1] + ["evict"]
+    P = ctypes.c_void_p
+    layers = []
+    for layer in range(n_layers):
+        ds = synth.decode_stream(layer, total=cap + nb * calls_per_layer)
+        q = bf16_dev(ds.window(cap, w))
+        k = bf16_dev(ds.k[None, :, :cap])
+        v = bf16_dev(ds.v[None, :, :cap])
+        # new tokens of call j: [calls][1][Hkv][nb][d], each call's block contiguous
+        rest = lambda a: np.ascontiguousarray(
+            a[:, cap:].reshape(HKV, calls_per_layer, nb, D).transpose(1, 0, 2, 3)[:, None])
+        kn, vn = bf16_dev(rest(ds.k)), bf16_dev(rest(ds.v))
+        pos = torch.arange(cap, dtype=torch.int32, device="cuda").repeat(HKV, 1)[None].contiguous()
+        ev = torch.empty((1, HKV, cap), dtype=torch.int32, device="cuda")
+        ne = torch.empty((1, HKV), dtype=torch.int32, device="cuda")
+        layers.append((q, k, v, kn, vn, pos, ev, ne))
+        del ds
+    lens = torch.full((1,), cap, dtype=torch.int32, device="cuda")
+    pos_new = torch.arange(cap, cap + nb * calls_per_layer, nb, dtype=torch.int32, device="cuda")
+    ws_bytes = K.kvsel_score_evict_workspace(1, HQ, HKV, D, w, cap, budget)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    sp = P(torch.cuda.current_stream().cuda_stream)
+    step_new = HKV * nb * D * 2
+
+    done = [0] * n_layers  # calls so far per layer: the stream position keeps advancing
+
+    def call(i, events=None):
+        q, k, v, kn, vn, pos, ev, ne = layers[i % n_layers]
+        j = done[i % n_layers] % calls_per_layer
+        done[i % n_layers] += 1
+        args = (K.KVSEL_BF16, mcode, P(q.data_ptr()), P(k.data_ptr()), P(lens.data_ptr()),
+                P(pos.data_ptr()), None, 1, HQ, HKV, D, w, cap, LAM, budget, P(ev.data_ptr()),
+                cap, P(ne.data_ptr()), None, P(ws.data_ptr()), ws_bytes, sp)
+        st = (lib.kvsel_score_evict_slots(*args) if events is None else
+              lib.kvsel_score_evict_slots_traced(*args, events, 2 * len(names)))
+        if st == 0:
+            st = lib.kvsel_slots_write(K.KVSEL_BF16, P(k.data_ptr()), P(v.data_ptr()),
+                                       P(pos.data_ptr()), P(kn.data_ptr() + j * step_new),
+                                       P(vn.data_ptr() + j * step_new),
+                                       P(pos_new.data_ptr() + 4 * j), P(ev.data_ptr()), cap,
+                                       P(ne.data_ptr()), 1, HKV, D, cap, nb, sp)
+        if st != 0:
+            raise RuntimeError(f"slot reuse call: {K.status_string(st)}")
+
+    total = n_layers * calls_per_layer
+    cost = rkv_cost(mode, 1, cap, budget)
+    r = time_calls(call, names, cost, total, 2 * n_layers, hip, traced_steps=512)
+    r["calls"] = total
+    r["tokens"] = total * cap
+    return r
+
+
 def run_batched(mode, hip, steps):
     """Batched prefill workload: 64 sequences of 8192 tokens, B = 1024 (1 GiB
     of K and 1 GiB of V, far beyond the 256 MB last-level cache)."""
@@ -478,6 +548,25 @@ def run_variants(a, hip) -> dict:
                 "loop_ms": round(r["ms_plain"] * r["calls"], 3),
                 "roofline": roofline(r, rkv_cost(mode, 1, 2176, 2048), a.profiles, f"decode_{mode}"),
                 "step_hbm_frac": hbm_frac(rkv_step_bytes(1, 2176, 2048), r["ms_plain"]),
+                "kernels": r["kernels"]}
+            torch.cuda.empty_cache()
+    if "decode" in want:
+        for mode in KERNELS:
+            r = run_decode_slots(mode, 32, hip)
+            log(f"decode_slots/{mode}", r)
+            tok = HKV * 2176
+            out[f"decode_slots_{mode}"] = {
+                "workload": "R-KV decode loop with slot reuse: 32 layers x 240 calls, each scoring "
+                            "a 2176-slot cache, listing the 128 evicted slots per head and "
+                            "writing the next 128 tokens into them (no compaction)",
+                "value": round(r["tokens"] / (r["ms_plain"] * 1e-3 * r["calls"]), 1),
+                "unit": "cache tokens scored/s", "us_per_call": round(r["ms_plain"] * 1000, 2),
+                "us_per_call_traced": round(r["ms"] * 1000, 2), "calls": r["calls"],
+                "loop_ms": round(r["ms_plain"] * r["calls"], 3),
+                "roofline": roofline(r, rkv_cost(mode, 1, 2176, 2048), a.profiles,
+                                     f"decode_slots_{mode}"),
+                "step_hbm_frac": hbm_frac(tok * D * 2 + 3 * 4 * tok + 4 * HKV * 128 * D * 2,
+                                          r["ms_plain"]),
                 "kernels": r["kernels"]}
             torch.cuda.empty_cache()
     if "batched" in want:

@@ -86,7 +86,7 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap) {
   w.gpart = c.take<float>(heads * (size_t)w.nsmax * cap);
   w.sel.nsc = (cap + kSelChunk - 1) / kSelChunk;
   w.sel.hist = c.take<uint32_t>(heads * kHistBins);
-  w.sel.thr = c.take<uint32_t>(heads * 2);
+  w.sel.thr = c.take<uint32_t>(heads * 4);
   w.sel.coff = c.take<uint32_t>(heads * w.sel.nsc);
   w.sel.ceqb = c.take<uint32_t>(heads * w.sel.nsc);
   w.bytes = (c.off + kAlign - 1) / kAlign * kAlign;
@@ -184,7 +184,7 @@ SelWs carve_select(Carver& c, int b, int hkv, int cap) {
   w.err = c.take<int32_t>(64);
   w.nsc = (cap + kSelChunk - 1) / kSelChunk;
   w.hist = c.take<uint32_t>(heads * kHistBins);
-  w.thr = c.take<uint32_t>(heads * 2);
+  w.thr = c.take<uint32_t>(heads * 4);
   w.coff = c.take<uint32_t>(heads * w.nsc);
   w.ceqb = c.take<uint32_t>(heads * w.nsc);
   return w;
@@ -311,6 +311,59 @@ kvsel_status kvsel_select_topb_heads(const float* z, const int32_t* lengths,
                      stream);
 }
 
+// Slot-reuse arguments: the evicted list must hold n - min(B_h, n) <= cap - B
+// entries per head (cap with per-head budgets, which may be 0).
+static kvsel_status check_slot_args(const int32_t* evict_out, int evict_stride,
+                                    const int32_t* n_evict_out, const int32_t* budgets, int cap,
+                                    int budget) {
+  if (!evict_out || !n_evict_out) return KVSEL_ERR_INVALID_ARG;
+  if (cap > kSelectLdsKeys) return KVSEL_ERR_UNSUPPORTED;
+  const int need = budgets ? cap : (cap > budget ? cap - budget : 0);
+  if (evict_stride < 1 || evict_stride < need) return KVSEL_ERR_INVALID_ARG;
+  return KVSEL_OK;
+}
+
+kvsel_status kvsel_select_evict_slots(const float* z, const int32_t* lengths, const int32_t* pos,
+                                      const int32_t* budgets, int b, int hkv, int cap, int budget,
+                                      int32_t* evict_out, int evict_stride, int32_t* n_evict_out,
+                                      void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!z || !lengths) return KVSEL_ERR_INVALID_ARG;
+  if (b < 1 || hkv < 1 || cap < 1 || budget < 1) return KVSEL_ERR_INVALID_ARG;
+  if (b > 65535 || hkv > 65535 || budget > 65536) return KVSEL_ERR_UNSUPPORTED;
+  kvsel_status st = check_slot_args(evict_out, evict_stride, n_evict_out, budgets, cap, budget);
+  if (st != KVSEL_OK) return st;
+  if (!workspace || ws_bytes < kvsel_select_workspace(b, hkv, cap)) return KVSEL_ERR_WORKSPACE;
+  Carver c{static_cast<char*>(workspace)};
+  const SelWs w = carve_select(c, b, hkv, cap);
+  SelectParams p = select_params(w, z, lengths, b, hkv, cap, budget, nullptr);
+  p.budgets = budgets;
+  p.pos = pos;
+  p.evict = evict_out;
+  p.evict_stride = evict_stride;
+  p.n_evict = n_evict_out;
+  KV_TRY(launch_hist(p, stream, nullptr));  // also clears the error word
+  return hip_status(launch_select_slots(p, stream, nullptr));
+}
+
+kvsel_status kvsel_slots_write(kvsel_dtype dt, void* k, void* v, int32_t* pos, const void* k_new,
+                               const void* v_new, const int32_t* pos_new, const int32_t* evict,
+                               int evict_stride, const int32_t* n_evict, int b, int hkv, int d,
+                               int cap, int count, hipStream_t stream) {
+  if (dt != KVSEL_BF16 && dt != KVSEL_F32) return KVSEL_ERR_INVALID_ARG;
+  if (!k || !v || !k_new || !v_new || !evict || !n_evict) return KVSEL_ERR_INVALID_ARG;
+  if (pos && !pos_new) return KVSEL_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_new) || !aligned16(v_new))
+    return KVSEL_ERR_INVALID_ARG;
+  if (b < 1 || hkv < 1 || cap < 1 || count < 0 || evict_stride < 1) return KVSEL_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return KVSEL_ERR_UNSUPPORTED;
+  if (b > 65535 || hkv > 65535 || cap >= (1 << 24)) return KVSEL_ERR_UNSUPPORTED;
+  if (count == 0) return KVSEL_OK;
+  SlotWriteParams p{static_cast<char*>(k), static_cast<char*>(v), pos,
+                    static_cast<const char*>(k_new), static_cast<const char*>(v_new), pos_new,
+                    evict, evict_stride, n_evict, b, hkv, cap, count};
+  return hip_status(launch_slots_write(dt, d, p, stream, nullptr));
+}
+
 kvsel_status kvsel_gather(kvsel_dtype dt, const void* k, const void* v, const int32_t* idx, int b,
                           int hkv, int d, int cap, int budget, void* k_out, void* v_out,
                           int cap_out, hipStream_t stream) {
@@ -424,6 +477,71 @@ kvsel_status kvsel_score_evict_heads_traced(kvsel_dtype dt, kvsel_redundancy mod
   return score_evict_impl(dt, mode, q_window, k, v, lengths, budgets, b, hq, hkv, d, w, cap,
                           lambda, budget_max, k_out, v_out, cap_out, idx_out, scores_out,
                           workspace, ws_bytes, stream, &tr);
+}
+
+static kvsel_status score_evict_slots_impl(kvsel_dtype dt, kvsel_redundancy mode,
+                                           const void* q_window, const void* k,
+                                           const int32_t* lengths, const int32_t* pos,
+                                           const int32_t* budgets, int b, int hq, int hkv, int d,
+                                           int w, int cap, float lambda, int budget,
+                                           int32_t* evict_out, int evict_stride,
+                                           int32_t* n_evict_out, float* scores_out,
+                                           void* workspace, size_t ws_bytes, hipStream_t stream,
+                                           Trace* tr) {
+  kvsel_status st = check_score_args(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda);
+  if (st != KVSEL_OK) return st;
+  if (budget < 1) return KVSEL_ERR_INVALID_ARG;
+  if (budget > 65536) return KVSEL_ERR_UNSUPPORTED;
+  st = check_slot_args(evict_out, evict_stride, n_evict_out, budgets, cap, budget);
+  if (st != KVSEL_OK) return st;
+  const ScoreWs need = score_ws(nullptr, b, hkv, d, (hq / hkv) * w, cap);
+  if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
+  const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap);
+  float* z = scores_out ? scores_out : ws.z;
+  st = run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, nullptr, nullptr,
+                  z, ws.sel.hist, ws, stream, tr);
+  if (st != KVSEL_OK) return st;
+  SelWs sw;
+  sw.hist = ws.sel.hist;
+  sw.thr = ws.sel.thr;
+  sw.coff = ws.sel.coff;
+  sw.ceqb = ws.sel.ceqb;
+  sw.nsc = ws.sel.nsc;
+  sw.err = ws.err;
+  SelectParams sp = select_params(sw, z, lengths, b, hkv, cap, budget, nullptr);
+  sp.budgets = budgets;
+  sp.pos = pos;
+  sp.evict = evict_out;
+  sp.evict_stride = evict_stride;
+  sp.n_evict = n_evict_out;
+  return hip_status(launch_select_slots(sp, stream, tr));
+}
+
+kvsel_status kvsel_score_evict_slots(kvsel_dtype dt, kvsel_redundancy mode, const void* q_window,
+                                     const void* k, const int32_t* lengths, const int32_t* pos,
+                                     const int32_t* budgets, int b, int hq, int hkv, int d, int w,
+                                     int cap, float lambda, int budget, int32_t* evict_out,
+                                     int evict_stride, int32_t* n_evict_out, float* scores_out,
+                                     void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return score_evict_slots_impl(dt, mode, q_window, k, lengths, pos, budgets, b, hq, hkv, d, w,
+                                cap, lambda, budget, evict_out, evict_stride, n_evict_out,
+                                scores_out, workspace, ws_bytes, stream, nullptr);
+}
+
+kvsel_status kvsel_score_evict_slots_traced(kvsel_dtype dt, kvsel_redundancy mode,
+                                            const void* q_window, const void* k,
+                                            const int32_t* lengths, const int32_t* pos,
+                                            const int32_t* budgets, int b, int hq, int hkv, int d,
+                                            int w, int cap, float lambda, int budget,
+                                            int32_t* evict_out, int evict_stride,
+                                            int32_t* n_evict_out, float* scores_out,
+                                            void* workspace, size_t ws_bytes, hipStream_t stream,
+                                            hipEvent_t* events, int n_events) {
+  if (!events || n_events < 2) return KVSEL_ERR_INVALID_ARG;
+  Trace tr{events, n_events, 0};
+  return score_evict_slots_impl(dt, mode, q_window, k, lengths, pos, budgets, b, hq, hkv, d, w,
+                                cap, lambda, budget, evict_out, evict_stride, n_evict_out,
+                                scores_out, workspace, ws_bytes, stream, &tr);
 }
 
 size_t kvsel_threshold_cut_workspace(int b, int hq, int hkv, int d, int cap) {

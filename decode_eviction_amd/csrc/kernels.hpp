@@ -71,7 +71,7 @@ struct SelectParams {
   int32_t* idx;             // [b][Hkv][budget]
   uint32_t* hist;           // [b][Hkv][kHistBins]: first-level key histogram of z
   // split select (cap <= kSelectLdsKeys): threshold per head, offsets per chunk
-  uint32_t* thr;            // [b][Hkv][2]: threshold key, copies of it to keep
+  uint32_t* thr;            // [b][Hkv][4]: threshold key, copies of it to keep, copies in all
   uint32_t* coff;           // [b][Hkv][nsc]: output slot of the chunk's first kept position
   uint32_t* ceqb;           // [b][Hkv][nsc]: keys equal to the threshold before the chunk
   int nsc;                  // ceil(cap / kSelChunk)
@@ -85,6 +85,24 @@ struct SelectParams {
   // budget being the row stride of idx and of the compacted cache
   const int32_t* budgets;   // [Hkv]
   int32_t* err;             // nullable error word: bit 0 length > cap, bit 1 budget clamped
+  // slot reuse (no compaction): evicted slots instead of kept positions
+  const int32_t* pos;       // nullable [b][Hkv][cap]: token position held by each slot
+  int32_t* evict;           // [b][Hkv][evict_stride]: evicted slots ascending, then -1
+  int evict_stride;
+  int32_t* n_evict;         // [b][Hkv]
+};
+
+struct SlotWriteParams {
+  char* k;                  // [b][Hkv][cap][d]
+  char* v;
+  int32_t* pos;             // nullable [b][Hkv][cap]
+  const char* k_new;        // [b][Hkv][count][d]
+  const char* v_new;
+  const int32_t* pos_new;   // nullable [b]: position of new token 0
+  const int32_t* evict;     // [b][Hkv][evict_stride]
+  int evict_stride;
+  const int32_t* n_evict;   // [b][Hkv]
+  int b, hkv, cap, count;
 };
 
 struct GatherParams {
@@ -138,6 +156,8 @@ hipError_t launch_gram(int dt, int d, const GramParams& p, hipStream_t s, Trace*
 hipError_t launch_select(const SelectParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_hist(const SelectParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_select_err_zero(const SelectParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_select_slots(const SelectParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_slots_write(int dt, int d, const SlotWriteParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_gather(int dt, int d, const GatherParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_cut_energy(const CutParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_cut_scan(const CutParams& p, hipStream_t s, Trace* tr);

@@ -257,9 +257,11 @@ __device__ __forceinline__ void write_chunk_offsets(const SelectParams& p, long 
     p.coff[head * p.nsc + lane] = y2 - kept;
     p.ceqb[head * p.nsc + lane] = eqb;
   }
+  const uint32_t eq_all = __shfl(x, 63, 64);  // keys equal to the threshold in all chunks
   if (lane == 0) {
-    p.thr[head * 2 + 0] = kth;
-    p.thr[head * 2 + 1] = need_eq;
+    p.thr[head * 4 + 0] = kth;
+    p.thr[head * 4 + 1] = need_eq;
+    p.thr[head * 4 + 2] = eq_all;
   }
 }
 
@@ -511,8 +513,8 @@ __global__ __launch_bounds__(256) void k_compact(SelectParams p) {
   const bool all = n <= B;
   uint32_t kth = 0, need_eq = 0, off = 0, eqb = 0;
   if (!all) {
-    kth = p.thr[head * 2 + 0];
-    need_eq = p.thr[head * 2 + 1];
+    kth = p.thr[head * 4 + 0];
+    need_eq = p.thr[head * 4 + 1];
     off = p.coff[head * p.nsc + chunk];
     eqb = p.ceqb[head * p.nsc + chunk];
   } else {
@@ -605,6 +607,187 @@ __global__ __launch_bounds__(256) void k_compact(SelectParams p) {
       }
     }
   }
+}
+
+// ------------------------------------------------------------- slot reuse
+//
+// Gather-free eviction (the ThinKV page's argument against compaction: a
+// gather rewrites almost the whole cache every time it runs): the cache stays
+// in place and the evicted slots are listed for new tokens to overwrite.  A
+// slot's token position comes from the caller's position map, so the tie rule
+// (equal score: the earlier token is kept) follows positions, not slots.
+//
+// Tied slots of one head split by token position, for k_evict_slots: an
+// adaptive radix select over ~pos (larger for earlier tokens) among the tied
+// slots gives the position threshold kth2 and the copies need2 of it to keep
+// (by slot order).  Returns, per lane, the tied slots above kth2 (g2m) and at
+// kth2 (e2m) as masks over the 32 rounds, and the first rank (r2) of this
+// lane's wave among the kth2 copies.  Kept out of line: ties that split are
+// rare, and inlined, its registers would spill in the common path.
+struct TieSplit {
+  uint32_t g2m, e2m, r2, need2;
+};
+
+__device__ __noinline__ TieSplit split_ties_by_position(const int32_t* ps, int w0, int lane,
+                                                        int wave, int tid, uint32_t eqm,
+                                                        uint32_t need_eq, uint32_t* hist,
+                                                        uint32_t* wsum, uint32_t* bc,
+                                                        uint32_t* wtot) {
+  constexpr int S = kKeysPerThread;
+  auto kpos = [&](int i) -> uint32_t {
+    const int s = w0 + kWave * i + lane;
+    return ~(uint32_t)(ps ? ps[s] : s);
+  };
+  uint32_t lo = 0u, hi = 0xffffffffu, need = need_eq;
+  while (lo < hi)
+    refine_round<kRegWaves>(lo, hi, need, hist, wsum, bc, tid, [&](auto f) {
+      for (int i = 0; i < S; ++i)
+        if ((eqm >> i) & 1u) f(kpos(i));
+    });
+  TieSplit t{0u, 0u, 0u, need};
+  uint32_t wc = 0u;
+  for (int i = 0; i < S; ++i) {
+    bool e2 = false;
+    if ((eqm >> i) & 1u) {
+      const uint32_t k2 = kpos(i);
+      t.g2m |= (k2 > lo ? 1u : 0u) << i;
+      e2 = k2 == lo;
+    }
+    t.e2m |= (e2 ? 1u : 0u) << i;
+    wc += (uint32_t)__popcll(__ballot(e2));
+  }
+  if (lane == 0) wtot[wave] = wc;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) t.r2 += wtot[w];
+  return t;
+}
+
+// k_evict_slots runs after k_select_thresh, which leaves the threshold key
+// kth, the number need_eq of slots with key kth to keep and the number of
+// such slots.  When only part of the tied slots is kept, the ones with the
+// lowest positions are taken: an adaptive radix select over ~pos among the
+// tied slots (equal positions, which a well-formed map does not have, fall
+// back to slot order).  One 1024-thread work-group per head; wave w owns
+// slots 2048w .. 2048w+2047, read 64 at a time (lane l: slot 2048w + 64i + l),
+// so loads are coalesced and the evicted list comes out in slot order from
+// ballots within the wave and one exchange of wave totals.
+__global__ __launch_bounds__(kRegThreads) void k_evict_slots(SelectParams p) {
+  constexpr int S = kKeysPerThread;          // rounds of 64 slots per wave
+  __shared__ uint32_t hist[kSelBins];
+  __shared__ uint32_t wsum[kRegWaves];
+  __shared__ uint32_t wtot[2][kRegWaves];
+  __shared__ uint32_t bc[2];
+  const int h = blockIdx.x, bi = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = min(p.lengths[bi], p.cap);
+  const int B = head_budget(p, h);
+  const long head = (long)bi * p.hkv + h;
+  int32_t* out = p.evict + head * p.evict_stride;
+  const int ne = n > B ? n - B : 0;
+  if (tid == 0) p.n_evict[head] = ne;
+  for (int t = ne + tid; t < p.evict_stride; t += kRegThreads) out[t] = -1;
+  if (ne == 0) return;
+  if (B == 0) {  // everything goes
+    for (int t = tid; t < n; t += kRegThreads) out[t] = t;
+    return;
+  }
+  const uint32_t kth = p.thr[head * 4 + 0];
+  const uint32_t need_eq = p.thr[head * 4 + 1];
+  const uint32_t count_eq = p.thr[head * 4 + 2];
+  const bool split = need_eq > 0u && need_eq < count_eq;
+  const bool keep_eq = need_eq >= count_eq;  // when not split: all tied slots kept, or none
+  const float* z = p.z + head * p.cap;
+  const int32_t* ps = p.pos ? p.pos + head * p.cap : nullptr;
+  const int w0 = wave * S * kWave;
+  // key flags; the loads go through a buffer resource (slots past n read 0)
+  // so that all are in flight before use, and only bit masks outlive the loop
+  uint32_t gtm = 0u, eqm = 0u;
+  {
+    const __amdgpu_buffer_rsrc_t rz = buf_rsrc(z, (uint32_t)n * 4u);
+    uint32_t zv[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) zv[i] = buf_ld32(rz, (uint32_t)(w0 + lane) * 4u, (uint32_t)(kWave * 4 * i));
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const bool ok = w0 + kWave * i + lane < n;
+      const uint32_t key = score_key(__uint_as_float(zv[i]));
+      gtm |= (ok && key > kth ? 1u : 0u) << i;
+      eqm |= (ok && key == kth ? 1u : 0u) << i;
+    }
+  }
+  // tied slots split by position (rare): kept are the tied slots with ~pos
+  // above kth2 and the first need2 (in slot order) with ~pos == kth2
+  TieSplit ts{0u, 0u, 0u, 0u};
+  if (split) ts = split_ties_by_position(ps, w0, lane, wave, tid, eqm, need_eq, hist, wsum, bc, wtot[0]);
+  const uint32_t g2m = ts.g2m, e2m = ts.e2m, need2 = ts.need2;
+  uint32_t r2 = ts.r2;
+  // evicted flags, counted per wave
+  uint32_t evm = 0u, wev = 0u;
+  for (int i = 0; i < S; ++i) {
+    const bool ok = w0 + kWave * i + lane < n;
+    bool kept = (gtm >> i) & 1u;
+    if ((eqm >> i) & 1u) kept = split ? ((g2m >> i) & 1u) != 0u : keep_eq;
+    if (split) {  // copies of (kth, kth2) in slot order
+      const uint64_t b2 = __ballot((e2m >> i) & 1u);
+      if ((e2m >> i) & 1u) kept = r2 + lanemask_lt_count(b2, lane) < need2;
+      r2 += (uint32_t)__popcll(b2);
+    }
+    const bool ev = ok && !kept;
+    evm |= (ev ? 1u : 0u) << i;
+    wev += (uint32_t)__popcll(__ballot(ev));
+  }
+  if (lane == 0) wtot[1][wave] = wev;
+  __syncthreads();
+  uint32_t o = 0u;
+  for (int w = 0; w < wave; ++w) o += wtot[1][w];
+  for (int i = 0; i < S; ++i) {
+    const uint64_t be = __ballot((evm >> i) & 1u);
+    if ((evm >> i) & 1u) {
+      const uint32_t at = o + lanemask_lt_count(be, lane);
+      if (at < (uint32_t)ne) out[at] = w0 + kWave * i + lane;
+    }
+    o += (uint32_t)__popcll(be);
+  }
+}
+
+hipError_t launch_select_slots(const SelectParams& p, hipStream_t s, Trace* tr) {
+  hipError_t e = launch_k(k_select_thresh, dim3(p.hkv, p.b), dim3(kRegThreads), s, tr, p);
+  if (e != hipSuccess) return e;
+  return launch_k(k_evict_slots, dim3(p.hkv, p.b), dim3(kRegThreads), s, tr, p);
+}
+
+// New tokens into evicted slots: token t < min(count, n_evict) of each head
+// replaces slot evict[t] (bit copies of its K and V rows) and, with a
+// position map, records position pos_new[b] + t there.  One 16-byte piece
+// per thread.
+template <int RB>
+__global__ __launch_bounds__(256) void k_slots_write(SlotWriteParams p) {
+  constexpr int CPR = RB / 16;
+  constexpr int RPW = 256 / CPR;
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const int t = blockIdx.x * RPW + threadIdx.x / CPR, c = threadIdx.x % CPR;
+  const long head = (long)bi * p.hkv + h;
+  if (t >= p.count || t >= p.n_evict[head]) return;
+  const int slot = p.evict[head * p.evict_stride + t];
+  if (slot < 0 || slot >= p.cap) return;
+  const long src = (head * p.count + t) * (long)RB + c * 16;
+  const long dst = (head * p.cap + slot) * (long)RB + c * 16;
+  const u32x4_t kv = ld16(p.k_new + src), vv = ld16(p.v_new + src);
+  *reinterpret_cast<u32x4_t*>(p.k + dst) = kv;
+  *reinterpret_cast<u32x4_t*>(p.v + dst) = vv;
+  if (c == 0 && p.pos) p.pos[head * p.cap + slot] = p.pos_new[bi] + t;
+}
+
+hipError_t launch_slots_write(int dt, int d, const SlotWriteParams& p, hipStream_t s, Trace* tr) {
+  const int rb = d * (dt == 0 ? 2 : 4);
+  auto go = [&](auto kern, int rpw) {
+    return launch_k(kern, dim3((p.count + rpw - 1) / rpw, p.hkv, p.b), dim3(256), s, tr, p);
+  };
+  switch (rb) {
+    case 128: return go(k_slots_write<128>, 256 / 8);
+    case 256: return go(k_slots_write<256>, 256 / 16);
+    case 512: return go(k_slots_write<512>, 256 / 32);
+  }
+  return hipErrorInvalidValue;
 }
 
 // Stage entry (scores given by the caller): zero, then fill the first-level

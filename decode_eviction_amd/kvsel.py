@@ -43,6 +43,12 @@ _SIGS = {
                                             _F, _I, _P, _P, _I, _P, _P, _P, _S, _P, _P, _I]),
     "kvsel_score_evict_traced": (_I, [_I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                                       _P, _P, _I, _P, _P, _P, _S, _P, _P, _I]),
+    "kvsel_select_evict_slots": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _S, _P]),
+    "kvsel_score_evict_slots": (_I, [_I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                                     _P, _I, _P, _P, _P, _S, _P]),
+    "kvsel_score_evict_slots_traced": (_I, [_I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                            _F, _I, _P, _I, _P, _P, _P, _S, _P, _P, _I]),
+    "kvsel_slots_write": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P]),
     "kvsel_threshold_cut_workspace": (_S, [_I] * 5),
     "kvsel_threshold_cut_traced": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P,
                                         _P, _S, _P, _P, _I]),
@@ -233,6 +239,58 @@ def kvsel_score_evict_heads(q_window, k, v, lengths, budgets, budget_max, lam=0.
                                        ws.numel(), _stream(stream))
     _check("kvsel_score_evict_heads", st)
     return k_out, v_out, idx_out
+
+
+# ------------------------------------------------------------------ slot reuse
+
+def kvsel_select_evict_slots(z, lengths, budget, pos=None, budgets=None, evict_out=None,
+                             n_evict_out=None, workspace=None, stream=None):
+    """Evicted slots (ascending, -1 padded) and their count per (sequence, KV head)."""
+    _need_cuda(z, lengths, pos, budgets, evict_out, n_evict_out)
+    b, hkv, cap = z.shape
+    if evict_out is None:
+        evict_out = torch.empty((b, hkv, cap), dtype=torch.int32, device=z.device)
+    if n_evict_out is None:
+        n_evict_out = torch.empty((b, hkv), dtype=torch.int32, device=z.device)
+    ws = _workspace(kvsel_select_workspace(b, hkv, cap), z.device, workspace)
+    st = lib().kvsel_select_evict_slots(_ptr(z), _ptr(lengths), _ptr(pos), _ptr(budgets), b, hkv,
+                                        cap, int(budget), _ptr(evict_out), evict_out.shape[2],
+                                        _ptr(n_evict_out), _ptr(ws), ws.numel(), _stream(stream))
+    _check("kvsel_select_evict_slots", st)
+    return evict_out, n_evict_out
+
+
+def kvsel_score_evict_slots(q_window, k, lengths, budget, lam=0.1, mode="gram", pos=None,
+                            budgets=None, evict_out=None, n_evict_out=None, scores_out=None,
+                            workspace=None, stream=None):
+    """Scores and evicted slots in one call; returns (evict_out, n_evict_out)."""
+    _need_cuda(q_window, k, lengths, pos, budgets, evict_out, n_evict_out, scores_out)
+    b, hq, w, d = q_window.shape
+    _, hkv, cap, _ = k.shape
+    dev = k.device
+    if evict_out is None:
+        evict_out = torch.empty((b, hkv, cap), dtype=torch.int32, device=dev)
+    if n_evict_out is None:
+        n_evict_out = torch.empty((b, hkv), dtype=torch.int32, device=dev)
+    ws = _workspace(kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, budget), dev, workspace)
+    st = lib().kvsel_score_evict_slots(_dtype(k), MODES[mode], _ptr(q_window), _ptr(k),
+                                       _ptr(lengths), _ptr(pos), _ptr(budgets), b, hq, hkv, d, w,
+                                       cap, float(lam), int(budget), _ptr(evict_out),
+                                       evict_out.shape[2], _ptr(n_evict_out), _ptr(scores_out),
+                                       _ptr(ws), ws.numel(), _stream(stream))
+    _check("kvsel_score_evict_slots", st)
+    return evict_out, n_evict_out
+
+
+def kvsel_slots_write(k, v, k_new, v_new, evict, n_evict, pos=None, pos_new=None, stream=None):
+    """Copy new tokens [b][Hkv][count][d] into the evicted slots of k/v (in place)."""
+    _need_cuda(k, v, k_new, v_new, evict, n_evict, pos, pos_new)
+    b, hkv, cap, d = k.shape
+    count = k_new.shape[2]
+    st = lib().kvsel_slots_write(_dtype(k), _ptr(k), _ptr(v), _ptr(pos), _ptr(k_new), _ptr(v_new),
+                                 _ptr(pos_new), _ptr(evict), evict.shape[2], _ptr(n_evict), b, hkv,
+                                 d, cap, count, _stream(stream))
+    _check("kvsel_slots_write", st)
 
 
 # ------------------------------------------------------------------ ReFreeKV

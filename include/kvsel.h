@@ -177,6 +177,59 @@ kvsel_status kvsel_score_evict_heads_traced(kvsel_dtype dt, kvsel_redundancy mod
                                             float* scores_out, void* workspace, size_t ws_bytes,
                                             hipStream_t stream, hipEvent_t* events, int n_events);
 
+/* ---------------------------------------------------------- slot reuse */
+
+/* Gather-free eviction for a cache that is never compacted (ThinKV page,
+ * "Continuous Thinking" section: compaction by gather rewrites the cache on
+ * every eviction, which evicted-slot reuse avoids).  Slots 0..n-1 of each
+ * (sequence, KV head) all hold tokens; pos [b][Hkv][cap] int32 (nullable:
+ * the slot index) holds the token position in each slot, non-negative and
+ * distinct per head.  The kept set is the min(B_h, n) largest scores, equal
+ * scores going to the lower token position (equal positions: lower slot), as
+ * in kvsel_select_topb; B_h is budget, or budgets[h] clamped to [0, budget]
+ * when budgets (nullable, [Hkv]) is given.  evict_out [b][Hkv][evict_stride]
+ * receives the other n - min(B_h, n) slots in ascending slot order, then -1;
+ * n_evict_out [b][Hkv] their count.  evict_stride >= cap - budget (>= cap
+ * with budgets).  Needs cap <= 32768.  Same workspace size as
+ * kvsel_select_topb. */
+kvsel_status kvsel_select_evict_slots(const float* z, const int32_t* lengths, const int32_t* pos,
+                                      const int32_t* budgets, int b, int Hkv, int cap, int budget,
+                                      int32_t* evict_out, int evict_stride, int32_t* n_evict_out,
+                                      void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Scores (as kvsel_scores) then kvsel_select_evict_slots in one call; k is
+ * read only.  Same workspace size as kvsel_score_evict. */
+kvsel_status kvsel_score_evict_slots(kvsel_dtype dt, kvsel_redundancy mode,
+                                     const void* q_window, const void* k, const int32_t* lengths,
+                                     const int32_t* pos, const int32_t* budgets,
+                                     int b, int Hq, int Hkv, int d, int w, int cap, float lambda,
+                                     int budget, int32_t* evict_out, int evict_stride,
+                                     int32_t* n_evict_out, float* scores_out,
+                                     void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* kvsel_score_evict_slots with per-kernel timing as in kvsel_score_evict_traced.
+ * Launch order: the score kernels of the mode, threshold, evict. */
+kvsel_status kvsel_score_evict_slots_traced(kvsel_dtype dt, kvsel_redundancy mode,
+                                            const void* q_window, const void* k,
+                                            const int32_t* lengths, const int32_t* pos,
+                                            const int32_t* budgets, int b, int Hq, int Hkv, int d,
+                                            int w, int cap, float lambda, int budget,
+                                            int32_t* evict_out, int evict_stride,
+                                            int32_t* n_evict_out, float* scores_out,
+                                            void* workspace, size_t ws_bytes, hipStream_t stream,
+                                            hipEvent_t* events, int n_events);
+
+/* New tokens into evicted slots: for each (sequence, KV head), token t <
+ * min(count, n_evict[b][h]) of k_new/v_new [b][Hkv][count][d] is copied (bit
+ * copy) into slot evict[b][h][t] of k/v [b][Hkv][cap][d], and, when pos is
+ * given, pos[b][h][slot] = pos_new[b] + t (pos_new [b] required then).
+ * Tokens beyond the evicted count are not written; evict entries outside
+ * [0, cap) are skipped. */
+kvsel_status kvsel_slots_write(kvsel_dtype dt, void* k, void* v, int32_t* pos,
+                               const void* k_new, const void* v_new, const int32_t* pos_new,
+                               const int32_t* evict, int evict_stride, const int32_t* n_evict,
+                               int b, int Hkv, int d, int cap, int count, hipStream_t stream);
+
 /* ------------------------------------------------------------ ReFreeKV */
 
 size_t kvsel_threshold_cut_workspace(int b, int Hq, int Hkv, int d, int cap);

@@ -116,6 +116,24 @@ def top_budget(z: np.ndarray, budget: int) -> np.ndarray:
     return np.sort(order[:budget]).astype(np.int64)
 
 
+def evict_slots(z: np.ndarray, budget: int, pos=None) -> np.ndarray:
+    """Slot reuse without compaction: the slots NOT among the min(budget, n)
+    largest z, ascending.  Equal z: the lower token position pos[slot] is
+    kept (the earlier token counts as the original); equal positions: the
+    lower slot.  pos defaults to the slot index (then the kept set is
+    top_budget's)."""
+    z = np.asarray(z, np.float64)
+    n = z.shape[0]
+    slots = np.arange(n)
+    pos = slots if pos is None else np.asarray(pos, np.int64)
+    if n <= budget:
+        return np.zeros(0, dtype=np.int64)
+    order = np.lexsort((slots, pos, -z))          # by -z, then position, then slot
+    keep = np.zeros(n, dtype=bool)
+    keep[order[:max(budget, 0)]] = True
+    return slots[~keep].astype(np.int64)
+
+
 def head_scores(q_rows, k, lam, form: str = "definition"):
     """(I, R, Z) of one KV head.  form: "definition" or "keysum" for R."""
     i_sc = importance(q_rows, k)

@@ -1,0 +1,177 @@
+"""Slot reuse (gather-free eviction) on the GPU against the fp64 oracle.
+
+The cache is never compacted: each call lists the evicted slots of every
+(sequence, KV head) and new tokens overwrite them (ThinKV page, "Continuous
+Thinking" section, on why compaction by gather is avoided).  A position map
+orders ties by token position.  Cases: the evicted lists on given scores
+(bit-exact, with position ties split at the threshold, duplicate positions
+and per-head budgets), the slot write (bit copies and position updates), and
+a decode loop at the R1-Llama-8B shape where each step is checked on the
+GPU's own pre-step cache.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from decode_eviction_amd import kvsel as K
+from decode_eviction_amd import synth
+from oracle import rkv
+from tests.gpu_util import SWAP_WINDOW, dev, dev_i32, host_bits, log, score_err, swaps
+
+pytestmark = pytest.mark.gpu
+
+
+def _kept(evicted, n):
+    gone = set(int(s) for s in evicted if s >= 0)
+    return np.array([s for s in range(n) if s not in gone], np.int64)
+
+
+@pytest.mark.parametrize("n,cap,budget,kind", [
+    (2176, 2176, 2048, "ties"), (5000, 5000, 900, "ties"), (32768, 32768, 2048, "normal"),
+    (1500, 2000, 1499, "allequal"), (300, 512, 400, "normal"), (4000, 4096, 1000, "duppos")])
+def test_evict_slots_stage_exact(n, cap, budget, kind):
+    rng = np.random.default_rng(21)
+    hkv = 3
+    if kind in ("ties", "duppos"):
+        z = (rng.integers(-40, 40, size=(2, hkv, cap)) * 2.0 ** -12).astype(np.float32)
+    elif kind == "allequal":
+        z = np.full((2, hkv, cap), -0.125, np.float32)
+    else:
+        z = rng.standard_normal((2, hkv, cap)).astype(np.float32) * 1e-3
+    if kind == "duppos":
+        pos = np.broadcast_to(np.arange(cap) // 3, (2, hkv, cap)).copy().astype(np.int32)
+    else:
+        pos = np.stack([np.stack([rng.permutation(50_000)[:cap] for _ in range(hkv)])
+                        for _ in range(2)]).astype(np.int32)
+    lens = np.array([n, max(1, n // 2)], np.int32)
+    log(f"[slots] n={n} cap={cap} B={budget} {kind}")
+    ev, ne = K.kvsel_select_evict_slots(dev(z, "f32"), dev_i32(lens), budget, pos=dev_i32(pos))
+    ev, ne = ev.cpu().numpy(), ne.cpu().numpy()
+    ev0, _ = K.kvsel_select_evict_slots(dev(z, "f32"), dev_i32(lens), budget)   # slot order
+    ev0 = ev0.cpu().numpy()
+    for b in range(2):
+        nb = int(lens[b])
+        for h in range(hkv):
+            want = rkv.evict_slots(z[b, h, :nb].astype(np.float64), budget, pos[b, h, :nb])
+            assert ne[b, h] == len(want)
+            assert ev[b, h, :len(want)].tolist() == want.tolist(), (kind, b, h)
+            assert (ev[b, h, len(want):] == -1).all()
+            want0 = rkv.evict_slots(z[b, h, :nb].astype(np.float64), budget)
+            assert ev0[b, h, :len(want0)].tolist() == want0.tolist()
+
+
+def test_evict_slots_per_head_budgets():
+    rng = np.random.default_rng(22)
+    hkv, cap, n = 5, 3000, 2900
+    z = (rng.integers(-30, 30, size=(1, hkv, cap)) * 2.0 ** -10).astype(np.float32)
+    pos = np.stack([rng.permutation(cap) for _ in range(hkv)])[None].astype(np.int32)
+    budgets = np.array([0, 1, 1450, 2900, 5000], np.int32)
+    ws = torch.empty(K.kvsel_select_workspace(1, hkv, cap), dtype=torch.uint8, device="cuda")
+    ev, ne = K.kvsel_select_evict_slots(dev(z, "f32"), dev_i32([n]), 3000, pos=dev_i32(pos),
+                                        budgets=dev_i32(budgets), workspace=ws)
+    assert K.kvsel_workspace_error(ws) == 2                 # 5000 > 3000 was clamped
+    ev, ne = ev.cpu().numpy(), ne.cpu().numpy()
+    for h in range(hkv):
+        bh = rkv.head_budget(budgets, h, 3000)
+        want = rkv.evict_slots(z[0, h, :n].astype(np.float64), bh, pos[0, h, :n])
+        assert ne[0, h] == len(want) == max(n - bh, 0)
+        assert ev[0, h, :len(want)].tolist() == want.tolist(), h
+
+
+def test_slots_write_bit_exact():
+    rng = np.random.default_rng(23)
+    for dtype, d in [("bf16", 128), ("f32", 64)]:
+        b, hkv, cap, count = 2, 3, 200, 16
+        if dtype == "bf16":
+            kh = rng.integers(0, 65536, size=(b, hkv, cap, d), dtype=np.uint16)
+            kn = rng.integers(0, 65536, size=(b, hkv, count, d), dtype=np.uint16)
+        else:
+            kh = rng.standard_normal((b, hkv, cap, d)).astype(np.float32)
+            kn = rng.standard_normal((b, hkv, count, d)).astype(np.float32)
+        vh, vn = kh[..., ::-1].copy(), kn[..., ::-1].copy()
+        ev = np.full((b, hkv, cap), -1, np.int32)
+        ne = np.zeros((b, hkv), np.int32)
+        for bb in range(b):
+            for h in range(hkv):
+                m = [20, 16, 5][h]
+                ev[bb, h, :m] = np.sort(rng.choice(cap, m, replace=False))
+                ne[bb, h] = m
+        pos = np.arange(b * hkv * cap, dtype=np.int32).reshape(b, hkv, cap)
+        pos_new = np.array([1000, 5000], np.int32)
+        k_d, v_d, p_d = dev(kh, dtype), dev(vh, dtype), dev_i32(pos)
+        K.kvsel_slots_write(k_d, v_d, dev(kn, dtype), dev(vn, dtype), dev_i32(ev), dev_i32(ne),
+                            pos=p_d, pos_new=dev_i32(pos_new))
+        kg, vg, pg = host_bits(k_d), host_bits(v_d), p_d.cpu().numpy()
+        kb = kh if dtype == "bf16" else kh.view(np.uint32)
+        vb = vh if dtype == "bf16" else vh.view(np.uint32)
+        knb = kn if dtype == "bf16" else kn.view(np.uint32)
+        vnb = vn if dtype == "bf16" else vn.view(np.uint32)
+        for bb in range(b):
+            for h in range(hkv):
+                m = min(count, int(ne[bb, h]))
+                slots = ev[bb, h, :m]
+                want_k, want_v, want_p = kb[bb, h].copy(), vb[bb, h].copy(), pos[bb, h].copy()
+                want_k[slots], want_v[slots] = knb[bb, h, :m], vnb[bb, h, :m]
+                want_p[slots] = pos_new[bb] + np.arange(m)
+                assert np.array_equal(kg[bb, h], want_k) and np.array_equal(vg[bb, h], want_v)
+                assert np.array_equal(pg[bb, h], want_p)
+
+
+B, BUF, W, LAM = 2048, 128, 8, 0.1
+
+
+@pytest.mark.parametrize("layer,mode,calls", [(3, "keysum", 60), (21, "gram", 24)])
+def test_decode_loop_slot_reuse(layer, mode, calls):
+    """The decode loop without compaction: each call frees 128 slots per head
+    and the next 128 tokens take them; slots always hold the stream's tokens
+    at the tracked positions."""
+    st = synth.decode_stream(layer, total=B + BUF + calls * BUF)
+    cap, hkv, d = B + BUF, st.hkv, st.d
+    ks, vs = dev(st.k, "bf16"), dev(st.v, "bf16")          # [hkv][total][d]
+    kc = ks[None, :, :cap].clone()
+    vc = vs[None, :, :cap].clone()
+    pos_h = np.broadcast_to(np.arange(cap, dtype=np.int32), (1, hkv, cap)).copy()
+    pos = dev_i32(pos_h)
+    lens = dev_i32([cap])
+    z = torch.empty((1, hkv, cap), dtype=torch.float32, device="cuda")
+    ws = torch.empty(K.kvsel_score_evict_workspace(1, st.hq, hkv, d, W, cap, B), dtype=torch.uint8,
+                     device="cuda")
+    t, worst, nswaps = cap, 0.0, 0
+    for call in range(calls):
+        qw = dev(st.window(t, W), "bf16")
+        check = call % 6 == 0
+        if check:
+            k_pre, v_pre = host_bits(kc), host_bits(vc)
+        ev, ne = K.kvsel_score_evict_slots(qw, kc, lens, B, LAM, mode, pos=pos, scores_out=z,
+                                           workspace=ws)
+        ev_h, ne_h = ev.cpu().numpy()[0], ne.cpu().numpy()[0]
+        assert (ne_h == BUF).all()
+        if check:
+            zf = z.cpu().numpy()[0]
+            qf = synth.bf16_bits_to_f32(host_bits(qw))
+            ref = rkv.score_evict(qf, synth.bf16_bits_to_f32(k_pre), synth.bf16_bits_to_f32(v_pre),
+                                  [cap], LAM, B)
+            for h in range(hkv):
+                worst = max(worst, score_err(zf[h], ref["Z"][0][h]))
+                want = rkv.evict_slots(zf[h].astype(np.float64), B, pos_h[0, h])   # on GPU scores: exact
+                assert ev_h[h, :BUF].tolist() == want.tolist(), (call, h)
+                ref_ev = rkv.evict_slots(ref["Z"][0][h], B, pos_h[0, h])
+                ns, gap = swaps(_kept(ev_h[h, :BUF], cap), _kept(ref_ev, cap), ref["Z"][0][h])
+                nswaps += ns
+                assert gap < SWAP_WINDOW, (call, h, gap)
+        # the next BUF tokens take the freed slots
+        kn = ks[None, :, t:t + BUF].contiguous()
+        vn = vs[None, :, t:t + BUF].contiguous()
+        K.kvsel_slots_write(kc, vc, kn, vn, ev, ne, pos=pos, pos_new=dev_i32([t]))
+        for h in range(hkv):
+            pos_h[0, h, ev_h[h, :BUF]] = t + np.arange(BUF)
+        t += BUF
+        pg = pos.cpu().numpy()
+        assert np.array_equal(pg, pos_h), call
+        kg = host_bits(kc)[0]
+        for h in range(hkv):
+            assert np.array_equal(kg[h], st.k[h, pos_h[0, h]]), (call, h)
+    log(f"[slots decode] layer={layer} mode={mode}: {calls} calls, worst Z err {worst:.2e}, "
+        f"swaps {nswaps}")
+    assert worst <= 1e-3

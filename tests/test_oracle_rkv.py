@@ -219,6 +219,30 @@ def test_top_budget_nested(seed):
         prev = cur
 
 
+@pytest.mark.parametrize("seed", range(30))
+def test_evict_slots_brute_force(seed):
+    # a slot-ordered cache holding tokens in permuted positions: the kept set is
+    # the best subset under the tie rule applied to positions (brute force over
+    # subsets in position order), the evicted slots are the rest
+    rng = np.random.default_rng(500 + seed)
+    n = int(rng.integers(1, 12))
+    budget = int(rng.integers(0, 8))
+    z = rng.integers(-2, 3, size=n) * 0.25
+    pos = rng.permutation(1000)[:n]
+    order = np.argsort(pos)                       # slots by token position
+    kept = set(order[_brute_top(z[order], budget)].tolist())
+    want = [s for s in range(n) if s not in kept]
+    assert rkv.evict_slots(z, budget, pos).tolist() == want
+
+
+def test_evict_slots_identity_positions_complement_top_budget():
+    rng = np.random.default_rng(11)
+    for n, budget in [(500, 100), (64, 64), (64, 65), (300, 1)]:
+        z = rng.integers(-20, 20, size=n) * 0.5
+        keep = set(rkv.top_budget(z, budget).tolist())
+        assert rkv.evict_slots(z, budget).tolist() == [s for s in range(n) if s not in keep]
+
+
 def test_duplicate_copy_golden():
     g = _golden("rkv_duplicate_copy.txt")
     d, n, budget = int(g["d"][0]), int(g["n"][0]), int(g["budget"][0])
