@@ -429,6 +429,67 @@ def run_refreekv(hip, n_layers, steps):
     return r
 
 
+def run_refreekv_rows(hip, n_layers, steps, k_rows=64):
+    """The ReFreeKV cut from the last k_rows attention rows (the k > 1
+    ablation; 28 q / 4 KV heads, so 7 * k_rows rows per KV head, scored in
+    groups of 128) with the sink + suffix compaction of K and V, at the same
+    Qwen2.5-7B shape and lengths as run_refreekv."""
+    import torch
+
+    from decode_eviction_amd import kvsel as K
+    from decode_eviction_amd import synth
+    hq, hkv, b = 28, 4, 16
+    g = hq // hkv
+    lengths = synth.refreekv_lengths(0, b)
+    cap = int(lengths.max())
+    layers = []
+    for layer in range(2, 2 + n_layers):
+        c = synth.cut_case(layer=layer, seed=0, lengths=lengths, cap=cap)
+        v = np.random.default_rng(layer).integers(0, 65536, size=c.k.shape, dtype=np.uint16)
+        layers.append((bf16_dev(synth.cut_rows_q(c, k_rows)), bf16_dev(c.k), bf16_dev(v)))
+    ko = torch.empty_like(layers[0][1])
+    vo = torch.empty_like(layers[0][2])
+    lens = torch.from_numpy(lengths).to("cuda")
+    kept = torch.empty((b, hkv), dtype=torch.int32, device="cuda")
+    ws_bytes = K.kvsel_threshold_cut_rows_workspace(b, hq, hkv, D, cap, k_rows)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    lib = K.lib()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
+    rows = g * k_rows
+    groups = [min(128, rows - r0) for r0 in range(0, rows, 128)]
+    names = [f"{kind}_g{i}" for i in range(len(groups)) for kind in ("stats", "reduce", "cut_energy")]
+    names += ["cut_scan", "cut_compact"]
+    tok = int(lengths.sum()) * hkv
+    cost = {"cut_scan": {"bytes": 0}}
+    for i, m in enumerate(groups):
+        cost[f"stats_g{i}"] = {"bytes": tok * D * 2 + tok * m * 4}
+        cost[f"reduce_g{i}"] = {"bytes": 0}
+        cost[f"cut_energy_g{i}"] = {"bytes": tok * m * 4 + tok * 8 * (2 if i else 1)}
+
+    def call(i, events=None):
+        q, k, v = layers[i % len(layers)]
+        args = (K.KVSEL_BF16, P(q.data_ptr()), k_rows, P(k.data_ptr()), P(v.data_ptr()),
+                P(lens.data_ptr()), b, hq, hkv, D, cap, 2 + i % len(layers), 2, 4, 0.01,
+                P(kept.data_ptr()), P(ko.data_ptr()), P(vo.data_ptr()), cap, P(ws.data_ptr()),
+                ws_bytes, sp)
+        st = (lib.kvsel_threshold_cut_rows(*args) if events is None else
+              lib.kvsel_threshold_cut_rows_traced(*args, events, 2 * len(names)))
+        if st != 0:
+            raise RuntimeError(f"kvsel_threshold_cut_rows: {K.status_string(st)}")
+
+    call(0)
+    torch.cuda.synchronize()
+    kept_tok = int(kept.sum().item())            # layer 2's kept rows: K and V read and written
+    cost["cut_compact"] = {"bytes": kept_tok * D * 2 * 4}
+    r = time_calls(call, names, cost, steps, 4, hip)
+    r["tokens"] = int(lengths.sum())
+    r["k_rows"] = k_rows
+    r["kept_fraction"] = kept_tok / tok
+    r["cost"] = cost
+    return r
+
+
 KERNEL_SOURCES = {"stats": "scores.hip", "reduce": "scores.hip", "pool": "scores.hip",
                   "gram": "gram.hip", "gram_fin": "gram.hip", "thresh": "select.hip",
                   "compact": "select.hip",
@@ -592,6 +653,18 @@ def run_variants(a, hip) -> dict:
             "ms_per_step": round(r["ms_plain"], 5), "ms_per_step_traced": round(r["ms"], 5),
             "roofline": roofline(r, cut_cost(synth_lengths(), 28, 4), a.profiles, "refreekv"),
             "step_hbm_frac": hbm_frac(r["step_bytes"], r["ms_plain"]), "kernels": r["kernels"]}
+        r = run_refreekv_rows(hip, 4, 8)
+        log("refreekv_rows", r)
+        out["refreekv_rows"] = {
+            "workload": f"ReFreeKV cut from the last {r['k_rows']} attention rows per query head "
+                        "(the k > 1 ablation: 7*k rows per KV head, causal) with the sink + "
+                        "suffix compaction of K and V; same Qwen2.5-7B shape and 16 sequences as "
+                        "refreekv",
+            "value": round(r["tokens"] / (r["ms_plain"] * 1e-3), 1), "unit": "tokens/s/layer",
+            "ms_per_step": round(r["ms_plain"], 5), "ms_per_step_traced": round(r["ms"], 5),
+            "kept_fraction": round(r["kept_fraction"], 4),
+            "roofline": roofline(r, r["cost"], a.profiles, "refreekv_rows"),
+            "kernels": r["kernels"]}
     return out
 
 

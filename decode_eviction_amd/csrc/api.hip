@@ -221,16 +221,18 @@ struct CutWs {
   size_t bytes;
 };
 
-CutWs cut_ws(void* base, int b, int hkv, int g, int cap) {
+// rows: attention rows scored per launch (g for the single last row; up to
+// kMaxRows of the g*k last rows)
+CutWs cut_ws(void* base, int b, int hkv, int rows, int cap) {
   const size_t heads = (size_t)b * hkv;
   const int nchunk = (cap + kChunk - 1) / kChunk;
-  const int mp = rows_padded(g);
+  const int mp = rows_padded(rows);
   Carver c{static_cast<char*>(base)};
   CutWs w;
   w.err = c.take<int32_t>(64);
   w.cstat = c.take<float2>(heads * nchunk * mp);
   w.rstat = c.take<float2>(heads * mp);
-  w.logits = c.take<float>(heads * g * (size_t)nchunk * kChunk);
+  w.logits = c.take<float>(heads * rows * (size_t)nchunk * kChunk);
   w.energy = c.take<uint64_t>(heads * (size_t)nchunk * kChunk);
   w.ctot = c.take<uint64_t>(heads * nchunk);
   w.bytes = (c.off + kAlign - 1) / kAlign * kAlign;
@@ -544,10 +546,22 @@ kvsel_status kvsel_score_evict_slots_traced(kvsel_dtype dt, kvsel_redundancy mod
                                 scores_out, workspace, ws_bytes, stream, &tr);
 }
 
+// attention rows scored per launch for the last k_rows rows of each query head
+static int cut_group_rows(int g, int k_rows) {
+  const long r = (long)g * k_rows;
+  return r < kMaxRows ? (int)r : kMaxRows;
+}
+
 size_t kvsel_threshold_cut_workspace(int b, int hq, int hkv, int d, int cap) {
   (void)d;
   if (b < 1 || hq < 1 || hkv < 1 || cap < 1 || hq % hkv) return 0;
   return cut_ws(nullptr, b, hkv, hq / hkv, cap).bytes;
+}
+
+size_t kvsel_threshold_cut_rows_workspace(int b, int hq, int hkv, int d, int cap, int k_rows) {
+  (void)d;
+  if (b < 1 || hq < 1 || hkv < 1 || cap < 1 || hq % hkv || k_rows < 1) return 0;
+  return cut_ws(nullptr, b, hkv, cut_group_rows(hq / hkv, k_rows), cap).bytes;
 }
 
 static kvsel_status check_cut_common(const int32_t* lengths, int b, int hq, int hkv, int cap,
@@ -575,6 +589,8 @@ static CutParams cut_params(const CutWs& ws, const int32_t* lengths, int b, int 
   c.nchunk = (cap + kChunk - 1) / kChunk;
   c.lstride = c.nchunk * kChunk;
   c.n_sink = n_sink;
+  c.rows = c.g;
+  c.accum = 0;
   c.T = T;
   c.energy = ws.energy;
   c.ctot = ws.ctot;
@@ -583,48 +599,75 @@ static CutParams cut_params(const CutWs& ws, const int32_t* lengths, int b, int 
   return c;
 }
 
-static kvsel_status threshold_cut_impl(kvsel_dtype dt, const void* q_last, const void* k,
-                                 const int32_t* lengths, int b, int hq, int hkv, int d, int cap,
-                                 int layer, int n_full_layers, int n_sink, float T,
-                                 int32_t* kept_len_out, void* workspace, size_t ws_bytes,
-                                 hipStream_t stream, Trace* tr) {
+// The cut over the last k_rows query rows of each query head (k_rows = 1: the
+// single last row), optionally followed by the sink + suffix compaction.
+static kvsel_status threshold_cut_impl(kvsel_dtype dt, const void* q_rows, int k_rows,
+                                       const void* k, const void* v, const int32_t* lengths,
+                                       int b, int hq, int hkv, int d, int cap, int layer,
+                                       int n_full_layers, int n_sink, float T,
+                                       int32_t* kept_len_out, void* k_out, void* v_out,
+                                       int cap_out, void* workspace, size_t ws_bytes,
+                                       hipStream_t stream, Trace* tr) {
   if (dt != KVSEL_BF16 && dt != KVSEL_F32) return KVSEL_ERR_INVALID_ARG;
   kvsel_status st = check_cut_common(lengths, b, hq, hkv, cap, n_sink, T, kept_len_out);
   if (st != KVSEL_OK) return st;
-  if (layer < 0 || n_full_layers < 0) return KVSEL_ERR_INVALID_ARG;
+  if (layer < 0 || n_full_layers < 0 || k_rows < 1 || k_rows > cap) return KVSEL_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return KVSEL_ERR_UNSUPPORTED;
+  if (k_out) {
+    if (!k || !v || !v_out || cap_out < cap) return KVSEL_ERR_INVALID_ARG;
+    if (!aligned16(v) || !aligned16(k_out) || !aligned16(v_out)) return KVSEL_ERR_INVALID_ARG;
+  }
   const int g = hq / hkv;
-  const CutWs need = cut_ws(nullptr, b, hkv, g, cap);
+  const int grp = cut_group_rows(g, k_rows);
+  const CutWs need = cut_ws(nullptr, b, hkv, grp, cap);
   if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
-  const CutWs ws = cut_ws(workspace, b, hkv, g, cap);
+  const CutWs ws = cut_ws(workspace, b, hkv, grp, cap);
   CutParams c = cut_params(ws, lengths, b, hq, hkv, cap, n_sink, T, kept_len_out);
-  if (layer < n_full_layers) return hip_status(launch_cut_full(c, stream, tr));
-  if (!q_last || !k || !aligned16(q_last) || !aligned16(k)) return KVSEL_ERR_INVALID_ARG;
-
-  ScoreParams p{};
-  p.q = static_cast<const char*>(q_last);
-  p.k = static_cast<const char*>(k);
-  p.lengths = lengths;
-  p.b = b;
-  p.hq = hq;
-  p.hkv = hkv;
-  p.g = g;
-  p.w = 1;
-  p.m = g;
-  p.mp = rows_padded(g);
-  p.cap = cap;
-  p.nchunk = c.nchunk;
-  p.scale2 = kLog2e / sqrtf((float)d);
-  p.cstat = ws.cstat;
-  p.rstat = ws.rstat;
-  p.logits = ws.logits;
-  p.err = ws.err;
-  KV_TRY(launch_stats(dt, d, kModeCut, p, stream, tr));
-  KV_TRY(launch_reduce(d, kModeCut, p, stream, tr));
-  c.logits = ws.logits;
-  c.attn = nullptr;
-  KV_TRY(launch_cut_energy(c, stream, tr));
-  KV_TRY(launch_cut_scan(c, stream, tr));
+  if (layer < n_full_layers) {
+    KV_TRY(launch_cut_full(c, stream, tr));
+  } else {
+    if (!q_rows || !k || !aligned16(q_rows) || !aligned16(k)) return KVSEL_ERR_INVALID_ARG;
+    ScoreParams p{};
+    p.q = static_cast<const char*>(q_rows);
+    p.k = static_cast<const char*>(k);
+    p.lengths = lengths;
+    p.b = b;
+    p.hq = hq;
+    p.hkv = hkv;
+    p.g = g;
+    p.w = k_rows;
+    p.krows = k_rows;
+    p.cap = cap;
+    p.nchunk = c.nchunk;
+    p.scale2 = kLog2e / sqrtf((float)d);
+    p.cstat = ws.cstat;
+    p.rstat = ws.rstat;
+    p.logits = ws.logits;
+    p.err = ws.err;
+    c.logits = ws.logits;
+    c.attn = nullptr;
+    // the g*k_rows rows of a KV head in groups of at most kMaxRows; each group
+    // adds its rows' integer energy terms to the earlier groups'
+    const int rows = g * k_rows;
+    for (int r0 = 0; r0 < rows; r0 += grp) {
+      p.rows0 = r0;
+      p.m = rows - r0 < grp ? rows - r0 : grp;
+      p.mp = rows_padded(p.m);
+      KV_TRY(launch_stats(dt, d, kModeCut, p, stream, tr));
+      KV_TRY(launch_reduce(d, kModeCut, p, stream, tr));
+      c.rows = p.m;
+      c.mp = p.mp;
+      c.accum = r0 > 0;
+      KV_TRY(launch_cut_energy(c, stream, tr));
+    }
+    KV_TRY(launch_cut_scan(c, stream, tr));
+  }
+  if (k_out) {
+    CutCompactParams cp{static_cast<const char*>(k), static_cast<const char*>(v),
+                        static_cast<char*>(k_out), static_cast<char*>(v_out), lengths,
+                        kept_len_out, b, hkv, cap, cap_out, n_sink};
+    KV_TRY(launch_cut_compact(dt, d, cp, stream, tr));
+  }
   return KVSEL_OK;
 }
 
@@ -633,8 +676,54 @@ kvsel_status kvsel_threshold_cut(kvsel_dtype dt, const void* q_last, const void*
                                  int layer, int n_full_layers, int n_sink, float T,
                                  int32_t* kept_len_out, void* workspace, size_t ws_bytes,
                                  hipStream_t stream) {
-  return threshold_cut_impl(dt, q_last, k, lengths, b, hq, hkv, d, cap, layer, n_full_layers,
-                            n_sink, T, kept_len_out, workspace, ws_bytes, stream, nullptr);
+  return threshold_cut_impl(dt, q_last, 1, k, nullptr, lengths, b, hq, hkv, d, cap, layer,
+                            n_full_layers, n_sink, T, kept_len_out, nullptr, nullptr, 0,
+                            workspace, ws_bytes, stream, nullptr);
+}
+
+kvsel_status kvsel_threshold_cut_rows(kvsel_dtype dt, const void* q_rows, int k_rows,
+                                      const void* k, const void* v, const int32_t* lengths, int b,
+                                      int hq, int hkv, int d, int cap, int layer,
+                                      int n_full_layers, int n_sink, float T,
+                                      int32_t* kept_len_out, void* k_out, void* v_out,
+                                      int cap_out, void* workspace, size_t ws_bytes,
+                                      hipStream_t stream) {
+  return threshold_cut_impl(dt, q_rows, k_rows, k, v, lengths, b, hq, hkv, d, cap, layer,
+                            n_full_layers, n_sink, T, kept_len_out, k_out, v_out, cap_out,
+                            workspace, ws_bytes, stream, nullptr);
+}
+
+kvsel_status kvsel_threshold_cut_rows_traced(kvsel_dtype dt, const void* q_rows, int k_rows,
+                                             const void* k, const void* v,
+                                             const int32_t* lengths, int b, int hq, int hkv,
+                                             int d, int cap, int layer, int n_full_layers,
+                                             int n_sink, float T, int32_t* kept_len_out,
+                                             void* k_out, void* v_out, int cap_out,
+                                             void* workspace, size_t ws_bytes,
+                                             hipStream_t stream, hipEvent_t* events,
+                                             int n_events) {
+  if (!events || n_events < 2) return KVSEL_ERR_INVALID_ARG;
+  Trace tr{events, n_events, 0};
+  return threshold_cut_impl(dt, q_rows, k_rows, k, v, lengths, b, hq, hkv, d, cap, layer,
+                            n_full_layers, n_sink, T, kept_len_out, k_out, v_out, cap_out,
+                            workspace, ws_bytes, stream, &tr);
+}
+
+kvsel_status kvsel_cut_compact(kvsel_dtype dt, const void* k, const void* v,
+                               const int32_t* lengths, const int32_t* kept_len, int b, int hkv,
+                               int d, int cap, int n_sink, void* k_out, void* v_out, int cap_out,
+                               hipStream_t stream) {
+  if (dt != KVSEL_BF16 && dt != KVSEL_F32) return KVSEL_ERR_INVALID_ARG;
+  if (!k || !v || !lengths || !kept_len || !k_out || !v_out) return KVSEL_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out))
+    return KVSEL_ERR_INVALID_ARG;
+  if (b < 1 || hkv < 1 || cap < 1 || n_sink < 0 || cap_out < 1) return KVSEL_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return KVSEL_ERR_UNSUPPORTED;
+  if (b > 65535 || hkv > 65535 || cap >= (1 << 24)) return KVSEL_ERR_UNSUPPORTED;
+  CutCompactParams cp{static_cast<const char*>(k), static_cast<const char*>(v),
+                      static_cast<char*>(k_out), static_cast<char*>(v_out), lengths, kept_len, b,
+                      hkv, cap, cap_out, n_sink};
+  return hip_status(launch_cut_compact(dt, d, cp, stream, nullptr));
 }
 
 kvsel_status kvsel_threshold_cut_traced(kvsel_dtype dt, const void* q_last, const void* k,
@@ -644,8 +733,9 @@ kvsel_status kvsel_threshold_cut_traced(kvsel_dtype dt, const void* q_last, cons
                                         hipStream_t stream, hipEvent_t* events, int n_events) {
   if (!events || n_events < 2) return KVSEL_ERR_INVALID_ARG;
   Trace tr{events, n_events, 0};
-  return threshold_cut_impl(dt, q_last, k, lengths, b, hq, hkv, d, cap, layer, n_full_layers,
-                            n_sink, T, kept_len_out, workspace, ws_bytes, stream, &tr);
+  return threshold_cut_impl(dt, q_last, 1, k, nullptr, lengths, b, hq, hkv, d, cap, layer,
+                            n_full_layers, n_sink, T, kept_len_out, nullptr, nullptr, 0,
+                            workspace, ws_bytes, stream, &tr);
 }
 
 kvsel_status kvsel_threshold_cut_from_attn(const float* attn_last, const int32_t* lengths, int b,

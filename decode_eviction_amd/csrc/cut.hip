@@ -5,8 +5,10 @@
 // The last-row logits and their per-row softmax statistics come from k_stats
 // / k_reduce (scores.hip, cut mode).  Here:
 //   k_cut_energy  per 256-token chunk: a = 2^(t - max) / sum for each of the
-//                 g query rows of the group, E[j] = sum_q floor(fl32(a*a) * 2^52)
+//                 query rows of the group, E[j] = sum_q floor(fl32(a*a) * 2^52)
 //                 as a 64-bit integer, and the chunk's exact integer total;
+//                 with more rows than one launch scores (the last k rows of
+//                 each query head), successive launches add their rows' terms;
 //   k_cut_scan    per KV head: tau = ceil(E_total * (1 - T)); if the sinks
 //                 alone reach tau the cut is m, otherwise a block-wide
 //                 inclusive scan walks the chunk totals from the newest chunk
@@ -58,21 +60,39 @@ __global__ __launch_bounds__(256) void k_cut_energy(CutParams p) {
   if (c0 >= n) return;
   const long head = (long)bi * p.hkv + h;
   const int tok = c0 + tid;
-  uint64_t e = 0;
+  uint64_t* ep = p.energy + head * (long)p.nchunk * kChunk + tok;
+  uint64_t e = p.accum ? *ep : 0u;  // row groups after the first add to the earlier ones
+  // floor(fl32(a*a) * 2^52) of one probability (a square of at most 1)
+  auto term = [](float a) -> uint64_t {
+    const float sq = fminf(__fmul_rn(a, a), 1.0f);
+    return (uint64_t)((double)sq * 4503599627370496.0);
+  };
   if (tok < n) {
-    for (int q = 0; q < p.g; ++q) {
-      float a;
-      if (p.attn) {
-        a = p.attn[((long)bi * p.hq + (long)h * p.g + q) * p.cap + tok];
-      } else {
-        const float2 st = p.rstat[head * p.mp + q];
-        a = exp2_fast(p.logits[(head * p.g + q) * (long)p.lstride + tok] - st.x) * st.y;
+    if (p.attn) {
+      for (int q = 0; q < p.rows; ++q)
+        e += term(p.attn[((long)bi * p.hq + (long)h * p.g + q) * p.cap + tok]);
+    } else {
+      // 8 rows at a time, their loads issued before use; a row that sees no
+      // key (sum 0) has no attention mass
+      constexpr int U = 8;
+      const float* lg = p.logits + head * p.rows * (long)p.lstride + tok;
+      const float2* rs = p.rstat + head * p.mp;
+      for (int q0 = 0; q0 < p.rows; q0 += U) {
+        float t[U];
+        float2 st[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int q = min(q0 + u, p.rows - 1);
+          t[u] = lg[q * (long)p.lstride];
+          st[u] = rs[q];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (q0 + u < p.rows) e += term(st[u].y > 0.f ? exp2_fast(t[u] - st[u].x) * st[u].y : 0.f);
       }
-      const float sq = fminf(__fmul_rn(a, a), 1.0f);
-      e += (uint64_t)((double)sq * 4503599627370496.0);  // floor(sq * 2^52)
     }
   }
-  p.energy[head * (long)p.nchunk * kChunk + tok] = e;
+  *ep = e;
   const uint64_t tot = block_sum_u64(e, wsum, tid);
   if (tid == 0) p.ctot[head * p.nchunk + chunk] = tot;
 }
@@ -154,6 +174,42 @@ __global__ void k_cut_full(CutParams p) {
   const int h = blockIdx.x, bi = blockIdx.y;
   if (h == 0 && bi == 0 && threadIdx.x == 0) write_err(p);
   if (threadIdx.x == 0) p.kept[(long)bi * p.hkv + h] = min(p.lengths[bi], p.cap);
+}
+
+// Sink + suffix compaction after the cut (the kept set is the m sinks and
+// the newest L - m tokens): row t < L of the compacted cache is position t for
+// t < min(m, n), else position n - L + t; bit copies of K and V, one 16-byte
+// piece per thread.  Rows from L on are left untouched.
+template <int RB>
+__global__ __launch_bounds__(256) void k_cut_compact(CutCompactParams p) {
+  constexpr int CPR = RB / 16;
+  constexpr int RPW = 256 / CPR;
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const int t = blockIdx.x * RPW + threadIdx.x / CPR, c = threadIdx.x % CPR;
+  const long head = (long)bi * p.hkv + h;
+  const int n = min(p.lengths[bi], p.cap);
+  const int L = min(p.kept[head], n);
+  if (t >= L || t >= p.cap_out) return;
+  const int ms = min(p.n_sink, n);
+  const int src = t < ms ? t : n - L + t;
+  const long from = (head * p.cap + src) * (long)RB + c * 16;
+  const long to = (head * p.cap_out + t) * (long)RB + c * 16;
+  const u32x4_t kv = ld16(p.k + from), vv = ld16(p.v + from);
+  *reinterpret_cast<u32x4_t*>(p.k_out + to) = kv;
+  *reinterpret_cast<u32x4_t*>(p.v_out + to) = vv;
+}
+
+hipError_t launch_cut_compact(int dt, int d, const CutCompactParams& p, hipStream_t s, Trace* tr) {
+  const int rb = d * (dt == 0 ? 2 : 4);
+  auto go = [&](auto kern, int rpw) {
+    return launch_k(kern, dim3((p.cap + rpw - 1) / rpw, p.hkv, p.b), dim3(256), s, tr, p);
+  };
+  switch (rb) {
+    case 128: return go(k_cut_compact<128>, 256 / 8);
+    case 256: return go(k_cut_compact<256>, 256 / 16);
+    case 512: return go(k_cut_compact<512>, 256 / 32);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_cut_energy(const CutParams& p, hipStream_t s, Trace* tr) {

@@ -29,6 +29,10 @@ struct ScoreParams {
   int cap, nchunk;          // nchunk = ceil(cap / kChunk)
   float scale2;             // log2(e)/sqrt(d): logits in base-2 units
   float lambda;
+  // cut mode over the last krows query rows of each q head (krows > 1: row r
+  // of a q head sees keys j <= n - krows + r); this launch scores the group
+  // of rows rows0 .. rows0 + m - 1 of the g*krows rows of a KV head
+  int rows0, krows;
   // workspace
   float2* cstat;            // [b][Hkv][nchunk][mp]  chunk (max, sum 2^(t - max))
   float2* rstat;            // [b][Hkv][mp]          (max, 1/sum), base 2
@@ -36,7 +40,7 @@ struct ScoreParams {
   float* ssum;              // [b][Hkv][d]           keysum: sum of unit keys
   float* inv_norm;          // [b][Hkv][wstride]     gram: 1/||k_j||, 0 past n in its chunk
   int wstride;              // per-head stride of inv_norm: cap rounded up to 512
-  float* logits;            // [b][Hkv][g][nchunk*kChunk]  cut: logits in base-2 units
+  float* logits;            // [b][Hkv][m][nchunk*kChunk]  cut: logits in base-2 units (-inf masked)
   int32_t* err;             // error word
   // outputs (never null; the host substitutes workspace buffers)
   float* i_out;             // [b][Hkv][cap]
@@ -115,16 +119,28 @@ struct GatherParams {
 };
 
 struct CutParams {
-  const float* logits;      // [b][Hkv][g][lstride]   (or null with attn)
+  const float* logits;      // [b][Hkv][rows][lstride] (or null with attn)
   const float* attn;        // [b][Hq][cap]           stage entry (or null)
   const float2* rstat;      // [b][Hkv][mp]
   const int32_t* lengths;
   int b, hq, hkv, g, mp, cap, nchunk, lstride, n_sink;
+  int rows;                 // attention rows per KV head in this launch (g for one last row)
+  int accum;                // add to the energies of earlier row groups
   float T;
   uint64_t* energy;         // [b][Hkv][nchunk*kChunk]
   uint64_t* ctot;           // [b][Hkv][nchunk]
   int32_t* kept;            // [b][Hkv]
   int32_t* err;
+};
+
+struct CutCompactParams {
+  const char* k;            // [b][Hkv][cap][d]
+  const char* v;
+  char* k_out;              // [b][Hkv][cap_out][d]
+  char* v_out;
+  const int32_t* lengths;
+  const int32_t* kept;      // [b][Hkv]
+  int b, hkv, cap, cap_out, n_sink;
 };
 
 // Optional per-kernel timing: the k-th kernel an entry point launches records
@@ -162,5 +178,6 @@ hipError_t launch_gather(int dt, int d, const GatherParams& p, hipStream_t s, Tr
 hipError_t launch_cut_energy(const CutParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_cut_scan(const CutParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_cut_full(const CutParams& p, hipStream_t s, Trace* tr);
+hipError_t launch_cut_compact(int dt, int d, const CutCompactParams& p, hipStream_t s, Trace* tr);
 
 }  // namespace kvsel

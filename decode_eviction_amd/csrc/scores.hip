@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
     for (int t = tid; t < kHistBins; t += 256) p.hist[head * kHistBins + t] = 0u;
   if (c0 >= n) return;
   const char* kb = p.k + head * (long)p.cap * G::kRowBytes;
-  const char* qb = p.q + ((long)bi * p.hq + (long)h * p.g) * p.w * G::kRowBytes;
+  const char* qb = p.q + (((long)bi * p.hq + (long)h * p.g) * p.w + p.rows0) * G::kRowBytes;
 
   Frag<NC> qf[MT];
 #pragma unroll
@@ -100,9 +100,15 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[tt][t] = mfma_tile<E, NC>(kf[tt], qf[t], zero16());
 
-  // per-row max and sum of 2^(t - max), t = logit * log2(e) / sqrt(d); only
-  // the wave holding the end of the sequence masks tokens
-  const bool full = tok0 + 64 <= n;
+  // per-row max and sum of 2^(t - max), t = logit * log2(e) / sqrt(d).  The
+  // last key a query row sees is n-1, or n - krows + r for row r of the last
+  // krows rows (causal); only waves past the smallest such limit mask keys.
+  const bool causal = MODE == kModeCut && p.krows > 1;
+  int lim[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+    lim[t] = causal ? n - p.krows + (p.rows0 + 32 * t + l32) % p.krows : n - 1;
+  const bool full = tok0 + 63 <= (causal ? n - p.krows : n - 1);
   const float sc2 = p.scale2;
   __shared__ float2 wst[4][MT * 32];
 #pragma unroll
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const bool ok = full || tok0 + 32 * tt + tile_row(i, hf) < n;
+        const bool ok = full || tok0 + 32 * tt + tile_row(i, hf) <= lim[t];
         m = ok ? fmaxf(m, acc[tt][t][i]) : m;
       }
     m = fmaxf(m, xor32(m));
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const bool ok = full || tok0 + 32 * tt + tile_row(i, hf) < n;
+          const bool ok = full || tok0 + 32 * tt + tile_row(i, hf) <= lim[t];
           const float e = exp2_fast(fmaf(acc[tt][t][i], sc2, -m2));
           s += ok ? e : 0.f;
         }
@@ -133,22 +139,26 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
   }
 
   if constexpr (MODE == kModeCut) {
-    // logits of rows < g in base-2 units, 4 consecutive tokens per store
-    if (l32 < p.g) {
-      const long ls = (long)p.nchunk * kChunk;
-      float* lrow = p.logits + (head * p.g + l32) * ls;
+    // logits of the m rows in base-2 units (-inf where a row does not see the
+    // key), 4 consecutive tokens per store
+    const long ls = (long)p.nchunk * kChunk;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+    for (int t = 0; t < MT; ++t) {
+      const int row = 32 * t + l32;
+      if (row < p.m) {
+        float* lrow = p.logits + (head * p.m + row) * ls;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int tb = tok0 + 32 * tt + 8 * q4 + 4 * hf;
-          f32x4_t v;
-          v[0] = acc[tt][0][4 * q4 + 0] * sc2;
-          v[1] = acc[tt][0][4 * q4 + 1] * sc2;
-          v[2] = acc[tt][0][4 * q4 + 2] * sc2;
-          v[3] = acc[tt][0][4 * q4 + 3] * sc2;
-          *reinterpret_cast<f32x4_t*>(lrow + tb) = v;
-        }
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int tb = tok0 + 32 * tt + 8 * q4 + 4 * hf;
+            f32x4_t v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[e] = full || tb + e <= lim[t] ? acc[tt][t][4 * q4 + e] * sc2 : -INFINITY;
+            *reinterpret_cast<f32x4_t*>(lrow + tb) = v;
+          }
+      }
     }
   } else {
     float inv[2];
@@ -363,9 +373,7 @@ static hipError_t stats_t(int mode, const ScoreParams& p, hipStream_t s, Trace* 
   switch (mode) {
     case kModeGram: return launch_k(k_stats<E, D, MT, kModeGram>, grid, dim3(256), s, tr, p);
     case kModeKeysum: return launch_k(k_stats<E, D, MT, kModeKeysum>, grid, dim3(256), s, tr, p);
-    default:
-      if constexpr (MT == 1) return launch_k(k_stats<E, D, 1, kModeCut>, grid, dim3(256), s, tr, p);
-      else return hipErrorInvalidValue;
+    default: return launch_k(k_stats<E, D, MT, kModeCut>, grid, dim3(256), s, tr, p);
   }
 }
 

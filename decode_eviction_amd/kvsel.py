@@ -55,6 +55,12 @@ _SIGS = {
     "kvsel_threshold_cut": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P,
                                  _P, _S, _P]),
     "kvsel_threshold_cut_from_attn": (_I, [_P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _S, _P]),
+    "kvsel_threshold_cut_rows_workspace": (_S, [_I] * 6),
+    "kvsel_threshold_cut_rows": (_I, [_I, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                      _F, _P, _P, _P, _I, _P, _S, _P]),
+    "kvsel_threshold_cut_rows_traced": (_I, [_I, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                             _I, _F, _P, _P, _P, _I, _P, _S, _P, _P, _I]),
+    "kvsel_cut_compact": (_I, [_I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P]),
     "kvsel_workspace_error": (_I, [_P, _P, _P]),
 }
 
@@ -313,6 +319,47 @@ def kvsel_threshold_cut(q_last, k, lengths, layer, n_full_layers=2, n_sink=4, T=
                                    _ptr(kept_out), _ptr(ws), ws.numel(), _stream(stream))
     _check("kvsel_threshold_cut", st)
     return kept_out
+
+
+def kvsel_threshold_cut_rows_workspace(b, hq, hkv, d, cap, k_rows) -> int:
+    return int(lib().kvsel_threshold_cut_rows_workspace(b, hq, hkv, d, cap, k_rows))
+
+
+def kvsel_threshold_cut_rows(q_rows, k, lengths, layer, n_full_layers=2, n_sink=4, T=0.01,
+                             v=None, k_out=None, v_out=None, kept_out=None, workspace=None,
+                             stream=None):
+    """Kept length per (sequence, KV head) from the last k rows, q_rows
+    [b][Hq][k][d]; with v and k_out/v_out also the sink + suffix compaction."""
+    _need_cuda(q_rows, k, v, lengths, k_out, v_out, kept_out)
+    b, hq, k_rows, d = q_rows.shape
+    _, hkv, cap, _ = k.shape
+    if kept_out is None:
+        kept_out = torch.empty((b, hkv), dtype=torch.int32, device=k.device)
+    ws = _workspace(kvsel_threshold_cut_rows_workspace(b, hq, hkv, d, cap, k_rows), k.device,
+                    workspace)
+    st = lib().kvsel_threshold_cut_rows(_dtype(k), _ptr(q_rows), k_rows, _ptr(k), _ptr(v),
+                                        _ptr(lengths), b, hq, hkv, d, cap, int(layer),
+                                        int(n_full_layers), int(n_sink), float(T), _ptr(kept_out),
+                                        _ptr(k_out), _ptr(v_out),
+                                        0 if k_out is None else k_out.shape[2], _ptr(ws),
+                                        ws.numel(), _stream(stream))
+    _check("kvsel_threshold_cut_rows", st)
+    return kept_out
+
+
+def kvsel_cut_compact(k, v, lengths, kept_len, n_sink=4, k_out=None, v_out=None, stream=None):
+    """Sink + suffix compaction from given kept lengths; returns (k_out, v_out)."""
+    _need_cuda(k, v, lengths, kept_len, k_out, v_out)
+    b, hkv, cap, d = k.shape
+    if k_out is None:
+        k_out = torch.zeros_like(k)
+    if v_out is None:
+        v_out = torch.zeros_like(v)
+    st = lib().kvsel_cut_compact(_dtype(k), _ptr(k), _ptr(v), _ptr(lengths), _ptr(kept_len), b,
+                                 hkv, d, cap, int(n_sink), _ptr(k_out), _ptr(v_out),
+                                 k_out.shape[2], _stream(stream))
+    _check("kvsel_cut_compact", st)
+    return k_out, v_out
 
 
 def kvsel_threshold_cut_from_attn(attn_last, lengths, hkv, n_sink=4, T=0.01, kept_out=None,

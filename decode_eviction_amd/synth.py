@@ -39,6 +39,7 @@ WL_DECODE = 3
 WL_BATCHED = 4
 WL_REFREEKV = 5
 WL_HEADLINE = 6
+WL_REFREEKV_ROWS = 7
 
 _THREADS = 8
 
@@ -305,6 +306,29 @@ def refreekv_lengths(seed: int = 0, b: int = 16, lo: int = 1024, hi: int = 16384
     return _rng(seed, WL_REFREEKV, 55_555).integers(lo, hi + 1, size=b).astype(np.int32)
 
 
+def cut_rows_q(case: "CutCase", k_rows: int) -> np.ndarray:
+    """Query rows of the last k_rows tokens for a cut case: [b][hq][k_rows][d]
+    in the case's storage type.  The last row is the case's own last-row
+    query; earlier rows are drawn like it (N(0,1)^d + sqrt(d)*u with the
+    head's direction u) from their own stream (zero for a zero-query case)."""
+    b, hq, hkv, d = case.b, case.hq, case.hkv, case.d
+    g = hq // hkv
+    seed = case.meta["seed"]
+    zero = bool(case.meta.get("zero_query", False))
+    last = case.as_f32("q")
+    out = np.zeros((b, hq, k_rows, d), np.float32)
+    for bi in range(b):
+        for h in range(hkv):
+            u = _rng(seed, WL_REFREEKV, bi, case.layer, h).standard_normal(d)
+            u /= np.linalg.norm(u)
+            rows = _rng(seed, WL_REFREEKV_ROWS, bi, case.layer, h).standard_normal(
+                (g, k_rows - 1, d), dtype=np.float32)
+            rows += np.float32(math.sqrt(d)) * u.astype(np.float32)
+            out[bi, h * g:(h + 1) * g, :k_rows - 1] = 0.0 if zero else rows
+            out[bi, h * g:(h + 1) * g, k_rows - 1] = last[bi, h * g:(h + 1) * g]
+    return _store(out, case.dtype)
+
+
 def cut_case(layer: int, seed: int = 0, b: int = 16, hq: int = 28, hkv: int = 4,
              d: int = 128, lengths=None, cap: Optional[int] = None,
              zero_query: bool = False, dtype: str = "bf16") -> CutCase:
@@ -347,4 +371,4 @@ def cut_case(layer: int, seed: int = 0, b: int = 16, hq: int = 28, hkv: int = 4,
     with ThreadPoolExecutor(_THREADS) as ex:
         list(ex.map(one, [(bi, h) for bi in range(b) for h in range(hkv)]))
     return CutCase("refreekv", dtype, b, hq, hkv, d, cap, layer, lengths, _store(q, dtype), k,
-                   meta=dict(seed=seed, taus=taus))
+                   meta=dict(seed=seed, taus=taus, zero_query=zero_query))

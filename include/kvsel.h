@@ -251,6 +251,52 @@ kvsel_status kvsel_threshold_cut_traced(kvsel_dtype dt, const void* q_last, cons
                                         int32_t* kept_len_out, void* workspace, size_t ws_bytes,
                                         hipStream_t stream, hipEvent_t* events, int n_events);
 
+/* The cut from the last k_rows attention rows instead of the single last row
+ * (the review's ablation of its k = 1 simplification, e.g. k = 10% of n; same
+ * section, ablation paragraph), optionally followed by the sink + suffix
+ * compaction.  q_rows [b][Hq][k_rows][d]: row r of a query head is the query
+ * of token n_b - k_rows + r and sees keys j <= n_b - k_rows + r (causal);
+ * rows of tokens before position 0 contribute nothing.  The energy of token j
+ * is the sum over the g*k_rows rows of the group of floor(fl32(a*a) * 2^52),
+ * then the same walk and cut as kvsel_threshold_cut; k_rows = 1 gives
+ * exactly kvsel_threshold_cut.  1 <= k_rows <= cap; the rows are scored in
+ * groups of 128, so the cost grows as k_rows * n.  When k_out is non-null,
+ * k_out/v_out [b][Hkv][cap_out][d] (cap_out >= cap) receive the kept tokens
+ * in position order: the min(n_sink, n) sinks, then the newest L - sinks
+ * (bit copies); rows from L on are left untouched.  Workspace:
+ * kvsel_threshold_cut_rows_workspace. */
+size_t kvsel_threshold_cut_rows_workspace(int b, int Hq, int Hkv, int d, int cap, int k_rows);
+kvsel_status kvsel_threshold_cut_rows(kvsel_dtype dt, const void* q_rows, int k_rows,
+                                      const void* k, const void* v, const int32_t* lengths,
+                                      int b, int Hq, int Hkv, int d, int cap, int layer,
+                                      int n_full_layers, int n_sink, float T,
+                                      int32_t* kept_len_out, void* k_out, void* v_out,
+                                      int cap_out, void* workspace, size_t ws_bytes,
+                                      hipStream_t stream);
+
+/* kvsel_threshold_cut_rows with per-kernel timing as in kvsel_score_evict_traced.
+ * Launch order: stats, reduce, energy once per group of 128 rows, then scan,
+ * then compact when k_out is given (a fill kernel replaces the scoring
+ * kernels for layer < n_full_layers). */
+kvsel_status kvsel_threshold_cut_rows_traced(kvsel_dtype dt, const void* q_rows, int k_rows,
+                                             const void* k, const void* v,
+                                             const int32_t* lengths, int b, int Hq, int Hkv,
+                                             int d, int cap, int layer, int n_full_layers,
+                                             int n_sink, float T, int32_t* kept_len_out,
+                                             void* k_out, void* v_out, int cap_out,
+                                             void* workspace, size_t ws_bytes,
+                                             hipStream_t stream, hipEvent_t* events,
+                                             int n_events);
+
+/* Stage entry: the sink + suffix compaction from given kept lengths
+ * kept_len [b][Hkv] (device): row t < L of k_out/v_out [b][Hkv][cap_out][d]
+ * is position t for t < min(n_sink, n), else position n - L + t; rows from
+ * min(L, cap_out) on are left untouched. */
+kvsel_status kvsel_cut_compact(kvsel_dtype dt, const void* k, const void* v,
+                               const int32_t* lengths, const int32_t* kept_len, int b, int Hkv,
+                               int d, int cap, int n_sink, void* k_out, void* v_out, int cap_out,
+                               hipStream_t stream);
+
 /* Stage entry: the same cut from given fp32 last-row attention probabilities
  * attn_last [b][Hq][cap] (values in [0, 1], used as given; squares are
  * clamped to 1).  Same workspace size as kvsel_threshold_cut. */

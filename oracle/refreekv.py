@@ -27,7 +27,10 @@ Readings where the review is silent or loose:
     softmax with scale 1/sqrt(d);
   * kept length L = max(min(m, n), smallest p >= 1 with C_p >= (1-T)*E_total);
     n = 0 gives L = 0; layers below n_full_layers give L = n;
-  * the kept set is the m sinks plus the last L - m positions.
+  * the kept set is the m sinks plus the last L - m positions;
+  * the k > 1 ablation (the review's last paragraph on ablations) uses the
+    last k rows of the causal attention matrix: row r is token n - k + r's
+    query over keys 0 .. n - k + r; the energy sums over all g*k rows.
 
 Bit-exact decision (reading, used where two implementations must reach the
 same integer L from the same fp32 attention probabilities): each squared
@@ -62,6 +65,30 @@ def last_row_attention(q_rows: np.ndarray, k: np.ndarray) -> np.ndarray:
     s = s - s.max(axis=1, keepdims=True)
     p = np.exp(s)
     return p / p.sum(axis=1, keepdims=True)
+
+
+def last_rows_attention(q_rows: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Causal attention rows of the last k tokens, fp64.
+
+    q_rows [g, k_rows, d]: row r of query head q is the query of token
+    n - k_rows + r and sees keys j <= n - k_rows + r (softmax over those,
+    scale 1/sqrt(d)); rows of tokens before position 0 see nothing and are 0.
+    Returns a [g * k_rows, n] (rows ordered head-major)."""
+    q64 = np.asarray(q_rows, np.float64)
+    k64 = np.asarray(k, np.float64)
+    g, kr, d = q64.shape
+    n = k64.shape[0]
+    a = np.zeros((g * kr, n))
+    for q in range(g):
+        for r in range(kr):
+            last = n - kr + r                       # position of the row's token
+            if last < 0:
+                continue
+            s = (k64[:last + 1] @ q64[q, r]) / np.sqrt(d)
+            s = s - s.max()
+            p = np.exp(s)
+            a[q * kr + r, :last + 1] = p / p.sum()
+    return a
 
 
 def energies(a: np.ndarray) -> np.ndarray:
@@ -140,6 +167,29 @@ def threshold_cut(q_last, k, lengths, layer: int, n_full_layers: int = 2, m: int
             continue
         a = last_row_attention(q_last[bi, h * g:(h + 1) * g], k[bi, h, :n])
         e = energies(a)
+        es[(bi, h)] = e
+        L[bi, h] = cut_length(e, m, T)
+    return L, es
+
+
+def threshold_cut_rows(q_rows, k, lengths, layer: int, n_full_layers: int = 2, m: int = 4,
+                       T: float = 0.01, heads=None):
+    """The cut from the last k rows: q_rows [b][Hq][k_rows][d] (exact input
+    values), k [b][Hkv][cap][d], lengths [b].  Energy of token j: the sum of
+    a^2 over the g*k_rows causal rows of the group.  Returns (L, energies)."""
+    q_rows = np.asarray(q_rows)
+    b, hq, kr, d = q_rows.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    L = np.zeros((b, hkv), np.int64)
+    es = {}
+    todo = heads if heads is not None else [(bi, h) for bi in range(b) for h in range(hkv)]
+    for bi, h in todo:
+        n = int(lengths[bi])
+        if layer < n_full_layers:
+            L[bi, h] = n
+            continue
+        e = energies(last_rows_attention(q_rows[bi, h * g:(h + 1) * g], k[bi, h, :n]))
         es[(bi, h)] = e
         L[bi, h] = cut_length(e, m, T)
     return L, es

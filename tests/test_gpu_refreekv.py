@@ -18,7 +18,7 @@ import torch
 from decode_eviction_amd import kvsel as K
 from decode_eviction_amd import synth
 from oracle import refreekv as rf
-from tests.gpu_util import dev, dev_i32, log
+from tests.gpu_util import dev, dev_i32, host_bits, log
 
 pytestmark = pytest.mark.gpu
 
@@ -134,3 +134,85 @@ def test_cut_deterministic():
     a = K.kvsel_threshold_cut(*args).cpu().numpy()
     b = K.kvsel_threshold_cut(*args).cpu().numpy()
     assert np.array_equal(a, b)
+
+
+# --------------------------------------------- last k rows and the compaction
+
+def _dev_rows(case, k_rows):
+    return dev(synth.cut_rows_q(case, k_rows), case.dtype)
+
+
+def test_cut_rows_k1_is_the_last_row_cut():
+    case = synth.cut_case(9, b=6)
+    qd, kd, ld = dev(case.q, "bf16"), dev(case.k, "bf16"), dev_i32(case.lengths)
+    a = K.kvsel_threshold_cut(qd, kd, ld, 9).cpu().numpy()
+    b = K.kvsel_threshold_cut_rows(qd[:, :, None].contiguous(), kd, ld, 9).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("k_rows", [3, 18, 40])
+def test_cut_rows_end_to_end(k_rows):
+    # g*k = 21, 126 (one group of rows) and 280 (three groups)
+    case = synth.cut_case(11, b=4, lengths=[3000, 777, 9000, 129])
+    log(f"[cut rows] k={k_rows} lengths={case.lengths.tolist()}")
+    qr = synth.cut_rows_q(case, k_rows)
+    got = K.kvsel_threshold_cut_rows(dev(qr, "bf16"), dev(case.k, "bf16"), dev_i32(case.lengths),
+                                     11).cpu().numpy()
+    L_ref, es = rf.threshold_cut_rows(synth.bf16_bits_to_f32(qr), case.as_f32("k"), case.lengths, 11)
+    exact = 0
+    for (bi, h), e in es.items():
+        assert _valid_cut(e, int(got[bi, h]), 4, 0.01), (bi, h, int(got[bi, h]), int(L_ref[bi, h]))
+        exact += int(got[bi, h] == L_ref[bi, h])
+    log(f"    exact-match rate {exact / len(es):.3f}")
+    assert exact / len(es) >= 0.75
+
+
+def test_cut_rows_zero_query_and_short_sequences():
+    # zero queries: each row is uniform over the keys it sees; sequences shorter
+    # than k have rows that see nothing
+    lengths = [2000, 5, 1, 37]
+    case = synth.cut_case(6, b=4, lengths=lengths, zero_query=True)
+    k_rows = 12
+    qr = synth.cut_rows_q(case, k_rows)
+    got = K.kvsel_threshold_cut_rows(dev(qr, "bf16"), dev(case.k, "bf16"), dev_i32(lengths),
+                                     6).cpu().numpy()
+    L_ref, es = rf.threshold_cut_rows(synth.bf16_bits_to_f32(qr), case.as_f32("k"), lengths, 6)
+    for (bi, h), e in es.items():
+        assert _valid_cut(e, int(got[bi, h]), 4, 0.01), (bi, h, int(got[bi, h]), int(L_ref[bi, h]))
+    assert got[1].tolist() == [5] * 4 and got[2].tolist() == [1] * 4
+
+
+def test_cut_compact_fused_and_stage():
+    case = synth.cut_case(7, b=3, lengths=[3000, 4, 1500], dtype="bf16")
+    rng = np.random.default_rng(3)
+    v = rng.integers(0, 65536, size=case.k.shape, dtype=np.uint16)
+    qd, kd, vd, ld = _dev_rows(case, 2), dev(case.k, "bf16"), dev(v, "bf16"), dev_i32(case.lengths)
+    ko = torch.zeros_like(kd)
+    vo = torch.zeros_like(vd)
+    kept = K.kvsel_threshold_cut_rows(qd, kd, ld, 7, v=vd, k_out=ko, v_out=vo).cpu().numpy()
+    ko, vo = host_bits(ko), host_bits(vo)
+    for bi in range(3):
+        n = int(case.lengths[bi])
+        for h in range(case.hkv):
+            L = int(kept[bi, h])
+            rows = rf.kept_positions(n, L, 4)
+            assert len(rows) == L
+            assert np.array_equal(ko[bi, h, :L], case.k[bi, h, rows]), (bi, h)
+            assert np.array_equal(vo[bi, h, :L], v[bi, h, rows]), (bi, h)
+            assert (ko[bi, h, L:] == 0).all()
+    # the stage entry from given lengths, fp32 and d = 64, into a larger cache
+    kf = rng.standard_normal((2, 3, 100, 64)).astype(np.float32)
+    vf = rng.standard_normal((2, 3, 100, 64)).astype(np.float32)
+    lens = np.array([100, 10], np.int32)
+    kl = np.array([[100, 4, 57], [10, 3, 0]], np.int32)
+    ko2, vo2 = K.kvsel_cut_compact(dev(kf, "f32"), dev(vf, "f32"), dev_i32(lens), dev_i32(kl),
+                                   n_sink=4, k_out=torch.zeros((2, 3, 128, 64), device="cuda"),
+                                   v_out=torch.zeros((2, 3, 128, 64), device="cuda"))
+    ko2, vo2 = ko2.cpu().numpy(), vo2.cpu().numpy()
+    for bi in range(2):
+        for h in range(3):
+            L = int(kl[bi, h])
+            rows = rf.kept_positions(int(lens[bi]), L, 4)
+            assert np.array_equal(ko2[bi, h, :L], kf[bi, h, rows])
+            assert np.array_equal(vo2[bi, h, :L], vf[bi, h, rows])
+            assert (ko2[bi, h, L:] == 0).all()

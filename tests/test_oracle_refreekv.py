@@ -165,3 +165,49 @@ def test_fixed_point_cut_agrees_with_fp64(seed):
     Lfx = rf.cut_length_fixed(rf.energies_fixed(a.astype(np.float32)), 4, 0.01)
     # both are valid cuts of the same energies up to fp32 rounding of a
     assert abs(L64 - Lfx) <= 1
+
+
+# ---------------------------------------------------------------- last k rows
+
+def test_last_rows_zero_query_closed_form():
+    # zero queries: row r (token n-k+r) is uniform over its n-k+r+1 visible keys,
+    # so e_j = g * sum over rows that see j of 1/(n-k+r+1)^2; rows of tokens
+    # before position 0 add nothing
+    g, d = 3, 8
+    for n, kr in [(50, 1), (50, 7), (6, 9), (1, 4)]:
+        k = np.random.default_rng(n + kr).standard_normal((n, d))
+        e = rf.energies(rf.last_rows_attention(np.zeros((g, kr, d)), k))
+        want = np.zeros(n)
+        for j in range(n):
+            for r in range(kr):
+                last = n - kr + r
+                if last >= j:
+                    want[j] += g / (last + 1) ** 2
+        assert np.allclose(e, want, rtol=1e-13, atol=0), (n, kr)
+
+
+def test_last_rows_brute_force_loops():
+    # per-row softmax over the visible keys written out with scalar loops
+    rng = np.random.default_rng(5)
+    g, kr, n, d = 2, 3, 5, 4
+    q = rng.integers(-2, 3, size=(g, kr, d)).astype(np.float64)
+    k = rng.integers(-2, 3, size=(n, d)).astype(np.float64)
+    a = rf.last_rows_attention(q, k)
+    for qi in range(g):
+        for r in range(kr):
+            last = n - kr + r
+            logits = [sum(q[qi, r, t] * k[j, t] for t in range(d)) / math.sqrt(d)
+                      for j in range(last + 1)]
+            mx = max(logits)
+            ex = [math.exp(x - mx) for x in logits]
+            tot = sum(ex)
+            for j in range(n):
+                want = ex[j] / tot if j <= last else 0.0
+                assert abs(a[qi * kr + r, j] - want) < 1e-15
+
+
+def test_last_rows_k1_is_last_row():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((4, 1, 16))
+    k = rng.standard_normal((40, 16))
+    assert np.allclose(rf.last_rows_attention(q, k), rf.last_row_attention(q[:, 0], k), rtol=1e-14)
