@@ -328,10 +328,13 @@ __global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
   if (n <= B || B == 0) return;  // k_compact keeps everything (or nothing)
   const float* z = p.z + head * p.cap;
 
-  // unconditional loads (index clamped into range): all in flight before use
+  // loads through a buffer resource (positions past n read 0): all in flight before use
   uint32_t key[kKeysPerThread];
+  {
+    const __amdgpu_buffer_rsrc_t rz = buf_rsrc(z, (uint32_t)n * 4u);
 #pragma unroll
-  for (int i = 0; i < kKeysPerThread; ++i) key[i] = __float_as_uint(z[min(tid + i * kRegThreads, n - 1)]);
+    for (int i = 0; i < kKeysPerThread; ++i) key[i] = buf_ld32(rz, (uint32_t)tid * 4u, (uint32_t)(i * kRegThreads * 4));
+  }
 
   // level 1: the bin (of kHistBins) where the count from the top reaches B
   const uint32_t c0 = p.hist[head * kHistBins + 2 * tid];
@@ -356,7 +359,9 @@ __global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
   uint32_t hi = lo | ((1u << (32 - kHistBits)) - 1u);
   need -= bc[1];
 
-  // positions past n get key 0: below every bin a valid score can fall in
+  // positions past n get key 0: below every bin a valid score can fall in;
+  // rounds (of kRegThreads positions) from nrr on hold no position
+  const int nrr = (n + kRegThreads - 1) / kRegThreads;
 #pragma unroll
   for (int i = 0; i < kKeysPerThread; ++i)
     key[i] = tid + i * kRegThreads < n ? score_key(__uint_as_float(key[i])) : 0u;
@@ -366,6 +371,7 @@ __global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
     uint32_t mine = 0, wcand = 0;
 #pragma unroll
     for (int i = 0; i < kKeysPerThread; ++i) {
+      if (i >= nrr) break;
       const uint32_t kb = hist_bin(key[i]);
       const uint64_t babove = __ballot(kb > b1);
       const uint64_t bin = __ballot(kb == b1);
@@ -385,6 +391,7 @@ __global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
     // pass 2: write the candidates (key, position) in wave order
 #pragma unroll
     for (int i = 0; i < kKeysPerThread; ++i) {
+      if (i >= nrr) break;
       const bool in = hist_bin(key[i]) == b1;
       const uint64_t bin = __ballot(in);
       if (in) {
@@ -423,16 +430,20 @@ __global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
       }
       __syncthreads();
       if (wave == 0) {
+        // lane c holds candidate c; each lane counts the candidates ranked
+        // before its own, broadcasting them one at a time from registers
         const uint32_t nr = nr_s;
         const uint32_t mk = lane < (int)nr ? rk[lane] : 0u;
         const int32_t mpos = lane < (int)nr ? rp[lane] : 0x7fffffff;
         uint32_t rank = 0;
-        for (uint32_t c = 0; c < nr; ++c)
-          rank += (rk[c] > mk || (rk[c] == mk && rp[c] < mpos)) ? 1u : 0u;
+        for (uint32_t c = 0; c < nr; ++c) {
+          const uint32_t kc = (uint32_t)__builtin_amdgcn_readlane((int)mk, (int)c);
+          const int32_t pc = __builtin_amdgcn_readlane(mpos, (int)c);
+          rank += (kc > mk || (kc == mk && pc < mpos)) ? 1u : 0u;
+        }
         const uint64_t who = __ballot(lane < (int)nr && rank == need - 1);
         const uint32_t kth = __shfl(mk, __ffsll((unsigned long long)who) - 1, 64);
-        uint32_t gtk = 0;
-        for (uint32_t c = 0; c < nr; ++c) gtk += rk[c] > kth ? 1u : 0u;
+        const uint32_t gtk = (uint32_t)__popcll(__ballot(lane < (int)nr && mk > kth));
         if (lane == 0) {
           bc[0] = kth;
           bc[1] = need - gtk;  // copies of the threshold key still to keep
