@@ -107,3 +107,58 @@ def test_stage_entries_reject(lib):
     assert lib.kvsel_threshold_cut_from_attn(NULL, _fake(), 1, 4, 1, 10, 4, 0.01, _fake(), _fake(),
                                              1 << 20, NULL) == K.KVSEL_ERR_INVALID_ARG
     assert lib.kvsel_workspace_error(NULL, NULL, NULL) == K.KVSEL_ERR_INVALID_ARG
+
+
+def test_binding_argument_counts_match_header():
+    import re
+    with open(K.HEADER_PATH) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    decls = re.findall(r"\b(kvsel_\w+)\s*\(([^;{]*?)\)\s*;", text, flags=re.S)
+    assert len(decls) == len(K._SIGS)
+    for name, params in decls:
+        params = params.strip()
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        assert n == len(K._SIGS[name][1]), (name, n, len(K._SIGS[name][1]))
+
+
+def test_next_row_entries_reject(lib):
+    f = _fake
+    BF = K.KVSEL_BF16
+    # per-head budgets: the budget row is required
+    assert lib.kvsel_select_topb_heads(f(), f(), NULL, 1, 2, 10, 5, f(), f(), 1 << 20,
+                                       NULL) == K.KVSEL_ERR_INVALID_ARG
+    assert lib.kvsel_score_evict_heads(BF, 0, f(), f(), f(), f(), NULL, 1, 4, 2, 128, 2, 64, 0.1,
+                                       16, f(), f(), 16, f(), NULL, f(), 1 << 30,
+                                       NULL) == K.KVSEL_ERR_INVALID_ARG
+    # slot reuse: the evicted list must hold cap - budget entries (cap with budgets)
+    assert lib.kvsel_select_evict_slots(f(), f(), NULL, NULL, 1, 2, 100, 60, f(), 39, f(), f(),
+                                        1 << 20, NULL) == K.KVSEL_ERR_INVALID_ARG
+    assert lib.kvsel_select_evict_slots(f(), f(), NULL, f(), 1, 2, 100, 60, f(), 99, f(), f(),
+                                        1 << 20, NULL) == K.KVSEL_ERR_INVALID_ARG
+    assert lib.kvsel_select_evict_slots(f(), f(), NULL, NULL, 1, 2, 40000, 60, f(), 40000, f(),
+                                        f(), 1 << 30, NULL) == K.KVSEL_ERR_UNSUPPORTED
+    assert lib.kvsel_select_evict_slots(f(), f(), NULL, NULL, 1, 2, 100, 60, NULL, 100, f(), f(),
+                                        1 << 20, NULL) == K.KVSEL_ERR_INVALID_ARG
+    assert lib.kvsel_score_evict_slots(BF, 0, f(), f(), f(), NULL, NULL, 1, 4, 2, 128, 2, 64, 0.1,
+                                       16, f(), 47, f(), NULL, f(), 1 << 30,
+                                       NULL) == K.KVSEL_ERR_INVALID_ARG
+    # slot write: positions need the new tokens' first position
+    assert lib.kvsel_slots_write(BF, f(), f(), f(), f(), f(), NULL, f(), 10, f(), 1, 2, 128, 10, 4,
+                                 NULL) == K.KVSEL_ERR_INVALID_ARG
+    assert lib.kvsel_slots_write(BF, f(), f(), NULL, f(), f(), NULL, f(), 10, f(), 1, 2, 80, 10, 4,
+                                 NULL) == K.KVSEL_ERR_UNSUPPORTED
+    # last-k-rows cut: 1 <= k_rows <= cap, compaction into a cache at least cap long
+    for k_rows in (0, 101):
+        assert lib.kvsel_threshold_cut_rows(BF, f(), k_rows, f(), NULL, f(), 1, 28, 4, 128, 100, 5,
+                                            2, 4, 0.01, f(), NULL, NULL, 0, f(), 1 << 30,
+                                            NULL) == K.KVSEL_ERR_INVALID_ARG
+    assert lib.kvsel_threshold_cut_rows(BF, f(), 3, f(), f(), f(), 1, 28, 4, 128, 100, 5, 2, 4, 0.01,
+                                        f(), f(), f(), 99, f(), 1 << 30,
+                                        NULL) == K.KVSEL_ERR_INVALID_ARG
+    assert lib.kvsel_threshold_cut_rows(BF, f(), 3, f(), NULL, f(), 1, 28, 4, 128, 100, 5, 2, 4, 0.01,
+                                        f(), NULL, NULL, 0, f(), 16, NULL) == K.KVSEL_ERR_WORKSPACE
+    assert lib.kvsel_cut_compact(BF, f(), f(), f(), NULL, 1, 2, 128, 10, 4, f(), f(), 10,
+                                 NULL) == K.KVSEL_ERR_INVALID_ARG
+    assert K.kvsel_threshold_cut_rows_workspace(16, 28, 4, 128, 16384, 64) > \
+        K.kvsel_threshold_cut_workspace(16, 28, 4, 128, 16384)
+    assert K.kvsel_threshold_cut_rows_workspace(16, 28, 4, 128, 16384, 0) == 0
