@@ -39,8 +39,12 @@
  *
  * Ownership: the caller allocates every buffer, device workspace included;
  * the library allocates nothing and keeps no state between calls.  Inputs are
- * never written.  A workspace may serve one call at a time; calls that share
- * one must be ordered on one stream.
+ * never written (kvsel_slots_write, which updates a cache in place, aside).
+ * A workspace may serve one call at a time; calls that share one must be
+ * ordered on one stream.  Every entry point only launches kernels on the
+ * given stream (no memory sets, copies or synchronisation), so a call can be
+ * captured into a HIP graph and replayed; kvsel_workspace_error reads back
+ * and synchronises and is the exception.
  *
  * Errors: argument checks run on the host before any launch and return
  * KVSEL_ERR_INVALID_ARG / KVSEL_ERR_UNSUPPORTED / KVSEL_ERR_WORKSPACE with
