@@ -149,6 +149,15 @@ def test_headline_n32768_full_size(mode):
     check_case(case, mode, form="keysum", sample_rows=48)
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_large_cap_ragged_lengths(mode):
+    # the 512-key-block Gram path (bf16, d=128, cap >= 8192) with lengths that
+    # end inside a block: 9001 keys (18 blocks, even) and 8300 (17 blocks, odd)
+    case = synth.rkv_case("bigragged", seed=13, wl=93, b=2, hq=8, hkv=2, d=128, w=8,
+                          lengths=[9001, 8300], cap=9216, budget=1000)
+    check_case(case, mode, form="keysum", sample_rows=24)
+
+
 @pytest.mark.parametrize("mode", ["keysum", "gram"])
 def test_batched_64x8192_sampled(mode):
     case = synth.batched_case(0)
