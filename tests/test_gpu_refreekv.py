@@ -216,3 +216,14 @@ def test_cut_compact_fused_and_stage():
             assert np.array_equal(ko2[bi, h, :L], kf[bi, h, rows])
             assert np.array_equal(vo2[bi, h, :L], vf[bi, h, rows])
             assert (ko2[bi, h, L:] == 0).all()
+
+
+def test_cut_rows_fp32_d64_two_groups():
+    # fp32 inputs, d = 64, 7 * 20 = 140 rows per KV head: two row groups
+    case = synth.cut_case(12, b=3, d=64, lengths=[2500, 300, 1024], dtype="f32")
+    qr = synth.cut_rows_q(case, 20)
+    got = K.kvsel_threshold_cut_rows(dev(qr, "f32"), dev(case.k, "f32"), dev_i32(case.lengths),
+                                     12).cpu().numpy()
+    L_ref, es = rf.threshold_cut_rows(qr, case.as_f32("k"), case.lengths, 12)
+    for (bi, h), e in es.items():
+        assert _valid_cut(e, int(got[bi, h]), 4, 0.01), (bi, h, int(got[bi, h]), int(L_ref[bi, h]))
