@@ -30,7 +30,7 @@ matrix) on a bounded sample: whole KV heads of one layer until --cpu-seconds
 have passed, scaled to a full layer.
 
     python bench.py [--gpus 1] [--steps 64] [--warmup 8] [--mode gram|keysum]
-                    [--no-variants | --variant decode|batched|refreekv|heads ...]
+                    [--no-variants | --variant decode|batched|refreekv|refreekv_rows|heads ...]
 """
 
 from __future__ import annotations
@@ -588,7 +588,7 @@ def copy_calibration(mib: int = 512):
 def run_variants(a, hip) -> dict:
     """The other workloads, each reported with its own value and kernels."""
     import torch
-    want = a.variant or ["decode", "batched", "refreekv"]
+    want = a.variant or ["decode", "batched", "refreekv", "refreekv_rows"]
     out = {}
 
     def log(name, r):
@@ -653,6 +653,7 @@ def run_variants(a, hip) -> dict:
             "ms_per_step": round(r["ms_plain"], 5), "ms_per_step_traced": round(r["ms"], 5),
             "roofline": roofline(r, cut_cost(synth_lengths(), 28, 4), a.profiles, "refreekv"),
             "step_hbm_frac": hbm_frac(r["step_bytes"], r["ms_plain"]), "kernels": r["kernels"]}
+    if "refreekv_rows" in want:
         r = run_refreekv_rows(hip, 4, 8)
         log("refreekv_rows", r)
         out["refreekv_rows"] = {
@@ -687,9 +688,11 @@ def main():
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the decode-loop, batched and ReFreeKV workloads")
     ap.add_argument("--variant", action="append",
-                    choices=["decode", "batched", "refreekv", "heads"],
+                    choices=["decode", "batched", "refreekv", "refreekv_rows", "heads"],
                     help="run only these extra workloads (repeatable)")
     ap.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--variants-only", action="store_true",
+                    help="skip the headline workload and print only the variants (for profiling)")
     a = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -705,6 +708,9 @@ def main():
         return
     torch.cuda.init()
     hip = Hip()
+    if a.variants_only:
+        print(json.dumps({"variants": run_variants(a, hip)}))
+        return
     layers, first = make_layers(a.layers)
     torch.cuda.synchronize()
 
