@@ -60,6 +60,10 @@ __device__ __forceinline__ uint32_t buf_ld32(__amdgpu_buffer_rsrc_t r, uint32_t 
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
 
+__device__ __forceinline__ u32x4_t buf_ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
@@ -101,6 +105,23 @@ __device__ __forceinline__ f32x16_t mfma_tile<BF16, 4>(const Frag<4>& a, const F
                                                   __builtin_bit_cast(bf16x8_t, b.c[j]), acc, 0, 0, 0);
   return acc;
 }
+// acc += one 16-byte chunk of A . the same chunk of B^T (the k-step a lane
+// pair (l32, hf) covers in mfma_tile for that chunk index)
+template <typename E>
+__device__ __forceinline__ f32x16_t mfma_chunk(u32x4_t a, u32x4_t b, f32x16_t acc);
+template <>
+__device__ __forceinline__ f32x16_t mfma_chunk<BF16>(u32x4_t a, u32x4_t b, f32x16_t acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16_t mfma_chunk<F32>(u32x4_t a, u32x4_t b, f32x16_t acc) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[e]), __uint_as_float(b[e]), acc, 0, 0, 0);
+  return acc;
+}
+
 template <int NC>
 __device__ __forceinline__ f32x16_t mfma_tile_f32(const Frag<NC>& a, const Frag<NC>& b,
                                                   f32x16_t acc) {

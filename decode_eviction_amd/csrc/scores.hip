@@ -56,6 +56,42 @@ __device__ __forceinline__ void scatter_down(float* v, int l32) {
   }
 }
 
+// The MT*32 query rows of a head are the same for the four waves of a
+// work-group.  Where they fit they are staged once in LDS, rows padded by one
+// 16-byte chunk (the 32 lanes of a half reading one chunk of 32 rows then hit
+// distinct banks), and the matrix-core loops read them a chunk at a time,
+// which keeps them out of registers.  load() issues the global reads (rows
+// >= m read as zero through the buffer range check, so no lane waits);
+// store() writes them to LDS once they have landed.
+template <typename E, int D, int MT>
+struct QStage {
+  static constexpr int QC = Geo<E, D>::kChunks;  // 16-byte chunks per row
+  static constexpr int QS = QC + 1;              // staged row stride in chunks
+  static constexpr int PER = (MT * 32 * QC + 255) / 256;
+  static constexpr bool kLds = MT * 32 * QS * 16 <= 40 * 1024;
+  static constexpr int kWords = kLds ? MT * 32 * QS : 1;
+  u32x4_t v[kLds ? PER : 1];
+  __device__ __forceinline__ void load(const char* qb, int m, int tid) {
+    const auto qr = buf_rsrc(qb, (uint32_t)m * Geo<E, D>::kRowBytes);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = min(tid + 256 * u, MT * 32 * QC - 1);
+      v[u] = buf_ld128(qr, (uint32_t)(i / QC) * Geo<E, D>::kRowBytes + 16 * (i % QC), 0);
+    }
+  }
+  __device__ __forceinline__ void store(u32x4_t* qs, int tid) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + 256 * u;
+      if (i < MT * 32 * QC) qs[(i / QC) * QS + i % QC] = v[u];
+    }
+  }
+  // chunk j of row 32t + l32 for lane half hf (the chunk load_frag puts in c[j])
+  static __device__ __forceinline__ u32x4_t chunk(const u32x4_t* qs, int t, int l32, int hf, int j) {
+    return qs[(32 * t + l32) * QS + 2 * j + hf];
+  }
+};
+
 template <typename E, int D, int MT, int MODE>
 __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
   using G = Geo<E, D>;
@@ -79,11 +115,18 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
   const char* kb = p.k + head * (long)p.cap * G::kRowBytes;
   const char* qb = p.q + (((long)bi * p.hq + (long)h * p.g) * p.w + p.rows0) * G::kRowBytes;
 
-  Frag<NC> qf[MT];
+  using QSt = QStage<E, D, MT>;
+  __shared__ u32x4_t qs[QSt::kWords];
+  QSt qst;
+  Frag<NC> qf[QSt::kLds ? 1 : MT];
+  if constexpr (QSt::kLds) {
+    qst.load(qb, p.m, tid);
+  } else {
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int r = 32 * t + l32;
-    load_frag<E, D>(qf[t], qb, r, r < p.m, hf);
+    for (int t = 0; t < MT; ++t) {
+      const int r = 32 * t + l32;
+      load_frag<E, D>(qf[t], qb, r, r < p.m, hf);
+    }
   }
   const int tok0 = c0 + wave * 64;
   Frag<NC> kf[2];
@@ -95,11 +138,77 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
 
   // C[token][row]: lane owns query row 32t + l32 and tokens tile_row(i, hf)
   f32x16_t acc[2][MT];
+  if constexpr (QSt::kLds) {
+    qst.store(qs, tid);
+    __syncthreads();
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[tt][t] = mfma_tile<E, NC>(kf[tt], qf[t], zero16());
+      for (int t = 0; t < MT; ++t) acc[tt][t] = zero16();
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const u32x4_t qc = QSt::chunk(qs, t, l32, hf, j);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) acc[tt][t] = mfma_chunk<E>(kf[tt].c[j], qc, acc[tt][t]);
+      }
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[tt][t] = mfma_tile<E, NC>(kf[tt], qf[t], zero16());
+  }
 
+  // key norms (and the unit-key sum) first: the key fragments are then dead
+  // before the attention tiles are read back
+  if constexpr (MODE != kModeCut) {
+    float inv[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float ss = frag_sumsq<E, NC>(kf[tt]);
+      ss += xor32(ss);
+      inv[tt] = inv_norm_of(ss);
+      const int tok = tok0 + 32 * tt + l32;
+      // every slot of the chunk is written (0 past n): the Gram kernel streams
+      // whole 128-key blocks of weights
+      if (MODE == kModeGram && hf == 0) p.inv_norm[head * (long)p.wstride + tok] = inv[tt];
+    }
+    if constexpr (MODE == kModeKeysum) {
+      // this chunk's sum of unit keys: per lane its two tokens, then a
+      // reduce-scatter over the 32 lanes of the half, then across waves
+      // (the first reduce-scatter step is taken as the values are formed, so
+      // that only half of them are ever held)
+      float v[LE / 2];
+      {
+        const bool up = (l32 & 16) != 0;
+#pragma unroll
+        for (int i = 0; i < LE / 2; ++i) {
+          const int j = i / PC, e = i % PC;
+          const float lo = inv[0] * frag_elem<E>(kf[0].c[j], e) + inv[1] * frag_elem<E>(kf[1].c[j], e);
+          const float hi = inv[0] * frag_elem<E>(kf[0].c[j + NC / 2], e) +
+                           inv[1] * frag_elem<E>(kf[1].c[j + NC / 2], e);
+          v[i] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, 16, 64);
+        }
+      }
+      scatter_down<LE / 2, 8, PC>(v, l32);
+      constexpr int R = 32 / NC;  // lanes of a half still to be summed
+      __shared__ float red[256 * PC];
+      float* mine = red + (wave * 64 + lane) * PC;
+#pragma unroll
+      for (int e = 0; e < PC; ++e) mine[e] = v[e];
+      __syncthreads();
+      if (tid < D) {
+        const int ch = tid / PC, e = tid % PC, hfd = ch & 1, j = ch >> 1;
+        float a = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv)
+#pragma unroll
+          for (int q = 0; q < R; ++q) a += red[(wv * 64 + hfd * 32 + j * R + q) * PC + e];
+        p.spart[(head * p.nchunk + chunk) * D + tid] = a;
+      }
+    }
+  }
   // per-row max and sum of 2^(t - max), t = logit * log2(e) / sqrt(d).  The
   // last key a query row sees is n-1, or n - krows + r for row r of the last
   // krows rows (causal); only waves past the smallest such limit mask keys.
@@ -158,44 +267,6 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
               v[e] = full || tb + e <= lim[t] ? acc[tt][t][4 * q4 + e] * sc2 : -INFINITY;
             *reinterpret_cast<f32x4_t*>(lrow + tb) = v;
           }
-      }
-    }
-  } else {
-    float inv[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      float ss = frag_sumsq<E, NC>(kf[tt]);
-      ss += xor32(ss);
-      inv[tt] = inv_norm_of(ss);
-      const int tok = tok0 + 32 * tt + l32;
-      // every slot of the chunk is written (0 past n): the Gram kernel streams
-      // whole 128-key blocks of weights
-      if (MODE == kModeGram && hf == 0) p.inv_norm[head * (long)p.wstride + tok] = inv[tt];
-    }
-    if constexpr (MODE == kModeKeysum) {
-      // this chunk's sum of unit keys: per lane its two tokens, then a
-      // reduce-scatter over the 32 lanes of the half, then across waves
-      float v[LE];
-#pragma unroll
-      for (int j = 0; j < NC; ++j)
-#pragma unroll
-        for (int e = 0; e < PC; ++e)
-          v[j * PC + e] = inv[0] * frag_elem<E>(kf[0].c[j], e) + inv[1] * frag_elem<E>(kf[1].c[j], e);
-      scatter_down<LE, 16, PC>(v, l32);
-      constexpr int R = 32 / NC;  // lanes of a half still to be summed
-      __shared__ float red[256 * PC];
-      float* mine = red + (wave * 64 + lane) * PC;
-#pragma unroll
-      for (int e = 0; e < PC; ++e) mine[e] = v[e];
-      __syncthreads();
-      if (tid < D) {
-        const int ch = tid / PC, e = tid % PC, hfd = ch & 1, j = ch >> 1;
-        float a = 0.f;
-#pragma unroll
-        for (int wv = 0; wv < 4; ++wv)
-#pragma unroll
-          for (int q = 0; q < R; ++q) a += red[(wv * 64 + hfd * 32 + j * R + q) * PC + e];
-        p.spart[(head * p.nchunk + chunk) * D + tid] = a;
       }
     }
   }
@@ -284,6 +355,9 @@ __global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
 
   __shared__ float2 rs[MT * 32];
   __shared__ uint32_t lh[MODE == kModeKeysum ? kHistBins : 1];
+  // key-sum form: the head's sum of unit keys, read from LDS 16 bytes at a
+  // time (kept out of registers so that more work-groups fit on a CU)
+  __shared__ __attribute__((aligned(16))) float ssh[MODE == kModeKeysum ? D : 4];
   if constexpr (MODE == kModeKeysum) {
     if (p.hist)
       for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
@@ -292,11 +366,18 @@ __global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
     float2 v = p.rstat[head * p.mp + tid];
     rs[tid] = tid < p.m ? v : make_float2(0.f, 0.f);  // padding rows contribute 0
   }
-  Frag<NC> qf[MT];
+  using QSt = QStage<E, D, MT>;
+  __shared__ u32x4_t qs[QSt::kWords];
+  QSt qst;
+  Frag<NC> qf[QSt::kLds ? 1 : MT];
+  if constexpr (QSt::kLds) {
+    qst.load(qb, p.m, tid);
+  } else {
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int r = 32 * t + l32;
-    load_frag<E, D>(qf[t], qb, r, r < p.m, hf);
+    for (int t = 0; t < MT; ++t) {
+      const int r = 32 * t + l32;
+      load_frag<E, D>(qf[t], qb, r, r < p.m, hf);
+    }
   }
   const int tok0 = c0 + wave * 64;
   Frag<NC> kf[2];
@@ -305,14 +386,32 @@ __global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
     const int tok = tok0 + 32 * tt + l32;
     load_frag<E, D>(kf[tt], kb, tok, tok < n, hf);
   }
-  float sv[MODE == kModeKeysum ? LE : 1];
   if constexpr (MODE == kModeKeysum) {
+    if (tid < D) ssh[tid] = p.ssum[head * D + tid];
+  }
+  if constexpr (QSt::kLds) qst.store(qs, tid);
+  __syncthreads();
+  // k_j . S and |k_j|^2 for the wave's two key tiles (lane: token l32 of
+  // each tile), taken before the attention products so that the unpacked
+  // key values are not live across them
+  float dots[2] = {0.f, 0.f}, sqs[2] = {0.f, 0.f};
+  if constexpr (MODE == kModeKeysum) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) sqs[tt] = frag_sumsq<E, NC>(kf[tt]);
 #pragma unroll
     for (int j = 0; j < NC; ++j)
 #pragma unroll
-      for (int e = 0; e < PC; ++e) sv[j * PC + e] = p.ssum[head * D + frag_dim<E>(j, e, hf)];
+      for (int q = 0; q < PC / 4; ++q) {
+        const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(&ssh[frag_dim<E>(j, 4 * q, hf)]);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dots[tt] = fmaf(frag_elem<E>(kf[tt].c[j], 4 * q + e), s4[e], dots[tt]);
+        // at most four LDS reads in flight (the compiler would otherwise issue
+        // all of them first and hold them in registers)
+        if ((j * (PC / 4) + q) % 4 == 3) asm volatile("" : "+v"(dots[0]), "+v"(dots[1])::"memory");
+      }
   }
-  __syncthreads();
 
   const float sc2 = p.scale2;
   const float inv_m = 1.0f / (float)p.m;
@@ -323,7 +422,13 @@ __global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       // C[row][token]: lane owns token l32, rows 32t + tile_row(i, hf)
-      const f32x16_t a = mfma_tile<E, NC>(qf[t], kf[tt], zero16());
+      f32x16_t a = zero16();
+      if constexpr (QSt::kLds) {
+#pragma unroll
+        for (int j = 0; j < NC; ++j) a = mfma_chunk<E>(QSt::chunk(qs, t, l32, hf, j), kf[tt].c[j], a);
+      } else {
+        a = mfma_tile<E, NC>(qf[t], kf[tt], a);
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float2 st = rs[32 * t + tile_row(i, hf)];
@@ -337,14 +442,10 @@ __global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
     if constexpr (MODE == kModeGram) {
       if (hf == 0 && tok < n) p.i_out[o] = imp;
     } else {
-      float ss = frag_sumsq<E, NC>(kf[tt]);
+      float ss = sqs[tt];
       ss += xor32(ss);
       const float inv = inv_norm_of(ss);
-      float dot = 0.f;
-#pragma unroll
-      for (int j = 0; j < NC; ++j)
-#pragma unroll
-        for (int e = 0; e < PC; ++e) dot = fmaf(frag_elem<E>(kf[tt].c[j], e), sv[j * PC + e], dot);
+      float dot = dots[tt];
       dot += xor32(dot);
       const float red = (inv * dot - inv * inv * ss) * inv_nm1;
       const float z = p.lambda * imp - (1.0f - p.lambda) * red;
