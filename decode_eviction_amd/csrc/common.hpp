@@ -60,6 +60,18 @@ __device__ __forceinline__ uint32_t buf_ld32(__amdgpu_buffer_rsrc_t r, uint32_t 
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
 
+// s_waitcnt immediates (gfx9 encoding): wait until at most N vector memory
+// operations of this wave are outstanding; LDS/scalar counters untouched.
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// 16 bytes per lane from a buffer straight into LDS: lane l of the wave
+// writes bytes [16 l, 16 l + 16) from lds_wave_base (wave-uniform); offsets
+// past the buffer's range write zeros.  Completion is counted by vmcnt.
+__device__ __forceinline__ void buf_lds16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           (int)voff, 0, 0, 0);
+}
+
 __device__ __forceinline__ u32x4_t buf_ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }

@@ -43,10 +43,6 @@ __device__ __forceinline__ int xcd_major(int L, int total) {
   return (L % kXcd) * (total / kXcd) + L / kXcd;
 }
 
-// s_waitcnt immediates (gfx9 encoding): wait until at most N vector memory
-// operations of this wave are outstanding; LDS/scalar counters untouched.
-constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
 // Blocks of columns (of 256 keys) that row block I computes; see above.
 __device__ __forceinline__ int gram_blocks(int I, int nb) {
   return 1 + (nb - 1) / 2 + ((nb % 2 == 0 && I < nb / 2) ? 1 : 0);

@@ -57,43 +57,52 @@ __device__ __forceinline__ void scatter_down(float* v, int l32) {
 }
 
 // The MT*32 query rows of a head are the same for the four waves of a
-// work-group.  Where they fit they are staged once in LDS, rows padded by one
-// 16-byte chunk (the 32 lanes of a half reading one chunk of 32 rows then hit
-// distinct banks), and the matrix-core loops read them a chunk at a time,
-// which keeps them out of registers.  load() issues the global reads (rows
-// >= m read as zero through the buffer range check, so no lane waits);
-// store() writes them to LDS once they have landed.
+// work-group.  Where they fit they are copied once into LDS, straight from
+// global memory (no registers), and the matrix-core loops read them a chunk
+// at a time.  Chunk c of row r sits at slot r*QC + (c ^ (r mod QC)), so the
+// 16 lanes of a group reading one chunk of 16 consecutive rows hit distinct
+// banks.  Rows >= m lie past the buffer's range and arrive as zeros.
 template <typename E, int D, int MT>
 struct QStage {
   static constexpr int QC = Geo<E, D>::kChunks;  // 16-byte chunks per row
-  static constexpr int QS = QC + 1;              // staged row stride in chunks
-  static constexpr int PER = (MT * 32 * QC + 255) / 256;
-  static constexpr bool kLds = MT * 32 * QS * 16 <= 40 * 1024;
-  static constexpr int kWords = kLds ? MT * 32 * QS : 1;
-  u32x4_t v[kLds ? PER : 1];
-  __device__ __forceinline__ void load(const char* qb, int m, int tid) {
+  static constexpr int SLOTS = MT * 32 * QC;
+  static_assert(SLOTS % 256 == 0, "whole work-group copies");
+  static constexpr bool kLds = SLOTS * 16 <= 40 * 1024;
+  static constexpr int kWords = kLds ? SLOTS : 1;
+  // issue the copies; the caller calls landed() and then synchronises
+  static __device__ __forceinline__ void issue(u32x4_t* qs, const char* qb, int m, int tid) {
     const auto qr = buf_rsrc(qb, (uint32_t)m * Geo<E, D>::kRowBytes);
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = min(tid + 256 * u, MT * 32 * QC - 1);
-      v[u] = buf_ld128(qr, (uint32_t)(i / QC) * Geo<E, D>::kRowBytes + 16 * (i % QC), 0);
+    for (int u = 0; u < SLOTS / 256; ++u) {
+      const int sl = 256 * u + tid, r = sl / QC, c = (sl % QC) ^ (r % QC);
+      buf_lds16(qr, qs + 256 * u + (tid & ~63), (uint32_t)r * Geo<E, D>::kRowBytes + 16 * c);
     }
   }
-  __device__ __forceinline__ void store(u32x4_t* qs, int tid) const {
+  // Reads back one word of each of this thread's copies before the barrier:
+  // the compiler then waits for exactly those copies (not for loads issued
+  // after them), and the barrier makes every wave's copies visible.
+  static __device__ __forceinline__ void landed(const u32x4_t* qs, int tid) {
+    uint32_t x = 0;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = tid + 256 * u;
-      if (i < MT * 32 * QC) qs[(i / QC) * QS + i % QC] = v[u];
-    }
+    for (int u = 0; u < SLOTS / 256; ++u) x |= reinterpret_cast<const uint32_t*>(qs + 256 * u + tid)[0];
+    asm volatile("" ::"v"(x));
   }
   // chunk j of row 32t + l32 for lane half hf (the chunk load_frag puts in c[j])
   static __device__ __forceinline__ u32x4_t chunk(const u32x4_t* qs, int t, int l32, int hf, int j) {
-    return qs[(32 * t + l32) * QS + 2 * j + hf];
+    const int r = 32 * t + l32;
+    return qs[r * QC + ((2 * j + hf) ^ (r % QC))];
   }
 };
 
+// Four waves per SIMD (every work-group of a 32K-token head resident at
+// once) where the two key tiles leave room for it; fp32 keys of 128
+// dimensions take 128 registers by themselves.
+template <typename E, int D>
+constexpr int kStatsWaves = E::kBytes == 2 || D == 64 ? 4 : 1;
+
 template <typename E, int D, int MT, int MODE>
-__global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kStatsWaves<E, D>)))
+void k_stats(ScoreParams p) {
   using G = Geo<E, D>;
   constexpr int NC = G::kNC;
   constexpr int LE = G::kLaneElems;
@@ -117,10 +126,9 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
 
   using QSt = QStage<E, D, MT>;
   __shared__ u32x4_t qs[QSt::kWords];
-  QSt qst;
   Frag<NC> qf[QSt::kLds ? 1 : MT];
   if constexpr (QSt::kLds) {
-    qst.load(qb, p.m, tid);
+    QSt::issue(qs, qb, p.m, tid);
   } else {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -136,99 +144,78 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
     load_frag<E, D>(kf[tt], kb, tok, tok < n, hf);
   }
 
-  // C[token][row]: lane owns query row 32t + l32 and tokens tile_row(i, hf)
-  f32x16_t acc[2][MT];
-  if constexpr (QSt::kLds) {
-    qst.store(qs, tid);
-    __syncthreads();
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[tt][t] = zero16();
-#pragma unroll
-    for (int j = 0; j < NC; ++j)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const u32x4_t qc = QSt::chunk(qs, t, l32, hf, j);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) acc[tt][t] = mfma_chunk<E>(kf[tt].c[j], qc, acc[tt][t]);
+  // key norms (and, key-sum mode, the chunk's unit-key sum)
+  auto norms = [&]() {
+    if constexpr (MODE != kModeCut) {
+      float inv[2];
+  #pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float ss = frag_sumsq<E, NC>(kf[tt]);
+        ss += xor32(ss);
+        inv[tt] = inv_norm_of(ss);
+        const int tok = tok0 + 32 * tt + l32;
+        // every slot of the chunk is written (0 past n): the Gram kernel streams
+        // whole 128-key blocks of weights
+        if (MODE == kModeGram && hf == 0) p.inv_norm[head * (long)p.wstride + tok] = inv[tt];
       }
-  } else {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[tt][t] = mfma_tile<E, NC>(kf[tt], qf[t], zero16());
-  }
-
-  // key norms (and the unit-key sum) first: the key fragments are then dead
-  // before the attention tiles are read back
-  if constexpr (MODE != kModeCut) {
-    float inv[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      float ss = frag_sumsq<E, NC>(kf[tt]);
-      ss += xor32(ss);
-      inv[tt] = inv_norm_of(ss);
-      const int tok = tok0 + 32 * tt + l32;
-      // every slot of the chunk is written (0 past n): the Gram kernel streams
-      // whole 128-key blocks of weights
-      if (MODE == kModeGram && hf == 0) p.inv_norm[head * (long)p.wstride + tok] = inv[tt];
-    }
-    if constexpr (MODE == kModeKeysum) {
-      // this chunk's sum of unit keys: per lane its two tokens, then a
-      // reduce-scatter over the 32 lanes of the half, then across waves
-      // (the first reduce-scatter step is taken as the values are formed, so
-      // that only half of them are ever held)
-      float v[LE / 2];
-      {
-        const bool up = (l32 & 16) != 0;
-#pragma unroll
-        for (int i = 0; i < LE / 2; ++i) {
-          const int j = i / PC, e = i % PC;
-          const float lo = inv[0] * frag_elem<E>(kf[0].c[j], e) + inv[1] * frag_elem<E>(kf[1].c[j], e);
-          const float hi = inv[0] * frag_elem<E>(kf[0].c[j + NC / 2], e) +
-                           inv[1] * frag_elem<E>(kf[1].c[j + NC / 2], e);
-          v[i] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, 16, 64);
+      if constexpr (MODE == kModeKeysum) {
+        // this chunk's sum of unit keys: per lane its two tokens, then a
+        // reduce-scatter over the 32 lanes of the half, then across waves
+        // (the first reduce-scatter step is taken as the values are formed, so
+        // that only half of them are ever held)
+        float v[LE / 2];
+        {
+          const bool up = (l32 & 16) != 0;
+  #pragma unroll
+          for (int i = 0; i < LE / 2; ++i) {
+            const int j = i / PC, e = i % PC;
+            const float lo = inv[0] * frag_elem<E>(kf[0].c[j], e) + inv[1] * frag_elem<E>(kf[1].c[j], e);
+            const float hi = inv[0] * frag_elem<E>(kf[0].c[j + NC / 2], e) +
+                             inv[1] * frag_elem<E>(kf[1].c[j + NC / 2], e);
+            v[i] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, 16, 64);
+          }
+        }
+        scatter_down<LE / 2, 8, PC>(v, l32);
+        constexpr int R = 32 / NC;  // lanes of a half still to be summed
+        __shared__ float red[256 * PC];
+        float* mine = red + (wave * 64 + lane) * PC;
+  #pragma unroll
+        for (int e = 0; e < PC; ++e) mine[e] = v[e];
+        __syncthreads();
+        if (tid < D) {
+          const int ch = tid / PC, e = tid % PC, hfd = ch & 1, j = ch >> 1;
+          float a = 0.f;
+  #pragma unroll
+          for (int wv = 0; wv < 4; ++wv)
+  #pragma unroll
+            for (int q = 0; q < R; ++q) a += red[(wv * 64 + hfd * 32 + j * R + q) * PC + e];
+          p.spart[(head * p.nchunk + chunk) * D + tid] = a;
         }
       }
-      scatter_down<LE / 2, 8, PC>(v, l32);
-      constexpr int R = 32 / NC;  // lanes of a half still to be summed
-      __shared__ float red[256 * PC];
-      float* mine = red + (wave * 64 + lane) * PC;
-#pragma unroll
-      for (int e = 0; e < PC; ++e) mine[e] = v[e];
-      __syncthreads();
-      if (tid < D) {
-        const int ch = tid / PC, e = tid % PC, hfd = ch & 1, j = ch >> 1;
-        float a = 0.f;
-#pragma unroll
-        for (int wv = 0; wv < 4; ++wv)
-#pragma unroll
-          for (int q = 0; q < R; ++q) a += red[(wv * 64 + hfd * 32 + j * R + q) * PC + e];
-        p.spart[(head * p.nchunk + chunk) * D + tid] = a;
-      }
     }
-  }
+  };
+
   // per-row max and sum of 2^(t - max), t = logit * log2(e) / sqrt(d).  The
   // last key a query row sees is n-1, or n - krows + r for row r of the last
   // krows rows (causal); only waves past the smallest such limit mask keys.
   const bool causal = MODE == kModeCut && p.krows > 1;
-  int lim[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t)
-    lim[t] = causal ? n - p.krows + (p.rows0 + 32 * t + l32) % p.krows : n - 1;
   const bool full = tok0 + 63 <= (causal ? n - p.krows : n - 1);
   const float sc2 = p.scale2;
   __shared__ float2 wst[4][MT * 32];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
+  // row tile t from its two accumulator tiles C[token][row] (lane: query row
+  // 32t + l32, tokens tile_row(i, hf) of each key tile)
+  auto row_tile = [&](int t, const f32x16_t (&a)[2]) {
+    const int lim = causal ? n - p.krows + (p.rows0 + 32 * t + l32) % p.krows : n - 1;
+    // token of slot (tt, i) is tok0 + 4 hf + 32 tt + 8 (i / 4) + i % 4: the
+    // masks compare constants against one per-lane value
+    const int rel = lim - (tok0 + 4 * hf);
     float m = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const bool ok = full || tok0 + 32 * tt + tile_row(i, hf) <= lim[t];
-        m = ok ? fmaxf(m, acc[tt][t][i]) : m;
+        const bool ok = full || 32 * tt + 8 * (i >> 2) + (i & 3) <= rel;
+        m = ok ? fmaxf(m, a[tt][i]) : m;
       }
     m = fmaxf(m, xor32(m));
     const float m2 = m * sc2;  // sc2 > 0: the max of the scaled logits
@@ -238,21 +225,18 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const bool ok = full || tok0 + 32 * tt + tile_row(i, hf) <= lim[t];
-          const float e = exp2_fast(fmaf(acc[tt][t][i], sc2, -m2));
+          const bool ok = full || 32 * tt + 8 * (i >> 2) + (i & 3) <= rel;
+          const float e = exp2_fast(fmaf(a[tt][i], sc2, -m2));
           s += ok ? e : 0.f;
         }
     }
     s += xor32(s);
     if (hf == 0) wst[wave][32 * t + l32] = make_float2(m2, s);
-  }
 
-  if constexpr (MODE == kModeCut) {
-    // logits of the m rows in base-2 units (-inf where a row does not see the
-    // key), 4 consecutive tokens per store
-    const long ls = (long)p.nchunk * kChunk;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
+    if constexpr (MODE == kModeCut) {
+      // logits of the m rows in base-2 units (-inf where a row does not see
+      // the key), 4 consecutive tokens per store
+      const long ls = (long)p.nchunk * kChunk;
       const int row = 32 * t + l32;
       if (row < p.m) {
         float* lrow = p.logits + (head * p.m + row) * ls;
@@ -263,12 +247,55 @@ __global__ __launch_bounds__(256) void k_stats(ScoreParams p) {
             const int tb = tok0 + 32 * tt + 8 * q4 + 4 * hf;
             f32x4_t v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              v[e] = full || tb + e <= lim[t] ? acc[tt][t][4 * q4 + e] * sc2 : -INFINITY;
+            for (int e = 0; e < 4; ++e) v[e] = full || 32 * tt + 8 * q4 + e <= rel ? a[tt][4 * q4 + e] * sc2 : -INFINITY;
             *reinterpret_cast<f32x4_t*>(lrow + tb) = v;
           }
       }
     }
+  };
+
+  if constexpr (QSt::kLds) {
+    QSt::landed(qs, tid);
+    __syncthreads();
+    // one row tile at a time: two accumulator tiles live, the query chunks
+    // re-read from LDS per tile
+    auto mfma_rows = [&](int t, f32x16_t (&a)[2]) {
+      a[0] = zero16();
+      a[1] = zero16();
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const u32x4_t qc = QSt::chunk(qs, t, l32, hf, j);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) a[tt] = mfma_chunk<E>(kf[tt].c[j], qc, a[tt]);
+      }
+    };
+    if constexpr (MT == 1) {
+      // the key fragments die in norms(), before the tile is read back
+      f32x16_t a[2];
+      mfma_rows(0, a);
+      norms();
+      row_tile(0, a);
+    } else {
+      norms();
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        f32x16_t a[2];
+        mfma_rows(t, a);
+        row_tile(t, a);
+        // keeps the next tile's products after this one's epilogue (two
+        // tiles in flight would double the accumulator registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
+    f32x16_t acc[MT][2];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) acc[t][tt] = mfma_tile<E, NC>(kf[tt], qf[t], zero16());
+    norms();
+#pragma unroll
+    for (int t = 0; t < MT; ++t) row_tile(t, acc[t]);
   }
   __syncthreads();
   if (tid < MT * 32) {
@@ -339,7 +366,8 @@ __global__ __launch_bounds__(1024) void k_reduce(ScoreParams p) {
 }
 
 template <typename E, int D, int MT, int MODE>
-__global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT > 1 ? kStatsWaves<E, D> : 1)))
+void k_pool(ScoreParams p) {
   using G = Geo<E, D>;
   constexpr int NC = G::kNC;
   constexpr int LE = G::kLaneElems;
@@ -368,10 +396,9 @@ __global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
   }
   using QSt = QStage<E, D, MT>;
   __shared__ u32x4_t qs[QSt::kWords];
-  QSt qst;
   Frag<NC> qf[QSt::kLds ? 1 : MT];
   if constexpr (QSt::kLds) {
-    qst.load(qb, p.m, tid);
+    QSt::issue(qs, qb, p.m, tid);
   } else {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -389,7 +416,7 @@ __global__ __launch_bounds__(256) void k_pool(ScoreParams p) {
   if constexpr (MODE == kModeKeysum) {
     if (tid < D) ssh[tid] = p.ssum[head * D + tid];
   }
-  if constexpr (QSt::kLds) qst.store(qs, tid);
+  if constexpr (QSt::kLds) QSt::landed(qs, tid);
   __syncthreads();
   // k_j . S and |k_j|^2 for the wave's two key tiles (lane: token l32 of
   // each tile), taken before the attention products so that the unpacked
