@@ -463,9 +463,13 @@ def run_refreekv_rows(hip, n_layers, steps, k_rows=64):
     tok = int(lengths.sum()) * hkv
     cost = {"cut_scan": {"bytes": 0}}
     for i, m in enumerate(groups):
-        cost[f"stats_g{i}"] = {"bytes": tok * D * 2 + tok * m * 4}
+        # groups of more than 32 rows store no logits: the energy kernel
+        # recomputes them from Q and K (one more read of K)
+        stored = m <= 32
+        cost[f"stats_g{i}"] = {"bytes": tok * D * 2 + (tok * m * 4 if stored else 0)}
         cost[f"reduce_g{i}"] = {"bytes": 0}
-        cost[f"cut_energy_g{i}"] = {"bytes": tok * m * 4 + tok * 8 * (2 if i else 1)}
+        cost[f"cut_energy_g{i}"] = {"bytes": (tok * m * 4 if stored else tok * D * 2) +
+                                    tok * 8 * (2 if i else 1)}
 
     def call(i, events=None):
         q, k, v = layers[i % len(layers)]

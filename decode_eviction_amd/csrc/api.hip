@@ -221,6 +221,12 @@ struct CutWs {
   size_t bytes;
 };
 
+// Row groups of at most this many rows store their logits for k_cut_energy
+// (8 bytes per row and position, written and read back); larger groups form
+// the energies in k_pool from logits recomputed from Q and K, which costs one
+// more read of K (256 bytes per position for bf16, d = 128) instead.
+constexpr int kStoredLogitRows = 32;
+
 // rows: attention rows scored per launch (g for the single last row; up to
 // kMaxRows of the g*k last rows)
 CutWs cut_ws(void* base, int b, int hkv, int rows, int cap) {
@@ -232,7 +238,7 @@ CutWs cut_ws(void* base, int b, int hkv, int rows, int cap) {
   w.err = c.take<int32_t>(64);
   w.cstat = c.take<float2>(heads * nchunk * mp);
   w.rstat = c.take<float2>(heads * mp);
-  w.logits = c.take<float>(heads * rows * (size_t)nchunk * kChunk);
+  w.logits = rows <= kStoredLogitRows ? c.take<float>(heads * rows * (size_t)nchunk * kChunk) : nullptr;
   w.energy = c.take<uint64_t>(heads * (size_t)nchunk * kChunk);
   w.ctot = c.take<uint64_t>(heads * nchunk);
   w.bytes = (c.off + kAlign - 1) / kAlign * kAlign;
@@ -642,7 +648,9 @@ static kvsel_status threshold_cut_impl(kvsel_dtype dt, const void* q_rows, int k
     p.scale2 = kLog2e / sqrtf((float)d);
     p.cstat = ws.cstat;
     p.rstat = ws.rstat;
-    p.logits = ws.logits;
+    p.logits = ws.logits;  // null: energies from recomputed logits
+    p.energy = ws.energy;
+    p.ctot = ws.ctot;
     p.err = ws.err;
     c.logits = ws.logits;
     c.attn = nullptr;
@@ -655,10 +663,15 @@ static kvsel_status threshold_cut_impl(kvsel_dtype dt, const void* q_rows, int k
       p.mp = rows_padded(p.m);
       KV_TRY(launch_stats(dt, d, kModeCut, p, stream, tr));
       KV_TRY(launch_reduce(d, kModeCut, p, stream, tr));
-      c.rows = p.m;
-      c.mp = p.mp;
-      c.accum = r0 > 0;
-      KV_TRY(launch_cut_energy(c, stream, tr));
+      if (ws.logits) {
+        c.rows = p.m;
+        c.mp = p.mp;
+        c.accum = r0 > 0;
+        KV_TRY(launch_cut_energy(c, stream, tr));
+      } else {
+        p.accum = r0 > 0;
+        KV_TRY(launch_pool(dt, d, kModeCut, p, stream, tr));
+      }
     }
     KV_TRY(launch_cut_scan(c, stream, tr));
   }

@@ -291,6 +291,13 @@ __device__ __forceinline__ void dma_lds4(const void* g, const void* lds_wave_bas
 
 #pragma clang diagnostic pop
 
+// x * y rounded to fp32 on its own, never fused into a following add (the
+// product is the value another kernel stores and reloads)
+__device__ __forceinline__ float mul_unfused(float x, float y) {
+#pragma clang fp contract(off)
+  return x * y;
+}
+
 // 2^x on the transcendental unit (v_exp_f32)
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

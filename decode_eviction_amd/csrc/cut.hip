@@ -62,15 +62,10 @@ __global__ __launch_bounds__(256) void k_cut_energy(CutParams p) {
   const int tok = c0 + tid;
   uint64_t* ep = p.energy + head * (long)p.nchunk * kChunk + tok;
   uint64_t e = p.accum ? *ep : 0u;  // row groups after the first add to the earlier ones
-  // floor(fl32(a*a) * 2^52) of one probability (a square of at most 1)
-  auto term = [](float a) -> uint64_t {
-    const float sq = fminf(__fmul_rn(a, a), 1.0f);
-    return (uint64_t)((double)sq * 4503599627370496.0);
-  };
   if (tok < n) {
     if (p.attn) {
       for (int q = 0; q < p.rows; ++q)
-        e += term(p.attn[((long)bi * p.hq + (long)h * p.g + q) * p.cap + tok]);
+        e += energy_term(p.attn[((long)bi * p.hq + (long)h * p.g + q) * p.cap + tok]);
     } else {
       // 8 rows at a time, their loads issued before use; a row that sees no
       // key (sum 0) has no attention mass
@@ -88,7 +83,7 @@ __global__ __launch_bounds__(256) void k_cut_energy(CutParams p) {
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (q0 + u < p.rows) e += term(st[u].y > 0.f ? exp2_fast(t[u] - st[u].x) * st[u].y : 0.f);
+          if (q0 + u < p.rows) e += energy_term(st[u].y > 0.f ? exp2_fast(t[u] - st[u].x) * st[u].y : 0.f);
       }
     }
   }

@@ -20,6 +20,31 @@ __device__ __forceinline__ uint32_t hist_bin(uint32_t key) { return key >> (32 -
 
 enum ScoreMode { kModeGram = 0, kModeKeysum = 1, kModeCut = 2 };
 
+// ReFreeKV energy term of one attention probability a (a square of at most
+// 1): floor(fl32(a*a) * 2^52) as an integer, so that sums are order-free.
+// energy_fixed takes x = fl32(a*a) * 2^20 (exact scaling): with hi = floor(x)
+// and f = x - hi (exact: Sterbenz for x >= 1, f = x below) the term is
+// hi * 2^32 + floor(f * 2^32) (f * 2^32 exact, below 2^32).  Equal to the
+// double-precision product floored, for every float square in [0, 1].
+__device__ __forceinline__ uint64_t energy_fixed(float x) {
+  const uint32_t hi = (uint32_t)x;
+  const float f = x - (float)hi;
+  const uint32_t lo = (uint32_t)(f * 4294967296.0f);
+  return ((uint64_t)hi << 32) | lo;
+}
+// acc += energy_fixed(x), acc held as two 32-bit words (add with carry)
+__device__ __forceinline__ void energy_add(uint32_t& lo_acc, uint32_t& hi_acc, float x) {
+  const uint32_t hi = (uint32_t)x;
+  const float f = x - (float)hi;
+  const uint32_t lo = (uint32_t)(f * 4294967296.0f);
+  uint32_t c;
+  lo_acc = __builtin_addc(lo_acc, lo, 0u, &c);
+  hi_acc = __builtin_addc(hi_acc, hi, c, &c);
+}
+__device__ __forceinline__ uint64_t energy_term(float a) {
+  return energy_fixed(fminf(__fmul_rn(a, a), 1.0f) * 1048576.0f);
+}
+
 struct ScoreParams {
   const char* q;            // [b][Hq][w][d]  (cut: [b][Hq][d], w = 1)
   const char* k;            // [b][Hkv][cap][d]
@@ -40,7 +65,11 @@ struct ScoreParams {
   float* ssum;              // [b][Hkv][d]           keysum: sum of unit keys
   float* inv_norm;          // [b][Hkv][wstride]     gram: 1/||k_j||, 0 past n in its chunk
   int wstride;              // per-head stride of inv_norm: cap rounded up to 512
-  float* logits;            // [b][Hkv][m][nchunk*kChunk]  cut: logits in base-2 units (-inf masked)
+  float* logits;            // nullable [b][Hkv][m][nchunk*kChunk]  cut: logits in base-2 units (-inf masked)
+  // cut mode, energies formed in k_pool from recomputed logits (no logits buffer)
+  uint64_t* energy;         // [b][Hkv][nchunk*kChunk]  integer energy per position
+  uint64_t* ctot;           // [b][Hkv][nchunk]          chunk totals of energy
+  int accum;                // add to the energies of earlier row groups
   int32_t* err;             // error word
   // outputs (never null; the host substitutes workspace buffers)
   float* i_out;             // [b][Hkv][cap]

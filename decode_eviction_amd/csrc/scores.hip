@@ -235,10 +235,11 @@ void k_stats(ScoreParams p) {
 
     if constexpr (MODE == kModeCut) {
       // logits of the m rows in base-2 units (-inf where a row does not see
-      // the key), 4 consecutive tokens per store
+      // the key), 4 consecutive tokens per store; none when k_pool forms the
+      // energies from recomputed logits
       const long ls = (long)p.nchunk * kChunk;
       const int row = 32 * t + l32;
-      if (row < p.m) {
+      if (p.logits && row < p.m) {
         float* lrow = p.logits + (head * p.m + row) * ls;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
@@ -366,7 +367,8 @@ __global__ __launch_bounds__(1024) void k_reduce(ScoreParams p) {
 }
 
 template <typename E, int D, int MT, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT > 1 ? kStatsWaves<E, D> : 1)))
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(MT > 1 && MODE != kModeCut ? kStatsWaves<E, D> : 1)))
 void k_pool(ScoreParams p) {
   using G = Geo<E, D>;
   constexpr int NC = G::kNC;
@@ -379,7 +381,7 @@ void k_pool(ScoreParams p) {
   if (c0 >= n) return;
   const long head = (long)bi * p.hkv + h;
   const char* kb = p.k + head * (long)p.cap * G::kRowBytes;
-  const char* qb = p.q + ((long)bi * p.hq + (long)h * p.g) * p.w * G::kRowBytes;
+  const char* qb = p.q + (((long)bi * p.hq + (long)h * p.g) * p.w + p.rows0) * G::kRowBytes;
 
   __shared__ float2 rs[MT * 32];
   __shared__ uint32_t lh[MODE == kModeKeysum ? kHistBins : 1];
@@ -441,6 +443,89 @@ void k_pool(ScoreParams p) {
   }
 
   const float sc2 = p.scale2;
+  if constexpr (MODE == kModeCut) {
+    // ReFreeKV energies of this row group from recomputed logits (the same
+    // scaled logit k_stats would store, then a = 2^(t - max) / sum), added to
+    // the earlier groups' and totalled per chunk.  Row r of a q head sees
+    // keys j <= n - krows + r.
+    const bool causal = p.krows > 1;
+    const bool full = tok0 + 63 <= (causal ? n - p.krows : n - 1);
+    __shared__ uint64_t wsum[4];
+    // per row: (c, last key the row sees) with
+    //   a^2 * 2^20 = 2^(2 (t - max) + 2 log2(1/sum) + 20) = 2^(acc * 2 sc2 + c),
+    //   c = 20 + 2 log2(1/sum) - 2 max,
+    // the input of energy_fixed (t = acc * sc2 the base-2 logit); c = -inf
+    // for rows past m and rows that see no key (1/sum = 0)
+    __shared__ float2 rsl[MT * 32];
+    if (tid < MT * 32) {
+      const float2 v = tid < p.m ? p.rstat[head * p.mp + tid] : make_float2(0.f, 0.f);
+      const int lim = causal ? n - p.krows + (p.rows0 + tid) % p.krows : n - 1;
+      const float c = v.y > 0.f ? 20.0f + 2.0f * __log2f(v.y) - 2.0f * v.x : -INFINITY;
+      rsl[tid] = make_float2(c, __int_as_float(lim));
+    }
+    const float sc4 = 2.0f * sc2;
+    __syncthreads();
+    // row tiles one at a time (the accumulators of two token tiles live),
+    // each token's terms summed over the rows in e[tt]
+    // per token tile: the energy as low and high 32-bit words
+    uint32_t elo[2] = {0u, 0u}, ehi[2] = {0u, 0u};
+    const int tokA = tok0 + l32, tokB = tokA + 32;
+#pragma unroll 1
+    for (int t = 0; t < MT; ++t) {
+      f32x16_t acc[2] = {zero16(), zero16()};
+      if constexpr (QSt::kLds) {
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+          const u32x4_t qc = QSt::chunk(qs, t, l32, hf, j);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) acc[tt] = mfma_chunk<E>(qc, kf[tt].c[j], acc[tt]);
+        }
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) acc[tt] = mfma_tile<E, NC>(qf[t], kf[tt], acc[tt]);
+      }
+      // row 32t + tile_row(i, hf) for both token tiles (a logit that rounds
+      // an ulp above the row's max gives x just above 2^20: hi still fits)
+      auto rows16 = [&](auto masked) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float2 st = rsl[32 * t + tile_row(i, hf)];
+          float x0 = exp2_fast(fmaf(acc[0][i], sc4, st.x));
+          float x1 = exp2_fast(fmaf(acc[1][i], sc4, st.x));
+          if constexpr (decltype(masked)::value) {
+            const int lim = __float_as_int(st.y);
+            x0 = tokA <= lim ? x0 : 0.f;
+            x1 = tokB <= lim ? x1 : 0.f;
+          }
+          energy_add(elo[0], ehi[0], x0);
+          energy_add(elo[1], ehi[1], x1);
+          // at most four rows' records in flight
+          if (i % 4 == 3) asm volatile("" : "+v"(elo[0]), "+v"(elo[1])::"memory");
+        }
+      };
+      if (full) rows16(std::false_type{});
+      else rows16(std::true_type{});
+    }
+    uint64_t wtot = 0;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tok = tok0 + 32 * tt + l32;
+      const uint64_t e = ((uint64_t)ehi[tt] << 32) | elo[tt];
+      uint64_t et = e + __shfl_xor(e, 32, 64);
+      uint64_t* ep = p.energy + head * (long)p.nchunk * kChunk + tok;
+      if (hf == 0) {
+        if (tok >= n) et = 0;
+        if (p.accum) et += *ep;
+        *ep = et;
+        wtot += et;
+      }
+    }
+    wtot = wave_sum_u64(wtot);
+    if (lane == 0) wsum[wave] = wtot;
+    __syncthreads();
+    if (tid == 0) p.ctot[head * p.nchunk + chunk] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    return;
+  }
   const float inv_m = 1.0f / (float)p.m;
   const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
 #pragma unroll
@@ -531,8 +616,11 @@ hipError_t launch_reduce(int d, int mode, const ScoreParams& p, hipStream_t s, T
 template <typename E, int D, int MT>
 static hipError_t pool_t(int mode, const ScoreParams& p, hipStream_t s, Trace* tr) {
   const dim3 grid(p.nchunk, p.hkv, p.b);
-  if (mode == kModeKeysum) return launch_k(k_pool<E, D, MT, kModeKeysum>, grid, dim3(256), s, tr, p);
-  return launch_k(k_pool<E, D, MT, kModeGram>, grid, dim3(256), s, tr, p);
+  switch (mode) {
+    case kModeKeysum: return launch_k(k_pool<E, D, MT, kModeKeysum>, grid, dim3(256), s, tr, p);
+    case kModeCut: return launch_k(k_pool<E, D, MT, kModeCut>, grid, dim3(256), s, tr, p);
+    default: return launch_k(k_pool<E, D, MT, kModeGram>, grid, dim3(256), s, tr, p);
+  }
 }
 
 template <typename E, int D>

@@ -264,7 +264,12 @@ kvsel_status kvsel_threshold_cut_traced(kvsel_dtype dt, const void* q_last, cons
  * is the sum over the g*k_rows rows of the group of floor(fl32(a*a) * 2^52),
  * then the same walk and cut as kvsel_threshold_cut; k_rows = 1 gives
  * exactly kvsel_threshold_cut.  1 <= k_rows <= cap; the rows are scored in
- * groups of 128, so the cost grows as k_rows * n.  When k_out is non-null,
+ * groups of 128, so the cost grows as k_rows * n.  When a group has at most
+ * 32 rows the scoring pass stores their logits in the workspace and the
+ * energy pass reads them back; larger groups store none, and the energy pass
+ * recomputes the logits from Q and K on the matrix cores (one more read of K
+ * per group) and forms a^2 * 2^20 as a single power of two, so its terms may
+ * differ from the stored-logit form in the last bits of a^2.  When k_out is non-null,
  * k_out/v_out [b][Hkv][cap_out][d] (cap_out >= cap) receive the kept tokens
  * in position order: the min(n_sink, n) sinks, then the newest L - sinks
  * (bit copies); rows from L on are left untouched.  Workspace:

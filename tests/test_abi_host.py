@@ -159,6 +159,9 @@ def test_next_row_entries_reject(lib):
                                         f(), NULL, NULL, 0, f(), 16, NULL) == K.KVSEL_ERR_WORKSPACE
     assert lib.kvsel_cut_compact(BF, f(), f(), f(), NULL, 1, 2, 128, 10, 4, f(), f(), 10,
                                  NULL) == K.KVSEL_ERR_INVALID_ARG
-    assert K.kvsel_threshold_cut_rows_workspace(16, 28, 4, 128, 16384, 64) > \
-        K.kvsel_threshold_cut_workspace(16, 28, 4, 128, 16384)
+    # groups of up to 32 rows store their logits (k = 4: 28 rows); larger
+    # groups recompute them, so the k = 64 workspace holds no logits buffer
+    base = K.kvsel_threshold_cut_workspace(16, 28, 4, 128, 16384)
+    assert K.kvsel_threshold_cut_rows_workspace(16, 28, 4, 128, 16384, 4) > base
+    assert 0 < K.kvsel_threshold_cut_rows_workspace(16, 28, 4, 128, 16384, 64) < base
     assert K.kvsel_threshold_cut_rows_workspace(16, 28, 4, 128, 16384, 0) == 0
