@@ -625,24 +625,28 @@ __global__ __launch_bounds__(256) void k_gram_fin(GramParams p) {
     const int nfull = (nb - 1) / 2;
     const bool opp = nb % 2 == 0 && ns >= 1 && J >= nb / 2;
     const float* pp = p.part + head * (long)p.nsmax * p.cap + j;
-    float tot = p.rs[head * p.cap + j];
-    int s = 0;
-    for (; s + 4 <= nfull; s += 4) {
-      const float a0 = pp[(long)(s + 0) * p.cap], a1 = pp[(long)(s + 1) * p.cap];
-      const float a2 = pp[(long)(s + 2) * p.cap], a3 = pp[(long)(s + 3) * p.cap];
-      tot += a0;
-      tot += a1;
-      tot += a2;
-      tot += a3;
-    }
-    for (; s < nfull; ++s) tot += pp[(long)s * p.cap];
-    if (opp) tot += pp[(long)(ns - 1) * p.cap];
+    const long o = head * p.cap + j;
+    // the loads that do not depend on the slot sum are issued first
     const float w = p.inv_norm[head * (long)p.wstride + j];
+    const float imp = p.i_in[o];
+    const float popp = opp ? pp[(long)(ns - 1) * p.cap] : 0.f;
+    float tot = p.rs[o];
+    // slots in batches of 32, every load of a batch in flight before the
+    // first add; indices past nfull re-read the last slot and add 0, so the
+    // sum is still the slots' in slot order
+    constexpr int SB = 32;
+    for (int s0 = 0; s0 < nfull; s0 += SB) {
+      float a[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) a[u] = pp[(long)min(s0 + u, nfull - 1) * p.cap];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) tot += s0 + u < nfull ? a[u] : 0.f;
+    }
+    if (opp) tot += popp;
     const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
     const float red_j = w * tot * inv_nm1;
-    const long o = head * p.cap + j;
     if (p.r_out) p.r_out[o] = red_j;
-    const float z = p.lambda * p.i_in[o] - (1.0f - p.lambda) * red_j;
+    const float z = p.lambda * imp - (1.0f - p.lambda) * red_j;
     p.z_out[o] = z;
     if (p.hist) atomicAdd(&lh[hist_bin(score_key(z))], 1u);
   }
