@@ -174,11 +174,15 @@ def test_select_stage_exact():
     for n, cap, budget, kind in [(5000, 5000, 700, "ties"), (32768, 32768, 2048, "normal"),
                                  (40000, 40001, 3000, "ties"), (2176, 2176, 2048, "normal"),
                                  (100, 128, 100, "normal"), (1000, 1000, 999, "allequal"),
-                                 (33000, 33000, 1, "normal")]:
+                                 (33000, 33000, 1, "normal"),
+                                 # threshold bins larger than the candidate buffer (8192 keys)
+                                 (32768, 32768, 2048, "allequal"), (32768, 32768, 5000, "few")]:
         if kind == "ties":
             z = (rng.integers(-40, 40, size=(2, 3, cap)) * 2.0 ** -12).astype(np.float32)
         elif kind == "allequal":
             z = np.full((2, 3, cap), 0.25, np.float32)
+        elif kind == "few":
+            z = rng.choice(np.array([0.5, 0.25, 0.125], np.float32), size=(2, 3, cap))
         else:
             z = rng.standard_normal((2, 3, cap)).astype(np.float32) * 1e-3
         z[..., 0] = -0.0

@@ -29,7 +29,8 @@ def _kept(evicted, n):
 
 @pytest.mark.parametrize("n,cap,budget,kind", [
     (2176, 2176, 2048, "ties"), (5000, 5000, 900, "ties"), (32768, 32768, 2048, "normal"),
-    (1500, 2000, 1499, "allequal"), (300, 512, 400, "normal"), (4000, 4096, 1000, "duppos")])
+    (1500, 2000, 1499, "allequal"), (300, 512, 400, "normal"), (4000, 4096, 1000, "duppos"),
+    (32768, 32768, 2048, "allequal")])  # a threshold bin larger than the candidate buffer
 def test_evict_slots_stage_exact(n, cap, budget, kind):
     rng = np.random.default_rng(21)
     hkv = 3
