@@ -424,6 +424,10 @@ static kvsel_status score_evict_impl(kvsel_dtype dt, kvsel_redundancy mode, cons
     sp.v_out = static_cast<char*>(v_out);
     sp.cap_out = cap_out;
     sp.row_bytes = d * (dt == KVSEL_BF16 ? 2 : 4);
+    // about 64 kept rows per gathering work-group: a chunk of kSelChunk
+    // positions keeps about kSelChunk * budget / cap of them
+    const long kept_chunk = ((long)kSelChunk * budget + cap - 1) / cap;
+    sp.gsplit = (int)std::min(8L, std::max(1L, (kept_chunk + 63) / 64));
     KV_TRY(launch_select(sp, stream, tr));
     return KVSEL_OK;
   }

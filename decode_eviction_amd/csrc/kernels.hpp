@@ -114,6 +114,9 @@ struct SelectParams {
   char* k_out;
   char* v_out;
   int cap_out, row_bytes;
+  // work-groups sharing one chunk's gather (>= 1): each takes its share of
+  // the chunk's kept rows; used when most rows are kept
+  int gsplit;
   // per-head budgets (nullable): head h keeps budgets[h] clamped to [0, budget],
   // budget being the row stride of idx and of the compacted cache
   const int32_t* budgets;   // [Hkv]

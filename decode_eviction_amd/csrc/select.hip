@@ -512,13 +512,17 @@ __global__ __launch_bounds__(256) void k_compact(SelectParams p) {
   constexpr int PPT = kSelChunk / 256;  // positions per thread
   __shared__ uint32_t wsum[4];
   __shared__ int32_t rows[kSelChunk];   // kept positions by slot - chunk offset
-  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
+  // gsplit work-groups per chunk: all find the chunk's kept positions, the
+  // first writes them, each gathers its share of the rows
+  const int gs = max(p.gsplit, 1);
+  const int chunk = blockIdx.x / gs, part = blockIdx.x % gs;
+  const int h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
   const int n = min(p.lengths[bi], p.cap);
   const int B = head_budget(p, h);
   const long head = (long)bi * p.hkv + h;
   int32_t* out = p.idx + head * p.budget;
   const int c0 = chunk * kSelChunk;
-  if (chunk == 0)
+  if (chunk == 0 && part == 0)
     for (int t = min(n, B) + tid; t < p.budget; t += 256) out[t] = -1;
   if (c0 >= n || B == 0) return;
   const bool all = n <= B;
@@ -587,19 +591,22 @@ __global__ __launch_bounds__(256) void k_compact(SelectParams p) {
       ++eqbf;
     }
     if (r >= 0 && off + r < (uint32_t)B) {
-      out[off + r] = p0 + e;
+      if (part == 0) out[off + r] = p0 + e;
       rows[r] = p0 + e;
     }
   }
   if (!p.k) return;
   const int kept = (int)((total & 0xffffu) + min(total >> 16, rem));
-  const int nk = min(kept, B - (int)off);
+  const int nkc = min(kept, B - (int)off);
+  // this work-group's share of the chunk's kept rows: [rb, nk)
+  const int share = (nkc + gs - 1) / gs;
+  const int rb = part * share, nk = min(nkc, rb + share);
   __syncthreads();
   // fused gather: row_bytes/16 lanes per row, all loads of a thread issued first
   const int lpr = p.row_bytes / 16, rpi = 256 / lpr;
   const int lr = tid / lpr, lc = tid % lpr;
   constexpr int U = 4;
-  for (int r0 = lr; r0 < nk; r0 += rpi * U) {
+  for (int r0 = rb + lr; r0 < nk; r0 += rpi * U) {
     u32x4_t kv[U], vv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -849,7 +856,7 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s, Trace* tr) {
   if (p.cap <= kSelectLdsKeys) {
     hipError_t e = launch_k(k_select_thresh, dim3(p.hkv, p.b), dim3(kRegThreads), s, tr, p);
     if (e != hipSuccess) return e;
-    return launch_k(k_compact, dim3(p.nsc, p.hkv, p.b), dim3(256), s, tr, p);
+    return launch_k(k_compact, dim3(p.nsc * std::max(p.gsplit, 1), p.hkv, p.b), dim3(256), s, tr, p);
   }
   return launch_k(k_select, dim3(p.hkv, p.b), dim3(kSelectThreads), s, tr, p);
 }
