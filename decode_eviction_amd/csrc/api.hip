@@ -81,7 +81,7 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap) {
   w.inv_norm = c.take<float>(heads * gram_wstride(cap));
   w.imp = c.take<float>(heads * cap);
   w.z = c.take<float>(heads * cap);
-  w.nsmax = ((cap + 255) / 256) / 2;
+  w.nsmax = cap <= kGramPairCap ? (cap + 127) / 128 : ((cap + 255) / 256) / 2;
   w.grs = c.take<float>(heads * cap);
   w.gpart = c.take<float>(heads * (size_t)w.nsmax * cap);
   w.sel.nsc = (cap + kSelChunk - 1) / kSelChunk;

@@ -606,6 +606,127 @@ __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
   }
 }
 
+// Small caches (cap <= kGramPairCap, bf16, d = 128): one work-group per pair
+// of 128-key blocks I <= J, so that even a short cache spreads over many CUs
+// (the sweep kernels give a 2K-token cache only nine work-groups per head).
+// Fragments come straight from global memory (L2-resident at this size).
+// Each wave takes 32 rows of block I and all 128 columns of block J on
+// 16x16x32 tiles.  The tile's w-weighted row sums go to slot J of block I's
+// keys; its w-weighted column sums (I < J) to slot I of block J's keys; so
+// every key ends with one slot per block of the cache, and k_gram_fin adds
+// them in slot order (deterministic) and removes the self term.
+__global__ __launch_bounds__(256) void k_gram_pairs(GramParams p) {
+  constexpr int RB = 256;  // bytes per key (128 bf16)
+  constexpr int BS = 128;  // keys per block
+  const int nbh = (p.cap + BS - 1) / BS;
+  const int h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // pair index -> (I, J): block I owns the pairs J = I .. nbh-1
+  int I = 0, rem = blockIdx.x;
+  while (rem >= nbh - I) {
+    rem -= nbh - I;
+    ++I;
+  }
+  const int J = I + rem;
+  const int n = min(p.lengths[bi], p.cap);
+  if (J * BS >= n) return;
+  const long head = (long)bi * p.hkv + h;
+  const char* kb = p.k + head * (long)p.cap * RB;
+  const float* wv = p.inv_norm + head * (long)p.wstride;
+  float* part = p.part + head * (long)p.nsmax * p.cap;
+
+  // A: rows I*BS + 32 wave + 16 rt + c16; lane chunk g of each 32-dim k-step
+  u32x4_t af[2][4];
+  float wrow[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = I * BS + 32 * wave + 16 * rt + c16;
+    const char* src = kb + (long)(row < n ? row : 0) * RB + g * 16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) af[rt][ks] = row < n ? ld16(src + 64 * ks) : zero4();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = I * BS + 32 * wave + 16 * rt + 4 * g + i;
+      wrow[rt][i] = r < n ? wv[r] : 0.f;
+    }
+  }
+  // block J, copied once into LDS (columns past n read as zeros): chunk q of
+  // column c at slot 16 c + (q xor (c mod 16)), so the 16 lanes reading one
+  // chunk of 16 consecutive columns hit distinct banks
+  __shared__ u32x4_t bs[BS * 16];
+  {
+    const auto rk = buf_rsrc(kb + (long)J * BS * RB, (uint32_t)min(n - J * BS, BS) * RB);
+#pragma unroll
+    for (int u = 0; u < BS * 16 / 256; ++u) {
+      const int sl = 256 * u + tid, c = sl / 16, q = (sl % 16) ^ (c % 16);
+      buf_lds16(rk, bs + 256 * u + (tid & ~63), (uint32_t)c * RB + 16 * q);
+    }
+    // this thread's copies have landed (the compiler waits for exactly
+    // these), then every wave's
+    uint32_t x = 0;
+#pragma unroll
+    for (int u = 0; u < BS * 16 / 256; ++u) x |= reinterpret_cast<const uint32_t*>(bs + 256 * u + tid)[0];
+    asm volatile("" ::"v"(x));
+    __syncthreads();
+  }
+  // C[row][col] over the 8 column tiles of block J; lane holds rows 4g + i
+  // of each row tile at column c16 of each column tile
+  f32x4_t acc[2][8];
+  float wcol[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    const int cl = 16 * ct + c16, col = J * BS + cl;
+    wcol[ct] = col < n ? wv[col] : 0.f;
+    u32x4_t bf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) bf[ks] = bs[cl * 16 + ((4 * ks + g) ^ c16)];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[rt][ks]),
+                                                    __builtin_bit_cast(bf16x8_t, bf[ks]), c, 0, 0, 0);
+      acc[rt][ct] = c;
+    }
+  }
+  // row sums (weights of the columns), summed over the 16 lanes of a row
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) v = fmaf(acc[rt][ct][i], wcol[ct], v);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+      const int r = I * BS + 32 * wave + 16 * rt + 4 * g + i;
+      if (c16 == 0 && r < n) part[(long)J * p.cap + r] = v;
+    }
+  if (I == J) return;
+  // column sums (weights of the rows): over the lane's 8 rows, the 4 lane
+  // groups, then the 4 waves in order
+  __shared__ float colred[4][BS];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    float v = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v = fmaf(acc[rt][ct][i], wrow[rt][i], v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (g == 0) colred[wave][16 * ct + c16] = v;
+  }
+  __syncthreads();
+  if (tid < BS) {
+    const int col = J * BS + tid;
+    const float v = (colred[0][tid] + colred[1][tid]) + (colred[2][tid] + colred[3][tid]);
+    if (col < n) part[(long)I * p.cap + col] = v;
+  }
+}
+
 // R and Z per key: own row sums plus the column sums of the blocks that
 // computed this key's block as their column block, in slot order.
 __global__ __launch_bounds__(256) void k_gram_fin(GramParams p) {
@@ -618,7 +739,31 @@ __global__ __launch_bounds__(256) void k_gram_fin(GramParams p) {
     for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
   __syncthreads();
   const int j = chunk * 256 + tid;
-  if (j < n) {
+  if (p.pairs && j < n) {
+    // one slot per block of the cache, in slot order, then the self term
+    // w_j ||k_j||^2 = 1 / w_j (0 for a zero key) removed
+    const int nb = (n + p.bs - 1) / p.bs;
+    const float* pp = p.part + head * (long)p.nsmax * p.cap + j;
+    const long o = head * p.cap + j;
+    const float w = p.inv_norm[head * (long)p.wstride + j];
+    const float imp = p.i_in[o];
+    float tot = 0.f;
+    constexpr int SB = 32;
+    for (int s0 = 0; s0 < nb; s0 += SB) {
+      float a[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) a[u] = pp[(long)min(s0 + u, nb - 1) * p.cap];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) tot += s0 + u < nb ? a[u] : 0.f;
+    }
+    tot -= w > 0.f ? 1.0f / w : 0.f;
+    const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
+    const float red_j = w * tot * inv_nm1;
+    if (p.r_out) p.r_out[o] = red_j;
+    const float z = p.lambda * imp - (1.0f - p.lambda) * red_j;
+    p.z_out[o] = z;
+    if (p.hist) atomicAdd(&lh[hist_bin(score_key(z))], 1u);
+  } else if (j < n) {
     const int nb = (n + p.bs - 1) / p.bs, J = j / p.bs, ns = nb / 2;
     // slot s holds the contribution of block J - (s+1); the slot of
     // distance nb/2 (nb even) is filled only for J >= nb/2
@@ -669,9 +814,15 @@ static hipError_t gram_t(const GramParams& p, hipStream_t s, Trace* tr) {
 hipError_t launch_gram(int dt, int d, const GramParams& p_in, hipStream_t s, Trace* tr) {
   GramParams p = p_in;
   const bool big = dt == 0 && d == 128 && p.cap >= 8192;
-  p.bs = big ? 512 : 256;
+  const bool small = dt == 0 && d == 128 && p.cap <= kGramPairCap;
+  p.bs = big ? 512 : (small ? 128 : 256);
+  p.pairs = small ? 1 : 0;
   hipError_t e;
   if (big) e = launch_k(k_gram512, dim3((p.cap + 511) / 512 * p.hkv * p.b), dim3(256), s, tr, p);
+  else if (small) {
+    const int nbh = (p.cap + 127) / 128;
+    e = launch_k(k_gram_pairs, dim3(nbh * (nbh + 1) / 2, p.hkv, p.b), dim3(256), s, tr, p);
+  }
   else if (dt == 0) e = d == 64 ? gram_t<BF16, 64>(p, s, tr) : gram_t<BF16, 128>(p, s, tr);
   else e = d == 64 ? gram_t<F32, 64>(p, s, tr) : gram_t<F32, 128>(p, s, tr);
   if (e != hipSuccess) return e;

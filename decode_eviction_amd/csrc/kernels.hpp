@@ -91,9 +91,14 @@ struct GramParams {
   uint32_t* hist;           // nullable [b][Hkv][kHistBins]
   float* rs;                // [b][Hkv][cap]  a key's own-block row sums minus its self term
   float* part;              // [b][Hkv][nsmax][cap]  column sums by block distance - 1
-  int nsmax;                // (ceil(cap / 256)) / 2: slots per head (enough for any block size)
+  int nsmax;                // slots per head: (ceil(cap / 256)) / 2, or ceil(cap / 128) when
+                            // cap <= kGramPairCap (enough for any block size)
   int bs;                   // symmetric block size of the launched Gram kernel (256 or 512)
+  int pairs;                // k_gram_pairs ran: slot s of a key holds its sums against block s
 };
+
+// caches of at most this many positions (bf16, d = 128) use k_gram_pairs
+constexpr int kGramPairCap = 4096;
 
 constexpr int kSelChunk = 512;     // positions per compaction work-group
 
