@@ -317,28 +317,30 @@ __global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
   __shared__ uint32_t cnt[kKeysPerThread][kRegWaves];   // keys above the level-1 bin per (round, wave)
   __shared__ uint32_t ccnt[64][2];                       // candidate (greater, equal) per chunk
   __shared__ uint32_t wsum[2][kRegWaves];
-  __shared__ uint32_t bc[2];
+  __shared__ uint32_t bc[3];
 
   const int h = blockIdx.x, bi = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = min(p.lengths[bi], p.cap);
-  const int B = head_budget(p, h);
   const long head = (long)bi * p.hkv + h;
-  if (tid == 0) flag_select_errors(p, h, bi);
-  if (n <= B || B == 0) return;  // k_compact keeps everything (or nothing)
   const float* z = p.z + head * p.cap;
-
-  // loads through a buffer resource (positions past n read 0): all in flight before use
+  // the histogram and the scores are requested before the length arrives:
+  // scores through a buffer resource over the cache's capacity (positions
+  // past cap read 0, past n are masked below), all in flight before use
+  const uint2 c01 = reinterpret_cast<const uint2*>(p.hist + head * kHistBins)[tid];
   uint32_t key[kKeysPerThread];
   {
-    const __amdgpu_buffer_rsrc_t rz = buf_rsrc(z, (uint32_t)n * 4u);
+    const __amdgpu_buffer_rsrc_t rz = buf_rsrc(z, (uint32_t)p.cap * 4u);
 #pragma unroll
     for (int i = 0; i < kKeysPerThread; ++i) key[i] = buf_ld32(rz, (uint32_t)tid * 4u, (uint32_t)(i * kRegThreads * 4));
   }
+  const int n = min(p.lengths[bi], p.cap);
+  const int B = head_budget(p, h);
+  if (tid == 0) flag_select_errors(p, h, bi);
+  if (n <= B || B == 0) return;  // k_compact keeps everything (or nothing)
 
-  // level 1: the bin (of kHistBins) where the count from the top reaches B
-  const uint32_t c0 = p.hist[head * kHistBins + 2 * tid];
-  const uint32_t c1 = p.hist[head * kHistBins + 2 * tid + 1];
+  // level 1: the bin (of kHistBins) where the count from the top reaches B;
+  // the thread that finds it also records its count
+  const uint32_t c0 = c01.x, c1 = c01.y;
   uint32_t need = (uint32_t)B;
   if (tid < 64) ccnt[tid][0] = ccnt[tid][1] = 0u;
   {
@@ -347,14 +349,16 @@ __global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
     if (above < need && above + c1 >= need) {
       bc[0] = 2 * tid + 1;
       bc[1] = above;
+      bc[2] = c1;
     } else if (above + c1 < need && above + c1 + c0 >= need) {
       bc[0] = 2 * tid;
       bc[1] = above + c1;
+      bc[2] = c0;
     }
     __syncthreads();
   }
   const uint32_t b1 = bc[0];
-  const uint32_t bin_count = p.hist[head * kHistBins + b1];
+  const uint32_t bin_count = bc[2];
   uint32_t lo = b1 << (32 - kHistBits);
   uint32_t hi = lo | ((1u << (32 - kHistBits)) - 1u);
   need -= bc[1];
