@@ -700,9 +700,23 @@ __global__ __launch_bounds__(kRegThreads) void k_evict_slots(SelectParams p) {
   __shared__ uint32_t wtot[2][kRegWaves];
   __shared__ uint32_t bc[2];
   const int h = blockIdx.x, bi = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long head = (long)bi * p.hkv + h;
+  const float* z = p.z + head * p.cap;
+  const int w0 = wave * S * kWave;
+  // the threshold record and the scores are requested before the length
+  // arrives: scores through a buffer resource over the cache's capacity
+  // (slots past cap read 0, past n are masked below), all in flight before use
+  const uint32_t kth = p.thr[head * 4 + 0];
+  const uint32_t need_eq = p.thr[head * 4 + 1];
+  const uint32_t count_eq = p.thr[head * 4 + 2];
+  uint32_t zv[S];
+  {
+    const __amdgpu_buffer_rsrc_t rz = buf_rsrc(z, (uint32_t)p.cap * 4u);
+#pragma unroll
+    for (int i = 0; i < S; ++i) zv[i] = buf_ld32(rz, (uint32_t)(w0 + lane) * 4u, (uint32_t)(kWave * 4 * i));
+  }
   const int n = min(p.lengths[bi], p.cap);
   const int B = head_budget(p, h);
-  const long head = (long)bi * p.hkv + h;
   int32_t* out = p.evict + head * p.evict_stride;
   const int ne = n > B ? n - B : 0;
   if (tid == 0) p.n_evict[head] = ne;
@@ -712,22 +726,12 @@ __global__ __launch_bounds__(kRegThreads) void k_evict_slots(SelectParams p) {
     for (int t = tid; t < n; t += kRegThreads) out[t] = t;
     return;
   }
-  const uint32_t kth = p.thr[head * 4 + 0];
-  const uint32_t need_eq = p.thr[head * 4 + 1];
-  const uint32_t count_eq = p.thr[head * 4 + 2];
   const bool split = need_eq > 0u && need_eq < count_eq;
   const bool keep_eq = need_eq >= count_eq;  // when not split: all tied slots kept, or none
-  const float* z = p.z + head * p.cap;
   const int32_t* ps = p.pos ? p.pos + head * p.cap : nullptr;
-  const int w0 = wave * S * kWave;
-  // key flags; the loads go through a buffer resource (slots past n read 0)
-  // so that all are in flight before use, and only bit masks outlive the loop
+  // key flags: only bit masks outlive the loop
   uint32_t gtm = 0u, eqm = 0u;
   {
-    const __amdgpu_buffer_rsrc_t rz = buf_rsrc(z, (uint32_t)n * 4u);
-    uint32_t zv[S];
-#pragma unroll
-    for (int i = 0; i < S; ++i) zv[i] = buf_ld32(rz, (uint32_t)(w0 + lane) * 4u, (uint32_t)(kWave * 4 * i));
 #pragma unroll
     for (int i = 0; i < S; ++i) {
       const bool ok = w0 + kWave * i + lane < n;
