@@ -68,9 +68,10 @@ def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int =
     kb = tok * d * 2
     gath = 2 * 2 * b * hkv * min(budget, n) * d * 2
     cost = {
-        "stats": {"bytes": kb + (4 * tok if mode == "gram" else 0)},
+        "stats": {"bytes": kb},
         "reduce": {"bytes": 0},
-        "pool": {"bytes": kb + (4 * tok if mode == "gram" else 8 * tok)},
+        # Gram form: I and the key weights 1/||k||; key-sum form: I and Z
+        "pool": {"bytes": kb + 8 * tok},
         "thresh": {"bytes": 4 * tok},
         "compact": {"bytes": 4 * tok + 4 * b * hkv * budget + gath},
     }

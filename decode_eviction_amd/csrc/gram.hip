@@ -728,72 +728,85 @@ __global__ __launch_bounds__(256) void k_gram_pairs(GramParams p) {
 }
 
 // R and Z per key: own row sums plus the column sums of the blocks that
-// computed this key's block as their column block, in slot order.
+// computed this key's block as their column block, in slot order.  A thread
+// takes V consecutive keys (one block, as V divides the block size) with
+// V-wide loads of every slot; V = 4 needs cap % 4 == 0 for aligned rows.
+template <int V>
 __global__ __launch_bounds__(256) void k_gram_fin(GramParams p) {
+  typedef float fv_t __attribute__((ext_vector_type(V)));
   __shared__ uint32_t lh[kHistBins];
   const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
   const int n = min(p.lengths[bi], p.cap);
-  if (chunk * 256 >= n) return;
+  if (chunk * 256 * V >= n) return;
   const long head = (long)bi * p.hkv + h;
   if (p.hist)
     for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
   __syncthreads();
-  const int j = chunk * 256 + tid;
-  if (p.pairs && j < n) {
-    // one slot per block of the cache, in slot order, then the self term
-    // w_j ||k_j||^2 = 1 / w_j (0 for a zero key) removed
-    const int nb = (n + p.bs - 1) / p.bs;
-    const float* pp = p.part + head * (long)p.nsmax * p.cap + j;
-    const long o = head * p.cap + j;
-    const float w = p.inv_norm[head * (long)p.wstride + j];
-    const float imp = p.i_in[o];
-    float tot = 0.f;
-    constexpr int SB = 32;
-    for (int s0 = 0; s0 < nb; s0 += SB) {
-      float a[SB];
-#pragma unroll
-      for (int u = 0; u < SB; ++u) a[u] = pp[(long)min(s0 + u, nb - 1) * p.cap];
-#pragma unroll
-      for (int u = 0; u < SB; ++u) tot += s0 + u < nb ? a[u] : 0.f;
-    }
-    tot -= w > 0.f ? 1.0f / w : 0.f;
-    const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
-    const float red_j = w * tot * inv_nm1;
-    if (p.r_out) p.r_out[o] = red_j;
-    const float z = p.lambda * imp - (1.0f - p.lambda) * red_j;
-    p.z_out[o] = z;
-    if (p.hist) atomicAdd(&lh[hist_bin(score_key(z))], 1u);
-  } else if (j < n) {
+  const int j = (chunk * 256 + tid) * V;
+  if (j < n) {
     const int nb = (n + p.bs - 1) / p.bs, J = j / p.bs, ns = nb / 2;
-    // slot s holds the contribution of block J - (s+1); the slot of
-    // distance nb/2 (nb even) is filled only for J >= nb/2
-    const int nfull = (nb - 1) / 2;
-    const bool opp = nb % 2 == 0 && ns >= 1 && J >= nb / 2;
     const float* pp = p.part + head * (long)p.nsmax * p.cap + j;
     const long o = head * p.cap + j;
+    auto ld = [](const float* q) { return *reinterpret_cast<const fv_t*>(q); };
     // the loads that do not depend on the slot sum are issued first
-    const float w = p.inv_norm[head * (long)p.wstride + j];
-    const float imp = p.i_in[o];
-    const float popp = opp ? pp[(long)(ns - 1) * p.cap] : 0.f;
-    float tot = p.rs[o];
-    // slots in batches of 32, every load of a batch in flight before the
-    // first add; indices past nfull re-read the last slot and add 0, so the
-    // sum is still the slots' in slot order
-    constexpr int SB = 32;
-    for (int s0 = 0; s0 < nfull; s0 += SB) {
-      float a[SB];
-#pragma unroll
-      for (int u = 0; u < SB; ++u) a[u] = pp[(long)min(s0 + u, nfull - 1) * p.cap];
-#pragma unroll
-      for (int u = 0; u < SB; ++u) tot += s0 + u < nfull ? a[u] : 0.f;
+    const fv_t w = ld(p.inv_norm + head * (long)p.wstride + j);
+    const fv_t imp = ld(p.i_in + o);
+    fv_t tot;
+    int ntake;
+    if (p.pairs) {
+      // one slot per block of the cache, in slot order (the self term is
+      // removed below)
+      for (int e = 0; e < V; ++e) tot[e] = 0.f;
+      ntake = nb;
+    } else {
+      // slot s holds the contribution of block J - (s+1); the slot of
+      // distance nb/2 (nb even) is filled only for J >= nb/2
+      tot = ld(p.rs + o);
+      ntake = (nb - 1) / 2;
     }
-    if (opp) tot += popp;
+    const bool opp = !p.pairs && nb % 2 == 0 && ns >= 1 && J >= nb / 2;
+    fv_t popp;
+    for (int e = 0; e < V; ++e) popp[e] = 0.f;
+    if (opp) popp = ld(pp + (long)(ns - 1) * p.cap);
+    // slots in batches, every load of a batch in flight before the first
+    // add; indices past the last slot re-read it and add 0, so the sum is
+    // still the slots' in slot order
+    constexpr int SB = 32;
+    for (int s0 = 0; s0 < ntake; s0 += SB) {
+      fv_t a[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) a[u] = ld(pp + (long)min(s0 + u, ntake - 1) * p.cap);
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const bool in = s0 + u < ntake;
+#pragma unroll
+        for (int e = 0; e < V; ++e) tot[e] += in ? a[u][e] : 0.f;
+      }
+    }
     const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
-    const float red_j = w * tot * inv_nm1;
-    if (p.r_out) p.r_out[o] = red_j;
-    const float z = p.lambda * imp - (1.0f - p.lambda) * red_j;
-    p.z_out[o] = z;
-    if (p.hist) atomicAdd(&lh[hist_bin(score_key(z))], 1u);
+    fv_t red, z;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      float t = tot[e];
+      if (opp) t += popp[e];
+      // pairs: the self term w_j ||k_j||^2 = 1 / w_j (0 for a zero key)
+      if (p.pairs) t -= w[e] > 0.f ? 1.0f / w[e] : 0.f;
+      red[e] = w[e] * t * inv_nm1;
+      z[e] = p.lambda * imp[e] - (1.0f - p.lambda) * red[e];
+    }
+    if (j + V <= n) {
+      if (p.r_out) *reinterpret_cast<fv_t*>(p.r_out + o) = red;
+      *reinterpret_cast<fv_t*>(p.z_out + o) = z;
+    } else {
+      for (int e = 0; e < V && j + e < n; ++e) {
+        if (p.r_out) p.r_out[o + e] = red[e];
+        p.z_out[o + e] = z[e];
+      }
+    }
+    if (p.hist)
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (j + e < n) atomicAdd(&lh[hist_bin(score_key(z[e]))], 1u);
   }
   if (p.hist) {
     __syncthreads();
@@ -826,7 +839,11 @@ hipError_t launch_gram(int dt, int d, const GramParams& p_in, hipStream_t s, Tra
   else if (dt == 0) e = d == 64 ? gram_t<BF16, 64>(p, s, tr) : gram_t<BF16, 128>(p, s, tr);
   else e = d == 64 ? gram_t<F32, 64>(p, s, tr) : gram_t<F32, 128>(p, s, tr);
   if (e != hipSuccess) return e;
-  return launch_k(k_gram_fin, dim3((p.cap + 255) / 256, p.hkv, p.b), dim3(256), s, tr, p);
+  auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+  if (p.cap % 4 == 0 && al16(p.part) && al16(p.rs) && al16(p.inv_norm) && al16(p.i_in) &&
+      al16(p.z_out) && al16(p.r_out))
+    return launch_k(k_gram_fin<4>, dim3((p.cap + 1023) / 1024, p.hkv, p.b), dim3(256), s, tr, p);
+  return launch_k(k_gram_fin<1>, dim3((p.cap + 255) / 256, p.hkv, p.b), dim3(256), s, tr, p);
 }
 
 }  // namespace kvsel

@@ -7,12 +7,13 @@
 // rows.  The softmax needs each row's global max and sum of exponentials, so
 // K is streamed twice:
 //   k_stats  per 256-token chunk: logits on the matrix cores, per-row chunk
-//            max / sum-exp, key norms (and, key-sum mode, the chunk's sum of
+//            max / sum-exp (key-sum mode: key norms and the chunk's sum of
 //            unit keys); ReFreeKV mode also stores the scaled logits;
 //   k_reduce per head: merges chunk partials (online-softmax merge) and the
 //            unit-key sums;
 //   k_pool   per 256-token chunk: logits again, p = exp(s - max) / sum,
-//            I[j] = mean over rows; key-sum mode adds
+//            I[j] = mean over rows; Gram mode writes the key weights
+//            1/||k_j||; key-sum mode adds
 //            R[j] = (u_j.S - u_j.u_j) / (n-1),  S = sum_i u_i, u = k/||k||
 //            and Z[j] = lambda I[j] - (1-lambda) R[j].
 //
@@ -144,21 +145,18 @@ void k_stats(ScoreParams p) {
     load_frag<E, D>(kf[tt], kb, tok, tok < n, hf);
   }
 
-  // key norms (and, key-sum mode, the chunk's unit-key sum)
+  // key-sum mode: key norms and the chunk's unit-key sum (the Gram form's
+  // norms are taken in k_pool, which reads K from the last-level cache)
   auto norms = [&]() {
-    if constexpr (MODE != kModeCut) {
+    if constexpr (MODE == kModeKeysum) {
       float inv[2];
   #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         float ss = frag_sumsq<E, NC>(kf[tt]);
         ss += xor32(ss);
         inv[tt] = inv_norm_of(ss);
-        const int tok = tok0 + 32 * tt + l32;
-        // every slot of the chunk is written (0 past n): the Gram kernel streams
-        // whole 128-key blocks of weights
-        if (MODE == kModeGram && hf == 0) p.inv_norm[head * (long)p.wstride + tok] = inv[tt];
       }
-      if constexpr (MODE == kModeKeysum) {
+      {
         // this chunk's sum of unit keys: per lane its two tokens, then a
         // reduce-scatter over the 32 lanes of the half, then across waves
         // (the first reduce-scatter step is taken as the values are formed, so
@@ -424,6 +422,16 @@ void k_pool(ScoreParams p) {
   // each tile), taken before the attention products so that the unpacked
   // key values are not live across them
   float dots[2] = {0.f, 0.f}, sqs[2] = {0.f, 0.f};
+  if constexpr (MODE == kModeGram) {
+    // 1/||k_j|| for the Gram kernel; every slot of the chunk is written (0
+    // past n), as it streams whole 128-key blocks of weights
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float ss = frag_sumsq<E, NC>(kf[tt]);
+      ss += xor32(ss);
+      if (hf == 0) p.inv_norm[head * (long)p.wstride + tok0 + 32 * tt + l32] = inv_norm_of(ss);
+    }
+  }
   if constexpr (MODE == kModeKeysum) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) sqs[tt] = frag_sumsq<E, NC>(kf[tt]);

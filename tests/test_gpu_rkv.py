@@ -100,6 +100,16 @@ def test_ragged_batch_bf16(mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("cap,lengths", [(1031, [1031, 500, 1001]), (5003, [5003, 4100, 4099])])
+def test_cap_not_multiple_of_4(mode, cap, lengths):
+    # rows of the per-key score buffers lose 16-byte alignment: the scalar
+    # finishing pass of the Gram form (pair kernel below 4097, 256-key blocks above)
+    case = synth.rkv_case("oddcap", seed=11, wl=95, b=3, hq=8, hkv=2, d=128, w=4,
+                          lengths=lengths, cap=cap, budget=300)
+    check_case(case, mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("hq,hkv,w", [(4, 4, 2), (16, 2, 8), (32, 2, 8)])
 def test_d64_row_tiles(mode, hq, hkv, w):
     case = synth.rkv_case("d64", seed=4, wl=98, b=2, hq=hq, hkv=hkv, d=64, w=w,
