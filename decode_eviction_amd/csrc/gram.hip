@@ -736,49 +736,71 @@ __global__ __launch_bounds__(256) void k_gram_fin(GramParams p) {
   typedef float fv_t __attribute__((ext_vector_type(V)));
   __shared__ uint32_t lh[kHistBins];
   const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
-  const int n = min(p.lengths[bi], p.cap);
-  if (chunk * 256 * V >= n) return;
   const long head = (long)bi * p.hkv + h;
+  const int j = (chunk * 256 + tid) * V;
+  // Everything but the slots past the first batch is requested before the
+  // length arrives: the key's weights, importance and own-block row sums and
+  // its first slots, as many as a full cache gives the work-group's last
+  // block (the count for n = cap; a shorter sequence needs at most as many;
+  // uniform over the work-group, so the slot offsets stay scalar), clamped
+  // to SB.
+  const int jl = min(j, p.cap - V);
+  const int nbc = (p.cap + p.bs - 1) / p.bs;
+  const int Jw = min((chunk * 256 + 255) * V, p.cap - 1) / p.bs;
+  const int ntc = p.pairs ? nbc : (nbc - 1) / 2 + (nbc % 2 == 0 && nbc >= 2 && Jw >= nbc / 2 ? 1 : 0);
+  const float* pp = p.part + head * (long)p.nsmax * p.cap + jl;
+  const long ol = head * p.cap + jl;
+  auto ld = [](const float* q) { return *reinterpret_cast<const fv_t*>(q); };
+  const fv_t w = ld(p.inv_norm + head * (long)p.wstride + jl);
+  const fv_t imp = ld(p.i_in + ol);
+  fv_t tot;
+  if (p.pairs) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) tot[e] = 0.f;
+  } else {
+    tot = ld(p.rs + ol);
+  }
+  constexpr int SB = 32;
+  fv_t a[SB];
+  if constexpr (V == 4) {
+    // buffer loads: one per-lane offset, the slot row as a scalar offset (the
+    // launcher keeps a head's slots below 2^31 bytes for this form)
+    const auto pr = buf_rsrc(p.part + head * (long)p.nsmax * p.cap, (uint32_t)p.nsmax * p.cap * 4u);
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+      a[u] = __builtin_bit_cast(fv_t, buf_ld128(pr, (uint32_t)jl * 4u, (uint32_t)min(u, max(ntc, 1) - 1) * p.cap * 4u));
+  } else {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) a[u] = ld(pp + (long)min(u, max(ntc, 1) - 1) * p.cap);
+  }
+  const int n = min(p.lengths[bi], p.cap);
+  // pairs: one slot per block of the cache.  Otherwise slot s holds the
+  // contribution of block J - (s+1) for s < (nb-1)/2, and the slot of
+  // distance nb/2 (nb even, filled only for J >= nb/2) is the next one,
+  // (nb-1)/2: either way the key's slots are a prefix, added in slot order.
+  // The first batch is added before anything branches on n, which keeps its
+  // loads ahead of the length's.
+  const int nb = (n + p.bs - 1) / p.bs, J = jl / p.bs;
+  const int nt = p.pairs ? nb : (nb - 1) / 2 + (nb % 2 == 0 && nb >= 2 && J >= nb / 2 ? 1 : 0);
+#pragma unroll
+  for (int u = 0; u < SB; ++u) {
+    const bool in = u < nt;
+#pragma unroll
+    for (int e = 0; e < V; ++e) tot[e] += in ? a[u][e] : 0.f;
+  }
+  if (chunk * 256 * V >= n) return;
   if (p.hist)
     for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
   __syncthreads();
-  const int j = (chunk * 256 + tid) * V;
   if (j < n) {
-    const int nb = (n + p.bs - 1) / p.bs, J = j / p.bs, ns = nb / 2;
-    const float* pp = p.part + head * (long)p.nsmax * p.cap + j;
-    const long o = head * p.cap + j;
-    auto ld = [](const float* q) { return *reinterpret_cast<const fv_t*>(q); };
-    // the loads that do not depend on the slot sum are issued first
-    const fv_t w = ld(p.inv_norm + head * (long)p.wstride + j);
-    const fv_t imp = ld(p.i_in + o);
-    fv_t tot;
-    int ntake;
-    if (p.pairs) {
-      // one slot per block of the cache, in slot order (the self term is
-      // removed below)
-      for (int e = 0; e < V; ++e) tot[e] = 0.f;
-      ntake = nb;
-    } else {
-      // slot s holds the contribution of block J - (s+1); the slot of
-      // distance nb/2 (nb even) is filled only for J >= nb/2
-      tot = ld(p.rs + o);
-      ntake = (nb - 1) / 2;
-    }
-    const bool opp = !p.pairs && nb % 2 == 0 && ns >= 1 && J >= nb / 2;
-    fv_t popp;
-    for (int e = 0; e < V; ++e) popp[e] = 0.f;
-    if (opp) popp = ld(pp + (long)(ns - 1) * p.cap);
-    // slots in batches, every load of a batch in flight before the first
-    // add; indices past the last slot re-read it and add 0, so the sum is
-    // still the slots' in slot order
-    constexpr int SB = 32;
-    for (int s0 = 0; s0 < ntake; s0 += SB) {
-      fv_t a[SB];
+    // later batches (more than SB slots: caches beyond 32K keys); indices
+    // past the last slot re-read it and add 0
+    for (int s0 = SB; s0 < nt; s0 += SB) {
 #pragma unroll
-      for (int u = 0; u < SB; ++u) a[u] = ld(pp + (long)min(s0 + u, ntake - 1) * p.cap);
+      for (int u = 0; u < SB; ++u) a[u] = ld(pp + (long)min(s0 + u, nt - 1) * p.cap);
 #pragma unroll
       for (int u = 0; u < SB; ++u) {
-        const bool in = s0 + u < ntake;
+        const bool in = s0 + u < nt;
 #pragma unroll
         for (int e = 0; e < V; ++e) tot[e] += in ? a[u][e] : 0.f;
       }
@@ -788,12 +810,12 @@ __global__ __launch_bounds__(256) void k_gram_fin(GramParams p) {
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       float t = tot[e];
-      if (opp) t += popp[e];
       // pairs: the self term w_j ||k_j||^2 = 1 / w_j (0 for a zero key)
       if (p.pairs) t -= w[e] > 0.f ? 1.0f / w[e] : 0.f;
       red[e] = w[e] * t * inv_nm1;
       z[e] = p.lambda * imp[e] - (1.0f - p.lambda) * red[e];
     }
+    const long o = head * p.cap + j;
     if (j + V <= n) {
       if (p.r_out) *reinterpret_cast<fv_t*>(p.r_out + o) = red;
       *reinterpret_cast<fv_t*>(p.z_out + o) = z;
@@ -840,8 +862,8 @@ hipError_t launch_gram(int dt, int d, const GramParams& p_in, hipStream_t s, Tra
   else e = d == 64 ? gram_t<F32, 64>(p, s, tr) : gram_t<F32, 128>(p, s, tr);
   if (e != hipSuccess) return e;
   auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
-  if (p.cap % 4 == 0 && al16(p.part) && al16(p.rs) && al16(p.inv_norm) && al16(p.i_in) &&
-      al16(p.z_out) && al16(p.r_out))
+  if (p.cap % 4 == 0 && (long)p.nsmax * p.cap * 4 < (1L << 31) && al16(p.part) && al16(p.rs) &&
+      al16(p.inv_norm) && al16(p.i_in) && al16(p.z_out) && al16(p.r_out))
     return launch_k(k_gram_fin<4>, dim3((p.cap + 1023) / 1024, p.hkv, p.b), dim3(256), s, tr, p);
   return launch_k(k_gram_fin<1>, dim3((p.cap + 255) / 256, p.hkv, p.b), dim3(256), s, tr, p);
 }

@@ -521,32 +521,38 @@ __global__ __launch_bounds__(256) void k_compact(SelectParams p) {
   const int gs = max(p.gsplit, 1);
   const int chunk = blockIdx.x / gs, part = blockIdx.x % gs;
   const int h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
-  const int n = min(p.lengths[bi], p.cap);
-  const int B = head_budget(p, h);
   const long head = (long)bi * p.hkv + h;
-  int32_t* out = p.idx + head * p.budget;
   const int c0 = chunk * kSelChunk;
+  const int p0 = c0 + tid * PPT;
+  // the threshold record, the chunk's offsets and its scores are requested
+  // before the length arrives (none depends on it; positions are clamped to
+  // the cache, and the record is ignored when everything is kept)
+  uint32_t kth = p.thr[head * 4 + 0], need_eq = p.thr[head * 4 + 1];
+  uint32_t off = p.coff[head * p.nsc + chunk], eqb = p.ceqb[head * p.nsc + chunk];
+  const float* z = p.z + head * p.cap;
+  float zv[PPT];
+#pragma unroll
+  for (int e = 0; e < PPT; ++e) zv[e] = z[min(p0 + e, p.cap - 1)];
+  const int len = p.lengths[bi];
+  const int B = head_budget(p, h);
+  // one wait for all of these loads (the compiler would otherwise request the
+  // record only after the length and budget have arrived)
+  asm volatile("" ::"s"(kth), "s"(need_eq), "s"(off), "s"(eqb), "s"(len), "s"(B));
+  const int n = min(len, p.cap);
+  int32_t* out = p.idx + head * p.budget;
   if (chunk == 0 && part == 0)
     for (int t = min(n, B) + tid; t < p.budget; t += 256) out[t] = -1;
   if (c0 >= n || B == 0) return;
   const bool all = n <= B;
-  uint32_t kth = 0, need_eq = 0, off = 0, eqb = 0;
-  if (!all) {
-    kth = p.thr[head * 4 + 0];
-    need_eq = p.thr[head * 4 + 1];
-    off = p.coff[head * p.nsc + chunk];
-    eqb = p.ceqb[head * p.nsc + chunk];
-  } else {
+  if (all) {
+    kth = 0;
+    need_eq = 0;
     off = c0;
+    eqb = 0;
   }
-  const float* z = p.z + head * p.cap;
-  const int p0 = c0 + tid * PPT;
   bool gt[PPT], eq[PPT];
   uint32_t cg = 0, ce = 0;
   if (!all) {
-    float zv[PPT];
-#pragma unroll
-    for (int e = 0; e < PPT; ++e) zv[e] = z[min(p0 + e, n - 1)];
 #pragma unroll
     for (int e = 0; e < PPT; ++e) {
       const bool ok = p0 + e < n;
