@@ -597,7 +597,6 @@ static CutParams cut_params(const CutWs& ws, const int32_t* lengths, int b, int 
   c.mp = rows_padded(c.g);
   c.cap = cap;
   c.nchunk = (cap + kChunk - 1) / kChunk;
-  c.lstride = c.nchunk * kChunk;
   c.n_sink = n_sink;
   c.rows = c.g;
   c.accum = 0;

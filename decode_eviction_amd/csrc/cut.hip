@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void k_cut_energy(CutParams p) {
       // 8 rows at a time, their loads issued before use; a row that sees no
       // key (sum 0) has no attention mass
       constexpr int U = 8;
-      const float* lg = p.logits + head * p.rows * (long)p.lstride + tok;
+      const float* lg = p.logits + (head * p.nchunk + chunk) * p.rows * (long)kChunk + tid;
       const float2* rs = p.rstat + head * p.mp;
       for (int q0 = 0; q0 < p.rows; q0 += U) {
         float t[U];
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void k_cut_energy(CutParams p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int q = min(q0 + u, p.rows - 1);
-          t[u] = lg[q * (long)p.lstride];
+          t[u] = lg[q * kChunk];
           st[u] = rs[q];
         }
 #pragma unroll

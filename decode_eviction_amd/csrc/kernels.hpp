@@ -65,7 +65,7 @@ struct ScoreParams {
   float* ssum;              // [b][Hkv][d]           keysum: sum of unit keys
   float* inv_norm;          // [b][Hkv][wstride]     gram: 1/||k_j||, 0 past n in its chunk
   int wstride;              // per-head stride of inv_norm: cap rounded up to 512
-  float* logits;            // nullable [b][Hkv][m][nchunk*kChunk]  cut: logits in base-2 units (-inf masked)
+  float* logits;            // nullable [b][Hkv][nchunk][m][kChunk]  cut: logits in base-2 units (-inf masked)
   // cut mode, energies formed in k_pool from recomputed logits (no logits buffer)
   uint64_t* energy;         // [b][Hkv][nchunk*kChunk]  integer energy per position
   uint64_t* ctot;           // [b][Hkv][nchunk]          chunk totals of energy
@@ -156,11 +156,11 @@ struct GatherParams {
 };
 
 struct CutParams {
-  const float* logits;      // [b][Hkv][rows][lstride] (or null with attn)
+  const float* logits;      // [b][Hkv][nchunk][rows][kChunk] (or null with attn)
   const float* attn;        // [b][Hq][cap]           stage entry (or null)
   const float2* rstat;      // [b][Hkv][mp]
   const int32_t* lengths;
-  int b, hq, hkv, g, mp, cap, nchunk, lstride, n_sink;
+  int b, hq, hkv, g, mp, cap, nchunk, n_sink;
   int rows;                 // attention rows per KV head in this launch (g for one last row)
   int accum;                // add to the energies of earlier row groups
   float T;

@@ -235,10 +235,11 @@ void k_stats(ScoreParams p) {
       // logits of the m rows in base-2 units (-inf where a row does not see
       // the key), 4 consecutive tokens per store; none when k_pool forms the
       // energies from recomputed logits
-      const long ls = (long)p.nchunk * kChunk;
+      // chunk-major ([head][chunk][row][token]): a work-group's logits are
+      // one contiguous block
       const int row = 32 * t + l32;
       if (p.logits && row < p.m) {
-        float* lrow = p.logits + (head * p.m + row) * ls;
+        float* lrow = p.logits + ((head * p.nchunk + chunk) * p.m + row) * (long)kChunk;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -247,7 +248,7 @@ void k_stats(ScoreParams p) {
             f32x4_t v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = full || 32 * tt + 8 * q4 + e <= rel ? a[tt][4 * q4 + e] * sc2 : -INFINITY;
-            *reinterpret_cast<f32x4_t*>(lrow + tb) = v;
+            *reinterpret_cast<f32x4_t*>(lrow + (tb - c0)) = v;
           }
       }
     }

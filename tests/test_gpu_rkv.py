@@ -168,6 +168,18 @@ def test_large_cap_ragged_lengths(mode):
     check_case(case, mode, form="keysum", sample_rows=24)
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_many_chunks_ragged(mode):
+    # 2048 chunks of 256 keys in the call: the statistics pass gives each
+    # work-group two consecutive chunks of a head; lengths end inside a chunk,
+    # on a chunk boundary, inside a work-group's first chunk and at 1
+    case = synth.rkv_case("manychunks", seed=17, wl=91, b=8, hq=8, hkv=4, d=128, w=4,
+                          lengths=[16384, 9000, 300, 16000, 12345, 1, 8192, 4097],
+                          cap=16384, budget=500)
+    check_case(case, mode, form="keysum", heads=[(0, 0), (1, 3), (2, 1), (4, 2), (5, 0), (6, 3), (7, 1)],
+               sample_rows=8)
+
+
 @pytest.mark.parametrize("mode", ["keysum", "gram"])
 def test_batched_64x8192_sampled(mode):
     case = synth.batched_case(0)
