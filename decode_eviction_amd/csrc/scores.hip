@@ -101,8 +101,12 @@ struct QStage {
 template <typename E, int D>
 constexpr int kStatsWaves = E::kBytes == 2 || D == 64 ? 4 : 1;
 
+// The ReFreeKV single-tile form (bf16, d = 128) fits five.
 template <typename E, int D, int MT, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kStatsWaves<E, D>)))
+constexpr int kStatsWavesFor = MODE == kModeCut && MT == 1 && E::kBytes == 2 && D == 128 ? 5 : kStatsWaves<E, D>;
+
+template <typename E, int D, int MT, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kStatsWavesFor<E, D, MT, MODE>)))
 void k_stats(ScoreParams p) {
   using G = Geo<E, D>;
   constexpr int NC = G::kNC;
@@ -200,6 +204,11 @@ void k_stats(ScoreParams p) {
   const bool full = tok0 + 63 <= (causal ? n - p.krows : n - 1);
   const float sc2 = p.scale2;
   __shared__ float2 wst[4][MT * 32];
+  // cut mode, one row tile: the chunk's logits of up to kLgRows rows, rows
+  // padded by 4 words so that the 16-byte writes of different rows spread
+  // over the banks
+  constexpr int kLgRows = 8, kLgStride = kChunk + 4;
+  __shared__ __attribute__((aligned(16))) float lgs[MODE == kModeCut && MT == 1 ? kLgRows * kLgStride : 4];
   // row tile t from its two accumulator tiles C[token][row] (lane: query row
   // 32t + l32, tokens tile_row(i, hf) of each key tile)
   auto row_tile = [&](int t, const f32x16_t (&a)[2]) {
@@ -236,19 +245,23 @@ void k_stats(ScoreParams p) {
       // the key), 4 consecutive tokens per store; none when k_pool forms the
       // energies from recomputed logits
       // chunk-major ([head][chunk][row][token]): a work-group's logits are
-      // one contiguous block
+      // one contiguous block.  Up to kLgRows rows go through LDS and are
+      // written out whole after the barrier (a lane here holds 4 consecutive
+      // tokens of one row: direct stores are 32-byte pieces of many lines)
       const int row = 32 * t + l32;
       if (p.logits && row < p.m) {
+        const bool staged = MT == 1 && p.m <= kLgRows;
         float* lrow = p.logits + ((head * p.nchunk + chunk) * p.m + row) * (long)kChunk;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const int tb = tok0 + 32 * tt + 8 * q4 + 4 * hf;
+            const int tr = wave * 64 + 32 * tt + 8 * q4 + 4 * hf;  // token within the chunk
             f32x4_t v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = full || 32 * tt + 8 * q4 + e <= rel ? a[tt][4 * q4 + e] * sc2 : -INFINITY;
-            *reinterpret_cast<f32x4_t*>(lrow + (tb - c0)) = v;
+            if (staged) *reinterpret_cast<f32x4_t*>(&lgs[row * kLgStride + tr]) = v;
+            else *reinterpret_cast<f32x4_t*>(lrow + tr) = v;
           }
       }
     }
@@ -303,6 +316,16 @@ void k_stats(ScoreParams p) {
 #pragma unroll
     for (int wv = 0; wv < 4; ++wv) softmax_merge(m, s, wst[wv][tid].x, wst[wv][tid].y);
     p.cstat[(head * p.nchunk + chunk) * p.mp + tid] = make_float2(m, s);
+  }
+  if constexpr (MODE == kModeCut && MT == 1) {
+    // the staged logits: m rows of 256 tokens, contiguous in global memory
+    if (p.logits && p.m <= kLgRows) {
+      float* blk = p.logits + (head * p.nchunk + chunk) * p.m * (long)kChunk;
+      for (int i = 4 * tid; i < p.m * kChunk; i += 4 * 256) {
+        const int r = i / kChunk, c = i % kChunk;
+        *reinterpret_cast<f32x4_t*>(blk + i) = *reinterpret_cast<const f32x4_t*>(&lgs[r * kLgStride + c]);
+      }
+    }
   }
 }
 
