@@ -58,6 +58,16 @@ KERNELS = {
 }
 
 
+def rkv_kernels(mode: str, cap: int) -> list:
+    """Kernels one R-KV call launches, in order: with at most 16 chunks of 256
+    keys per head k_pool merges the chunk partials itself and k_reduce is not
+    launched."""
+    ks = list(KERNELS[mode])
+    if -(-cap // 256) <= 16:
+        ks.remove("reduce")
+    return ks
+
+
 def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int = HKV,
              d: int = D) -> dict:
     """Bytes (and flops) each R-KV kernel must move per call.
@@ -210,8 +220,8 @@ def rkv_caller(mode, layers, b, n, budget, out_bufs=None, budgets=None):
     from decode_eviction_amd import kvsel as K
     lib = K.lib()
     mcode = K.MODES[mode]
-    nk = len(KERNELS[mode])
     q0, k0, _ = layers[0]
+    nk = len(rkv_kernels(mode, k0.shape[2]))
     hq, w = q0.shape[1], q0.shape[2]
     hkv, cap = k0.shape[1], k0.shape[2]
     lens = torch.full((b,), n, dtype=torch.int32, device="cuda")
@@ -247,7 +257,7 @@ def rkv_caller(mode, layers, b, n, budget, out_bufs=None, budgets=None):
 
 def run_mode(mode, layers, steps, warmup, hip):
     call, keep = rkv_caller(mode, layers, 1, N, BUDGET)
-    return time_calls(call, KERNELS[mode], rkv_cost(mode), steps, warmup, hip)
+    return time_calls(call, rkv_kernels(mode, N), rkv_cost(mode), steps, warmup, hip)
 
 
 # an uneven per-head allocation with the same total as B=2048 per head
@@ -260,7 +270,7 @@ def run_heads(mode, layers, steps, warmup, hip):
     import torch
     budgets = torch.tensor(HEAD_BUDGETS, dtype=torch.int32, device="cuda")
     call, keep = rkv_caller(mode, layers, 1, N, max(HEAD_BUDGETS), budgets=budgets)
-    return time_calls(call, KERNELS[mode], rkv_cost(mode), steps, warmup, hip)
+    return time_calls(call, rkv_kernels(mode, N), rkv_cost(mode), steps, warmup, hip)
 
 
 def bf16_dev(a):
@@ -299,7 +309,7 @@ def run_decode(mode, n_layers, hip, calls_per_layer=240):
     call, keep = rkv_caller(mode, seq, 1, cap, budget, out_bufs=obuf)
     total = n_layers * calls_per_layer
     cost = rkv_cost(mode, 1, cap, budget)
-    r = time_calls(call, KERNELS[mode], cost, total, 2 * n_layers, hip, traced_steps=512)
+    r = time_calls(call, rkv_kernels(mode, cap), cost, total, 2 * n_layers, hip, traced_steps=512)
     r["calls"] = total
     r["tokens"] = total * cap
     return r
@@ -319,7 +329,7 @@ def run_decode_slots(mode, n_layers, hip, calls_per_layer=240):
     cap, budget, w, nb = 2176, 2048, W, 2176 - 2048
     lib = K.lib()
     mcode = K.MODES[mode]
-    names = KERNELS[mode][:-1] + ["evict"]
+    names = rkv_kernels(mode, cap)[:-1] + ["evict"]
     P = ctypes.c_void_p
     layers = []
     for layer in range(n_layers):
@@ -380,7 +390,7 @@ def run_batched(mode, hip, steps):
     del c
     b, n, budget = 64, 8192, 1024
     call, keep = rkv_caller(mode, [layer], b, n, budget)
-    r = time_calls(call, KERNELS[mode], rkv_cost(mode, b, n, budget), steps, 2, hip)
+    r = time_calls(call, rkv_kernels(mode, n), rkv_cost(mode, b, n, budget), steps, 2, hip)
     r["tokens"] = b * n
     r["step_bytes"] = rkv_step_bytes(b, n, budget)
     return r
@@ -746,7 +756,7 @@ def main():
         "config": {"workload": "R-KV score-and-evict, one layer at the 8B shape: 32 q / 8 KV heads, "
                                "d=128, batch 1, n=32768, w=8, B=2048, lambda=0.1",
                    "redundancy": a.mode, "distinct_layer_caches": a.layers,
-                   "kernels_per_step": len(KERNELS[a.mode])},
+                   "kernels_per_step": len(rkv_kernels(a.mode, N))},
         "roofline": roofline(main_res, rkv_cost(a.mode), a.profiles, a.mode),
         "step_hbm_frac": hbm_frac(rkv_step_bytes(), main_res["ms_plain"]),
         "ms_per_step_traced": round(main_res["ms"], 5),

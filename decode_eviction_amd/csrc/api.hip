@@ -142,8 +142,9 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
   p.z_out = z_out;
   p.hist = hist;
   const int sm = mode == KVSEL_R_GRAM ? kModeGram : kModeKeysum;
+  p.fuse_reduce = p.nchunk <= kFuseReduceChunks;
   KV_TRY(launch_stats(dt, d, sm, p, stream, tr));
-  KV_TRY(launch_reduce(d, sm, p, stream, tr));
+  if (!p.fuse_reduce) KV_TRY(launch_reduce(d, sm, p, stream, tr));
   KV_TRY(launch_pool(dt, d, sm, p, stream, tr));
   if (mode == KVSEL_R_GRAM) {
     GramParams gp{};

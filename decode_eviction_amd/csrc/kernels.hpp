@@ -10,6 +10,7 @@
 namespace kvsel {
 
 constexpr int kChunk = 256;        // tokens per work-group in the streaming passes
+constexpr int kFuseReduceChunks = 16;
 constexpr int kMaxRows = 128;      // g*w (R-KV) or g (cut) rows, in 32-row tiles
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectLdsKeys = 32768;
@@ -71,6 +72,9 @@ struct ScoreParams {
   uint64_t* ctot;           // [b][Hkv][nchunk]          chunk totals of energy
   int accum;                // add to the energies of earlier row groups
   int32_t* err;             // error word
+  // R-KV modes with nchunk <= kFuseReduceChunks: k_pool merges the chunk
+  // partials itself (in k_reduce's order) and k_reduce is not launched
+  int fuse_reduce;
   // outputs (never null; the host substitutes workspace buffers)
   float* i_out;             // [b][Hkv][cap]
   float* r_out;             // [b][Hkv][cap] (may be null in keysum mode)

@@ -10,7 +10,8 @@
 //            max / sum-exp (key-sum mode: key norms and the chunk's sum of
 //            unit keys); ReFreeKV mode also stores the scaled logits;
 //   k_reduce per head: merges chunk partials (online-softmax merge) and the
-//            unit-key sums;
+//            unit-key sums (R-KV calls of at most kFuseReduceChunks chunks
+//            per head skip it: k_pool merges them itself);
 //   k_pool   per 256-token chunk: logits again, p = exp(s - max) / sum,
 //            I[j] = mean over rows; Gram mode writes the key weights
 //            1/||k_j||; key-sum mode adds
@@ -415,7 +416,30 @@ void k_pool(ScoreParams p) {
       for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
   }
   if (tid < MT * 32) {
-    float2 v = p.rstat[head * p.mp + tid];
+    float2 v;
+    if (MODE != kModeCut && p.fuse_reduce) {
+      // few chunks: the row's chunk partials merged here, in the order
+      // k_reduce uses (group g of its 32/MT groups takes chunks g, g + 32/MT,
+      // ...; the groups are merged in turn), so the result is the same
+      constexpr int G = 32 / MT, F = kFuseReduceChunks;
+      const int nch = (n + kChunk - 1) / kChunk;
+      const float2* cs = p.cstat + head * p.nchunk * p.mp + tid;
+      float2 c[F];
+#pragma unroll
+      for (int u = 0; u < F; ++u) c[u] = cs[(long)min(u, nch - 1) * p.mp];
+      float m = -INFINITY, s = 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float mg = -INFINITY, sg = 0.f;
+#pragma unroll
+        for (int ci = g; ci < F; ci += G)
+          if (ci < nch) softmax_merge(mg, sg, c[ci].x, c[ci].y);
+        softmax_merge(m, s, mg, sg);
+      }
+      v = make_float2(m, s > 0.f ? 1.0f / s : 0.f);
+    } else {
+      v = p.rstat[head * p.mp + tid];
+    }
     rs[tid] = tid < p.m ? v : make_float2(0.f, 0.f);  // padding rows contribute 0
   }
   using QSt = QStage<E, D, MT>;
@@ -438,7 +462,29 @@ void k_pool(ScoreParams p) {
     load_frag<E, D>(kf[tt], kb, tok, tok < n, hf);
   }
   if constexpr (MODE == kModeKeysum) {
-    if (tid < D) ssh[tid] = p.ssum[head * D + tid];
+    if (tid < D) {
+      if (p.fuse_reduce) {
+        // the head's unit-key sum from the chunk sums, in k_reduce's order
+        // (group g of 1024/D takes chunks g, g + 1024/D, ...)
+        constexpr int GD = 1024 / D, F = kFuseReduceChunks;
+        const int nch = (n + kChunk - 1) / kChunk;
+        const float* sp = p.spart + head * p.nchunk * D + tid;
+        float c[F];
+#pragma unroll
+        for (int u = 0; u < F; ++u) c[u] = sp[(long)min(u, nch - 1) * D];
+        float a = 0.f;
+#pragma unroll
+        for (int g = 0; g < GD; ++g) {
+          float ag = 0.f;
+#pragma unroll
+          for (int ci = g; ci < F; ci += GD) ag += ci < nch ? c[ci] : 0.f;
+          a += ag;
+        }
+        ssh[tid] = a;
+      } else {
+        ssh[tid] = p.ssum[head * D + tid];
+      }
+    }
   }
   if constexpr (QSt::kLds) QSt::landed(qs, tid);
   __syncthreads();

@@ -161,7 +161,9 @@ kvsel_status kvsel_score_evict_heads(kvsel_dtype dt, kvsel_redundancy mode,
  * Launch order for cap <= 32768: KVSEL_R_GRAM: stats, reduce, pool, gram,
  * gram_fin, threshold, compact (the compaction kernel also gathers the kept rows);
  * KVSEL_R_KEYSUM: stats, reduce, pool, threshold, compact.  For larger cap
- * the last two are replaced by select, gather. */
+ * the last two are replaced by select, gather.  With cap <= 4096 (at most 16
+ * chunks of 256 keys per head) there is no reduce kernel: pool merges the
+ * chunk partials itself. */
 kvsel_status kvsel_score_evict_traced(kvsel_dtype dt, kvsel_redundancy mode,
                                       const void* q_window, const void* k, const void* v,
                                       const int32_t* lengths, int b, int Hq, int Hkv, int d,
