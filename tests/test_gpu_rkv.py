@@ -8,6 +8,8 @@ on oracle scores, gather), per-head budgets (stage and whole step),
 determinism and the clamped-length flag.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -166,6 +168,26 @@ def test_large_cap_ragged_lengths(mode):
     case = synth.rkv_case("bigragged", seed=13, wl=93, b=2, hq=8, hkv=2, d=128, w=8,
                           lengths=[9001, 8300], cap=9216, budget=1000)
     check_case(case, mode, form="keysum", sample_rows=24)
+
+
+def test_pool_merge_matches_reduce_kernel():
+    # cap 4096 (16 chunks): k_pool merges the chunk partials itself; the same
+    # keys in a 4352-slot cache (17 chunks) go through k_reduce.  Both merge
+    # in one order, so the key-sum scores and selections are bitwise equal.
+    case = synth.rkv_case("fusedreduce", seed=19, wl=89, b=2, hq=16, hkv=4, d=128, w=8,
+                          lengths=[4096, 2500], cap=4096, budget=700)
+    pad = 4352 - case.cap
+    wide = dataclasses.replace(
+        case, cap=4352,
+        k=np.concatenate([case.k, np.zeros(case.k.shape[:2] + (pad, case.d), case.k.dtype)], axis=2),
+        v=np.concatenate([case.v, np.zeros(case.v.shape[:2] + (pad, case.d), case.v.dtype)], axis=2))
+    log("[rkv] fused reduce: cap 4096 vs 4352, keysum")
+    a = gpu_run(case, "keysum")
+    b = gpu_run(wide, "keysum")
+    for bi, n in enumerate(case.lengths.tolist()):
+        for name in ("I", "R", "Z"):
+            assert np.array_equal(a[name][bi, :, :n], b[name][bi, :, :n]), name
+    assert np.array_equal(a["idx"], b["idx"])
 
 
 @pytest.mark.parametrize("mode", MODES)
