@@ -165,3 +165,23 @@ def test_next_row_entries_reject(lib):
     assert K.kvsel_threshold_cut_rows_workspace(16, 28, 4, 128, 16384, 4) > base
     assert 0 < K.kvsel_threshold_cut_rows_workspace(16, 28, 4, 128, 16384, 64) < base
     assert K.kvsel_threshold_cut_rows_workspace(16, 28, 4, 128, 16384, 0) == 0
+
+
+def test_bench_kernel_names_follow_the_reduce_folding():
+    # the benchmark names traced kernels by launch order; the library skips
+    # k_reduce for R-KV calls with at most kFuseReduceChunks chunks of 256
+    # keys per head, and the benchmark's list must drop it at the same caps
+    import os
+    import re
+
+    import bench
+    hdr = os.path.join(os.path.dirname(K.__file__), "csrc", "kernels.hpp")
+    src = open(hdr).read()
+    fuse = int(re.search(r"constexpr int kFuseReduceChunks = (\d+);", src).group(1))
+    chunk = int(re.search(r"constexpr int kChunk = (\d+);", src).group(1))
+    for mode in ("gram", "keysum"):
+        for cap in (1, 2176, fuse * chunk, fuse * chunk + 1, 32768):
+            names = bench.rkv_kernels(mode, cap)
+            folded = -(-cap // chunk) <= fuse
+            assert ("reduce" not in names) == folded, (mode, cap)
+            assert [k for k in bench.KERNELS[mode] if k != "reduce"] == [k for k in names if k != "reduce"]
