@@ -11,6 +11,34 @@ namespace kvsel {
 
 constexpr int kChunk = 256;        // tokens per work-group in the streaming passes
 constexpr int kFuseReduceChunks = 16;
+
+// Calls of at most kActiveFirstMaxB sequences map work-group L of a
+// (chunk, head, sequence) grid to the L-th chunk that holds keys, in
+// (sequence, head, chunk) order: on a ragged batch the work-groups with work
+// are dispatched first and those past the last such chunk exit at once
+// (with every sequence at full length the map is the identity).  Returns
+// false past the last chunk with keys.
+constexpr int kActiveFirstMaxB = 16;
+__device__ __forceinline__ bool active_chunk(const int32_t* lengths, int b, int hkv, int cap, int nchunk,
+                                             int& bi, int& h, int& chunk) {
+  int L = blockIdx.x + nchunk * (blockIdx.y + hkv * blockIdx.z);
+  int lens[kActiveFirstMaxB];
+#pragma unroll
+  for (int i = 0; i < kActiveFirstMaxB; ++i) lens[i] = lengths[min(i, b - 1)];
+#pragma unroll
+  for (int i = 0; i < kActiveFirstMaxB; ++i) {
+    const int n = max(0, min(lens[i], cap));  // a negative length holds no keys
+    const int nch = i < b ? (n + kChunk - 1) / kChunk : 0;
+    if (L < nch * hkv) {
+      bi = i;
+      h = L / nch;
+      chunk = L - h * nch;
+      return true;
+    }
+    L -= nch * hkv;
+  }
+  return false;
+}
 constexpr int kMaxRows = 128;      // g*w (R-KV) or g (cut) rows, in 32-row tiles
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectLdsKeys = 32768;

@@ -113,19 +113,23 @@ void k_stats(ScoreParams p) {
   constexpr int NC = G::kNC;
   constexpr int LE = G::kLaneElems;
   constexpr int PC = E::kPerChunk;
-  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
 
-  if (chunk == 0 && h == 0 && bi == 0 && tid == 0) {
+  // per-call and per-head duties by grid position
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) {
     int f = 0;
     for (int i = 0; i < p.b; ++i) f |= p.lengths[i] > p.cap ? 1 : 0;
     *p.err = f;
   }
+  if (p.hist && blockIdx.x == 0)  // the later passes accumulate into it
+    for (int t = tid; t < kHistBins; t += 256)
+      p.hist[((long)blockIdx.z * p.hkv + blockIdx.y) * kHistBins + t] = 0u;
+  int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  if (p.b > 1 && p.b <= kActiveFirstMaxB && !active_chunk(p.lengths, p.b, p.hkv, p.cap, p.nchunk, bi, h, chunk))
+    return;
   const int n = min(p.lengths[bi], p.cap);
   const int c0 = chunk * kChunk;
   const long head = (long)bi * p.hkv + h;
-  if (p.hist && chunk == 0)  // the later passes accumulate into it
-    for (int t = tid; t < kHistBins; t += 256) p.hist[head * kHistBins + t] = 0u;
   if (c0 >= n) return;
   const char* kb = p.k + head * (long)p.cap * G::kRowBytes;
   const char* qb = p.q + (((long)bi * p.hq + (long)h * p.g) * p.w + p.rows0) * G::kRowBytes;
@@ -397,7 +401,9 @@ void k_pool(ScoreParams p) {
   constexpr int NC = G::kNC;
   constexpr int LE = G::kLaneElems;
   constexpr int PC = E::kPerChunk;
-  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  if (p.b > 1 && p.b <= kActiveFirstMaxB && !active_chunk(p.lengths, p.b, p.hkv, p.cap, p.nchunk, bi, h, chunk))
+    return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   const int n = min(p.lengths[bi], p.cap);
   const int c0 = chunk * kChunk;
