@@ -25,8 +25,9 @@ def _run_pins(module):
         params = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
         calls = [{}]
         if params:
-            argname, values = params[0].args[0], list(params[0].args[1])
-            calls = [{argname: v} for v in values[:6]]
+            names = [a.strip() for a in params[0].args[0].split(",")]
+            values = list(params[0].args[1])[:6]
+            calls = [dict(zip(names, v if len(names) > 1 else (v,))) for v in values]
         for kw in calls:
             try:
                 with np.errstate(all="ignore"):
@@ -142,6 +143,92 @@ def _attn_no_scale(q, k):
     return _softmax_rows(np.asarray(q, float) @ np.asarray(k, float).T)
 
 
+def _cut_strided(q_last, k, lengths, layer, n_full_layers=2, m=4, T=0.01, heads=None):
+    # GQA group of KV head h taken as q heads h, h + Hkv, ... (strided, not contiguous)
+    q_last = np.asarray(q_last)
+    b, hq, d = q_last.shape
+    hkv = k.shape[1]
+    L = np.zeros((b, hkv), np.int64)
+    es = {}
+    for bi in range(b):
+        for h in range(hkv):
+            n = int(lengths[bi])
+            if layer < n_full_layers:
+                L[bi, h] = n
+                continue
+            e = rf.energies(rf.last_row_attention(q_last[bi, h::hkv], k[bi, h, :n]))
+            es[(bi, h)] = e
+            L[bi, h] = rf.cut_length(e, m, T)
+    return L, es
+
+
+def _cut_rows_strided(q_rows, k, lengths, layer, n_full_layers=2, m=4, T=0.01, heads=None):
+    q_rows = np.asarray(q_rows)
+    b = q_rows.shape[0]
+    hkv = k.shape[1]
+    L = np.zeros((b, hkv), np.int64)
+    es = {}
+    for bi in range(b):
+        for h in range(hkv):
+            n = int(lengths[bi])
+            if layer < n_full_layers:
+                L[bi, h] = n
+                continue
+            e = rf.energies(rf.last_rows_attention(q_rows[bi, h::hkv], k[bi, h, :n]))
+            es[(bi, h)] = e
+            L[bi, h] = rf.cut_length(e, m, T)
+    return L, es
+
+
+def _from_attn_strided(attn32, lengths, hkv, m=4, T=0.01):
+    attn32 = np.asarray(attn32, np.float32)
+    b = attn32.shape[0]
+    L = np.zeros((b, hkv), np.int64)
+    for bi in range(b):
+        n = int(lengths[bi])
+        for h in range(hkv):
+            L[bi, h] = rf.cut_length_fixed(rf.energies_fixed(attn32[bi, h::hkv, :n]), m, T)
+    return L
+
+
+def _last_rows_not_causal(q_rows, k):
+    # every row attends to all n keys
+    q64 = np.asarray(q_rows, np.float64)
+    k64 = np.asarray(k, np.float64)
+    g, kr, d = q64.shape
+    return _softmax_rows(q64.reshape(g * kr, d) @ k64.T / np.sqrt(d)) if len(k64) else np.zeros((g * kr, 0))
+
+
+def _energies_fixed_linear(a32):
+    # the probability itself rounded, not its square
+    a32 = np.asarray(a32, np.float32).astype(np.float64)
+    return np.floor(a32 * float(1 << rf.FIX_SHIFT)).astype(np.uint64).sum(axis=0, dtype=np.uint64)
+
+
+def _evict_ties_by_slot(z, budget, pos=None):
+    # equal scores split by slot index instead of token position
+    z = np.asarray(z, np.float64)
+    n = z.shape[0]
+    if n <= budget:
+        return np.zeros(0, dtype=np.int64)
+    order = np.lexsort((np.arange(n), -z))
+    keep = np.zeros(n, dtype=bool)
+    keep[order[:max(budget, 0)]] = True
+    return np.arange(n)[~keep].astype(np.int64)
+
+
+def _head_budget_unclamped(budgets, h, budget):
+    return budget if budgets is None else int(budgets[h])
+
+
+def _red_keysum_no_self(k):
+    u = rkv.unit_keys(k)
+    n = len(u)
+    if n <= 1:
+        return np.zeros(n)
+    return (u @ u.sum(axis=0)) / (n - 1)
+
+
 MUTANTS = [
     (rkv, "importance", _imp_no_scale, pins_rkv),
     (rkv, "importance", _imp_max_pool, pins_rkv),
@@ -159,6 +246,14 @@ MUTANTS = [
     (rf, "cut_length", _cut_off_by_one, pins_rf),
     (rf, "cut_length", _cut_wrong_threshold, pins_rf),
     (rf, "last_row_attention", _attn_no_scale, pins_rf),
+    (rf, "threshold_cut", _cut_strided, pins_rf),
+    (rf, "threshold_cut_rows", _cut_rows_strided, pins_rf),
+    (rf, "threshold_cut_from_attn", _from_attn_strided, pins_rf),
+    (rf, "last_rows_attention", _last_rows_not_causal, pins_rf),
+    (rf, "energies_fixed", _energies_fixed_linear, pins_rf),
+    (rkv, "evict_slots", _evict_ties_by_slot, pins_rkv),
+    (rkv, "head_budget", _head_budget_unclamped, pins_rkv),
+    (rkv, "redundancy_keysum", _red_keysum_no_self, pins_rkv),
 ]
 
 

@@ -211,3 +211,104 @@ def test_last_rows_k1_is_last_row():
     q = rng.standard_normal((4, 1, 16))
     k = rng.standard_normal((40, 16))
     assert np.allclose(rf.last_rows_attention(q, k), rf.last_row_attention(q[:, 0], k), rtol=1e-14)
+
+
+# ------------------------------------------------- GQA grouping, whole calls
+#
+# Hq = 4 query heads over Hkv = 2 KV heads (g = 2): query heads 0, 1 form KV
+# head 0's group and 2, 3 KV head 1's.  Head 0's queries are zero, so its
+# attention is uniform whatever its keys (the uniform closed form); head 1's
+# queries are e0 and its keys spike (logit 30) on the sinks and on the old
+# positions 100..109, so every row spends ~1/14 on each of those 14 tokens and
+# the walk (sinks, then newest first) must reach back to position 100:
+#   L = m + (n - 100)   since 13/14 of the energy is below 1 - T.
+# Head 0's keys spike on positions 200..209 along e0: a grouping that hands
+# head 0 one of head 1's e0 queries (for instance a strided q[h::Hkv]) no
+# longer sees uniform attention there and cuts near m + (n - 200).
+
+_GN, _GD, _GM, _GT = 1234, 8, 4, 0.01
+
+
+def _gqa_case(k_rows=None):
+    rng = np.random.default_rng(77)
+    k = rng.standard_normal((1, 2, _GN, _GD))
+    spike = 30.0 * math.sqrt(_GD)                  # logit 30 against e0
+    k[0, 0, 200:210, 0] = spike
+    k[0, 1] = 0.0
+    k[0, 1, list(range(_GM)) + list(range(100, 110)), 0] = spike
+    q = np.zeros((1, 4, _GD))
+    q[0, 2:, 0] = 1.0
+    if k_rows is not None:
+        q = np.repeat(q[:, :, None, :], k_rows, axis=2)
+    return q, k
+
+
+def _uniform_causal_cut(n, kr, g, m, T):
+    """Kept length for zero queries over the last kr causal rows: token j's
+    energy is g * sum over rows r with n-kr+r >= j of 1/(n-kr+r+1)^2; the cut
+    by an exactly rounded linear search down the queue."""
+    e = [0.0] * n
+    for j in range(n):
+        e[j] = g * math.fsum(1.0 / (n - kr + r + 1) ** 2 for r in range(kr) if n - kr + r >= j)
+    order = list(range(min(m, n))) + list(range(n - 1, min(m, n) - 1, -1))
+    total = math.fsum(e)
+    acc = []
+    for p in range(1, n + 1):
+        acc.append(e[order[p - 1]])
+        if math.fsum(acc) >= (1 - T) * total:
+            return max(min(m, n), p)
+    return n
+
+
+def test_gqa_groups_whole_call_last_row():
+    q, k = _gqa_case()
+    L, es = rf.threshold_cut(q, k, [_GN], layer=2, m=_GM, T=_GT)
+    assert L.tolist() == [[1222, _GM + _GN - 100]]
+    # head 0 uniform: every token carries 2/n^2 (two zero queries)
+    assert np.allclose(es[(0, 0)], 2.0 / _GN ** 2, rtol=1e-12, atol=0)
+
+
+def test_gqa_groups_whole_call_rows_k1():
+    q, k = _gqa_case(k_rows=1)
+    L, _ = rf.threshold_cut_rows(q, k, [_GN], layer=3, m=_GM, T=_GT)
+    assert L.tolist() == [[1222, _GM + _GN - 100]]
+
+
+def test_gqa_groups_whole_call_rows_causal():
+    kr = 3
+    q, k = _gqa_case(k_rows=kr)
+    L, _ = rf.threshold_cut_rows(q, k, [_GN], layer=2, m=_GM, T=_GT)
+    want0 = _uniform_causal_cut(_GN, kr, 2, _GM, _GT)
+    assert L.tolist() == [[want0, _GM + _GN - 100]]
+    # layers below n_full_layers keep everything for both heads
+    L, _ = rf.threshold_cut_rows(q, k, [_GN], layer=1, m=_GM, T=_GT)
+    assert L.tolist() == [[_GN, _GN]]
+
+
+def test_gqa_groups_whole_call_from_attn():
+    # the same two groups given as fp32 attention rows: rows 0, 1 uniform,
+    # rows 2, 3 equal to 1/14 on the sinks and positions 100..109
+    a = np.zeros((1, 4, _GN + 6), np.float32)        # cap above n: slots past n ignored
+    a[0, :2, :_GN] = np.float32(1.0 / _GN)
+    a[0, 2:, list(range(_GM)) + list(range(100, 110))] = np.float32(1.0 / 14)
+    a[0, :, _GN:] = 0.5                               # junk past n
+    L = rf.threshold_cut_from_attn(a, [_GN], hkv=2, m=_GM, T=_GT)
+    assert L.tolist() == [[1222, _GM + _GN - 100]]
+
+
+@pytest.mark.parametrize("T,m", [(0.001, 4), (0.1, 4), (0.01, 0), (0.01, 10)])
+def test_uniform_cut_other_T_and_sinks(T, m):
+    # zero query: L = max(min(m, n), ceil((1 - T) n)) when (1 - T) n is not an integer
+    n, d = 1237, 16
+    k = np.random.default_rng(5).standard_normal((1, 1, n, d))
+    got, _ = rf.threshold_cut(np.zeros((1, 1, d)), k, [n], layer=2, m=m, T=T)
+    assert int(got[0, 0]) == max(min(m, n), math.ceil((1 - T) * n))
+
+
+def test_fixed_cut_zero_energy():
+    # all-zero rows: the total is 0, tau = 0, and the first queued token
+    # already reaches it, so L = max(min(m, n), 1)
+    for m in (0, 4):
+        for n in (1, 3, 10):
+            assert rf.cut_length_fixed(np.zeros(n, np.uint64), m, 0.01) == max(min(m, n), 1)
+    assert rf.cut_length_fixed(np.zeros(0, np.uint64), 4, 0.01) == 0
