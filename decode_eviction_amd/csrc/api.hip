@@ -4,10 +4,12 @@
 // include/kvsel.h.
 #include <math.h>
 
+
 #include "../../include/kvsel.h"
 #include "kernels.hpp"
 
 using namespace kvsel;
+
 
 namespace {
 
@@ -67,23 +69,31 @@ struct ScoreWs {
 // in blocks of up to 512 keys
 int gram_wstride(int cap) { return (cap + 511) / 512 * 512; }
 
-ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap) {
+// Layout of one call's workspace.  The key-sum form needs the unit-key sums,
+// the Gram form the key weights, own-block row sums and column-sum slots;
+// each carves only its own (the size query returns the larger of the two).
+ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap, kvsel_redundancy mode) {
   const size_t heads = (size_t)b * hkv;
   const int nchunk = (cap + kChunk - 1) / kChunk;
   const int mp = rows_padded(m);
+  const bool gram = mode == KVSEL_R_GRAM;
   Carver c{static_cast<char*>(base)};
-  ScoreWs w;
+  ScoreWs w{};
   w.err = c.take<int32_t>(64);
   w.cstat = c.take<float2>(heads * nchunk * mp);
   w.rstat = c.take<float2>(heads * mp);
-  w.spart = c.take<float>(heads * nchunk * d);
-  w.ssum = c.take<float>(heads * d);
-  w.inv_norm = c.take<float>(heads * gram_wstride(cap));
+  if (!gram) {
+    w.spart = c.take<float>(heads * nchunk * d);
+    w.ssum = c.take<float>(heads * d);
+  }
   w.imp = c.take<float>(heads * cap);
   w.z = c.take<float>(heads * cap);
   w.nsmax = cap <= kGramPairCap ? (cap + 127) / 128 : ((cap + 255) / 256) / 2;
-  w.grs = c.take<float>(heads * cap);
-  w.gpart = c.take<float>(heads * (size_t)w.nsmax * cap);
+  if (gram) {
+    w.inv_norm = c.take<float>(heads * gram_wstride(cap));
+    w.grs = c.take<float>(heads * cap);
+    w.gpart = c.take<float>(heads * (size_t)w.nsmax * cap);
+  }
   w.sel.nsc = (cap + kSelChunk - 1) / kSelChunk;
   w.sel.hist = c.take<uint32_t>(heads * kHistBins);
   w.sel.thr = c.take<uint32_t>(heads * 4);
@@ -264,7 +274,10 @@ const char* kvsel_status_string(kvsel_status s) {
 size_t kvsel_score_evict_workspace(int b, int hq, int hkv, int d, int w, int cap, int budget) {
   (void)budget;
   if (b < 1 || hq < 1 || hkv < 1 || w < 1 || cap < 1 || (d != 64 && d != 128)) return 0;
-  return score_ws(nullptr, b, hkv, d, (hq / hkv) * w, cap).bytes;
+  const int m = (hq / hkv) * w;
+  const size_t g = score_ws(nullptr, b, hkv, d, m, cap, KVSEL_R_GRAM).bytes;
+  const size_t ks = score_ws(nullptr, b, hkv, d, m, cap, KVSEL_R_KEYSUM).bytes;
+  return g > ks ? g : ks;
 }
 
 kvsel_status kvsel_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q_window,
@@ -274,9 +287,9 @@ kvsel_status kvsel_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q_w
   kvsel_status st = check_score_args(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda);
   if (st != KVSEL_OK) return st;
   if (!z_out) return KVSEL_ERR_INVALID_ARG;
-  const ScoreWs need = score_ws(nullptr, b, hkv, d, (hq / hkv) * w, cap);
+  const ScoreWs need = score_ws(nullptr, b, hkv, d, (hq / hkv) * w, cap, mode);
   if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
-  const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap);
+  const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap, mode);
   return run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, i_out, r_out,
                     z_out, nullptr, ws, stream, nullptr);
 }
@@ -401,9 +414,9 @@ static kvsel_status score_evict_impl(kvsel_dtype dt, kvsel_redundancy mode, cons
   if (!aligned16(v) || !aligned16(k_out) || !aligned16(v_out)) return KVSEL_ERR_INVALID_ARG;
   if (budget < 1 || budget > cap_out) return KVSEL_ERR_INVALID_ARG;
   if (budget > 65536) return KVSEL_ERR_UNSUPPORTED;
-  const ScoreWs need = score_ws(nullptr, b, hkv, d, (hq / hkv) * w, cap);
+  const ScoreWs need = score_ws(nullptr, b, hkv, d, (hq / hkv) * w, cap, mode);
   if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
-  const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap);
+  const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap, mode);
   float* z = scores_out ? scores_out : ws.z;
   uint32_t* hist = cap <= kSelectLdsKeys ? ws.sel.hist : nullptr;
   st = run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, nullptr, nullptr,
@@ -507,9 +520,9 @@ static kvsel_status score_evict_slots_impl(kvsel_dtype dt, kvsel_redundancy mode
   if (budget > 65536) return KVSEL_ERR_UNSUPPORTED;
   st = check_slot_args(evict_out, evict_stride, n_evict_out, budgets, cap, budget);
   if (st != KVSEL_OK) return st;
-  const ScoreWs need = score_ws(nullptr, b, hkv, d, (hq / hkv) * w, cap);
+  const ScoreWs need = score_ws(nullptr, b, hkv, d, (hq / hkv) * w, cap, mode);
   if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
-  const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap);
+  const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap, mode);
   float* z = scores_out ? scores_out : ws.z;
   st = run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, nullptr, nullptr,
                   z, ws.sel.hist, ws, stream, tr);

@@ -47,7 +47,7 @@ __device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, uint64_t* ws
 
 __device__ __forceinline__ void write_err(const CutParams& p) {
   int f = 0;
-  for (int i = 0; i < p.b; ++i) f |= p.lengths[i] > p.cap ? 1 : 0;
+  for (int i = 0; i < p.b; ++i) f |= len_bad(p.lengths[i], p.cap) ? 1 : 0;
   *p.err = f;
 }
 
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void k_cut_energy(CutParams p) {
   __shared__ uint64_t wsum[4];
   const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
   if (p.attn && chunk == 0 && h == 0 && bi == 0 && tid == 0) write_err(p);
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   const int c0 = chunk * kChunk;
   if (c0 >= n) return;
   const long head = (long)bi * p.hkv + h;
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void k_cut_scan(CutParams p) {
   __shared__ uint64_t found_above;
   const int h = blockIdx.x, bi = blockIdx.y, tid = threadIdx.x;
   const long head = (long)bi * p.hkv + h;
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   if (n == 0) {
     if (tid == 0) p.kept[head] = 0;
     return;
@@ -123,8 +123,10 @@ __global__ __launch_bounds__(256) void k_cut_scan(CutParams p) {
   esk_cm = block_sum_u64(esk_cm, wsum, tid);
   const double taud = ceil((double)tot * (1.0 - (double)p.T));
   const uint64_t tau = (uint64_t)taud;
-  if (m > 0 && esk >= tau) {
-    if (tid == 0) p.kept[head] = m;
+  // the sinks alone reach tau (with no sinks this happens only when tau is 0,
+  // a total energy of 0: then the first queued token already reaches it)
+  if (esk >= tau) {
+    if (tid == 0) p.kept[head] = max(m, 1);
     return;
   }
 
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(256) void k_cut_scan(CutParams p) {
 __global__ void k_cut_full(CutParams p) {
   const int h = blockIdx.x, bi = blockIdx.y;
   if (h == 0 && bi == 0 && threadIdx.x == 0) write_err(p);
-  if (threadIdx.x == 0) p.kept[(long)bi * p.hkv + h] = min(p.lengths[bi], p.cap);
+  if (threadIdx.x == 0) p.kept[(long)bi * p.hkv + h] = clamp_len(p.lengths[bi], p.cap);
 }
 
 // Sink + suffix compaction after the cut (the kept set is the m sinks and
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(256) void k_cut_compact(CutCompactParams p) {
   const int h = blockIdx.y, bi = blockIdx.z;
   const int t = blockIdx.x * RPW + threadIdx.x / CPR, c = threadIdx.x % CPR;
   const long head = (long)bi * p.hkv + h;
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   const int L = min(p.kept[head], n);
   if (t >= L || t >= p.cap_out) return;
   const int ms = min(p.n_sink, n);

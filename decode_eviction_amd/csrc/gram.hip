@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256, 1) void k_gram(GramParams p) {
   const int h = hh % p.hkv, bi = hh / p.hkv;
   const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   const int r0 = rb * ROWS;
   if (r0 >= n) return;
   const int nb = (n + ROWS - 1) / ROWS;
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
   const int h = hh % p.hkv, bi = hh / p.hkv;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   const int r0 = rb * ROWS;
   if (r0 >= n) return;
   const int nb = (n + ROWS - 1) / ROWS;
@@ -629,7 +629,7 @@ __global__ __launch_bounds__(256) void k_gram_pairs(GramParams p) {
     ++I;
   }
   const int J = I + rem;
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   if (J * BS >= n) return;
   const long head = (long)bi * p.hkv + h;
   const char* kb = p.k + head * (long)p.cap * RB;
@@ -773,7 +773,7 @@ __global__ __launch_bounds__(256) void k_gram_fin(GramParams p) {
 #pragma unroll
     for (int u = 0; u < SB; ++u) a[u] = ld(pp + (long)min(u, max(ntc, 1) - 1) * p.cap);
   }
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   // pairs: one slot per block of the cache.  Otherwise slot s holds the
   // contribution of block J - (s+1) for s < (nb-1)/2, and the slot of
   // distance nb/2 (nb even, filled only for J >= nb/2) is the next one,

@@ -10,6 +10,11 @@
 namespace kvsel {
 
 constexpr int kChunk = 256;        // tokens per work-group in the streaming passes
+
+// A sequence length as the kernels use it: clamped into [0, cap].  A length
+// outside that range is reported in bit 0 of the error word (len_bad).
+__device__ __forceinline__ int clamp_len(int len, int cap) { return len < 0 ? 0 : (len > cap ? cap : len); }
+__device__ __forceinline__ bool len_bad(int len, int cap) { return len < 0 || len > cap; }
 constexpr int kFuseReduceChunks = 16;
 
 // Calls of at most kActiveFirstMaxB sequences map work-group L of a

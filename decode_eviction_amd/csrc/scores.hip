@@ -118,7 +118,7 @@ void k_stats(ScoreParams p) {
   // per-call and per-head duties by grid position
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) {
     int f = 0;
-    for (int i = 0; i < p.b; ++i) f |= p.lengths[i] > p.cap ? 1 : 0;
+    for (int i = 0; i < p.b; ++i) f |= len_bad(p.lengths[i], p.cap) ? 1 : 0;
     *p.err = f;
   }
   if (p.hist && blockIdx.x == 0)  // the later passes accumulate into it
@@ -127,7 +127,7 @@ void k_stats(ScoreParams p) {
   int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   if (p.b > 1 && p.b <= kActiveFirstMaxB && !active_chunk(p.lengths, p.b, p.hkv, p.cap, p.nchunk, bi, h, chunk))
     return;
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   const int c0 = chunk * kChunk;
   const long head = (long)bi * p.hkv + h;
   if (c0 >= n) return;
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(1024) void k_reduce(ScoreParams p) {
   __shared__ float2 part[1024];
   __shared__ float spar[1024];
   const int h = blockIdx.x, bi = blockIdx.y, tid = threadIdx.x;
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   const int nch = (n + kChunk - 1) / kChunk;
   const long head = (long)bi * p.hkv + h;
   {
@@ -405,7 +405,7 @@ void k_pool(ScoreParams p) {
   if (p.b > 1 && p.b <= kActiveFirstMaxB && !active_chunk(p.lengths, p.b, p.hkv, p.cap, p.nchunk, bi, h, chunk))
     return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   const int c0 = chunk * kChunk;
   if (c0 >= n) return;
   const long head = (long)bi * p.hkv + h;

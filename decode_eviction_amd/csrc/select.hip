@@ -67,7 +67,7 @@ __device__ __forceinline__ int head_budget(const SelectParams& p, int h) {
 // budget outside [0, budget] (bit 1).
 __device__ __forceinline__ void flag_select_errors(const SelectParams& p, int h, int bi) {
   if (!p.err) return;
-  int f = p.lengths[bi] > p.cap ? 1 : 0;
+  int f = len_bad(p.lengths[bi], p.cap) ? 1 : 0;
   if (p.budgets) {
     const int v = p.budgets[h];
     f |= (v < 0 || v > p.budget) ? 2 : 0;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(SelectParams p) {
 
   const int h = blockIdx.x, bi = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   const int B = head_budget(p, h);
   const long head = (long)bi * p.hkv + h;
   int32_t* out = p.idx + head * p.budget;
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
 #pragma unroll
     for (int i = 0; i < kKeysPerThread; ++i) key[i] = buf_ld32(rz, (uint32_t)tid * 4u, (uint32_t)(i * kRegThreads * 4));
   }
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   const int B = head_budget(p, h);
   if (tid == 0) flag_select_errors(p, h, bi);
   if (n <= B || B == 0) return;  // k_compact keeps everything (or nothing)
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(256) void k_compact(SelectParams p) {
   // one wait for all of these loads (the compiler would otherwise request the
   // record only after the length and budget have arrived)
   asm volatile("" ::"s"(kth), "s"(need_eq), "s"(off), "s"(eqb), "s"(len), "s"(B));
-  const int n = min(len, p.cap);
+  const int n = clamp_len(len, p.cap);
   int32_t* out = p.idx + head * p.budget;
   if (chunk == 0 && part == 0)
     for (int t = min(n, B) + tid; t < p.budget; t += 256) out[t] = -1;
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(kRegThreads) void k_evict_slots(SelectParams p) {
 #pragma unroll
     for (int i = 0; i < S; ++i) zv[i] = buf_ld32(rz, (uint32_t)(w0 + lane) * 4u, (uint32_t)(kWave * 4 * i));
   }
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   const int B = head_budget(p, h);
   int32_t* out = p.evict + head * p.evict_stride;
   const int ne = n > B ? n - B : 0;
@@ -833,7 +833,7 @@ __global__ __launch_bounds__(256) void k_hist_zero(SelectParams p) {
 __global__ __launch_bounds__(256) void k_hist(SelectParams p) {
   __shared__ uint32_t lh[kHistBins];
   const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
-  const int n = min(p.lengths[bi], p.cap);
+  const int n = clamp_len(p.lengths[bi], p.cap);
   const int c0 = chunk * 2048;
   if (c0 >= n) return;
   const long head = (long)bi * p.hkv + h;

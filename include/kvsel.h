@@ -33,8 +33,9 @@
  * Layouts (all row-major, element type per kvsel_dtype):
  *   q_window [b][Hq][w][d], q_last [b][Hq][d],
  *   k, v     [b][Hkv][cap][d]        (token j of head h of sequence b at row j)
- *   lengths  [b] int32 on the device; values above cap are clamped to cap and
- *            reported by kvsel_workspace_error().
+ *   lengths  [b] int32 on the device; a value outside [0, cap] is clamped into
+ *            it (a negative length holds no tokens) and reported by
+ *            kvsel_workspace_error().
  *   GQA: query head q belongs to KV head q / (Hq / Hkv).
  *
  * Ownership: the caller allocates every buffer, device workspace included;
@@ -113,9 +114,10 @@ kvsel_status kvsel_select_topb(const float* z, const int32_t* lengths, int b, in
 /* Top-budget choice with one budget per KV head: head h keeps the
  * min(budgets[h], n) largest scores, chosen and ordered as in
  * kvsel_select_topb.  budgets [Hkv] int32 on the device is one row of a
- * per-(layer, head) allocation table (the interface a learned or profiled
- * budget allocator feeds; QbitAI R-KV article, section on joint eviction
- * under a KV budget, with per-head budgets as the allocation layer above it).
+ * static per-(layer, head) budget table: the LU-KV page (Baidu Baige and
+ * Fudan, "Predicting Future Utility"), third step, profiles the best budget
+ * share of every head offline into a lookup table and reads it at inference
+ * time before the per-head eviction runs; that table's row is this argument.
  * idx_out is [b][Hkv][budget_max]: head h's entries, then -1 up to
  * budget_max.  A budget outside [0, budget_max] is clamped into it and sets
  * bit 1 of the workspace error word; budget 0 keeps nothing.  Same workspace
@@ -319,9 +321,9 @@ kvsel_status kvsel_threshold_cut_from_attn(const float* attn_last, const int32_t
 /* ------------------------------------------------------------ utility */
 
 /* Reads the device error word left in the workspace by the last call that
- * used it (synchronises the stream).  Bit 0: some lengths[i] exceeded cap and
- * was clamped; bit 1: some per-head budget lay outside [0, budget_max] and
- * was clamped.  Returns KVSEL_ERR_HIP if the copy fails. */
+ * used it (synchronises the stream).  Bit 0: some lengths[i] lay outside
+ * [0, cap] and was clamped into it; bit 1: some per-head budget lay outside
+ * [0, budget_max] and was clamped.  Returns KVSEL_ERR_HIP if the copy fails. */
 kvsel_status kvsel_workspace_error(const void* workspace, int32_t* flags_host, hipStream_t stream);
 
 #ifdef __cplusplus
