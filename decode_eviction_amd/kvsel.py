@@ -6,6 +6,17 @@ unless one is given, and the workspace is a torch uint8 tensor the binding
 allocates when the caller passes none.  Every step of the computation runs in
 the HIP kernels of libkvsel.so; if the library is missing this module raises
 instead of computing anything itself.
+
+Streams: every tensor the binding allocates (outputs, zero-filled compacted
+caches, the workspace) is allocated and filled on the stream the kernels run
+on, inside ``torch.cuda.stream(s)``, so the fills are ordered before the
+kernels and the caching allocator does not reuse a temporary workspace
+before the kernels on ``s`` are done with it.  Tensors the caller passes are
+the caller's to order, as with any torch operation on a side stream.
+
+Arguments are checked before the call: device, contiguity, element types
+(lengths int32 with at least b entries, q/v of k's dtype) and the shapes and
+dtypes of caller-given outputs; a mismatch raises ValueError or TypeError.
 """
 
 from __future__ import annotations
@@ -116,8 +127,11 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
-    s = stream if stream is not None else torch.cuda.current_stream()
+def _stream_of(stream):
+    return stream if stream is not None else torch.cuda.current_stream()
+
+
+def _handle(s):
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -127,8 +141,54 @@ def _need_cuda(*ts):
             raise ValueError("tensors must be contiguous device tensors")
 
 
+def _need_lengths(lengths, b):
+    if lengths.dtype != torch.int32:
+        raise TypeError(f"lengths must be int32, got {lengths.dtype}")
+    if lengths.numel() < b:
+        raise ValueError(f"lengths has {lengths.numel()} entries for {b} sequences")
+
+
+def _need_i32(t, name, numel=None, shape=None):
+    if t is None:
+        return
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} entries, needs {numel}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, needs {tuple(shape)}")
+
+
+def _need_like(ref, name, t):
+    """t (nullable) has ref's dtype (q and v against k)."""
+    if t is not None and t.dtype != ref.dtype:
+        raise TypeError(f"{name} is {t.dtype} but k is {ref.dtype}")
+
+
+def _need_out(t, name, dtype, lead, min_rows=None, rows=None, tail=None):
+    """Caller-given output: dtype, leading dims lead, then (rows[, tail])."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    sh = tuple(t.shape)
+    want_nd = len(lead) + 1 + (1 if tail is not None else 0)
+    if len(sh) != want_nd or sh[:len(lead)] != tuple(lead):
+        raise ValueError(f"{name} has shape {sh}, needs leading dims {tuple(lead)} and {want_nd} dims")
+    if tail is not None and sh[-1] != tail:
+        raise ValueError(f"{name} has last dim {sh[-1]}, needs {tail}")
+    r = sh[len(lead)]
+    if rows is not None and r != rows:
+        raise ValueError(f"{name} has {r} rows per head, needs {rows}")
+    if min_rows is not None and r < min_rows:
+        raise ValueError(f"{name} has {r} rows per head, needs at least {min_rows}")
+
+
 def _workspace(nbytes: int, device, workspace):
+    """Caller's workspace, or a new one (allocate inside the launch stream's context)."""
     if workspace is not None:
+        if workspace.dtype != torch.uint8:
+            raise TypeError("workspace must be a uint8 tensor")
         return workspace
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
@@ -139,19 +199,39 @@ def kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, budget) -> int:
     return int(lib().kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, budget))
 
 
+def _rkv_inputs(q_window, k, v, lengths):
+    """Checks of the R-KV inputs; returns (b, hq, w, d, hkv, cap)."""
+    _need_cuda(q_window, k, v, lengths)
+    if q_window.dim() != 4 or k.dim() != 4:
+        raise ValueError("q_window must be [b][Hq][w][d] and k [b][Hkv][cap][d]")
+    b, hq, w, d = q_window.shape
+    bk, hkv, cap, dk = k.shape
+    if bk != b or dk != d:
+        raise ValueError(f"k has shape {tuple(k.shape)} for q_window {tuple(q_window.shape)}")
+    _dtype(k)
+    _need_like(k, "q_window", q_window)
+    _need_like(k, "v", v)
+    if v is not None and tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v has shape {tuple(v.shape)}, k {tuple(k.shape)}")
+    _need_lengths(lengths, b)
+    return b, hq, w, d, hkv, cap
+
+
 def kvsel_scores(q_window, k, lengths, lam=0.1, mode="gram", i_out=None, r_out=None, z_out=None,
                  workspace=None, stream=None):
     """I, R, Z (fp32 [b][Hkv][cap]) for q_window [b][Hq][w][d], k [b][Hkv][cap][d]."""
-    _need_cuda(q_window, k, lengths, i_out, r_out, z_out)
-    b, hq, w, d = q_window.shape
-    _, hkv, cap, _ = k.shape
-    dev = k.device
-    if z_out is None:
-        z_out = torch.empty((b, hkv, cap), dtype=torch.float32, device=dev)
-    ws = _workspace(kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, 1), dev, workspace)
-    st = lib().kvsel_scores(_dtype(k), MODES[mode], _ptr(q_window), _ptr(k), _ptr(lengths),
-                            b, hq, hkv, d, w, cap, float(lam), _ptr(i_out), _ptr(r_out),
-                            _ptr(z_out), _ptr(ws), ws.numel(), _stream(stream))
+    b, hq, w, d, hkv, cap = _rkv_inputs(q_window, k, None, lengths)
+    _need_cuda(i_out, r_out, z_out)
+    for name, t in (("i_out", i_out), ("r_out", r_out), ("z_out", z_out)):
+        _need_out(t, name, torch.float32, (b, hkv), rows=cap)
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if z_out is None:
+            z_out = torch.empty((b, hkv, cap), dtype=torch.float32, device=k.device)
+        ws = _workspace(kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, 1), k.device, workspace)
+        st = lib().kvsel_scores(_dtype(k), MODES[mode], _ptr(q_window), _ptr(k), _ptr(lengths),
+                                b, hq, hkv, d, w, cap, float(lam), _ptr(i_out), _ptr(r_out),
+                                _ptr(z_out), _ptr(ws), ws.numel(), _handle(s))
     _check("kvsel_scores", st)
     return i_out, r_out, z_out
 
@@ -160,14 +240,26 @@ def kvsel_select_workspace(b, hkv, cap) -> int:
     return int(lib().kvsel_select_workspace(b, hkv, cap))
 
 
-def kvsel_select_topb(z, lengths, budget, idx_out=None, workspace=None, stream=None):
-    _need_cuda(z, lengths, idx_out)
+def _select_inputs(z, lengths):
+    _need_cuda(z, lengths)
+    if z.dtype != torch.float32 or z.dim() != 3:
+        raise TypeError("z must be a float32 [b][Hkv][cap] tensor")
     b, hkv, cap = z.shape
-    if idx_out is None:
-        idx_out = torch.empty((b, hkv, budget), dtype=torch.int32, device=z.device)
-    ws = _workspace(kvsel_select_workspace(b, hkv, cap), z.device, workspace)
-    st = lib().kvsel_select_topb(_ptr(z), _ptr(lengths), b, hkv, cap, int(budget), _ptr(idx_out),
-                                 _ptr(ws), ws.numel(), _stream(stream))
+    _need_lengths(lengths, b)
+    return b, hkv, cap
+
+
+def kvsel_select_topb(z, lengths, budget, idx_out=None, workspace=None, stream=None):
+    b, hkv, cap = _select_inputs(z, lengths)
+    _need_cuda(idx_out)
+    _need_out(idx_out, "idx_out", torch.int32, (b, hkv), rows=budget)
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if idx_out is None:
+            idx_out = torch.empty((b, hkv, budget), dtype=torch.int32, device=z.device)
+        ws = _workspace(kvsel_select_workspace(b, hkv, cap), z.device, workspace)
+        st = lib().kvsel_select_topb(_ptr(z), _ptr(lengths), b, hkv, cap, int(budget),
+                                     _ptr(idx_out), _ptr(ws), ws.numel(), _handle(s))
     _check("kvsel_select_topb", st)
     return idx_out
 
@@ -175,50 +267,80 @@ def kvsel_select_topb(z, lengths, budget, idx_out=None, workspace=None, stream=N
 def kvsel_select_topb_heads(z, lengths, budgets, budget_max, idx_out=None, workspace=None,
                             stream=None):
     """Top-budget per KV head with budgets [Hkv] (int32 device tensor)."""
-    _need_cuda(z, lengths, budgets, idx_out)
-    b, hkv, cap = z.shape
-    if idx_out is None:
-        idx_out = torch.empty((b, hkv, budget_max), dtype=torch.int32, device=z.device)
-    ws = _workspace(kvsel_select_workspace(b, hkv, cap), z.device, workspace)
-    st = lib().kvsel_select_topb_heads(_ptr(z), _ptr(lengths), _ptr(budgets), b, hkv, cap,
-                                       int(budget_max), _ptr(idx_out), _ptr(ws), ws.numel(),
-                                       _stream(stream))
+    b, hkv, cap = _select_inputs(z, lengths)
+    _need_cuda(budgets, idx_out)
+    _need_i32(budgets, "budgets", numel=hkv)
+    _need_out(idx_out, "idx_out", torch.int32, (b, hkv), rows=budget_max)
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if idx_out is None:
+            idx_out = torch.empty((b, hkv, budget_max), dtype=torch.int32, device=z.device)
+        ws = _workspace(kvsel_select_workspace(b, hkv, cap), z.device, workspace)
+        st = lib().kvsel_select_topb_heads(_ptr(z), _ptr(lengths), _ptr(budgets), b, hkv, cap,
+                                           int(budget_max), _ptr(idx_out), _ptr(ws), ws.numel(),
+                                           _handle(s))
     _check("kvsel_select_topb_heads", st)
     return idx_out
 
 
 def kvsel_gather(k, v, idx, k_out=None, v_out=None, stream=None):
     _need_cuda(k, v, idx, k_out, v_out)
+    if k.dim() != 4:
+        raise ValueError("k must be [b][Hkv][cap][d]")
     b, hkv, cap, d = k.shape
+    _dtype(k)
+    _need_like(k, "v", v)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v has shape {tuple(v.shape)}, k {tuple(k.shape)}")
+    if idx.dim() != 3 or tuple(idx.shape[:2]) != (b, hkv):
+        raise ValueError(f"idx must be [b][Hkv][budget], got {tuple(idx.shape)}")
+    _need_i32(idx, "idx")
     budget = idx.shape[2]
-    if k_out is None:
-        k_out = torch.zeros((b, hkv, budget, d), dtype=k.dtype, device=k.device)
-    if v_out is None:
-        v_out = torch.zeros((b, hkv, budget, d), dtype=v.dtype, device=v.device)
-    st = lib().kvsel_gather(_dtype(k), _ptr(k), _ptr(v), _ptr(idx), b, hkv, d, cap, budget,
-                            _ptr(k_out), _ptr(v_out), k_out.shape[2], _stream(stream))
+    _need_out(k_out, "k_out", k.dtype, (b, hkv), min_rows=budget, tail=d)
+    _need_out(v_out, "v_out", k.dtype, (b, hkv), min_rows=budget, tail=d)
+    if k_out is not None and v_out is not None and k_out.shape != v_out.shape:
+        raise ValueError("k_out and v_out differ in shape")
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if k_out is None:
+            k_out = torch.zeros((b, hkv, budget, d), dtype=k.dtype, device=k.device)
+        if v_out is None:
+            v_out = torch.zeros(tuple(k_out.shape), dtype=v.dtype, device=v.device)
+        st = lib().kvsel_gather(_dtype(k), _ptr(k), _ptr(v), _ptr(idx), b, hkv, d, cap, budget,
+                                _ptr(k_out), _ptr(v_out), k_out.shape[2], _handle(s))
     _check("kvsel_gather", st)
     return k_out, v_out
+
+
+def _evict_outputs(k, b, hkv, d, budget, k_out, v_out, idx_out, scores_out, cap):
+    _need_cuda(k_out, v_out, idx_out, scores_out)
+    _need_out(k_out, "k_out", k.dtype, (b, hkv), min_rows=budget, tail=d)
+    _need_out(v_out, "v_out", k.dtype, (b, hkv), min_rows=budget, tail=d)
+    if k_out is not None and v_out is not None and k_out.shape != v_out.shape:
+        raise ValueError("k_out and v_out differ in shape")
+    _need_out(idx_out, "idx_out", torch.int32, (b, hkv), rows=budget)
+    _need_out(scores_out, "scores_out", torch.float32, (b, hkv), rows=cap)
 
 
 def kvsel_score_evict(q_window, k, v, lengths, budget, lam=0.1, mode="gram", k_out=None,
                       v_out=None, idx_out=None, scores_out=None, workspace=None, stream=None):
     """The whole step; returns (k_out, v_out, idx_out)."""
-    _need_cuda(q_window, k, v, lengths, k_out, v_out, idx_out, scores_out)
-    b, hq, w, d = q_window.shape
-    _, hkv, cap, _ = k.shape
+    b, hq, w, d, hkv, cap = _rkv_inputs(q_window, k, v, lengths)
+    _evict_outputs(k, b, hkv, d, budget, k_out, v_out, idx_out, scores_out, cap)
     dev = k.device
-    if k_out is None:
-        k_out = torch.zeros((b, hkv, budget, d), dtype=k.dtype, device=dev)
-    if v_out is None:
-        v_out = torch.zeros((b, hkv, budget, d), dtype=v.dtype, device=dev)
-    if idx_out is None:
-        idx_out = torch.empty((b, hkv, budget), dtype=torch.int32, device=dev)
-    ws = _workspace(kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, budget), dev, workspace)
-    st = lib().kvsel_score_evict(_dtype(k), MODES[mode], _ptr(q_window), _ptr(k), _ptr(v),
-                                 _ptr(lengths), b, hq, hkv, d, w, cap, float(lam), int(budget),
-                                 _ptr(k_out), _ptr(v_out), k_out.shape[2], _ptr(idx_out),
-                                 _ptr(scores_out), _ptr(ws), ws.numel(), _stream(stream))
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if k_out is None:
+            k_out = torch.zeros((b, hkv, budget, d), dtype=k.dtype, device=dev)
+        if v_out is None:
+            v_out = torch.zeros(tuple(k_out.shape), dtype=v.dtype, device=dev)
+        if idx_out is None:
+            idx_out = torch.empty((b, hkv, budget), dtype=torch.int32, device=dev)
+        ws = _workspace(kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, budget), dev, workspace)
+        st = lib().kvsel_score_evict(_dtype(k), MODES[mode], _ptr(q_window), _ptr(k), _ptr(v),
+                                     _ptr(lengths), b, hq, hkv, d, w, cap, float(lam), int(budget),
+                                     _ptr(k_out), _ptr(v_out), k_out.shape[2], _ptr(idx_out),
+                                     _ptr(scores_out), _ptr(ws), ws.numel(), _handle(s))
     _check("kvsel_score_evict", st)
     return k_out, v_out, idx_out
 
@@ -227,41 +349,56 @@ def kvsel_score_evict_heads(q_window, k, v, lengths, budgets, budget_max, lam=0.
                             k_out=None, v_out=None, idx_out=None, scores_out=None,
                             workspace=None, stream=None):
     """The whole step with per-head budgets; returns (k_out, v_out, idx_out)."""
-    _need_cuda(q_window, k, v, lengths, budgets, k_out, v_out, idx_out, scores_out)
-    b, hq, w, d = q_window.shape
-    _, hkv, cap, _ = k.shape
+    b, hq, w, d, hkv, cap = _rkv_inputs(q_window, k, v, lengths)
+    _need_cuda(budgets)
+    _need_i32(budgets, "budgets", numel=hkv)
+    _evict_outputs(k, b, hkv, d, budget_max, k_out, v_out, idx_out, scores_out, cap)
     dev = k.device
-    if k_out is None:
-        k_out = torch.zeros((b, hkv, budget_max, d), dtype=k.dtype, device=dev)
-    if v_out is None:
-        v_out = torch.zeros((b, hkv, budget_max, d), dtype=v.dtype, device=dev)
-    if idx_out is None:
-        idx_out = torch.empty((b, hkv, budget_max), dtype=torch.int32, device=dev)
-    ws = _workspace(kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, budget_max), dev, workspace)
-    st = lib().kvsel_score_evict_heads(_dtype(k), MODES[mode], _ptr(q_window), _ptr(k), _ptr(v),
-                                       _ptr(lengths), _ptr(budgets), b, hq, hkv, d, w, cap,
-                                       float(lam), int(budget_max), _ptr(k_out), _ptr(v_out),
-                                       k_out.shape[2], _ptr(idx_out), _ptr(scores_out), _ptr(ws),
-                                       ws.numel(), _stream(stream))
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if k_out is None:
+            k_out = torch.zeros((b, hkv, budget_max, d), dtype=k.dtype, device=dev)
+        if v_out is None:
+            v_out = torch.zeros(tuple(k_out.shape), dtype=v.dtype, device=dev)
+        if idx_out is None:
+            idx_out = torch.empty((b, hkv, budget_max), dtype=torch.int32, device=dev)
+        ws = _workspace(kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, budget_max), dev,
+                        workspace)
+        st = lib().kvsel_score_evict_heads(_dtype(k), MODES[mode], _ptr(q_window), _ptr(k),
+                                           _ptr(v), _ptr(lengths), _ptr(budgets), b, hq, hkv, d, w,
+                                           cap, float(lam), int(budget_max), _ptr(k_out),
+                                           _ptr(v_out), k_out.shape[2], _ptr(idx_out),
+                                           _ptr(scores_out), _ptr(ws), ws.numel(), _handle(s))
     _check("kvsel_score_evict_heads", st)
     return k_out, v_out, idx_out
 
 
 # ------------------------------------------------------------------ slot reuse
 
+def _slot_outputs(b, hkv, cap, pos, budgets, evict_out, n_evict_out):
+    _need_cuda(pos, budgets, evict_out, n_evict_out)
+    _need_i32(pos, "pos", shape=(b, hkv, cap))
+    _need_i32(budgets, "budgets", numel=hkv)
+    _need_out(evict_out, "evict_out", torch.int32, (b, hkv))
+    _need_i32(n_evict_out, "n_evict_out", shape=(b, hkv))
+
+
 def kvsel_select_evict_slots(z, lengths, budget, pos=None, budgets=None, evict_out=None,
                              n_evict_out=None, workspace=None, stream=None):
     """Evicted slots (ascending, -1 padded) and their count per (sequence, KV head)."""
-    _need_cuda(z, lengths, pos, budgets, evict_out, n_evict_out)
-    b, hkv, cap = z.shape
-    if evict_out is None:
-        evict_out = torch.empty((b, hkv, cap), dtype=torch.int32, device=z.device)
-    if n_evict_out is None:
-        n_evict_out = torch.empty((b, hkv), dtype=torch.int32, device=z.device)
-    ws = _workspace(kvsel_select_workspace(b, hkv, cap), z.device, workspace)
-    st = lib().kvsel_select_evict_slots(_ptr(z), _ptr(lengths), _ptr(pos), _ptr(budgets), b, hkv,
-                                        cap, int(budget), _ptr(evict_out), evict_out.shape[2],
-                                        _ptr(n_evict_out), _ptr(ws), ws.numel(), _stream(stream))
+    b, hkv, cap = _select_inputs(z, lengths)
+    _slot_outputs(b, hkv, cap, pos, budgets, evict_out, n_evict_out)
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if evict_out is None:
+            evict_out = torch.empty((b, hkv, cap), dtype=torch.int32, device=z.device)
+        if n_evict_out is None:
+            n_evict_out = torch.empty((b, hkv), dtype=torch.int32, device=z.device)
+        ws = _workspace(kvsel_select_workspace(b, hkv, cap), z.device, workspace)
+        st = lib().kvsel_select_evict_slots(_ptr(z), _ptr(lengths), _ptr(pos), _ptr(budgets), b,
+                                            hkv, cap, int(budget), _ptr(evict_out),
+                                            evict_out.shape[2], _ptr(n_evict_out), _ptr(ws),
+                                            ws.numel(), _handle(s))
     _check("kvsel_select_evict_slots", st)
     return evict_out, n_evict_out
 
@@ -270,20 +407,23 @@ def kvsel_score_evict_slots(q_window, k, lengths, budget, lam=0.1, mode="gram", 
                             budgets=None, evict_out=None, n_evict_out=None, scores_out=None,
                             workspace=None, stream=None):
     """Scores and evicted slots in one call; returns (evict_out, n_evict_out)."""
-    _need_cuda(q_window, k, lengths, pos, budgets, evict_out, n_evict_out, scores_out)
-    b, hq, w, d = q_window.shape
-    _, hkv, cap, _ = k.shape
+    b, hq, w, d, hkv, cap = _rkv_inputs(q_window, k, None, lengths)
+    _slot_outputs(b, hkv, cap, pos, budgets, evict_out, n_evict_out)
+    _need_cuda(scores_out)
+    _need_out(scores_out, "scores_out", torch.float32, (b, hkv), rows=cap)
     dev = k.device
-    if evict_out is None:
-        evict_out = torch.empty((b, hkv, cap), dtype=torch.int32, device=dev)
-    if n_evict_out is None:
-        n_evict_out = torch.empty((b, hkv), dtype=torch.int32, device=dev)
-    ws = _workspace(kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, budget), dev, workspace)
-    st = lib().kvsel_score_evict_slots(_dtype(k), MODES[mode], _ptr(q_window), _ptr(k),
-                                       _ptr(lengths), _ptr(pos), _ptr(budgets), b, hq, hkv, d, w,
-                                       cap, float(lam), int(budget), _ptr(evict_out),
-                                       evict_out.shape[2], _ptr(n_evict_out), _ptr(scores_out),
-                                       _ptr(ws), ws.numel(), _stream(stream))
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if evict_out is None:
+            evict_out = torch.empty((b, hkv, cap), dtype=torch.int32, device=dev)
+        if n_evict_out is None:
+            n_evict_out = torch.empty((b, hkv), dtype=torch.int32, device=dev)
+        ws = _workspace(kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, budget), dev, workspace)
+        st = lib().kvsel_score_evict_slots(_dtype(k), MODES[mode], _ptr(q_window), _ptr(k),
+                                           _ptr(lengths), _ptr(pos), _ptr(budgets), b, hq, hkv, d,
+                                           w, cap, float(lam), int(budget), _ptr(evict_out),
+                                           evict_out.shape[2], _ptr(n_evict_out),
+                                           _ptr(scores_out), _ptr(ws), ws.numel(), _handle(s))
     _check("kvsel_score_evict_slots", st)
     return evict_out, n_evict_out
 
@@ -291,11 +431,27 @@ def kvsel_score_evict_slots(q_window, k, lengths, budget, lam=0.1, mode="gram", 
 def kvsel_slots_write(k, v, k_new, v_new, evict, n_evict, pos=None, pos_new=None, stream=None):
     """Copy new tokens [b][Hkv][count][d] into the evicted slots of k/v (in place)."""
     _need_cuda(k, v, k_new, v_new, evict, n_evict, pos, pos_new)
+    if k.dim() != 4 or k_new.dim() != 4:
+        raise ValueError("k must be [b][Hkv][cap][d] and k_new [b][Hkv][count][d]")
     b, hkv, cap, d = k.shape
+    _dtype(k)
+    for name, t in (("v", v), ("k_new", k_new), ("v_new", v_new)):
+        _need_like(k, name, t)
+    if tuple(v.shape) != tuple(k.shape) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("v / v_new must have the shapes of k / k_new")
+    if tuple(k_new.shape[:2]) != (b, hkv) or k_new.shape[3] != d:
+        raise ValueError(f"k_new has shape {tuple(k_new.shape)} for k {tuple(k.shape)}")
+    if evict.dim() != 3 or tuple(evict.shape[:2]) != (b, hkv):
+        raise ValueError(f"evict must be [b][Hkv][stride], got {tuple(evict.shape)}")
+    _need_i32(evict, "evict")
+    _need_i32(n_evict, "n_evict", shape=(b, hkv))
+    _need_i32(pos, "pos", shape=(b, hkv, cap))
+    _need_i32(pos_new, "pos_new", numel=b)
     count = k_new.shape[2]
+    s = _stream_of(stream)
     st = lib().kvsel_slots_write(_dtype(k), _ptr(k), _ptr(v), _ptr(pos), _ptr(k_new), _ptr(v_new),
                                  _ptr(pos_new), _ptr(evict), evict.shape[2], _ptr(n_evict), b, hkv,
-                                 d, cap, count, _stream(stream))
+                                 d, cap, count, _handle(s))
     _check("kvsel_slots_write", st)
 
 
@@ -305,18 +461,33 @@ def kvsel_threshold_cut_workspace(b, hq, hkv, d, cap) -> int:
     return int(lib().kvsel_threshold_cut_workspace(b, hq, hkv, d, cap))
 
 
+def _cut_inputs(q, k, lengths, nd):
+    _need_cuda(q, k, lengths)
+    if q.dim() != nd or k.dim() != 4:
+        raise ValueError("q must be [b][Hq](" + ("[k]" if nd == 4 else "") + ")[d], k [b][Hkv][cap][d]")
+    b, hkv, cap, d = k.shape
+    if q.shape[0] != b or q.shape[-1] != d:
+        raise ValueError(f"q has shape {tuple(q.shape)} for k {tuple(k.shape)}")
+    _dtype(k)
+    _need_like(k, "q", q)
+    _need_lengths(lengths, b)
+    return b, q.shape[1], hkv, cap, d
+
+
 def kvsel_threshold_cut(q_last, k, lengths, layer, n_full_layers=2, n_sink=4, T=0.01,
                         kept_out=None, workspace=None, stream=None):
     """Kept length per (sequence, KV head), int32 [b][Hkv]."""
-    _need_cuda(q_last, k, lengths, kept_out)
-    b, hq, d = q_last.shape
-    _, hkv, cap, _ = k.shape
-    if kept_out is None:
-        kept_out = torch.empty((b, hkv), dtype=torch.int32, device=k.device)
-    ws = _workspace(kvsel_threshold_cut_workspace(b, hq, hkv, d, cap), k.device, workspace)
-    st = lib().kvsel_threshold_cut(_dtype(k), _ptr(q_last), _ptr(k), _ptr(lengths), b, hq, hkv, d,
-                                   cap, int(layer), int(n_full_layers), int(n_sink), float(T),
-                                   _ptr(kept_out), _ptr(ws), ws.numel(), _stream(stream))
+    b, hq, hkv, cap, d = _cut_inputs(q_last, k, lengths, 3)
+    _need_cuda(kept_out)
+    _need_i32(kept_out, "kept_out", shape=(b, hkv))
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if kept_out is None:
+            kept_out = torch.empty((b, hkv), dtype=torch.int32, device=k.device)
+        ws = _workspace(kvsel_threshold_cut_workspace(b, hq, hkv, d, cap), k.device, workspace)
+        st = lib().kvsel_threshold_cut(_dtype(k), _ptr(q_last), _ptr(k), _ptr(lengths), b, hq,
+                                       hkv, d, cap, int(layer), int(n_full_layers), int(n_sink),
+                                       float(T), _ptr(kept_out), _ptr(ws), ws.numel(), _handle(s))
     _check("kvsel_threshold_cut", st)
     return kept_out
 
@@ -330,19 +501,29 @@ def kvsel_threshold_cut_rows(q_rows, k, lengths, layer, n_full_layers=2, n_sink=
                              stream=None):
     """Kept length per (sequence, KV head) from the last k rows, q_rows
     [b][Hq][k][d]; with v and k_out/v_out also the sink + suffix compaction."""
-    _need_cuda(q_rows, k, v, lengths, k_out, v_out, kept_out)
-    b, hq, k_rows, d = q_rows.shape
-    _, hkv, cap, _ = k.shape
-    if kept_out is None:
-        kept_out = torch.empty((b, hkv), dtype=torch.int32, device=k.device)
-    ws = _workspace(kvsel_threshold_cut_rows_workspace(b, hq, hkv, d, cap, k_rows), k.device,
-                    workspace)
-    st = lib().kvsel_threshold_cut_rows(_dtype(k), _ptr(q_rows), k_rows, _ptr(k), _ptr(v),
-                                        _ptr(lengths), b, hq, hkv, d, cap, int(layer),
-                                        int(n_full_layers), int(n_sink), float(T), _ptr(kept_out),
-                                        _ptr(k_out), _ptr(v_out),
-                                        0 if k_out is None else k_out.shape[2], _ptr(ws),
-                                        ws.numel(), _stream(stream))
+    b, hq, hkv, cap, d = _cut_inputs(q_rows, k, lengths, 4)
+    k_rows = q_rows.shape[2]
+    _need_cuda(v, k_out, v_out, kept_out)
+    _need_like(k, "v", v)
+    if v is not None and tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v has shape {tuple(v.shape)}, k {tuple(k.shape)}")
+    _need_out(k_out, "k_out", k.dtype, (b, hkv), min_rows=cap, tail=d)
+    _need_out(v_out, "v_out", k.dtype, (b, hkv), min_rows=cap, tail=d)
+    if k_out is not None and v_out is not None and k_out.shape != v_out.shape:
+        raise ValueError("k_out and v_out differ in shape")
+    _need_i32(kept_out, "kept_out", shape=(b, hkv))
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if kept_out is None:
+            kept_out = torch.empty((b, hkv), dtype=torch.int32, device=k.device)
+        ws = _workspace(kvsel_threshold_cut_rows_workspace(b, hq, hkv, d, cap, k_rows), k.device,
+                        workspace)
+        st = lib().kvsel_threshold_cut_rows(_dtype(k), _ptr(q_rows), k_rows, _ptr(k), _ptr(v),
+                                            _ptr(lengths), b, hq, hkv, d, cap, int(layer),
+                                            int(n_full_layers), int(n_sink), float(T),
+                                            _ptr(kept_out), _ptr(k_out), _ptr(v_out),
+                                            0 if k_out is None else k_out.shape[2], _ptr(ws),
+                                            ws.numel(), _handle(s))
     _check("kvsel_threshold_cut_rows", st)
     return kept_out
 
@@ -350,14 +531,28 @@ def kvsel_threshold_cut_rows(q_rows, k, lengths, layer, n_full_layers=2, n_sink=
 def kvsel_cut_compact(k, v, lengths, kept_len, n_sink=4, k_out=None, v_out=None, stream=None):
     """Sink + suffix compaction from given kept lengths; returns (k_out, v_out)."""
     _need_cuda(k, v, lengths, kept_len, k_out, v_out)
+    if k.dim() != 4:
+        raise ValueError("k must be [b][Hkv][cap][d]")
     b, hkv, cap, d = k.shape
-    if k_out is None:
-        k_out = torch.zeros_like(k)
-    if v_out is None:
-        v_out = torch.zeros_like(v)
-    st = lib().kvsel_cut_compact(_dtype(k), _ptr(k), _ptr(v), _ptr(lengths), _ptr(kept_len), b,
-                                 hkv, d, cap, int(n_sink), _ptr(k_out), _ptr(v_out),
-                                 k_out.shape[2], _stream(stream))
+    _dtype(k)
+    _need_like(k, "v", v)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v has shape {tuple(v.shape)}, k {tuple(k.shape)}")
+    _need_lengths(lengths, b)
+    _need_i32(kept_len, "kept_len", shape=(b, hkv))
+    _need_out(k_out, "k_out", k.dtype, (b, hkv), tail=d)
+    _need_out(v_out, "v_out", k.dtype, (b, hkv), tail=d)
+    if k_out is not None and v_out is not None and k_out.shape != v_out.shape:
+        raise ValueError("k_out and v_out differ in shape")
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if k_out is None:
+            k_out = torch.zeros_like(k)
+        if v_out is None:
+            v_out = torch.zeros(tuple(k_out.shape), dtype=v.dtype, device=v.device)
+        st = lib().kvsel_cut_compact(_dtype(k), _ptr(k), _ptr(v), _ptr(lengths), _ptr(kept_len),
+                                     b, hkv, d, cap, int(n_sink), _ptr(k_out), _ptr(v_out),
+                                     k_out.shape[2], _handle(s))
     _check("kvsel_cut_compact", st)
     return k_out, v_out
 
@@ -365,19 +560,26 @@ def kvsel_cut_compact(k, v, lengths, kept_len, n_sink=4, k_out=None, v_out=None,
 def kvsel_threshold_cut_from_attn(attn_last, lengths, hkv, n_sink=4, T=0.01, kept_out=None,
                                   workspace=None, stream=None):
     _need_cuda(attn_last, lengths, kept_out)
+    if attn_last.dtype != torch.float32 or attn_last.dim() != 3:
+        raise TypeError("attn_last must be a float32 [b][Hq][cap] tensor")
     b, hq, cap = attn_last.shape
-    if kept_out is None:
-        kept_out = torch.empty((b, hkv), dtype=torch.int32, device=attn_last.device)
-    ws = _workspace(kvsel_threshold_cut_workspace(b, hq, hkv, 64, cap), attn_last.device, workspace)
-    st = lib().kvsel_threshold_cut_from_attn(_ptr(attn_last), _ptr(lengths), b, hq, hkv, cap,
-                                             int(n_sink), float(T), _ptr(kept_out), _ptr(ws),
-                                             ws.numel(), _stream(stream))
+    _need_lengths(lengths, b)
+    _need_i32(kept_out, "kept_out", shape=(b, hkv))
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if kept_out is None:
+            kept_out = torch.empty((b, hkv), dtype=torch.int32, device=attn_last.device)
+        ws = _workspace(kvsel_threshold_cut_workspace(b, hq, hkv, 64, cap), attn_last.device,
+                        workspace)
+        st = lib().kvsel_threshold_cut_from_attn(_ptr(attn_last), _ptr(lengths), b, hq, hkv, cap,
+                                                 int(n_sink), float(T), _ptr(kept_out), _ptr(ws),
+                                                 ws.numel(), _handle(s))
     _check("kvsel_threshold_cut_from_attn", st)
     return kept_out
 
 
 def kvsel_workspace_error(workspace, stream=None) -> int:
     flag = ctypes.c_int32(0)
-    st = lib().kvsel_workspace_error(_ptr(workspace), ctypes.byref(flag), _stream(stream))
+    st = lib().kvsel_workspace_error(_ptr(workspace), ctypes.byref(flag), _handle(_stream_of(stream)))
     _check("kvsel_workspace_error", st)
     return int(flag.value)
