@@ -3,7 +3,7 @@
 Cases: the tiny fp32 layer (n=512), the 8B-shaped layer (n=4096), ragged and
 padded batches covering several tiles and ragged tails, d=64 with 8/64/128
 window rows, the n=32768 layer in the launch configuration the benchmark
-times, the batched 64 x 8192 workload (sampled heads), stage entries (top-B
+times, the batched 64 x 8192 workload (all 512 heads), stage entries (top-B
 on oracle scores, gather), per-head budgets (stage and whole step),
 determinism and the clamped-length flag.
 """
@@ -203,13 +203,12 @@ def test_many_chunks_ragged(mode):
 
 
 @pytest.mark.parametrize("mode", ["keysum", "gram"])
-def test_batched_64x8192_sampled(mode):
+def test_batched_64x8192_all_heads(mode):
+    # every one of the 512 (sequence, KV head) pairs against the key-sum
+    # oracle; a few heads also against the pairwise definition on sampled rows
     case = synth.batched_case(0)
-    heads = [(0, 0), (7, 3), (31, 7), (63, 5)]
-    got, _ = check_case(case, mode, form="keysum", heads=heads, sample_rows=16)
-    for b in range(case.b):
-        for h in range(case.hkv):
-            check_idx_structure(got["idx"][b, h], 8192, case.budget)
+    check_case(case, mode, form="keysum", sample_rows=0)
+    check_case(case, mode, form="keysum", heads=[(0, 0), (31, 7), (63, 5)], sample_rows=16)
 
 
 def test_select_stage_exact():
