@@ -4,12 +4,42 @@
 // include/kvsel.h.
 #include <math.h>
 
+#include <mutex>
 
 #include "../../include/kvsel.h"
 #include "kernels.hpp"
 
 using namespace kvsel;
 
+// Workspace of the allocation-free entry point (kvsel_score_evict_static): a
+// file-scope device array, one copy per GPU, held until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory; kernels
+// receive the address hipGetSymbolAddress returns for the current device,
+// looked up once per device and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[KVSEL_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+}  // namespace
 
 namespace {
 
@@ -461,6 +491,23 @@ kvsel_status kvsel_score_evict(kvsel_dtype dt, kvsel_redundancy mode, const void
   return score_evict_impl(dt, mode, q_window, k, v, lengths, nullptr, b, hq, hkv, d, w, cap, lambda,
                           budget, k_out, v_out, cap_out, idx_out, scores_out, workspace, ws_bytes,
                           stream, nullptr);
+}
+
+kvsel_status kvsel_score_evict_static(kvsel_dtype dt, kvsel_redundancy mode,
+                                      const void* q_window, const void* k, const void* v,
+                                      const int32_t* lengths, int b, int hq, int hkv, int d, int w,
+                                      int cap, float lambda, int budget, void* k_out, void* v_out,
+                                      int cap_out, int32_t* idx_out, float* scores_out,
+                                      hipStream_t stream) {
+  kvsel_status st = check_score_args(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda);
+  if (st != KVSEL_OK) return st;
+  if (score_ws(nullptr, b, hkv, d, (hq / hkv) * w, cap, mode).bytes > KVSEL_STATIC_SCRATCH_BYTES)
+    return KVSEL_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return KVSEL_ERR_HIP;
+  return score_evict_impl(dt, mode, q_window, k, v, lengths, nullptr, b, hq, hkv, d, w, cap, lambda,
+                          budget, k_out, v_out, cap_out, idx_out, scores_out, ws,
+                          KVSEL_STATIC_SCRATCH_BYTES, stream, nullptr);
 }
 
 kvsel_status kvsel_score_evict_heads(kvsel_dtype dt, kvsel_redundancy mode, const void* q_window,

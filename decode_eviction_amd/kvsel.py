@@ -48,6 +48,8 @@ _SIGS = {
     "kvsel_gather": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P]),
     "kvsel_score_evict": (_I, [_I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                                _P, _P, _I, _P, _P, _P, _S, _P]),
+    "kvsel_score_evict_static": (_I, [_I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                                      _P, _P, _I, _P, _P, _P]),
     "kvsel_score_evict_heads": (_I, [_I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                                      _P, _P, _I, _P, _P, _P, _S, _P]),
     "kvsel_score_evict_heads_traced": (_I, [_I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
@@ -342,6 +344,34 @@ def kvsel_score_evict(q_window, k, v, lengths, budget, lam=0.1, mode="gram", k_o
                                      _ptr(k_out), _ptr(v_out), k_out.shape[2], _ptr(idx_out),
                                      _ptr(scores_out), _ptr(ws), ws.numel(), _handle(s))
     _check("kvsel_score_evict", st)
+    return k_out, v_out, idx_out
+
+
+STATIC_SCRATCH_BYTES = 16 << 20   # KVSEL_STATIC_SCRATCH_BYTES
+
+
+def kvsel_score_evict_static(q_window, k, v, lengths, budget, lam=0.1, mode="gram", k_out=None,
+                             v_out=None, idx_out=None, scores_out=None, stream=None):
+    """The whole step in the library's own device scratch array (no
+    workspace); returns (k_out, v_out, idx_out).  Outputs not given are
+    allocated here; pass all three to keep the call free of allocations."""
+    b, hq, w, d, hkv, cap = _rkv_inputs(q_window, k, v, lengths)
+    _evict_outputs(k, b, hkv, d, budget, k_out, v_out, idx_out, scores_out, cap)
+    dev = k.device
+    s = _stream_of(stream)
+    with torch.cuda.stream(s):
+        if k_out is None:
+            k_out = torch.zeros((b, hkv, budget, d), dtype=k.dtype, device=dev)
+        if v_out is None:
+            v_out = torch.zeros(tuple(k_out.shape), dtype=v.dtype, device=dev)
+        if idx_out is None:
+            idx_out = torch.empty((b, hkv, budget), dtype=torch.int32, device=dev)
+        st = lib().kvsel_score_evict_static(_dtype(k), MODES[mode], _ptr(q_window), _ptr(k),
+                                            _ptr(v), _ptr(lengths), b, hq, hkv, d, w, cap,
+                                            float(lam), int(budget), _ptr(k_out), _ptr(v_out),
+                                            k_out.shape[2], _ptr(idx_out), _ptr(scores_out),
+                                            _handle(s))
+    _check("kvsel_score_evict_static", st)
     return k_out, v_out, idx_out
 
 

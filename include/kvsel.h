@@ -144,6 +144,32 @@ kvsel_status kvsel_score_evict(kvsel_dtype dt, kvsel_redundancy mode,
                                int32_t* idx_out, float* scores_out,
                                void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of the device array kvsel_score_evict_static works in (16 MiB per
+ * GPU the library runs on, held until the process ends). */
+#define KVSEL_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* kvsel_score_evict without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The call works in a file-scope device
+ * array of KVSEL_STATIC_SCRATCH_BYTES (one per GPU) and allocates nothing;
+ * the caller still passes every input and output.  Same arguments, results
+ * and error returns as kvsel_score_evict, plus KVSEL_ERR_WORKSPACE when the
+ * call's layout exceeds the array: the key-sum form needs about
+ * 11 bytes per (sequence, KV head, cap position) (2.9 MiB at 8 KV heads and
+ * cap 32768); the Gram form about 12 + 4 * ceil(cap / 256) / 2 bytes per
+ * position (1.5 MiB at 8 KV heads and cap 2176; caps above about 8192 at
+ * 8 heads do not fit).  Calls share the array: every call overwrites it, and
+ * calls that overlap on one GPU (on different streams, or from several
+ * threads without ordering) race.  Lengths outside [0, cap] are clamped as
+ * in kvsel_score_evict but not reported (kvsel_workspace_error needs a
+ * workspace). */
+kvsel_status kvsel_score_evict_static(kvsel_dtype dt, kvsel_redundancy mode,
+                                      const void* q_window, const void* k, const void* v,
+                                      const int32_t* lengths, int b, int Hq, int Hkv, int d, int w,
+                                      int cap, float lambda, int budget,
+                                      void* k_out, void* v_out, int cap_out,
+                                      int32_t* idx_out, float* scores_out, hipStream_t stream);
+
 /* The whole step with one budget per KV head (budgets [Hkv] int32 on the
  * device, as in kvsel_select_topb_heads): k_out/v_out [b][Hkv][cap_out][d]
  * receive head h's kept rows in rows 0 .. min(budgets[h], n)-1, later rows
