@@ -58,14 +58,54 @@ KERNELS = {
 }
 
 
-def rkv_kernels(mode: str, cap: int) -> list:
-    """Kernels one R-KV call launches, in order: with at most 16 chunks of 256
-    keys per head k_pool merges the chunk partials itself and k_reduce is not
-    launched."""
+FUSED_MAX_CHUNKS = 16     # kFusedMaxChunks: chunks of 256 tokens per head
+FUSED_CAPACITY = 256      # work-groups of the fused step resident at once (one per CU)
+
+
+def fused_step(mode: str, cap: int, b: int = 1, hkv: int = HKV, m: int = HQ // HKV * W) -> bool:
+    """The library runs a key-sum call on a short cache (bf16, d = 128, at
+    most 32 window rows per KV head) as one fused launch when its grid of
+    ceil(cap / 256) * Hkv * b work-groups fits on the device at once."""
+    nch = -(-cap // 256)
+    return (mode == "keysum" and m <= 32 and nch <= FUSED_MAX_CHUNKS
+            and nch * hkv * b <= FUSED_CAPACITY)
+
+
+def rkv_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV) -> list:
+    """Kernels one R-KV call launches, in order: the fused step alone when it
+    applies; otherwise with at most 16 chunks of 256 keys per head k_pool
+    merges the chunk partials itself and k_reduce is not launched."""
+    if fused_step(mode, cap, b, hkv):
+        return ["fused"]
+    return unfused_kernels(mode, cap)
+
+
+def unfused_kernels(mode: str, cap: int) -> list:
+    """The multi-kernel launch sequence (also the score kernels of the slot
+    reuse entry points, which are never fused)."""
     ks = list(KERNELS[mode])
     if -(-cap // 256) <= 16:
         ks.remove("reduce")
     return ks
+
+
+def gram_flops(b: int, hkv: int, n: int, d: int = D) -> tuple:
+    """(algorithmic, executed) matrix-core flops of the symmetric Gram form.
+
+    Algorithmic: every distinct key pair once, 2 d flops each, the diagonal
+    included: n (n + 1) d per head.  Executed: whole block pairs of the
+    kernel that runs (pairs of 128-key blocks up to cap 4096, 512-key blocks
+    from 8192 (bf16, d = 128), 256-key blocks between), diagonal blocks in
+    full; the SQ_VALU_MFMA_BUSY_CYCLES counter agrees with this count."""
+    alg = float(b) * hkv * n * (n + 1) * d
+    if n <= 4096:
+        nbh = -(-n // 128)
+        pairs, bs = nbh * (nbh + 1) // 2, 128
+    else:
+        bs = 512 if n >= 8192 else 256
+        nb = -(-n // bs)
+        pairs = sum(1 + (nb - 1) // 2 + (1 if nb % 2 == 0 and i < nb // 2 else 0) for i in range(nb))
+    return alg, 2.0 * b * hkv * pairs * bs * bs * d
 
 
 def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int = HKV,
@@ -87,15 +127,15 @@ def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int =
     }
     # slot reuse: scores and position map read, evicted list written
     cost["evict"] = {"bytes": 8 * tok + 4 * b * hkv * max(n - budget, 0)}
+    # the fused short-cache step: K once, Z and the indices written, the kept
+    # rows of V read and of K and V written (K rows come from registers)
+    cost["fused"] = {"bytes": kb + 4 * tok + 4 * b * hkv * budget + 3 * b * hkv * min(budget, n) * d * 2}
     if mode == "gram":
-        # symmetric Gram: each pair of 256-key blocks once; matrix-core flops
-        # as executed (2 d per key pair and block padding included)
-        nb = -(-n // 256)
-        blocks = sum(1 + (nb - 1) // 2 + (1 if nb % 2 == 0 and i < nb // 2 else 0)
-                     for i in range(nb))
-        ns = nb // 2
-        cost["gram"] = {"bytes": kb + 4 * tok * 2 + 4 * tok * ns // 2,
-                        "flops": 2.0 * b * hkv * blocks * 256 * 256 * d}
+        # symmetric Gram: achieved = algorithmic flops (each key pair once)
+        ns = -(-n // 256) // 2
+        alg, exe = gram_flops(b, hkv, n, d)
+        cost["gram"] = {"bytes": kb + 4 * tok * 2 + 4 * tok * ns // 2, "flops": alg,
+                        "flops_executed": exe}
         cost["gram_fin"] = {"bytes": 4 * tok * 5 + 4 * tok * ns // 2}
     return cost
 
@@ -329,7 +369,7 @@ def run_decode_slots(mode, n_layers, hip, calls_per_layer=240):
     cap, budget, w, nb = 2176, 2048, W, 2176 - 2048
     lib = K.lib()
     mcode = K.MODES[mode]
-    names = rkv_kernels(mode, cap)[:-1] + ["evict"]
+    names = unfused_kernels(mode, cap)[:-1] + ["evict"]
     P = ctypes.c_void_p
     layers = []
     for layer in range(n_layers):

@@ -30,7 +30,7 @@ HIP_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
-SOURCES = ["api.hip", "scores.hip", "gram.hip", "select.hip", "cut.hip"]
+SOURCES = ["api.hip", "scores.hip", "gram.hip", "select.hip", "cut.hip", "fused.hip"]
 
 # Per-file code generation options.  The Gram kernel folds every matrix-core
 # result with fp32 FMAs; keeping the results (and accumulator inputs) in

@@ -75,6 +75,12 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 struct ScoreWs {
   int32_t* err;
+  // fused short-cache step (key-sum form): barrier epochs and tokens, tagged
+  // chunk partials and score keys
+  uint64_t* fepoch;
+  uint64_t* fflags;
+  uint64_t* fpub_a;
+  uint64_t* fpub_b;
   float2* cstat;
   float2* rstat;
   float* spart;
@@ -90,6 +96,10 @@ struct ScoreWs {
     uint32_t* thr;
     uint32_t* coff;
     uint32_t* ceqb;
+    uint32_t* acnt;
+    uint32_t* ccnt;
+    uint32_t* candk;
+    int32_t* candp;
     int nsc;
   } sel;
   size_t bytes;
@@ -110,6 +120,12 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap, kvsel_redund
   Carver c{static_cast<char*>(base)};
   ScoreWs w{};
   w.err = c.take<int32_t>(64);
+  if (!gram && (cap + kChunk - 1) / kChunk <= kFusedMaxChunks) {
+    w.fepoch = c.take<uint64_t>(heads);
+    w.fflags = c.take<uint64_t>(2 * heads * kFusedMaxChunks);
+    w.fpub_a = c.take<uint64_t>(heads * kFusedMaxChunks * kFusedWordsA);
+    w.fpub_b = c.take<uint64_t>(heads * cap);
+  }
   w.cstat = c.take<float2>(heads * nchunk * mp);
   w.rstat = c.take<float2>(heads * mp);
   if (!gram) {
@@ -125,10 +141,14 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap, kvsel_redund
     w.gpart = c.take<float>(heads * (size_t)w.nsmax * cap);
   }
   w.sel.nsc = (cap + kSelChunk - 1) / kSelChunk;
-  w.sel.hist = c.take<uint32_t>(heads * kHistBins);
+  w.sel.hist = c.take<uint32_t>(heads * kHistStride);
   w.sel.thr = c.take<uint32_t>(heads * 4);
   w.sel.coff = c.take<uint32_t>(heads * w.sel.nsc);
   w.sel.ceqb = c.take<uint32_t>(heads * w.sel.nsc);
+  w.sel.acnt = c.take<uint32_t>(heads * w.sel.nsc);
+  w.sel.ccnt = c.take<uint32_t>(heads * w.sel.nsc);
+  w.sel.candk = c.take<uint32_t>(heads * cap);
+  w.sel.candp = c.take<int32_t>(heads * cap);
   w.bytes = (c.off + kAlign - 1) / kAlign * kAlign;
   return w;
 }
@@ -216,6 +236,10 @@ struct SelWs {
   uint32_t* thr;
   uint32_t* coff;
   uint32_t* ceqb;
+  uint32_t* acnt;
+  uint32_t* ccnt;
+  uint32_t* candk;
+  int32_t* candp;
   int nsc;
 };
 
@@ -224,10 +248,14 @@ SelWs carve_select(Carver& c, int b, int hkv, int cap) {
   SelWs w;
   w.err = c.take<int32_t>(64);
   w.nsc = (cap + kSelChunk - 1) / kSelChunk;
-  w.hist = c.take<uint32_t>(heads * kHistBins);
+  w.hist = c.take<uint32_t>(heads * kHistStride);
   w.thr = c.take<uint32_t>(heads * 4);
   w.coff = c.take<uint32_t>(heads * w.nsc);
   w.ceqb = c.take<uint32_t>(heads * w.nsc);
+  w.acnt = c.take<uint32_t>(heads * w.nsc);
+  w.ccnt = c.take<uint32_t>(heads * w.nsc);
+  w.candk = c.take<uint32_t>(heads * cap);
+  w.candp = c.take<int32_t>(heads * cap);
   return w;
 }
 
@@ -246,6 +274,10 @@ SelectParams select_params(const SelWs& w, const float* z, const int32_t* length
   sp.coff = w.coff;
   sp.ceqb = w.ceqb;
   sp.nsc = w.nsc;
+  sp.acnt = w.acnt;
+  sp.ccnt = w.ccnt;
+  sp.candk = w.candk;
+  sp.candp = w.candp;
   sp.err = w.err;
   return sp;
 }
@@ -448,6 +480,38 @@ static kvsel_status score_evict_impl(kvsel_dtype dt, kvsel_redundancy mode, cons
   if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
   const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap, mode);
   float* z = scores_out ? scores_out : ws.z;
+  // short caches, key-sum form: the whole step in one launch when its grid
+  // fits on the device at once
+  if (mode == KVSEL_R_KEYSUM && dt == KVSEL_BF16 && d == 128 && (hq / hkv) * w <= 32 &&
+      (cap + kChunk - 1) / kChunk <= kFusedMaxChunks) {
+    FusedParams fp{};
+    fp.q = static_cast<const char*>(q_window);
+    fp.k = static_cast<const char*>(k);
+    fp.v = static_cast<const char*>(v);
+    fp.lengths = lengths;
+    fp.b = b;
+    fp.hq = hq;
+    fp.hkv = hkv;
+    fp.g = hq / hkv;
+    fp.w = w;
+    fp.m = fp.g * w;
+    fp.cap = cap;
+    fp.budget = budget;
+    fp.cap_out = cap_out;
+    fp.scale2 = kLog2e / sqrtf((float)d);
+    fp.lambda = lambda;
+    fp.budgets = budgets;
+    fp.z_out = z;
+    fp.idx = idx_out;
+    fp.k_out = static_cast<char*>(k_out);
+    fp.v_out = static_cast<char*>(v_out);
+    fp.err = ws.err;
+    fp.epoch = ws.fepoch;
+    fp.flags = ws.fflags;
+    fp.pub_a = ws.fpub_a;
+    fp.pub_b = ws.fpub_b;
+    if (fused_fits(fp)) return hip_status(launch_fused(fp, stream, tr));
+  }
   uint32_t* hist = cap <= kSelectLdsKeys ? ws.sel.hist : nullptr;
   st = run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, nullptr, nullptr,
                   z, hist, ws, stream, tr);
@@ -457,6 +521,10 @@ static kvsel_status score_evict_impl(kvsel_dtype dt, kvsel_redundancy mode, cons
   sw.thr = ws.sel.thr;
   sw.coff = ws.sel.coff;
   sw.ceqb = ws.sel.ceqb;
+  sw.acnt = ws.sel.acnt;
+  sw.ccnt = ws.sel.ccnt;
+  sw.candk = ws.sel.candk;
+  sw.candp = ws.sel.candp;
   sw.nsc = ws.sel.nsc;
   sw.err = ws.err;  // set by the first score kernel; the select kernels add to it
   SelectParams sp = select_params(sw, z, lengths, b, hkv, cap, budget, idx_out);
@@ -579,6 +647,10 @@ static kvsel_status score_evict_slots_impl(kvsel_dtype dt, kvsel_redundancy mode
   sw.thr = ws.sel.thr;
   sw.coff = ws.sel.coff;
   sw.ceqb = ws.sel.ceqb;
+  sw.acnt = ws.sel.acnt;
+  sw.ccnt = ws.sel.ccnt;
+  sw.candk = ws.sel.candk;
+  sw.candp = ws.sel.candp;
   sw.nsc = ws.sel.nsc;
   sw.err = ws.err;
   SelectParams sp = select_params(sw, z, lengths, b, hkv, cap, budget, nullptr);

@@ -291,6 +291,34 @@ __device__ __forceinline__ void dma_lds4(const void* g, const void* lds_wave_bas
 
 #pragma clang diagnostic pop
 
+// Device-scope relaxed stores and loads (gfx950: global stores/loads with
+// sc1, written through to / read from the point where every XCD sees the
+// same data).  Work-groups on different XCDs exchange small records with
+// these instead of device-scope release/acquire fences, which write back or
+// invalidate the whole L2 of an XCD.  A writer waits for its stores
+// (vmem_done) before it signals, so a reader that has seen the signal reads
+// the records it was waiting for.
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_dev(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until this wave's vector memory operations (stores included) are done
+__device__ __forceinline__ void vmem_done() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); }
+
 // x * y rounded to fp32 on its own, never fused into a following add (the
 // product is the value another kernel stores and reloads)
 __device__ __forceinline__ float mul_unfused(float x, float y) {
@@ -311,7 +339,9 @@ __device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, floa
     s = 0.f;
     return;
   }
-  s = s * exp2_fast(m - mm) + s2 * exp2_fast(m2 - mm);
+  // one explicit FMA, so that every kernel that merges the same partials
+  // rounds them the same way, whatever the compiler would have fused
+  s = fmaf(s, exp2_fast(m - mm), s2 * exp2_fast(m2 - mm));
   m = mm;
 }
 

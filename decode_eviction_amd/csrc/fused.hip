@@ -1,0 +1,518 @@
+// One launch for the whole R-KV step on short caches (key-sum redundancy).
+//
+// R-KV compresses the cache while decoding (QbitAI R-KV article, section
+// "R-KV三步走": importance from the window's attention, redundancy from key
+// cosine similarity, joint eviction under a KV budget), so the step runs on
+// a small cache very often: the decode loop scores a 2176-slot cache every
+// 128 tokens.  There the separate passes (statistics, pooling, threshold,
+// compaction) are each bound by launch and memory latency, not bandwidth.
+// k_rkv_fused runs them in one grid, one 256-thread work-group per
+// 256-token chunk and head, with two per-head barriers:
+//   1. logits on the matrix cores, per-row chunk max / sum of 2^(t - max),
+//      key norms and the chunk's sum of unit keys (as k_stats);  barrier A
+//   2. every work-group merges its head's chunk partials in the same fixed
+//      order, then importance, the key-sum redundancy and Z for its tokens
+//      (as k_pool), and publishes its tokens' order-preserving score keys;
+//      barrier B
+//   3. every work-group loads the head's whole key row (at most 4096 keys)
+//      into LDS and selects there: a 2048-bin histogram of the top 11 bits,
+//      then rounds of 8 bits inside the bin that holds the B-th largest key,
+//      give the threshold key and how many of its copies are kept (lowest
+//      positions first); one scan over the row gives every kept position its
+//      ascending output slot.  Each work-group writes the slots of its own
+//      positions and copies those K rows (still in registers) and V rows
+//      (prefetched into LDS at the start).
+// The arithmetic of phases 1 and 2 is the one of k_stats / k_pool (same
+// expressions, same merge order), so the scores equal the multi-kernel
+// path's bit for bit, and the selection is exact.
+//
+// Barriers.  Values that cross work-groups are 64-bit words, the value in
+// the low half and the call's tag in the high half, written and read with
+// device-scope accesses (they pass between XCDs).  A work-group issues its
+// words, then writes a 64-bit token into its slot of the head's flag row; a
+// reader waits until the row holds the token, then reads the words and reads
+// again any whose tag is not there yet (its store was issued before the
+// flag's but may land later).  Tag and token derive from the head's epoch, a
+// counter in the workspace that each call advances by one after barrier A:
+// consecutive calls differ in the tag by construction, and the token is a
+// 64-bit hash (SplitMix64 finaliser), so what a fresh workspace holds does
+// not pass for a signal.  No initialisation kernel is needed and graph
+// replays work.  The host launches this kernel only when the whole grid fits
+// on the device at once, so every wait ends; a wait that still exceeds its
+// poll limit sets bit 2 of the error word and continues.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "scan.hpp"
+#include "tiles.hpp"
+
+namespace kvsel {
+
+constexpr int kSpinLimit = 1 << 20;
+constexpr int kFusedKeys = kFusedMaxChunks * kChunk;   // 4096
+
+// SplitMix64 finaliser (Steele, Lea and Flood's SplitMix generator): a
+// bijection of 64-bit words with good avalanche.
+__device__ __forceinline__ uint64_t mix64(uint64_t x) {
+  x += 0x9e3779b97f4a7c15ull;
+  x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
+  x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
+  return x ^ (x >> 31);
+}
+
+__device__ __forceinline__ uint64_t* flag_row(const FusedParams& p, int which, long head) {
+  return p.flags + ((long)which * p.b * p.hkv + head) * kFusedMaxChunks;
+}
+
+// This work-group's signal, once every wave has issued its tagged words.
+__device__ __forceinline__ void signal(const FusedParams& p, int which, long head, int chunk,
+                                       uint64_t tok, int tid) {
+  __syncthreads();
+  if (tid == 0) st_dev(flag_row(p, which, head) + chunk, tok);
+}
+
+// Wait (wave 0 polls) until the head's nwg work-groups have signalled.
+__device__ __forceinline__ void wait_flags(const FusedParams& p, int which, long head, int nwg,
+                                           uint64_t tok, int tid) {
+  if (tid < kWave) {
+    const uint64_t* fl = flag_row(p, which, head);
+    bool ok = false;
+    for (int it = 0; it < kSpinLimit && !ok; ++it) {
+      const uint64_t v = tid < nwg ? ld_dev(fl + tid) : tok;
+      ok = __ballot(v != tok) == 0ull;
+      if (!ok) __builtin_amdgcn_s_sleep(2);
+    }
+    if (!ok && tid == 0) atomicOr(p.err, 4);
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t v) { return ((uint64_t)tag << 32) | v; }
+
+// The value of a tagged word already read as w: read again while the tag is
+// missing.
+__device__ __forceinline__ uint32_t untag(const FusedParams& p, const uint64_t* at, uint64_t w,
+                                          uint32_t tag) {
+  for (int it = 0; (uint32_t)(w >> 32) != tag; ++it) {
+    if (it == kSpinLimit) {
+      atomicOr(p.err, 4);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    w = ld_dev(at);
+  }
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ int fused_budget(const FusedParams& p, int h) {
+  if (!p.budgets) return p.budget;
+  const int v = p.budgets[h];
+  return v < 0 ? 0 : (v > p.budget ? p.budget : v);
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
+  using G = Geo<E, D>;
+  constexpr int NC = G::kNC;
+  constexpr int LE = G::kLaneElems;
+  constexpr int PC = E::kPerChunk;
+  constexpr int RB = G::kRowBytes;
+  constexpr int NW = 4;
+  constexpr int KPT = kFusedKeys / 256;  // keys of the row per thread in phase 3
+  static_assert(RB * kChunk <= 64 * 1024, "V chunk staged in LDS");
+  static_assert(D <= 128, "unit-key sums fit the partial record");
+  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const long head = (long)bi * p.hkv + h;
+  const int c0 = chunk * kChunk;
+
+  if (chunk == 0 && h == 0 && bi == 0 && tid == 0) {
+    int f = 0;
+    for (int i = 0; i < p.b; ++i) f |= len_bad(p.lengths[i], p.cap) ? 1 : 0;
+    if (p.budgets)
+      for (int i = 0; i < p.hkv; ++i) f |= (p.budgets[i] < 0 || p.budgets[i] > p.budget) ? 2 : 0;
+    *p.err = f;
+  }
+  const int n = clamp_len(p.lengths[bi], p.cap);
+  const int B = fused_budget(p, h);
+  int32_t* out = p.idx + head * p.budget;
+  if (chunk == 0)
+    for (int t = min(n, B) + tid; t < p.budget; t += 256) out[t] = -1;
+  if (c0 >= n) return;
+  const int nwg = (n + kChunk - 1) / kChunk;
+  const uint64_t ep = ld_dev(p.epoch + head);
+  const uint32_t tag = (uint32_t)ep ^ 0x9e3779b9u;
+  const char* kb = p.k + head * (long)p.cap * RB;
+  const char* qb = p.q + ((long)bi * p.hq + (long)h * p.g) * p.w * RB;
+  uint64_t* pa = p.pub_a + head * kFusedMaxChunks * kFusedWordsA;
+
+  // V rows of the chunk into LDS (rows past cap arrive as zeros), for the
+  // gather at the end
+  __shared__ __attribute__((aligned(16))) char vl[kChunk * RB];
+  {
+    const __amdgpu_buffer_rsrc_t rv =
+        buf_rsrc(p.v + (head * p.cap + c0) * (long)RB, (uint32_t)(p.cap - c0) * RB);
+    constexpr int PER_WAVE = kChunk * RB / (NW * 1024);
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int off = (wave * PER_WAVE + u) * 1024;
+      buf_lds16(rv, vl + off, (uint32_t)(off + 16 * lane));
+    }
+  }
+  using QSt = QStage<E, D, 1>;
+  __shared__ u32x4_t qs[QSt::kWords];
+  QSt::issue(qs, qb, p.m, tid);
+  const int tok0 = c0 + wave * 64;
+  Frag<NC> kf[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tok = tok0 + 32 * tt + l32;
+    load_frag<E, D>(kf[tt], kb, tok, tok < n, hf);
+  }
+
+  // ---- phase 1: chunk statistics and unit-key sums (k_stats' arithmetic)
+  const float sc2 = p.scale2;
+  __shared__ float2 wst[NW][32];
+  __shared__ float red[256 * PC];
+  QSt::landed(qs, tid);
+  __syncthreads();
+  f32x16_t a[2];
+  a[0] = zero16();
+  a[1] = zero16();
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const u32x4_t qc = QSt::chunk(qs, 0, l32, hf, j);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) a[tt] = mfma_chunk<E>(kf[tt].c[j], qc, a[tt]);
+  }
+  float sqs[2];
+  {
+    float inv[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sqs[tt] = frag_sumsq<E, NC>(kf[tt]);
+      float ss = sqs[tt];
+      ss += xor32(ss);
+      inv[tt] = inv_norm_of(ss);
+    }
+    float v[LE / 2];
+    {
+      const bool up = (l32 & 16) != 0;
+#pragma unroll
+      for (int i = 0; i < LE / 2; ++i) {
+        const int j = i / PC, e = i % PC;
+        const float lo = fmaf(inv[0], frag_elem<E>(kf[0].c[j], e), inv[1] * frag_elem<E>(kf[1].c[j], e));
+        const float hi = fmaf(inv[0], frag_elem<E>(kf[0].c[j + NC / 2], e),
+                         inv[1] * frag_elem<E>(kf[1].c[j + NC / 2], e));
+        v[i] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, 16, 64);
+      }
+    }
+    scatter_down<LE / 2, 8, PC>(v, l32);
+    constexpr int R = 32 / NC;
+    float* mine = red + (wave * 64 + lane) * PC;
+#pragma unroll
+    for (int e = 0; e < PC; ++e) mine[e] = v[e];
+    __syncthreads();
+    if (tid < D) {
+      const int ch = tid / PC, e = tid % PC, hfd = ch & 1, j = ch >> 1;
+      float s = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv)
+#pragma unroll
+        for (int q = 0; q < R; ++q) s += red[(wv * 64 + hfd * 32 + j * R + q) * PC + e];
+      st_dev(pa + chunk * kFusedWordsA + 64 + tid, tagged(tag, __float_as_uint(s)));
+    }
+  }
+  {
+    const bool full = tok0 + 63 <= n - 1;
+    const int rel = n - 1 - (tok0 + 4 * hf);
+    float m = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool ok = full || 32 * tt + 8 * (i >> 2) + (i & 3) <= rel;
+        m = ok ? fmaxf(m, a[tt][i]) : m;
+      }
+    m = fmaxf(m, xor32(m));
+    const float m2 = m * sc2;
+    float s = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool ok = full || 32 * tt + 8 * (i >> 2) + (i & 3) <= rel;
+          const float e = exp2_fast(fmaf(a[tt][i], sc2, -m2));
+          s += ok ? e : 0.f;
+        }
+    }
+    s += xor32(s);
+    if (hf == 0) wst[wave][l32] = make_float2(m2, s);
+  }
+  __syncthreads();
+  if (tid < 32) {
+    float m = -INFINITY, s = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) softmax_merge(m, s, wst[wv][tid].x, wst[wv][tid].y);
+    st_dev(pa + chunk * kFusedWordsA + 2 * tid, tagged(tag, __float_as_uint(m)));
+    st_dev(pa + chunk * kFusedWordsA + 2 * tid + 1, tagged(tag, __float_as_uint(s)));
+  }
+  signal(p, 0, head, chunk, mix64(2 * ep + 1), tid);
+  wait_flags(p, 0, head, nwg, mix64(2 * ep + 1), tid);
+  if (chunk == 0 && tid == 0) st_dev(p.epoch + head, ep + 1);  // every work-group has read ep
+
+  // ---- phase 2: merged statistics, importance, redundancy, Z (k_pool's arithmetic)
+  __shared__ float2 rs[32];
+  __shared__ __attribute__((aligned(16))) float ssh[D];
+  if (tid < 32) {
+    uint64_t cw[2 * kFusedMaxChunks];
+#pragma unroll
+    for (int u = 0; u < kFusedMaxChunks; ++u) {
+      const uint64_t* at = pa + min(u, nwg - 1) * kFusedWordsA + 2 * tid;
+      cw[2 * u] = ld_dev(at);
+      cw[2 * u + 1] = ld_dev(at + 1);
+    }
+    float m = -INFINITY, s = 0.f;
+#pragma unroll
+    for (int u = 0; u < kFusedMaxChunks; ++u)
+      if (u < nwg) {
+        const uint64_t* at = pa + u * kFusedWordsA + 2 * tid;
+        const float cm = __uint_as_float(untag(p, at, cw[2 * u], tag));
+        const float cs = __uint_as_float(untag(p, at + 1, cw[2 * u + 1], tag));
+        softmax_merge(m, s, cm, cs);
+      }
+    const float2 v = make_float2(m, s > 0.f ? 1.0f / s : 0.f);
+    rs[tid] = tid < p.m ? v : make_float2(0.f, 0.f);
+  }
+  if (tid < D) {
+    // the order k_pool merges them in: group g of 1024 / D takes chunks g,
+    // g + 1024 / D, ...; the groups are added in turn
+    constexpr int GD = 1024 / D, F = kFusedMaxChunks;
+    uint64_t cw[F];
+#pragma unroll
+    for (int u = 0; u < F; ++u) cw[u] = ld_dev(pa + min(u, nwg - 1) * kFusedWordsA + 64 + tid);
+    float c[F];
+#pragma unroll
+    for (int u = 0; u < F; ++u)
+      c[u] = u < nwg ? __uint_as_float(untag(p, pa + u * kFusedWordsA + 64 + tid, cw[u], tag)) : 0.f;
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < GD; ++g) {
+      float ag = 0.f;
+#pragma unroll
+      for (int ci = g; ci < F; ci += GD) ag += ci < nwg ? c[ci] : 0.f;
+      s += ag;
+    }
+    ssh[tid] = s;
+  }
+  __syncthreads();
+  float dots[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int q = 0; q < PC / 4; ++q) {
+      const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(&ssh[frag_dim<E>(j, 4 * q, hf)]);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dots[tt] = fmaf(frag_elem<E>(kf[tt].c[j], 4 * q + e), s4[e], dots[tt]);
+      if ((j * (PC / 4) + q) % 4 == 3) asm volatile("" : "+v"(dots[0]), "+v"(dots[1])::"memory");
+    }
+  const float inv_m = 1.0f / (float)p.m;
+  const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
+  uint64_t* pb = p.pub_b + head * p.cap;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    f32x16_t c = zero16();
+#pragma unroll
+    for (int j = 0; j < NC; ++j) c = mfma_chunk<E>(QSt::chunk(qs, 0, l32, hf, j), kf[tt].c[j], c);
+    float isum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float2 st = rs[tile_row(i, hf)];
+      isum = fmaf(exp2_fast(fmaf(c[i], sc2, -st.x)), st.y, isum);
+    }
+    isum += xor32(isum);
+    const float imp = isum * inv_m;
+    float ss = sqs[tt];
+    ss += xor32(ss);
+    const float inv = inv_norm_of(ss);
+    float dot = dots[tt];
+    dot += xor32(dot);
+    const float rd = fmaf(inv, dot, -(inv * inv) * ss) * inv_nm1;
+    const float z = fmaf(p.lambda, imp, -(1.0f - p.lambda) * rd);
+    const int tok = tok0 + 32 * tt + l32;
+    if (hf == 0 && tok < n) {
+      p.z_out[head * p.cap + tok] = z;
+      if (n > B && B > 0) st_dev(pb + tok, tagged(tag, score_key(z)));
+    }
+  }
+
+  // ---- output slots of this chunk's tokens (-1: evicted), then the copies
+  __shared__ int32_t sl[kChunk];
+  auto gather = [&]() {
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int lt = wave * 64 + 32 * tt + l32;
+      const int slot = sl[lt];
+      if (slot >= 0) {
+        char* ko = p.k_out + (head * p.cap_out + slot) * (long)RB;
+        char* vo = p.v_out + (head * p.cap_out + slot) * (long)RB;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+          const int off = (2 * j + hf) * 16;
+          *reinterpret_cast<u32x4_t*>(ko + off) = kf[tt].c[j];
+          *reinterpret_cast<u32x4_t*>(vo + off) = *reinterpret_cast<const u32x4_t*>(vl + lt * RB + off);
+        }
+      }
+    }
+  };
+  if (B == 0) return;
+  if (n <= B) {  // everything is kept, in place
+    const int pos = c0 + tid;
+    sl[tid] = pos < n ? pos : -1;
+    if (pos < n) out[pos] = pos;
+    gather();
+    return;
+  }
+  signal(p, 1, head, chunk, mix64(2 * ep + 2), tid);
+  wait_flags(p, 1, head, nwg, mix64(2 * ep + 2), tid);
+
+  // ---- phase 3: the head's keys in LDS, the threshold, slots of this chunk
+  __shared__ uint32_t kall[kFusedKeys];
+  __shared__ uint32_t lh[kHistBins];
+  __shared__ uint32_t rh[256];
+  __shared__ uint32_t wsum[NW];
+  __shared__ uint32_t bc[4];
+  {
+    uint64_t kw[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) kw[i] = ld_dev(pb + min(tid + 256 * i, n - 1));
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int pos = tid + 256 * i;
+      if (pos < n) kall[pos] = untag(p, pb + pos, kw[i], tag);
+    }
+  }
+  for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
+  __syncthreads();
+  // thread t owns positions KPT t .. KPT t + KPT - 1 from here on
+  uint32_t mk[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int pos = KPT * tid + i;
+    mk[i] = pos < n ? kall[pos] : 0u;
+    if (pos < n) atomicAdd(&lh[hist_bin(mk[i])], 1u);
+  }
+  __syncthreads();
+  // level 1: the bin where the count from the top reaches B
+  uint32_t hb[8], hs = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    hb[i] = lh[8 * tid + i];
+    hs += hb[i];
+  }
+  if (tid == 0) bc[0] = bc[1] = 0u;
+  {
+    const uint2 sc = block_scan_u32<NW>(hs, wsum, tid);
+    uint32_t above = sc.y - sc.x - hs;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      if (above < (uint32_t)B && above + hb[i] >= (uint32_t)B) {
+        bc[0] = 8 * tid + i;
+        bc[1] = above;
+      }
+      above += hb[i];
+    }
+    __syncthreads();
+  }
+  uint32_t lo = bc[0] << (32 - kHistBits);
+  uint32_t hi = lo | ((1u << (32 - kHistBits)) - 1u);
+  uint32_t need = (uint32_t)B - bc[1];
+  // rounds of 8 bits inside the bin until one key value remains
+  while (lo < hi) {
+    const uint32_t span = hi - lo;
+    const int bits = 32 - __clz(span);
+    const int shift = bits > 8 ? bits - 8 : 0;
+    const int nb = (int)(span >> shift) + 1;
+    rh[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const uint32_t off = mk[i] - lo;
+      if (KPT * tid + i < n && off <= span) atomicAdd(&rh[off >> shift], 1u);
+    }
+    __syncthreads();
+    const uint32_t c = tid < nb ? rh[tid] : 0u;
+    const uint2 sc = block_scan_u32<NW>(c, wsum, tid);
+    const uint32_t above = sc.y - sc.x - c;
+    if (above < need && above + c >= need) {
+      bc[0] = tid;
+      bc[1] = above;
+    }
+    __syncthreads();
+    const uint32_t bin = bc[0];
+    need -= bc[1];
+    const uint64_t nlo = (uint64_t)lo + ((uint64_t)bin << shift);
+    const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
+    lo = (uint32_t)nlo;
+    hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+    __syncthreads();
+  }
+  const uint32_t kth = lo, need_eq = need;  // keys above kth all kept; need_eq copies of kth
+  {
+    uint32_t cg = 0, ce = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const bool ok = KPT * tid + i < n;
+      cg += (ok && mk[i] > kth) ? 1u : 0u;
+      ce += (ok && mk[i] == kth) ? 1u : 0u;
+    }
+    const uint2 sc = block_scan_u32<NW>(cg | (ce << 16), wsum, tid);
+    uint32_t gtb = sc.x & 0xffffu, eqb = sc.x >> 16;
+    // this chunk's positions are owned by threads c0 / KPT .. (c0 + kChunk) / KPT - 1
+    const bool mine = KPT * tid >= c0 && KPT * tid < c0 + kChunk;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int pos = KPT * tid + i;
+      const bool ok = pos < n;
+      int slot = -1;
+      if (ok && mk[i] > kth) {
+        slot = (int)(gtb + min(eqb, need_eq));
+        ++gtb;
+      } else if (ok && mk[i] == kth) {
+        if (eqb < need_eq) slot = (int)(gtb + eqb);
+        ++eqb;
+      }
+      if (mine) {
+        sl[pos - c0] = slot;
+        if (slot >= 0) out[slot] = pos;
+      }
+    }
+  }
+  gather();
+}
+
+static int g_fused_capacity[64];
+
+bool fused_fits(const FusedParams& p) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (g_fused_capacity[dev] == 0) {
+    int per_cu = 0, ncu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_rkv_fused<BF16, 128>, 256, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return false;
+    g_fused_capacity[dev] = per_cu * ncu > 0 ? per_cu * ncu : -1;
+  }
+  const long grid = (long)((p.cap + kChunk - 1) / kChunk) * p.hkv * p.b;
+  return g_fused_capacity[dev] > 0 && grid <= g_fused_capacity[dev];
+}
+
+hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr) {
+  const dim3 grid((p.cap + kChunk - 1) / kChunk, p.hkv, p.b);
+  return launch_k(k_rkv_fused<BF16, 128>, grid, dim3(256), s, tr, p);
+}
+
+}  // namespace kvsel

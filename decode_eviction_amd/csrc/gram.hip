@@ -833,7 +833,7 @@ __global__ __launch_bounds__(256) void k_gram_fin(GramParams p) {
   if (p.hist) {
     __syncthreads();
     for (int t = tid; t < kHistBins; t += 256)
-      if (lh[t]) atomicAdd(&p.hist[head * kHistBins + t], lh[t]);
+      if (lh[t]) atomicAdd(&p.hist[head * kHistStride + t], lh[t]);
   }
 }
 

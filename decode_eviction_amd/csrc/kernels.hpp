@@ -50,6 +50,10 @@ constexpr int kSelectLdsKeys = 32768;
 // First-level histogram of score keys: the top kHistBits bits.
 constexpr int kHistBits = 11;
 constexpr int kHistBins = 1 << kHistBits;
+// Per head the histogram is followed by a few words of selection state (the
+// arrival counter of the threshold kernel's work-groups), zeroed with it.
+constexpr int kHistStride = kHistBins + 64;
+constexpr int kHistArrive = kHistBins;
 __device__ __forceinline__ uint32_t hist_bin(uint32_t key) { return key >> (32 - kHistBits); }
 
 enum ScoreMode { kModeGram = 0, kModeKeysum = 1, kModeCut = 2 };
@@ -112,7 +116,7 @@ struct ScoreParams {
   float* i_out;             // [b][Hkv][cap]
   float* r_out;             // [b][Hkv][cap] (may be null in keysum mode)
   float* z_out;             // [b][Hkv][cap]
-  uint32_t* hist;           // nullable [b][Hkv][kHistBins]: first-level key histogram of Z
+  uint32_t* hist;           // nullable [b][Hkv][kHistStride]: first-level key histogram of Z
 };
 
 struct GramParams {
@@ -125,7 +129,7 @@ struct GramParams {
   const float* i_in;        // [b][Hkv][cap]
   float* r_out;             // nullable
   float* z_out;
-  uint32_t* hist;           // nullable [b][Hkv][kHistBins]
+  uint32_t* hist;           // nullable [b][Hkv][kHistStride]
   float* rs;                // [b][Hkv][cap]  a key's own-block row sums minus its self term
   float* part;              // [b][Hkv][nsmax][cap]  column sums by block distance - 1
   int nsmax;                // slots per head: (ceil(cap / 256)) / 2, or ceil(cap / 128) when
@@ -144,12 +148,18 @@ struct SelectParams {
   const int32_t* lengths;
   int b, hkv, cap, budget;
   int32_t* idx;             // [b][Hkv][budget]
-  uint32_t* hist;           // [b][Hkv][kHistBins]: first-level key histogram of z
+  uint32_t* hist;           // [b][Hkv][kHistStride]: first-level key histogram of z
   // split select (cap <= kSelectLdsKeys): threshold per head, offsets per chunk
   uint32_t* thr;            // [b][Hkv][4]: threshold key, copies of it to keep, copies in all
   uint32_t* coff;           // [b][Hkv][nsc]: output slot of the chunk's first kept position
   uint32_t* ceqb;           // [b][Hkv][nsc]: keys equal to the threshold before the chunk
   int nsc;                  // ceil(cap / kSelChunk)
+  // threshold kernel, per chunk: keys above the first-level bin, and the
+  // bin's keys (candidates) with their positions, at the chunk's own offset
+  uint32_t* acnt;           // [b][Hkv][nsc]
+  uint32_t* ccnt;           // [b][Hkv][nsc]
+  uint32_t* candk;          // [b][Hkv][cap]
+  int32_t* candp;           // [b][Hkv][cap]
   // fused gather (k == nullptr: indices only)
   const char* k;
   const char* v;
@@ -217,6 +227,34 @@ struct CutCompactParams {
   int b, hkv, cap, cap_out, n_sink;
 };
 
+// One-launch R-KV step for short caches (fused.hip): key-sum redundancy,
+// bf16 keys of 128 dimensions, at most 32 window rows per KV head and at most
+// kFusedMaxChunks chunks of kChunk tokens per head, every work-group of the
+// grid resident at once (the host checks the grid against the device's
+// capacity for this kernel before choosing it).
+constexpr int kFusedMaxChunks = 16;
+constexpr int kFusedWordsA = 64 + 128;  // per chunk: 32 row (max, sum) pairs, 128 unit-key sums
+struct FusedParams {
+  const char* q;            // [b][Hq][w][d]
+  const char* k;            // [b][Hkv][cap][d]
+  const char* v;
+  const int32_t* lengths;
+  int b, hq, hkv, g, w, m;  // m = g*w <= 32
+  int cap, budget, cap_out;
+  float scale2, lambda;
+  const int32_t* budgets;   // nullable [Hkv]
+  float* z_out;             // [b][Hkv][cap]
+  int32_t* idx;             // [b][Hkv][budget]
+  char* k_out;              // [b][Hkv][cap_out][d]
+  char* v_out;
+  int32_t* err;
+  // workspace
+  uint64_t* epoch;          // [b][Hkv]: advanced by one every call
+  uint64_t* flags;          // [2][b][Hkv][kFusedMaxChunks]: barrier tokens
+  uint64_t* pub_a;          // [b][Hkv][kFusedMaxChunks][kFusedWordsA]: tagged chunk partials
+  uint64_t* pub_b;          // [b][Hkv][cap]: tagged score keys
+};
+
 // Optional per-kernel timing: the k-th kernel an entry point launches records
 // ev[2k] when it starts and ev[2k+1] when it ends (hipExtLaunchKernelGGL).
 struct Trace {
@@ -253,5 +291,9 @@ hipError_t launch_cut_energy(const CutParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_cut_scan(const CutParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_cut_full(const CutParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_cut_compact(int dt, int d, const CutCompactParams& p, hipStream_t s, Trace* tr);
+// the fused short-cache step: false when the grid does not fit on the device
+// at once (then nothing is launched)
+bool fused_fits(const FusedParams& p);
+hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr);
 
 }  // namespace kvsel

@@ -24,77 +24,9 @@
 // owns one token and reduces over rows in registers (plus one lane swap).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tiles.hpp"
 
 namespace kvsel {
-
-__device__ __forceinline__ f32x16_t zero16() {
-  f32x16_t z;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = 0.f;
-  return z;
-}
-
-// One reduce-scatter step over lanes l and l ^ M of a 32-lane half: the
-// lane with bit M set keeps the upper half of v (summed with its partner's),
-// the other the lower half.
-template <int L, int M>
-__device__ __forceinline__ void scatter_step(float* v, int l32) {
-  const bool up = (l32 & M) != 0;
-#pragma unroll
-  for (int i = 0; i < L / 2; ++i) {
-    const float send = up ? v[i] : v[L / 2 + i];
-    const float keep = up ? v[L / 2 + i] : v[i];
-    v[i] = keep + __shfl_xor(send, M, 64);
-  }
-}
-// Repeat until PC values are left: with NC chunks per lane the lane then holds
-// chunk (l32 / (32 / NC)) of its half, summed over the lanes that differ from
-// it in the upper log2(NC) bits of l32.
-template <int L, int M, int PC>
-__device__ __forceinline__ void scatter_down(float* v, int l32) {
-  if constexpr (L > PC) {
-    scatter_step<L, M>(v, l32);
-    scatter_down<L / 2, M / 2, PC>(v, l32);
-  }
-}
-
-// The MT*32 query rows of a head are the same for the four waves of a
-// work-group.  Where they fit they are copied once into LDS, straight from
-// global memory (no registers), and the matrix-core loops read them a chunk
-// at a time.  Chunk c of row r sits at slot r*QC + (c ^ (r mod QC)), so the
-// 16 lanes of a group reading one chunk of 16 consecutive rows hit distinct
-// banks.  Rows >= m lie past the buffer's range and arrive as zeros.
-template <typename E, int D, int MT>
-struct QStage {
-  static constexpr int QC = Geo<E, D>::kChunks;  // 16-byte chunks per row
-  static constexpr int SLOTS = MT * 32 * QC;
-  static_assert(SLOTS % 256 == 0, "whole work-group copies");
-  static constexpr bool kLds = SLOTS * 16 <= 40 * 1024;
-  static constexpr int kWords = kLds ? SLOTS : 1;
-  // issue the copies; the caller calls landed() and then synchronises
-  static __device__ __forceinline__ void issue(u32x4_t* qs, const char* qb, int m, int tid) {
-    const auto qr = buf_rsrc(qb, (uint32_t)m * Geo<E, D>::kRowBytes);
-#pragma unroll
-    for (int u = 0; u < SLOTS / 256; ++u) {
-      const int sl = 256 * u + tid, r = sl / QC, c = (sl % QC) ^ (r % QC);
-      buf_lds16(qr, qs + 256 * u + (tid & ~63), (uint32_t)r * Geo<E, D>::kRowBytes + 16 * c);
-    }
-  }
-  // Reads back one word of each of this thread's copies before the barrier:
-  // the compiler then waits for exactly those copies (not for loads issued
-  // after them), and the barrier makes every wave's copies visible.
-  static __device__ __forceinline__ void landed(const u32x4_t* qs, int tid) {
-    uint32_t x = 0;
-#pragma unroll
-    for (int u = 0; u < SLOTS / 256; ++u) x |= reinterpret_cast<const uint32_t*>(qs + 256 * u + tid)[0];
-    asm volatile("" ::"v"(x));
-  }
-  // chunk j of row 32t + l32 for lane half hf (the chunk load_frag puts in c[j])
-  static __device__ __forceinline__ u32x4_t chunk(const u32x4_t* qs, int t, int l32, int hf, int j) {
-    const int r = 32 * t + l32;
-    return qs[r * QC + ((2 * j + hf) ^ (r % QC))];
-  }
-};
 
 // Four waves per SIMD (every work-group of a 32K-token head resident at
 // once) where the two key tiles leave room for it; fp32 keys of 128
@@ -121,9 +53,9 @@ void k_stats(ScoreParams p) {
     for (int i = 0; i < p.b; ++i) f |= len_bad(p.lengths[i], p.cap) ? 1 : 0;
     *p.err = f;
   }
-  if (p.hist && blockIdx.x == 0)  // the later passes accumulate into it
-    for (int t = tid; t < kHistBins; t += 256)
-      p.hist[((long)blockIdx.z * p.hkv + blockIdx.y) * kHistBins + t] = 0u;
+  if (p.hist && blockIdx.x == 0)  // the later passes accumulate into it (selection state with it)
+    for (int t = tid; t < kHistStride; t += 256)
+      p.hist[((long)blockIdx.z * p.hkv + blockIdx.y) * kHistStride + t] = 0u;
   int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   if (p.b > 1 && p.b <= kActiveFirstMaxB && !active_chunk(p.lengths, p.b, p.hkv, p.cap, p.nchunk, bi, h, chunk))
     return;
@@ -176,9 +108,9 @@ void k_stats(ScoreParams p) {
   #pragma unroll
           for (int i = 0; i < LE / 2; ++i) {
             const int j = i / PC, e = i % PC;
-            const float lo = inv[0] * frag_elem<E>(kf[0].c[j], e) + inv[1] * frag_elem<E>(kf[1].c[j], e);
-            const float hi = inv[0] * frag_elem<E>(kf[0].c[j + NC / 2], e) +
-                             inv[1] * frag_elem<E>(kf[1].c[j + NC / 2], e);
+            const float lo = fmaf(inv[0], frag_elem<E>(kf[0].c[j], e), inv[1] * frag_elem<E>(kf[1].c[j], e));
+            const float hi = fmaf(inv[0], frag_elem<E>(kf[0].c[j + NC / 2], e),
+                             inv[1] * frag_elem<E>(kf[1].c[j + NC / 2], e));
             v[i] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, 16, 64);
           }
         }
@@ -643,8 +575,8 @@ void k_pool(ScoreParams p) {
       const float inv = inv_norm_of(ss);
       float dot = dots[tt];
       dot += xor32(dot);
-      const float red = (inv * dot - inv * inv * ss) * inv_nm1;
-      const float z = p.lambda * imp - (1.0f - p.lambda) * red;
+      const float red = fmaf(inv, dot, -(inv * inv) * ss) * inv_nm1;
+      const float z = fmaf(p.lambda, imp, -(1.0f - p.lambda) * red);
       if (hf == 0 && tok < n) {
         p.i_out[o] = imp;
         if (p.r_out) p.r_out[o] = red;
@@ -657,7 +589,7 @@ void k_pool(ScoreParams p) {
     if (p.hist) {
       __syncthreads();
       for (int t = tid; t < kHistBins; t += 256)
-        if (lh[t]) atomicAdd(&p.hist[head * kHistBins + t], lh[t]);
+        if (lh[t]) atomicAdd(&p.hist[head * kHistStride + t], lh[t]);
     }
   }
 }

@@ -21,39 +21,12 @@
 // k_gather: bit copies of the kept K and V rows, 16 bytes per lane.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "scan.hpp"
 
 namespace kvsel {
 
 constexpr int kSelBins = 2048;
-constexpr int kSelWaves = kSelectThreads / kWave;
 constexpr int kLoadUnroll = 8;
-
-__device__ __forceinline__ uint32_t lanemask_lt_count(uint64_t m, int lane) {
-  return (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-}
-
-// exclusive prefix sum over the NW*64 threads of the block; returns (prefix, total)
-template <int NW = kSelWaves>
-__device__ __forceinline__ uint2 block_scan_u32(uint32_t v, uint32_t* wsum, int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  uint32_t before = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t t = wsum[w];
-    before += w < wave ? t : 0u;
-    total += t;
-  }
-  __syncthreads();
-  return make_uint2(before + x - v, total);
-}
 
 // Budget of KV head h: the scalar budget, or budgets[h] clamped to
 // [0, budget] (budget is then the row stride of the outputs).
@@ -211,25 +184,24 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(SelectParams p) {
 // Split select for cap <= 32768.
 //
 // The kernels that produce Z also count its keys into a first-level
-// histogram on the top kHistBits bits (hist).  k_select_thresh (one
-// 1024-thread work-group per head) finds the bin holding the B-th largest key
-// from that histogram, then refines inside the bin: thread t holds the keys of
-// positions t + 1024 i (i < 32) in registers.  The level-1 bin holds a small
-// share of the keys (its size is known from the histogram): those keys and
-// their positions are compacted into LDS with ballots, and the remaining radix
-// rounds touch only them.  A bin too large for LDS (many ties) is refined over
-// the register keys instead.  It then
-// counts, per 512-position chunk, the keys above the threshold and equal to
-// it, and writes each chunk's first output slot.  k_compact (one 256-thread
-// work-group per chunk and head) gives every kept position its ascending
-// output slot with one block scan of packed (greater, equal) counts and copies
-// the kept K and V rows (the gather is fused).
+// histogram on the top kHistBits bits (hist).  k_select_thresh runs one
+// 256-thread work-group per 512-position chunk and head: every work-group
+// reads the head's histogram and finds the bin b1 where the count from the
+// top reaches B (the same bin in all of them), counts its chunk's keys above
+// b1 and writes the chunk's keys inside b1 (the candidates, with their
+// positions) to the chunk's own part of a candidate buffer.  It then adds one
+// to the head's arrival counter; the work-group that arrives last refines the
+// threshold over the head's candidates (radix rounds of 8 bits on an LDS
+// histogram until at most 64 candidates remain, then an exact rank), counts
+// per chunk the keys above the threshold and equal to it, and writes each
+// chunk's first output slot.  No work-group waits for another.  k_compact
+// (one 256-thread work-group per chunk and head) gives every kept position
+// its ascending output slot with one block scan of packed (greater, equal)
+// counts and copies the kept K and V rows (the gather is fused).
 constexpr int kRegThreads = 1024;
 constexpr int kRegWaves = kRegThreads / kWave;
 constexpr int kKeysPerThread = kSelectLdsKeys / kRegThreads;   // 32
 constexpr int kChunksPerRound = kRegThreads / kSelChunk;       // 2
-
-constexpr int kCandMax = 8192;   // candidates refined in LDS; larger bins use the register path
 
 // Per-chunk offsets from per-chunk (greater, equal) counts; run by wave 0,
 // lane c = chunk c (at most 64 chunks).
@@ -310,7 +282,290 @@ __device__ __forceinline__ void refine_round(uint32_t& lo, uint32_t& hi, uint32_
   hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
 }
 
-__global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
+
+constexpr int kCandLds = 4096;   // candidates the finishing work-group stages in LDS
+
+__global__ __launch_bounds__(256) void k_select_thresh(SelectParams p) {
+  constexpr int NT = 256, NW = NT / kWave;
+  __shared__ uint32_t rh[256];                 // refinement histogram
+  __shared__ uint32_t ck[kCandLds];
+  __shared__ int32_t cpo[kCandLds];
+  __shared__ uint32_t wsum[2][NW];
+  __shared__ uint32_t cpre[65];                // prefix of the per-chunk candidate counts
+  __shared__ uint32_t cgt[64], ceq[64];        // per chunk: keys above / equal to the threshold
+  __shared__ uint32_t rk[kWave];
+  __shared__ int32_t rp[kWave];
+  __shared__ uint32_t bc[4];
+  __shared__ int last_s;
+
+  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long head = (long)bi * p.hkv + h;
+  uint32_t* hg = p.hist + head * kHistStride;
+  const int c0 = chunk * kSelChunk;
+  // the histogram (8 bins per thread) and the chunk's scores (positions past
+  // cap read 0) are requested before the length arrives
+  const uint4 hv0 = reinterpret_cast<const uint4*>(hg)[2 * tid];
+  const uint4 hv1 = reinterpret_cast<const uint4*>(hg)[2 * tid + 1];
+  uint32_t zr[2];
+  {
+    const __amdgpu_buffer_rsrc_t rz = buf_rsrc(p.z + head * p.cap, (uint32_t)p.cap * 4u);
+    zr[0] = buf_ld32(rz, (uint32_t)(c0 + tid) * 4u, 0);
+    zr[1] = buf_ld32(rz, (uint32_t)(c0 + NT + tid) * 4u, 0);
+  }
+  const int n = clamp_len(p.lengths[bi], p.cap);
+  const int B = head_budget(p, h);
+  if (chunk == 0 && tid == 0) flag_select_errors(p, h, bi);
+  if (n <= B || B == 0 || c0 >= n) return;  // k_compact keeps everything (or nothing)
+  const int nch = (n + kSelChunk - 1) / kSelChunk;
+
+  // level 1: the bin where the count from the top reaches B; thread t holds
+  // bins 8t .. 8t+7 and the count of keys above them
+  const uint32_t hb[8] = {hv0.x, hv0.y, hv0.z, hv0.w, hv1.x, hv1.y, hv1.z, hv1.w};
+  uint32_t hs = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) hs += hb[i];
+  if (tid == 0) bc[0] = bc[1] = 0u;
+  {
+    const uint2 sc = block_scan_u32<NW>(hs, wsum[0], tid);  // (exclusive prefix, total)
+    uint32_t above = sc.y - sc.x - hs;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      if (above < (uint32_t)B && above + hb[i] >= (uint32_t)B) {
+        bc[0] = 8 * tid + i;
+        bc[1] = above;
+      }
+      above += hb[i];
+    }
+    __syncthreads();
+  }
+  const uint32_t b1 = bc[0];
+  const uint32_t need1 = (uint32_t)B - bc[1];  // keys still to take from bin b1
+
+  // this chunk: keys above b1 (counted) and keys in b1 (written out)
+  uint32_t key[2];
+  bool in[2];
+  uint32_t gt = 0;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int pos = c0 + e * NT + tid;
+    key[e] = score_key(__uint_as_float(zr[e]));
+    const uint32_t kb = hist_bin(key[e]);
+    const bool ok = pos < n;
+    gt += (ok && kb > b1) ? 1u : 0u;
+    in[e] = ok && kb == b1;
+  }
+  const uint64_t m0 = __ballot(in[0]), m1 = __ballot(in[1]);
+  uint32_t gtw = gt;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) gtw += __shfl_xor(gtw, o, 64);
+  if (lane == 0) {
+    wsum[0][wave] = (uint32_t)(__popcll(m0) + __popcll(m1));
+    wsum[1][wave] = gtw;
+  }
+  __syncthreads();
+  uint32_t wbase = 0, ncand = 0, agt = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    wbase += w < wave ? wsum[0][w] : 0u;
+    ncand += wsum[0][w];
+    agt += wsum[1][w];
+  }
+  // publish (device-scope stores), wait for them, then arrive; the last of
+  // the head's nch work-groups finishes
+  const long cbase = head * p.cap + c0;
+  if (in[0]) {
+    const uint32_t slot = wbase + lanemask_lt_count(m0, lane);
+    st_dev(p.candk + cbase + slot, key[0]);
+    st_dev(p.candp + cbase + slot, c0 + tid);
+  }
+  if (in[1]) {
+    const uint32_t slot = wbase + (uint32_t)__popcll(m0) + lanemask_lt_count(m1, lane);
+    st_dev(p.candk + cbase + slot, key[1]);
+    st_dev(p.candp + cbase + slot, c0 + NT + tid);
+  }
+  if (tid == 0) {
+    st_dev(p.ccnt + head * p.nsc + chunk, ncand);
+    st_dev(p.acnt + head * p.nsc + chunk, agt);
+  }
+  vmem_done();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(hg + kHistArrive, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    last_s = old == (uint32_t)(nch - 1);
+  }
+  __syncthreads();
+  if (!last_s) return;
+
+  // ---- the head's last work-group: per-chunk counts and candidates
+  if (wave == 0) {
+    const uint32_t cc = lane < nch ? ld_dev(p.ccnt + head * p.nsc + lane) : 0u;
+    const uint32_t ac = lane < nch ? ld_dev(p.acnt + head * p.nsc + lane) : 0u;
+    uint32_t x = cc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    cpre[lane + 1] = x;
+    if (lane == 0) cpre[0] = 0u;
+    cgt[lane] = ac;
+    ceq[lane] = 0u;
+  }
+  __syncthreads();
+  const uint32_t nc = cpre[nch];
+  const bool staged = nc <= (uint32_t)kCandLds;
+  // candidate i: chunk c with cpre[c] <= i < cpre[c+1], entry i - cpre[c]
+  auto cand_src = [&](uint32_t i) -> long {
+    int lo = 0, hi = nch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cpre[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    return head * p.cap + (long)lo * kSelChunk + (i - cpre[lo]);
+  };
+  if (staged) {
+    for (uint32_t i0 = tid; i0 < nc; i0 += 4 * NT) {
+      uint32_t kk[4];
+      int32_t pp[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t i = i0 + u * NT;
+        const long src = cand_src(i < nc ? i : nc - 1);
+        kk[u] = ld_dev(p.candk + src);
+        pp[u] = ld_dev(p.candp + src);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t i = i0 + u * NT;
+        if (i < nc) {
+          ck[i] = kk[u];
+          cpo[i] = pp[u];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // visit(f): f(key, pos) for every candidate, from LDS or (a bin too large
+  // for LDS) from the candidate buffer, eight loads in flight per thread
+  auto visit = [&](auto f) {
+    if (staged) {
+      for (uint32_t i = tid; i < nc; i += NT) f(ck[i], cpo[i]);
+      return;
+    }
+    for (uint32_t i0 = tid; i0 < nc; i0 += 8 * NT) {
+      uint32_t kk[8];
+      int32_t pp[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t i = i0 + u * NT;
+        const long src = cand_src(i < nc ? i : nc - 1);
+        kk[u] = ld_dev(p.candk + src);
+        pp[u] = ld_dev(p.candp + src);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u * NT < nc) f(kk[u], pp[u]);
+    }
+  };
+
+  // refinement inside bin b1: rounds of 8 bits until at most 64 candidates
+  // remain in [lo, hi]
+  uint32_t lo = b1 << (32 - kHistBits);
+  uint32_t hi = lo | ((1u << (32 - kHistBits)) - 1u);
+  uint32_t need = need1, inr = nc;
+  while (lo < hi && inr > (uint32_t)kWave) {
+    const uint32_t span = hi - lo;
+    const int bits = 32 - __clz(span);
+    const int shift = bits > 8 ? bits - 8 : 0;
+    const int nb = (int)(span >> shift) + 1;
+    rh[tid] = 0u;
+    __syncthreads();
+    visit([&](uint32_t k, int32_t) {
+      const uint32_t off = k - lo;
+      if (off <= span) atomicAdd(&rh[off >> shift], 1u);
+    });
+    __syncthreads();
+    const uint32_t c = tid < nb ? rh[tid] : 0u;
+    const uint2 sc = block_scan_u32<NW>(c, wsum[0], tid);
+    const uint32_t above = sc.y - sc.x - c;  // candidates in bins above this one
+    if (above < need && above + c >= need) {
+      bc[0] = tid;
+      bc[1] = above;
+      bc[2] = c;
+    }
+    __syncthreads();
+    const uint32_t bin = bc[0];
+    need -= bc[1];
+    inr = bc[2];
+    const uint64_t nlo = (uint64_t)lo + ((uint64_t)bin << shift);
+    const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
+    lo = (uint32_t)nlo;
+    hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+    __syncthreads();
+  }
+  if (lo < hi) {
+    // at most 64 candidates in range: wave 0 ranks them (larger key, or
+    // equal key at a lower position, first); rank need-1 is the threshold
+    if (tid == 0) bc[3] = 0u;
+    __syncthreads();
+    visit([&](uint32_t k, int32_t pos) {
+      if (k >= lo && k <= hi) {
+        const uint32_t slot = atomicAdd(&bc[3], 1u);
+        if (slot < (uint32_t)kWave) {
+          rk[slot] = k;
+          rp[slot] = pos;
+        }
+      }
+    });
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t nr = min(bc[3], (uint32_t)kWave);
+      const uint32_t mk = lane < (int)nr ? rk[lane] : 0u;
+      const int32_t mpos = lane < (int)nr ? rp[lane] : 0x7fffffff;
+      uint32_t rank = 0;
+      for (uint32_t c = 0; c < nr; ++c) {
+        const uint32_t kc = (uint32_t)__builtin_amdgcn_readlane((int)mk, (int)c);
+        const int32_t pc = __builtin_amdgcn_readlane(mpos, (int)c);
+        rank += (kc > mk || (kc == mk && pc < mpos)) ? 1u : 0u;
+      }
+      const uint64_t who = __ballot(lane < (int)nr && rank == need - 1);
+      const uint32_t kth = __shfl(mk, __ffsll((unsigned long long)who) - 1, 64);
+      const uint32_t gtk = (uint32_t)__popcll(__ballot(lane < (int)nr && mk > kth));
+      if (lane == 0) {
+        bc[0] = kth;
+        bc[1] = need - gtk;  // copies of the threshold key still to keep
+      }
+    }
+    __syncthreads();
+    lo = hi = bc[0];
+    need = bc[1];
+  }
+  const uint32_t kth = lo;
+  // per chunk: candidates above the threshold and equal to it
+  visit([&](uint32_t k, int32_t pos) {
+    const int c = pos / kSelChunk;
+    if (k > kth) atomicAdd(&cgt[c], 1u);
+    else if (k == kth) atomicAdd(&ceq[c], 1u);
+  });
+  __syncthreads();
+  if (wave == 0) write_chunk_offsets(p, head, n, cgt[lane], ceq[lane], kth, need, lane);
+}
+
+// One 1024-thread work-group per head, for calls with many heads (the
+// per-chunk kernel above re-reads the histogram and passes candidates
+// through memory, which a grid of hundreds of heads pays for in rounds of
+// work-groups).  It finds the level-1 bin from the histogram, then refines
+// inside the bin: thread t holds the keys of positions t + 1024 i (i < 32) in
+// registers; the bin's keys (its size is known from the histogram) and their
+// positions are compacted into LDS with ballots and the remaining radix
+// rounds touch only them; a bin too large for LDS (many ties) is refined over
+// the register keys.  Then the per-chunk counts and offsets as above.
+constexpr int kCandMax = 8192;
+
+__global__ __launch_bounds__(kRegThreads) void k_select_thresh_head(SelectParams p) {
   __shared__ uint32_t hist[kSelBins];
   __shared__ uint32_t cand_key[kCandMax];
   __shared__ int32_t cand_pos[kCandMax];
@@ -326,7 +581,7 @@ __global__ __launch_bounds__(kRegThreads) void k_select_thresh(SelectParams p) {
   // the histogram and the scores are requested before the length arrives:
   // scores through a buffer resource over the cache's capacity (positions
   // past cap read 0, past n are masked below), all in flight before use
-  const uint2 c01 = reinterpret_cast<const uint2*>(p.hist + head * kHistBins)[tid];
+  const uint2 c01 = reinterpret_cast<const uint2*>(p.hist + head * kHistStride)[tid];
   uint32_t key[kKeysPerThread];
   {
     const __amdgpu_buffer_rsrc_t rz = buf_rsrc(z, (uint32_t)p.cap * 4u);
@@ -781,8 +1036,17 @@ __global__ __launch_bounds__(kRegThreads) void k_evict_slots(SelectParams p) {
   }
 }
 
+// The threshold kernel for a call: one work-group per chunk and head while
+// the grid is small, one per head (k_select_thresh_head) for many heads.
+constexpr int kThreshHeadsMany = 64;
+static hipError_t launch_thresh(const SelectParams& p, hipStream_t s, Trace* tr) {
+  if ((long)p.b * p.hkv >= kThreshHeadsMany)
+    return launch_k(k_select_thresh_head, dim3(p.hkv, p.b), dim3(kRegThreads), s, tr, p);
+  return launch_k(k_select_thresh, dim3(p.nsc, p.hkv, p.b), dim3(256), s, tr, p);
+}
+
 hipError_t launch_select_slots(const SelectParams& p, hipStream_t s, Trace* tr) {
-  hipError_t e = launch_k(k_select_thresh, dim3(p.hkv, p.b), dim3(kRegThreads), s, tr, p);
+  hipError_t e = launch_thresh(p, s, tr);
   if (e != hipSuccess) return e;
   return launch_k(k_evict_slots, dim3(p.hkv, p.b), dim3(kRegThreads), s, tr, p);
 }
@@ -827,7 +1091,7 @@ hipError_t launch_slots_write(int dt, int d, const SlotWriteParams& p, hipStream
 __global__ __launch_bounds__(256) void k_hist_zero(SelectParams p) {
   const long head = (long)blockIdx.y * p.hkv + blockIdx.x;
   if (p.err && head == 0 && threadIdx.x == 0) *p.err = 0;
-  for (int t = threadIdx.x; t < kHistBins; t += 256) p.hist[head * kHistBins + t] = 0u;
+  for (int t = threadIdx.x; t < kHistStride; t += 256) p.hist[head * kHistStride + t] = 0u;
 }
 
 __global__ __launch_bounds__(256) void k_hist(SelectParams p) {
@@ -848,7 +1112,7 @@ __global__ __launch_bounds__(256) void k_hist(SelectParams p) {
     if (c0 + e * 256 + tid < n) atomicAdd(&lh[hist_bin(score_key(zv[e]))], 1u);
   __syncthreads();
   for (int t = tid; t < kHistBins; t += 256)
-    if (lh[t]) atomicAdd(&p.hist[head * kHistBins + t], lh[t]);
+    if (lh[t]) atomicAdd(&p.hist[head * kHistStride + t], lh[t]);
 }
 
 hipError_t launch_hist(const SelectParams& p, hipStream_t s, Trace* tr) {
@@ -868,7 +1132,7 @@ hipError_t launch_select_err_zero(const SelectParams& p, hipStream_t s, Trace* t
 
 hipError_t launch_select(const SelectParams& p, hipStream_t s, Trace* tr) {
   if (p.cap <= kSelectLdsKeys) {
-    hipError_t e = launch_k(k_select_thresh, dim3(p.hkv, p.b), dim3(kRegThreads), s, tr, p);
+    hipError_t e = launch_thresh(p, s, tr);
     if (e != hipSuccess) return e;
     return launch_k(k_compact, dim3(p.nsc * std::max(p.gsplit, 1), p.hkv, p.b), dim3(256), s, tr, p);
   }

@@ -135,7 +135,12 @@ kvsel_status kvsel_gather(kvsel_dtype dt, const void* k, const void* v, const in
                           void* k_out, void* v_out, int cap_out, hipStream_t stream);
 
 /* The whole step: scores, top-budget, gather.  budget <= cap_out.
- * scores_out (nullable) receives Z as in kvsel_scores. */
+ * scores_out (nullable) receives Z as in kvsel_scores.  A short cache with
+ * the key-sum form (bf16, d = 128, g*w <= 32, cap <= 4096) runs as a single
+ * launch when its grid of ceil(cap / 256) * Hkv * b work-groups fits on the
+ * device at once (the device's capacity for that kernel is queried once per
+ * device and kept); its scores and selection are identical to the
+ * multi-kernel path's. */
 kvsel_status kvsel_score_evict(kvsel_dtype dt, kvsel_redundancy mode,
                                const void* q_window, const void* k, const void* v,
                                const int32_t* lengths, int b, int Hq, int Hkv, int d, int w,
@@ -191,7 +196,8 @@ kvsel_status kvsel_score_evict_heads(kvsel_dtype dt, kvsel_redundancy mode,
  * KVSEL_R_KEYSUM: stats, reduce, pool, threshold, compact.  For larger cap
  * the last two are replaced by select, gather.  With cap <= 4096 (at most 16
  * chunks of 256 keys per head) there is no reduce kernel: pool merges the
- * chunk partials itself. */
+ * chunk partials itself; a key-sum call that takes the single-launch path
+ * (see kvsel_score_evict) launches one kernel. */
 kvsel_status kvsel_score_evict_traced(kvsel_dtype dt, kvsel_redundancy mode,
                                       const void* q_window, const void* k, const void* v,
                                       const int32_t* lengths, int b, int Hq, int Hkv, int d,
@@ -349,7 +355,11 @@ kvsel_status kvsel_threshold_cut_from_attn(const float* attn_last, const int32_t
 /* Reads the device error word left in the workspace by the last call that
  * used it (synchronises the stream).  Bit 0: some lengths[i] lay outside
  * [0, cap] and was clamped into it; bit 1: some per-head budget lay outside
- * [0, budget_max] and was clamped.  Returns KVSEL_ERR_HIP if the copy fails. */
+ * [0, budget_max] and was clamped; bit 2: a wait between the work-groups of
+ * the single-launch short-cache step exceeded its poll limit (the results of
+ * that call are not to be trusted; it cannot happen while the device runs
+ * the whole grid at once, which the library checks before choosing that
+ * path).  Returns KVSEL_ERR_HIP if the copy fails. */
 kvsel_status kvsel_workspace_error(const void* workspace, int32_t* flags_host, hipStream_t stream);
 
 #ifdef __cplusplus

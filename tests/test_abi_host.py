@@ -179,9 +179,16 @@ def test_bench_kernel_names_follow_the_reduce_folding():
     src = open(hdr).read()
     fuse = int(re.search(r"constexpr int kFuseReduceChunks = (\d+);", src).group(1))
     chunk = int(re.search(r"constexpr int kChunk = (\d+);", src).group(1))
+    fmax = int(re.search(r"constexpr int kFusedMaxChunks = (\d+);", src).group(1))
+    assert fmax == bench.FUSED_MAX_CHUNKS
     for mode in ("gram", "keysum"):
         for cap in (1, 2176, fuse * chunk, fuse * chunk + 1, 32768):
             names = bench.rkv_kernels(mode, cap)
+            if bench.fused_step(mode, cap):
+                assert names == ["fused"] and mode == "keysum" and -(-cap // chunk) <= fmax
+                continue
             folded = -(-cap // chunk) <= fuse
             assert ("reduce" not in names) == folded, (mode, cap)
             assert [k for k in bench.KERNELS[mode] if k != "reduce"] == [k for k in names if k != "reduce"]
+    # 64 sequences of 2176 tokens: 9 * 8 * 64 work-groups do not fit at once
+    assert bench.rkv_kernels("keysum", 2176, b=64) != ["fused"]

@@ -1,0 +1,115 @@
+"""The one-launch R-KV step for short caches (key-sum form, bf16, d = 128,
+at most 32 window rows per KV head, at most 16 chunks of 256 tokens).
+
+Its scores must equal the multi-kernel path's bit for bit (kvsel_scores runs
+the separate passes with the same arithmetic and merge order), its kept set
+must be exactly the stage select's on those scores, the compacted rows bit
+copies, and no barrier may time out (bit 2 of the error word).  Repeated
+calls on one workspace exercise the barrier epochs; ragged lengths, lengths
+ending inside a chunk, n <= B, B = 0 per head and a length above cap cover
+the branches."""
+
+import numpy as np
+import pytest
+import torch
+
+from decode_eviction_amd import kvsel as K
+from decode_eviction_amd import synth
+from oracle import rkv
+from tests.gpu_util import SCORE_RTOL, dev, dev_i32, host_bits, log, score_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(case, budgets=None, reps=3):
+    q, k, v = dev(case.q, "bf16"), dev(case.k, "bf16"), dev(case.v, "bf16")
+    lens = dev_i32(case.lengths)
+    b, hkv, cap, d = case.b, case.hkv, case.cap, case.d
+    ws = torch.empty(K.kvsel_score_evict_workspace(b, case.hq, hkv, d, case.w, cap, case.budget),
+                     dtype=torch.uint8, device="cuda")
+    ws.fill_(0x5a)                                     # arbitrary contents before the first call
+    _, _, z_ref = K.kvsel_scores(q, k, lens, case.lam, "keysum")
+    outs = []
+    for rep in range(reps):
+        z = torch.full((b, hkv, cap), float("nan"), device="cuda")
+        if budgets is None:
+            ko, vo, idx = K.kvsel_score_evict(q, k, v, lens, case.budget, case.lam, "keysum",
+                                              scores_out=z, workspace=ws)
+        else:
+            ko, vo, idx = K.kvsel_score_evict_heads(q, k, v, lens, dev_i32(budgets), case.budget,
+                                                    case.lam, "keysum", scores_out=z, workspace=ws)
+        flags = K.kvsel_workspace_error(ws)
+        assert flags & 4 == 0, f"a barrier timed out (call {rep})"
+        outs.append((z.cpu().numpy(), idx.cpu().numpy(), host_bits(ko), host_bits(vo), flags))
+    return outs, z_ref.cpu().numpy()
+
+
+def _check(case, budgets=None):
+    log(f"[fused] {case.name} b={case.b} hkv={case.hkv} cap={case.cap} lengths={case.lengths.tolist()} "
+        f"B={case.budget} budgets={None if budgets is None else list(budgets)}")
+    outs, z_ref = _run(case, budgets)
+    z, idx, ko, vo, flags = outs[0]
+    for o in outs[1:]:
+        for x, y in zip(o[:4], outs[0][:4]):
+            assert np.array_equal(x, y, equal_nan=True)
+    # the same selection as the stage entry on the same scores
+    lens = np.minimum(case.lengths, case.cap)
+    want = K.kvsel_select_topb_heads(dev(z_ref, "f32"), dev_i32(lens), dev_i32(budgets), case.budget) \
+        if budgets is not None else K.kvsel_select_topb(dev(z_ref, "f32"), dev_i32(lens), case.budget)
+    want = want.cpu().numpy()
+    ref = rkv.score_evict(case.as_f32("q"), case.as_f32("k"), case.as_f32("v"), lens, case.lam,
+                          case.budget, form="keysum", budgets=budgets)
+    for b in range(case.b):
+        n = int(lens[b])
+        for h in range(case.hkv):
+            assert np.array_equal(z[b, h, :n], z_ref[b, h, :n]), (b, h)
+            assert score_err(z[b, h, :n], ref["Z"][b][h]) <= SCORE_RTOL
+            assert np.array_equal(idx[b, h], want[b, h]), (b, h)
+            m = int((idx[b, h] >= 0).sum())
+            assert np.array_equal(ko[b, h, :m], case.k[b, h, idx[b, h, :m]])
+            assert np.array_equal(vo[b, h, :m], case.v[b, h, idx[b, h, :m]])
+    return flags
+
+
+def test_fused_decode_shape():
+    case = synth.layer8b_case(4, n=2176, budget=2048, cap=2176)
+    assert _check(case) == 0
+
+
+def test_fused_full_4096():
+    assert _check(synth.layer8b_case(5, n=4096, budget=1024, cap=4096)) == 0
+
+
+def test_fused_ragged_and_small():
+    case = synth.rkv_case("fused_ragged", seed=51, wl=61, b=4, hq=8, hkv=2, d=128, w=4,
+                          lengths=[1000, 37, 256, 257], cap=1024, budget=100)
+    assert _check(case) == 0
+    case = synth.rkv_case("fused_keepall", seed=52, wl=62, b=2, hq=8, hkv=2, d=128, w=4,
+                          lengths=[90, 600], cap=640, budget=100)
+    assert _check(case) == 0
+
+
+def test_fused_per_head_budgets():
+    case = synth.rkv_case("fused_heads", seed=53, wl=63, b=2, hq=32, hkv=8, d=128, w=4,
+                          lengths=[3000, 1700], cap=3072, budget=1024)
+    budgets = np.array([1024, 0, 700, 1800, 1, 1023, 5, 2000], np.int32)  # two clamped
+    assert _check(case, budgets) == 2
+
+
+def test_fused_length_above_cap_flagged():
+    case = synth.rkv_case("fused_clamp", seed=54, wl=64, b=2, hq=8, hkv=2, d=128, w=4,
+                          lengths=[512, 400], cap=512, budget=64)
+    case.lengths[0] = 700
+    assert _check(case) == 1
+
+
+def test_fused_tied_scores_take_the_fallback():
+    # identical keys: every score is equal, more than the sample select
+    # ranks directly, so the histogram rounds decide (lowest positions kept);
+    # three groups of exact duplicates: three score values, large tied groups
+    case = synth.rkv_case("fused_ties", seed=55, wl=65, b=2, hq=32, hkv=8, d=128, w=8,
+                          lengths=[2176, 1800], cap=2176, budget=1000, frac=0.0, sink_scale=None)
+    case.k[0] = case.k[0, :, :1]                      # sequence 0: one key repeated
+    for g, (a, b_) in enumerate([(0, 700), (700, 1500), (1500, 2176)]):
+        case.k[1, :, a:b_] = case.k[1, :, a:a + 1]    # sequence 1: three repeated keys
+    assert _check(case) == 0

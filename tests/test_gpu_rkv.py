@@ -241,6 +241,35 @@ def test_select_stage_exact():
                 assert (idx[b, h, m:] == -1).all()
 
 
+def test_select_stage_exact_many_heads():
+    """64 heads or more: the threshold kernel runs one work-group per head; normal
+    scores, ties, all-equal scores (the register path for bins larger than its
+    candidate buffer) and caps below and at 32768."""
+    rng = np.random.default_rng(27)
+    for b, hkv, n, budget, kind in [(8, 8, 4000, 700, "normal"), (16, 4, 2176, 2048, "ties"),
+                                    (8, 8, 32768, 2048, "allequal"), (2, 32, 32768, 3000, "few"),
+                                    (4, 16, 9000, 1, "normal")]:
+        cap = n
+        if kind == "ties":
+            z = (rng.integers(-40, 40, size=(b, hkv, cap)) * 2.0 ** -12).astype(np.float32)
+        elif kind == "allequal":
+            z = np.full((b, hkv, cap), -0.5, np.float32)
+        elif kind == "few":
+            z = rng.choice(np.array([0.5, 0.25, 0.125], np.float32), size=(b, hkv, cap))
+        else:
+            z = rng.standard_normal((b, hkv, cap)).astype(np.float32) * 1e-3
+        lens = np.array([n - (i % 3) * (n // 5) for i in range(b)], np.int32)
+        log(f"[select many heads] b={b} hkv={hkv} n={n} B={budget} {kind}")
+        idx = K.kvsel_select_topb(dev(z, "f32"), dev_i32(lens), budget).cpu().numpy()
+        for bi in range(b):
+            for h in range(hkv):
+                nb = int(lens[bi])
+                want = rkv.top_budget(z[bi, h, :nb].astype(np.float64), budget)
+                m = min(nb, budget)
+                assert idx[bi, h, :m].tolist() == want.tolist(), (kind, bi, h)
+                assert (idx[bi, h, m:] == -1).all()
+
+
 def test_select_heads_stage_exact():
     """Per-head budgets on given scores: each head's set is the oracle's for its own budget."""
     rng = np.random.default_rng(17)
