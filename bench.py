@@ -6,7 +6,9 @@ budget B = 2048, lambda = 0.1).  Steps rotate over --layers distinct seeded
 synthetic layer caches (32 x 128 MiB of K+V, beyond the 256 MB last-level
 cache) that are resident in HBM before timing starts.
 
-Per step the library launches stats, reduce, pool, [gram,] thresh, compact
+Per step the library launches stats, reduce, pool, gram, gram_fin, thresh,
+compact for the Gram form, and for the key-sum form one score kernel (the
+statistics, their merge and the pooling in one launch) then thresh, compact
 (the compaction kernel also gathers the kept K/V rows).
 The timed region (`value`, `ms_per_step`) runs kvsel_score_evict; right
 after it the same steps run through kvsel_score_evict_traced, whose kernels
@@ -71,13 +73,30 @@ def fused_step(mode: str, cap: int, b: int = 1, hkv: int = HKV, m: int = HQ // H
             and nch * hkv * b <= FUSED_CAPACITY)
 
 
+SCORES_FUSED_CAPACITY = 1024  # work-groups of the one-launch score pass resident at once (four per CU)
+
+
+def scores_fused(mode: str, cap: int, b: int = 1, hkv: int = HKV, m: int = HQ // HKV * W) -> bool:
+    """The library scores a key-sum call on a longer cache (more than 16
+    chunks of 256 tokens per head; bf16, d = 128, at most 32 window rows per
+    KV head) in one launch when its grid of ceil(cap / 256) * Hkv * b
+    work-groups fits on the device at once."""
+    nch = -(-cap // 256)
+    return (mode == "keysum" and m <= 32 and nch > FUSED_MAX_CHUNKS
+            and nch * hkv * b <= SCORES_FUSED_CAPACITY)
+
+
 def rkv_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV) -> list:
     """Kernels one R-KV call launches, in order: the fused step alone when it
-    applies; otherwise with at most 16 chunks of 256 keys per head k_pool
+    applies; the one-launch score pass in place of stats, reduce and pool when
+    that applies; otherwise with at most 16 chunks of 256 keys per head k_pool
     merges the chunk partials itself and k_reduce is not launched."""
     if fused_step(mode, cap, b, hkv):
         return ["fused"]
-    return unfused_kernels(mode, cap)
+    ks = unfused_kernels(mode, cap)
+    if scores_fused(mode, cap, b, hkv):
+        ks = ["scores"] + [k for k in ks if k not in ("stats", "reduce", "pool")]
+    return ks
 
 
 def unfused_kernels(mode: str, cap: int) -> list:
@@ -130,6 +149,8 @@ def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int =
     # the fused short-cache step: K once, Z and the indices written, the kept
     # rows of V read and of K and V written (K rows come from registers)
     cost["fused"] = {"bytes": kb + 4 * tok + 4 * b * hkv * budget + 3 * b * hkv * min(budget, n) * d * 2}
+    # the one-launch score pass: K once, I and Z written
+    cost["scores"] = {"bytes": kb + 8 * tok}
     if mode == "gram":
         # symmetric Gram: achieved = algorithmic flops (each key pair once)
         ns = -(-n // 256) // 2
@@ -179,6 +200,13 @@ class Hip:
             arr[i] = h
         return arr
 
+    def recorded(self, arr, k) -> bool:
+        """Whether kernel k of a traced call recorded its event pair."""
+        ms = ctypes.c_float()
+        ok = self.lib.hipEventElapsedTime(ctypes.byref(ms), arr[2 * k], arr[2 * k + 1]) == 0
+        self.lib.hipGetLastError()  # a failed query of an unrecorded pair is not left behind
+        return ok
+
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()
         if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
@@ -222,7 +250,8 @@ def time_calls(call, names, cost, steps, warmup, hip, traced_steps=None):
     ms_plain = t0.elapsed_time(t1) / steps
 
     ts = traced_steps or steps
-    evs = [hip.events(2 * nk) for _ in range(ts)]
+    # one event pair more than the predicted launches: it must stay unrecorded
+    evs = [hip.events(2 * nk + 2) for _ in range(ts)]
     torch.cuda.synchronize()
     t0.record()
     for i in range(ts):
@@ -230,6 +259,8 @@ def time_calls(call, names, cost, steps, warmup, hip, traced_steps=None):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / ts
+    if not hip.recorded(evs[0], nk - 1) or hip.recorded(evs[0], nk):
+        raise RuntimeError(f"the call did not launch the {nk} kernels {names}")
     per = {nm: [] for nm in names}
     for e in evs:
         for j, nm in enumerate(names):
@@ -261,7 +292,7 @@ def rkv_caller(mode, layers, b, n, budget, out_bufs=None, budgets=None):
     lib = K.lib()
     mcode = K.MODES[mode]
     q0, k0, _ = layers[0]
-    nk = len(rkv_kernels(mode, k0.shape[2]))
+    nk = len(rkv_kernels(mode, k0.shape[2], b, k0.shape[1]))
     hq, w = q0.shape[1], q0.shape[2]
     hkv, cap = k0.shape[1], k0.shape[2]
     lens = torch.full((b,), n, dtype=torch.int32, device="cuda")
@@ -284,11 +315,11 @@ def rkv_caller(mode, layers, b, n, budget, out_bufs=None, budgets=None):
         if budgets is not None:
             args = head + (P(budgets.data_ptr()),) + tail
             st = (lib.kvsel_score_evict_heads(*args) if events is None else
-                  lib.kvsel_score_evict_heads_traced(*args, events, 2 * nk))
+                  lib.kvsel_score_evict_heads_traced(*args, events, len(events)))
         elif events is None:
             st = lib.kvsel_score_evict(*head, *tail)
         else:
-            st = lib.kvsel_score_evict_traced(*head, *tail, events, 2 * nk)
+            st = lib.kvsel_score_evict_traced(*head, *tail, events, len(events))
         if st != 0:
             raise RuntimeError(f"kvsel_score_evict: {K.status_string(st)}")
 
@@ -403,7 +434,7 @@ def run_decode_slots(mode, n_layers, hip, calls_per_layer=240):
                 P(pos.data_ptr()), None, 1, HQ, HKV, D, w, cap, LAM, budget, P(ev.data_ptr()),
                 cap, P(ne.data_ptr()), None, P(ws.data_ptr()), ws_bytes, sp)
         st = (lib.kvsel_score_evict_slots(*args) if events is None else
-              lib.kvsel_score_evict_slots_traced(*args, events, 2 * len(names)))
+              lib.kvsel_score_evict_slots_traced(*args, events, len(events)))
         if st == 0:
             st = lib.kvsel_slots_write(K.KVSEL_BF16, P(k.data_ptr()), P(v.data_ptr()),
                                        P(pos.data_ptr()), P(kn.data_ptr() + j * step_new),
@@ -430,7 +461,7 @@ def run_batched(mode, hip, steps):
     del c
     b, n, budget = 64, 8192, 1024
     call, keep = rkv_caller(mode, [layer], b, n, budget)
-    r = time_calls(call, rkv_kernels(mode, n), rkv_cost(mode, b, n, budget), steps, 2, hip)
+    r = time_calls(call, rkv_kernels(mode, n, b), rkv_cost(mode, b, n, budget), steps, 2, hip)
     r["tokens"] = b * n
     r["step_bytes"] = rkv_step_bytes(b, n, budget)
     return r
@@ -469,7 +500,7 @@ def run_refreekv(hip, n_layers, steps):
                 D, cap, 2 + i % len(layers), 2, 4, 0.01, P(kept.data_ptr()), P(ws.data_ptr()),
                 ws_bytes, sp)
         st = (lib.kvsel_threshold_cut(*args) if events is None else
-              lib.kvsel_threshold_cut_traced(*args, events, 2 * len(CUT_KERNELS)))
+              lib.kvsel_threshold_cut_traced(*args, events, len(events)))
         if st != 0:
             raise RuntimeError(f"kvsel_threshold_cut: {K.status_string(st)}")
 
@@ -529,7 +560,7 @@ def run_refreekv_rows(hip, n_layers, steps, k_rows=64):
                 P(kept.data_ptr()), P(ko.data_ptr()), P(vo.data_ptr()), cap, P(ws.data_ptr()),
                 ws_bytes, sp)
         st = (lib.kvsel_threshold_cut_rows(*args) if events is None else
-              lib.kvsel_threshold_cut_rows_traced(*args, events, 2 * len(names)))
+              lib.kvsel_threshold_cut_rows_traced(*args, events, len(events)))
         if st != 0:
             raise RuntimeError(f"kvsel_threshold_cut_rows: {K.status_string(st)}")
 
@@ -547,15 +578,16 @@ def run_refreekv_rows(hip, n_layers, steps, k_rows=64):
 
 KERNEL_SOURCES = {"stats": "scores.hip", "reduce": "scores.hip", "pool": "scores.hip",
                   "gram": "gram.hip", "gram_fin": "gram.hip", "thresh": "select.hip",
-                  "compact": "select.hip",
+                  "compact": "select.hip", "fused": "fused.hip", "scores": "fused.hip",
                   "cut_energy": "cut.hip", "cut_scan": "cut.hip"}
 
 
 def source_digest(kernel: str) -> str:
-    """sha1 over the sources a kernel is built from (its file + common.hpp)."""
+    """sha1 over the sources a kernel is built from (its file and the shared
+    headers)."""
     import hashlib
     h = hashlib.sha1()
-    for f in (KERNEL_SOURCES[kernel], "common.hpp", "kernels.hpp"):
+    for f in (KERNEL_SOURCES[kernel], "common.hpp", "kernels.hpp", "tiles.hpp", "scan.hpp"):
         with open(os.path.join(ROOT, "decode_eviction_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

@@ -75,12 +75,14 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 struct ScoreWs {
   int32_t* err;
-  // fused short-cache step (key-sum form): barrier epochs and tokens, tagged
-  // chunk partials and score keys
+  // one-launch kernels of the key-sum form: per-head epochs and tagged chunk
+  // partials; the short-cache step also has barrier tokens and tagged score
+  // keys, the long-cache score pass a tagged merged record per head
   uint64_t* fepoch;
   uint64_t* fflags;
   uint64_t* fpub_a;
   uint64_t* fpub_b;
+  uint64_t* fmerged;
   float2* cstat;
   float2* rstat;
   float* spart;
@@ -120,11 +122,16 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap, kvsel_redund
   Carver c{static_cast<char*>(base)};
   ScoreWs w{};
   w.err = c.take<int32_t>(64);
-  if (!gram && (cap + kChunk - 1) / kChunk <= kFusedMaxChunks) {
+  if (!gram) {
     w.fepoch = c.take<uint64_t>(heads);
-    w.fflags = c.take<uint64_t>(2 * heads * kFusedMaxChunks);
-    w.fpub_a = c.take<uint64_t>(heads * kFusedMaxChunks * kFusedWordsA);
-    w.fpub_b = c.take<uint64_t>(heads * cap);
+    if (nchunk <= kFusedMaxChunks) {
+      w.fflags = c.take<uint64_t>(2 * heads * kFusedMaxChunks);
+      w.fpub_a = c.take<uint64_t>(heads * kFusedMaxChunks * kFusedWordsA);
+      w.fpub_b = c.take<uint64_t>(heads * cap);
+    } else {
+      w.fpub_a = c.take<uint64_t>(heads * nchunk * kFusedWordsA);
+      w.fmerged = c.take<uint64_t>(heads * kFusedWordsA);
+    }
   }
   w.cstat = c.take<float2>(heads * nchunk * mp);
   w.rstat = c.take<float2>(heads * mp);
@@ -202,6 +209,15 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
   p.z_out = z_out;
   p.hist = hist;
   const int sm = mode == KVSEL_R_GRAM ? kModeGram : kModeKeysum;
+  // long caches, key-sum form: one launch reading K once, when its grid fits
+  // on the device at once
+  if (sm == kModeKeysum && dt == KVSEL_BF16 && d == 128 && p.m <= 32 && ws.fmerged) {
+    const ScoresFusedParams fp{p, ws.fepoch, ws.fpub_a, ws.fmerged};
+    if (scores_fused_fits(fp)) {
+      KV_TRY(launch_scores_fused(fp, stream, tr));
+      return KVSEL_OK;
+    }
+  }
   p.fuse_reduce = p.nchunk <= kFuseReduceChunks;
   KV_TRY(launch_stats(dt, d, sm, p, stream, tr));
   if (!p.fuse_reduce) KV_TRY(launch_reduce(d, sm, p, stream, tr));

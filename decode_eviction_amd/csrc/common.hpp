@@ -234,7 +234,15 @@ __device__ __forceinline__ float inv_norm_of(float sumsq) {
 // Row of register i in the 32x32 output tile for lane half hf.
 __device__ __forceinline__ int tile_row(int i, int hf) { return 8 * (i >> 2) + 4 * hf + (i & 3); }
 
-__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+// The value of lane l ^ 32.  v_permlane32_swap exchanges the upper half of
+// its first operand with the lower half of its second; with both set to v,
+// the first result holds v of the lower half in every lane of the upper half
+// and the second v of the upper half in the lower half.  A VALU exchange:
+// no LDS round trip and no lane-index register (as a bpermute would need).
+__device__ __forceinline__ float xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
+}
 
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 -> +0.
 __device__ __forceinline__ uint32_t score_key(float z) {

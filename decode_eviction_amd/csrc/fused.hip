@@ -32,11 +32,11 @@
 // words, then writes a 64-bit token into its slot of the head's flag row; a
 // reader waits until the row holds the token, then reads the words and reads
 // again any whose tag is not there yet (its store was issued before the
-// flag's but may land later).  Tag and token derive from the head's epoch, a
-// counter in the workspace that each call advances by one after barrier A:
-// consecutive calls differ in the tag by construction, and the token is a
-// 64-bit hash (SplitMix64 finaliser), so what a fresh workspace holds does
-// not pass for a signal.  No initialisation kernel is needed and graph
+// flag's but may land later).  Tag and token are hashes (SplitMix64
+// finaliser) of the head's index and its epoch, a counter in the workspace
+// that each call advances by one after barrier A: consecutive calls and
+// different heads differ in both, so neither what a fresh workspace holds nor
+// what earlier calls left there passes for a signal.  No initialisation kernel is needed and graph
 // replays work.  The host launches this kernel only when the whole grid fits
 // on the device at once, so every wait ends; a wait that still exceeds its
 // poll limit sets bit 2 of the error word and continues.
@@ -57,6 +57,17 @@ __device__ __forceinline__ uint64_t mix64(uint64_t x) {
   x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
   x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
   return x ^ (x >> 31);
+}
+
+// The 32-bit tag of a head's data words and its 64-bit barrier tokens in
+// one call: hashes of the head's epoch and the head's index, so that words
+// another head or an earlier call left in the workspace (one reused across
+// shapes holds them at any address) never pass for this call's.
+__device__ __forceinline__ uint64_t head_key(uint64_t ep, long head, uint64_t k) {
+  return mix64(4 * ep + k + ((uint64_t)head << 44));
+}
+__device__ __forceinline__ uint32_t head_tag(uint64_t ep, long head) {
+  return (uint32_t)(head_key(ep, head, 0) >> 32);
 }
 
 __device__ __forceinline__ uint64_t* flag_row(const FusedParams& p, int which, long head) {
@@ -109,6 +120,167 @@ __device__ __forceinline__ int fused_budget(const FusedParams& p, int h) {
   return v < 0 ? 0 : (v > p.budget ? p.budget : v);
 }
 
+// Phase 1 for one 256-token chunk, as k_stats computes it (key-sum form, one
+// tile of up to 32 query rows); each wave holds two 32-token key tiles,
+// tokens tok0 .. tok0 + 63.  Hands the chunk's partials to the sinks:
+// stat(r, max, sum of 2^(t - max)) for the 32 rows and sum(dim, s) for the
+// D dimensions of the chunk's sum of unit keys.  sqs receives each lane's
+// half-row squared norms (for the pooling phase).
+template <typename E, int D, typename StatSink, typename SumSink>
+__device__ __forceinline__ void chunk_partials(const Frag<Geo<E, D>::kNC> (&kf)[2], const u32x4_t* qs,
+                                               int n, int tok0, float sc2, float (&sqs)[2],
+                                               float2 (*wst)[32], float* red, int tid,
+                                               StatSink&& stat, SumSink&& sum) {
+  using G = Geo<E, D>;
+  using QSt = QStage<E, D, 1>;
+  constexpr int NC = G::kNC, LE = G::kLaneElems, PC = E::kPerChunk, NW = 4;
+  const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  // the row statistics first, so that the accumulator tiles are dead before
+  // the unit-key values are formed (the keys stay live for the pooling)
+  {
+    f32x16_t a[2];
+    a[0] = zero16();
+    a[1] = zero16();
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const u32x4_t qc = QSt::chunk(qs, 0, l32, hf, j);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) a[tt] = mfma_chunk<E>(kf[tt].c[j], qc, a[tt]);
+    }
+    const bool full = tok0 + 63 <= n - 1;
+    const int rel = n - 1 - (tok0 + 4 * hf);
+    float m = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool ok = full || 32 * tt + 8 * (i >> 2) + (i & 3) <= rel;
+        m = ok ? fmaxf(m, a[tt][i]) : m;
+      }
+    m = fmaxf(m, xor32(m));
+    const float m2 = m * sc2;
+    float s = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool ok = full || 32 * tt + 8 * (i >> 2) + (i & 3) <= rel;
+          const float e = exp2_fast(fmaf(a[tt][i], sc2, -m2));
+          s += ok ? e : 0.f;
+        }
+    }
+    s += xor32(s);
+    if (hf == 0) wst[wave][l32] = make_float2(m2, s);
+  }
+  {
+    float inv[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sqs[tt] = frag_sumsq<E, NC>(kf[tt]);
+      float ss = sqs[tt];
+      ss += xor32(ss);
+      inv[tt] = inv_norm_of(ss);
+    }
+    float v[LE / 2];
+    {
+      const bool up = (l32 & 16) != 0;
+#pragma unroll
+      for (int i = 0; i < LE / 2; ++i) {
+        const int j = i / PC, e = i % PC;
+        const float lo = fmaf(inv[0], frag_elem<E>(kf[0].c[j], e), inv[1] * frag_elem<E>(kf[1].c[j], e));
+        const float hi = fmaf(inv[0], frag_elem<E>(kf[0].c[j + NC / 2], e),
+                         inv[1] * frag_elem<E>(kf[1].c[j + NC / 2], e));
+        v[i] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, 16, 64);
+      }
+    }
+    scatter_down<LE / 2, 8, PC>(v, l32);
+    float* mine = red + (wave * 64 + lane) * PC;
+#pragma unroll
+    for (int e = 0; e < PC; ++e) mine[e] = v[e];
+  }
+  __syncthreads();
+  if (tid < D) {
+    constexpr int R = 32 / NC;
+    const int ch = tid / PC, e = tid % PC, hfd = ch & 1, j = ch >> 1;
+    float s = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv)
+#pragma unroll
+      for (int q = 0; q < R; ++q) s += red[(wv * 64 + hfd * 32 + j * R + q) * PC + e];
+    sum(tid, s);
+  }
+  if (tid < 32) {
+    float m = -INFINITY, s = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) softmax_merge(m, s, wst[wv][tid].x, wst[wv][tid].y);
+    stat(tid, m, s);
+  }
+}
+
+// Phase 2 for a wave's two key tiles, as k_pool computes it: importance, the
+// key-sum redundancy and Z of tokens tok0 + 32 tt + l32 from the merged row
+// statistics rs (max, 1/sum; zero for rows past m) and the head's sum of
+// unit keys ssh, both in LDS.  Both lanes of a token (hf = 0, 1) return the
+// same values.
+template <typename E, int D>
+__device__ __forceinline__ void pool_tokens(const Frag<Geo<E, D>::kNC> (&kf)[2], const u32x4_t* qs,
+                                            const float2* rs, const float* ssh,
+                                            const float (&sqs)[2], int n, int m, float sc2,
+                                            float lambda, int tid, float (&imp)[2], float (&rd)[2],
+                                            float (&z)[2]) {
+  using G = Geo<E, D>;
+  using QSt = QStage<E, D, 1>;
+  constexpr int NC = G::kNC, PC = E::kPerChunk;
+  // LDS addresses recomputed here rather than kept from the partials
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  float dots[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int q = 0; q < PC / 4; ++q) {
+      const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(&ssh[frag_dim<E>(j, 4 * q, hf)]);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dots[tt] = fmaf(frag_elem<E>(kf[tt].c[j], 4 * q + e), s4[e], dots[tt]);
+      if ((j * (PC / 4) + q) % 4 == 3) asm volatile("" : "+v"(dots[0]), "+v"(dots[1])::"memory");
+    }
+  const float inv_m = 1.0f / (float)m;
+  const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    // at most two query chunks and four row records read ahead from LDS
+    // (the keys stay in registers: the one-launch score pass runs at four
+    // waves per SIMD)
+    f32x16_t c = zero16();
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      c = mfma_chunk<E>(QSt::chunk(qs, 0, l32, hf, j), kf[tt].c[j], c);
+      if (j % 2 == 1) asm volatile("" ::: "memory");
+    }
+    float isum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float2 st = rs[tile_row(i, hf)];
+      isum = fmaf(exp2_fast(fmaf(c[i], sc2, -st.x)), st.y, isum);
+      if (i % 4 == 3) asm volatile("" : "+v"(isum)::"memory");
+    }
+    isum += xor32(isum);
+    imp[tt] = isum * inv_m;
+    float ss = sqs[tt];
+    ss += xor32(ss);
+    const float inv = inv_norm_of(ss);
+    float dot = dots[tt];
+    dot += xor32(dot);
+    rd[tt] = fmaf(inv, dot, -(inv * inv) * ss) * inv_nm1;
+    z[tt] = fmaf(lambda, imp[tt], -(1.0f - lambda) * rd[tt]);
+    __builtin_amdgcn_sched_barrier(0);  // one accumulator tile live at a time
+  }
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   using G = Geo<E, D>;
@@ -140,7 +312,7 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   if (c0 >= n) return;
   const int nwg = (n + kChunk - 1) / kChunk;
   const uint64_t ep = ld_dev(p.epoch + head);
-  const uint32_t tag = (uint32_t)ep ^ 0x9e3779b9u;
+  const uint32_t tag = head_tag(ep, head);
   const char* kb = p.k + head * (long)p.cap * RB;
   const char* qb = p.q + ((long)bi * p.hq + (long)h * p.g) * p.w * RB;
   uint64_t* pa = p.pub_a + head * kFusedMaxChunks * kFusedWordsA;
@@ -175,90 +347,17 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   __shared__ float red[256 * PC];
   QSt::landed(qs, tid);
   __syncthreads();
-  f32x16_t a[2];
-  a[0] = zero16();
-  a[1] = zero16();
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    const u32x4_t qc = QSt::chunk(qs, 0, l32, hf, j);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) a[tt] = mfma_chunk<E>(kf[tt].c[j], qc, a[tt]);
-  }
   float sqs[2];
-  {
-    float inv[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      sqs[tt] = frag_sumsq<E, NC>(kf[tt]);
-      float ss = sqs[tt];
-      ss += xor32(ss);
-      inv[tt] = inv_norm_of(ss);
-    }
-    float v[LE / 2];
-    {
-      const bool up = (l32 & 16) != 0;
-#pragma unroll
-      for (int i = 0; i < LE / 2; ++i) {
-        const int j = i / PC, e = i % PC;
-        const float lo = fmaf(inv[0], frag_elem<E>(kf[0].c[j], e), inv[1] * frag_elem<E>(kf[1].c[j], e));
-        const float hi = fmaf(inv[0], frag_elem<E>(kf[0].c[j + NC / 2], e),
-                         inv[1] * frag_elem<E>(kf[1].c[j + NC / 2], e));
-        v[i] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, 16, 64);
-      }
-    }
-    scatter_down<LE / 2, 8, PC>(v, l32);
-    constexpr int R = 32 / NC;
-    float* mine = red + (wave * 64 + lane) * PC;
-#pragma unroll
-    for (int e = 0; e < PC; ++e) mine[e] = v[e];
-    __syncthreads();
-    if (tid < D) {
-      const int ch = tid / PC, e = tid % PC, hfd = ch & 1, j = ch >> 1;
-      float s = 0.f;
-#pragma unroll
-      for (int wv = 0; wv < 4; ++wv)
-#pragma unroll
-        for (int q = 0; q < R; ++q) s += red[(wv * 64 + hfd * 32 + j * R + q) * PC + e];
-      st_dev(pa + chunk * kFusedWordsA + 64 + tid, tagged(tag, __float_as_uint(s)));
-    }
-  }
-  {
-    const bool full = tok0 + 63 <= n - 1;
-    const int rel = n - 1 - (tok0 + 4 * hf);
-    float m = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bool ok = full || 32 * tt + 8 * (i >> 2) + (i & 3) <= rel;
-        m = ok ? fmaxf(m, a[tt][i]) : m;
-      }
-    m = fmaxf(m, xor32(m));
-    const float m2 = m * sc2;
-    float s = 0.f;
-    if (m != -INFINITY) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const bool ok = full || 32 * tt + 8 * (i >> 2) + (i & 3) <= rel;
-          const float e = exp2_fast(fmaf(a[tt][i], sc2, -m2));
-          s += ok ? e : 0.f;
-        }
-    }
-    s += xor32(s);
-    if (hf == 0) wst[wave][l32] = make_float2(m2, s);
-  }
-  __syncthreads();
-  if (tid < 32) {
-    float m = -INFINITY, s = 0.f;
-#pragma unroll
-    for (int wv = 0; wv < NW; ++wv) softmax_merge(m, s, wst[wv][tid].x, wst[wv][tid].y);
-    st_dev(pa + chunk * kFusedWordsA + 2 * tid, tagged(tag, __float_as_uint(m)));
-    st_dev(pa + chunk * kFusedWordsA + 2 * tid + 1, tagged(tag, __float_as_uint(s)));
-  }
-  signal(p, 0, head, chunk, mix64(2 * ep + 1), tid);
-  wait_flags(p, 0, head, nwg, mix64(2 * ep + 1), tid);
+  uint64_t* rec = pa + chunk * kFusedWordsA;
+  chunk_partials<E, D>(
+      kf, qs, n, tok0, sc2, sqs, wst, red, tid,
+      [&](int r, float m, float s) {
+        st_dev(rec + 2 * r, tagged(tag, __float_as_uint(m)));
+        st_dev(rec + 2 * r + 1, tagged(tag, __float_as_uint(s)));
+      },
+      [&](int dim, float s) { st_dev(rec + 64 + dim, tagged(tag, __float_as_uint(s))); });
+  signal(p, 0, head, chunk, head_key(ep, head, 1), tid);
+  wait_flags(p, 0, head, nwg, head_key(ep, head, 1), tid);
   if (chunk == 0 && tid == 0) st_dev(p.epoch + head, ep + 1);  // every work-group has read ep
 
   // ---- phase 2: merged statistics, importance, redundancy, Z (k_pool's arithmetic)
@@ -306,45 +405,15 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
     ssh[tid] = s;
   }
   __syncthreads();
-  float dots[2] = {0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < NC; ++j)
-#pragma unroll
-    for (int q = 0; q < PC / 4; ++q) {
-      const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(&ssh[frag_dim<E>(j, 4 * q, hf)]);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dots[tt] = fmaf(frag_elem<E>(kf[tt].c[j], 4 * q + e), s4[e], dots[tt]);
-      if ((j * (PC / 4) + q) % 4 == 3) asm volatile("" : "+v"(dots[0]), "+v"(dots[1])::"memory");
-    }
-  const float inv_m = 1.0f / (float)p.m;
-  const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
+  float imp[2], rd[2], z[2];
+  pool_tokens<E, D>(kf, qs, rs, ssh, sqs, n, p.m, sc2, p.lambda, tid, imp, rd, z);
   uint64_t* pb = p.pub_b + head * p.cap;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    f32x16_t c = zero16();
-#pragma unroll
-    for (int j = 0; j < NC; ++j) c = mfma_chunk<E>(QSt::chunk(qs, 0, l32, hf, j), kf[tt].c[j], c);
-    float isum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float2 st = rs[tile_row(i, hf)];
-      isum = fmaf(exp2_fast(fmaf(c[i], sc2, -st.x)), st.y, isum);
-    }
-    isum += xor32(isum);
-    const float imp = isum * inv_m;
-    float ss = sqs[tt];
-    ss += xor32(ss);
-    const float inv = inv_norm_of(ss);
-    float dot = dots[tt];
-    dot += xor32(dot);
-    const float rd = fmaf(inv, dot, -(inv * inv) * ss) * inv_nm1;
-    const float z = fmaf(p.lambda, imp, -(1.0f - p.lambda) * rd);
     const int tok = tok0 + 32 * tt + l32;
     if (hf == 0 && tok < n) {
-      p.z_out[head * p.cap + tok] = z;
-      if (n > B && B > 0) st_dev(pb + tok, tagged(tag, score_key(z)));
+      p.z_out[head * p.cap + tok] = z[tt];
+      if (n > B && B > 0) st_dev(pb + tok, tagged(tag, score_key(z[tt])));
     }
   }
 
@@ -376,8 +445,8 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
     gather();
     return;
   }
-  signal(p, 1, head, chunk, mix64(2 * ep + 2), tid);
-  wait_flags(p, 1, head, nwg, mix64(2 * ep + 2), tid);
+  signal(p, 1, head, chunk, head_key(ep, head, 2), tid);
+  wait_flags(p, 1, head, nwg, head_key(ep, head, 2), tid);
 
   // ---- phase 3: the head's keys in LDS, the threshold, slots of this chunk
   __shared__ uint32_t kall[kFusedKeys];
@@ -494,25 +563,268 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   gather();
 }
 
-static int g_fused_capacity[64];
-
-bool fused_fits(const FusedParams& p) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-  if (g_fused_capacity[dev] == 0) {
-    int per_cu = 0, ncu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_rkv_fused<BF16, 128>, 256, 0) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return false;
-    g_fused_capacity[dev] = per_cu * ncu > 0 ? per_cu * ncu : -1;
-  }
-  const long grid = (long)((p.cap + kChunk - 1) / kChunk) * p.hkv * p.b;
-  return g_fused_capacity[dev] > 0 && grid <= g_fused_capacity[dev];
-}
-
 hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr) {
   const dim3 grid((p.cap + kChunk - 1) / kChunk, p.hkv, p.b);
   return launch_k(k_rkv_fused<BF16, 128>, grid, dim3(256), s, tr, p);
+}
+
+// ------------------------------------------------------------------------
+// One-launch score pass for long caches (key-sum redundancy).
+//
+// The multi-kernel pass streams K twice (k_stats, then k_pool after
+// k_reduce).  k_scores_fused reads each key once: a work-group per 256-token
+// chunk and head computes the chunk's partials as k_stats does and keeps its
+// keys in registers; the head's first kScoreMergeParts work-groups each merge
+// one slice of the partials in k_reduce's order (the row statistics of rows
+// 0-15 and 16-31, then the unit-key sums 32 dimensions at a time); every
+// work-group then pools its own tokens from the merged record as k_pool
+// does.  The scores equal the multi-kernel pass's bit for bit.
+//
+// Records that cross work-groups are tagged words (value in the low half,
+// the call's tag for the head in the high half) written and read with
+// device-scope accesses; a reader polls each word until it holds the tag, so
+// arrival needs no separate flag and no store acknowledgement.  The merger
+// of rows 0-15 advances the head's epoch once it has read every chunk's
+// words (then every work-group of the head has read the epoch).  The host
+// launches the kernel only when the whole grid fits on the device at once; a
+// poll that still exceeds its limit sets bit 2 of the error word.
+
+// The value of the tagged word at `at`, read once as w: polled again until
+// its tag is there.
+__device__ __forceinline__ uint32_t untag_w(const uint64_t* at, uint64_t w, uint32_t tag, int32_t* err) {
+  for (int it = 0; (uint32_t)(w >> 32) != tag; ++it) {
+    if (it == kSpinLimit) {
+      atomicOr(err, 4);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    w = ld_dev(at);
+  }
+  return (uint32_t)w;
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void k_scores_fused(ScoresFusedParams fp) {
+  const ScoreParams& p = fp.s;
+  using G = Geo<E, D>;
+  using QSt = QStage<E, D, 1>;
+  constexpr int NC = G::kNC, RB = G::kRowBytes, PC = E::kPerChunk, W = kFusedWordsA;
+  constexpr int NP = 2 + D / 32;  // merge slices: rows 0-15, rows 16-31, 32 dimensions each
+  static_assert(D == 128 && NP == kScoreMergeParts, "merge slices of the 128-dimension record");
+  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  // the wave index in a scalar register (the compiler cannot prove tid >> 6
+  // uniform): wave-derived offsets then take no vector registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const long head = (long)bi * p.hkv + h;
+  const int c0 = chunk * kChunk;
+  if (chunk == 0 && h == 0 && bi == 0 && tid == 0) {
+    int f = 0;
+    for (int i = 0; i < p.b; ++i) f |= len_bad(p.lengths[i], p.cap) ? 1 : 0;
+    *p.err = f;
+  }
+  // the head's first-level histogram (and the selection state after it)
+  // starts at zero: chunk 0 clears it before it publishes its merged rows,
+  // which every work-group reads before adding to it
+  uint32_t* hg = p.hist ? p.hist + head * kHistStride : nullptr;
+  if (hg && chunk == 0)
+    for (int t = tid; t < kHistStride; t += 256) st_dev(hg + t, 0u);
+  const int n = clamp_len(p.lengths[bi], p.cap);
+  if (c0 >= n) return;
+  const int nwg = (n + kChunk - 1) / kChunk;
+  const uint64_t ep = ld_dev(fp.epoch + head);
+  const uint32_t tag = head_tag(ep, head);
+  const char* kb = p.k + head * (long)p.cap * RB;
+  const char* qb = p.q + ((long)bi * p.hq + (long)h * p.g) * p.w * RB;
+
+  __shared__ u32x4_t qs[QSt::kWords];
+  QSt::issue(qs, qb, p.m, tid);
+  const int tok0 = c0 + wave * 64;
+  // the chunk's keys through a buffer resource that ends at token n: keys
+  // past it read as zeros (as load_frag gives them), without a branch
+  Frag<NC> kf[2];
+  {
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kb + (long)c0 * RB, (uint32_t)min(n - c0, kChunk) * RB);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const uint32_t off = (uint32_t)((wave * 64 + 32 * tt + l32) * RB + hf * 16);
+#pragma unroll
+      for (int j = 0; j < NC; ++j) kf[tt].c[j] = buf_ld128(rk, off + 32 * j, 0);
+    }
+  }
+  __shared__ uint32_t lh[kHistBins];
+  if (hg)
+    for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
+
+  // ---- chunk partials (k_stats' arithmetic) as tagged words
+  const float sc2 = p.scale2;
+  __shared__ float2 wst[4][32];
+  __shared__ float red[256 * PC];  // also the merge's group partials
+  static_assert(256 * PC >= 2 * 32 * 16, "group partials of 16 rows fit");
+  QSt::landed(qs, tid);
+  __syncthreads();
+  float sqs[2];
+  uint64_t* pr = fp.part + head * p.nchunk * W;  // [chunk][W]
+  uint64_t* mr = fp.merged + head * W;
+  {
+    uint64_t* rec = pr + (long)chunk * W;
+    chunk_partials<E, D>(
+        kf, qs, n, tok0, sc2, sqs, wst, red, tid,
+        [&](int r, float m, float s) {
+          st_dev(rec + 2 * r, tagged(tag, __float_as_uint(m)));
+          st_dev(rec + 2 * r + 1, tagged(tag, __float_as_uint(s)));
+        },
+        [&](int dim, float s) { st_dev(rec + 64 + dim, tagged(tag, __float_as_uint(s))); });
+  }
+  // the keys and the staged queries as opaque values from here: the pooling
+  // unpacks and reads them again instead of keeping copies from the partials
+  // alive (in scratch) across the waits
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int j = 0; j < NC; ++j) asm volatile("" : "+v"(kf[tt].c[j]));
+  asm volatile("" ::: "memory");
+
+  // ---- merged slices (k_reduce's order), by the head's first work-groups
+  for (int part = chunk; part < NP; part += nwg) {
+    __syncthreads();  // red is free
+    if (part < 2) {
+      // rows 16 part .. + 15.  Group gi of the 32 (1024 / 32 rows) takes
+      // chunks gi, gi + 32, ... in turn; the groups are then merged in
+      // order.  Thread (r, q) runs groups q and q + 16 of row 16 part + r.
+      const int r = tid & 15, q = tid >> 4, row = 16 * part + r;
+      float m[2], s[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        m[k] = -INFINITY;
+        s[k] = 0.f;
+      }
+      for (int base = 0; base < nwg; base += 128) {
+        uint64_t v[2][4][2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint64_t* at = pr + (long)min(q + 16 * k + base + 32 * u, nwg - 1) * W + 2 * row;
+            v[k][u][0] = ld_dev(at);
+            v[k][u][1] = ld_dev(at + 1);
+          }
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int c = q + 16 * k + base + 32 * u;
+            if (c < nwg) {
+              const uint64_t* at = pr + (long)c * W + 2 * row;
+              const float cm = __uint_as_float(untag_w(at, v[k][u][0], tag, p.err));
+              const float cs = __uint_as_float(untag_w(at + 1, v[k][u][1], tag, p.err));
+              softmax_merge(m[k], s[k], cm, cs);
+            }
+          }
+      }
+      float2* gp = reinterpret_cast<float2*>(red);  // [group][16 rows]
+#pragma unroll
+      for (int k = 0; k < 2; ++k) gp[(q + 16 * k) * 16 + r] = make_float2(m[k], s[k]);
+      vmem_done();  // chunk 0's histogram clearing is done before its rows are published
+      __syncthreads();
+      // every chunk's words have been read: each work-group of the head has
+      // read the epoch
+      if (part == 0 && tid == 0) st_dev(fp.epoch + head, ep + 1);
+      if (tid < 16) {
+        float mm = -INFINITY, ss = 0.f;
+        for (int g = 0; g < 32; ++g) softmax_merge(mm, ss, gp[g * 16 + tid].x, gp[g * 16 + tid].y);
+        st_dev(mr + 2 * row, tagged(tag, __float_as_uint(mm)));
+        st_dev(mr + 2 * row + 1, tagged(tag, __float_as_uint(ss > 0.f ? 1.0f / ss : 0.f)));
+      }
+    } else {
+      // unit-key sums of dimensions 32 (part - 2) .. + 31: group gi of 8
+      // (1024 / D) takes chunks gi, gi + 8, ... in blocks of four (a block
+      // reaching past the last chunk adds zeros); the groups are then added
+      // in order
+      const int dim = 32 * (part - 2) + (tid & 31), gi = tid >> 5;
+      float a = 0.f;
+      for (int base = 0; base < nwg; base += 128) {
+        uint64_t v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = ld_dev(pr + (long)min(gi + base + 8 * u, nwg - 1) * W + 64 + dim);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int c = gi + base + 8 * u;
+          if (gi + base + 32 * (u / 4) < nwg)
+            a += c < nwg ? __uint_as_float(untag_w(pr + (long)c * W + 64 + dim, v[u], tag, p.err)) : 0.f;
+        }
+      }
+      red[gi * 32 + (tid & 31)] = a;
+      __syncthreads();
+      if (tid < 32) {
+        float t = 0.f;
+        for (int g = 0; g < 8; ++g) t += red[g * 32 + tid];
+        st_dev(mr + 64 + 32 * (part - 2) + tid, tagged(tag, __float_as_uint(t)));
+      }
+    }
+  }
+
+  // ---- importance, redundancy, Z of this chunk's tokens (k_pool's arithmetic)
+  __shared__ float2 rs[32];
+  __shared__ __attribute__((aligned(16))) float ssh[D];
+  if (tid < 64 + D) {
+    const uint32_t v = untag_w(mr + tid, ld_dev(mr + tid), tag, p.err);
+    if (tid < 64) reinterpret_cast<float*>(rs)[tid] = (tid >> 1) < p.m ? __uint_as_float(v) : 0.f;
+    else ssh[tid - 64] = __uint_as_float(v);
+  }
+  __syncthreads();
+  float imp[2], rd[2], z[2];
+  pool_tokens<E, D>(kf, qs, rs, ssh, sqs, n, p.m, sc2, p.lambda, tid, imp, rd, z);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tok = tok0 + 32 * tt + l32;
+    if (hf == 0 && tok < n) {
+      const long o = head * p.cap + tok;
+      p.i_out[o] = imp[tt];
+      if (p.r_out) p.r_out[o] = rd[tt];
+      p.z_out[o] = z[tt];
+      if (hg) atomicAdd(&lh[hist_bin(score_key(z[tt]))], 1u);
+    }
+  }
+  if (hg) {
+    __syncthreads();
+    for (int t = tid; t < kHistBins; t += 256)
+      if (lh[t]) atomicAdd(&hg[t], lh[t]);
+  }
+}
+
+// Work-groups of kern resident on the device at once (cached per device;
+// -1 when the query fails).
+template <typename K>
+static bool grid_fits(K kern, int* cache, long grid) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (cache[dev] == 0) {
+    int per_cu = 0, ncu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return false;
+    cache[dev] = per_cu * ncu > 0 ? per_cu * ncu : -1;
+  }
+  return cache[dev] > 0 && grid <= cache[dev];
+}
+
+static int g_fused_capacity[64];
+
+bool fused_fits(const FusedParams& p) {
+  return grid_fits(k_rkv_fused<BF16, 128>, g_fused_capacity,
+                   (long)((p.cap + kChunk - 1) / kChunk) * p.hkv * p.b);
+}
+
+static int g_scores_capacity[64];
+
+bool scores_fused_fits(const ScoresFusedParams& p) {
+  return grid_fits(k_scores_fused<BF16, 128>, g_scores_capacity, (long)p.s.nchunk * p.s.hkv * p.s.b);
+}
+
+hipError_t launch_scores_fused(const ScoresFusedParams& p, hipStream_t s, Trace* tr) {
+  return launch_k(k_scores_fused<BF16, 128>, dim3(p.s.nchunk, p.s.hkv, p.s.b), dim3(256), s, tr, p);
 }
 
 }  // namespace kvsel

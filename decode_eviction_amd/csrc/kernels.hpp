@@ -255,6 +255,22 @@ struct FusedParams {
   uint64_t* pub_b;          // [b][Hkv][cap]: tagged score keys
 };
 
+// One-launch score pass for long caches (fused.hip): the key-sum scores of
+// k_stats, k_reduce and k_pool in one grid of kChunk-token work-groups (bf16
+// keys of 128 dimensions, at most 32 window rows per KV head), every
+// work-group of the grid resident at once.  Chunk partials and the merged
+// record are tagged words in the layout of the short-cache step's records
+// (kFusedWordsA per record); the first kScoreMergeParts work-groups of a head
+// each merge one slice (rows 0-15, rows 16-31, then the unit-key sums 32
+// dimensions at a time).
+constexpr int kScoreMergeParts = 2 + 128 / 32;
+struct ScoresFusedParams {
+  ScoreParams s;            // shapes, inputs, outputs, histogram, error word
+  uint64_t* epoch;          // [b][Hkv]: advanced by one every call
+  uint64_t* part;           // [b][Hkv][nchunk][kFusedWordsA]: tagged chunk partials
+  uint64_t* merged;         // [b][Hkv][kFusedWordsA]: tagged merged record
+};
+
 // Optional per-kernel timing: the k-th kernel an entry point launches records
 // ev[2k] when it starts and ev[2k+1] when it ends (hipExtLaunchKernelGGL).
 struct Trace {
@@ -295,5 +311,9 @@ hipError_t launch_cut_compact(int dt, int d, const CutCompactParams& p, hipStrea
 // at once (then nothing is launched)
 bool fused_fits(const FusedParams& p);
 hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr);
+// the one-launch score pass: false when its grid does not fit on the device
+// at once (then nothing is launched)
+bool scores_fused_fits(const ScoresFusedParams& p);
+hipError_t launch_scores_fused(const ScoresFusedParams& p, hipStream_t s, Trace* tr);
 
 }  // namespace kvsel

@@ -94,7 +94,12 @@ const char* kvsel_status_string(kvsel_status s);
 size_t kvsel_score_evict_workspace(int b, int Hq, int Hkv, int d, int w, int cap, int budget);
 
 /* Scores only.  Writes Z (and I, R when non-null) as fp32 [b][Hkv][cap];
- * entries at positions >= n are left untouched.  lambda in [0, 1]. */
+ * entries at positions >= n are left untouched.  lambda in [0, 1].
+ * Key-sum form on a cache of more than 4096 slots (bf16, d = 128, g*w <= 32):
+ * when the grid of ceil(cap / 256) * Hkv * b work-groups fits on the device
+ * at once (1024 on 256 compute units), one kernel computes the scores,
+ * reading each key once; otherwise the statistics, their merge and the
+ * pooling run as separate kernels.  Both give the same bits. */
 kvsel_status kvsel_scores(kvsel_dtype dt, kvsel_redundancy mode,
                           const void* q_window, const void* k, const int32_t* lengths,
                           int b, int Hq, int Hkv, int d, int w, int cap, float lambda,
@@ -197,7 +202,9 @@ kvsel_status kvsel_score_evict_heads(kvsel_dtype dt, kvsel_redundancy mode,
  * the last two are replaced by select, gather.  With cap <= 4096 (at most 16
  * chunks of 256 keys per head) there is no reduce kernel: pool merges the
  * chunk partials itself; a key-sum call that takes the single-launch path
- * (see kvsel_score_evict) launches one kernel. */
+ * (see kvsel_score_evict) launches one kernel, and one that takes the
+ * one-launch score pass (see kvsel_scores) launches scores, threshold,
+ * compact (select, gather above cap 32768). */
 kvsel_status kvsel_score_evict_traced(kvsel_dtype dt, kvsel_redundancy mode,
                                       const void* q_window, const void* k, const void* v,
                                       const int32_t* lengths, int b, int Hq, int Hkv, int d,
@@ -356,10 +363,11 @@ kvsel_status kvsel_threshold_cut_from_attn(const float* attn_last, const int32_t
  * used it (synchronises the stream).  Bit 0: some lengths[i] lay outside
  * [0, cap] and was clamped into it; bit 1: some per-head budget lay outside
  * [0, budget_max] and was clamped; bit 2: a wait between the work-groups of
- * the single-launch short-cache step exceeded its poll limit (the results of
- * that call are not to be trusted; it cannot happen while the device runs
- * the whole grid at once, which the library checks before choosing that
- * path).  Returns KVSEL_ERR_HIP if the copy fails. */
+ * the single-launch short-cache step or of the one-launch score pass
+ * exceeded its poll limit (the results of that call are not to be trusted;
+ * it cannot happen while the device runs the whole grid at once, which the
+ * library checks before choosing those paths, unless kernels of other
+ * streams hold compute units for that long).  Returns KVSEL_ERR_HIP if the copy fails. */
 kvsel_status kvsel_workspace_error(const void* workspace, int32_t* flags_host, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -187,8 +187,18 @@ def test_bench_kernel_names_follow_the_reduce_folding():
             if bench.fused_step(mode, cap):
                 assert names == ["fused"] and mode == "keysum" and -(-cap // chunk) <= fmax
                 continue
+            if bench.scores_fused(mode, cap):
+                assert mode == "keysum" and -(-cap // chunk) > fmax
+                assert names == ["scores"] + [k for k in bench.KERNELS[mode]
+                                              if k not in ("stats", "reduce", "pool")]
+                continue
             folded = -(-cap // chunk) <= fuse
             assert ("reduce" not in names) == folded, (mode, cap)
             assert [k for k in bench.KERNELS[mode] if k != "reduce"] == [k for k in names if k != "reduce"]
     # 64 sequences of 2176 tokens: 9 * 8 * 64 work-groups do not fit at once
     assert bench.rkv_kernels("keysum", 2176, b=64) != ["fused"]
+    # the n = 32768 layer: 128 * 8 work-groups of the score pass fit at four per
+    # compute unit; 64 sequences of 8192 tokens do not
+    assert bench.rkv_kernels("keysum", 32768)[0] == "scores"
+    assert bench.rkv_kernels("keysum", 8192, b=64)[0] == "stats"
+    assert set(bench.KERNEL_SOURCES) >= set(bench.rkv_cost("gram")) - {"evict"}
