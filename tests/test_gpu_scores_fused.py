@@ -1,21 +1,25 @@
-"""The one-launch key-sum score pass for long caches: more than 16 chunks of
-256 tokens per head, bf16 keys of 128 dimensions, at most 32 window rows per
-KV head, taken when the whole grid is resident at once (four work-groups per
+"""The one-launch key-sum path for longer caches: more than 16 chunks of 256
+tokens per head, bf16 keys of 128 dimensions, at most 32 window rows per KV
+head, taken when the whole grid is resident at once (four work-groups per
 compute unit, 1024 on the device).
 
-It computes each chunk's partials as k_stats does, merges them in k_reduce's
-order and pools as k_pool does, so I, R and Z must equal the multi-kernel
-pass's bit for bit.  The reference call repeats the same sequences along the
-batch until the grid no longer fits: the library then runs the separate
-passes, whose per-sequence arithmetic does not depend on the batch.  Each
-case reads from the traced entry point which path ran (a silent fallback
-would make the comparison vacuous), checks that no wait timed out (bit 2 of
-the error word) and compares sampled heads with the oracle within the score
-tolerance.  Repeated calls on one workspace filled with junk exercise the
-per-head epochs.  Cases: the n = 32768 layer, a ragged batch, a cache of 256
-chunks (the merges loop over blocks of 128 chunks), sequences of fewer than
-five chunks (one work-group merges several slices), empty and one-token
-sequences, a length above cap and 16 window rows per KV head."""
+The score pass computes each chunk's partials as k_stats does, merges them in
+k_reduce's order and pools as k_pool does, so I, R and Z must equal the
+multi-kernel pass's bit for bit, and so must the indices and compacted K
+and V rows that the selection kernels then derive from those scores.  The
+reference call repeats the same sequences along the batch until the grid no
+longer fits: the library then runs the separate kernels, whose per-sequence
+results do not depend on the batch.  Each case reads from the traced entry
+point which path ran (a silent fallback would make the comparison vacuous),
+checks that no wait timed out (bit 2 of the error word) and compares sampled
+heads with the oracle within the score tolerance.  Repeated calls on one
+workspace filled with junk exercise the per-head epochs.  Cases: the n =
+32768 layer, a ragged batch, a cache of 256 chunks (the merges loop over
+blocks of 128 chunks; selection through the large-cache kernels), sequences of fewer
+than five chunks (one work-group merges several slices), empty and one-token
+sequences, n <= B, a length above cap, 16 window rows per KV head, per-head
+budgets (0, 1, out of range), all-equal keys (the threshold bin holds every
+key and is read from memory) and three-valued ties."""
 
 import ctypes
 
@@ -26,7 +30,7 @@ import torch
 from decode_eviction_amd import kvsel as K
 from decode_eviction_amd import synth
 from oracle import rkv
-from tests.gpu_util import SCORE_RTOL, dev, dev_i32, host_bits, log, score_err
+from tests.gpu_util import SCORE_RTOL, SWAP_WINDOW, dev, dev_i32, host_bits, log, score_err, swaps
 
 pytestmark = pytest.mark.gpu
 
@@ -94,46 +98,84 @@ def _reps_unfused(b, hkv, cap):
     return -(-2049 // per) + 1
 
 
-def _check(case, oracle_heads=2, calls=3, lengths=None):
+def _host(t):
+    """Device tensor -> numpy (bf16 as its raw 16-bit words)."""
+    return host_bits(t) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def _evict(q, k, v, lens, budget, lam, budgets=None, ws=None):
+    b, hkv, cap = k.shape[0], k.shape[1], k.shape[2]
+    z = torch.full((b, hkv, cap), float("nan"), device="cuda")
+    ko = torch.zeros((b, hkv, budget, k.shape[3]), dtype=k.dtype, device="cuda")
+    vo = torch.zeros_like(ko)
+    if budgets is None:
+        _, _, idx = K.kvsel_score_evict(q, k, v, lens, budget, lam, "keysum", k_out=ko, v_out=vo,
+                                        scores_out=z, workspace=ws)
+    else:
+        _, _, idx = K.kvsel_score_evict_heads(q, k, v, lens, dev_i32(budgets), budget, lam, "keysum",
+                                              k_out=ko, v_out=vo, scores_out=z, workspace=ws)
+    return z, idx, ko, vo
+
+
+def _check(case, oracle_heads=2, calls=3, lengths=None, budget=None, budgets=None, heads=None):
     lengths = case.lengths if lengths is None else np.asarray(lengths, np.int32)
+    budget = case.budget if budget is None else budget
     log(f"[scores_fused] {case.name} b={case.b} hq={case.hq} hkv={case.hkv} cap={case.cap} "
-        f"lengths={lengths.tolist()}")
+        f"lengths={lengths.tolist()} B={budget} budgets={budgets}")
     q, k, v = dev(case.q, "bf16"), dev(case.k, "bf16"), dev(case.v, "bf16")
     lens = dev_i32(lengths)
-    B = 64
-    assert launched_kernels(q, k, v, lens, B, case.lam) == 3, "the one-launch score pass did not run"
+    assert launched_kernels(q, k, v, lens, budget, case.lam) == 3, "the one-launch score pass did not run"
     reps = _reps_unfused(case.b, case.hkv, case.cap)
     qr, kr, vr = (torch.cat([t] * reps, 0).contiguous() for t in (q, k, v))
     lr = dev_i32(np.tile(lengths, reps))
-    assert launched_kernels(qr, kr, vr, lr, B, case.lam) == 5, "the reference ran a fused path"
+    assert launched_kernels(qr, kr, vr, lr, budget, case.lam) == 5, "the reference ran a fused path"
     ref = [x.cpu().numpy()[:case.b] for x in _scores(qr, kr, lr, case.lam)]
+    ref_ev = [_host(x)[:case.b] for x in _evict(qr, kr, vr, lr, budget, case.lam, budgets)]
 
-    ws = torch.empty(K.kvsel_score_evict_workspace(case.b, case.hq, case.hkv, case.d, case.w,
-                                                   case.cap, 1), dtype=torch.uint8, device="cuda")
-    ws.fill_(0x5a)
     n_eff = np.clip(lengths, 0, case.cap)
-    want_err = 1 if ((lengths < 0) | (lengths > case.cap)).any() else 0
+    bad_len = ((lengths < 0) | (lengths > case.cap)).any()
+    bad_budget = budgets is not None and any(x < 0 or x > budget for x in budgets)
+    wsb = K.kvsel_score_evict_workspace(case.b, case.hq, case.hkv, case.d, case.w, case.cap, budget)
+    wss = {e: torch.full((wsb,), 0x5a, dtype=torch.uint8, device="cuda") for e in ("scores", "evict")}
     for call in range(calls):
-        got = [x.cpu().numpy() for x in _scores(q, k, lens, case.lam, ws)]
-        flags = K.kvsel_workspace_error(ws)
-        assert flags & 4 == 0, f"a wait timed out (call {call})"
-        assert flags == want_err, flags
-        for bi in range(case.b):
-            n = int(n_eff[bi])
-            for h in range(case.hkv):
-                for name, g, rf in zip("IRZ", got, ref):
-                    assert np.array_equal(g[bi, h, :n].view(np.uint32), rf[bi, h, :n].view(np.uint32)), \
-                        (call, name, bi, h)
-                    assert np.isnan(g[bi, h, n:]).all(), (call, name, bi, h, "written past n")
+        for entry in ("scores", "evict"):
+            ws = wss[entry]
+            if entry == "scores":
+                got = [x.cpu().numpy() for x in _scores(q, k, lens, case.lam, ws)]
+                want_err = 1 if bad_len else 0
+            else:
+                got = [_host(x) for x in _evict(q, k, v, lens, budget, case.lam, budgets, ws)]
+                want_err = (1 if bad_len else 0) | (2 if bad_budget else 0)
+            flags = K.kvsel_workspace_error(ws)
+            assert flags & 4 == 0, f"a wait timed out (call {call}, {entry})"
+            assert flags == want_err, (entry, flags)
+            for bi in range(case.b):
+                n = int(n_eff[bi])
+                for h in range(case.hkv):
+                    if entry == "scores":
+                        for name, g, rf in zip("IRZ", got, ref):
+                            assert np.array_equal(g[bi, h, :n].view(np.uint32), rf[bi, h, :n].view(np.uint32)), \
+                                (call, name, bi, h)
+                            assert np.isnan(g[bi, h, n:]).all(), (call, name, bi, h, "written past n")
+                    else:
+                        z, idx, ko, vo = got
+                        assert np.array_equal(z[bi, h, :n].view(np.uint32), ref_ev[0][bi, h, :n].view(np.uint32)), \
+                            (call, "Z", bi, h)
+                        assert np.array_equal(idx[bi, h], ref_ev[1][bi, h]), (call, "idx", bi, h)
+                        assert np.array_equal(ko[bi, h], ref_ev[2][bi, h]), (call, "k_out", bi, h)
+                        assert np.array_equal(vo[bi, h], ref_ev[3][bi, h]), (call, "v_out", bi, h)
     # sampled heads against the oracle
-    heads = [(bi, h) for bi in range(case.b) for h in range(case.hkv) if n_eff[bi] > 0][:oracle_heads]
+    if heads is None:
+        heads = [(bi, h) for bi in range(case.b) for h in range(case.hkv) if n_eff[bi] > 0][:oracle_heads]
     if heads:
-        orc = rkv.score_evict(case.as_f32("q"), case.as_f32("k"), case.as_f32("v"), n_eff, case.lam, B,
-                              form="keysum", heads=heads)
+        orc = rkv.score_evict(case.as_f32("q"), case.as_f32("k"), case.as_f32("v"), n_eff, case.lam, budget,
+                              form="keysum", heads=heads, budgets=budgets)
+        z, idx = got[0], got[1]
         for bi, h in heads:
-            for name, g in zip("IRZ", got):
-                err = score_err(g[bi, h, :n_eff[bi]], orc[name][bi][h])
-                assert err <= SCORE_RTOL, (name, bi, h, err)
+            err = score_err(z[bi, h, :n_eff[bi]], orc["Z"][bi][h])
+            assert err <= SCORE_RTOL, ("Z", bi, h, err)
+            ns, gap = swaps(idx[bi, h], orc["idx"][bi, h], orc["Z"][bi][h])
+            assert gap < SWAP_WINDOW, (bi, h, ns, gap)
 
 
 def test_scores_fused_headline():
@@ -153,9 +195,13 @@ def test_scores_fused_256_chunks():
 
 
 def test_scores_fused_few_chunks_and_empty():
+    # sequence 0 keeps everything (700 <= B), 1 is empty, 2 holds one token
     case = synth.rkv_case("short", seed=5, wl=synth.WL_LAYER8B, b=3, hq=32, hkv=8, d=128, w=8,
                           lengths=[700, 0, 1], cap=8192, budget=1024)
-    _check(case, oracle_heads=4)
+    _check(case, heads=[(0, 0), (0, 5), (2, 0), (2, 7)])
+    case = synth.rkv_case("short2", seed=12, wl=synth.WL_LAYER8B, b=3, hq=32, hkv=8, d=128, w=8,
+                          lengths=[1300, 0, 1], cap=8192, budget=256)
+    _check(case)
 
 
 def test_scores_fused_length_above_cap():
@@ -170,20 +216,32 @@ def test_scores_fused_16_rows():
     _check(case)
 
 
-def test_score_evict_headline_selection():
-    """The whole call on the fused scores: the kept set equals the stage
-    select's on the same Z, and the kept rows are bit copies."""
-    case = synth.headline_case(layer=1)
-    q, k, v = dev(case.q, "bf16"), dev(case.k, "bf16"), dev(case.v, "bf16")
-    lens = dev_i32(case.lengths)
-    z = torch.empty((1, case.hkv, case.cap), device="cuda")
-    ko, vo, idx = K.kvsel_score_evict(q, k, v, lens, case.budget, case.lam, "keysum", scores_out=z)
-    want = K.kvsel_select_topb(z, lens, case.budget).cpu().numpy()
-    idx = idx.cpu().numpy()
-    assert np.array_equal(idx, want)
-    kb, vb = host_bits(ko), host_bits(vo)
-    for h in range(case.hkv):
-        m = int((idx[0, h] >= 0).sum())
-        assert m == case.budget
-        assert np.array_equal(kb[0, h, :m], case.k[0, h, idx[0, h, :m]])
-        assert np.array_equal(vb[0, h, :m], case.v[0, h, idx[0, h, :m]])
+def test_scores_fused_head_budgets():
+    case = synth.rkv_case("budgets", seed=8, wl=synth.WL_LAYER8B, b=2, hq=32, hkv=8, d=128, w=8,
+                          lengths=[16000, 9000], cap=16384, budget=2048)
+    _check(case, budgets=[0, 1, 2048, 3000, -4, 777, 2047, 1024], calls=2,
+           heads=[(0, 1), (0, 5), (1, 7)])
+
+
+def _tied(case, values):
+    """Keys that take only the given rows (all positions share a few keys),
+    so that Z takes a few values with thousands of copies each."""
+    k = case.k.copy()
+    rng = np.random.default_rng(11)
+    rows = synth.f32_to_bf16_bits(rng.standard_normal((values, case.d), dtype=np.float32))
+    pick = rng.integers(0, values, size=case.cap)
+    k[:, :] = rows[pick][None, None]
+    case.k = k
+    return case
+
+
+def test_scores_fused_all_equal():
+    case = _tied(synth.rkv_case("equal", seed=9, wl=synth.WL_LAYER8B, b=1, hq=32, hkv=8, d=128, w=8,
+                                lengths=[30000], cap=32768, budget=2048), 1)
+    _check(case, calls=2, heads=[(0, 0)])
+
+
+def test_scores_fused_three_values():
+    case = _tied(synth.rkv_case("three", seed=10, wl=synth.WL_LAYER8B, b=1, hq=32, hkv=8, d=128, w=8,
+                                lengths=[32768], cap=32768, budget=2048), 3)
+    _check(case, calls=2, heads=[(0, 3)])
