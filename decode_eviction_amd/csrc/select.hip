@@ -287,7 +287,7 @@ constexpr int kCandLds = 4096;   // candidates the finishing work-group stages i
 
 __global__ __launch_bounds__(256) void k_select_thresh(SelectParams p) {
   constexpr int NT = 256, NW = NT / kWave;
-  __shared__ uint32_t rh[256];                 // refinement histogram
+  __shared__ uint32_t rh[kHistBins];          // refinement histogram (11 bits per round)
   __shared__ uint32_t ck[kCandLds];
   __shared__ int32_t cpo[kCandLds];
   __shared__ uint32_t wsum[2][NW];
@@ -427,22 +427,26 @@ __global__ __launch_bounds__(256) void k_select_thresh(SelectParams p) {
     return head * p.cap + (long)lo * kSelChunk + (i - cpre[lo]);
   };
   if (staged) {
-    for (uint32_t i0 = tid; i0 < nc; i0 += 4 * NT) {
-      uint32_t kk[4];
-      int32_t pp[4];
+    // four threads per chunk, eight candidates each in flight, at known
+    // addresses (the chunk's candidates sit at its own offset)
+    const int c = tid >> 2;
+    const uint32_t cnt = c < nch ? cpre[c + 1] - cpre[c] : 0u;
+    const long src = head * p.cap + (long)c * kSelChunk;
+    for (uint32_t e0 = tid & 3; e0 < cnt; e0 += 32) {
+      uint32_t kk[8];
+      int32_t pp[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t i = i0 + u * NT;
-        const long src = cand_src(i < nc ? i : nc - 1);
-        kk[u] = ld_dev(p.candk + src);
-        pp[u] = ld_dev(p.candp + src);
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t e = min(e0 + 4 * u, cnt - 1);
+        kk[u] = ld_dev(p.candk + src + e);
+        pp[u] = ld_dev(p.candp + src + e);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t i = i0 + u * NT;
-        if (i < nc) {
-          ck[i] = kk[u];
-          cpo[i] = pp[u];
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t e = e0 + 4 * u;
+        if (e < cnt) {
+          ck[cpre[c] + e] = kk[u];
+          cpo[cpre[c] + e] = pp[u];
         }
       }
     }
@@ -471,30 +475,41 @@ __global__ __launch_bounds__(256) void k_select_thresh(SelectParams p) {
     }
   };
 
-  // refinement inside bin b1: rounds of 8 bits until at most 64 candidates
-  // remain in [lo, hi]
+  // refinement inside bin b1: rounds of 11 bits (thread t: sub-bins 8t ..
+  // 8t + 7) until at most 64 candidates remain in [lo, hi]; the bin's 21 low
+  // bits take at most two rounds
   uint32_t lo = b1 << (32 - kHistBits);
   uint32_t hi = lo | ((1u << (32 - kHistBits)) - 1u);
   uint32_t need = need1, inr = nc;
   while (lo < hi && inr > (uint32_t)kWave) {
     const uint32_t span = hi - lo;
     const int bits = 32 - __clz(span);
-    const int shift = bits > 8 ? bits - 8 : 0;
+    const int shift = bits > kHistBits ? bits - kHistBits : 0;
     const int nb = (int)(span >> shift) + 1;
-    rh[tid] = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rh[8 * tid + i] = 0u;
     __syncthreads();
     visit([&](uint32_t k, int32_t) {
       const uint32_t off = k - lo;
       if (off <= span) atomicAdd(&rh[off >> shift], 1u);
     });
     __syncthreads();
-    const uint32_t c = tid < nb ? rh[tid] : 0u;
-    const uint2 sc = block_scan_u32<NW>(c, wsum[0], tid);
-    const uint32_t above = sc.y - sc.x - c;  // candidates in bins above this one
-    if (above < need && above + c >= need) {
-      bc[0] = tid;
-      bc[1] = above;
-      bc[2] = c;
+    uint32_t hb[8], hs = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      hb[i] = 8 * tid + i < nb ? rh[8 * tid + i] : 0u;
+      hs += hb[i];
+    }
+    const uint2 sc = block_scan_u32<NW>(hs, wsum[0], tid);
+    uint32_t above = sc.y - sc.x - hs;  // candidates in sub-bins above this thread's
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      if (above < need && above + hb[i] >= need) {
+        bc[0] = 8 * tid + i;
+        bc[1] = above;
+        bc[2] = hb[i];
+      }
+      above += hb[i];
     }
     __syncthreads();
     const uint32_t bin = bc[0];
