@@ -234,6 +234,20 @@ __device__ __forceinline__ float inv_norm_of(float sumsq) {
 // Row of register i in the 32x32 output tile for lane half hf.
 __device__ __forceinline__ int tile_row(int i, int hf) { return 8 * (i >> 2) + 4 * hf + (i & 3); }
 
+// Inclusive prefix sum over the 64 lanes of a wave by DPP moves: shifts by
+// 1, 2, 4 and 8 lanes inside each 16-lane row, then lane 15's row total
+// added to rows 1 and 3 and lane 31's to rows 2 and 3.  Six VALU operations,
+// no LDS round trip (a shuffle-up ladder takes six).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // The value of lane l ^ 32.  v_permlane32_swap exchanges the upper half of
 // its first operand with the lower half of its second; with both set to v,
 // the first result holds v of the lower half in every lane of the upper half

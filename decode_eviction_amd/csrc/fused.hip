@@ -16,7 +16,7 @@
 //      barrier B
 //   3. every work-group loads the head's whole key row (at most 4096 keys)
 //      into LDS and selects there: a 2048-bin histogram of the top 11 bits,
-//      then rounds of 8 bits inside the bin that holds the B-th largest key,
+//      then rounds of 11 bits inside the bin that holds the B-th largest key,
 //      give the threshold key and how many of its copies are kept (lowest
 //      positions first); one scan over the row gives every kept position its
 //      ascending output slot.  Each work-group writes the slots of its own
@@ -317,6 +317,23 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   const char* qb = p.q + ((long)bi * p.hq + (long)h * p.g) * p.w * RB;
   uint64_t* pa = p.pub_a + head * kFusedMaxChunks * kFusedWordsA;
 
+  // q, then the chunk's keys (through a buffer resource that ends at token n:
+  // keys past it read as zeros, as load_frag gives them, without a branch),
+  // then V, which only the copies at the end need
+  using QSt = QStage<E, D, 1>;
+  __shared__ u32x4_t qs[QSt::kWords];
+  QSt::issue(qs, qb, p.m, tid);
+  const int tok0 = c0 + wave * 64;
+  Frag<NC> kf[2];
+  {
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kb + (long)c0 * RB, (uint32_t)min(n - c0, kChunk) * RB);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const uint32_t off = (uint32_t)((wave * 64 + 32 * tt + l32) * RB + hf * 16);
+#pragma unroll
+      for (int j = 0; j < NC; ++j) kf[tt].c[j] = buf_ld128(rk, off + 32 * j, 0);
+    }
+  }
   // V rows of the chunk into LDS (rows past cap arrive as zeros), for the
   // gather at the end
   __shared__ __attribute__((aligned(16))) char vl[kChunk * RB];
@@ -329,16 +346,6 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
       const int off = (wave * PER_WAVE + u) * 1024;
       buf_lds16(rv, vl + off, (uint32_t)(off + 16 * lane));
     }
-  }
-  using QSt = QStage<E, D, 1>;
-  __shared__ u32x4_t qs[QSt::kWords];
-  QSt::issue(qs, qb, p.m, tid);
-  const int tok0 = c0 + wave * 64;
-  Frag<NC> kf[2];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int tok = tok0 + 32 * tt + l32;
-    load_frag<E, D>(kf[tt], kb, tok, tok < n, hf);
   }
 
   // ---- phase 1: chunk statistics and unit-key sums (k_stats' arithmetic)
@@ -451,7 +458,6 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   // ---- phase 3: the head's keys in LDS, the threshold, slots of this chunk
   __shared__ uint32_t kall[kFusedKeys];
   __shared__ uint32_t lh[kHistBins];
-  __shared__ uint32_t rh[256];
   __shared__ uint32_t wsum[NW];
   __shared__ uint32_t bc[4];
   {
@@ -482,7 +488,7 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
     hb[i] = lh[8 * tid + i];
     hs += hb[i];
   }
-  if (tid == 0) bc[0] = bc[1] = 0u;
+  if (tid == 0) bc[0] = bc[1] = bc[2] = 0u;
   {
     const uint2 sc = block_scan_u32<NW>(hs, wsum, tid);
     uint32_t above = sc.y - sc.x - hs;
@@ -491,6 +497,7 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
       if (above < (uint32_t)B && above + hb[i] >= (uint32_t)B) {
         bc[0] = 8 * tid + i;
         bc[1] = above;
+        bc[2] = hb[i];
       }
       above += hb[i];
     }
@@ -499,26 +506,40 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   uint32_t lo = bc[0] << (32 - kHistBits);
   uint32_t hi = lo | ((1u << (32 - kHistBits)) - 1u);
   uint32_t need = (uint32_t)B - bc[1];
-  // rounds of 8 bits inside the bin until one key value remains
+  // rounds of 11 bits inside the bin (lh reused: thread t holds sub-bins
+  // 8t .. 8t + 7) until one key value remains: the bin's 21 low bits take
+  // at most two
   while (lo < hi) {
     const uint32_t span = hi - lo;
     const int bits = 32 - __clz(span);
-    const int shift = bits > 8 ? bits - 8 : 0;
+    const int shift = bits > kHistBits ? bits - kHistBits : 0;
     const int nb = (int)(span >> shift) + 1;
-    rh[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lh[8 * tid + i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const uint32_t off = mk[i] - lo;
-      if (KPT * tid + i < n && off <= span) atomicAdd(&rh[off >> shift], 1u);
+      if (KPT * tid + i < n && off <= span) atomicAdd(&lh[off >> shift], 1u);
     }
     __syncthreads();
-    const uint32_t c = tid < nb ? rh[tid] : 0u;
-    const uint2 sc = block_scan_u32<NW>(c, wsum, tid);
-    const uint32_t above = sc.y - sc.x - c;
-    if (above < need && above + c >= need) {
-      bc[0] = tid;
-      bc[1] = above;
+    uint32_t rb[8], rs = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      rb[i] = 8 * tid + i < nb ? lh[8 * tid + i] : 0u;
+      rs += rb[i];
+    }
+    const uint2 sc = block_scan_u32<NW>(rs, wsum, tid);
+    uint32_t above = sc.y - sc.x - rs;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      if (above < need && above + rb[i] >= need) {
+        bc[0] = 8 * tid + i;
+        bc[1] = above;
+        bc[2] = rb[i];
+      }
+      above += rb[i];
     }
     __syncthreads();
     const uint32_t bin = bc[0];
@@ -527,7 +548,6 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
     const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
     lo = (uint32_t)nlo;
     hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
-    __syncthreads();
   }
   const uint32_t kth = lo, need_eq = need;  // keys above kth all kept; need_eq copies of kth
   {

@@ -18,12 +18,7 @@ __device__ __forceinline__ uint32_t lanemask_lt_count(uint64_t m, int lane) {
 template <int NW = kSelWaves>
 __device__ __forceinline__ uint2 block_scan_u32(uint32_t v, uint32_t* wsum, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   uint32_t before = 0, total = 0;

@@ -210,21 +210,11 @@ __device__ __forceinline__ void write_chunk_offsets(const SelectParams& p, long 
                                                     uint32_t need_eq, int lane) {
   const int nch = (n + kSelChunk - 1) / kSelChunk;
   if (lane >= nch) gt = eq = 0u;
-  uint32_t x = eq;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(eq);
   const uint32_t eqb = x - eq;
   const uint32_t rem = need_eq > eqb ? need_eq - eqb : 0u;
   const uint32_t kept = gt + min(eq, rem);
-  uint32_t y2 = kept;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(y2, o, 64);
-    if (lane >= o) y2 += y;
-  }
+  const uint32_t y2 = wave_incl_scan(kept);
   if (lane < nch) {
     p.coff[head * p.nsc + lane] = y2 - kept;
     p.ceqb[head * p.nsc + lane] = eqb;
@@ -402,12 +392,7 @@ __global__ __launch_bounds__(256) void k_select_thresh(SelectParams p) {
   if (wave == 0) {
     const uint32_t cc = lane < nch ? ld_dev(p.ccnt + head * p.nsc + lane) : 0u;
     const uint32_t ac = lane < nch ? ld_dev(p.acnt + head * p.nsc + lane) : 0u;
-    uint32_t x = cc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_scan(cc);
     cpre[lane + 1] = x;
     if (lane == 0) cpre[0] = 0u;
     cgt[lane] = ac;
@@ -843,12 +828,7 @@ __global__ __launch_bounds__(256) void k_compact(SelectParams p) {
   // exclusive scan of packed counts over the 256 threads (each field < 2^16)
   const int lane = tid & 63, wave = tid >> 6;
   const uint32_t v = cg | (ce << 16);
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   uint32_t before = 0, total = 0;
