@@ -39,6 +39,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import glob
 import json
 import os
 import sys
@@ -380,7 +381,7 @@ def run_decode(mode, n_layers, hip, calls_per_layer=240):
     call, keep = rkv_caller(mode, seq, 1, cap, budget, out_bufs=obuf)
     total = n_layers * calls_per_layer
     cost = rkv_cost(mode, 1, cap, budget)
-    r = time_calls(call, rkv_kernels(mode, cap), cost, total, 2 * n_layers, hip, traced_steps=512)
+    r = time_calls(call, rkv_kernels(mode, cap), cost, total, 2 * n_layers, hip, traced_steps=min(512, total))
     r["calls"] = total
     r["tokens"] = total * cap
     return r
@@ -446,7 +447,7 @@ def run_decode_slots(mode, n_layers, hip, calls_per_layer=240):
 
     total = n_layers * calls_per_layer
     cost = rkv_cost(mode, 1, cap, budget)
-    r = time_calls(call, names, cost, total, 2 * n_layers, hip, traced_steps=512)
+    r = time_calls(call, names, cost, total, 2 * n_layers, hip, traced_steps=min(512, total))
     r["calls"] = total
     r["tokens"] = total * cap
     return r
@@ -579,7 +580,8 @@ def run_refreekv_rows(hip, n_layers, steps, k_rows=64):
 KERNEL_SOURCES = {"stats": "scores.hip", "reduce": "scores.hip", "pool": "scores.hip",
                   "gram": "gram.hip", "gram_fin": "gram.hip", "thresh": "select.hip",
                   "compact": "select.hip", "fused": "fused.hip", "scores": "fused.hip",
-                  "cut_energy": "cut.hip", "cut_scan": "cut.hip"}
+                  "evict": "select.hip", "select": "select.hip", "gather": "select.hip",
+                  "cut_energy": "cut.hip", "cut_scan": "cut.hip", "cut_compact": "cut.hip"}
 
 
 def source_digest(kernel: str) -> str:
@@ -611,21 +613,46 @@ def measured_traffic(profiles: str, mode: str, kernel: str):
     return int(float(vals["bytes_per_launch"]))
 
 
+def rocprof_avg_us(profiles: str, tag: str, kernel: str):
+    """(average duration in us, file) of the workload's kernel from a committed
+    rocprofv3 kernel-trace summary (profiles/kernel_trace_*.txt, lines
+    "bench: <tag> | <kernel> | <rocprof name> | <avg_us> | <source sha1>"),
+    or None when absent or when the kernel's sources changed since the trace."""
+    for path in sorted(glob.glob(os.path.join(profiles, "kernel_trace_*.txt"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("bench:"):
+                    continue
+                parts = [x.strip() for x in line[len("bench:"):].split("|")]
+                if len(parts) == 5 and parts[0] == tag and parts[1] == kernel and \
+                        parts[4] == source_digest(kernel):
+                    return float(parts[3]), os.path.basename(path)
+    return None
+
+
 def roofline(res, cost, profiles, tag):
     """Roofline of the call's dominant (longest) kernel: algorithmic flops or
-    bytes per launch over its average duration, with the counter-measured HBM
-    traffic from profiles/traffic_<tag>_<kernel>.txt when it is current."""
+    bytes per launch over its average duration (HIP events on the launch
+    stream, this run), with the counter-measured HBM traffic from
+    profiles/traffic_<tag>_<kernel>.txt and the same figure over the rocprofv3
+    kernel-trace duration committed under profiles/, each when current."""
     kern = res["kernels"]
     dom = max(kern, key=lambda k: kern[k]["avg_us"])
     c = cost[dom]
     traffic = measured_traffic(profiles, tag, dom)
-    if "flops" in c:
-        ach = c["flops"] / (kern[dom]["avg_us"] * 1e-6) / 1e12
-        return {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
-    ach = c["bytes"] / (kern[dom]["avg_us"] * 1e-6) / 1e9
-    return {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic}
+    mfma = "flops" in c
+    work, peak = (c["flops"], PEAK_BF16_TFLOPS) if mfma else (c["bytes"], PEAK_HBM_GBS)
+    scale = 1e12 if mfma else 1e9
+    ach = work / (kern[dom]["avg_us"] * 1e-6) / scale
+    out = {"kernel": dom, "bound": "mfma" if mfma else "hbm", "achieved": round(ach, 1), "peak": peak,
+           "unit": "TFLOP/s" if mfma else "GB/s", "frac": round(ach / peak, 4), "traffic": traffic,
+           "duration_source": "hipEvent average over the traced pass of this run"}
+    rp = rocprof_avg_us(profiles, tag, dom) if dom in KERNEL_SOURCES else None
+    if rp is not None:
+        a2 = work / (rp[0] * 1e-6) / scale
+        out["rocprof"] = {"avg_us": rp[0], "achieved": round(a2, 1), "frac": round(a2 / peak, 4),
+                          "source": "profiles/" + rp[1]}
+    return out
 
 
 def hbm_frac(nbytes, ms):
@@ -652,12 +679,94 @@ def cpu_baseline(case, seconds: float) -> dict:
     rkv.score_evict(qf, kf, vf, case.lengths, LAM, BUDGET, form="keysum")
     ks = time.perf_counter() - t1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t2 = time.perf_counter()
+        rkv.score_evict(qf, kf, vf, case.lengths, LAM, BUDGET, form="definition", heads=[(0, 0)])
+        one = time.perf_counter() - t2
     return {"value": round(N / per_layer, 1), "unit": "tokens/s/layer", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{heads} of {HKV} KV heads of one n={N} layer through the fp64 oracle "
                       f"(definition form: n x n cosine matrix), {el:.1f} s, scaled x{HKV / heads:g} "
                       f"to a layer; host has {os.cpu_count()} logical CPUs",
+            "one_thread_value": round(N / (one * HKV), 1),
+            "one_thread_sample": f"1 of {HKV} KV heads with one BLAS thread, {one:.1f} s, scaled x{HKV}",
             "keysum_form_value": round(N / ks, 1)}
+
+
+def _per_run(fn, min_seconds: float) -> float:
+    """Seconds per call of fn, repeated until min_seconds have passed (at least once)."""
+    t0 = time.perf_counter()
+    k = 0
+    while True:
+        fn()
+        k += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            return el / k
+
+
+def cpu_config_baselines(seconds: float = 1.0) -> dict:
+    """The oracle on each workload of the benchmark, with BLAS's default
+    threads and with one thread: tokens/s of the key-sum (identity) form of
+    the redundancy on every R-KV workload, of the pairwise definition on the
+    tiny and n = 4096 configurations, and of the ReFreeKV cut.  Each figure
+    times whole calls (or whole heads / sequences, scaled up) for about
+    `seconds`; the oracle is a reported baseline, not a target."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from decode_eviction_amd import synth
+    from oracle import refreekv, rkv
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    out = {}
+
+    def both(name, unit, tokens, fn, sample):
+        mt = _per_run(fn, seconds)
+        with threadpool_limits(limits=1):
+            st = _per_run(fn, seconds)
+        out[name] = {"value": round(tokens / mt, 1), "one_thread_value": round(tokens / st, 1),
+                     "unit": unit, "threads": int(threads), "kind": "oracle", "sample": sample}
+
+    c = synth.tiny_case(0)
+    q, k, v = c.as_f32("q"), c.as_f32("k"), c.as_f32("v")
+    for form in ("definition", "keysum"):
+        both(f"tiny_{form}", "tokens/s", 512,
+             lambda: rkv.score_evict(q, k, v, c.lengths, c.lam, c.budget, form=form),
+             f"the whole tiny call (1 head, n=512, fp32), {form} form")
+    c = synth.layer8b_case(0)
+    q, k, v = c.as_f32("q"), c.as_f32("k"), c.as_f32("v")
+    both("layer_n4096_definition", "tokens/s/layer", 4096 / 8,
+         lambda: rkv.score_evict(q, k, v, c.lengths, c.lam, c.budget, form="definition", heads=[(0, 0)]),
+         "one of 8 KV heads of the n=4096 layer, definition form (n x n cosine matrix), scaled x8")
+    both("layer_n4096_keysum", "tokens/s/layer", 4096,
+         lambda: rkv.score_evict(q, k, v, c.lengths, c.lam, c.budget, form="keysum"),
+         "the whole n=4096 layer (8 KV heads), key-sum form")
+    del c, q, k, v
+    c = synth.headline_case(layer=0)
+    q, k, v = c.as_f32("q"), c.as_f32("k"), c.as_f32("v")
+    both("headline_keysum", "tokens/s/layer", N,
+         lambda: rkv.score_evict(q, k, v, c.lengths, c.lam, c.budget, form="keysum"),
+         "the whole n=32768 layer (8 KV heads), key-sum form")
+    del c, q, k, v
+    ds = synth.decode_stream(0, total=2176 + 128)
+    qd = synth.bf16_bits_to_f32(ds.window(2176, W))
+    kd = synth.bf16_bits_to_f32(ds.k[None, :, :2176])
+    vd = synth.bf16_bits_to_f32(ds.v[None, :, :2176])
+    both("decode_keysum", "cache tokens scored/s", 2176,
+         lambda: rkv.score_evict(qd, kd, vd, [2176], LAM, 2048, form="keysum"),
+         "one decode-loop call (2176-slot cache, 8 KV heads, B=2048), key-sum form")
+    c = synth.batched_case(seed=0, b=4)
+    q, k, v = c.as_f32("q"), c.as_f32("k"), c.as_f32("v")
+    both("batched_keysum", "tokens/s/layer", 4 * 8192,
+         lambda: rkv.score_evict(q, k, v, c.lengths, c.lam, c.budget, form="keysum"),
+         "4 of the 64 sequences of 8192 tokens (8 KV heads each), key-sum form")
+    del c, q, k, v
+    cc = synth.cut_case(layer=2)
+    qc, kc = cc.as_f32("q"), cc.as_f32("k")
+    both("refreekv", "tokens/s/layer", int(np.sum(cc.lengths)),
+         lambda: refreekv.threshold_cut(qc, kc, cc.lengths, 2),
+         "one scored layer (16 ragged sequences of 1K-16K tokens, 4 KV heads) of the threshold cut")
+    return out
 
 
 def copy_calibration(mib: int = 512):
@@ -685,7 +794,7 @@ def run_variants(a, hip) -> dict:
 
     if "decode" in want:
         for mode in KERNELS:
-            r = run_decode(mode, 32, hip)
+            r = run_decode(mode, a.decode_layers, hip, a.decode_calls)
             log(f"decode/{mode}", r)
             out[f"decode_{mode}"] = {
                 "workload": "R-KV decode loop: 32 layers x 240 calls, each compressing a "
@@ -700,7 +809,7 @@ def run_variants(a, hip) -> dict:
             torch.cuda.empty_cache()
     if "decode" in want:
         for mode in KERNELS:
-            r = run_decode_slots(mode, 32, hip)
+            r = run_decode_slots(mode, a.decode_layers, hip, a.decode_calls)
             log(f"decode_slots/{mode}", r)
             tok = HKV * 2176
             out[f"decode_slots_{mode}"] = {
@@ -719,7 +828,7 @@ def run_variants(a, hip) -> dict:
             torch.cuda.empty_cache()
     if "batched" in want:
         for mode in KERNELS:
-            r = run_batched(mode, hip, 16 if mode == "keysum" else 6)
+            r = run_batched(mode, hip, a.batched_steps or (16 if mode == "keysum" else 6))
             log(f"batched/{mode}", r)
             out[f"batched_{mode}"] = {
                 "workload": "R-KV batched: 64 sequences x 8192 tokens, B=1024 (8B shape, w=8)",
@@ -780,6 +889,10 @@ def main():
     ap.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--variants-only", action="store_true",
                     help="skip the headline workload and print only the variants (for profiling)")
+    # shorter variant runs for counter collection (which serialises every kernel)
+    ap.add_argument("--decode-layers", type=int, default=32)
+    ap.add_argument("--decode-calls", type=int, default=240)
+    ap.add_argument("--batched-steps", type=int, default=0)
     a = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -862,6 +975,14 @@ def main():
         out.setdefault("variants", {}).update(run_variants(a, hip))
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(first, a.cpu_seconds)
+        # the oracle on every workload, beside the workload's own figures
+        per = cpu_config_baselines()
+        out["cpu_baseline"]["configs"] = per
+        where = {"decode_keysum": "decode_keysum", "batched_keysum": "batched_keysum",
+                 "refreekv": "refreekv", "headline_keysum": "keysum"}
+        for key, var in where.items():
+            if var in out.get("variants", {}):
+                out["variants"][var]["cpu_baseline"] = per[key]
     print(json.dumps(out))
 
 
