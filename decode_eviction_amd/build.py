@@ -1,6 +1,7 @@
 """Build libkvsel.so (gfx950) in-tree with hipcc.
 
     python -m decode_eviction_amd.build        # or __graft_entry__.build()
+    python -m decode_eviction_amd.build --debug  # libkvsel_debug.so (KVSEL_DEBUG)
 
 Each csrc/*.hip file is compiled to an object in _build/ and linked into
 decode_eviction_amd/libkvsel.so.  Every HIP compile disables the packed fp32
@@ -20,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvsel.so")
+LIB_DEBUG = os.path.join(PKG, "libkvsel_debug.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -38,9 +40,10 @@ SOURCES = ["api.hip", "scores.hip", "gram.hip", "select.hip", "cut.hip", "fused.
 EXTRA_FLAGS = {"gram.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, debug: bool = False) -> str:
+    obj = os.path.join(BUILD, ("debug_" if debug else "") + os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), *(["-DKVSEL_DEBUG"] if debug else []),
+           "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -51,20 +54,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, debug: bool = False) -> str:
+    """Build libkvsel.so; with debug=True build libkvsel_debug.so instead,
+    compiled with -DKVSEL_DEBUG (every launch waited for and a failing kernel
+    named on stderr).  The binding loads the library named by the KVSEL_LIB
+    environment variable when it is set."""
     os.makedirs(BUILD, exist_ok=True)
+    lib = LIB_DEBUG if debug else LIB
     with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, debug), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(debug="--debug" in sys.argv[1:])

@@ -6,6 +6,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
 
 namespace kvsel {
 
@@ -279,6 +280,31 @@ struct Trace {
   int k;
 };
 
+// Debug builds (-DKVSEL_DEBUG, `python -m decode_eviction_amd.build --debug`):
+// every launch is followed by a wait on the stream (skipped while the stream
+// is being captured), and a failing kernel is named on stderr with its grid,
+// so that a fault is reported at the kernel that caused it instead of at a
+// later call.
+inline hipError_t debug_check(const void* kern, dim3 grid, dim3 block, hipStream_t s, hipError_t e) {
+#ifdef KVSEL_DEBUG
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (e == hipSuccess && hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone)
+    e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    hipFunction_t f = nullptr;
+    const char* name = hipGetFuncBySymbol(&f, kern) == hipSuccess && f ? hipKernelNameRef(f) : nullptr;
+    fprintf(stderr, "kvsel: kernel %s, grid %u x %u x %u, block %u: %s\n", name ? name : "(unknown)",
+            grid.x, grid.y, grid.z, block.x, hipGetErrorString(e));
+  }
+#else
+  (void)kern;
+  (void)grid;
+  (void)block;
+  (void)s;
+#endif
+  return e;
+}
+
 template <typename F, typename... Args>
 inline hipError_t launch_k(F kern, dim3 grid, dim3 block, hipStream_t s, Trace* tr, Args... args) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -290,7 +316,7 @@ inline hipError_t launch_k(F kern, dim3 grid, dim3 block, hipStream_t s, Trace* 
     tr->k++;
   }
   hipExtLaunchKernelGGL(kern, grid, block, 0, s, e0, e1, 0, args...);
-  return hipGetLastError();
+  return debug_check(reinterpret_cast<const void*>(kern), grid, block, s, hipGetLastError());
 }
 
 hipError_t launch_stats(int dt, int d, int mode, const ScoreParams& p, hipStream_t s, Trace* tr);

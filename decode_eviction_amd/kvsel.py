@@ -28,7 +28,9 @@ import re
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvsel.so")
+# the library to load: $KVSEL_LIB when set (for instance the debug build,
+# decode_eviction_amd/libkvsel_debug.so), else the in-tree libkvsel.so
+LIB_PATH = os.environ.get("KVSEL_LIB") or os.path.join(_HERE, "libkvsel.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "kvsel.h")
 
 KVSEL_OK, KVSEL_ERR_INVALID_ARG, KVSEL_ERR_UNSUPPORTED, KVSEL_ERR_WORKSPACE, KVSEL_ERR_HIP = range(5)

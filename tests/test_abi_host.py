@@ -24,6 +24,20 @@ def test_exports_every_declared_function(lib):
     assert set(names) == set(K._SIGS)
 
 
+def test_debug_build_exports_the_same_functions():
+    """The KVSEL_DEBUG build (every launch waited for, a failing kernel named)
+    exports the same C ABI; __graft_entry__.build() builds it beside the
+    release library."""
+    import os
+
+    from decode_eviction_amd import build as B
+    if not os.path.exists(B.LIB_DEBUG):
+        pytest.skip("debug library not built (python -m decode_eviction_amd.build --debug)")
+    dbg = ctypes.CDLL(B.LIB_DEBUG)
+    missing = [n for n in K.header_functions() if not hasattr(dbg, n)]
+    assert not missing, missing
+
+
 def test_status_strings(lib):
     for s in range(5):
         assert K.status_string(s)
