@@ -3,6 +3,7 @@
 // caller's stream.  The formulas each entry point computes are stated in
 // include/kvsel.h.
 #include <math.h>
+#include <stdlib.h>
 
 #include <mutex>
 
@@ -62,6 +63,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int rows_padded(int m) { return m <= 32 ? 32 : (m <= 64 ? 64 : 128); }
 
 kvsel_status hip_status(hipError_t e) { return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP; }
+
+// KVSEL_SEPARATE_KERNELS=1 in the environment: the key-sum form always runs
+// its separate kernels (the one-launch kernels rely on all of their
+// work-groups being resident together, which kernels of other streams
+// holding compute units for long can prevent; results are the same bits)
+bool separate_kernels() {
+  const char* e = getenv("KVSEL_SEPARATE_KERNELS");
+  return e && e[0] == '1';
+}
 
 #define KV_TRY(expr)                         \
   do {                                       \
@@ -209,12 +219,13 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
   p.z_out = z_out;
   p.hist = hist;
   const int sm = mode == KVSEL_R_GRAM ? kModeGram : kModeKeysum;
-  // long caches, key-sum form: one launch reading K once, when its grid fits
-  // on the device at once
-  if (sm == kModeKeysum && dt == KVSEL_BF16 && d == 128 && p.m <= 32 && ws.fmerged) {
+  // longer caches, key-sum form: one launch reading K once, when its grid
+  // fits on the device at once
+  if (sm == kModeKeysum && dt == KVSEL_BF16 && d == 128 && p.m <= 32 && ws.fmerged && !separate_kernels()) {
     const ScoresFusedParams fp{p, ws.fepoch, ws.fpub_a, ws.fmerged};
-    if (scores_fused_fits(fp)) {
-      KV_TRY(launch_scores_fused(fp, stream, tr));
+    const int grid = scores_fused_grid(fp);
+    if (grid > 0) {
+      KV_TRY(launch_scores_fused(fp, grid, stream, tr));
       return KVSEL_OK;
     }
   }
@@ -526,7 +537,7 @@ static kvsel_status score_evict_impl(kvsel_dtype dt, kvsel_redundancy mode, cons
     fp.flags = ws.fflags;
     fp.pub_a = ws.fpub_a;
     fp.pub_b = ws.fpub_b;
-    if (fused_fits(fp)) return hip_status(launch_fused(fp, stream, tr));
+    if (!separate_kernels() && fused_fits(fp)) return hip_status(launch_fused(fp, stream, tr));
   }
   uint32_t* hist = cap <= kSelectLdsKeys ? ws.sel.hist : nullptr;
   st = run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, nullptr, nullptr,

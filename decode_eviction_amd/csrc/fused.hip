@@ -623,16 +623,16 @@ __device__ __forceinline__ uint32_t untag_w(const uint64_t* at, uint64_t w, uint
   return (uint32_t)w;
 }
 
+// One (chunk, head, sequence) unit of the score pass; k_scores_fused runs
+// the units of a call in rounds (below).
 template <typename E, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
-void k_scores_fused(ScoresFusedParams fp) {
+__device__ __forceinline__ void scores_fused_unit(const ScoresFusedParams& fp, int chunk, int h, int bi) {
   const ScoreParams& p = fp.s;
   using G = Geo<E, D>;
   using QSt = QStage<E, D, 1>;
   constexpr int NC = G::kNC, RB = G::kRowBytes, PC = E::kPerChunk, W = kFusedWordsA;
   constexpr int NP = 2 + D / 32;  // merge slices: rows 0-15, rows 16-31, 32 dimensions each
   static_assert(D == 128 && NP == kScoreMergeParts, "merge slices of the 128-dimension record");
-  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   // the wave index in a scalar register (the compiler cannot prove tid >> 6
   // uniform): wave-derived offsets then take no vector registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -814,6 +814,19 @@ void k_scores_fused(ScoresFusedParams fp) {
   }
 }
 
+// One unit per work-group over a grid of (chunk, head, sequence) units, all
+// resident at once (the host checks it; unit v = chunk + nchunk (head + Hkv
+// sequence)).  A persistent form that ran a larger call in rounds of
+// resident work-groups was slower than the separate kernels on 64 sequences
+// of 8192 tokens (511 against 463 us): a work-group cannot load its next
+// unit's keys while it waits for its head's merge, so rounds do not overlap.
+template <typename E, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void k_scores_fused(ScoresFusedParams fp) {
+  const int v = blockIdx.x, hb = v / fp.s.nchunk;
+  scores_fused_unit<E, D>(fp, v - hb * fp.s.nchunk, hb % fp.s.hkv, hb / fp.s.hkv);
+}
+
 // Work-groups of kern resident on the device at once (cached per device;
 // -1 when the query fails).
 template <typename K>
@@ -839,12 +852,14 @@ bool fused_fits(const FusedParams& p) {
 
 static int g_scores_capacity[64];
 
-bool scores_fused_fits(const ScoresFusedParams& p) {
-  return grid_fits(k_scores_fused<BF16, 128>, g_scores_capacity, (long)p.s.nchunk * p.s.hkv * p.s.b);
+int scores_fused_grid(const ScoresFusedParams& p) {
+  const long total = (long)p.s.nchunk * p.s.hkv * p.s.b;
+  if (total >= (1L << 31)) return 0;
+  return grid_fits(k_scores_fused<BF16, 128>, g_scores_capacity, total) ? (int)total : 0;
 }
 
-hipError_t launch_scores_fused(const ScoresFusedParams& p, hipStream_t s, Trace* tr) {
-  return launch_k(k_scores_fused<BF16, 128>, dim3(p.s.nchunk, p.s.hkv, p.s.b), dim3(256), s, tr, p);
+hipError_t launch_scores_fused(const ScoresFusedParams& p, int grid, hipStream_t s, Trace* tr) {
+  return launch_k(k_scores_fused<BF16, 128>, dim3(grid), dim3(256), s, tr, p);
 }
 
 }  // namespace kvsel

@@ -337,9 +337,10 @@ hipError_t launch_cut_compact(int dt, int d, const CutCompactParams& p, hipStrea
 // at once (then nothing is launched)
 bool fused_fits(const FusedParams& p);
 hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr);
-// the one-launch score pass: false when its grid does not fit on the device
-// at once (then nothing is launched)
-bool scores_fused_fits(const ScoresFusedParams& p);
-hipError_t launch_scores_fused(const ScoresFusedParams& p, hipStream_t s, Trace* tr);
+// the one-launch score pass: its grid (one work-group per (chunk, head,
+// sequence)), or 0 when those do not all fit on the device at once (then the
+// separate kernels run)
+int scores_fused_grid(const ScoresFusedParams& p);
+hipError_t launch_scores_fused(const ScoresFusedParams& p, int grid, hipStream_t s, Trace* tr);
 
 }  // namespace kvsel

@@ -98,8 +98,14 @@ size_t kvsel_score_evict_workspace(int b, int Hq, int Hkv, int d, int w, int cap
  * Key-sum form on a cache of more than 4096 slots (bf16, d = 128, g*w <= 32):
  * when the grid of ceil(cap / 256) * Hkv * b work-groups fits on the device
  * at once (1024 on 256 compute units), one kernel computes the scores,
- * reading each key once; otherwise the statistics, their merge and the
- * pooling run as separate kernels.  Both give the same bits. */
+ * reading each key once; otherwise, or with KVSEL_SEPARATE_KERNELS=1 in the
+ * environment, the
+ * statistics, their merge and the pooling run as separate kernels.  Both give
+ * the same bits.  The one-launch kernels (this one and the short-cache step
+ * of kvsel_score_evict) wait on work-groups of the same head: kernels of
+ * other streams that hold compute units for milliseconds can make a wait
+ * run out (reported in bit 2 of the error word); KVSEL_SEPARATE_KERNELS=1
+ * avoids them. */
 kvsel_status kvsel_scores(kvsel_dtype dt, kvsel_redundancy mode,
                           const void* q_window, const void* k, const int32_t* lengths,
                           int b, int Hq, int Hkv, int d, int w, int cap, float lambda,

@@ -7,9 +7,7 @@ The score pass computes each chunk's partials as k_stats does, merges them in
 k_reduce's order and pools as k_pool does, so I, R and Z must equal the
 multi-kernel pass's bit for bit, and so must the indices and compacted K
 and V rows that the selection kernels then derive from those scores.  The
-reference call repeats the same sequences along the batch until the grid no
-longer fits: the library then runs the separate kernels, whose per-sequence
-results do not depend on the batch.  Each case reads from the traced entry
+reference call runs the separate kernels (KVSEL_SEPARATE_KERNELS=1).  Each case reads from the traced entry
 point which path ran (a silent fallback would make the comparison vacuous),
 checks that no wait timed out (bit 2 of the error word) and compares sampled
 heads with the oracle within the score tolerance.  Repeated calls on one
@@ -22,6 +20,7 @@ budgets (0, 1, out of range), all-equal keys (the threshold bin holds every
 key and is read from memory) and three-valued ties."""
 
 import ctypes
+import os
 
 import numpy as np
 import pytest
@@ -91,11 +90,14 @@ def _scores(q, k, lens, lam, ws=None):
     return i, r, z
 
 
-def _reps_unfused(b, hkv, cap):
-    """Copies of the batch whose grid exceeds the capacity of every device
-    this library targets (256 compute units, at most 8 work-groups each)."""
-    per = -(-cap // 256) * hkv * b
-    return -(-2049 // per) + 1
+class _separate:
+    """Calls inside run the separate kernels (KVSEL_SEPARATE_KERNELS=1)."""
+
+    def __enter__(self):
+        os.environ["KVSEL_SEPARATE_KERNELS"] = "1"
+
+    def __exit__(self, *a):
+        os.environ.pop("KVSEL_SEPARATE_KERNELS", None)
 
 
 def _host(t):
@@ -125,12 +127,10 @@ def _check(case, oracle_heads=2, calls=3, lengths=None, budget=None, budgets=Non
     q, k, v = dev(case.q, "bf16"), dev(case.k, "bf16"), dev(case.v, "bf16")
     lens = dev_i32(lengths)
     assert launched_kernels(q, k, v, lens, budget, case.lam) == 3, "the one-launch score pass did not run"
-    reps = _reps_unfused(case.b, case.hkv, case.cap)
-    qr, kr, vr = (torch.cat([t] * reps, 0).contiguous() for t in (q, k, v))
-    lr = dev_i32(np.tile(lengths, reps))
-    assert launched_kernels(qr, kr, vr, lr, budget, case.lam) == 5, "the reference ran a fused path"
-    ref = [x.cpu().numpy()[:case.b] for x in _scores(qr, kr, lr, case.lam)]
-    ref_ev = [_host(x)[:case.b] for x in _evict(qr, kr, vr, lr, budget, case.lam, budgets)]
+    with _separate():
+        assert launched_kernels(q, k, v, lens, budget, case.lam) == 5, "the reference ran a fused path"
+        ref = [x.cpu().numpy() for x in _scores(q, k, lens, case.lam)]
+        ref_ev = [_host(x) for x in _evict(q, k, v, lens, budget, case.lam, budgets)]
 
     n_eff = np.clip(lengths, 0, case.cap)
     bad_len = ((lengths < 0) | (lengths > case.cap)).any()
@@ -245,3 +245,4 @@ def test_scores_fused_three_values():
     case = _tied(synth.rkv_case("three", seed=10, wl=synth.WL_LAYER8B, b=1, hq=32, hkv=8, d=128, w=8,
                                 lengths=[32768], cap=32768, budget=2048), 3)
     _check(case, calls=2, heads=[(0, 3)])
+
