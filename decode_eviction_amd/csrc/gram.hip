@@ -446,27 +446,42 @@ __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
         for (int i = 0; i < 4; ++i) acc[s2][rt][h2][i] = 0.f;
   float w_carry[2] = {0.f, 0.f}, csA_carry[2] = {0.f, 0.f};
 
-  // fold row tile t4 of set S: 8 row-sum FMAs, 8 column-sum FMAs
-  auto fold_part = [&](int S, int t4, const float* w, float* cs) {
-    const int rt = 4 * S + t4;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        rsum[rt][i] = fmaf(acc[S][t4][h2][i], w[h2], rsum[rt][i]);
-        cs[2 * h2 + (i & 1)] = fmaf(acc[S][t4][h2][i], wrow[rt][i], cs[2 * h2 + (i & 1)]);
-      }
+  // element e = 4 h2 + i of row tile t4 of set S: one row-sum FMA, one
+  // column-sum FMA
+  auto fold_one = [&](int S, int t4, int e, const float* w, float* cs) {
+    const int rt = 4 * S + t4, h2 = e >> 2, i = e & 3;
+    rsum[rt][i] = fmaf(acc[S][t4][h2][i], w[h2], rsum[rt][i]);
+    cs[2 * h2 + (i & 1)] = fmaf(acc[S][t4][h2][i], wrow[rt][i], cs[2 * h2 + (i & 1)]);
+    // pinned beside their product: left free, the compiler sinks a tile's
+    // folds past the column flush into one run that the matrix core waits out
+    asm volatile("" : "+v"(rsum[rt][i]), "+v"(cs[2 * h2 + (i & 1)]));
   };
-  auto mfma8 = [&](int S, int j, const u32x4_t* b) {
+  auto fold_part = [&](int S, int t4, const float* w, float* cs) {
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        f32x4_t c = acc[S][t4][h2];
-        if (j == 0) c = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        acc[S][t4][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, af[4 * S + t4][j]), __builtin_bit_cast(bf16x8_t, b[h2]), c, 0, 0, 0);
-      }
+    for (int e = 0; e < 8; ++e) fold_one(S, t4, e, w, cs);
+  };
+  // One 16x16x32 product into the accumulator of row tile t4 of set S,
+  // column half h2: fragments in accumulation registers, the accumulator in
+  // arch registers, where the folds read it.  A product runs 16 cycles, and
+  // the SIMD keeps the matrix core fed only while at most two vector
+  // instructions sit between consecutive products; the fold is exactly two
+  // per product.  The instruction is written out because with the builtin
+  // the compiler regroups products and folds (and pads them with wait
+  // states), leaving gaps the matrix core waits out.  Written out, the
+  // product is invisible to the compiler's hazard tracking, so the schedule
+  // itself provides the wait states a vector read of a result needs: every
+  // fold reads an accumulator at least seven products and fourteen folds
+  // (over 20 instructions) after the product that completed it, and nothing
+  // in the loop copies a fragment or an accumulator.
+  auto mfma1 = [&](int S, int t4, int h2, int j, const u32x4_t& b) {
+    if (j == 0)
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0"
+                   : "=v"(acc[S][t4][h2])
+                   : "a"(af[4 * S + t4][j]), "a"(b));
+    else
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                   : "+v"(acc[S][t4][h2])
+                   : "a"(af[4 * S + t4][j]), "a"(b));
   };
 
 #pragma unroll
@@ -527,24 +542,19 @@ __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
           dma_lds16(src + (2 * j + 1) * 32, dst + (2 * j + 1) * 4096);
           if (j == 0) dma_lds4(wv + c0n + (wave & 1) * 64 + lane, &wcol[dbuf][(wave & 1) * 64]);
         }
-        // B fragments only feed the matrix cores: keep them in accumulation
-        // registers; the constraint sits at the k-step's first use, where
-        // its read is waited for
-        asm volatile("" : "+a"(bq[cur][j][0]), "+a"(bq[cur][j][1]));
-        mfma8(0, j, bq[cur][j]);
-        fold_part(1, j, wprev, b4);
+        // issue order: one matrix-core instruction, then its two folds,
+        // eight times; the next tile's LDS reads after the first
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-          bq[prv][j][h2] = *reinterpret_cast<const u32x4_t*>(b_addr(nb_buf, nct, h2, j));
-        // issue order: one matrix-core instruction, then two vector ALU
-        // instructions, eight times; the next tile's LDS reads after the first
+        for (int q = 0; q < 8; ++q) {
+          mfma1(0, q >> 1, q & 1, j, bq[cur][j][q & 1]);
+          fold_one(1, j, q, wprev, b4);
+          if (q == 0) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          if (k == 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            for (int h2 = 0; h2 < 2; ++h2)
+              bq[prv][j][h2] = *reinterpret_cast<const u32x4_t*>(b_addr(nb_buf, nct, h2, j));
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
       if (ct == 0 && st >= 2) flush_finish(st - 2);
       {
@@ -558,14 +568,12 @@ __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
       float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        mfma8(1, j, bq[cur][j]);
-        fold_part(0, j, wt[ct], a4);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        for (int q = 0; q < 8; ++q) {
+          mfma1(1, q >> 1, q & 1, j, bq[cur][j][q & 1]);
+          fold_one(0, j, q, wt[ct], a4);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
       csA_carry[0] = a4[0] + a4[1];
       csA_carry[1] = a4[2] + a4[3];
