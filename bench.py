@@ -87,16 +87,37 @@ def scores_fused(mode: str, cap: int, b: int = 1, hkv: int = HKV, m: int = HQ //
             and nch * hkv * b <= SCORES_FUSED_CAPACITY)
 
 
-def rkv_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV) -> list:
+SEL_CHUNK = 512               # kSelChunk: positions per selection work-group
+SELECT_COMPACT_CAPACITY = 1280  # work-groups of the one-launch selection resident at once (five per CU)
+THRESH_HEADS_MANY = 64       # kThreshHeadsMany: from this many heads, one threshold work-group per head
+
+
+def select_one_launch(cap: int, b: int = 1, hkv: int = HKV, budget: int = BUDGET) -> bool:
+    """The library selects and compacts in one launch (k_select_compact) when
+    the cache fits the split select (cap <= 32768), the heads are few, a
+    chunk of 512 positions keeps about 64 rows or fewer (one gathering
+    work-group: the host's split is ceil(kept / 64) with kept = ceil(512 B /
+    cap)) and the grid of ceil(cap / 512) * Hkv * b work-groups fits at once."""
+    nsc = -(-cap // SEL_CHUNK)
+    kept_chunk = -(-SEL_CHUNK * budget // cap)
+    gsplit = min(8, max(1, -(-kept_chunk // 64)))
+    return (cap <= 32768 and b * hkv < THRESH_HEADS_MANY and gsplit == 1 and nsc <= 64
+            and nsc * hkv * b <= SELECT_COMPACT_CAPACITY)
+
+
+def rkv_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV, budget: int = BUDGET) -> list:
     """Kernels one R-KV call launches, in order: the fused step alone when it
     applies; the one-launch score pass in place of stats, reduce and pool when
     that applies; otherwise with at most 16 chunks of 256 keys per head k_pool
-    merges the chunk partials itself and k_reduce is not launched."""
+    merges the chunk partials itself and k_reduce is not launched; the
+    one-launch selection in place of thresh and compact when it applies."""
     if fused_step(mode, cap, b, hkv):
         return ["fused"]
     ks = unfused_kernels(mode, cap)
     if scores_fused(mode, cap, b, hkv):
         ks = ["scores"] + [k for k in ks if k not in ("stats", "reduce", "pool")]
+    if select_one_launch(cap, b, hkv, budget):
+        ks = [k for k in ks if k not in ("thresh", "compact")] + ["select_compact"]
     return ks
 
 
@@ -145,6 +166,8 @@ def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int =
         "thresh": {"bytes": 4 * tok},
         "compact": {"bytes": 4 * tok + 4 * b * hkv * budget + gath},
     }
+    # the one-launch selection: the scores once, the indices and the gather
+    cost["select_compact"] = {"bytes": 4 * tok + 4 * b * hkv * budget + gath}
     # slot reuse: scores and position map read, evicted list written
     cost["evict"] = {"bytes": 8 * tok + 4 * b * hkv * max(n - budget, 0)}
     # the fused short-cache step: K once, Z and the indices written, the kept
@@ -462,7 +485,7 @@ def run_batched(mode, hip, steps):
     del c
     b, n, budget = 64, 8192, 1024
     call, keep = rkv_caller(mode, [layer], b, n, budget)
-    r = time_calls(call, rkv_kernels(mode, n, b), rkv_cost(mode, b, n, budget), steps, 2, hip)
+    r = time_calls(call, rkv_kernels(mode, n, b, budget=budget), rkv_cost(mode, b, n, budget), steps, 2, hip)
     r["tokens"] = b * n
     r["step_bytes"] = rkv_step_bytes(b, n, budget)
     return r
@@ -578,7 +601,7 @@ def run_refreekv_rows(hip, n_layers, steps, k_rows=64):
 
 
 KERNEL_SOURCES = {"stats": "scores.hip", "reduce": "scores.hip", "pool": "scores.hip",
-                  "gram": "gram.hip", "gram_fin": "gram.hip", "thresh": "select.hip",
+                  "gram": "gram.hip", "gram_fin": "gram.hip", "thresh": "select.hip", "select_compact": "select.hip",
                   "compact": "select.hip", "fused": "fused.hip", "scores": "fused.hip",
                   "evict": "select.hip", "select": "select.hip", "gather": "select.hip",
                   "cut_energy": "cut.hip", "cut_scan": "cut.hip", "cut_compact": "cut.hip"}

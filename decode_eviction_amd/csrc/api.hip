@@ -162,10 +162,10 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap, kvsel_redund
   w.sel.thr = c.take<uint32_t>(heads * 4);
   w.sel.coff = c.take<uint32_t>(heads * w.sel.nsc);
   w.sel.ceqb = c.take<uint32_t>(heads * w.sel.nsc);
-  w.sel.acnt = c.take<uint32_t>(heads * w.sel.nsc);
-  w.sel.ccnt = c.take<uint32_t>(heads * w.sel.nsc);
-  w.sel.candk = c.take<uint32_t>(heads * cap);
-  w.sel.candp = c.take<int32_t>(heads * cap);
+  w.sel.acnt = reinterpret_cast<uint32_t*>(c.take<uint64_t>(heads * w.sel.nsc));
+  w.sel.ccnt = w.sel.acnt ? w.sel.acnt + heads * w.sel.nsc : nullptr;
+  w.sel.candk = reinterpret_cast<uint32_t*>(c.take<uint64_t>(heads * cap));
+  w.sel.candp = w.sel.candk ? reinterpret_cast<int32_t*>(w.sel.candk + heads * cap) : nullptr;
   w.bytes = (c.off + kAlign - 1) / kAlign * kAlign;
   return w;
 }
@@ -279,10 +279,12 @@ SelWs carve_select(Carver& c, int b, int hkv, int cap) {
   w.thr = c.take<uint32_t>(heads * 4);
   w.coff = c.take<uint32_t>(heads * w.nsc);
   w.ceqb = c.take<uint32_t>(heads * w.nsc);
-  w.acnt = c.take<uint32_t>(heads * w.nsc);
-  w.ccnt = c.take<uint32_t>(heads * w.nsc);
-  w.candk = c.take<uint32_t>(heads * cap);
-  w.candp = c.take<int32_t>(heads * cap);
+  // per-chunk counts and candidates: each pair one region, which the
+  // one-launch selection uses as 64-bit tagged words instead
+  w.acnt = reinterpret_cast<uint32_t*>(c.take<uint64_t>(heads * w.nsc));
+  w.ccnt = w.acnt ? w.acnt + heads * w.nsc : nullptr;
+  w.candk = reinterpret_cast<uint32_t*>(c.take<uint64_t>(heads * cap));
+  w.candp = w.candk ? reinterpret_cast<int32_t*>(w.candk + heads * cap) : nullptr;
   return w;
 }
 
@@ -305,6 +307,9 @@ SelectParams select_params(const SelWs& w, const float* z, const int32_t* length
   sp.ccnt = w.ccnt;
   sp.candk = w.candk;
   sp.candp = w.candp;
+  sp.cand64 = reinterpret_cast<uint64_t*>(w.candk);
+  sp.cnt64 = reinterpret_cast<uint64_t*>(w.acnt);
+  sp.one_launch = separate_kernels() ? 0 : 1;
   sp.err = w.err;
   return sp;
 }

@@ -341,6 +341,49 @@ __device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
 // wait until this wave's vector memory operations (stores included) are done
 __device__ __forceinline__ void vmem_done() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); }
 
+// ---- records exchanged between work-groups of one launch
+//
+// Bounded waits: a wait that runs this many polls sets bit 2 of the call's
+// error word and gives up (the kernel still finishes).
+constexpr int kSpinLimit = 1 << 20;
+
+// SplitMix64 finaliser (Steele, Lea and Flood's SplitMix generator): a
+// bijection of 64-bit words with good avalanche.
+__device__ __forceinline__ uint64_t mix64(uint64_t x) {
+  x += 0x9e3779b97f4a7c15ull;
+  x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
+  x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
+  return x ^ (x >> 31);
+}
+
+// The 32-bit tag of a head's data words and its 64-bit barrier tokens in
+// one call: hashes of the head's epoch and the head's index, so that words
+// another head or an earlier call left in the workspace (one reused across
+// shapes holds them at any address) never pass for this call's.
+__device__ __forceinline__ uint64_t head_key(uint64_t ep, long head, uint64_t k) {
+  return mix64(4 * ep + k + ((uint64_t)head << 44));
+}
+__device__ __forceinline__ uint32_t head_tag(uint64_t ep, long head) {
+  return (uint32_t)(head_key(ep, head, 0) >> 32);
+}
+
+// A 64-bit word holding a 32-bit value (low half) and a call's tag (high half).
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t v) { return ((uint64_t)tag << 32) | v; }
+
+// The value of the tagged word at `at`, read once as w: polled again until
+// its tag is there (at most kSpinLimit times; then bit 2 of *err, if given).
+__device__ __forceinline__ uint32_t untag_w(const uint64_t* at, uint64_t w, uint32_t tag, int32_t* err) {
+  for (int it = 0; (uint32_t)(w >> 32) != tag; ++it) {
+    if (it == kSpinLimit) {
+      if (err) atomicOr(err, 4);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    w = ld_dev(at);
+  }
+  return (uint32_t)w;
+}
+
 // x * y rounded to fp32 on its own, never fused into a following add (the
 // product is the value another kernel stores and reloads)
 __device__ __forceinline__ float mul_unfused(float x, float y) {

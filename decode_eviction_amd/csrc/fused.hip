@@ -47,28 +47,7 @@
 
 namespace kvsel {
 
-constexpr int kSpinLimit = 1 << 20;
 constexpr int kFusedKeys = kFusedMaxChunks * kChunk;   // 4096
-
-// SplitMix64 finaliser (Steele, Lea and Flood's SplitMix generator): a
-// bijection of 64-bit words with good avalanche.
-__device__ __forceinline__ uint64_t mix64(uint64_t x) {
-  x += 0x9e3779b97f4a7c15ull;
-  x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
-  x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
-  return x ^ (x >> 31);
-}
-
-// The 32-bit tag of a head's data words and its 64-bit barrier tokens in
-// one call: hashes of the head's epoch and the head's index, so that words
-// another head or an earlier call left in the workspace (one reused across
-// shapes holds them at any address) never pass for this call's.
-__device__ __forceinline__ uint64_t head_key(uint64_t ep, long head, uint64_t k) {
-  return mix64(4 * ep + k + ((uint64_t)head << 44));
-}
-__device__ __forceinline__ uint32_t head_tag(uint64_t ep, long head) {
-  return (uint32_t)(head_key(ep, head, 0) >> 32);
-}
 
 __device__ __forceinline__ uint64_t* flag_row(const FusedParams& p, int which, long head) {
   return p.flags + ((long)which * p.b * p.hkv + head) * kFusedMaxChunks;
@@ -97,7 +76,6 @@ __device__ __forceinline__ void wait_flags(const FusedParams& p, int which, long
   __syncthreads();
 }
 
-__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t v) { return ((uint64_t)tag << 32) | v; }
 
 // The value of a tagged word already read as w: read again while the tag is
 // missing.
@@ -302,7 +280,10 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
     for (int i = 0; i < p.b; ++i) f |= len_bad(p.lengths[i], p.cap) ? 1 : 0;
     if (p.budgets)
       for (int i = 0; i < p.hkv; ++i) f |= (p.budgets[i] < 0 || p.budgets[i] > p.budget) ? 2 : 0;
-    *p.err = f;
+    // device scope, as the other work-groups' atomicOr of bit 2: a plain
+    // store would stay in this XCD's L2 and, written back at the end,
+    // could overwrite a bit set meanwhile from another XCD
+    __hip_atomic_store(p.err, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int n = clamp_len(p.lengths[bi], p.cap);
   const int B = fused_budget(p, h);
@@ -609,20 +590,6 @@ hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr) {
 // launches the kernel only when the whole grid fits on the device at once; a
 // poll that still exceeds its limit sets bit 2 of the error word.
 
-// The value of the tagged word at `at`, read once as w: polled again until
-// its tag is there.
-__device__ __forceinline__ uint32_t untag_w(const uint64_t* at, uint64_t w, uint32_t tag, int32_t* err) {
-  for (int it = 0; (uint32_t)(w >> 32) != tag; ++it) {
-    if (it == kSpinLimit) {
-      atomicOr(err, 4);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-    w = ld_dev(at);
-  }
-  return (uint32_t)w;
-}
-
 // One (chunk, head, sequence) unit of the score pass; k_scores_fused runs
 // the units of a call in rounds (below).
 template <typename E, int D>
@@ -642,7 +609,10 @@ __device__ __forceinline__ void scores_fused_unit(const ScoresFusedParams& fp, i
   if (chunk == 0 && h == 0 && bi == 0 && tid == 0) {
     int f = 0;
     for (int i = 0; i < p.b; ++i) f |= len_bad(p.lengths[i], p.cap) ? 1 : 0;
-    *p.err = f;
+    // device scope, as the other work-groups' atomicOr of bit 2: a plain
+    // store would stay in this XCD's L2 and, written back at the end,
+    // could overwrite a bit set meanwhile from another XCD
+    __hip_atomic_store(p.err, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // the head's first-level histogram (and the selection state after it)
   // starts at zero: chunk 0 clears it before it publishes its merged rows,
@@ -825,22 +795,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 void k_scores_fused(ScoresFusedParams fp) {
   const int v = blockIdx.x, hb = v / fp.s.nchunk;
   scores_fused_unit<E, D>(fp, v - hb * fp.s.nchunk, hb % fp.s.hkv, hb / fp.s.hkv);
-}
-
-// Work-groups of kern resident on the device at once (cached per device;
-// -1 when the query fails).
-template <typename K>
-static bool grid_fits(K kern, int* cache, long grid) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-  if (cache[dev] == 0) {
-    int per_cu = 0, ncu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return false;
-    cache[dev] = per_cu * ncu > 0 ? per_cu * ncu : -1;
-  }
-  return cache[dev] > 0 && grid <= cache[dev];
 }
 
 static int g_fused_capacity[64];

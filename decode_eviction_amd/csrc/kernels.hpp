@@ -161,6 +161,13 @@ struct SelectParams {
   uint32_t* ccnt;           // [b][Hkv][nsc]
   uint32_t* candk;          // [b][Hkv][cap]
   int32_t* candp;           // [b][Hkv][cap]
+  // one-launch selection and compaction (k_select_compact): tagged words
+  // over the memory of candk/candp ([b][Hkv][cap], candidate keys at the
+  // chunk's own offset) and of acnt/ccnt ([b][Hkv][nsc], candidates | keys
+  // above the bin << 16); the head's epoch is word 3 of its thr record
+  uint64_t* cand64;
+  uint64_t* cnt64;
+  int one_launch;           // the caller allows it (otherwise always two kernels)
   // fused gather (k == nullptr: indices only)
   const char* k;
   const char* v;
@@ -342,5 +349,21 @@ hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr);
 // separate kernels run)
 int scores_fused_grid(const ScoresFusedParams& p);
 hipError_t launch_scores_fused(const ScoresFusedParams& p, int grid, hipStream_t s, Trace* tr);
+
+// Work-groups of kern resident on the device at once (cached per device;
+// -1 when the query fails).
+template <typename K>
+inline bool grid_fits(K kern, int* cache, long grid) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (cache[dev] == 0) {
+    int per_cu = 0, ncu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return false;
+    cache[dev] = per_cu * ncu > 0 ? per_cu * ncu : -1;
+  }
+  return cache[dev] > 0 && grid <= cache[dev];
+}
 
 }  // namespace kvsel

@@ -887,6 +887,403 @@ __global__ __launch_bounds__(256) void k_compact(SelectParams p) {
   }
 }
 
+// The threshold kernel for a call: one work-group per chunk and head while
+// the grid is small, one per head (k_select_thresh_head) for many heads.
+constexpr int kThreshHeadsMany = 64;
+
+// ------------------------------------------------- one-launch selection
+//
+// k_select_thresh and k_compact in one launch, for calls whose grid is
+// resident at once and whose chunks keep few rows (about B/cap of 512, at
+// most 64: one work-group gathers them).  The finishing work-group of
+// k_select_thresh, and the launch of k_compact after it, wait on each
+// other; here no work-group waits for a finisher.  Every work-group
+// publishes its chunk's candidates (the keys in the first-level bin) and
+// counts as tagged words, reads those of every chunk of its head, finds the
+// threshold itself (the same rounds as k_select_thresh over the same keys,
+// so the same threshold in every work-group) and its chunk's output slot from
+// the per-chunk counts, and compacts its chunk.  Ties at the final rank are
+// ordered by candidate index instead of position: any strict order gives the
+// same threshold key and the same number of its copies to keep (which
+// copies are kept is decided by position, in the compaction, as in
+// k_compact).  Results equal the two-kernel path's bit for bit.
+//
+// The tags hash the head's epoch (word 3 of its thr record, advanced by
+// chunk 0 once it has every chunk's counts, by which time every work-group of
+// the head has read the epoch); a poll that exceeds its limit sets bit 2 of
+// the error word.
+constexpr int kSelFusedCand = 4096;  // candidates staged in LDS (more: read from memory)
+
+__global__ __launch_bounds__(256) void k_select_compact(SelectParams p) {
+  constexpr int NT = 256, NW = NT / kWave, PPT = kSelChunk / NT;
+  __shared__ uint32_t rh[kHistBins];          // refinement histogram
+  __shared__ uint32_t ck[kSelFusedCand];      // staged candidate keys
+  __shared__ uint8_t cch[kSelFusedCand];      // and their chunks
+  __shared__ uint32_t wsum[2][NW];
+  __shared__ uint32_t cpre[65];               // prefix of the per-chunk candidate counts
+  __shared__ uint32_t cgt[64], ceq[64];       // per chunk: keys above / equal to the threshold
+  __shared__ uint32_t rk[kWave], ri[kWave];
+  __shared__ uint32_t bc[4];
+  __shared__ uint32_t mine[2];                // this chunk's first output slot, copies of kth before it
+  __shared__ int32_t rows[kSelChunk];         // kept positions by slot - chunk offset
+
+  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long head = (long)bi * p.hkv + h;
+  const uint32_t* hg = p.hist + head * kHistStride;
+  const int c0 = chunk * kSelChunk;
+  const int p0 = c0 + tid * PPT;
+  // the histogram (8 bins per thread), the chunk's scores and the head's
+  // epoch are requested before the length arrives
+  const uint4 hv0 = reinterpret_cast<const uint4*>(hg)[2 * tid];
+  const uint4 hv1 = reinterpret_cast<const uint4*>(hg)[2 * tid + 1];
+  const float* zp = p.z + head * p.cap;
+  float zv[PPT];
+#pragma unroll
+  for (int e = 0; e < PPT; ++e) zv[e] = zp[min(p0 + e, p.cap - 1)];
+  const uint32_t ep = ld_dev(p.thr + head * 4 + 3);
+  const int n = clamp_len(p.lengths[bi], p.cap);
+  const int B = head_budget(p, h);
+  if (chunk == 0 && tid == 0) flag_select_errors(p, h, bi);
+  int32_t* out = p.idx + head * p.budget;
+  if (chunk == 0)
+    for (int t = min(n, B) + tid; t < p.budget; t += NT) out[t] = -1;
+  if (c0 >= n || B == 0) return;
+  const int nch = (n + kSelChunk - 1) / kSelChunk;
+  const bool all = n <= B;
+  uint32_t key[PPT];
+#pragma unroll
+  for (int e = 0; e < PPT; ++e) key[e] = score_key(zv[e]);
+  uint32_t kth = 0u, need_eq = 0u, off = (uint32_t)c0, eqb = 0u;
+
+  if (!all) {
+    const uint32_t tag = head_tag(ep, head);
+    // level 1: the bin where the count from the top reaches B (as in
+    // k_select_thresh)
+    const uint32_t hb[8] = {hv0.x, hv0.y, hv0.z, hv0.w, hv1.x, hv1.y, hv1.z, hv1.w};
+    uint32_t hs = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hs += hb[i];
+    if (tid == 0) bc[0] = bc[1] = 0u;
+    {
+      const uint2 sc = block_scan_u32<NW>(hs, wsum[0], tid);
+      uint32_t above = sc.y - sc.x - hs;
+#pragma unroll
+      for (int i = 7; i >= 0; --i) {
+        if (above < (uint32_t)B && above + hb[i] >= (uint32_t)B) {
+          bc[0] = 8 * tid + i;
+          bc[1] = above;
+        }
+        above += hb[i];
+      }
+      __syncthreads();
+    }
+    const uint32_t b1 = bc[0];
+    const uint32_t need1 = (uint32_t)B - bc[1];
+
+    // this chunk: keys above b1 (counted) and the keys in b1 (published)
+    bool in[PPT];
+    uint32_t gt = 0;
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) {
+      const bool ok = p0 + e < n;
+      const uint32_t kb = hist_bin(key[e]);
+      gt += (ok && kb > b1) ? 1u : 0u;
+      in[e] = ok && kb == b1;
+    }
+    const uint64_t m0 = __ballot(in[0]), m1 = __ballot(in[1]);
+    uint32_t gtw = gt;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) gtw += __shfl_xor(gtw, o, 64);
+    __syncthreads();  // wsum is free
+    if (lane == 0) {
+      wsum[0][wave] = (uint32_t)(__popcll(m0) + __popcll(m1));
+      wsum[1][wave] = gtw;
+    }
+    __syncthreads();
+    uint32_t wbase = 0, ncand = 0, agt = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      wbase += w < wave ? wsum[0][w] : 0u;
+      ncand += wsum[0][w];
+      agt += wsum[1][w];
+    }
+    uint64_t* cw = p.cand64 + head * p.cap + c0;
+    if (in[0]) st_dev(cw + wbase + lanemask_lt_count(m0, lane), tagged(tag, key[0]));
+    if (in[1]) st_dev(cw + wbase + (uint32_t)__popcll(m0) + lanemask_lt_count(m1, lane), tagged(tag, key[1]));
+    if (tid == 0) st_dev(p.cnt64 + head * p.nsc + chunk, tagged(tag, ncand | (agt << 16)));
+
+    // every chunk's counts (wave 0, lane c = chunk c)
+    if (wave == 0) {
+      uint32_t cc = 0u, ac = 0u;
+      if (lane < nch) {
+        const uint64_t* at = p.cnt64 + head * p.nsc + lane;
+        const uint32_t v = untag_w(at, ld_dev(at), tag, p.err);
+        cc = v & 0xffffu;
+        ac = v >> 16;
+      }
+      const uint32_t x = wave_incl_scan(cc);
+      cpre[lane + 1] = x;
+      if (lane == 0) cpre[0] = 0u;
+      cgt[lane] = ac;
+      ceq[lane] = 0u;
+      // every work-group of the head has published, so has read the epoch
+      if (chunk == 0 && lane == 0) st_dev(p.thr + head * 4 + 3, ep + 1u);
+    }
+    __syncthreads();
+    const uint32_t nc = cpre[nch];
+    const bool staged = nc <= (uint32_t)kSelFusedCand;
+    // candidate i: chunk c with cpre[c] <= i < cpre[c+1], entry i - cpre[c]
+    auto chunk_of = [&](uint32_t i) -> int {
+      int lo = 0, hi = nch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cpre[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      return lo;
+    };
+    if (staged) {
+      // four threads per chunk, eight candidates each in flight
+      const int c = tid >> 2;
+      const uint32_t cnt = c < nch ? cpre[c + 1] - cpre[c] : 0u;
+      const uint64_t* src = p.cand64 + head * p.cap + (long)c * kSelChunk;
+      for (uint32_t e0 = tid & 3; e0 < cnt; e0 += 32) {
+        uint64_t w8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) w8[u] = ld_dev(src + min(e0 + 4u * u, cnt - 1));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t e = e0 + 4u * u;
+          if (e < cnt) {
+            ck[cpre[c] + e] = untag_w(src + e, w8[u], tag, p.err);
+            cch[cpre[c] + e] = (uint8_t)c;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    // visit(f): f(key, chunk, index) for every candidate, from LDS or (a bin
+    // too large for LDS: many ties) from memory, eight loads in flight
+    auto visit = [&](auto f) {
+      if (staged) {
+        for (uint32_t i = tid; i < nc; i += NT) f(ck[i], (int)cch[i], i);
+        return;
+      }
+      for (uint32_t i0 = tid; i0 < nc; i0 += 8 * NT) {
+        uint64_t w8[8];
+        int c8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t i = min(i0 + u * NT, nc - 1);
+          c8[u] = chunk_of(i);
+          w8[u] = ld_dev(p.cand64 + head * p.cap + (long)c8[u] * kSelChunk + (i - cpre[c8[u]]));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t i = i0 + u * NT;
+          if (i < nc) {
+            const uint64_t* at = p.cand64 + head * p.cap + (long)c8[u] * kSelChunk + (i - cpre[c8[u]]);
+            f(untag_w(at, w8[u], tag, p.err), c8[u], i);
+          }
+        }
+      }
+    };
+
+    // refinement inside bin b1 (as in k_select_thresh)
+    uint32_t lo = b1 << (32 - kHistBits);
+    uint32_t hi = lo | ((1u << (32 - kHistBits)) - 1u);
+    uint32_t need = need1, inr = nc;
+    while (lo < hi && inr > (uint32_t)kWave) {
+      const uint32_t span = hi - lo;
+      const int bits = 32 - __clz(span);
+      const int shift = bits > kHistBits ? bits - kHistBits : 0;
+      const int nb = (int)(span >> shift) + 1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rh[8 * tid + i] = 0u;
+      __syncthreads();
+      visit([&](uint32_t k, int, uint32_t) {
+        const uint32_t o = k - lo;
+        if (o <= span) atomicAdd(&rh[o >> shift], 1u);
+      });
+      __syncthreads();
+      uint32_t hb2[8], hs2 = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hb2[i] = 8 * tid + i < nb ? rh[8 * tid + i] : 0u;
+        hs2 += hb2[i];
+      }
+      const uint2 sc = block_scan_u32<NW>(hs2, wsum[0], tid);
+      uint32_t above = sc.y - sc.x - hs2;
+#pragma unroll
+      for (int i = 7; i >= 0; --i) {
+        if (above < need && above + hb2[i] >= need) {
+          bc[0] = 8 * tid + i;
+          bc[1] = above;
+          bc[2] = hb2[i];
+        }
+        above += hb2[i];
+      }
+      __syncthreads();
+      const uint32_t bin = bc[0];
+      need -= bc[1];
+      inr = bc[2];
+      const uint64_t nlo = (uint64_t)lo + ((uint64_t)bin << shift);
+      const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
+      lo = (uint32_t)nlo;
+      hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+      __syncthreads();
+    }
+    if (lo < hi) {
+      // at most 64 candidates in range: wave 0 ranks them (larger key, or
+      // equal key at a lower candidate index, first); rank need-1 is the
+      // threshold
+      if (tid == 0) bc[3] = 0u;
+      __syncthreads();
+      visit([&](uint32_t k, int, uint32_t i) {
+        if (k >= lo && k <= hi) {
+          const uint32_t slot = atomicAdd(&bc[3], 1u);
+          if (slot < (uint32_t)kWave) {
+            rk[slot] = k;
+            ri[slot] = i;
+          }
+        }
+      });
+      __syncthreads();
+      if (wave == 0) {
+        const uint32_t nr = min(bc[3], (uint32_t)kWave);
+        const uint32_t mk = lane < (int)nr ? rk[lane] : 0u;
+        const uint32_t mi = lane < (int)nr ? ri[lane] : 0xffffffffu;
+        uint32_t rank = 0;
+        for (uint32_t c = 0; c < nr; ++c) {
+          const uint32_t kc = (uint32_t)__builtin_amdgcn_readlane((int)mk, (int)c);
+          const uint32_t ic = (uint32_t)__builtin_amdgcn_readlane((int)mi, (int)c);
+          rank += (kc > mk || (kc == mk && ic < mi)) ? 1u : 0u;
+        }
+        const uint64_t who = __ballot(lane < (int)nr && rank == need - 1);
+        const uint32_t kk = __shfl(mk, __ffsll((unsigned long long)who) - 1, 64);
+        const uint32_t gtk = (uint32_t)__popcll(__ballot(lane < (int)nr && mk > kk));
+        if (lane == 0) {
+          bc[0] = kk;
+          bc[1] = need - gtk;
+        }
+      }
+      __syncthreads();
+      lo = hi = bc[0];
+      need = bc[1];
+    }
+    kth = lo;
+    need_eq = need;
+    // per chunk: candidates above the threshold and equal to it
+    visit([&](uint32_t k, int c, uint32_t) {
+      if (k > kth) atomicAdd(&cgt[c], 1u);
+      else if (k == kth) atomicAdd(&ceq[c], 1u);
+    });
+    __syncthreads();
+    if (wave == 0) {
+      // chunk offsets as write_chunk_offsets forms them; this chunk's only
+      const uint32_t g2 = lane < nch ? cgt[lane] : 0u, e2 = lane < nch ? ceq[lane] : 0u;
+      const uint32_t x = wave_incl_scan(e2);
+      const uint32_t eqbl = x - e2;
+      const uint32_t rem = need_eq > eqbl ? need_eq - eqbl : 0u;
+      const uint32_t kept = g2 + min(e2, rem);
+      const uint32_t y2 = wave_incl_scan(kept);
+      if (lane == chunk) {
+        mine[0] = y2 - kept;
+        mine[1] = eqbl;
+      }
+      // the head's threshold record, as k_select_thresh leaves it
+      const uint32_t eq_all = __shfl(x, 63, 64);
+      if (chunk == 0 && lane == 0) {
+        st_dev(p.thr + head * 4 + 0, kth);
+        st_dev(p.thr + head * 4 + 1, need_eq);
+        st_dev(p.thr + head * 4 + 2, eq_all);
+      }
+    }
+    __syncthreads();
+    off = mine[0];
+    eqb = mine[1];
+  }
+
+  // ---- compaction of this chunk (k_compact with one work-group per chunk)
+  bool gtf[PPT], eqf[PPT];
+  uint32_t cg = 0, ce = 0;
+#pragma unroll
+  for (int e = 0; e < PPT; ++e) {
+    const bool ok = p0 + e < n;
+    gtf[e] = all ? ok : (ok && key[e] > kth);
+    eqf[e] = !all && ok && key[e] == kth;
+    cg += gtf[e];
+    ce += eqf[e];
+  }
+  const uint32_t v = cg | (ce << 16);
+  const uint32_t x = wave_incl_scan(v);
+  __syncthreads();  // wsum is free
+  if (lane == 63) wsum[0][wave] = x;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    before += w < wave ? wsum[0][w] : 0u;
+    total += wsum[0][w];
+  }
+  const uint32_t pre = before + x - v;
+  const uint32_t rem = need_eq > eqb ? need_eq - eqb : 0u;
+  uint32_t gtb = pre & 0xffffu, eqbf = pre >> 16;
+#pragma unroll
+  for (int e = 0; e < PPT; ++e) {
+    int r = -1;
+    if (gtf[e]) {
+      r = (int)(gtb + min(eqbf, rem));
+      ++gtb;
+    } else if (eqf[e]) {
+      if (eqbf < rem) r = (int)(gtb + eqbf);
+      ++eqbf;
+    }
+    if (r >= 0 && off + r < (uint32_t)B) {
+      out[off + r] = p0 + e;
+      rows[r] = p0 + e;
+    }
+  }
+  if (!p.k) return;
+  const int kept = (int)((total & 0xffffu) + min(total >> 16, rem));
+  const int nk = min(kept, B - (int)off);
+  __syncthreads();
+  const int lpr = p.row_bytes / 16, rpi = NT / lpr;
+  const int lr = tid / lpr, lc = tid % lpr;
+  constexpr int U = 4;
+  for (int r0 = lr; r0 < nk; r0 += rpi * U) {
+    u32x4_t kv[U], vv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = min(r0 + u * rpi, nk - 1);
+      const long src = (head * p.cap + rows[r]) * (long)p.row_bytes + lc * 16;
+      kv[u] = ld16(p.k + src);
+      vv[u] = ld16(p.v + src);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u * rpi;
+      if (r < nk) {
+        const long dst = (head * p.cap_out + (long)(off + r)) * p.row_bytes + lc * 16;
+        *reinterpret_cast<u32x4_t*>(p.k_out + dst) = kv[u];
+        *reinterpret_cast<u32x4_t*>(p.v_out + dst) = vv[u];
+      }
+    }
+  }
+}
+
+static int g_selcompact_capacity[64];
+
+// The one-launch selection runs when the caller allows it, the chunks keep
+// few rows, the heads are few (many heads take k_select_thresh_head) and the
+// whole grid is resident at once.
+static bool select_compact_ok(const SelectParams& p) {
+  if (!p.one_launch || !p.cand64 || !p.cnt64 || p.gsplit > 1 || p.nsc > 64) return false;
+  if ((long)p.b * p.hkv >= kThreshHeadsMany) return false;
+  return grid_fits(k_select_compact, g_selcompact_capacity, (long)p.nsc * p.hkv * p.b);
+}
+
 // ------------------------------------------------------------- slot reuse
 //
 // Gather-free eviction (the ThinKV page's argument against compaction: a
@@ -1031,9 +1428,6 @@ __global__ __launch_bounds__(kRegThreads) void k_evict_slots(SelectParams p) {
   }
 }
 
-// The threshold kernel for a call: one work-group per chunk and head while
-// the grid is small, one per head (k_select_thresh_head) for many heads.
-constexpr int kThreshHeadsMany = 64;
 static hipError_t launch_thresh(const SelectParams& p, hipStream_t s, Trace* tr) {
   if ((long)p.b * p.hkv >= kThreshHeadsMany)
     return launch_k(k_select_thresh_head, dim3(p.hkv, p.b), dim3(kRegThreads), s, tr, p);
@@ -1127,6 +1521,7 @@ hipError_t launch_select_err_zero(const SelectParams& p, hipStream_t s, Trace* t
 
 hipError_t launch_select(const SelectParams& p, hipStream_t s, Trace* tr) {
   if (p.cap <= kSelectLdsKeys) {
+    if (select_compact_ok(p)) return launch_k(k_select_compact, dim3(p.nsc, p.hkv, p.b), dim3(256), s, tr, p);
     hipError_t e = launch_thresh(p, s, tr);
     if (e != hipSuccess) return e;
     return launch_k(k_compact, dim3(p.nsc * std::max(p.gsplit, 1), p.hkv, p.b), dim3(256), s, tr, p);

@@ -210,7 +210,12 @@ kvsel_status kvsel_score_evict_heads(kvsel_dtype dt, kvsel_redundancy mode,
  * chunk partials itself; a key-sum call that takes the single-launch path
  * (see kvsel_score_evict) launches one kernel, and one that takes the
  * one-launch score pass (see kvsel_scores) launches scores, threshold,
- * compact (select, gather above cap 32768). */
+ * compact (select, gather above cap 32768).  Threshold and compact become
+ * one kernel, select_compact, when a chunk of 512 positions keeps about 64
+ * rows or fewer (budget <= cap / 8), fewer than 64 heads are scored and the
+ * whole grid fits on the device at once (each work-group finds the threshold
+ * from every chunk's published candidates and compacts its own chunk: the
+ * same bits; KVSEL_SEPARATE_KERNELS=1 keeps the two kernels). */
 kvsel_status kvsel_score_evict_traced(kvsel_dtype dt, kvsel_redundancy mode,
                                       const void* q_window, const void* k, const void* v,
                                       const int32_t* lengths, int b, int Hq, int Hkv, int d,
@@ -369,8 +374,8 @@ kvsel_status kvsel_threshold_cut_from_attn(const float* attn_last, const int32_t
  * used it (synchronises the stream).  Bit 0: some lengths[i] lay outside
  * [0, cap] and was clamped into it; bit 1: some per-head budget lay outside
  * [0, budget_max] and was clamped; bit 2: a wait between the work-groups of
- * the single-launch short-cache step or of the one-launch score pass
- * exceeded its poll limit (the results of that call are not to be trusted;
+ * the single-launch short-cache step, of the one-launch score pass or of
+ * the one-launch selection exceeded its poll limit (the results of that call are not to be trusted;
  * it cannot happen while the device runs the whole grid at once, which the
  * library checks before choosing those paths, unless kernels of other
  * streams hold compute units for that long).  Returns KVSEL_ERR_HIP if the copy fails. */

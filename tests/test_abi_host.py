@@ -201,18 +201,30 @@ def test_bench_kernel_names_follow_the_reduce_folding():
             if bench.fused_step(mode, cap):
                 assert names == ["fused"] and mode == "keysum" and -(-cap // chunk) <= fmax
                 continue
+            sel = ["select_compact"] if bench.select_one_launch(cap) else ["thresh", "compact"]
+            assert names[-len(sel):] == sel, (mode, cap)
+            names = names[:-len(sel)]
             if bench.scores_fused(mode, cap):
                 assert mode == "keysum" and -(-cap // chunk) > fmax
                 assert names == ["scores"] + [k for k in bench.KERNELS[mode]
-                                              if k not in ("stats", "reduce", "pool")]
+                                              if k not in ("stats", "reduce", "pool", "thresh", "compact")]
                 continue
             folded = -(-cap // chunk) <= fuse
             assert ("reduce" not in names) == folded, (mode, cap)
-            assert [k for k in bench.KERNELS[mode] if k != "reduce"] == [k for k in names if k != "reduce"]
+            assert [k for k in bench.KERNELS[mode] if k not in ("reduce", "thresh", "compact")] == \
+                [k for k in names if k != "reduce"]
     # 64 sequences of 2176 tokens: 9 * 8 * 64 work-groups do not fit at once
     assert bench.rkv_kernels("keysum", 2176, b=64) != ["fused"]
     # the n = 32768 layer: 128 * 8 work-groups of the score pass fit at four per
     # compute unit; 64 sequences of 8192 tokens do not
     assert bench.rkv_kernels("keysum", 32768)[0] == "scores"
     assert bench.rkv_kernels("keysum", 8192, b=64)[0] == "stats"
+    # the one-launch selection: the n = 32768 layer (32 of 512 kept per chunk),
+    # not the decode cache (about 480 of 512 kept) nor 64 sequences (many heads)
+    assert bench.rkv_kernels("gram", 32768)[-1] == "select_compact"
+    assert bench.rkv_kernels("gram", 2176)[-2:] == ["thresh", "compact"]
+    assert bench.rkv_kernels("keysum", 8192, b=64, budget=1024)[-2:] == ["thresh", "compact"]
+    src_sel = open(os.path.join(os.path.dirname(K.__file__), "csrc", "select.hip")).read()
+    assert int(re.search(r"constexpr int kThreshHeadsMany = (\d+);", src_sel).group(1)) == bench.THRESH_HEADS_MANY
+    assert int(re.search(r"constexpr int kSelChunk = (\d+);", src).group(1)) == bench.SEL_CHUNK
     assert set(bench.KERNEL_SOURCES) >= set(bench.rkv_cost("gram")) - {"evict"}

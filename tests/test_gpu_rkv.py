@@ -211,8 +211,12 @@ def test_batched_64x8192_all_heads(mode):
     check_case(case, mode, form="keysum", heads=[(0, 0), (31, 7), (63, 5)], sample_rows=16)
 
 
-def test_select_stage_exact():
-    """Top-B on given scores is exact: same set as the oracle on the same fp32 values."""
+@pytest.mark.parametrize("separate", [False, True], ids=["one_launch", "two_kernels"])
+def test_select_stage_exact(separate, monkeypatch):
+    """Top-B on given scores is exact: same set as the oracle on the same fp32 values,
+    through the one-launch selection (caps up to 32768) and the two-kernel one."""
+    if separate:
+        monkeypatch.setenv("KVSEL_SEPARATE_KERNELS", "1")
     rng = np.random.default_rng(7)
     for n, cap, budget, kind in [(5000, 5000, 700, "ties"), (32768, 32768, 2048, "normal"),
                                  (40000, 40001, 3000, "ties"), (2176, 2176, 2048, "normal"),
@@ -270,8 +274,11 @@ def test_select_stage_exact_many_heads():
                 assert (idx[bi, h, m:] == -1).all()
 
 
-def test_select_heads_stage_exact():
+@pytest.mark.parametrize("separate", [False, True], ids=["one_launch", "two_kernels"])
+def test_select_heads_stage_exact(separate, monkeypatch):
     """Per-head budgets on given scores: each head's set is the oracle's for its own budget."""
+    if separate:
+        monkeypatch.setenv("KVSEL_SEPARATE_KERNELS", "1")
     rng = np.random.default_rng(17)
     for n, cap, bmax, kind in [(2176, 2176, 2048, "normal"), (5000, 5000, 900, "ties"),
                                (40000, 40001, 3000, "ties"), (300, 512, 256, "normal")]:
