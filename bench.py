@@ -78,13 +78,13 @@ SCORES_FUSED_CAPACITY = 1024  # work-groups of the one-launch score pass residen
 
 
 def scores_fused(mode: str, cap: int, b: int = 1, hkv: int = HKV, m: int = HQ // HKV * W) -> bool:
-    """The library scores a key-sum call on a longer cache (more than 16
-    chunks of 256 tokens per head; bf16, d = 128, at most 32 window rows per
-    KV head) in one launch when its grid of ceil(cap / 256) * Hkv * b
-    work-groups fits on the device at once."""
+    """The library scores a call on a longer cache (more than 16 chunks of
+    256 tokens per head; bf16, d = 128, at most 32 window rows per KV head)
+    in one launch when its grid of ceil(cap / 256) * Hkv * b work-groups fits
+    on the device at once: the key-sum scores, or the importance and key
+    weights of the Gram form."""
     nch = -(-cap // 256)
-    return (mode == "keysum" and m <= 32 and nch > FUSED_MAX_CHUNKS
-            and nch * hkv * b <= SCORES_FUSED_CAPACITY)
+    return m <= 32 and nch > FUSED_MAX_CHUNKS and nch * hkv * b <= SCORES_FUSED_CAPACITY
 
 
 SEL_CHUNK = 512               # kSelChunk: positions per selection work-group
@@ -94,15 +94,15 @@ THRESH_HEADS_MANY = 64       # kThreshHeadsMany: from this many heads, one thres
 
 def select_one_launch(cap: int, b: int = 1, hkv: int = HKV, budget: int = BUDGET) -> bool:
     """The library selects and compacts in one launch (k_select_compact) when
-    the cache fits the split select (cap <= 32768), the heads are few, a
-    chunk of 512 positions keeps about 64 rows or fewer (one gathering
-    work-group: the host's split is ceil(kept / 64) with kept = ceil(512 B /
-    cap)) and the grid of ceil(cap / 512) * Hkv * b work-groups fits at once."""
+    the cache fits the split select (cap <= 32768), the heads are few and the
+    grid of ceil(cap / 512) * gsplit * Hkv * b work-groups fits at once
+    (gsplit work-groups gather a chunk's kept rows: ceil(kept / 64), at most
+    8, with kept = ceil(512 B / cap))."""
     nsc = -(-cap // SEL_CHUNK)
     kept_chunk = -(-SEL_CHUNK * budget // cap)
     gsplit = min(8, max(1, -(-kept_chunk // 64)))
-    return (cap <= 32768 and b * hkv < THRESH_HEADS_MANY and gsplit == 1 and nsc <= 64
-            and nsc * hkv * b <= SELECT_COMPACT_CAPACITY)
+    return (cap <= 32768 and b * hkv < THRESH_HEADS_MANY and nsc <= 64
+            and nsc * gsplit * hkv * b <= SELECT_COMPACT_CAPACITY)
 
 
 def rkv_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV, budget: int = BUDGET) -> list:
@@ -119,6 +119,17 @@ def rkv_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV, budget: int = B
     if select_one_launch(cap, b, hkv, budget):
         ks = [k for k in ks if k not in ("thresh", "compact")] + ["select_compact"]
     return ks
+
+
+def slot_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV) -> list:
+    """Kernels one slot-reuse call (kvsel_score_evict_slots) launches: the
+    scores as a compacting call computes them (the one-launch score pass
+    where it applies, never the fused step), the threshold, the evicted
+    list."""
+    ks = [k for k in unfused_kernels(mode, cap) if k not in ("thresh", "compact")]
+    if scores_fused(mode, cap, b, hkv):
+        ks = ["scores"] + [k for k in ks if k not in ("stats", "reduce", "pool")]
+    return ks + ["thresh", "evict"]
 
 
 def unfused_kernels(mode: str, cap: int) -> list:
@@ -424,7 +435,7 @@ def run_decode_slots(mode, n_layers, hip, calls_per_layer=240):
     cap, budget, w, nb = 2176, 2048, W, 2176 - 2048
     lib = K.lib()
     mcode = K.MODES[mode]
-    names = unfused_kernels(mode, cap)[:-1] + ["evict"]
+    names = slot_kernels(mode, cap)
     P = ctypes.c_void_p
     layers = []
     for layer in range(n_layers):

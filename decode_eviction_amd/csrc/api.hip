@@ -85,9 +85,9 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 struct ScoreWs {
   int32_t* err;
-  // one-launch kernels of the key-sum form: per-head epochs and tagged chunk
-  // partials; the short-cache step also has barrier tokens and tagged score
-  // keys, the long-cache score pass a tagged merged record per head
+  // one-launch kernels: per-head epochs and tagged chunk partials; the
+  // short-cache step of the key-sum form also has barrier tokens and tagged
+  // score keys, the score pass a tagged merged record per head
   uint64_t* fepoch;
   uint64_t* fflags;
   uint64_t* fpub_a;
@@ -132,7 +132,13 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap, kvsel_redund
   Carver c{static_cast<char*>(base)};
   ScoreWs w{};
   w.err = c.take<int32_t>(64);
-  if (!gram) {
+  if (gram) {
+    if (nchunk > kFusedMaxChunks) {
+      w.fepoch = c.take<uint64_t>(heads);
+      w.fpub_a = c.take<uint64_t>(heads * nchunk * kGramWordsA);
+      w.fmerged = c.take<uint64_t>(heads * kGramWordsA);
+    }
+  } else {
     w.fepoch = c.take<uint64_t>(heads);
     if (nchunk <= kFusedMaxChunks) {
       w.fflags = c.take<uint64_t>(2 * heads * kFusedMaxChunks);
@@ -162,7 +168,7 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap, kvsel_redund
   w.sel.thr = c.take<uint32_t>(heads * 4);
   w.sel.coff = c.take<uint32_t>(heads * w.sel.nsc);
   w.sel.ceqb = c.take<uint32_t>(heads * w.sel.nsc);
-  w.sel.acnt = reinterpret_cast<uint32_t*>(c.take<uint64_t>(heads * w.sel.nsc));
+  w.sel.acnt = reinterpret_cast<uint32_t*>(c.take<uint64_t>(heads * w.sel.nsc * kMaxGsplit));
   w.sel.ccnt = w.sel.acnt ? w.sel.acnt + heads * w.sel.nsc : nullptr;
   w.sel.candk = reinterpret_cast<uint32_t*>(c.take<uint64_t>(heads * cap));
   w.sel.candp = w.sel.candk ? reinterpret_cast<int32_t*>(w.sel.candk + heads * cap) : nullptr;
@@ -219,20 +225,28 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
   p.z_out = z_out;
   p.hist = hist;
   const int sm = mode == KVSEL_R_GRAM ? kModeGram : kModeKeysum;
-  // longer caches, key-sum form: one launch reading K once, when its grid
-  // fits on the device at once
-  if (sm == kModeKeysum && dt == KVSEL_BF16 && d == 128 && p.m <= 32 && ws.fmerged && !separate_kernels()) {
+  // longer caches (more than kFusedMaxChunks chunks per head; the workspace
+  // then holds the merged records): one launch reading K once for the
+  // scores (the Gram form's importance and key weights), when its grid fits
+  // on the device at once.  On shorter caches the separate kernels measured
+  // as fast: k_pool merges the partials itself there, so one launch
+  // boundary is all a score pass would save, and its two exchanges between
+  // work-groups cost as much.
+  bool scored = false;
+  if (dt == KVSEL_BF16 && d == 128 && p.m <= 32 && ws.fmerged && !separate_kernels()) {
     const ScoresFusedParams fp{p, ws.fepoch, ws.fpub_a, ws.fmerged};
-    const int grid = scores_fused_grid(fp);
+    const int grid = scores_fused_grid(sm, fp);
     if (grid > 0) {
-      KV_TRY(launch_scores_fused(fp, grid, stream, tr));
-      return KVSEL_OK;
+      KV_TRY(launch_scores_fused(sm, fp, grid, stream, tr));
+      scored = true;
     }
   }
-  p.fuse_reduce = p.nchunk <= kFuseReduceChunks;
-  KV_TRY(launch_stats(dt, d, sm, p, stream, tr));
-  if (!p.fuse_reduce) KV_TRY(launch_reduce(d, sm, p, stream, tr));
-  KV_TRY(launch_pool(dt, d, sm, p, stream, tr));
+  if (!scored) {
+    p.fuse_reduce = p.nchunk <= kFuseReduceChunks;
+    KV_TRY(launch_stats(dt, d, sm, p, stream, tr));
+    if (!p.fuse_reduce) KV_TRY(launch_reduce(d, sm, p, stream, tr));
+    KV_TRY(launch_pool(dt, d, sm, p, stream, tr));
+  }
   if (mode == KVSEL_R_GRAM) {
     GramParams gp{};
     gp.k = p.k;
@@ -280,8 +294,9 @@ SelWs carve_select(Carver& c, int b, int hkv, int cap) {
   w.coff = c.take<uint32_t>(heads * w.nsc);
   w.ceqb = c.take<uint32_t>(heads * w.nsc);
   // per-chunk counts and candidates: each pair one region, which the
-  // one-launch selection uses as 64-bit tagged words instead
-  w.acnt = reinterpret_cast<uint32_t*>(c.take<uint64_t>(heads * w.nsc));
+  // one-launch selection uses as 64-bit tagged words instead (a count word
+  // per work-group: up to kMaxGsplit per chunk)
+  w.acnt = reinterpret_cast<uint32_t*>(c.take<uint64_t>(heads * w.nsc * kMaxGsplit));
   w.ccnt = w.acnt ? w.acnt + heads * w.nsc : nullptr;
   w.candk = reinterpret_cast<uint32_t*>(c.take<uint64_t>(heads * cap));
   w.candp = w.candk ? reinterpret_cast<int32_t*>(w.candk + heads * cap) : nullptr;
@@ -571,7 +586,7 @@ static kvsel_status score_evict_impl(kvsel_dtype dt, kvsel_redundancy mode, cons
     // about 64 kept rows per gathering work-group: a chunk of kSelChunk
     // positions keeps about kSelChunk * budget / cap of them
     const long kept_chunk = ((long)kSelChunk * budget + cap - 1) / cap;
-    sp.gsplit = (int)std::min(8L, std::max(1L, (kept_chunk + 63) / 64));
+    sp.gsplit = (int)std::min((long)kMaxGsplit, std::max(1L, (kept_chunk + 63) / 64));
     KV_TRY(launch_select(sp, stream, tr));
     return KVSEL_OK;
   }

@@ -98,13 +98,13 @@ __device__ __forceinline__ int fused_budget(const FusedParams& p, int h) {
   return v < 0 ? 0 : (v > p.budget ? p.budget : v);
 }
 
-// Phase 1 for one 256-token chunk, as k_stats computes it (key-sum form, one
-// tile of up to 32 query rows); each wave holds two 32-token key tiles,
-// tokens tok0 .. tok0 + 63.  Hands the chunk's partials to the sinks:
-// stat(r, max, sum of 2^(t - max)) for the 32 rows and sum(dim, s) for the
-// D dimensions of the chunk's sum of unit keys.  sqs receives each lane's
-// half-row squared norms (for the pooling phase).
-template <typename E, int D, typename StatSink, typename SumSink>
+// Phase 1 for one 256-token chunk, as k_stats computes it (one tile of up to
+// 32 query rows); each wave holds two 32-token key tiles, tokens tok0 ..
+// tok0 + 63.  Hands the chunk's partials to the sinks: stat(r, max, sum of
+// 2^(t - max)) for the 32 rows and, with kSums (the key-sum form),
+// sum(dim, s) for the D dimensions of the chunk's sum of unit keys.  sqs
+// receives each lane's half-row squared norms (for the pooling phase).
+template <typename E, int D, bool kSums, typename StatSink, typename SumSink>
 __device__ __forceinline__ void chunk_partials(const Frag<Geo<E, D>::kNC> (&kf)[2], const u32x4_t* qs,
                                                int n, int tok0, float sc2, float (&sqs)[2],
                                                float2 (*wst)[32], float* red, int tid,
@@ -151,7 +151,12 @@ __device__ __forceinline__ void chunk_partials(const Frag<Geo<E, D>::kNC> (&kf)[
     s += xor32(s);
     if (hf == 0) wst[wave][l32] = make_float2(m2, s);
   }
-  {
+  if constexpr (!kSums) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) sqs[tt] = frag_sumsq<E, NC>(kf[tt]);
+    __syncthreads();
+  } else {
     float inv[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -176,17 +181,17 @@ __device__ __forceinline__ void chunk_partials(const Frag<Geo<E, D>::kNC> (&kf)[
     float* mine = red + (wave * 64 + lane) * PC;
 #pragma unroll
     for (int e = 0; e < PC; ++e) mine[e] = v[e];
-  }
-  __syncthreads();
-  if (tid < D) {
-    constexpr int R = 32 / NC;
-    const int ch = tid / PC, e = tid % PC, hfd = ch & 1, j = ch >> 1;
-    float s = 0.f;
+    __syncthreads();
+    if (tid < D) {
+      constexpr int R = 32 / NC;
+      const int ch = tid / PC, e = tid % PC, hfd = ch & 1, j = ch >> 1;
+      float s = 0.f;
 #pragma unroll
-    for (int wv = 0; wv < 4; ++wv)
+      for (int wv = 0; wv < 4; ++wv)
 #pragma unroll
-      for (int q = 0; q < R; ++q) s += red[(wv * 64 + hfd * 32 + j * R + q) * PC + e];
-    sum(tid, s);
+        for (int q = 0; q < R; ++q) s += red[(wv * 64 + hfd * 32 + j * R + q) * PC + e];
+      sum(tid, s);
+    }
   }
   if (tid < 32) {
     float m = -INFINITY, s = 0.f;
@@ -194,6 +199,35 @@ __device__ __forceinline__ void chunk_partials(const Frag<Geo<E, D>::kNC> (&kf)[
     for (int wv = 0; wv < NW; ++wv) softmax_merge(m, s, wst[wv][tid].x, wst[wv][tid].y);
     stat(tid, m, s);
   }
+}
+
+// The attention that token l32 of key tile kf receives from the window's
+// rows, summed (the importance before its 1/m), as k_pool computes it from
+// the merged row statistics rs (max, 1/sum; zero for rows past m) in LDS.
+// Both lanes of the token (hf = 0, 1) return the same value.
+template <typename E, int D>
+__device__ __forceinline__ float token_attention(const Frag<Geo<E, D>::kNC>& kf, const u32x4_t* qs,
+                                                 const float2* rs, float sc2, int l32, int hf) {
+  using QSt = QStage<E, D, 1>;
+  constexpr int NC = Geo<E, D>::kNC;
+  // at most two query chunks and four row records read ahead from LDS (the
+  // keys stay in registers: the one-launch score pass runs at four waves
+  // per SIMD)
+  f32x16_t c = zero16();
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    c = mfma_chunk<E>(QSt::chunk(qs, 0, l32, hf, j), kf.c[j], c);
+    if (j % 2 == 1) asm volatile("" ::: "memory");
+  }
+  float isum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float2 st = rs[tile_row(i, hf)];
+    isum = fmaf(exp2_fast(fmaf(c[i], sc2, -st.x)), st.y, isum);
+    if (i % 4 == 3) asm volatile("" : "+v"(isum)::"memory");
+  }
+  isum += xor32(isum);
+  return isum;
 }
 
 // Phase 2 for a wave's two key tiles, as k_pool computes it: importance, the
@@ -207,9 +241,7 @@ __device__ __forceinline__ void pool_tokens(const Frag<Geo<E, D>::kNC> (&kf)[2],
                                             const float (&sqs)[2], int n, int m, float sc2,
                                             float lambda, int tid, float (&imp)[2], float (&rd)[2],
                                             float (&z)[2]) {
-  using G = Geo<E, D>;
-  using QSt = QStage<E, D, 1>;
-  constexpr int NC = G::kNC, PC = E::kPerChunk;
+  constexpr int NC = Geo<E, D>::kNC, PC = E::kPerChunk;
   // LDS addresses recomputed here rather than kept from the partials
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
@@ -230,24 +262,7 @@ __device__ __forceinline__ void pool_tokens(const Frag<Geo<E, D>::kNC> (&kf)[2],
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    // at most two query chunks and four row records read ahead from LDS
-    // (the keys stay in registers: the one-launch score pass runs at four
-    // waves per SIMD)
-    f32x16_t c = zero16();
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      c = mfma_chunk<E>(QSt::chunk(qs, 0, l32, hf, j), kf[tt].c[j], c);
-      if (j % 2 == 1) asm volatile("" ::: "memory");
-    }
-    float isum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float2 st = rs[tile_row(i, hf)];
-      isum = fmaf(exp2_fast(fmaf(c[i], sc2, -st.x)), st.y, isum);
-      if (i % 4 == 3) asm volatile("" : "+v"(isum)::"memory");
-    }
-    isum += xor32(isum);
-    imp[tt] = isum * inv_m;
+    imp[tt] = token_attention<E, D>(kf[tt], qs, rs, sc2, l32, hf) * inv_m;
     float ss = sqs[tt];
     ss += xor32(ss);
     const float inv = inv_norm_of(ss);
@@ -337,7 +352,7 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   __syncthreads();
   float sqs[2];
   uint64_t* rec = pa + chunk * kFusedWordsA;
-  chunk_partials<E, D>(
+  chunk_partials<E, D, true>(
       kf, qs, n, tok0, sc2, sqs, wst, red, tid,
       [&](int r, float m, float s) {
         st_dev(rec + 2 * r, tagged(tag, __float_as_uint(m)));
@@ -570,16 +585,21 @@ hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr) {
 }
 
 // ------------------------------------------------------------------------
-// One-launch score pass for long caches (key-sum redundancy).
+// One-launch score pass (key-sum form on long caches; the importance and
+// key weights of the Gram form on any cache).
 //
 // The multi-kernel pass streams K twice (k_stats, then k_pool after
-// k_reduce).  k_scores_fused reads each key once: a work-group per 256-token
-// chunk and head computes the chunk's partials as k_stats does and keeps its
-// keys in registers; the head's first kScoreMergeParts work-groups each merge
-// one slice of the partials in k_reduce's order (the row statistics of rows
-// 0-15 and 16-31, then the unit-key sums 32 dimensions at a time); every
-// work-group then pools its own tokens from the merged record as k_pool
-// does.  The scores equal the multi-kernel pass's bit for bit.
+// k_reduce, or k_pool merging the partials itself on short caches).
+// k_scores_fused reads each key once: a work-group per 256-token chunk and
+// head computes the chunk's partials as k_stats does and keeps its keys in
+// registers; the head's first work-groups each merge one slice of the
+// partials in k_reduce's order (the row statistics of rows 0-15 and 16-31,
+// then, in the key-sum form, the unit-key sums 32 dimensions at a time);
+// every work-group then pools its own tokens from the merged record as
+// k_pool does: importance, redundancy, Z and the histogram in the key-sum
+// form; importance and the inverse key norms 1/||k_j|| (the weights of the
+// Gram kernels, which run next) in the Gram form.  The results equal the
+// multi-kernel pass's bit for bit.
 //
 // Records that cross work-groups are tagged words (value in the low half,
 // the call's tag for the head in the high half) written and read with
@@ -592,14 +612,18 @@ hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr) {
 
 // One (chunk, head, sequence) unit of the score pass; k_scores_fused runs
 // the units of a call in rounds (below).
-template <typename E, int D>
+template <typename E, int D, int MODE>
 __device__ __forceinline__ void scores_fused_unit(const ScoresFusedParams& fp, int chunk, int h, int bi) {
   const ScoreParams& p = fp.s;
   using G = Geo<E, D>;
   using QSt = QStage<E, D, 1>;
-  constexpr int NC = G::kNC, RB = G::kRowBytes, PC = E::kPerChunk, W = kFusedWordsA;
-  constexpr int NP = 2 + D / 32;  // merge slices: rows 0-15, rows 16-31, 32 dimensions each
-  static_assert(D == 128 && NP == kScoreMergeParts, "merge slices of the 128-dimension record");
+  constexpr bool kGram = MODE == kModeGram;
+  static_assert(kGram || MODE == kModeKeysum, "R-KV score forms");
+  constexpr int NC = G::kNC, RB = G::kRowBytes, PC = E::kPerChunk;
+  constexpr int W = kGram ? kGramWordsA : kFusedWordsA;
+  // merge slices: rows 0-15, rows 16-31, then 32 dimensions each
+  constexpr int NP = kGram ? 2 : 2 + D / 32;
+  static_assert(D == 128 && (kGram || NP == kScoreMergeParts), "merge slices of the 128-dimension record");
   // the wave index in a scalar register (the compiler cannot prove tid >> 6
   // uniform): wave-derived offsets then take no vector registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -644,7 +668,7 @@ __device__ __forceinline__ void scores_fused_unit(const ScoresFusedParams& fp, i
     }
   }
   __shared__ uint32_t lh[kHistBins];
-  if (hg)
+  if (!kGram && hg)
     for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
 
   // ---- chunk partials (k_stats' arithmetic) as tagged words
@@ -659,13 +683,23 @@ __device__ __forceinline__ void scores_fused_unit(const ScoresFusedParams& fp, i
   uint64_t* mr = fp.merged + head * W;
   {
     uint64_t* rec = pr + (long)chunk * W;
-    chunk_partials<E, D>(
+    chunk_partials<E, D, !kGram>(
         kf, qs, n, tok0, sc2, sqs, wst, red, tid,
         [&](int r, float m, float s) {
           st_dev(rec + 2 * r, tagged(tag, __float_as_uint(m)));
           st_dev(rec + 2 * r + 1, tagged(tag, __float_as_uint(s)));
         },
         [&](int dim, float s) { st_dev(rec + 64 + dim, tagged(tag, __float_as_uint(s))); });
+  }
+  if constexpr (kGram) {
+    // the weight 1/||k_j|| of every slot of the chunk (0 past n), as k_stats
+    // writes it
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float ss = sqs[tt];
+      ss += xor32(ss);
+      if (hf == 0) p.inv_norm[head * (long)p.wstride + tok0 + 32 * tt + l32] = inv_norm_of(ss);
+    }
   }
   // the keys and the staged queries as opaque values from here: the pooling
   // unpacks and reads them again instead of keeping copies from the partials
@@ -758,12 +792,24 @@ __device__ __forceinline__ void scores_fused_unit(const ScoresFusedParams& fp, i
   // ---- importance, redundancy, Z of this chunk's tokens (k_pool's arithmetic)
   __shared__ float2 rs[32];
   __shared__ __attribute__((aligned(16))) float ssh[D];
-  if (tid < 64 + D) {
+  if (tid < (kGram ? 64 : 64 + D)) {
     const uint32_t v = untag_w(mr + tid, ld_dev(mr + tid), tag, p.err);
     if (tid < 64) reinterpret_cast<float*>(rs)[tid] = (tid >> 1) < p.m ? __uint_as_float(v) : 0.f;
     else ssh[tid - 64] = __uint_as_float(v);
   }
   __syncthreads();
+  if constexpr (kGram) {
+    // importance (k_pool's arithmetic)
+    const float inv_m = 1.0f / (float)p.m;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const float imp = token_attention<E, D>(kf[tt], qs, rs, sc2, l32, hf) * inv_m;
+      const int tok = tok0 + 32 * tt + l32;
+      if (hf == 0 && tok < n) p.i_out[head * p.cap + tok] = imp;
+      __builtin_amdgcn_sched_barrier(0);  // one accumulator tile live at a time
+    }
+    return;
+  }
   float imp[2], rd[2], z[2];
   pool_tokens<E, D>(kf, qs, rs, ssh, sqs, n, p.m, sc2, p.lambda, tid, imp, rd, z);
 #pragma unroll
@@ -790,11 +836,11 @@ __device__ __forceinline__ void scores_fused_unit(const ScoresFusedParams& fp, i
 // resident work-groups was slower than the separate kernels on 64 sequences
 // of 8192 tokens (511 against 463 us): a work-group cannot load its next
 // unit's keys while it waits for its head's merge, so rounds do not overlap.
-template <typename E, int D>
+template <typename E, int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 void k_scores_fused(ScoresFusedParams fp) {
   const int v = blockIdx.x, hb = v / fp.s.nchunk;
-  scores_fused_unit<E, D>(fp, v - hb * fp.s.nchunk, hb % fp.s.hkv, hb / fp.s.hkv);
+  scores_fused_unit<E, D, MODE>(fp, v - hb * fp.s.nchunk, hb % fp.s.hkv, hb / fp.s.hkv);
 }
 
 static int g_fused_capacity[64];
@@ -804,16 +850,20 @@ bool fused_fits(const FusedParams& p) {
                    (long)((p.cap + kChunk - 1) / kChunk) * p.hkv * p.b);
 }
 
-static int g_scores_capacity[64];
+static int g_scores_capacity[2][64];
 
-int scores_fused_grid(const ScoresFusedParams& p) {
+int scores_fused_grid(int mode, const ScoresFusedParams& p) {
   const long total = (long)p.s.nchunk * p.s.hkv * p.s.b;
   if (total >= (1L << 31)) return 0;
-  return grid_fits(k_scores_fused<BF16, 128>, g_scores_capacity, total) ? (int)total : 0;
+  const bool ok = mode == kModeGram
+                      ? grid_fits(k_scores_fused<BF16, 128, kModeGram>, g_scores_capacity[0], total)
+                      : grid_fits(k_scores_fused<BF16, 128, kModeKeysum>, g_scores_capacity[1], total);
+  return ok ? (int)total : 0;
 }
 
-hipError_t launch_scores_fused(const ScoresFusedParams& p, int grid, hipStream_t s, Trace* tr) {
-  return launch_k(k_scores_fused<BF16, 128>, dim3(grid), dim3(256), s, tr, p);
+hipError_t launch_scores_fused(int mode, const ScoresFusedParams& p, int grid, hipStream_t s, Trace* tr) {
+  if (mode == kModeGram) return launch_k(k_scores_fused<BF16, 128, kModeGram>, dim3(grid), dim3(256), s, tr, p);
+  return launch_k(k_scores_fused<BF16, 128, kModeKeysum>, dim3(grid), dim3(256), s, tr, p);
 }
 
 }  // namespace kvsel

@@ -622,16 +622,19 @@ __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
 // 16x16x32 tiles.  The tile's w-weighted row sums go to slot J of block I's
 // keys; its w-weighted column sums (I < J) to slot I of block J's keys; so
 // every key ends with one slot per block of the cache, and k_gram_fin adds
-// them in slot order (deterministic) and removes the self term.
+// them in slot order (deterministic) and removes the self term.  The grid is
+// one-dimensional, (pair, head) units in XCD-major order: the pairs of one
+// head run on one XCD and share its keys through that XCD's L2.
 __global__ __launch_bounds__(256) void k_gram_pairs(GramParams p) {
   constexpr int RB = 256;  // bytes per key (128 bf16)
   constexpr int BS = 128;  // keys per block
-  const int nbh = (p.cap + BS - 1) / BS;
-  const int h = blockIdx.y, bi = blockIdx.z, tid = threadIdx.x;
+  const int nbh = (p.cap + BS - 1) / BS, npairs = nbh * (nbh + 1) / 2;
+  const int unit = xcd_major(blockIdx.x, npairs * p.hkv * p.b);
+  const int hb = unit / npairs, h = hb % p.hkv, bi = hb / p.hkv, tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // pair index -> (I, J): block I owns the pairs J = I .. nbh-1
-  int I = 0, rem = blockIdx.x;
+  int I = 0, rem = unit - hb * npairs;
   while (rem >= nbh - I) {
     rem -= nbh - I;
     ++I;
@@ -860,11 +863,14 @@ hipError_t launch_gram(int dt, int d, const GramParams& p_in, hipStream_t s, Tra
   const bool small = dt == 0 && d == 128 && p.cap <= kGramPairCap;
   p.bs = big ? 512 : (small ? 128 : 256);
   p.pairs = small ? 1 : 0;
+  // one-dimensional grids: every work-group index must fit an int
+  const long nbk = (p.cap + p.bs - 1) / p.bs;
+  if ((small ? nbk * (nbk + 1) / 2 : nbk) * p.hkv * p.b >= (1L << 31)) return hipErrorInvalidValue;
   hipError_t e;
   if (big) e = launch_k(k_gram512, dim3((p.cap + 511) / 512 * p.hkv * p.b), dim3(256), s, tr, p);
   else if (small) {
     const int nbh = (p.cap + 127) / 128;
-    e = launch_k(k_gram_pairs, dim3(nbh * (nbh + 1) / 2, p.hkv, p.b), dim3(256), s, tr, p);
+    e = launch_k(k_gram_pairs, dim3(nbh * (nbh + 1) / 2 * p.hkv * p.b), dim3(256), s, tr, p);
   }
   else if (dt == 0) e = d == 64 ? gram_t<BF16, 64>(p, s, tr) : gram_t<BF16, 128>(p, s, tr);
   else e = d == 64 ? gram_t<F32, 64>(p, s, tr) : gram_t<F32, 128>(p, s, tr);

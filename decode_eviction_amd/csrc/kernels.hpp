@@ -144,6 +144,8 @@ constexpr int kGramPairCap = 4096;
 
 constexpr int kSelChunk = 512;     // positions per compaction work-group
 
+// most work-groups that share one selection chunk's gather
+constexpr int kMaxGsplit = 8;
 struct SelectParams {
   const float* z;           // [b][Hkv][cap]
   const int32_t* lengths;
@@ -174,8 +176,8 @@ struct SelectParams {
   char* k_out;
   char* v_out;
   int cap_out, row_bytes;
-  // work-groups sharing one chunk's gather (>= 1): each takes its share of
-  // the chunk's kept rows; used when most rows are kept
+  // work-groups sharing one chunk's gather (1 .. kMaxGsplit): each takes its
+  // share of the chunk's kept rows; used when most rows are kept
   int gsplit;
   // per-head budgets (nullable): head h keeps budgets[h] clamped to [0, budget],
   // budget being the row stride of idx and of the compacted cache
@@ -263,20 +265,23 @@ struct FusedParams {
   uint64_t* pub_b;          // [b][Hkv][cap]: tagged score keys
 };
 
-// One-launch score pass for long caches (fused.hip): the key-sum scores of
-// k_stats, k_reduce and k_pool in one grid of kChunk-token work-groups (bf16
-// keys of 128 dimensions, at most 32 window rows per KV head), every
-// work-group of the grid resident at once.  Chunk partials and the merged
-// record are tagged words in the layout of the short-cache step's records
-// (kFusedWordsA per record); the first kScoreMergeParts work-groups of a head
-// each merge one slice (rows 0-15, rows 16-31, then the unit-key sums 32
-// dimensions at a time).
+// One-launch score pass (fused.hip): what k_stats, k_reduce and k_pool
+// compute, in one grid of kChunk-token work-groups (bf16 keys of 128
+// dimensions, at most 32 window rows per KV head), every work-group of the
+// grid resident at once: the key-sum scores, or the importance and key
+// weights of the Gram form.  Chunk partials and the merged record are tagged
+// words: kFusedWordsA per record in the key-sum form (the layout of the
+// short-cache step's records), kGramWordsA (the row statistics alone) in the
+// Gram form.  The first work-groups of a head each merge one slice (rows
+// 0-15, rows 16-31, then in the key-sum form the unit-key sums 32 dimensions
+// at a time: kScoreMergeParts slices).
 constexpr int kScoreMergeParts = 2 + 128 / 32;
+constexpr int kGramWordsA = 64;  // per chunk: 32 row (max, sum) pairs
 struct ScoresFusedParams {
   ScoreParams s;            // shapes, inputs, outputs, histogram, error word
   uint64_t* epoch;          // [b][Hkv]: advanced by one every call
-  uint64_t* part;           // [b][Hkv][nchunk][kFusedWordsA]: tagged chunk partials
-  uint64_t* merged;         // [b][Hkv][kFusedWordsA]: tagged merged record
+  uint64_t* part;           // [b][Hkv][nchunk][words per record]: tagged chunk partials
+  uint64_t* merged;         // [b][Hkv][words per record]: tagged merged record
 };
 
 // Optional per-kernel timing: the k-th kernel an entry point launches records
@@ -347,8 +352,8 @@ hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr);
 // the one-launch score pass: its grid (one work-group per (chunk, head,
 // sequence)), or 0 when those do not all fit on the device at once (then the
 // separate kernels run)
-int scores_fused_grid(const ScoresFusedParams& p);
-hipError_t launch_scores_fused(const ScoresFusedParams& p, int grid, hipStream_t s, Trace* tr);
+int scores_fused_grid(int mode, const ScoresFusedParams& p);
+hipError_t launch_scores_fused(int mode, const ScoresFusedParams& p, int grid, hipStream_t s, Trace* tr);
 
 // Work-groups of kern resident on the device at once (cached per device;
 // -1 when the query fails).

@@ -894,8 +894,9 @@ constexpr int kThreshHeadsMany = 64;
 // ------------------------------------------------- one-launch selection
 //
 // k_select_thresh and k_compact in one launch, for calls whose grid is
-// resident at once and whose chunks keep few rows (about B/cap of 512, at
-// most 64: one work-group gathers them).  The finishing work-group of
+// resident at once.  As in k_compact, gsplit work-groups share a chunk whose
+// kept rows are many (about 64 rows per gathering work-group): all of them
+// select and scan the chunk, each gathers its share.  The finishing work-group of
 // k_select_thresh, and the launch of k_compact after it, wait on each
 // other; here no work-group waits for a finisher.  Every work-group
 // publishes its chunk's candidates (the keys in the first-level bin) and
@@ -909,9 +910,9 @@ constexpr int kThreshHeadsMany = 64;
 // k_compact).  Results equal the two-kernel path's bit for bit.
 //
 // The tags hash the head's epoch (word 3 of its thr record, advanced by
-// chunk 0 once it has every chunk's counts, by which time every work-group of
-// the head has read the epoch); a poll that exceeds its limit sets bit 2 of
-// the error word.
+// chunk 0 once it has the count words of every work-group of the head, by
+// which time each of them has read the epoch); a poll that exceeds its limit
+// sets bit 2 of the error word.
 constexpr int kSelFusedCand = 4096;  // candidates staged in LDS (more: read from memory)
 
 __global__ __launch_bounds__(256) void k_select_compact(SelectParams p) {
@@ -927,7 +928,8 @@ __global__ __launch_bounds__(256) void k_select_compact(SelectParams p) {
   __shared__ uint32_t mine[2];                // this chunk's first output slot, copies of kth before it
   __shared__ int32_t rows[kSelChunk];         // kept positions by slot - chunk offset
 
-  const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int gs = max(p.gsplit, 1);
+  const int chunk = blockIdx.x / gs, part = blockIdx.x % gs, h = blockIdx.y, bi = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const long head = (long)bi * p.hkv + h;
   const uint32_t* hg = p.hist + head * kHistStride;
@@ -944,9 +946,10 @@ __global__ __launch_bounds__(256) void k_select_compact(SelectParams p) {
   const uint32_t ep = ld_dev(p.thr + head * 4 + 3);
   const int n = clamp_len(p.lengths[bi], p.cap);
   const int B = head_budget(p, h);
-  if (chunk == 0 && tid == 0) flag_select_errors(p, h, bi);
+  const bool lead = chunk == 0 && part == 0;
+  if (lead && tid == 0) flag_select_errors(p, h, bi);
   int32_t* out = p.idx + head * p.budget;
-  if (chunk == 0)
+  if (lead)
     for (int t = min(n, B) + tid; t < p.budget; t += NT) out[t] = -1;
   if (c0 >= n || B == 0) return;
   const int nch = (n + kSelChunk - 1) / kSelChunk;
@@ -1008,16 +1011,21 @@ __global__ __launch_bounds__(256) void k_select_compact(SelectParams p) {
       ncand += wsum[0][w];
       agt += wsum[1][w];
     }
+    // the chunk's candidates (its first work-group), and a count word from
+    // every work-group (word part of the chunk's gs)
     uint64_t* cw = p.cand64 + head * p.cap + c0;
-    if (in[0]) st_dev(cw + wbase + lanemask_lt_count(m0, lane), tagged(tag, key[0]));
-    if (in[1]) st_dev(cw + wbase + (uint32_t)__popcll(m0) + lanemask_lt_count(m1, lane), tagged(tag, key[1]));
-    if (tid == 0) st_dev(p.cnt64 + head * p.nsc + chunk, tagged(tag, ncand | (agt << 16)));
+    if (part == 0) {
+      if (in[0]) st_dev(cw + wbase + lanemask_lt_count(m0, lane), tagged(tag, key[0]));
+      if (in[1]) st_dev(cw + wbase + (uint32_t)__popcll(m0) + lanemask_lt_count(m1, lane), tagged(tag, key[1]));
+    }
+    const uint64_t* cnt = p.cnt64 + head * p.nsc * gs;
+    if (tid == 0) st_dev(p.cnt64 + (head * p.nsc + chunk) * gs + part, tagged(tag, ncand | (agt << 16)));
 
     // every chunk's counts (wave 0, lane c = chunk c)
     if (wave == 0) {
       uint32_t cc = 0u, ac = 0u;
       if (lane < nch) {
-        const uint64_t* at = p.cnt64 + head * p.nsc + lane;
+        const uint64_t* at = cnt + (long)lane * gs;
         const uint32_t v = untag_w(at, ld_dev(at), tag, p.err);
         cc = v & 0xffffu;
         ac = v >> 16;
@@ -1027,8 +1035,13 @@ __global__ __launch_bounds__(256) void k_select_compact(SelectParams p) {
       if (lane == 0) cpre[0] = 0u;
       cgt[lane] = ac;
       ceq[lane] = 0u;
-      // every work-group of the head has published, so has read the epoch
-      if (chunk == 0 && lane == 0) st_dev(p.thr + head * 4 + 3, ep + 1u);
+      if (lead) {
+        // the other work-groups of each chunk have published too
+        for (int i = lane; i < nch * gs; i += kWave)
+          if (i % gs != 0) untag_w(cnt + i, ld_dev(cnt + i), tag, p.err);
+        // every work-group of the head has published, so has read the epoch
+        if (lane == 0) st_dev(p.thr + head * 4 + 3, ep + 1u);
+      }
     }
     __syncthreads();
     const uint32_t nc = cpre[nch];
@@ -1194,7 +1207,7 @@ __global__ __launch_bounds__(256) void k_select_compact(SelectParams p) {
       }
       // the head's threshold record, as k_select_thresh leaves it
       const uint32_t eq_all = __shfl(x, 63, 64);
-      if (chunk == 0 && lane == 0) {
+      if (lead && lane == 0) {
         st_dev(p.thr + head * 4 + 0, kth);
         st_dev(p.thr + head * 4 + 1, need_eq);
         st_dev(p.thr + head * 4 + 2, eq_all);
@@ -1241,18 +1254,21 @@ __global__ __launch_bounds__(256) void k_select_compact(SelectParams p) {
       ++eqbf;
     }
     if (r >= 0 && off + r < (uint32_t)B) {
-      out[off + r] = p0 + e;
+      if (part == 0) out[off + r] = p0 + e;
       rows[r] = p0 + e;
     }
   }
   if (!p.k) return;
   const int kept = (int)((total & 0xffffu) + min(total >> 16, rem));
-  const int nk = min(kept, B - (int)off);
+  const int nkc = min(kept, B - (int)off);
+  // this work-group's share of the chunk's kept rows: [rb, nk)
+  const int share = (nkc + gs - 1) / gs;
+  const int rb = part * share, nk = min(nkc, rb + share);
   __syncthreads();
   const int lpr = p.row_bytes / 16, rpi = NT / lpr;
   const int lr = tid / lpr, lc = tid % lpr;
   constexpr int U = 4;
-  for (int r0 = lr; r0 < nk; r0 += rpi * U) {
+  for (int r0 = rb + lr; r0 < nk; r0 += rpi * U) {
     u32x4_t kv[U], vv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1275,13 +1291,13 @@ __global__ __launch_bounds__(256) void k_select_compact(SelectParams p) {
 
 static int g_selcompact_capacity[64];
 
-// The one-launch selection runs when the caller allows it, the chunks keep
-// few rows, the heads are few (many heads take k_select_thresh_head) and the
-// whole grid is resident at once.
+// The one-launch selection runs when the caller allows it, the heads are few
+// (many heads take k_select_thresh_head) and the whole grid is resident at
+// once.
 static bool select_compact_ok(const SelectParams& p) {
-  if (!p.one_launch || !p.cand64 || !p.cnt64 || p.gsplit > 1 || p.nsc > 64) return false;
+  if (!p.one_launch || !p.cand64 || !p.cnt64 || p.gsplit > kMaxGsplit || p.nsc > 64) return false;
   if ((long)p.b * p.hkv >= kThreshHeadsMany) return false;
-  return grid_fits(k_select_compact, g_selcompact_capacity, (long)p.nsc * p.hkv * p.b);
+  return grid_fits(k_select_compact, g_selcompact_capacity, (long)p.nsc * max(p.gsplit, 1) * p.hkv * p.b);
 }
 
 // ------------------------------------------------------------- slot reuse
@@ -1521,7 +1537,8 @@ hipError_t launch_select_err_zero(const SelectParams& p, hipStream_t s, Trace* t
 
 hipError_t launch_select(const SelectParams& p, hipStream_t s, Trace* tr) {
   if (p.cap <= kSelectLdsKeys) {
-    if (select_compact_ok(p)) return launch_k(k_select_compact, dim3(p.nsc, p.hkv, p.b), dim3(256), s, tr, p);
+    if (select_compact_ok(p))
+      return launch_k(k_select_compact, dim3(p.nsc * max(p.gsplit, 1), p.hkv, p.b), dim3(256), s, tr, p);
     hipError_t e = launch_thresh(p, s, tr);
     if (e != hipSuccess) return e;
     return launch_k(k_compact, dim3(p.nsc * std::max(p.gsplit, 1), p.hkv, p.b), dim3(256), s, tr, p);

@@ -205,7 +205,7 @@ def test_bench_kernel_names_follow_the_reduce_folding():
             assert names[-len(sel):] == sel, (mode, cap)
             names = names[:-len(sel)]
             if bench.scores_fused(mode, cap):
-                assert mode == "keysum" and -(-cap // chunk) > fmax
+                assert -(-cap // chunk) > fmax
                 assert names == ["scores"] + [k for k in bench.KERNELS[mode]
                                               if k not in ("stats", "reduce", "pool", "thresh", "compact")]
                 continue
@@ -219,11 +219,24 @@ def test_bench_kernel_names_follow_the_reduce_folding():
     # compute unit; 64 sequences of 8192 tokens do not
     assert bench.rkv_kernels("keysum", 32768)[0] == "scores"
     assert bench.rkv_kernels("keysum", 8192, b=64)[0] == "stats"
-    # the one-launch selection: the n = 32768 layer (32 of 512 kept per chunk),
-    # not the decode cache (about 480 of 512 kept) nor 64 sequences (many heads)
+    # the Gram form's score pass on the same caches
+    assert bench.rkv_kernels("gram", 2176) == ["stats", "pool", "gram", "gram_fin", "select_compact"]
+    assert bench.rkv_kernels("gram", 32768)[:3] == ["scores", "gram", "gram_fin"]
+    assert bench.rkv_kernels("gram", 8192, b=64)[0] == "stats"
+    # slot reuse scores as a compacting call does (never the fused step)
+    assert bench.slot_kernels("gram", 2176) == ["stats", "pool", "gram", "gram_fin", "thresh", "evict"]
+    assert bench.slot_kernels("keysum", 2176) == ["stats", "pool", "thresh", "evict"]
+    assert bench.slot_kernels("gram", 8192)[:2] == ["scores", "gram"]
+    # the one-launch selection: the n = 32768 layer (32 of 512 kept per chunk)
+    # and the decode cache (about 480 of 512 kept: eight gathering work-groups
+    # per chunk), not 64 sequences (many heads)
     assert bench.rkv_kernels("gram", 32768)[-1] == "select_compact"
-    assert bench.rkv_kernels("gram", 2176)[-2:] == ["thresh", "compact"]
+    assert bench.rkv_kernels("gram", 2176)[-1] == "select_compact"
     assert bench.rkv_kernels("keysum", 8192, b=64, budget=1024)[-2:] == ["thresh", "compact"]
+    # 40 heads of the decode cache: 5 chunks * 8 work-groups * 40 do not fit at once
+    assert bench.rkv_kernels("gram", 2176, b=5)[-2:] == ["thresh", "compact"]
+    src_k = open(hdr).read()
+    assert int(re.search(r"constexpr int kMaxGsplit = (\d+);", src_k).group(1)) == 8
     src_sel = open(os.path.join(os.path.dirname(K.__file__), "csrc", "select.hip")).read()
     assert int(re.search(r"constexpr int kThreshHeadsMany = (\d+);", src_sel).group(1)) == bench.THRESH_HEADS_MANY
     assert int(re.search(r"constexpr int kSelChunk = (\d+);", src).group(1)) == bench.SEL_CHUNK
