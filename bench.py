@@ -815,6 +815,31 @@ def copy_calibration(mib: int = 512):
     print(json.dumps({"copy_calibration_bytes": mib << 20, "launches": 5}))
 
 
+def achievable_copy(mib: int = 1024, reps: int = 10) -> dict:
+    """What a plain device-to-device copy reaches on this GPU (torch's copy
+    kernel, 1 GiB read + 1 GiB written per launch, timed with events on its
+    own stream), reported beside the kernels' fractions of the nameplate
+    peak."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    gbps = 2 * (mib << 20) / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBS, 4),
+            "bytes_per_launch": 2 * (mib << 20), "kernel": "torch copy_ (read + write)"}
+
+
 def run_variants(a, hip) -> dict:
     """The other workloads, each reported with its own value and kernels."""
     import torch
@@ -981,6 +1006,7 @@ def main():
         "ms_per_step_traced": round(main_res["ms"], 5),
         "kernels": main_res["kernels"],
     }
+    out["hbm_copy"] = achievable_copy()
     for mode in order[1:]:
         r = res[mode]
         out.setdefault("variants", {})[mode] = {
