@@ -5,6 +5,10 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
 #include <mutex>
 
 #include "../../include/kvsel.h"
@@ -71,6 +75,22 @@ kvsel_status hip_status(hipError_t e) { return e == hipSuccess ? KVSEL_OK : KVSE
 bool separate_kernels() {
   const char* e = getenv("KVSEL_SEPARATE_KERNELS");
   return e && e[0] == '1';
+}
+
+// Salts of the one-launch kernels' tags (head_tag): a per-process random
+// start (the clock and the process id through the SplitMix64 finaliser),
+// then an even stride per launch, so that a stale word in a workspace never
+// carries the tag of a later call (see head_tag).
+static uint32_t next_salt() {
+  static std::atomic<uint32_t> next{[] {
+    uint64_t x = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                 ((uint64_t)getpid() << 32);
+    x += 0x9e3779b97f4a7c15ull;
+    x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
+    x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
+    return (uint32_t)((x ^ (x >> 31)) >> 32);
+  }()};
+  return next.fetch_add(0x9e3779b8u, std::memory_order_relaxed);
 }
 
 #define KV_TRY(expr)                         \
@@ -234,7 +254,7 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
   // work-groups cost as much.
   bool scored = false;
   if (dt == KVSEL_BF16 && d == 128 && p.m <= 32 && ws.fmerged && !separate_kernels()) {
-    const ScoresFusedParams fp{p, ws.fepoch, ws.fpub_a, ws.fmerged};
+    const ScoresFusedParams fp{p, ws.fepoch, ws.fpub_a, ws.fmerged, next_salt()};
     const int grid = scores_fused_grid(sm, fp);
     if (grid > 0) {
       KV_TRY(launch_scores_fused(sm, fp, grid, stream, tr));
@@ -326,6 +346,7 @@ SelectParams select_params(const SelWs& w, const float* z, const int32_t* length
   sp.cnt64 = reinterpret_cast<uint64_t*>(w.acnt);
   sp.one_launch = separate_kernels() ? 0 : 1;
   sp.err = w.err;
+  sp.salt = next_salt();
   return sp;
 }
 
@@ -554,9 +575,10 @@ static kvsel_status score_evict_impl(kvsel_dtype dt, kvsel_redundancy mode, cons
     fp.v_out = static_cast<char*>(v_out);
     fp.err = ws.err;
     fp.epoch = ws.fepoch;
-    fp.flags = ws.fflags;
     fp.pub_a = ws.fpub_a;
+    fp.flags = ws.fflags;
     fp.pub_b = ws.fpub_b;
+    fp.salt = next_salt();
     if (!separate_kernels() && fused_fits(fp)) return hip_status(launch_fused(fp, stream, tr));
   }
   uint32_t* hist = cap <= kSelectLdsKeys ? ws.sel.hist : nullptr;

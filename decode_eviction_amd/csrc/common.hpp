@@ -347,24 +347,18 @@ __device__ __forceinline__ void vmem_done() { __builtin_amdgcn_s_waitcnt(waitcnt
 // error word and gives up (the kernel still finishes).
 constexpr int kSpinLimit = 1 << 20;
 
-// SplitMix64 finaliser (Steele, Lea and Flood's SplitMix generator): a
-// bijection of 64-bit words with good avalanche.
-__device__ __forceinline__ uint64_t mix64(uint64_t x) {
-  x += 0x9e3779b97f4a7c15ull;
-  x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
-  x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
-  return x ^ (x >> 31);
-}
-
-// The 32-bit tag of a head's data words and its 64-bit barrier tokens in
-// one call: hashes of the head's epoch and the head's index, so that words
-// another head or an earlier call left in the workspace (one reused across
-// shapes holds them at any address) never pass for this call's.
-__device__ __forceinline__ uint64_t head_key(uint64_t ep, long head, uint64_t k) {
-  return mix64(4 * ep + k + ((uint64_t)head << 44));
-}
-__device__ __forceinline__ uint32_t head_tag(uint64_t ep, long head) {
-  return (uint32_t)(head_key(ep, head, 0) >> 32);
+// The 32-bit tag of a head's words in one call: the head's epoch (a
+// counter in the workspace that every call advances by one) plus the call's
+// salt (a value the host draws for every launch: an even stride apart from
+// the previous launch's, from a per-process random start), with the head
+// index spread by an odd constant.  On one workspace, consecutive calls
+// move the tag by the stride plus one (odd), so the last 2^32 calls' tags
+// all differ and words an earlier call left behind never pass for this
+// call's; graph replays (same salt) move it by one.  A workspace whose
+// memory held other data (its epoch words overwritten, for instance with
+// zeros) still gets a new tag from the salt.
+__device__ __forceinline__ uint32_t head_tag(uint64_t ep, long head, uint32_t salt) {
+  return salt + (uint32_t)ep + (uint32_t)head * 0x85ebca6bu;
 }
 
 // A 64-bit word holding a 32-bit value (low half) and a call's tag (high half).

@@ -29,14 +29,14 @@
 // Barriers.  Values that cross work-groups are 64-bit words, the value in
 // the low half and the call's tag in the high half, written and read with
 // device-scope accesses (they pass between XCDs).  A work-group issues its
-// words, then writes a 64-bit token into its slot of the head's flag row; a
-// reader waits until the row holds the token, then reads the words and reads
-// again any whose tag is not there yet (its store was issued before the
-// flag's but may land later).  Tag and token are hashes (SplitMix64
-// finaliser) of the head's index and its epoch, a counter in the workspace
-// that each call advances by one after barrier A: consecutive calls and
-// different heads differ in both, so neither what a fresh workspace holds nor
-// what earlier calls left there passes for a signal.  No initialisation kernel is needed and graph
+// words, then writes a flag word (the tag and the barrier's number) into its
+// slot of the head's flag row; a reader waits until the row holds every
+// flag, then reads the words and reads again any whose tag is not there yet
+// (its store was issued before the flag's but may land later).
+// The tag (head_tag) combines the head's epoch, a counter in the workspace
+// that each call advances by one after barrier A, with the call's salt from
+// the host, so neither what a fresh workspace holds nor what earlier calls
+// left there passes for this call's.  No initialisation kernel is needed and graph
 // replays work.  The host launches this kernel only when the whole grid fits
 // on the device at once, so every wait ends; a wait that still exceeds its
 // poll limit sets bit 2 of the error word and continues.
@@ -49,21 +49,24 @@ namespace kvsel {
 
 constexpr int kFusedKeys = kFusedMaxChunks * kChunk;   // 4096
 
+// The head's flag row of barrier `which` (A: 0, B: 1).
 __device__ __forceinline__ uint64_t* flag_row(const FusedParams& p, int which, long head) {
   return p.flags + ((long)which * p.b * p.hkv + head) * kFusedMaxChunks;
 }
 
-// This work-group's signal, once every wave has issued its tagged words.
+// This work-group's signal, once every wave has issued its tagged words: the
+// call's tag and the barrier's number in one word.
 __device__ __forceinline__ void signal(const FusedParams& p, int which, long head, int chunk,
-                                       uint64_t tok, int tid) {
+                                       uint32_t tag, int tid) {
   __syncthreads();
-  if (tid == 0) st_dev(flag_row(p, which, head) + chunk, tok);
+  if (tid == 0) st_dev(flag_row(p, which, head) + chunk, tagged(tag, (uint32_t)which + 1u));
 }
 
 // Wait (wave 0 polls) until the head's nwg work-groups have signalled.
 __device__ __forceinline__ void wait_flags(const FusedParams& p, int which, long head, int nwg,
-                                           uint64_t tok, int tid) {
+                                           uint32_t tag, int tid) {
   if (tid < kWave) {
+    const uint64_t tok = tagged(tag, (uint32_t)which + 1u);
     const uint64_t* fl = flag_row(p, which, head);
     bool ok = false;
     for (int it = 0; it < kSpinLimit && !ok; ++it) {
@@ -75,7 +78,6 @@ __device__ __forceinline__ void wait_flags(const FusedParams& p, int which, long
   }
   __syncthreads();
 }
-
 
 // The value of a tagged word already read as w: read again while the tag is
 // missing.
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   if (c0 >= n) return;
   const int nwg = (n + kChunk - 1) / kChunk;
   const uint64_t ep = ld_dev(p.epoch + head);
-  const uint32_t tag = head_tag(ep, head);
+  const uint32_t tag = head_tag(ep, head, p.salt);
   const char* kb = p.k + head * (long)p.cap * RB;
   const char* qb = p.q + ((long)bi * p.hq + (long)h * p.g) * p.w * RB;
   uint64_t* pa = p.pub_a + head * kFusedMaxChunks * kFusedWordsA;
@@ -359,8 +361,8 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
         st_dev(rec + 2 * r + 1, tagged(tag, __float_as_uint(s)));
       },
       [&](int dim, float s) { st_dev(rec + 64 + dim, tagged(tag, __float_as_uint(s))); });
-  signal(p, 0, head, chunk, head_key(ep, head, 1), tid);
-  wait_flags(p, 0, head, nwg, head_key(ep, head, 1), tid);
+  signal(p, 0, head, chunk, tag, tid);
+  wait_flags(p, 0, head, nwg, tag, tid);
   if (chunk == 0 && tid == 0) st_dev(p.epoch + head, ep + 1);  // every work-group has read ep
 
   // ---- phase 2: merged statistics, importance, redundancy, Z (k_pool's arithmetic)
@@ -448,8 +450,8 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
     gather();
     return;
   }
-  signal(p, 1, head, chunk, head_key(ep, head, 2), tid);
-  wait_flags(p, 1, head, nwg, head_key(ep, head, 2), tid);
+  signal(p, 1, head, chunk, tag, tid);
+  wait_flags(p, 1, head, nwg, tag, tid);
 
   // ---- phase 3: the head's keys in LDS, the threshold, slots of this chunk
   __shared__ uint32_t kall[kFusedKeys];
@@ -555,6 +557,12 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
       ce += (ok && mk[i] == kth) ? 1u : 0u;
     }
     const uint2 sc = block_scan_u32<NW>(cg | (ce << 16), wsum, tid);
+    // a consistent threshold keeps exactly B keys, so every slot below is in
+    // [0, B); anything else (never seen) is flagged and nothing is written
+    if ((sc.y & 0xffffu) + min(sc.y >> 16, need_eq) != (uint32_t)B) {
+      if (tid == 0) atomicOr(p.err, 8);
+      return;
+    }
     uint32_t gtb = sc.x & 0xffffu, eqb = sc.x >> 16;
     // this chunk's positions are owned by threads c0 / KPT .. (c0 + kChunk) / KPT - 1
     const bool mine = KPT * tid >= c0 && KPT * tid < c0 + kChunk;
@@ -648,7 +656,7 @@ __device__ __forceinline__ void scores_fused_unit(const ScoresFusedParams& fp, i
   if (c0 >= n) return;
   const int nwg = (n + kChunk - 1) / kChunk;
   const uint64_t ep = ld_dev(fp.epoch + head);
-  const uint32_t tag = head_tag(ep, head);
+  const uint32_t tag = head_tag(ep, head, fp.salt);
   const char* kb = p.k + head * (long)p.cap * RB;
   const char* qb = p.q + ((long)bi * p.hq + (long)h * p.g) * p.w * RB;
 

@@ -147,6 +147,7 @@ constexpr int kSelChunk = 512;     // positions per compaction work-group
 // most work-groups that share one selection chunk's gather
 constexpr int kMaxGsplit = 8;
 struct SelectParams {
+  uint32_t salt;            // per-call salt of the one-launch selection's tags (head_tag)
   const float* z;           // [b][Hkv][cap]
   const int32_t* lengths;
   int b, hkv, cap, budget;
@@ -260,9 +261,10 @@ struct FusedParams {
   int32_t* err;
   // workspace
   uint64_t* epoch;          // [b][Hkv]: advanced by one every call
-  uint64_t* flags;          // [2][b][Hkv][kFusedMaxChunks]: barrier tokens
+  uint64_t* flags;          // [2][b][Hkv][kFusedMaxChunks]: barrier flag words
   uint64_t* pub_a;          // [b][Hkv][kFusedMaxChunks][kFusedWordsA]: tagged chunk partials
   uint64_t* pub_b;          // [b][Hkv][cap]: tagged score keys
+  uint32_t salt;            // per-call salt of the tags (head_tag)
 };
 
 // One-launch score pass (fused.hip): what k_stats, k_reduce and k_pool
@@ -282,6 +284,7 @@ struct ScoresFusedParams {
   uint64_t* epoch;          // [b][Hkv]: advanced by one every call
   uint64_t* part;           // [b][Hkv][nchunk][words per record]: tagged chunk partials
   uint64_t* merged;         // [b][Hkv][words per record]: tagged merged record
+  uint32_t salt;            // per-call salt of the tags (head_tag)
 };
 
 // Optional per-kernel timing: the k-th kernel an entry point launches records

@@ -960,7 +960,7 @@ __global__ __launch_bounds__(256) void k_select_compact(SelectParams p) {
   uint32_t kth = 0u, need_eq = 0u, off = (uint32_t)c0, eqb = 0u;
 
   if (!all) {
-    const uint32_t tag = head_tag(ep, head);
+    const uint32_t tag = head_tag(ep, head, p.salt);
     // level 1: the bin where the count from the top reaches B (as in
     // k_select_thresh)
     const uint32_t hb[8] = {hv0.x, hv0.y, hv0.z, hv0.w, hv1.x, hv1.y, hv1.z, hv1.w};

@@ -378,7 +378,12 @@ kvsel_status kvsel_threshold_cut_from_attn(const float* attn_last, const int32_t
  * the one-launch selection exceeded its poll limit (the results of that call are not to be trusted;
  * it cannot happen while the device runs the whole grid at once, which the
  * library checks before choosing those paths, unless kernels of other
- * streams hold compute units for that long).  Returns KVSEL_ERR_HIP if the copy fails. */
+ * streams hold compute units for that long); bit 3: a work-group of the
+ * single-launch short-cache step found a threshold that does not keep
+ * exactly the budget, which a consistent selection never does (that
+ * work-group writes no slots or rows; the call's results are not to be
+ * trusted).  Returns KVSEL_ERR_HIP if the copy
+ * fails. */
 kvsel_status kvsel_workspace_error(const void* workspace, int32_t* flags_host, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -113,3 +113,37 @@ def test_fused_tied_scores_take_the_fallback():
     for g, (a, b_) in enumerate([(0, 700), (700, 1500), (1500, 2176)]):
         case.k[1, :, a:b_] = case.k[1, :, a:a + 1]    # sequence 1: three repeated keys
     assert _check(case) == 0
+
+
+@pytest.mark.parametrize("n", [2176, 32768])
+def test_words_left_in_a_reused_workspace_never_pass(n):
+    # A workspace whose memory held an earlier call's data: its per-head
+    # epochs back at the values that call started from (zero here, as a
+    # zero-filled buffer reused for it leaves them) while the tagged words
+    # the call published are still there.  A later call on other keys must
+    # not take those words for its own: its results equal those of a call on
+    # a clean workspace.  n = 2176 runs the one-launch short-cache step,
+    # n = 32768 the one-launch score pass and selection.  Layout used here:
+    # the error words (256 bytes), then one 8-byte epoch per (sequence, head).
+    first = synth.layer8b_case(5, n=n, budget=2048, cap=n)
+    later = synth.layer8b_case(6, n=n, budget=2048, cap=n)
+    log(f"[fused] reused workspace n={n}")
+    nbytes = K.kvsel_score_evict_workspace(1, first.hq, first.hkv, 128, first.w, n, 2048)
+    epochs_end = 256 + 8 * first.b * first.hkv
+
+    def call(case, ws):
+        q, k, v = dev(case.q, "bf16"), dev(case.k, "bf16"), dev(case.v, "bf16")
+        z = torch.full((case.b, case.hkv, n), float("nan"), device="cuda")
+        ko, vo, idx = K.kvsel_score_evict(q, k, v, dev_i32(case.lengths), 2048, case.lam, "keysum",
+                                          scores_out=z, workspace=ws)
+        flags = K.kvsel_workspace_error(ws)
+        return z.cpu().numpy(), idx.cpu().numpy(), host_bits(ko), host_bits(vo), flags
+
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    call(first, ws)
+    ws[:epochs_end] = 0
+    got = call(later, ws)
+    want = call(later, torch.zeros(nbytes, dtype=torch.uint8, device="cuda"))
+    assert got[4] & 4 == 0 and want[4] & 4 == 0
+    for x, y in zip(got[:4], want[:4]):
+        assert np.array_equal(x, y, equal_nan=True)
