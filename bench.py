@@ -123,9 +123,12 @@ def rkv_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV, budget: int = B
 
 def slot_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV) -> list:
     """Kernels one slot-reuse call (kvsel_score_evict_slots) launches: the
-    scores as a compacting call computes them (the one-launch score pass
-    where it applies, never the fused step), the threshold, the evicted
-    list."""
+    fused step's slot-reuse form alone where the fused step applies (scores,
+    threshold and the evicted list in one launch); otherwise the scores as a
+    compacting call computes them (the one-launch score pass where it
+    applies), the threshold, the evicted list."""
+    if fused_step(mode, cap, b, hkv):
+        return ["fused_slots"]
     ks = [k for k in unfused_kernels(mode, cap) if k not in ("thresh", "compact")]
     if scores_fused(mode, cap, b, hkv):
         ks = ["scores"] + [k for k in ks if k not in ("stats", "reduce", "pool")]
@@ -184,6 +187,8 @@ def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int =
     # the fused short-cache step: K once, Z and the indices written, the kept
     # rows of V read and of K and V written (K rows come from registers)
     cost["fused"] = {"bytes": kb + 4 * tok + 4 * b * hkv * budget + 3 * b * hkv * min(budget, n) * d * 2}
+    # its slot-reuse form: K once, Z and the evicted list written
+    cost["fused_slots"] = {"bytes": kb + 4 * tok + 4 * b * hkv * max(n - budget, 0)}
     # the one-launch score pass: K once, I and Z written
     cost["scores"] = {"bytes": kb + 8 * tok}
     if mode == "gram":
@@ -613,7 +618,7 @@ def run_refreekv_rows(hip, n_layers, steps, k_rows=64):
 
 KERNEL_SOURCES = {"stats": "scores.hip", "reduce": "scores.hip", "pool": "scores.hip",
                   "gram": "gram.hip", "gram_fin": "gram.hip", "thresh": "select.hip", "select_compact": "select.hip",
-                  "compact": "select.hip", "fused": "fused.hip", "scores": "fused.hip",
+                  "compact": "select.hip", "fused": "fused.hip", "fused_slots": "fused.hip", "scores": "fused.hip",
                   "evict": "select.hip", "select": "select.hip", "gather": "select.hip",
                   "cut_energy": "cut.hip", "cut_scan": "cut.hip", "cut_compact": "cut.hip"}
 

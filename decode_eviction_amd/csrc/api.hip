@@ -323,6 +323,43 @@ SelWs carve_select(Carver& c, int b, int hkv, int cap) {
   return w;
 }
 
+// The single-launch short-cache step (key-sum form, bf16, d = 128, at most 32
+// window rows per KV head, at most kFusedMaxChunks chunks per head) applies.
+static bool fused_step_applies(kvsel_dtype dt, kvsel_redundancy mode, int hq, int hkv, int d,
+                               int w, int cap) {
+  return mode == KVSEL_R_KEYSUM && dt == KVSEL_BF16 && d == 128 && (hq / hkv) * w <= 32 &&
+         (cap + kChunk - 1) / kChunk <= kFusedMaxChunks;
+}
+
+// Its parameters shared by the compacting and the slot-reuse forms.
+static FusedParams fused_params(const void* q_window, const void* k, const int32_t* lengths, int b,
+                                int hq, int hkv, int d, int w, int cap, float lambda, int budget,
+                                const int32_t* budgets, float* z, const ScoreWs& ws) {
+  FusedParams fp{};
+  fp.q = static_cast<const char*>(q_window);
+  fp.k = static_cast<const char*>(k);
+  fp.lengths = lengths;
+  fp.b = b;
+  fp.hq = hq;
+  fp.hkv = hkv;
+  fp.g = hq / hkv;
+  fp.w = w;
+  fp.m = fp.g * w;
+  fp.cap = cap;
+  fp.budget = budget;
+  fp.scale2 = kLog2e / sqrtf((float)d);
+  fp.lambda = lambda;
+  fp.budgets = budgets;
+  fp.z_out = z;
+  fp.err = ws.err;
+  fp.epoch = ws.fepoch;
+  fp.flags = ws.fflags;
+  fp.pub_a = ws.fpub_a;
+  fp.pub_b = ws.fpub_b;
+  fp.salt = next_salt();
+  return fp;
+}
+
 SelectParams select_params(const SelWs& w, const float* z, const int32_t* lengths, int b, int hkv,
                            int cap, int budget, int32_t* idx) {
   SelectParams sp{};
@@ -550,35 +587,14 @@ static kvsel_status score_evict_impl(kvsel_dtype dt, kvsel_redundancy mode, cons
   float* z = scores_out ? scores_out : ws.z;
   // short caches, key-sum form: the whole step in one launch when its grid
   // fits on the device at once
-  if (mode == KVSEL_R_KEYSUM && dt == KVSEL_BF16 && d == 128 && (hq / hkv) * w <= 32 &&
-      (cap + kChunk - 1) / kChunk <= kFusedMaxChunks) {
-    FusedParams fp{};
-    fp.q = static_cast<const char*>(q_window);
-    fp.k = static_cast<const char*>(k);
+  if (fused_step_applies(dt, mode, hq, hkv, d, w, cap)) {
+    FusedParams fp = fused_params(q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, budget,
+                                  budgets, z, ws);
     fp.v = static_cast<const char*>(v);
-    fp.lengths = lengths;
-    fp.b = b;
-    fp.hq = hq;
-    fp.hkv = hkv;
-    fp.g = hq / hkv;
-    fp.w = w;
-    fp.m = fp.g * w;
-    fp.cap = cap;
-    fp.budget = budget;
     fp.cap_out = cap_out;
-    fp.scale2 = kLog2e / sqrtf((float)d);
-    fp.lambda = lambda;
-    fp.budgets = budgets;
-    fp.z_out = z;
     fp.idx = idx_out;
     fp.k_out = static_cast<char*>(k_out);
     fp.v_out = static_cast<char*>(v_out);
-    fp.err = ws.err;
-    fp.epoch = ws.fepoch;
-    fp.pub_a = ws.fpub_a;
-    fp.flags = ws.fflags;
-    fp.pub_b = ws.fpub_b;
-    fp.salt = next_salt();
     if (!separate_kernels() && fused_fits(fp)) return hip_status(launch_fused(fp, stream, tr));
   }
   uint32_t* hist = cap <= kSelectLdsKeys ? ws.sel.hist : nullptr;
@@ -708,6 +724,17 @@ static kvsel_status score_evict_slots_impl(kvsel_dtype dt, kvsel_redundancy mode
   if (!workspace || ws_bytes < need.bytes) return KVSEL_ERR_WORKSPACE;
   const ScoreWs ws = score_ws(workspace, b, hkv, d, (hq / hkv) * w, cap, mode);
   float* z = scores_out ? scores_out : ws.z;
+  // short caches, key-sum form: scores, threshold and the evicted list in
+  // one launch when its grid fits on the device at once
+  if (fused_step_applies(dt, mode, hq, hkv, d, w, cap)) {
+    FusedParams fp = fused_params(q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, budget,
+                                  budgets, z, ws);
+    fp.pos = pos;
+    fp.evict = evict_out;
+    fp.evict_stride = evict_stride;
+    fp.n_evict = n_evict_out;
+    if (!separate_kernels() && fused_fits(fp)) return hip_status(launch_fused(fp, stream, tr));
+  }
   st = run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, nullptr, nullptr,
                   z, ws.sel.hist, ws, stream, tr);
   if (st != KVSEL_OK) return st;

@@ -276,7 +276,62 @@ __device__ __forceinline__ void pool_tokens(const Frag<Geo<E, D>::kNC> (&kf)[2],
   }
 }
 
-template <typename E, int D>
+// The need-th largest (need >= 1, at most the count of keys in play) of the
+// keys v[i] that bit i of `play` marks, over the work-group's threads, by
+// rounds of 11-bit histograms in lh (2048 counters) until one key value is
+// left: returns that key and how many of its copies rank within the first
+// need.  The slot-reuse step's split of threshold ties by position.
+template <int KPT, int NW>
+__device__ __noinline__ uint2 nth_largest(const uint32_t (&v)[KPT], uint32_t play, uint32_t need,
+                                          uint32_t* lh, uint32_t* wsum, uint32_t* bc, int tid) {
+  uint32_t lo = 0u, hi = 0xffffffffu;
+  while (lo < hi) {
+    const uint32_t span = hi - lo;
+    const int bits = 32 - __clz(span);
+    const int shift = bits > kHistBits ? bits - kHistBits : 0;
+    const int nb = (int)(span >> shift) + 1;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lh[8 * tid + i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const uint32_t off = v[i] - lo;
+      if (((play >> i) & 1u) && off <= span) atomicAdd(&lh[off >> shift], 1u);
+    }
+    __syncthreads();
+    uint32_t rb[8], rs = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      rb[i] = 8 * tid + i < nb ? lh[8 * tid + i] : 0u;
+      rs += rb[i];
+    }
+    const uint2 sc = block_scan_u32<NW>(rs, wsum, tid);
+    uint32_t above = sc.y - sc.x - rs;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      if (above < need && above + rb[i] >= need) {
+        bc[0] = 8 * tid + i;
+        bc[1] = above;
+      }
+      above += rb[i];
+    }
+    __syncthreads();
+    const uint32_t bin = bc[0];
+    need -= bc[1];
+    const uint64_t nlo = (uint64_t)lo + ((uint64_t)bin << shift);
+    const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
+    lo = (uint32_t)nlo;
+    hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+  }
+  return make_uint2(lo, need);
+}
+
+// SLOTS: the slot-reuse form (kvsel_score_evict_slots): the same scores and
+// threshold, ties at the threshold kept by lower token position (the
+// caller's position map; equal positions: lower slot), and instead of the
+// compaction the evicted slots listed in slot order; V is not read.
+template <typename E, int D, bool SLOTS>
 __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   using G = Geo<E, D>;
   constexpr int NC = G::kNC;
@@ -304,9 +359,17 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   }
   const int n = clamp_len(p.lengths[bi], p.cap);
   const int B = fused_budget(p, h);
-  int32_t* out = p.idx + head * p.budget;
-  if (chunk == 0)
+  int32_t* out = SLOTS ? p.evict + head * (long)p.evict_stride : p.idx + head * p.budget;
+  if constexpr (SLOTS) {
+    // n - min(B, n) evicted slots, then -1
+    const int nev = n - min(n, B);
+    if (chunk == 0) {
+      for (int t = nev + tid; t < p.evict_stride; t += 256) out[t] = -1;
+      if (tid == 0) p.n_evict[head] = nev;
+    }
+  } else if (chunk == 0) {
     for (int t = min(n, B) + tid; t < p.budget; t += 256) out[t] = -1;
+  }
   if (c0 >= n) return;
   const int nwg = (n + kChunk - 1) / kChunk;
   const uint64_t ep = ld_dev(p.epoch + head);
@@ -335,7 +398,7 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   // V rows of the chunk into LDS (rows past cap arrive as zeros), for the
   // gather at the end
   __shared__ __attribute__((aligned(16))) char vl[kChunk * RB];
-  {
+  if constexpr (!SLOTS) {
     const __amdgpu_buffer_rsrc_t rv =
         buf_rsrc(p.v + (head * p.cap + c0) * (long)RB, (uint32_t)(p.cap - c0) * RB);
     constexpr int PER_WAVE = kChunk * RB / (NW * 1024);
@@ -442,6 +505,12 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
       }
     }
   };
+  if constexpr (SLOTS) {
+    if (B == 0 || n <= B) {  // every slot evicted (in slot order), or none
+      if (B == 0 && c0 + tid < n) out[c0 + tid] = c0 + tid;
+      return;
+    }
+  }
   if (B == 0) return;
   if (n <= B) {  // everything is kept, in place
     const int pos = c0 + tid;
@@ -563,6 +632,68 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
       if (tid == 0) atomicOr(p.err, 8);
       return;
     }
+    if constexpr (SLOTS) {
+      // kept: above the threshold, or one of the need_eq copies of it that
+      // come first by (position, slot)
+      uint32_t kept = 0u, tied = 0u;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const bool ok = KPT * tid + i < n;
+        kept |= (ok && mk[i] > kth) ? 1u << i : 0u;
+        tied |= (ok && mk[i] == kth) ? 1u << i : 0u;
+      }
+      if (need_eq == (sc.y >> 16) || !p.pos) {
+        // every copy kept, or positions are the slots: the first need_eq
+        // copies in slot order
+        uint32_t eqb = sc.x >> 16;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+          if ((tied >> i) & 1u) {
+            kept |= eqb < need_eq ? 1u << i : 0u;
+            ++eqb;
+          }
+      } else {
+        // the copies split by position: the need_eq-th smallest position
+        // among them (as the need_eq-th largest of ~pos), equal positions
+        // in slot order
+        const int32_t* pm = p.pos + head * (long)p.cap;
+        uint32_t v2[KPT];
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) v2[i] = ((tied >> i) & 1u) ? ~(uint32_t)pm[KPT * tid + i] : 0u;
+        const uint2 pt = nth_largest<KPT, NW>(v2, tied, need_eq, lh, wsum, bc, tid);
+        uint32_t c2 = 0;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) c2 += (((tied >> i) & 1u) && v2[i] == pt.x) ? 1u : 0u;
+        uint32_t e2 = block_scan_u32<NW>(c2, wsum, tid).x;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+          if ((tied >> i) & 1u) {
+            if (v2[i] > pt.x) {
+              kept |= 1u << i;
+            } else if (v2[i] == pt.x) {
+              kept |= e2 < pt.y ? 1u << i : 0u;
+              ++e2;
+            }
+          }
+      }
+      // evicted slots in slot order: this thread's evicted positions follow
+      // those of the threads before it
+      uint32_t ne = 0;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) ne += (KPT * tid + i < n && !((kept >> i) & 1u)) ? 1u : 0u;
+      uint32_t eb = block_scan_u32<NW>(ne, wsum, tid).x;
+      const bool mine = KPT * tid >= c0 && KPT * tid < c0 + kChunk;
+      const uint32_t nev = (uint32_t)(n - B);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int pos = KPT * tid + i;
+        if (pos < n && !((kept >> i) & 1u)) {
+          if (mine && eb < nev) out[eb] = pos;
+          ++eb;
+        }
+      }
+      return;
+    }
     uint32_t gtb = sc.x & 0xffffu, eqb = sc.x >> 16;
     // this chunk's positions are owned by threads c0 / KPT .. (c0 + kChunk) / KPT - 1
     const bool mine = KPT * tid >= c0 && KPT * tid < c0 + kChunk;
@@ -589,7 +720,8 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
 
 hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr) {
   const dim3 grid((p.cap + kChunk - 1) / kChunk, p.hkv, p.b);
-  return launch_k(k_rkv_fused<BF16, 128>, grid, dim3(256), s, tr, p);
+  if (p.evict) return launch_k(k_rkv_fused<BF16, 128, true>, grid, dim3(256), s, tr, p);
+  return launch_k(k_rkv_fused<BF16, 128, false>, grid, dim3(256), s, tr, p);
 }
 
 // ------------------------------------------------------------------------
@@ -851,11 +983,12 @@ void k_scores_fused(ScoresFusedParams fp) {
   scores_fused_unit<E, D, MODE>(fp, v - hb * fp.s.nchunk, hb % fp.s.hkv, hb / fp.s.hkv);
 }
 
-static int g_fused_capacity[64];
+static int g_fused_capacity[2][64];
 
 bool fused_fits(const FusedParams& p) {
-  return grid_fits(k_rkv_fused<BF16, 128>, g_fused_capacity,
-                   (long)((p.cap + kChunk - 1) / kChunk) * p.hkv * p.b);
+  const long total = (long)((p.cap + kChunk - 1) / kChunk) * p.hkv * p.b;
+  if (p.evict) return grid_fits(k_rkv_fused<BF16, 128, true>, g_fused_capacity[1], total);
+  return grid_fits(k_rkv_fused<BF16, 128, false>, g_fused_capacity[0], total);
 }
 
 static int g_scores_capacity[2][64];

@@ -259,6 +259,11 @@ struct FusedParams {
   char* k_out;              // [b][Hkv][cap_out][d]
   char* v_out;
   int32_t* err;
+  // slot reuse (non-null evict: evicted slots listed instead of the compaction)
+  const int32_t* pos;       // nullable [b][Hkv][cap]: token position of each slot
+  int32_t* evict;           // [b][Hkv][evict_stride]
+  int evict_stride;
+  int32_t* n_evict;         // [b][Hkv]
   // workspace
   uint64_t* epoch;          // [b][Hkv]: advanced by one every call
   uint64_t* flags;          // [2][b][Hkv][kFusedMaxChunks]: barrier flag words

@@ -256,7 +256,12 @@ kvsel_status kvsel_select_evict_slots(const float* z, const int32_t* lengths, co
                                       void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Scores (as kvsel_scores) then kvsel_select_evict_slots in one call; k is
- * read only.  Same workspace size as kvsel_score_evict. */
+ * read only.  Same workspace size as kvsel_score_evict.  Key-sum form on a
+ * cache of at most 4096 slots (bf16, d = 128, g*w <= 32), when its grid of
+ * ceil(cap / 256) * Hkv * b work-groups fits on the device at once: one
+ * kernel computes the scores, the threshold and the evicted list (the same
+ * scores and the same list as the separate kernels, which run otherwise or
+ * with KVSEL_SEPARATE_KERNELS=1). */
 kvsel_status kvsel_score_evict_slots(kvsel_dtype dt, kvsel_redundancy mode,
                                      const void* q_window, const void* k, const int32_t* lengths,
                                      const int32_t* pos, const int32_t* budgets,
@@ -266,7 +271,8 @@ kvsel_status kvsel_score_evict_slots(kvsel_dtype dt, kvsel_redundancy mode,
                                      void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* kvsel_score_evict_slots with per-kernel timing as in kvsel_score_evict_traced.
- * Launch order: the score kernels of the mode, threshold, evict. */
+ * Launch order: the score kernels of the mode, threshold, evict; or the
+ * single kernel of the short-cache key-sum form. */
 kvsel_status kvsel_score_evict_slots_traced(kvsel_dtype dt, kvsel_redundancy mode,
                                             const void* q_window, const void* k,
                                             const int32_t* lengths, const int32_t* pos,

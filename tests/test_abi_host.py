@@ -223,9 +223,11 @@ def test_bench_kernel_names_follow_the_reduce_folding():
     assert bench.rkv_kernels("gram", 2176) == ["stats", "pool", "gram", "gram_fin", "select_compact"]
     assert bench.rkv_kernels("gram", 32768)[:3] == ["scores", "gram", "gram_fin"]
     assert bench.rkv_kernels("gram", 8192, b=64)[0] == "stats"
-    # slot reuse scores as a compacting call does (never the fused step)
+    # slot reuse: the fused step's slot form where the fused step applies,
+    # otherwise the scores as a compacting call computes them
     assert bench.slot_kernels("gram", 2176) == ["stats", "pool", "gram", "gram_fin", "thresh", "evict"]
-    assert bench.slot_kernels("keysum", 2176) == ["stats", "pool", "thresh", "evict"]
+    assert bench.slot_kernels("keysum", 2176) == ["fused_slots"]
+    assert bench.slot_kernels("keysum", 2176, b=64) == ["stats", "pool", "thresh", "evict"]
     assert bench.slot_kernels("gram", 8192)[:2] == ["scores", "gram"]
     # the one-launch selection: the n = 32768 layer (32 of 512 kept per chunk)
     # and the decode cache (about 480 of 512 kept: eight gathering work-groups

@@ -147,3 +147,86 @@ def test_words_left_in_a_reused_workspace_never_pass(n):
     assert got[4] & 4 == 0 and want[4] & 4 == 0
     for x, y in zip(got[:4], want[:4]):
         assert np.array_equal(x, y, equal_nan=True)
+
+
+# ---- the slot-reuse form of the one-launch step (kvsel_score_evict_slots)
+
+def _slots_check(case, pos=None, budgets=None, separate=False, monkeypatch=None):
+    """The one-launch slot step against the multi-kernel scores and the
+    stage selection on them (bit for bit), and the oracle's evicted list on
+    the same scores."""
+    q, k = dev(case.q, "bf16"), dev(case.k, "bf16")
+    lens = dev_i32(case.lengths)
+    b, hkv, cap = case.b, case.hkv, case.cap
+    log(f"[fused slots] {case.name} b={b} hkv={hkv} cap={cap} lengths={case.lengths.tolist()} "
+        f"B={case.budget} budgets={None if budgets is None else list(budgets)} pos={pos is not None}")
+    ws = torch.empty(K.kvsel_score_evict_workspace(b, case.hq, hkv, case.d, case.w, cap, case.budget),
+                     dtype=torch.uint8, device="cuda")
+    ws.fill_(0x5a)
+    pos_d = None if pos is None else dev_i32(pos)
+    bud_d = None if budgets is None else dev_i32(budgets)
+    runs = []
+    for rep in range(2):
+        z = torch.full((b, hkv, cap), float("nan"), device="cuda")
+        ev, ne = K.kvsel_score_evict_slots(q, k, lens, case.budget, case.lam, "keysum", pos=pos_d,
+                                           budgets=bud_d, scores_out=z, workspace=ws)
+        flags = K.kvsel_workspace_error(ws)
+        assert flags & 12 == 0, f"flags {flags}"
+        runs.append((z.cpu().numpy(), ev.cpu().numpy(), ne.cpu().numpy(), flags))
+    z, ev, ne, flags = runs[0]
+    for x, y in zip(runs[1][:3], runs[0][:3]):
+        assert np.array_equal(x, y, equal_nan=True)
+    lens_c = np.minimum(case.lengths, cap)
+    _, _, z_ref = K.kvsel_scores(q, k, lens, case.lam, "keysum")
+    want_ev, want_ne = K.kvsel_select_evict_slots(z_ref, dev_i32(lens_c), case.budget, pos=pos_d,
+                                                  budgets=bud_d)
+    z_ref, want_ev, want_ne = z_ref.cpu().numpy(), want_ev.cpu().numpy(), want_ne.cpu().numpy()
+    for bb in range(b):
+        n = int(lens_c[bb])
+        for h in range(hkv):
+            assert np.array_equal(z[bb, h, :n], z_ref[bb, h, :n]), (bb, h)
+            assert ne[bb, h] == want_ne[bb, h], (bb, h)
+            assert np.array_equal(ev[bb, h], want_ev[bb, h]), (bb, h)
+            bh = case.budget if budgets is None else rkv.head_budget(budgets, h, case.budget)
+            want = rkv.evict_slots(z[bb, h, :n].astype(np.float64), bh,
+                                   None if pos is None else pos[bb, h, :n])
+            assert ev[bb, h, :len(want)].tolist() == want.tolist(), (bb, h)
+            assert (ev[bb, h, len(want):] == -1).all()
+    return flags
+
+
+def test_fused_slots_decode_shape():
+    case = synth.layer8b_case(7, n=2176, budget=2048, cap=2176)
+    rng = np.random.default_rng(71)
+    pos = np.stack([rng.permutation(40_000)[:2176] for _ in range(case.hkv)])[None].astype(np.int32)
+    _slots_check(case, pos=pos)
+    _slots_check(case)                                  # no position map: slot order
+
+
+def test_fused_slots_ties_split_by_position():
+    # three groups of exact duplicate keys per head: three score values,
+    # the threshold inside a large tied group; positions a permutation (ties
+    # go to the lower position) and then with duplicates (equal positions:
+    # lower slot)
+    case = synth.rkv_case("slots_ties", seed=72, wl=66, b=2, hq=32, hkv=8, d=128, w=8,
+                          lengths=[2176, 1800], cap=2176, budget=1000, frac=0.0, sink_scale=None)
+    for bb in range(2):
+        for a, e in [(0, 700), (700, 1500), (1500, 2176)]:
+            case.k[bb, :, a:e] = case.k[bb, :, a:a + 1]
+    rng = np.random.default_rng(73)
+    perm = np.stack([np.stack([rng.permutation(2176) for _ in range(8)]) for _ in range(2)])
+    _slots_check(case, pos=perm.astype(np.int32))
+    _slots_check(case, pos=(perm // 3).astype(np.int32))
+
+
+def test_fused_slots_budgets_and_edges():
+    # per-head budgets 0 (every slot evicted), 1, >= n (none evicted) and one
+    # clamped; ragged lengths with one inside a chunk and one empty
+    case = synth.rkv_case("slots_heads", seed=74, wl=67, b=3, hq=32, hkv=8, d=128, w=4,
+                          lengths=[2000, 257, 0], cap=2048, budget=1500)
+    budgets = np.array([0, 1, 300, 1500, 2047, 9000, 700, 256], np.int32)
+    rng = np.random.default_rng(75)
+    pos = np.stack([np.stack([rng.permutation(10_000)[:2048] for _ in range(8)])
+                    for _ in range(3)]).astype(np.int32)
+    flags = _slots_check(case, pos=pos, budgets=budgets)
+    assert flags & 2                                   # 9000 > 1500 was clamped
