@@ -135,12 +135,21 @@ def slot_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV) -> list:
     return ks + ["thresh", "evict"]
 
 
+GRAM_PAIR_CAP = 4096         # kGramPairCap: pair-block Gram units up to this cache size
+
+
 def unfused_kernels(mode: str, cap: int) -> list:
     """The multi-kernel launch sequence (also the score kernels of the slot
-    reuse entry points, which are never fused)."""
+    reuse entry points outside the fused step).  Short Gram-form caches (bf16,
+    d = 128, at most 32 window rows) run the pooling and the pair-block Gram
+    units in one launch (pool_pairs) after k_stats, which then writes the key
+    weights."""
     ks = list(KERNELS[mode])
     if -(-cap // 256) <= 16:
         ks.remove("reduce")
+    if mode == "gram" and cap <= GRAM_PAIR_CAP:
+        ks = [k for k in ks if k != "gram"]
+        ks[ks.index("pool")] = "pool_pairs"
     return ks
 
 
@@ -197,6 +206,10 @@ def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int =
         alg, exe = gram_flops(b, hkv, n, d)
         cost["gram"] = {"bytes": kb + 4 * tok * 2 + 4 * tok * ns // 2, "flops": alg,
                         "flops_executed": exe}
+        # short caches: the pooling (K again, I written) and the pair-block
+        # Gram units in one launch; counted by its matrix-core work
+        cost["pool_pairs"] = {"bytes": 2 * kb + 4 * tok + 4 * tok * -(-n // 128), "flops": alg,
+                              "flops_executed": exe}
         cost["gram_fin"] = {"bytes": 4 * tok * 5 + 4 * tok * ns // 2}
     return cost
 
@@ -619,6 +632,7 @@ def run_refreekv_rows(hip, n_layers, steps, k_rows=64):
 KERNEL_SOURCES = {"stats": "scores.hip", "reduce": "scores.hip", "pool": "scores.hip",
                   "gram": "gram.hip", "gram_fin": "gram.hip", "thresh": "select.hip", "select_compact": "select.hip",
                   "compact": "select.hip", "fused": "fused.hip", "fused_slots": "fused.hip", "scores": "fused.hip",
+                  "pool_pairs": "scores.hip",
                   "evict": "select.hip", "select": "select.hip", "gather": "select.hip",
                   "cut_energy": "cut.hip", "cut_scan": "cut.hip", "cut_compact": "cut.hip"}
 

@@ -261,11 +261,17 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
       scored = true;
     }
   }
+  // short Gram-form caches: k_stats writes the key weights, then the pooling
+  // and the pair-block Gram units share one launch (same arithmetic, same
+  // bits as the separate kernels)
+  const bool pool_pairs = !scored && mode == KVSEL_R_GRAM && dt == KVSEL_BF16 && d == 128 &&
+                          p.mp == 32 && cap <= kGramPairCap && p.nchunk <= kFuseReduceChunks;
   if (!scored) {
     p.fuse_reduce = p.nchunk <= kFuseReduceChunks;
+    p.w_in_stats = pool_pairs ? 1 : 0;
     KV_TRY(launch_stats(dt, d, sm, p, stream, tr));
     if (!p.fuse_reduce) KV_TRY(launch_reduce(d, sm, p, stream, tr));
-    KV_TRY(launch_pool(dt, d, sm, p, stream, tr));
+    if (!pool_pairs) KV_TRY(launch_pool(dt, d, sm, p, stream, tr));
   }
   if (mode == KVSEL_R_GRAM) {
     GramParams gp{};
@@ -284,7 +290,13 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
     gp.rs = ws.grs;
     gp.part = ws.gpart;
     gp.nsmax = ws.nsmax;
-    KV_TRY(launch_gram(dt, d, gp, stream, tr));
+    if (pool_pairs) {
+      const GramParams gc = gram_config(dt, d, gp);
+      KV_TRY(launch_pool_pairs(p, gc, stream, tr));
+      KV_TRY(launch_gram_fin(gc, stream, tr));
+    } else {
+      KV_TRY(launch_gram(dt, d, gp, stream, tr));
+    }
   }
   return KVSEL_OK;
 }

@@ -29,19 +29,10 @@
 // matrix-core instructions) and two accumulator sets (a tile's fp32 epilogue
 // runs between the matrix-core instructions of the next tile).
 #include "common.hpp"
+#include "gram_pairs.hpp"
 #include "kernels.hpp"
 
 namespace kvsel {
-
-// Map the linear work-group index to (head, row block) so that consecutive
-// indices on one XCD (work-groups are dealt to the 8 XCDs round-robin) take
-// row blocks of the same head: the CUs of an XCD then sweep the same keys
-// through their shared L2.
-__device__ __forceinline__ int xcd_major(int L, int total) {
-  constexpr int kXcd = 8;
-  if (total % kXcd != 0) return L;
-  return (L % kXcd) * (total / kXcd) + L / kXcd;
-}
 
 // Blocks of columns (of 256 keys) that row block I computes; see above.
 __device__ __forceinline__ int gram_blocks(int I, int nb) {
@@ -614,129 +605,8 @@ __global__ __launch_bounds__(256, 1) void k_gram512(GramParams p) {
   }
 }
 
-// Small caches (cap <= kGramPairCap, bf16, d = 128): one work-group per pair
-// of 128-key blocks I <= J, so that even a short cache spreads over many CUs
-// (the sweep kernels give a 2K-token cache only nine work-groups per head).
-// Fragments come straight from global memory (L2-resident at this size).
-// Each wave takes 32 rows of block I and all 128 columns of block J on
-// 16x16x32 tiles.  The tile's w-weighted row sums go to slot J of block I's
-// keys; its w-weighted column sums (I < J) to slot I of block J's keys; so
-// every key ends with one slot per block of the cache, and k_gram_fin adds
-// them in slot order (deterministic) and removes the self term.  The grid is
-// one-dimensional, (pair, head) units in XCD-major order: the pairs of one
-// head run on one XCD and share its keys through that XCD's L2.
-__global__ __launch_bounds__(256) void k_gram_pairs(GramParams p) {
-  constexpr int RB = 256;  // bytes per key (128 bf16)
-  constexpr int BS = 128;  // keys per block
-  const int nbh = (p.cap + BS - 1) / BS, npairs = nbh * (nbh + 1) / 2;
-  const int unit = xcd_major(blockIdx.x, npairs * p.hkv * p.b);
-  const int hb = unit / npairs, h = hb % p.hkv, bi = hb / p.hkv, tid = threadIdx.x;
-  const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // pair index -> (I, J): block I owns the pairs J = I .. nbh-1
-  int I = 0, rem = unit - hb * npairs;
-  while (rem >= nbh - I) {
-    rem -= nbh - I;
-    ++I;
-  }
-  const int J = I + rem;
-  const int n = clamp_len(p.lengths[bi], p.cap);
-  if (J * BS >= n) return;
-  const long head = (long)bi * p.hkv + h;
-  const char* kb = p.k + head * (long)p.cap * RB;
-  const float* wv = p.inv_norm + head * (long)p.wstride;
-  float* part = p.part + head * (long)p.nsmax * p.cap;
-
-  // A: rows I*BS + 32 wave + 16 rt + c16; lane chunk g of each 32-dim k-step
-  u32x4_t af[2][4];
-  float wrow[2][4];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = I * BS + 32 * wave + 16 * rt + c16;
-    const char* src = kb + (long)(row < n ? row : 0) * RB + g * 16;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) af[rt][ks] = row < n ? ld16(src + 64 * ks) : zero4();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = I * BS + 32 * wave + 16 * rt + 4 * g + i;
-      wrow[rt][i] = r < n ? wv[r] : 0.f;
-    }
-  }
-  // block J, copied once into LDS (columns past n read as zeros): chunk q of
-  // column c at slot 16 c + (q xor (c mod 16)), so the 16 lanes reading one
-  // chunk of 16 consecutive columns hit distinct banks
-  __shared__ u32x4_t bs[BS * 16];
-  {
-    const auto rk = buf_rsrc(kb + (long)J * BS * RB, (uint32_t)min(n - J * BS, BS) * RB);
-#pragma unroll
-    for (int u = 0; u < BS * 16 / 256; ++u) {
-      const int sl = 256 * u + tid, c = sl / 16, q = (sl % 16) ^ (c % 16);
-      buf_lds16(rk, bs + 256 * u + (tid & ~63), (uint32_t)c * RB + 16 * q);
-    }
-    // this thread's copies have landed (the compiler waits for exactly
-    // these), then every wave's
-    uint32_t x = 0;
-#pragma unroll
-    for (int u = 0; u < BS * 16 / 256; ++u) x |= reinterpret_cast<const uint32_t*>(bs + 256 * u + tid)[0];
-    asm volatile("" ::"v"(x));
-    __syncthreads();
-  }
-  // C[row][col] over the 8 column tiles of block J; lane holds rows 4g + i
-  // of each row tile at column c16 of each column tile
-  f32x4_t acc[2][8];
-  float wcol[8];
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    const int cl = 16 * ct + c16, col = J * BS + cl;
-    wcol[ct] = col < n ? wv[col] : 0.f;
-    u32x4_t bf[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) bf[ks] = bs[cl * 16 + ((4 * ks + g) ^ c16)];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[rt][ks]),
-                                                    __builtin_bit_cast(bf16x8_t, bf[ks]), c, 0, 0, 0);
-      acc[rt][ct] = c;
-    }
-  }
-  // row sums (weights of the columns), summed over the 16 lanes of a row
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) v = fmaf(acc[rt][ct][i], wcol[ct], v);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
-      const int r = I * BS + 32 * wave + 16 * rt + 4 * g + i;
-      if (c16 == 0 && r < n) part[(long)J * p.cap + r] = v;
-    }
-  if (I == J) return;
-  // column sums (weights of the rows): over the lane's 8 rows, the 4 lane
-  // groups, then the 4 waves in order
-  __shared__ float colred[4][BS];
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    float v = 0.f;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v = fmaf(acc[rt][ct][i], wrow[rt][i], v);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    if (g == 0) colred[wave][16 * ct + c16] = v;
-  }
-  __syncthreads();
-  if (tid < BS) {
-    const int col = J * BS + tid;
-    const float v = (colred[0][tid] + colred[1][tid]) + (colred[2][tid] + colred[3][tid]);
-    if (col < n) part[(long)I * p.cap + col] = v;
-  }
-}
+// Small caches: one work-group per pair of 128-key blocks (gram_pairs_unit).
+__global__ __launch_bounds__(256) void k_gram_pairs(GramParams p) { gram_pairs_unit(p, blockIdx.x); }
 
 // R and Z per key: own row sums plus the column sums of the blocks that
 // computed this key's block as their column block, in slot order.  A thread
@@ -857,24 +727,35 @@ static hipError_t gram_t(const GramParams& p, hipStream_t s, Trace* tr) {
 // bf16 keys of 128 dimensions use 512-key blocks once there are at least 16
 // of them per head at full length (enough work-groups to fill the chip at the
 // shapes this path serves); everything else uses 256-key blocks.
-hipError_t launch_gram(int dt, int d, const GramParams& p_in, hipStream_t s, Trace* tr) {
+GramParams gram_config(int dt, int d, const GramParams& p_in) {
   GramParams p = p_in;
   const bool big = dt == 0 && d == 128 && p.cap >= 8192;
   const bool small = dt == 0 && d == 128 && p.cap <= kGramPairCap;
   p.bs = big ? 512 : (small ? 128 : 256);
   p.pairs = small ? 1 : 0;
+  return p;
+}
+
+long gram_pair_units(const GramParams& p) {
+  const long nbh = (p.cap + 127) / 128;
+  return nbh * (nbh + 1) / 2 * p.hkv * p.b;
+}
+
+hipError_t launch_gram(int dt, int d, const GramParams& p_in, hipStream_t s, Trace* tr) {
+  const GramParams p = gram_config(dt, d, p_in);
   // one-dimensional grids: every work-group index must fit an int
   const long nbk = (p.cap + p.bs - 1) / p.bs;
-  if ((small ? nbk * (nbk + 1) / 2 : nbk) * p.hkv * p.b >= (1L << 31)) return hipErrorInvalidValue;
+  if ((p.pairs ? gram_pair_units(p) : nbk * p.hkv * p.b) >= (1L << 31)) return hipErrorInvalidValue;
   hipError_t e;
-  if (big) e = launch_k(k_gram512, dim3((p.cap + 511) / 512 * p.hkv * p.b), dim3(256), s, tr, p);
-  else if (small) {
-    const int nbh = (p.cap + 127) / 128;
-    e = launch_k(k_gram_pairs, dim3(nbh * (nbh + 1) / 2 * p.hkv * p.b), dim3(256), s, tr, p);
-  }
+  if (p.bs == 512) e = launch_k(k_gram512, dim3((p.cap + 511) / 512 * p.hkv * p.b), dim3(256), s, tr, p);
+  else if (p.pairs) e = launch_k(k_gram_pairs, dim3(gram_pair_units(p)), dim3(256), s, tr, p);
   else if (dt == 0) e = d == 64 ? gram_t<BF16, 64>(p, s, tr) : gram_t<BF16, 128>(p, s, tr);
   else e = d == 64 ? gram_t<F32, 64>(p, s, tr) : gram_t<F32, 128>(p, s, tr);
   if (e != hipSuccess) return e;
+  return launch_gram_fin(p, s, tr);
+}
+
+hipError_t launch_gram_fin(const GramParams& p, hipStream_t s, Trace* tr) {
   auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
   if (p.cap % 4 == 0 && (long)p.nsmax * p.cap * 4 < (1L << 31) && al16(p.part) && al16(p.rs) &&
       al16(p.inv_norm) && al16(p.i_in) && al16(p.z_out) && al16(p.r_out))

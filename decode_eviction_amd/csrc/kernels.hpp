@@ -25,9 +25,8 @@ constexpr int kFuseReduceChunks = 16;
 // (with every sequence at full length the map is the identity).  Returns
 // false past the last chunk with keys.
 constexpr int kActiveFirstMaxB = 16;
-__device__ __forceinline__ bool active_chunk(const int32_t* lengths, int b, int hkv, int cap, int nchunk,
-                                             int& bi, int& h, int& chunk) {
-  int L = blockIdx.x + nchunk * (blockIdx.y + hkv * blockIdx.z);
+__device__ __forceinline__ bool active_chunk_at(int L, const int32_t* lengths, int b, int hkv, int cap,
+                                                int& bi, int& h, int& chunk) {
   int lens[kActiveFirstMaxB];
 #pragma unroll
   for (int i = 0; i < kActiveFirstMaxB; ++i) lens[i] = lengths[min(i, b - 1)];
@@ -44,6 +43,12 @@ __device__ __forceinline__ bool active_chunk(const int32_t* lengths, int b, int 
     L -= nch * hkv;
   }
   return false;
+}
+// The same for work-group (blockIdx.x, .y, .z) of a (chunk, head, sequence) grid.
+__device__ __forceinline__ bool active_chunk(const int32_t* lengths, int b, int hkv, int cap, int nchunk,
+                                             int& bi, int& h, int& chunk) {
+  return active_chunk_at(blockIdx.x + nchunk * (blockIdx.y + hkv * blockIdx.z), lengths, b, hkv, cap, bi,
+                         h, chunk);
 }
 constexpr int kMaxRows = 128;      // g*w (R-KV) or g (cut) rows, in 32-row tiles
 constexpr int kSelectThreads = 1024;
@@ -113,6 +118,9 @@ struct ScoreParams {
   // R-KV modes with nchunk <= kFuseReduceChunks: k_pool merges the chunk
   // partials itself (in k_reduce's order) and k_reduce is not launched
   int fuse_reduce;
+  // Gram form: k_stats writes the key weights 1/||k_j|| (and k_pool does
+  // not), so that the Gram units can run beside the pooling
+  int w_in_stats;
   // outputs (never null; the host substitutes workspace buffers)
   float* i_out;             // [b][Hkv][cap]
   float* r_out;             // [b][Hkv][cap] (may be null in keysum mode)
@@ -343,6 +351,16 @@ hipError_t launch_stats(int dt, int d, int mode, const ScoreParams& p, hipStream
 hipError_t launch_reduce(int d, int mode, const ScoreParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_pool(int dt, int d, int mode, const ScoreParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_gram(int dt, int d, const GramParams& p, hipStream_t s, Trace* tr);
+// The Gram parameters of the kernel launch_gram picks (block size, pair form).
+GramParams gram_config(int dt, int d, const GramParams& p);
+// Work-groups of the pair-block Gram kernel (one per pair of 128-key blocks).
+long gram_pair_units(const GramParams& p);
+// k_gram_fin alone (after the pair units ran inside k_pool_pairs).
+hipError_t launch_gram_fin(const GramParams& p, hipStream_t s, Trace* tr);
+// Short Gram-form caches (bf16, d = 128, at most 32 window rows per KV head,
+// cap <= kGramPairCap): the importance pooling and the pair-block Gram units
+// in one launch, after k_stats wrote the key weights (p.w_in_stats).
+hipError_t launch_pool_pairs(const ScoreParams& p, const GramParams& g, hipStream_t s, Trace* tr);
 hipError_t launch_select(const SelectParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_hist(const SelectParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_select_err_zero(const SelectParams& p, hipStream_t s, Trace* tr);

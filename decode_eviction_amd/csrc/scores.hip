@@ -23,6 +23,7 @@
 // and reduces over tokens in registers; k_pool forms C[row][token] so a lane
 // owns one token and reduces over rows in registers (plus one lane swap).
 #include "common.hpp"
+#include "gram_pairs.hpp"
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -87,7 +88,19 @@ void k_stats(ScoreParams p) {
   }
 
   // key-sum mode: key norms and the chunk's unit-key sum (the Gram form's
-  // norms are taken in k_pool, which reads K from the last-level cache)
+  // norms are taken in k_pool, which reads K from the last-level cache,
+  // unless the Gram units run beside the pooling: then here, with the same
+  // arithmetic)
+  if constexpr (MODE == kModeGram) {
+    if (p.w_in_stats) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float ss = frag_sumsq<E, NC>(kf[tt]);
+        ss += xor32(ss);
+        if (hf == 0) p.inv_norm[head * (long)p.wstride + tok0 + 32 * tt + l32] = inv_norm_of(ss);
+      }
+    }
+  }
   auto norms = [&]() {
     if constexpr (MODE == kModeKeysum) {
       float inv[2];
@@ -336,263 +349,42 @@ void k_pool(ScoreParams p) {
   int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
   if (p.b > 1 && p.b <= kActiveFirstMaxB && !active_chunk(p.lengths, p.b, p.hkv, p.cap, p.nchunk, bi, h, chunk))
     return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
-  const int n = clamp_len(p.lengths[bi], p.cap);
-  const int c0 = chunk * kChunk;
-  if (c0 >= n) return;
-  const long head = (long)bi * p.hkv + h;
-  const char* kb = p.k + head * (long)p.cap * G::kRowBytes;
-  const char* qb = p.q + (((long)bi * p.hq + (long)h * p.g) * p.w + p.rows0) * G::kRowBytes;
+#include "pool_body.inc"
+}
 
-  __shared__ float2 rs[MT * 32];
-  __shared__ uint32_t lh[MODE == kModeKeysum ? kHistBins : 1];
-  // key-sum form: the head's sum of unit keys, read from LDS 16 bytes at a
-  // time (kept out of registers so that more work-groups fit on a CU)
-  __shared__ __attribute__((aligned(16))) float ssh[MODE == kModeKeysum ? D : 4];
-  if constexpr (MODE == kModeKeysum) {
-    if (p.hist)
-      for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
-  }
-  if (tid < MT * 32) {
-    float2 v;
-    if (MODE != kModeCut && p.fuse_reduce) {
-      // few chunks: the row's chunk partials merged here, in the order
-      // k_reduce uses (group g of its 32/MT groups takes chunks g, g + 32/MT,
-      // ...; the groups are merged in turn), so the result is the same
-      constexpr int G = 32 / MT, F = kFuseReduceChunks;
-      const int nch = (n + kChunk - 1) / kChunk;
-      const float2* cs = p.cstat + head * p.nchunk * p.mp + tid;
-      float2 c[F];
-#pragma unroll
-      for (int u = 0; u < F; ++u) c[u] = cs[(long)min(u, nch - 1) * p.mp];
-      float m = -INFINITY, s = 0.f;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float mg = -INFINITY, sg = 0.f;
-#pragma unroll
-        for (int ci = g; ci < F; ci += G)
-          if (ci < nch) softmax_merge(mg, sg, c[ci].x, c[ci].y);
-        softmax_merge(m, s, mg, sg);
-      }
-      v = make_float2(m, s > 0.f ? 1.0f / s : 0.f);
-    } else {
-      v = p.rstat[head * p.mp + tid];
-    }
-    rs[tid] = tid < p.m ? v : make_float2(0.f, 0.f);  // padding rows contribute 0
-  }
-  using QSt = QStage<E, D, MT>;
-  __shared__ u32x4_t qs[QSt::kWords];
-  Frag<NC> qf[QSt::kLds ? 1 : MT];
-  if constexpr (QSt::kLds) {
-    QSt::issue(qs, qb, p.m, tid);
-  } else {
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int r = 32 * t + l32;
-      load_frag<E, D>(qf[t], qb, r, r < p.m, hf);
-    }
-  }
-  const int tok0 = c0 + wave * 64;
-  Frag<NC> kf[2];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int tok = tok0 + 32 * tt + l32;
-    load_frag<E, D>(kf[tt], kb, tok, tok < n, hf);
-  }
-  if constexpr (MODE == kModeKeysum) {
-    if (tid < D) {
-      if (p.fuse_reduce) {
-        // the head's unit-key sum from the chunk sums, in k_reduce's order
-        // (group g of 1024/D takes chunks g, g + 1024/D, ...)
-        constexpr int GD = 1024 / D, F = kFuseReduceChunks;
-        const int nch = (n + kChunk - 1) / kChunk;
-        const float* sp = p.spart + head * p.nchunk * D + tid;
-        float c[F];
-#pragma unroll
-        for (int u = 0; u < F; ++u) c[u] = sp[(long)min(u, nch - 1) * D];
-        float a = 0.f;
-#pragma unroll
-        for (int g = 0; g < GD; ++g) {
-          float ag = 0.f;
-#pragma unroll
-          for (int ci = g; ci < F; ci += GD) ag += ci < nch ? c[ci] : 0.f;
-          a += ag;
-        }
-        ssh[tid] = a;
-      } else {
-        ssh[tid] = p.ssum[head * D + tid];
-      }
-    }
-  }
-  if constexpr (QSt::kLds) QSt::landed(qs, tid);
-  __syncthreads();
-  // k_j . S and |k_j|^2 for the wave's two key tiles (lane: token l32 of
-  // each tile), taken before the attention products so that the unpacked
-  // key values are not live across them
-  float dots[2] = {0.f, 0.f}, sqs[2] = {0.f, 0.f};
-  if constexpr (MODE == kModeGram) {
-    // 1/||k_j|| for the Gram kernel; every slot of the chunk is written (0
-    // past n), as it streams whole 128-key blocks of weights
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      float ss = frag_sumsq<E, NC>(kf[tt]);
-      ss += xor32(ss);
-      if (hf == 0) p.inv_norm[head * (long)p.wstride + tok0 + 32 * tt + l32] = inv_norm_of(ss);
-    }
-  }
-  if constexpr (MODE == kModeKeysum) {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) sqs[tt] = frag_sumsq<E, NC>(kf[tt]);
-#pragma unroll
-    for (int j = 0; j < NC; ++j)
-#pragma unroll
-      for (int q = 0; q < PC / 4; ++q) {
-        const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(&ssh[frag_dim<E>(j, 4 * q, hf)]);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dots[tt] = fmaf(frag_elem<E>(kf[tt].c[j], 4 * q + e), s4[e], dots[tt]);
-        // at most four LDS reads in flight (the compiler would otherwise issue
-        // all of them first and hold them in registers)
-        if ((j * (PC / 4) + q) % 4 == 3) asm volatile("" : "+v"(dots[0]), "+v"(dots[1])::"memory");
-      }
-  }
+// Short Gram-form caches: the pooling units (importance; the key weights
+// came from k_stats) and the pair-block Gram units in one grid.  Both read
+// only what k_stats wrote, so they are independent: the pooling work-groups
+// come first (their count rounded up to a multiple of 8, so that the Gram
+// units keep their XCD-major order) and fill CUs the pair units leave idle
+// in their second round.
+struct PoolPairsParams {
+  ScoreParams s;
+  GramParams g;
+  int npool;  // pooling work-groups, a multiple of 8
+};
 
-  const float sc2 = p.scale2;
-  if constexpr (MODE == kModeCut) {
-    // ReFreeKV energies of this row group from recomputed logits (the same
-    // scaled logit k_stats would store, then a = 2^(t - max) / sum), added to
-    // the earlier groups' and totalled per chunk.  Row r of a q head sees
-    // keys j <= n - krows + r.
-    const bool causal = p.krows > 1;
-    const bool full = tok0 + 63 <= (causal ? n - p.krows : n - 1);
-    __shared__ uint64_t wsum[4];
-    // per row: (c, last key the row sees) with
-    //   a^2 * 2^20 = 2^(2 (t - max) + 2 log2(1/sum) + 20) = 2^(acc * 2 sc2 + c),
-    //   c = 20 + 2 log2(1/sum) - 2 max,
-    // the input of energy_fixed (t = acc * sc2 the base-2 logit); c = -inf
-    // for rows past m and rows that see no key (1/sum = 0)
-    __shared__ float2 rsl[MT * 32];
-    if (tid < MT * 32) {
-      const float2 v = tid < p.m ? p.rstat[head * p.mp + tid] : make_float2(0.f, 0.f);
-      const int lim = causal ? n - p.krows + (p.rows0 + tid) % p.krows : n - 1;
-      const float c = v.y > 0.f ? 20.0f + 2.0f * __log2f(v.y) - 2.0f * v.x : -INFINITY;
-      rsl[tid] = make_float2(c, __int_as_float(lim));
-    }
-    const float sc4 = 2.0f * sc2;
-    __syncthreads();
-    // row tiles one at a time (the accumulators of two token tiles live),
-    // each token's terms summed over the rows in e[tt]
-    // per token tile: the energy as low and high 32-bit words
-    uint32_t elo[2] = {0u, 0u}, ehi[2] = {0u, 0u};
-    const int tokA = tok0 + l32, tokB = tokA + 32;
-#pragma unroll 1
-    for (int t = 0; t < MT; ++t) {
-      f32x16_t acc[2] = {zero16(), zero16()};
-      if constexpr (QSt::kLds) {
-#pragma unroll
-        for (int j = 0; j < NC; ++j) {
-          const u32x4_t qc = QSt::chunk(qs, t, l32, hf, j);
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) acc[tt] = mfma_chunk<E>(qc, kf[tt].c[j], acc[tt]);
-        }
-      } else {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) acc[tt] = mfma_tile<E, NC>(qf[t], kf[tt], acc[tt]);
-      }
-      // row 32t + tile_row(i, hf) for both token tiles (a logit that rounds
-      // an ulp above the row's max gives x just above 2^20: hi still fits)
-      auto rows16 = [&](auto masked) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float2 st = rsl[32 * t + tile_row(i, hf)];
-          float x0 = exp2_fast(fmaf(acc[0][i], sc4, st.x));
-          float x1 = exp2_fast(fmaf(acc[1][i], sc4, st.x));
-          if constexpr (decltype(masked)::value) {
-            const int lim = __float_as_int(st.y);
-            x0 = tokA <= lim ? x0 : 0.f;
-            x1 = tokB <= lim ? x1 : 0.f;
-          }
-          energy_add(elo[0], ehi[0], x0);
-          energy_add(elo[1], ehi[1], x1);
-          // at most four rows' records in flight
-          if (i % 4 == 3) asm volatile("" : "+v"(elo[0]), "+v"(elo[1])::"memory");
-        }
-      };
-      if (full) rows16(std::false_type{});
-      else rows16(std::true_type{});
-    }
-    uint64_t wtot = 0;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int tok = tok0 + 32 * tt + l32;
-      const uint64_t e = ((uint64_t)ehi[tt] << 32) | elo[tt];
-      uint64_t et = e + __shfl_xor(e, 32, 64);
-      uint64_t* ep = p.energy + head * (long)p.nchunk * kChunk + tok;
-      if (hf == 0) {
-        if (tok >= n) et = 0;
-        if (p.accum) et += *ep;
-        *ep = et;
-        wtot += et;
-      }
-    }
-    wtot = wave_sum_u64(wtot);
-    if (lane == 0) wsum[wave] = wtot;
-    __syncthreads();
-    if (tid == 0) p.ctot[head * p.nchunk + chunk] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+__global__ __launch_bounds__(256) void k_pool_pairs(PoolPairsParams pp) {
+  const int bx = blockIdx.x;
+  if (bx >= pp.npool) {
+    gram_pairs_unit(pp.g, bx - pp.npool);
     return;
   }
-  const float inv_m = 1.0f / (float)p.m;
-  const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    float isum = 0.f;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      // C[row][token]: lane owns token l32, rows 32t + tile_row(i, hf)
-      f32x16_t a = zero16();
-      if constexpr (QSt::kLds) {
-#pragma unroll
-        for (int j = 0; j < NC; ++j) a = mfma_chunk<E>(QSt::chunk(qs, t, l32, hf, j), kf[tt].c[j], a);
-      } else {
-        a = mfma_tile<E, NC>(qf[t], kf[tt], a);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float2 st = rs[32 * t + tile_row(i, hf)];
-        isum = fmaf(exp2_fast(fmaf(a[i], sc2, -st.x)), st.y, isum);
-      }
-    }
-    isum += xor32(isum);
-    const float imp = isum * inv_m;
-    const int tok = tok0 + 32 * tt + l32;
-    const long o = head * p.cap + tok;
-    if constexpr (MODE == kModeGram) {
-      if (hf == 0 && tok < n) p.i_out[o] = imp;
-    } else {
-      float ss = sqs[tt];
-      ss += xor32(ss);
-      const float inv = inv_norm_of(ss);
-      float dot = dots[tt];
-      dot += xor32(dot);
-      const float red = fmaf(inv, dot, -(inv * inv) * ss) * inv_nm1;
-      const float z = fmaf(p.lambda, imp, -(1.0f - p.lambda) * red);
-      if (hf == 0 && tok < n) {
-        p.i_out[o] = imp;
-        if (p.r_out) p.r_out[o] = red;
-        p.z_out[o] = z;
-        if (p.hist) atomicAdd(&lh[hist_bin(score_key(z))], 1u);
-      }
-    }
-  }
-  if constexpr (MODE == kModeKeysum) {
-    if (p.hist) {
-      __syncthreads();
-      for (int t = tid; t < kHistBins; t += 256)
-        if (lh[t]) atomicAdd(&p.hist[head * kHistStride + t], lh[t]);
-    }
-  }
+  using E = BF16;
+  constexpr int D = 128, MT = 1, MODE = kModeGram;
+  using G = Geo<E, D>;
+  constexpr int NC = G::kNC;
+  constexpr int LE = G::kLaneElems;
+  constexpr int PC = E::kPerChunk;
+  const ScoreParams& p = pp.s;
+  if (bx >= p.nchunk * p.hkv * p.b) return;
+  const int hb = bx / p.nchunk;
+  int chunk = bx - hb * p.nchunk, h = hb % p.hkv, bi = hb / p.hkv;
+  if (p.b > 1 && p.b <= kActiveFirstMaxB && !active_chunk_at(bx, p.lengths, p.b, p.hkv, p.cap, bi, h, chunk))
+    return;
+#include "pool_body.inc"
 }
+
 
 // ---------------------------------------------------------------- launchers
 
@@ -647,6 +439,14 @@ static hipError_t pool_d(int mode, const ScoreParams& p, hipStream_t s, Trace* t
     case 4: return pool_t<E, D, 4>(mode, p, s, tr);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_pool_pairs(const ScoreParams& p, const GramParams& g, hipStream_t s, Trace* tr) {
+  const long npool = ((long)p.nchunk * p.hkv * p.b + 7) / 8 * 8;
+  const long total = npool + gram_pair_units(g);
+  if (total >= (1L << 31)) return hipErrorInvalidValue;
+  const PoolPairsParams pp{p, g, (int)npool};
+  return launch_k(k_pool_pairs, dim3((unsigned)total), dim3(256), s, tr, pp);
 }
 
 hipError_t launch_pool(int dt, int d, int mode, const ScoreParams& p, hipStream_t s, Trace* tr) {

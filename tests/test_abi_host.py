@@ -194,7 +194,8 @@ def test_bench_kernel_names_follow_the_reduce_folding():
     fuse = int(re.search(r"constexpr int kFuseReduceChunks = (\d+);", src).group(1))
     chunk = int(re.search(r"constexpr int kChunk = (\d+);", src).group(1))
     fmax = int(re.search(r"constexpr int kFusedMaxChunks = (\d+);", src).group(1))
-    assert fmax == bench.FUSED_MAX_CHUNKS
+    pair_cap = int(re.search(r"constexpr int kGramPairCap = (\d+);", src).group(1))
+    assert fmax == bench.FUSED_MAX_CHUNKS and pair_cap == bench.GRAM_PAIR_CAP
     for mode in ("gram", "keysum"):
         for cap in (1, 2176, fuse * chunk, fuse * chunk + 1, 32768):
             names = bench.rkv_kernels(mode, cap)
@@ -211,8 +212,10 @@ def test_bench_kernel_names_follow_the_reduce_folding():
                 continue
             folded = -(-cap // chunk) <= fuse
             assert ("reduce" not in names) == folded, (mode, cap)
-            assert [k for k in bench.KERNELS[mode] if k not in ("reduce", "thresh", "compact")] == \
-                [k for k in names if k != "reduce"]
+            want = [k for k in bench.KERNELS[mode] if k not in ("reduce", "thresh", "compact")]
+            if mode == "gram" and cap <= pair_cap:   # pooling and pair units in one launch
+                want = ["stats", "pool_pairs", "gram_fin"]
+            assert want == [k for k in names if k != "reduce"], (mode, cap)
     # 64 sequences of 2176 tokens: 9 * 8 * 64 work-groups do not fit at once
     assert bench.rkv_kernels("keysum", 2176, b=64) != ["fused"]
     # the n = 32768 layer: 128 * 8 work-groups of the score pass fit at four per
@@ -220,12 +223,12 @@ def test_bench_kernel_names_follow_the_reduce_folding():
     assert bench.rkv_kernels("keysum", 32768)[0] == "scores"
     assert bench.rkv_kernels("keysum", 8192, b=64)[0] == "stats"
     # the Gram form's score pass on the same caches
-    assert bench.rkv_kernels("gram", 2176) == ["stats", "pool", "gram", "gram_fin", "select_compact"]
+    assert bench.rkv_kernels("gram", 2176) == ["stats", "pool_pairs", "gram_fin", "select_compact"]
     assert bench.rkv_kernels("gram", 32768)[:3] == ["scores", "gram", "gram_fin"]
     assert bench.rkv_kernels("gram", 8192, b=64)[0] == "stats"
     # slot reuse: the fused step's slot form where the fused step applies,
     # otherwise the scores as a compacting call computes them
-    assert bench.slot_kernels("gram", 2176) == ["stats", "pool", "gram", "gram_fin", "thresh", "evict"]
+    assert bench.slot_kernels("gram", 2176) == ["stats", "pool_pairs", "gram_fin", "thresh", "evict"]
     assert bench.slot_kernels("keysum", 2176) == ["fused_slots"]
     assert bench.slot_kernels("keysum", 2176, b=64) == ["stats", "pool", "thresh", "evict"]
     assert bench.slot_kernels("gram", 8192)[:2] == ["scores", "gram"]
