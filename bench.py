@@ -74,6 +74,16 @@ def fused_step(mode: str, cap: int, b: int = 1, hkv: int = HKV, m: int = HQ // H
             and nch * hkv * b <= FUSED_CAPACITY)
 
 
+def fused_gram_step(mode: str, cap: int, b: int = 1, hkv: int = HKV, m: int = HQ // HKV * W) -> bool:
+    """Short Gram-form caches (bf16, d = 128, at most 32 window rows per KV
+    head, the pair-block Gram units), slot reuse: after k_stats and the
+    pooling with the Gram units, one launch forms Z from the Gram slots,
+    selects and lists the evicted slots, when its grid fits at once."""
+    nch = -(-cap // 256)
+    return (mode == "gram" and m <= 32 and cap <= GRAM_PAIR_CAP and nch <= FUSED_MAX_CHUNKS
+            and nch * hkv * b <= FUSED_CAPACITY)
+
+
 SCORES_FUSED_CAPACITY = 1024  # work-groups of the one-launch score pass resident at once (four per CU)
 
 
@@ -129,6 +139,8 @@ def slot_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV) -> list:
     applies), the threshold, the evicted list."""
     if fused_step(mode, cap, b, hkv):
         return ["fused_slots"]
+    if fused_gram_step(mode, cap, b, hkv):
+        return ["stats", "pool_pairs", "fused_fin_slots"]
     ks = [k for k in unfused_kernels(mode, cap) if k not in ("thresh", "compact")]
     if scores_fused(mode, cap, b, hkv):
         ks = ["scores"] + [k for k in ks if k not in ("stats", "reduce", "pool")]
@@ -210,6 +222,10 @@ def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int =
         # Gram units in one launch; counted by its matrix-core work
         cost["pool_pairs"] = {"bytes": 2 * kb + 4 * tok + 4 * tok * -(-n // 128), "flops": alg,
                               "flops_executed": exe}
+        # the one-launch finish of short caches (slot reuse): the Gram slots,
+        # weights and importance read, Z and the evicted list written
+        cost["fused_fin_slots"] = {"bytes": 4 * tok * -(-n // 128) + 12 * tok
+                                   + 4 * b * hkv * max(n - budget, 0)}
         cost["gram_fin"] = {"bytes": 4 * tok * 5 + 4 * tok * ns // 2}
     return cost
 
@@ -632,7 +648,7 @@ def run_refreekv_rows(hip, n_layers, steps, k_rows=64):
 KERNEL_SOURCES = {"stats": "scores.hip", "reduce": "scores.hip", "pool": "scores.hip",
                   "gram": "gram.hip", "gram_fin": "gram.hip", "thresh": "select.hip", "select_compact": "select.hip",
                   "compact": "select.hip", "fused": "fused.hip", "fused_slots": "fused.hip", "scores": "fused.hip",
-                  "pool_pairs": "scores.hip",
+                  "pool_pairs": "scores.hip", "fused_fin_slots": "fused.hip",
                   "evict": "select.hip", "select": "select.hip", "gather": "select.hip",
                   "cut_energy": "cut.hip", "cut_scan": "cut.hip", "cut_compact": "cut.hip"}
 

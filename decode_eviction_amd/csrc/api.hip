@@ -153,10 +153,14 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap, kvsel_redund
   ScoreWs w{};
   w.err = c.take<int32_t>(64);
   if (gram) {
+    w.fepoch = c.take<uint64_t>(heads);
     if (nchunk > kFusedMaxChunks) {
-      w.fepoch = c.take<uint64_t>(heads);
       w.fpub_a = c.take<uint64_t>(heads * nchunk * kGramWordsA);
       w.fmerged = c.take<uint64_t>(heads * kGramWordsA);
+    } else {
+      // the short-cache step's Gram finish: barrier flags and score keys
+      w.fflags = c.take<uint64_t>(2 * heads * kFusedMaxChunks);
+      w.fpub_b = c.take<uint64_t>(heads * cap);
     }
   } else {
     w.fepoch = c.take<uint64_t>(heads);
@@ -215,7 +219,8 @@ kvsel_status check_score_args(kvsel_dtype dt, kvsel_redundancy mode, const void*
 kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, const void* k,
                         const int32_t* lengths, int b, int hq, int hkv, int d, int w, int cap,
                         float lambda, float* i_out, float* r_out, float* z_out,
-                        uint32_t* hist, const ScoreWs& ws, hipStream_t stream, Trace* tr) {
+                        uint32_t* hist, const ScoreWs& ws, hipStream_t stream, Trace* tr,
+                        bool gram_fin = true) {
   const int g = hq / hkv;
   ScoreParams p{};
   p.q = static_cast<const char*>(q);
@@ -293,7 +298,7 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
     if (pool_pairs) {
       const GramParams gc = gram_config(dt, d, gp);
       KV_TRY(launch_pool_pairs(p, gc, stream, tr));
-      KV_TRY(launch_gram_fin(gc, stream, tr));
+      if (gram_fin) KV_TRY(launch_gram_fin(gc, stream, tr));
     } else {
       KV_TRY(launch_gram(dt, d, gp, stream, tr));
     }
@@ -343,6 +348,14 @@ static bool fused_step_applies(kvsel_dtype dt, kvsel_redundancy mode, int hq, in
          (cap + kChunk - 1) / kChunk <= kFusedMaxChunks;
 }
 
+// The Gram form's finish inside the short-cache step applies (bf16, d = 128,
+// at most 32 window rows per KV head, the pair-block Gram units).
+static bool fused_gram_applies(kvsel_dtype dt, kvsel_redundancy mode, int hq, int hkv, int d,
+                               int w, int cap) {
+  return mode == KVSEL_R_GRAM && dt == KVSEL_BF16 && d == 128 && (hq / hkv) * w <= 32 &&
+         cap <= kGramPairCap && (cap + kChunk - 1) / kChunk <= kFusedMaxChunks;
+}
+
 // Its parameters shared by the compacting and the slot-reuse forms.
 static FusedParams fused_params(const void* q_window, const void* k, const int32_t* lengths, int b,
                                 int hq, int hkv, int d, int w, int cap, float lambda, int budget,
@@ -370,6 +383,16 @@ static FusedParams fused_params(const void* q_window, const void* k, const int32
   fp.pub_b = ws.fpub_b;
   fp.salt = next_salt();
   return fp;
+}
+
+// The Gram finish's inputs: the pooling's importance, the key weights and
+// the pair-block Gram slots in the workspace.
+static void fused_gram_inputs(FusedParams& fp, const ScoreWs& ws, int cap) {
+  fp.gpart = ws.gpart;
+  fp.nsmax = ws.nsmax;
+  fp.inv_norm = ws.inv_norm;
+  fp.wstride = gram_wstride(cap);
+  fp.i_in = ws.imp;
 }
 
 SelectParams select_params(const SelWs& w, const float* z, const int32_t* lengths, int b, int hkv,
@@ -746,6 +769,25 @@ static kvsel_status score_evict_slots_impl(kvsel_dtype dt, kvsel_redundancy mode
     fp.evict_stride = evict_stride;
     fp.n_evict = n_evict_out;
     if (!separate_kernels() && fused_fits(fp)) return hip_status(launch_fused(fp, stream, tr));
+  }
+  // short caches, Gram form: the score kernels up to the Gram units, then
+  // the finish, threshold and the evicted list in one launch (for the
+  // compaction the separate finish and the one-launch selection, whose
+  // gather is spread over more work-groups, measured faster)
+  if (fused_gram_applies(dt, mode, hq, hkv, d, w, cap) && !separate_kernels()) {
+    FusedParams fp = fused_params(q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, budget,
+                                  budgets, z, ws);
+    fused_gram_inputs(fp, ws, cap);
+    fp.pos = pos;
+    fp.evict = evict_out;
+    fp.evict_stride = evict_stride;
+    fp.n_evict = n_evict_out;
+    if (fused_fits(fp)) {
+      st = run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, nullptr,
+                      nullptr, z, nullptr, ws, stream, tr, false);
+      if (st != KVSEL_OK) return st;
+      return hip_status(launch_fused(fp, stream, tr));
+    }
   }
   st = run_scores(dt, mode, q_window, k, lengths, b, hq, hkv, d, w, cap, lambda, nullptr, nullptr,
                   z, ws.sel.hist, ws, stream, tr);

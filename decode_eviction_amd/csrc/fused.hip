@@ -331,8 +331,13 @@ __device__ __noinline__ uint2 nth_largest(const uint32_t (&v)[KPT], uint32_t pla
 // threshold, ties at the threshold kept by lower token position (the
 // caller's position map; equal positions: lower slot), and instead of the
 // compaction the evicted slots listed in slot order; V is not read.
-template <typename E, int D, bool SLOTS>
+// GRAM (with SLOTS): the Gram form's finish instead of phases 1 and 2: Z of
+// each token from the pooling's importance, the key weights and the
+// pair-block Gram slots (k_gram_fin's arithmetic, one token per thread),
+// then phase 3 and the evicted list; neither q, K nor V is read.
+template <typename E, int D, bool SLOTS, bool GRAM>
 __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
+  static_assert(SLOTS || !GRAM, "the Gram finish serves the slot-reuse form");
   using G = Geo<E, D>;
   constexpr int NC = G::kNC;
   constexpr int LE = G::kLaneElems;
@@ -383,10 +388,10 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   // then V, which only the copies at the end need
   using QSt = QStage<E, D, 1>;
   __shared__ u32x4_t qs[QSt::kWords];
-  QSt::issue(qs, qb, p.m, tid);
+  if constexpr (!GRAM) QSt::issue(qs, qb, p.m, tid);
   const int tok0 = c0 + wave * 64;
   Frag<NC> kf[2];
-  {
+  if constexpr (!GRAM) {
     const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kb + (long)c0 * RB, (uint32_t)min(n - c0, kChunk) * RB);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -409,79 +414,100 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
     }
   }
 
-  // ---- phase 1: chunk statistics and unit-key sums (k_stats' arithmetic)
-  const float sc2 = p.scale2;
-  __shared__ float2 wst[NW][32];
-  __shared__ float red[256 * PC];
-  QSt::landed(qs, tid);
-  __syncthreads();
-  float sqs[2];
-  uint64_t* rec = pa + chunk * kFusedWordsA;
-  chunk_partials<E, D, true>(
-      kf, qs, n, tok0, sc2, sqs, wst, red, tid,
-      [&](int r, float m, float s) {
-        st_dev(rec + 2 * r, tagged(tag, __float_as_uint(m)));
-        st_dev(rec + 2 * r + 1, tagged(tag, __float_as_uint(s)));
-      },
-      [&](int dim, float s) { st_dev(rec + 64 + dim, tagged(tag, __float_as_uint(s))); });
-  signal(p, 0, head, chunk, tag, tid);
-  wait_flags(p, 0, head, nwg, tag, tid);
-  if (chunk == 0 && tid == 0) st_dev(p.epoch + head, ep + 1);  // every work-group has read ep
-
-  // ---- phase 2: merged statistics, importance, redundancy, Z (k_pool's arithmetic)
-  __shared__ float2 rs[32];
-  __shared__ __attribute__((aligned(16))) float ssh[D];
-  if (tid < 32) {
-    uint64_t cw[2 * kFusedMaxChunks];
-#pragma unroll
-    for (int u = 0; u < kFusedMaxChunks; ++u) {
-      const uint64_t* at = pa + min(u, nwg - 1) * kFusedWordsA + 2 * tid;
-      cw[2 * u] = ld_dev(at);
-      cw[2 * u + 1] = ld_dev(at + 1);
-    }
-    float m = -INFINITY, s = 0.f;
-#pragma unroll
-    for (int u = 0; u < kFusedMaxChunks; ++u)
-      if (u < nwg) {
-        const uint64_t* at = pa + u * kFusedWordsA + 2 * tid;
-        const float cm = __uint_as_float(untag(p, at, cw[2 * u], tag));
-        const float cs = __uint_as_float(untag(p, at + 1, cw[2 * u + 1], tag));
-        softmax_merge(m, s, cm, cs);
-      }
-    const float2 v = make_float2(m, s > 0.f ? 1.0f / s : 0.f);
-    rs[tid] = tid < p.m ? v : make_float2(0.f, 0.f);
-  }
-  if (tid < D) {
-    // the order k_pool merges them in: group g of 1024 / D takes chunks g,
-    // g + 1024 / D, ...; the groups are added in turn
-    constexpr int GD = 1024 / D, F = kFusedMaxChunks;
-    uint64_t cw[F];
-#pragma unroll
-    for (int u = 0; u < F; ++u) cw[u] = ld_dev(pa + min(u, nwg - 1) * kFusedWordsA + 64 + tid);
-    float c[F];
-#pragma unroll
-    for (int u = 0; u < F; ++u)
-      c[u] = u < nwg ? __uint_as_float(untag(p, pa + u * kFusedWordsA + 64 + tid, cw[u], tag)) : 0.f;
-    float s = 0.f;
-#pragma unroll
-    for (int g = 0; g < GD; ++g) {
-      float ag = 0.f;
-#pragma unroll
-      for (int ci = g; ci < F; ci += GD) ag += ci < nwg ? c[ci] : 0.f;
-      s += ag;
-    }
-    ssh[tid] = s;
-  }
-  __syncthreads();
-  float imp[2], rd[2], z[2];
-  pool_tokens<E, D>(kf, qs, rs, ssh, sqs, n, p.m, sc2, p.lambda, tid, imp, rd, z);
   uint64_t* pb = p.pub_b + head * p.cap;
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int tok = tok0 + 32 * tt + l32;
-    if (hf == 0 && tok < n) {
-      p.z_out[head * p.cap + tok] = z[tt];
-      if (n > B && B > 0) st_dev(pb + tok, tagged(tag, score_key(z[tt])));
+  if constexpr (GRAM) {
+    // Z of token c0 + tid as k_gram_fin forms it: the key's Gram slots (one
+    // per 128-key block of the cache) added in slot order, less the self
+    // term 1 / w_j, times w_j / (n - 1), then lambda I - (1 - lambda) R
+    const int tz = c0 + tid;
+    if (tz < n) {
+      const int nt = (n + 127) / 128;
+      const float* sp = p.gpart + head * (long)p.nsmax * p.cap + tz;
+      const float w = p.inv_norm[head * (long)p.wstride + tz];
+      const float imp = p.i_in[head * p.cap + tz];
+      float tot = 0.f;
+      for (int sl = 0; sl < nt; ++sl) tot += sp[(long)sl * p.cap];
+      const float inv_nm1 = n > 1 ? 1.0f / (float)(n - 1) : 0.f;
+      const float t = tot - (w > 0.f ? 1.0f / w : 0.f);
+      const float red = w * t * inv_nm1;
+      const float z = fmaf(p.lambda, imp, -(1.0f - p.lambda) * red);
+      p.z_out[head * p.cap + tz] = z;
+      if (n > B && B > 0) st_dev(pb + tz, tagged(tag, score_key(z)));
+    }
+  } else {
+    // ---- phase 1: chunk statistics and unit-key sums (k_stats' arithmetic)
+    const float sc2 = p.scale2;
+    __shared__ float2 wst[NW][32];
+    __shared__ float red[256 * PC];
+    QSt::landed(qs, tid);
+    __syncthreads();
+    float sqs[2];
+    uint64_t* rec = pa + chunk * kFusedWordsA;
+    chunk_partials<E, D, true>(
+        kf, qs, n, tok0, sc2, sqs, wst, red, tid,
+        [&](int r, float m, float s) {
+          st_dev(rec + 2 * r, tagged(tag, __float_as_uint(m)));
+          st_dev(rec + 2 * r + 1, tagged(tag, __float_as_uint(s)));
+        },
+        [&](int dim, float s) { st_dev(rec + 64 + dim, tagged(tag, __float_as_uint(s))); });
+    signal(p, 0, head, chunk, tag, tid);
+    wait_flags(p, 0, head, nwg, tag, tid);
+    if (chunk == 0 && tid == 0) st_dev(p.epoch + head, ep + 1);  // every work-group has read ep
+
+    // ---- phase 2: merged statistics, importance, redundancy, Z (k_pool's arithmetic)
+    __shared__ float2 rs[32];
+    __shared__ __attribute__((aligned(16))) float ssh[D];
+    if (tid < 32) {
+      uint64_t cw[2 * kFusedMaxChunks];
+  #pragma unroll
+      for (int u = 0; u < kFusedMaxChunks; ++u) {
+        const uint64_t* at = pa + min(u, nwg - 1) * kFusedWordsA + 2 * tid;
+        cw[2 * u] = ld_dev(at);
+        cw[2 * u + 1] = ld_dev(at + 1);
+      }
+      float m = -INFINITY, s = 0.f;
+  #pragma unroll
+      for (int u = 0; u < kFusedMaxChunks; ++u)
+        if (u < nwg) {
+          const uint64_t* at = pa + u * kFusedWordsA + 2 * tid;
+          const float cm = __uint_as_float(untag(p, at, cw[2 * u], tag));
+          const float cs = __uint_as_float(untag(p, at + 1, cw[2 * u + 1], tag));
+          softmax_merge(m, s, cm, cs);
+        }
+      const float2 v = make_float2(m, s > 0.f ? 1.0f / s : 0.f);
+      rs[tid] = tid < p.m ? v : make_float2(0.f, 0.f);
+    }
+    if (tid < D) {
+      // the order k_pool merges them in: group g of 1024 / D takes chunks g,
+      // g + 1024 / D, ...; the groups are added in turn
+      constexpr int GD = 1024 / D, F = kFusedMaxChunks;
+      uint64_t cw[F];
+  #pragma unroll
+      for (int u = 0; u < F; ++u) cw[u] = ld_dev(pa + min(u, nwg - 1) * kFusedWordsA + 64 + tid);
+      float c[F];
+  #pragma unroll
+      for (int u = 0; u < F; ++u)
+        c[u] = u < nwg ? __uint_as_float(untag(p, pa + u * kFusedWordsA + 64 + tid, cw[u], tag)) : 0.f;
+      float s = 0.f;
+  #pragma unroll
+      for (int g = 0; g < GD; ++g) {
+        float ag = 0.f;
+  #pragma unroll
+        for (int ci = g; ci < F; ci += GD) ag += ci < nwg ? c[ci] : 0.f;
+        s += ag;
+      }
+      ssh[tid] = s;
+    }
+    __syncthreads();
+    float imp[2], rd[2], z[2];
+    pool_tokens<E, D>(kf, qs, rs, ssh, sqs, n, p.m, sc2, p.lambda, tid, imp, rd, z);
+  #pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tok = tok0 + 32 * tt + l32;
+      if (hf == 0 && tok < n) {
+        p.z_out[head * p.cap + tok] = z[tt];
+        if (n > B && B > 0) st_dev(pb + tok, tagged(tag, score_key(z[tt])));
+      }
     }
   }
 
@@ -521,6 +547,8 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
   }
   signal(p, 1, head, chunk, tag, tid);
   wait_flags(p, 1, head, nwg, tag, tid);
+  if constexpr (GRAM)  // no barrier A: every work-group has read ep by now
+    if (chunk == 0 && tid == 0) st_dev(p.epoch + head, ep + 1);
 
   // ---- phase 3: the head's keys in LDS, the threshold, slots of this chunk
   __shared__ uint32_t kall[kFusedKeys];
@@ -720,8 +748,12 @@ __global__ __launch_bounds__(256) void k_rkv_fused(FusedParams p) {
 
 hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr) {
   const dim3 grid((p.cap + kChunk - 1) / kChunk, p.hkv, p.b);
-  if (p.evict) return launch_k(k_rkv_fused<BF16, 128, true>, grid, dim3(256), s, tr, p);
-  return launch_k(k_rkv_fused<BF16, 128, false>, grid, dim3(256), s, tr, p);
+  if (p.gpart) {  // the Gram finish serves the slot-reuse form
+    if (!p.evict) return hipErrorInvalidValue;
+    return launch_k(k_rkv_fused<BF16, 128, true, true>, grid, dim3(256), s, tr, p);
+  }
+  if (p.evict) return launch_k(k_rkv_fused<BF16, 128, true, false>, grid, dim3(256), s, tr, p);
+  return launch_k(k_rkv_fused<BF16, 128, false, false>, grid, dim3(256), s, tr, p);
 }
 
 // ------------------------------------------------------------------------
@@ -983,12 +1015,13 @@ void k_scores_fused(ScoresFusedParams fp) {
   scores_fused_unit<E, D, MODE>(fp, v - hb * fp.s.nchunk, hb % fp.s.hkv, hb / fp.s.hkv);
 }
 
-static int g_fused_capacity[2][64];
+static int g_fused_capacity[3][64];
 
 bool fused_fits(const FusedParams& p) {
   const long total = (long)((p.cap + kChunk - 1) / kChunk) * p.hkv * p.b;
-  if (p.evict) return grid_fits(k_rkv_fused<BF16, 128, true>, g_fused_capacity[1], total);
-  return grid_fits(k_rkv_fused<BF16, 128, false>, g_fused_capacity[0], total);
+  if (p.gpart) return p.evict && grid_fits(k_rkv_fused<BF16, 128, true, true>, g_fused_capacity[2], total);
+  if (p.evict) return grid_fits(k_rkv_fused<BF16, 128, true, false>, g_fused_capacity[1], total);
+  return grid_fits(k_rkv_fused<BF16, 128, false, false>, g_fused_capacity[0], total);
 }
 
 static int g_scores_capacity[2][64];

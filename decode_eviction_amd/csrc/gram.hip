@@ -694,7 +694,7 @@ __global__ __launch_bounds__(256) void k_gram_fin(GramParams p) {
       // pairs: the self term w_j ||k_j||^2 = 1 / w_j (0 for a zero key)
       if (p.pairs) t -= w[e] > 0.f ? 1.0f / w[e] : 0.f;
       red[e] = w[e] * t * inv_nm1;
-      z[e] = p.lambda * imp[e] - (1.0f - p.lambda) * red[e];
+      z[e] = fmaf(p.lambda, imp[e], -(1.0f - p.lambda) * red[e]);
     }
     const long o = head * p.cap + j;
     if (j + V <= n) {

@@ -272,6 +272,13 @@ struct FusedParams {
   int32_t* evict;           // [b][Hkv][evict_stride]
   int evict_stride;
   int32_t* n_evict;         // [b][Hkv]
+  // Gram form (non-null gpart): Z from the pooling's importance, the key
+  // weights and the pair-block Gram slots instead of phases 1 and 2
+  const float* gpart;       // [b][Hkv][nsmax][cap]: slot s = sums against block s
+  int nsmax;
+  const float* inv_norm;    // [b][Hkv][wstride]
+  int wstride;
+  const float* i_in;        // [b][Hkv][cap]
   // workspace
   uint64_t* epoch;          // [b][Hkv]: advanced by one every call
   uint64_t* flags;          // [2][b][Hkv][kFusedMaxChunks]: barrier flag words

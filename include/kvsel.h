@@ -261,7 +261,9 @@ kvsel_status kvsel_select_evict_slots(const float* z, const int32_t* lengths, co
  * ceil(cap / 256) * Hkv * b work-groups fits on the device at once: one
  * kernel computes the scores, the threshold and the evicted list (the same
  * scores and the same list as the separate kernels, which run otherwise or
- * with KVSEL_SEPARATE_KERNELS=1). */
+ * with KVSEL_SEPARATE_KERNELS=1).  Gram form on such caches (cap <= 4096):
+ * after the score kernels up to the Gram units, one kernel forms Z, the
+ * threshold and the evicted list, under the same conditions. */
 kvsel_status kvsel_score_evict_slots(kvsel_dtype dt, kvsel_redundancy mode,
                                      const void* q_window, const void* k, const int32_t* lengths,
                                      const int32_t* pos, const int32_t* budgets,

@@ -224,11 +224,13 @@ def test_bench_kernel_names_follow_the_reduce_folding():
     assert bench.rkv_kernels("keysum", 8192, b=64)[0] == "stats"
     # the Gram form's score pass on the same caches
     assert bench.rkv_kernels("gram", 2176) == ["stats", "pool_pairs", "gram_fin", "select_compact"]
+    assert bench.rkv_kernels("gram", 2176, b=64) == ["stats", "pool_pairs", "gram_fin", "thresh", "compact"]
     assert bench.rkv_kernels("gram", 32768)[:3] == ["scores", "gram", "gram_fin"]
     assert bench.rkv_kernels("gram", 8192, b=64)[0] == "stats"
     # slot reuse: the fused step's slot form where the fused step applies,
     # otherwise the scores as a compacting call computes them
-    assert bench.slot_kernels("gram", 2176) == ["stats", "pool_pairs", "gram_fin", "thresh", "evict"]
+    assert bench.slot_kernels("gram", 2176) == ["stats", "pool_pairs", "fused_fin_slots"]
+    assert bench.slot_kernels("gram", 2176, b=64) == ["stats", "pool_pairs", "gram_fin", "thresh", "evict"]
     assert bench.slot_kernels("keysum", 2176) == ["fused_slots"]
     assert bench.slot_kernels("keysum", 2176, b=64) == ["stats", "pool", "thresh", "evict"]
     assert bench.slot_kernels("gram", 8192)[:2] == ["scores", "gram"]

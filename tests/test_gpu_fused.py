@@ -230,3 +230,69 @@ def test_fused_slots_budgets_and_edges():
                     for _ in range(3)]).astype(np.int32)
     flags = _slots_check(case, pos=pos, budgets=budgets)
     assert flags & 2                                   # 9000 > 1500 was clamped
+
+
+# ---- the Gram form's finish inside the one-launch step (short caches)
+
+def _gram_outputs(case, slots, pos=None, budgets=None):
+    q, k, v = dev(case.q, "bf16"), dev(case.k, "bf16"), dev(case.v, "bf16")
+    lens = dev_i32(case.lengths)
+    b, hkv, cap = case.b, case.hkv, case.cap
+    ws = torch.empty(K.kvsel_score_evict_workspace(b, case.hq, hkv, case.d, case.w, cap, case.budget),
+                     dtype=torch.uint8, device="cuda")
+    ws.fill_(0x5a)
+    z = torch.full((b, hkv, cap), float("nan"), device="cuda")
+    bud = None if budgets is None else dev_i32(budgets)
+    if slots:
+        ev, ne = K.kvsel_score_evict_slots(q, k, lens, case.budget, case.lam, "gram",
+                                           pos=None if pos is None else dev_i32(pos), budgets=bud,
+                                           scores_out=z, workspace=ws)
+        outs = [ev.cpu().numpy(), ne.cpu().numpy()]
+    elif budgets is None:
+        ko, vo, idx = K.kvsel_score_evict(q, k, v, lens, case.budget, case.lam, "gram", scores_out=z,
+                                          workspace=ws)
+        outs = [idx.cpu().numpy(), host_bits(ko), host_bits(vo)]
+    else:
+        ko, vo, idx = K.kvsel_score_evict_heads(q, k, v, lens, bud, case.budget, case.lam, "gram",
+                                                scores_out=z, workspace=ws)
+        outs = [idx.cpu().numpy(), host_bits(ko), host_bits(vo)]
+    flags = K.kvsel_workspace_error(ws)
+    assert flags & 12 == 0, f"flags {flags}"
+    zh = z.cpu().numpy()
+    lens_c = np.minimum(case.lengths, cap)
+    zs = [zh[bb, h, :int(lens_c[bb])] for bb in range(b) for h in range(hkv)]
+    return zs, outs
+
+
+@pytest.mark.parametrize("slots", [True, False])
+@pytest.mark.parametrize("kind", ["decode", "ties", "heads"])
+def test_fused_gram_finish_equals_separate_kernels(kind, slots, monkeypatch):
+    # slot reuse: Z formed from the Gram slots inside the one-launch step,
+    # then the threshold and the evicted list, bit for bit as the separate
+    # finish, threshold and evicted-list kernels give them; compaction (the
+    # separate finish and the one-launch selection either way): the same
+    # against the two-kernel selection
+    pos, budgets = None, None
+    if kind == "decode":
+        case = synth.layer8b_case(9, n=2176, budget=2048, cap=2176)
+    elif kind == "ties":
+        case = synth.rkv_case("gram_ties", seed=76, wl=68, b=2, hq=32, hkv=8, d=128, w=8,
+                              lengths=[2176, 1800], cap=2176, budget=1000, frac=0.0, sink_scale=None)
+        for bb in range(2):
+            for a, e in [(0, 700), (700, 1500), (1500, 2176)]:
+                case.k[bb, :, a:e] = case.k[bb, :, a:a + 1]
+        rng = np.random.default_rng(77)
+        pos = np.stack([np.stack([rng.permutation(2176) for _ in range(8)]) for _ in range(2)])
+        pos = (pos // 2).astype(np.int32)
+    else:
+        case = synth.rkv_case("gram_heads", seed=78, wl=69, b=3, hq=32, hkv=8, d=128, w=4,
+                              lengths=[4000, 257, 0], cap=4096, budget=1500)
+        budgets = np.array([0, 1, 300, 1500, 2047, 9000, 700, 256], np.int32)
+    log(f"[fused gram] {kind} slots={slots} lengths={case.lengths.tolist()} B={case.budget}")
+    z1, o1 = _gram_outputs(case, slots, pos, budgets)
+    monkeypatch.setenv("KVSEL_SEPARATE_KERNELS", "1")
+    z2, o2 = _gram_outputs(case, slots, pos, budgets)
+    for a, b_ in zip(z1, z2):
+        assert np.array_equal(a, b_)
+    for a, b_ in zip(o1, o2):
+        assert np.array_equal(a, b_)

@@ -334,10 +334,11 @@ def test_select_compact_split_gather(form):
 
 
 def test_select_compact_split_gather_ties():
-    # all keys equal: every score ties, the kept copies are the lowest positions
-    case = _tied(synth.rkv_case("decode_tied", seed=18, wl=synth.WL_LAYER8B, b=1, hq=32, hkv=8, d=128,
-                                w=8, lengths=[2176], cap=2176, budget=2048), 1)
+    # all keys equal: every score ties, the kept copies are the lowest
+    # positions
+    case = _tied(synth.rkv_case("decode_tied", seed=18, wl=synth.WL_LAYER8B, b=4, hq=32, hkv=8, d=128,
+                                w=8, lengths=[2176, 2176, 2000, 2176], cap=2176, budget=2048), 1)
     _check_select(case, "gram")
-    case = _tied(synth.rkv_case("decode_three", seed=19, wl=synth.WL_LAYER8B, b=1, hq=32, hkv=8, d=128,
-                                w=8, lengths=[2176], cap=2176, budget=2048), 3)
+    case = _tied(synth.rkv_case("decode_three", seed=19, wl=synth.WL_LAYER8B, b=4, hq=32, hkv=8, d=128,
+                                w=8, lengths=[2176, 1900, 2176, 2176], cap=2176, budget=2048), 3)
     _check_select(case, "gram")
