@@ -14,9 +14,13 @@ from tests.gpu_util import dev, dev_i32, log
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("n", [2176, 32768])
 @pytest.mark.parametrize("mode", ["keysum", "gram"])
-def test_score_evict_graph_replays(mode):
-    case = synth.layer8b_case(2, n=2176, budget=2048, cap=2176)
+def test_score_evict_graph_replays(mode, n):
+    # n = 2176: the one-launch short-cache step (key-sum) and the pooling
+    # with the pair-block Gram units (Gram); n = 32768: the one-launch score
+    # pass and the one-launch selection, whose tags change every replay
+    case = synth.layer8b_case(2, n=n, budget=2048, cap=n)
     q, k, v = dev(case.q, "bf16"), dev(case.k, "bf16"), dev(case.v, "bf16")
     lens = dev_i32(case.lengths)
     b, hq, w, d = case.q.shape
@@ -52,7 +56,7 @@ def test_score_evict_graph_replays(mode):
         with torch.cuda.stream(s):
             step()                                 # eager work between replays
         torch.cuda.synchronize()
-    log(f"[graph] {mode}: 4 replays equal to the eager step")
+    log(f"[graph] {mode} n={n}: 4 replays equal to the eager step")
 
 
 def test_threshold_cut_graph_replays():
@@ -76,3 +80,47 @@ def test_threshold_cut_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(kept, want), rep
+
+
+@pytest.mark.parametrize("mode", ["keysum", "gram"])
+def test_score_evict_slots_graph_replays(mode):
+    # the slot-reuse entry on the decode cache: the one-launch step's slot
+    # form (key-sum) or the Gram finish (Gram), captured once and replayed
+    case = synth.layer8b_case(3, n=2176, budget=2048, cap=2176)
+    q, k = dev(case.q, "bf16"), dev(case.k, "bf16")
+    lens = dev_i32(case.lengths)
+    b, hq, w, d = case.q.shape
+    hkv, cap = case.k.shape[1], case.k.shape[2]
+    rng = np.random.default_rng(5)
+    pos = dev_i32(np.stack([rng.permutation(50_000)[:cap] for _ in range(hkv)])[None])
+    ws = torch.empty(K.kvsel_score_evict_workspace(b, hq, hkv, d, w, cap, 2048), dtype=torch.uint8,
+                     device="cuda")
+    ev = torch.empty((b, hkv, cap), dtype=torch.int32, device="cuda")
+    ne = torch.empty((b, hkv), dtype=torch.int32, device="cuda")
+    z = torch.empty((b, hkv, cap), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+
+    def step():
+        K.kvsel_score_evict_slots(q, k, lens, 2048, 0.1, mode, pos=pos, evict_out=ev, n_evict_out=ne,
+                                  scores_out=z, workspace=ws, stream=s)
+
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (ev, ne, z)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (ev, ne, z):
+            t.fill_(-3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, w_ in zip((ev, ne, z), want):
+            assert torch.equal(t, w_), (mode, rep)
+        with torch.cuda.stream(s):
+            step()                                 # eager work between replays
+        torch.cuda.synchronize()
+    log(f"[graph] slots {mode}: 4 replays equal to the eager step")
