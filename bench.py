@@ -84,6 +84,20 @@ def fused_gram_step(mode: str, cap: int, b: int = 1, hkv: int = HKV, m: int = HQ
             and nch * hkv * b <= FUSED_CAPACITY)
 
 
+SCORES_PAIRS_CAPACITY = 768   # work-groups of k_scores_pairs resident at once (three per CU)
+
+
+def scores_pairs_step(mode: str, cap: int, b: int = 1, hkv: int = HKV, m: int = HQ // HKV * W) -> bool:
+    """Short Gram-form caches (bf16, d = 128, at most 32 window rows per KV
+    head, the pair-block Gram units): the one-launch score units and the
+    pair-block Gram units in one launch, when the score units (their count
+    rounded up to a multiple of 8) fit on the device at once; otherwise
+    k_stats, then the pooling beside the pair units."""
+    nch = -(-cap // 256)
+    return (mode == "gram" and m <= 32 and cap <= GRAM_PAIR_CAP and nch <= FUSED_MAX_CHUNKS
+            and -(-nch * hkv * b // 8) * 8 <= SCORES_PAIRS_CAPACITY)
+
+
 SCORES_FUSED_CAPACITY = 1024  # work-groups of the one-launch score pass resident at once (four per CU)
 
 
@@ -124,6 +138,8 @@ def rkv_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV, budget: int = B
     if fused_step(mode, cap, b, hkv):
         return ["fused"]
     ks = unfused_kernels(mode, cap)
+    if scores_pairs_step(mode, cap, b, hkv):
+        ks = ["scores_pairs"] + [k for k in ks if k not in ("stats", "pool_pairs")]
     if scores_fused(mode, cap, b, hkv):
         ks = ["scores"] + [k for k in ks if k not in ("stats", "reduce", "pool")]
     if select_one_launch(cap, b, hkv, budget):
@@ -140,8 +156,11 @@ def slot_kernels(mode: str, cap: int, b: int = 1, hkv: int = HKV) -> list:
     if fused_step(mode, cap, b, hkv):
         return ["fused_slots"]
     if fused_gram_step(mode, cap, b, hkv):
-        return ["stats", "pool_pairs", "fused_fin_slots"]
+        return (["scores_pairs"] if scores_pairs_step(mode, cap, b, hkv) else ["stats", "pool_pairs"]) \
+            + ["fused_fin_slots"]
     ks = [k for k in unfused_kernels(mode, cap) if k not in ("thresh", "compact")]
+    if scores_pairs_step(mode, cap, b, hkv):
+        ks = ["scores_pairs"] + [k for k in ks if k not in ("stats", "pool_pairs")]
     if scores_fused(mode, cap, b, hkv):
         ks = ["scores"] + [k for k in ks if k not in ("stats", "reduce", "pool")]
     return ks + ["thresh", "evict"]
@@ -222,6 +241,10 @@ def rkv_cost(mode: str, b: int = 1, n: int = N, budget: int = BUDGET, hkv: int =
         # Gram units in one launch; counted by its matrix-core work
         cost["pool_pairs"] = {"bytes": 2 * kb + 4 * tok + 4 * tok * -(-n // 128), "flops": alg,
                               "flops_executed": exe}
+        # the score units (K once, I and the key weights written) beside the
+        # pair units; counted by its matrix-core work
+        cost["scores_pairs"] = {"bytes": kb + 8 * tok + 4 * tok * -(-n // 128), "flops": alg,
+                                "flops_executed": exe}
         # the one-launch finish of short caches (slot reuse): the Gram slots,
         # weights and importance read, Z and the evicted list written
         cost["fused_fin_slots"] = {"bytes": 4 * tok * -(-n // 128) + 12 * tok
@@ -648,7 +671,7 @@ def run_refreekv_rows(hip, n_layers, steps, k_rows=64):
 KERNEL_SOURCES = {"stats": "scores.hip", "reduce": "scores.hip", "pool": "scores.hip",
                   "gram": "gram.hip", "gram_fin": "gram.hip", "thresh": "select.hip", "select_compact": "select.hip",
                   "compact": "select.hip", "fused": "fused.hip", "fused_slots": "fused.hip", "scores": "fused.hip",
-                  "pool_pairs": "scores.hip", "fused_fin_slots": "fused.hip",
+                  "pool_pairs": "scores.hip", "fused_fin_slots": "fused.hip", "scores_pairs": "fused.hip",
                   "evict": "select.hip", "select": "select.hip", "gather": "select.hip",
                   "cut_energy": "cut.hip", "cut_scan": "cut.hip", "cut_compact": "cut.hip"}
 

@@ -153,11 +153,12 @@ ScoreWs score_ws(void* base, int b, int hkv, int d, int m, int cap, kvsel_redund
   ScoreWs w{};
   w.err = c.take<int32_t>(64);
   if (gram) {
+    // the one-launch score pass (any length: beside the pair units on short
+    // caches) and, on short caches, the one-launch finish
     w.fepoch = c.take<uint64_t>(heads);
-    if (nchunk > kFusedMaxChunks) {
-      w.fpub_a = c.take<uint64_t>(heads * nchunk * kGramWordsA);
-      w.fmerged = c.take<uint64_t>(heads * kGramWordsA);
-    } else {
+    w.fpub_a = c.take<uint64_t>(heads * nchunk * kGramWordsA);
+    w.fmerged = c.take<uint64_t>(heads * kGramWordsA);
+    if (nchunk <= kFusedMaxChunks) {
       // the short-cache step's Gram finish: barrier flags and score keys
       w.fflags = c.take<uint64_t>(2 * heads * kFusedMaxChunks);
       w.fpub_b = c.take<uint64_t>(heads * cap);
@@ -250,36 +251,8 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
   p.z_out = z_out;
   p.hist = hist;
   const int sm = mode == KVSEL_R_GRAM ? kModeGram : kModeKeysum;
-  // longer caches (more than kFusedMaxChunks chunks per head; the workspace
-  // then holds the merged records): one launch reading K once for the
-  // scores (the Gram form's importance and key weights), when its grid fits
-  // on the device at once.  On shorter caches the separate kernels measured
-  // as fast: k_pool merges the partials itself there, so one launch
-  // boundary is all a score pass would save, and its two exchanges between
-  // work-groups cost as much.
-  bool scored = false;
-  if (dt == KVSEL_BF16 && d == 128 && p.m <= 32 && ws.fmerged && !separate_kernels()) {
-    const ScoresFusedParams fp{p, ws.fepoch, ws.fpub_a, ws.fmerged, next_salt()};
-    const int grid = scores_fused_grid(sm, fp);
-    if (grid > 0) {
-      KV_TRY(launch_scores_fused(sm, fp, grid, stream, tr));
-      scored = true;
-    }
-  }
-  // short Gram-form caches: k_stats writes the key weights, then the pooling
-  // and the pair-block Gram units share one launch (same arithmetic, same
-  // bits as the separate kernels)
-  const bool pool_pairs = !scored && mode == KVSEL_R_GRAM && dt == KVSEL_BF16 && d == 128 &&
-                          p.mp == 32 && cap <= kGramPairCap && p.nchunk <= kFuseReduceChunks;
-  if (!scored) {
-    p.fuse_reduce = p.nchunk <= kFuseReduceChunks;
-    p.w_in_stats = pool_pairs ? 1 : 0;
-    KV_TRY(launch_stats(dt, d, sm, p, stream, tr));
-    if (!p.fuse_reduce) KV_TRY(launch_reduce(d, sm, p, stream, tr));
-    if (!pool_pairs) KV_TRY(launch_pool(dt, d, sm, p, stream, tr));
-  }
+  GramParams gp{};
   if (mode == KVSEL_R_GRAM) {
-    GramParams gp{};
     gp.k = p.k;
     gp.lengths = lengths;
     gp.b = b;
@@ -295,9 +268,47 @@ kvsel_status run_scores(kvsel_dtype dt, kvsel_redundancy mode, const void* q, co
     gp.rs = ws.grs;
     gp.part = ws.gpart;
     gp.nsmax = ws.nsmax;
-    if (pool_pairs) {
+  }
+  // short Gram-form caches: the pair-block Gram units (which weigh keys
+  // themselves) run beside the importance pass, in one launch with the
+  // one-launch score units when those fit on the device together, else
+  // beside the pooling after k_stats; the same bits either way
+  const bool short_gram = mode == KVSEL_R_GRAM && dt == KVSEL_BF16 && d == 128 && p.mp == 32 &&
+                          cap <= kGramPairCap && p.nchunk <= kFuseReduceChunks;
+  bool scored = false, paired = false;
+  if (short_gram && !separate_kernels()) {
+    const ScoresFusedParams fp{p, ws.fepoch, ws.fpub_a, ws.fmerged, next_salt()};
+    const GramParams gc = gram_config(dt, d, gp);
+    if (scores_pairs_fit(fp)) {
+      KV_TRY(launch_scores_pairs(fp, gc, stream, tr));
+      scored = paired = true;
+    }
+  }
+  // longer caches (more than kFusedMaxChunks chunks per head): one launch
+  // reading K once for the scores (the Gram form's importance and key
+  // weights), when its grid fits on the device at once.  On shorter caches
+  // the separate kernels measured as fast: k_pool merges the partials itself
+  // there, so one launch boundary is all a score pass would save, and its
+  // two exchanges between work-groups cost as much.
+  if (!scored && dt == KVSEL_BF16 && d == 128 && p.m <= 32 && ws.fmerged &&
+      p.nchunk > kFusedMaxChunks && !separate_kernels()) {
+    const ScoresFusedParams fp{p, ws.fepoch, ws.fpub_a, ws.fmerged, next_salt()};
+    const int grid = scores_fused_grid(sm, fp);
+    if (grid > 0) {
+      KV_TRY(launch_scores_fused(sm, fp, grid, stream, tr));
+      scored = true;
+    }
+  }
+  if (!scored) {
+    p.fuse_reduce = p.nchunk <= kFuseReduceChunks;
+    KV_TRY(launch_stats(dt, d, sm, p, stream, tr));
+    if (!p.fuse_reduce) KV_TRY(launch_reduce(d, sm, p, stream, tr));
+    if (!short_gram) KV_TRY(launch_pool(dt, d, sm, p, stream, tr));
+  }
+  if (mode == KVSEL_R_GRAM) {
+    if (short_gram) {
       const GramParams gc = gram_config(dt, d, gp);
-      KV_TRY(launch_pool_pairs(p, gc, stream, tr));
+      if (!paired) KV_TRY(launch_pool_pairs(p, gc, stream, tr));
       if (gram_fin) KV_TRY(launch_gram_fin(gc, stream, tr));
     } else {
       KV_TRY(launch_gram(dt, d, gp, stream, tr));

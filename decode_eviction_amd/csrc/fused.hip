@@ -41,6 +41,7 @@
 // on the device at once, so every wait ends; a wait that still exceeds its
 // poll limit sets bit 2 of the error word and continues.
 #include "common.hpp"
+#include "gram_pairs.hpp"
 #include "kernels.hpp"
 #include "scan.hpp"
 #include "tiles.hpp"
@@ -839,9 +840,10 @@ __device__ __forceinline__ void scores_fused_unit(const ScoresFusedParams& fp, i
       for (int j = 0; j < NC; ++j) kf[tt].c[j] = buf_ld128(rk, off + 32 * j, 0);
     }
   }
-  __shared__ uint32_t lh[kHistBins];
-  if (!kGram && hg)
-    for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
+  __shared__ uint32_t lh[kGram ? 1 : kHistBins];
+  if constexpr (!kGram)
+    if (hg)
+      for (int t = tid; t < kHistBins; t += 256) lh[t] = 0u;
 
   // ---- chunk partials (k_stats' arithmetic) as tagged words
   const float sc2 = p.scale2;
@@ -1013,6 +1015,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 void k_scores_fused(ScoresFusedParams fp) {
   const int v = blockIdx.x, hb = v / fp.s.nchunk;
   scores_fused_unit<E, D, MODE>(fp, v - hb * fp.s.nchunk, hb % fp.s.hkv, hb / fp.s.hkv);
+}
+
+// Short Gram-form caches: the score units of the one-launch pass (chunk
+// partials, merged through tagged words; importance and the key weights)
+// and the pair-block Gram units (which weigh keys from their own fragments)
+// in one grid.  The score units come first, their count rounded up to a
+// multiple of 8 so that the pair units keep their XCD-major placement:
+// dispatched before any pair unit, they are resident together, which their
+// exchange needs (the host checks that this many work-groups of the kernel
+// fit on the device at once); the pair units depend on K alone.
+struct ScoresPairsParams {
+  ScoresFusedParams f;
+  GramParams g;
+  int nscore;  // score work-groups, a multiple of 8
+};
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_scores_pairs(ScoresPairsParams sp) {
+  const int bx = blockIdx.x;
+  if (bx >= sp.nscore) {
+    gram_pairs_unit(sp.g, bx - sp.nscore);
+    return;
+  }
+  const int nch = sp.f.s.nchunk;
+  if (bx >= nch * sp.f.s.hkv * sp.f.s.b) return;
+  const int hb = bx / nch;
+  scores_fused_unit<BF16, 128, kModeGram>(sp.f, bx - hb * nch, hb % sp.f.s.hkv, hb / sp.f.s.hkv);
+}
+
+static int g_scores_pairs_capacity[64];
+
+bool scores_pairs_fit(const ScoresFusedParams& f) {
+  const long nscore = ((long)f.s.nchunk * f.s.hkv * f.s.b + 7) / 8 * 8;
+  return grid_fits(k_scores_pairs, g_scores_pairs_capacity, nscore);
+}
+
+hipError_t launch_scores_pairs(const ScoresFusedParams& f, const GramParams& g, hipStream_t s, Trace* tr) {
+  const long nscore = ((long)f.s.nchunk * f.s.hkv * f.s.b + 7) / 8 * 8;
+  const long total = nscore + gram_pair_units(g);
+  if (total >= (1L << 31)) return hipErrorInvalidValue;
+  const ScoresPairsParams sp{f, g, (int)nscore};
+  return launch_k(k_scores_pairs, dim3((unsigned)total), dim3(256), s, tr, sp);
 }
 
 static int g_fused_capacity[3][64];

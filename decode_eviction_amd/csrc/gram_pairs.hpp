@@ -48,23 +48,34 @@ __device__ __forceinline__ void gram_pairs_unit(const GramParams& p, int bx) {
   if (J * BS >= n) return;
   const long head = (long)bi * p.hkv + h;
   const char* kb = p.k + head * (long)p.cap * RB;
-  const float* wv = p.inv_norm + head * (long)p.wstride;
   float* part = p.part + head * (long)p.nsmax * p.cap;
 
   // A: rows I*BS + 32 wave + 16 rt + c16; lane chunk g of each 32-dim k-step
   u32x4_t af[2][4];
-  float wrow[2][4];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const int row = I * BS + 32 * wave + 16 * rt + c16;
     const char* src = kb + (long)(row < n ? row : 0) * RB + g * 16;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) af[rt][ks] = row < n ? ld16(src + 64 * ks) : zero4();
+  }
+  // The weights 1/||k|| of the fold, taken from the fragments themselves (so
+  // that the unit depends on nothing but K): the four lanes g of a row hold
+  // its 128 dimensions; lane 4g + i then passes row 4g + i of the tile to the
+  // lanes that fold it.  Rows past n are zero and weigh 0.
+  float wrow[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = I * BS + 32 * wave + 16 * rt + 4 * g + i;
-      wrow[rt][i] = r < n ? wv[r] : 0.f;
-    }
+  for (int rt = 0; rt < 2; ++rt) {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = dot2_bf16(af[rt][ks][e], af[rt][ks][e], ss);
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float wr = inv_norm_of(ss);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wrow[rt][i] = __shfl(wr, 4 * g + i, 64);
   }
   // block J, copied once into LDS (columns past n read as zeros): chunk q of
   // column c at slot 16 c + (q xor (c mod 16)), so the 16 lanes reading one
@@ -91,11 +102,21 @@ __device__ __forceinline__ void gram_pairs_unit(const GramParams& p, int bx) {
   float wcol[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
-    const int cl = 16 * ct + c16, col = J * BS + cl;
-    wcol[ct] = col < n ? wv[col] : 0.f;
+    const int cl = 16 * ct + c16;
     u32x4_t bf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) bf[ks] = bs[cl * 16 + ((4 * ks + g) ^ c16)];
+    {
+      // the column's weight from its fragments (columns past n read as zeros)
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = dot2_bf16(bf[ks][e], bf[ks][e], ss);
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      wcol[ct] = inv_norm_of(ss);
+    }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};

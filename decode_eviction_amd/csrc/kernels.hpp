@@ -118,9 +118,6 @@ struct ScoreParams {
   // R-KV modes with nchunk <= kFuseReduceChunks: k_pool merges the chunk
   // partials itself (in k_reduce's order) and k_reduce is not launched
   int fuse_reduce;
-  // Gram form: k_stats writes the key weights 1/||k_j|| (and k_pool does
-  // not), so that the Gram units can run beside the pooling
-  int w_in_stats;
   // outputs (never null; the host substitutes workspace buffers)
   float* i_out;             // [b][Hkv][cap]
   float* r_out;             // [b][Hkv][cap] (may be null in keysum mode)
@@ -365,8 +362,9 @@ long gram_pair_units(const GramParams& p);
 // k_gram_fin alone (after the pair units ran inside k_pool_pairs).
 hipError_t launch_gram_fin(const GramParams& p, hipStream_t s, Trace* tr);
 // Short Gram-form caches (bf16, d = 128, at most 32 window rows per KV head,
-// cap <= kGramPairCap): the importance pooling and the pair-block Gram units
-// in one launch, after k_stats wrote the key weights (p.w_in_stats).
+// cap <= kGramPairCap): the importance pooling (with the key weights) and the
+// pair-block Gram units (which weigh keys themselves) in one launch, after
+// k_stats.
 hipError_t launch_pool_pairs(const ScoreParams& p, const GramParams& g, hipStream_t s, Trace* tr);
 hipError_t launch_select(const SelectParams& p, hipStream_t s, Trace* tr);
 hipError_t launch_hist(const SelectParams& p, hipStream_t s, Trace* tr);
@@ -386,6 +384,11 @@ hipError_t launch_fused(const FusedParams& p, hipStream_t s, Trace* tr);
 // sequence)), or 0 when those do not all fit on the device at once (then the
 // separate kernels run)
 int scores_fused_grid(int mode, const ScoresFusedParams& p);
+// Short Gram-form caches: the one-launch score units and the pair-block Gram
+// units in one grid (k_scores_pairs), when the score units fit on the device
+// together.
+bool scores_pairs_fit(const ScoresFusedParams& f);
+hipError_t launch_scores_pairs(const ScoresFusedParams& f, const GramParams& g, hipStream_t s, Trace* tr);
 hipError_t launch_scores_fused(int mode, const ScoresFusedParams& p, int grid, hipStream_t s, Trace* tr);
 
 // Work-groups of kern resident on the device at once (cached per device;

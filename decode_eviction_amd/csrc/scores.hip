@@ -88,19 +88,7 @@ void k_stats(ScoreParams p) {
   }
 
   // key-sum mode: key norms and the chunk's unit-key sum (the Gram form's
-  // norms are taken in k_pool, which reads K from the last-level cache,
-  // unless the Gram units run beside the pooling: then here, with the same
-  // arithmetic)
-  if constexpr (MODE == kModeGram) {
-    if (p.w_in_stats) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        float ss = frag_sumsq<E, NC>(kf[tt]);
-        ss += xor32(ss);
-        if (hf == 0) p.inv_norm[head * (long)p.wstride + tok0 + 32 * tt + l32] = inv_norm_of(ss);
-      }
-    }
-  }
+  // norms are taken in k_pool, which reads K from the last-level cache)
   auto norms = [&]() {
     if constexpr (MODE == kModeKeysum) {
       float inv[2];
@@ -352,12 +340,14 @@ void k_pool(ScoreParams p) {
 #include "pool_body.inc"
 }
 
-// Short Gram-form caches: the pooling units (importance; the key weights
-// came from k_stats) and the pair-block Gram units in one grid.  Both read
-// only what k_stats wrote, so they are independent: the pooling work-groups
-// come first (their count rounded up to a multiple of 8, so that the Gram
-// units keep their XCD-major order) and fill CUs the pair units leave idle
-// in their second round.
+// Short Gram-form caches: the pooling units (importance and the key weights
+// the finish uses) and the pair-block Gram units (which weigh keys from
+// their own fragments) in one grid.  Both read only K and what k_stats
+// wrote, so they are independent: the pooling work-groups come first (their
+// count rounded up to a multiple of 8, so that the Gram units keep their
+// XCD-major order) and fill CUs the pair units leave idle in their second
+// round.  Used where the one-launch score units cannot run beside the pairs
+// (k_scores_pairs in fused.hip) and with KVSEL_SEPARATE_KERNELS=1.
 struct PoolPairsParams {
   ScoreParams s;
   GramParams g;

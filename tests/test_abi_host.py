@@ -213,8 +213,9 @@ def test_bench_kernel_names_follow_the_reduce_folding():
             folded = -(-cap // chunk) <= fuse
             assert ("reduce" not in names) == folded, (mode, cap)
             want = [k for k in bench.KERNELS[mode] if k not in ("reduce", "thresh", "compact")]
-            if mode == "gram" and cap <= pair_cap:   # pooling and pair units in one launch
-                want = ["stats", "pool_pairs", "gram_fin"]
+            if mode == "gram" and cap <= pair_cap:   # the pair units beside the importance pass
+                want = ["scores_pairs", "gram_fin"] if bench.scores_pairs_step(mode, cap) else \
+                    ["stats", "pool_pairs", "gram_fin"]
             assert want == [k for k in names if k != "reduce"], (mode, cap)
     # 64 sequences of 2176 tokens: 9 * 8 * 64 work-groups do not fit at once
     assert bench.rkv_kernels("keysum", 2176, b=64) != ["fused"]
@@ -223,13 +224,13 @@ def test_bench_kernel_names_follow_the_reduce_folding():
     assert bench.rkv_kernels("keysum", 32768)[0] == "scores"
     assert bench.rkv_kernels("keysum", 8192, b=64)[0] == "stats"
     # the Gram form's score pass on the same caches
-    assert bench.rkv_kernels("gram", 2176) == ["stats", "pool_pairs", "gram_fin", "select_compact"]
+    assert bench.rkv_kernels("gram", 2176) == ["scores_pairs", "gram_fin", "select_compact"]
     assert bench.rkv_kernels("gram", 2176, b=64) == ["stats", "pool_pairs", "gram_fin", "thresh", "compact"]
     assert bench.rkv_kernels("gram", 32768)[:3] == ["scores", "gram", "gram_fin"]
     assert bench.rkv_kernels("gram", 8192, b=64)[0] == "stats"
     # slot reuse: the fused step's slot form where the fused step applies,
     # otherwise the scores as a compacting call computes them
-    assert bench.slot_kernels("gram", 2176) == ["stats", "pool_pairs", "fused_fin_slots"]
+    assert bench.slot_kernels("gram", 2176) == ["scores_pairs", "fused_fin_slots"]
     assert bench.slot_kernels("gram", 2176, b=64) == ["stats", "pool_pairs", "gram_fin", "thresh", "evict"]
     assert bench.slot_kernels("keysum", 2176) == ["fused_slots"]
     assert bench.slot_kernels("keysum", 2176, b=64) == ["stats", "pool", "thresh", "evict"]
