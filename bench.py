@@ -677,12 +677,15 @@ KERNEL_SOURCES = {"stats": "scores.hip", "reduce": "scores.hip", "pool": "scores
 
 
 def source_digest(kernel: str) -> str:
-    """sha1 over the sources a kernel is built from (its file and the shared
-    headers)."""
+    """sha1 over the sources a kernel is built from (its file and every
+    shared header or included source)."""
     import hashlib
     h = hashlib.sha1()
-    for f in (KERNEL_SOURCES[kernel], "common.hpp", "kernels.hpp", "tiles.hpp", "scan.hpp"):
-        with open(os.path.join(ROOT, "decode_eviction_amd", "csrc", f), "rb") as fh:
+    csrc = os.path.join(ROOT, "decode_eviction_amd", "csrc")
+    shared = sorted(os.path.basename(p) for p in glob.glob(os.path.join(csrc, "*.hpp")) +
+                    glob.glob(os.path.join(csrc, "*.inc")))
+    for f in [KERNEL_SOURCES[kernel]] + shared:
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
