@@ -1034,6 +1034,10 @@ struct ScoresPairsParams {
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_scores_pairs(ScoresPairsParams sp) {
   const int bx = blockIdx.x;
   if (bx >= sp.nscore) {
+    // the pair units, whose rounds set the launch's length, take issue
+    // priority over the score units' waves on a shared CU (decode call
+    // 39.4-39.6 -> 38.3 us; the reverse measured no change)
+    __builtin_amdgcn_s_setprio(2);
     gram_pairs_unit(sp.g, bx - sp.nscore);
     return;
   }
