@@ -229,6 +229,60 @@ def _red_keysum_no_self(k):
     return (u @ u.sum(axis=0)) / (n - 1)
 
 
+def _kept_oldest(n, L, m):
+    # the oldest L - m positions after the sinks instead of the newest
+    s = min(m, n, L)
+    return np.concatenate([np.arange(s), np.arange(s, L)]).astype(np.int64)
+
+
+def _cut_fixed_no_sink_floor(E, m, T):
+    # the walk's length without the floor of m sink tokens
+    E = np.asarray(E, np.uint64)
+    n = E.shape[0]
+    if n == 0:
+        return 0
+    tau = int(np.ceil(float(int(E.sum(dtype=np.uint64))) * (1.0 - float(np.float32(T)))))
+    acc = 0
+    for pos, j in enumerate(rf.rank_order(n, m)):
+        acc += int(E[j])
+        if acc >= tau:
+            return pos + 1
+    return n
+
+
+def _unit_keys_squared_norm(k):
+    # divided by the squared norm instead of the norm
+    k64 = np.asarray(k, np.float64)
+    nrm2 = (k64 * k64).sum(axis=1)
+    out = np.zeros_like(k64)
+    nz = nrm2 > 0
+    out[nz] = k64[nz] / nrm2[nz, None]
+    return out
+
+
+def _red_rows_with_self(k, rows):
+    # the i == j term left in
+    u = rkv.unit_keys(k)
+    n = len(u)
+    rows = np.asarray(rows, dtype=np.int64)
+    if n <= 1:
+        return np.zeros(len(rows))
+    return (u[rows] @ u.T).sum(axis=1) / (n - 1)
+
+
+_score_evict_orig = rkv.score_evict
+
+
+def _score_evict_strided(q, k, v, lengths, lam, budget, form="definition", heads=None,
+                         budgets=None):
+    # query heads grouped by stride (h, h + Hkv, ...) instead of contiguously
+    q = np.asarray(q)
+    hkv = k.shape[1]
+    g = q.shape[1] // hkv
+    perm = np.arange(q.shape[1]).reshape(g, hkv).T.reshape(-1)
+    return _score_evict_orig(q[:, perm], k, v, lengths, lam, budget, form, heads, budgets)
+
+
 MUTANTS = [
     (rkv, "importance", _imp_no_scale, pins_rkv),
     (rkv, "importance", _imp_max_pool, pins_rkv),
@@ -254,6 +308,11 @@ MUTANTS = [
     (rkv, "evict_slots", _evict_ties_by_slot, pins_rkv),
     (rkv, "head_budget", _head_budget_unclamped, pins_rkv),
     (rkv, "redundancy_keysum", _red_keysum_no_self, pins_rkv),
+    (rf, "kept_positions", _kept_oldest, pins_rf),
+    (rf, "cut_length_fixed", _cut_fixed_no_sink_floor, pins_rf),
+    (rkv, "unit_keys", _unit_keys_squared_norm, pins_rkv),
+    (rkv, "redundancy_rows", _red_rows_with_self, pins_rkv),
+    (rkv, "score_evict", _score_evict_strided, pins_rkv),
 ]
 
 
